@@ -1,0 +1,321 @@
+/*
+ * atlas_oracle.c -- fp64 CPU oracle for the ATLAS / Titans test-time memory.
+ *
+ * TEST INFRASTRUCTURE ONLY: the plain, slow, sequential reference the GPU
+ * library is checked against.  It shares no code with the GPU library.
+ *
+ * The update is replayed exactly in the order the pages state it, with the
+ * memory weights materialised after every token:
+ *
+ *   for each chunk of b tokens (ATLAS review, sec. 3.3 "Parallelizing Omega
+ *   Rule"; Miras review, chunk-wise parallel training):
+ *     theta_c <- current weights            (state at the end of the last chunk)
+ *     for every token i whose window reaches into the chunk:
+ *        G_i <- gradient of gamma_i * l(theta_c; phi(k_i), v_i)
+ *     for every token n of the chunk, in order:
+ *        g_n   = sum of G_i over the window i = n-c+1 .. n     (Omega rule,
+ *                ATLAS review sec. 3.2; window truncated at the first token)
+ *        S     = eta_n * S - theta_n * g_n                      (Titans review,
+ *                sec. 3.1, momentum / "past surprise")
+ *        W     = (1 - alpha_n) * W + S                          (Titans review,
+ *                sec. 3.1, "Forgetting Mechanism")
+ *        y_n   = f_W(phi(q_n))                                  (Titans review,
+ *                sec. 3.1, "Retrieving a Memory")
+ *
+ * Memory forms (Titans review sec. 3.1 "Memory Architecture"; ATLAS review
+ * sec. 2 "Deep Memory Module"): linear f(x) = M x, or the two-layer MLP
+ * f(x) = [r +] W2 gelu(W1 x) with the exact erf GELU and no biases.
+ * phi follows ATLAS review sec. 3.1 "Polynomial Feature Mapping".
+ *
+ * The per-token gradient is written out from the chain rule; its
+ * factors are the per-token error and hidden activations.  No blocking,
+ * fusion or reordering is applied beyond materialising each G_i once per chunk.
+ */
+#include "atlas_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+static int poly_block(int p) { return p + p * (p + 1) / 2; }
+
+int oracle_feature_dim(const oracle_config* cfg) {
+  switch (cfg->feature_map) {
+    case ORC_PHI_ID: return cfg->d_k;
+    case ORC_PHI_POLY2: return poly_block(cfg->d_k);
+    case ORC_PHI_RAW_POLY2: return cfg->d_k + poly_block(cfg->poly_dims);
+    default: return -1;
+  }
+}
+
+long oracle_param_count(const oracle_config* cfg) {
+  long D = oracle_feature_dim(cfg);
+  if (cfg->memory == ORC_LINEAR) return (long)cfg->d_v * D;
+  return (long)cfg->hidden * D + (long)cfg->d_v * cfg->hidden;
+}
+
+/* [x_0..x_{p-1}, then x_a*x_b for a <= b in row-major upper-triangle order] */
+static void poly2(const double* x, int p, double* out) {
+  int o = 0;
+  for (int a = 0; a < p; ++a) out[o++] = x[a];
+  for (int a = 0; a < p; ++a)
+    for (int b = a; b < p; ++b) out[o++] = x[a] * x[b];
+}
+
+void oracle_phi(const oracle_config* cfg, const double* x, double* out) {
+  switch (cfg->feature_map) {
+    case ORC_PHI_ID:
+      memcpy(out, x, sizeof(double) * cfg->d_k);
+      break;
+    case ORC_PHI_POLY2:
+      poly2(x, cfg->d_k, out);
+      break;
+    case ORC_PHI_RAW_POLY2:
+      memcpy(out, x, sizeof(double) * cfg->d_k);
+      poly2(x, cfg->poly_dims, out + cfg->d_k);
+      break;
+  }
+}
+
+static double gelu(double z) { return 0.5 * z * (1.0 + erf(z / sqrt(2.0))); }
+/* d/dz of z * Phi(z) = Phi(z) + z * N(z; 0, 1) */
+static double gelu_prime(double z) {
+  const double pi = 3.14159265358979323846;
+  return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * exp(-0.5 * z * z) / sqrt(2.0 * pi);
+}
+
+/* Forward pass; keeps the hidden pre-activation z when asked (MLP only). */
+static void apply(const oracle_config* cfg, const double* th, const double* x,
+                  const double* r, double* y, double* z_keep) {
+  const int D = oracle_feature_dim(cfg), dv = cfg->d_v, h = cfg->hidden;
+  if (cfg->memory == ORC_LINEAR) {
+    for (int o = 0; o < dv; ++o) {
+      double s = 0.0;
+      for (int d = 0; d < D; ++d) s += th[(long)o * D + d] * x[d];
+      y[o] = s;
+    }
+    return;
+  }
+  const double* W1 = th;
+  const double* W2 = th + (long)h * D;
+  double* z = z_keep ? z_keep : (double*)malloc(sizeof(double) * h);
+  double* a = (double*)malloc(sizeof(double) * h);
+  for (int j = 0; j < h; ++j) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += W1[(long)j * D + d] * x[d];
+    z[j] = s;
+    a[j] = gelu(s);
+  }
+  for (int o = 0; o < dv; ++o) {
+    double s = cfg->residual ? r[o] : 0.0;
+    for (int j = 0; j < h; ++j) s += W2[(long)o * h + j] * a[j];
+    y[o] = s;
+  }
+  free(a);
+  if (!z_keep) free(z);
+}
+
+void oracle_memory_apply(const oracle_config* cfg, const double* theta,
+                         const double* x, const double* r, double* y) {
+  apply(cfg, theta, x, r, y, NULL);
+}
+
+/* Factors of one token's gradient at theta:
+ *   linear: dY (d_v)            G = dY x^T
+ *   MLP   : d1 (h), d2 (d_v), a (h)   G = { d1 x^T , d2 a^T }
+ * dY / d2 = dLoss/df: L2 -> s*gamma*(f - v);  DOT -> -s*gamma*v.          */
+static void grad_factors(const oracle_config* cfg, const double* th,
+                         const double* x, const double* r, const double* v,
+                         double gamma, double* d1, double* d2, double* a) {
+  const int D = oracle_feature_dim(cfg), dv = cfg->d_v, h = cfg->hidden;
+  const double s = cfg->grad_scale;
+  double* f = (double*)malloc(sizeof(double) * dv);
+  double* z = cfg->memory == ORC_MLP ? (double*)malloc(sizeof(double) * h) : NULL;
+  apply(cfg, th, x, r, f, z);
+  for (int o = 0; o < dv; ++o)
+    d2[o] = cfg->bias == ORC_BIAS_L2 ? s * gamma * (f[o] - v[o]) : -s * gamma * v[o];
+  if (cfg->memory == ORC_MLP) {
+    const double* W2 = th + (long)h * D;
+    for (int j = 0; j < h; ++j) {
+      double back = 0.0;
+      for (int o = 0; o < dv; ++o) back += W2[(long)o * h + j] * d2[o];
+      d1[j] = back * gelu_prime(z[j]);
+      a[j] = gelu(z[j]);
+    }
+    free(z);
+  }
+  free(f);
+}
+
+/* g += G(d1, d2, a, x), the outer-product form of one token's gradient. */
+static void add_grad(const oracle_config* cfg, const double* x, const double* d1,
+                     const double* d2, const double* a, double* g) {
+  const int D = oracle_feature_dim(cfg), dv = cfg->d_v, h = cfg->hidden;
+  if (cfg->memory == ORC_LINEAR) {
+    for (int o = 0; o < dv; ++o)
+      for (int d = 0; d < D; ++d) g[(long)o * D + d] += d2[o] * x[d];
+    return;
+  }
+  double* gW2 = g + (long)h * D;
+  for (int j = 0; j < h; ++j)
+    for (int d = 0; d < D; ++d) g[(long)j * D + d] += d1[j] * x[d];
+  for (int o = 0; o < dv; ++o)
+    for (int j = 0; j < h; ++j) gW2[(long)o * h + j] += d2[o] * a[j];
+}
+
+void oracle_token_grad(const oracle_config* cfg, const double* theta,
+                       const double* x, const double* r, const double* v,
+                       double gamma, double* grad) {
+  const int dv = cfg->d_v, h = cfg->hidden > 0 ? cfg->hidden : 1;
+  double* d1 = (double*)malloc(sizeof(double) * h);
+  double* d2 = (double*)malloc(sizeof(double) * dv);
+  double* a = (double*)malloc(sizeof(double) * h);
+  memset(grad, 0, sizeof(double) * oracle_param_count(cfg));
+  grad_factors(cfg, theta, x, r, v, gamma, d1, d2, a);
+  add_grad(cfg, x, d1, d2, a, grad);
+  free(d1); free(d2); free(a);
+}
+
+static int config_ok(const oracle_config* c) {
+  if (c->n_seq < 0 || c->seq_len < 0 || c->d_k <= 0 || c->d_v <= 0) return 0;
+  if (c->window < 1 || c->chunk < 1) return 0;
+  if (oracle_feature_dim(c) <= 0) return 0;
+  if (c->feature_map == ORC_PHI_RAW_POLY2 && (c->poly_dims < 1 || c->poly_dims > c->d_k)) return 0;
+  if (c->memory == ORC_MLP) {
+    if (c->hidden < 1) return 0;
+    if (c->residual && c->d_k != c->d_v) return 0;
+  } else if (c->memory != ORC_LINEAR) {
+    return 0;
+  }
+  return c->bias == ORC_BIAS_L2 || c->bias == ORC_BIAS_DOT;
+}
+
+/* One sequence. */
+static void run_sequence(const oracle_config* cfg, const double* q, const double* k,
+                         const double* v, const double* al, const double* et,
+                         const double* th, const double* ga, double* W, double* S,
+                         double* hk, double* hv, double* hg, int64_t* count,
+                         double* out) {
+  const int N = cfg->seq_len, dk = cfg->d_k, dv = cfg->d_v, c = cfg->window;
+  const int b = cfg->chunk, h = cfg->hidden > 0 ? cfg->hidden : 1;
+  const int D = oracle_feature_dim(cfg);
+  const long P = oracle_param_count(cfg);
+  const int halo = c - 1;
+  /* tokens before this call that still exist (sequence start truncates) */
+  const int halo_valid = (int)(*count < halo ? *count : halo);
+
+  double* Wc = (double*)malloc(sizeof(double) * P);
+  double* g = (double*)malloc(sizeof(double) * P);
+  const int win = b + c - 1;
+  double* X = (double*)malloc(sizeof(double) * win * D);
+  double* D1 = (double*)malloc(sizeof(double) * win * h);
+  double* D2 = (double*)malloc(sizeof(double) * win * dv);
+  double* A = (double*)malloc(sizeof(double) * win * h);
+  double* xq = (double*)malloc(sizeof(double) * D);
+  double* Sloc = (double*)calloc(P, sizeof(double));
+
+  for (int t0 = 0; t0 < N; t0 += b) {
+    const int te = (t0 + b < N ? t0 + b : N) - 1;
+    memcpy(Wc, W, sizeof(double) * P);
+    /* window tokens i in [lo, te], relative to the call start; i < 0 is halo */
+    int lo = t0 - (c - 1);
+    if (lo < -halo_valid) lo = -halo_valid;
+    for (int i = lo; i <= te; ++i) {
+      const double *ki, *vi;
+      double gi;
+      if (i >= 0) {
+        ki = k + (long)i * dk; vi = v + (long)i * dv; gi = ga[i];
+      } else {
+        ki = hk + (long)(halo + i) * dk; vi = hv + (long)(halo + i) * dv; gi = hg[halo + i];
+      }
+      const int w = i - lo;
+      oracle_phi(cfg, ki, X + (long)w * D);
+      grad_factors(cfg, Wc, X + (long)w * D, ki, vi, gi, D1 + (long)w * h,
+                   D2 + (long)w * dv, A + (long)w * h);
+    }
+    for (int n = t0; n <= te; ++n) {
+      memset(g, 0, sizeof(double) * P);
+      int i0 = n - c + 1;
+      if (i0 < lo) i0 = lo;
+      for (int i = i0; i <= n; ++i) {
+        const int w = i - lo;
+        add_grad(cfg, X + (long)w * D, D1 + (long)w * h, D2 + (long)w * dv,
+                 A + (long)w * h, g);
+      }
+      const double eta_n = cfg->momentum ? et[n] : 0.0;
+      double* Sx = cfg->momentum ? S : Sloc;
+      for (long p = 0; p < P; ++p) {
+        Sx[p] = eta_n * Sx[p] - th[n] * g[p];
+        W[p] = (1.0 - al[n]) * W[p] + Sx[p];
+      }
+      oracle_phi(cfg, q + (long)n * dk, xq);
+      apply(cfg, W, xq, q + (long)n * dk, out + (long)n * dv, NULL);
+    }
+  }
+
+  /* new halo: the last c-1 tokens of (old halo ++ this call) */
+  if (halo > 0) {
+    double* nk = (double*)malloc(sizeof(double) * halo * dk);
+    double* nv = (double*)malloc(sizeof(double) * halo * dv);
+    double* ng = (double*)malloc(sizeof(double) * halo);
+    for (int j = 0; j < halo; ++j) {
+      const int i = N - halo + j;
+      if (i >= 0) {
+        memcpy(nk + (long)j * dk, k + (long)i * dk, sizeof(double) * dk);
+        memcpy(nv + (long)j * dv, v + (long)i * dv, sizeof(double) * dv);
+        ng[j] = ga[i];
+      } else {
+        memcpy(nk + (long)j * dk, hk + (long)(halo + i) * dk, sizeof(double) * dk);
+        memcpy(nv + (long)j * dv, hv + (long)(halo + i) * dv, sizeof(double) * dv);
+        ng[j] = hg[halo + i];
+      }
+    }
+    memcpy(hk, nk, sizeof(double) * halo * dk);
+    memcpy(hv, nv, sizeof(double) * halo * dv);
+    memcpy(hg, ng, sizeof(double) * halo);
+    free(nk); free(nv); free(ng);
+  }
+  *count += N;
+
+  free(Wc); free(g); free(X); free(D1); free(D2); free(A); free(xq); free(Sloc);
+}
+
+int oracle_forward(const oracle_config* cfg,
+                   const double* q, const double* k, const double* v,
+                   const double* alpha, const double* eta,
+                   const double* theta, const double* gamma,
+                   double* mem, double* mom,
+                   double* halo_k, double* halo_v, double* halo_g,
+                   int64_t* count, double* out) {
+  if (!config_ok(cfg)) return -1;
+  const long N = cfg->seq_len, dk = cfg->d_k, dv = cfg->d_v, halo = cfg->window - 1;
+  const long P = oracle_param_count(cfg);
+  int threads = 1;
+#pragma omp parallel
+  {
+#ifdef _OPENMP
+#pragma omp single
+    threads = omp_get_num_threads();
+#endif
+#pragma omp for schedule(dynamic, 1)
+    for (int s = 0; s < cfg->n_seq; ++s) {
+      run_sequence(cfg, q + s * N * dk, k + s * N * dk, v + s * N * dv,
+                   alpha + s * N, eta + s * N, theta + s * N, gamma + s * N,
+                   mem + s * P, mom + s * P,
+                   halo_k + s * halo * dk, halo_v + s * halo * dv, halo_g + s * halo,
+                   count + s, out + s * N * dv);
+    }
+  }
+  return threads;
+}

@@ -1,0 +1,107 @@
+/*
+ * atlas_oracle.h -- fp64 CPU oracle for the ATLAS / Titans test-time memory.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This header and atlas_oracle.c are the slow,
+ * sequential reference that the GPU library is checked against.  Only the
+ * test suite, the smoke check and the CPU-baseline leg of the benchmark may
+ * load it.  It shares no code, header, constant or helper with the GPU
+ * library, and nothing in the library may include or link it.
+ *
+ * What it computes (per sequence, tokens processed in the order given):
+ *   - feature map phi on keys and queries (ATLAS review, section 3.1,
+ *     "Polynomial Feature Mapping": all monomials up to degree p; here p<=2,
+ *     raw monomials, each unordered pair once, diagonal included);
+ *   - the Omega-rule inner loss over the last c tokens,
+ *     sum_i gamma_i * l(M; phi(k_i), v_i)  (ATLAS review, section 3.2,
+ *     "Sliding window recurrent model" / "Omega Rule");
+ *   - chunked gradients: every gradient in a chunk of b tokens is taken at
+ *     the memory state left by the previous chunk (ATLAS review, section
+ *     3.3 "Parallelizing Omega Rule"; Miras review, "Training"/parallelism);
+ *   - Titans momentum S_t = eta_t S_{t-1} - theta_t grad and decay
+ *     M_t = (1 - alpha_t) M_{t-1} + S_t (Titans review, section 3.1,
+ *     "Learning Process and Surprise Metric" and "Forgetting Mechanism");
+ *   - retrieval y_t = M_t(phi(q_t)), a plain forward pass with the memory
+ *     after token t's update (Titans review, section 3.1 "Retrieving a
+ *     Memory").
+ *
+ * Parity unpinned: the combination MLP memory + window c > 1 + chunk b > 1 +
+ * momentum is fixed by no closed form on the pages; it is pinned only through
+ * the special cases that reduce to one (see tests/test_oracle_pins.py).
+ */
+#ifndef ATLAS_ORACLE_H
+#define ATLAS_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_LINEAR = 0, ORC_MLP = 1 };
+enum { ORC_PHI_ID = 0, ORC_PHI_POLY2 = 1, ORC_PHI_RAW_POLY2 = 2 };
+enum { ORC_BIAS_L2 = 0, ORC_BIAS_DOT = 1 };
+
+typedef struct {
+  int n_seq;        /* independent sequences (batch * heads)                 */
+  int seq_len;      /* tokens per sequence in this call                       */
+  int d_k, d_v;     /* raw key/query width, value width                       */
+  int memory;       /* ORC_LINEAR: y = M x; ORC_MLP: y = [r] + W2 gelu(W1 x)  */
+  int hidden;       /* MLP hidden width                                       */
+  int residual;     /* MLP only: add the raw key/query r (needs d_k == d_v)   */
+  int feature_map;  /* ORC_PHI_*                                              */
+  int poly_dims;    /* p: leading dims fed to the degree-2 map                */
+  int window;       /* c >= 1                                                 */
+  int chunk;        /* b >= 1                                                 */
+  int momentum;     /* 0: eta treated as 0 and S not carried                  */
+  int bias;         /* ORC_BIAS_L2: gamma/2*s*|f-v|^2 ; ORC_BIAS_DOT: -s*gamma*<f,v> */
+  double grad_scale;/* s                                                      */
+} oracle_config;
+
+/* Sets the OpenMP thread count used by oracle_forward (n <= 0: default). */
+void oracle_set_threads(int n);
+
+/* Width D of phi(x). */
+int oracle_feature_dim(const oracle_config* cfg);
+/* Number of memory weights P (linear: d_v*D; MLP: hidden*D + d_v*hidden). */
+long oracle_param_count(const oracle_config* cfg);
+
+/* phi(x): x has d_k entries, out receives D entries. */
+void oracle_phi(const oracle_config* cfg, const double* x, double* out);
+
+/* Memory read f_theta(x, r) for one token; theta laid out as in
+ * oracle_forward.  x = phi(key or query) (D), r = raw key or query (d_k). */
+void oracle_memory_apply(const oracle_config* cfg, const double* theta,
+                         const double* x, const double* r, double* y);
+
+/* Gradient of ONE token's weighted inner loss at theta, written into grad
+ * (P entries, same layout as theta):
+ *   L2 : gamma * s/2 * |f_theta(x, r) - v|^2
+ *   DOT: -gamma * s * <f_theta(x, r), v>                                   */
+void oracle_token_grad(const oracle_config* cfg, const double* theta,
+                       const double* x, const double* r, const double* v,
+                       double gamma, double* grad);
+
+/* Run the memory over one call's tokens for every sequence.
+ *   q, k   [n_seq][seq_len][d_k]     v [n_seq][seq_len][d_v]
+ *   alpha, eta, theta, gamma         [n_seq][seq_len]
+ *   mem    [n_seq][P]  in: M_0 / theta_0, out: final weights
+ *          linear: M [d_v][D];  MLP: W1 [hidden][D] then W2 [d_v][hidden]
+ *   mom    [n_seq][P]  in/out momentum S (ignored when momentum == 0)
+ *   halo_k [n_seq][c-1][d_k], halo_v [n_seq][c-1][d_v], halo_g [n_seq][c-1]
+ *          in/out: the last c-1 tokens seen before this call, oldest first
+ *   count  [n_seq]     in/out: tokens seen before this call
+ *   out    [n_seq][seq_len][d_v]
+ * Chunks start at the call's first token.  Returns the number of OpenMP
+ * threads used, or a negative value on a bad configuration.               */
+int oracle_forward(const oracle_config* cfg,
+                   const double* q, const double* k, const double* v,
+                   const double* alpha, const double* eta,
+                   const double* theta, const double* gamma,
+                   double* mem, double* mom,
+                   double* halo_k, double* halo_v, double* halo_g,
+                   int64_t* count, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,46 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a private copy of the oracle's C source
+(built into a temporary directory, on the CPU), runs the pin suite against
+that copy in a child process, and requires at least one pin to fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MUTANTS = {
+    "eta_theta_swapped": ("Sx[p] = eta_n * Sx[p] - th[n] * g[p];", "Sx[p] = th[n] * Sx[p] - eta_n * g[p];"),
+    "keep_factor_for_forget": ("W[p] = (1.0 - al[n]) * W[p] + Sx[p];", "W[p] = al[n] * W[p] + Sx[p];"),
+    "window_off_by_one": ("int i0 = n - c + 1;", "int i0 = n - c;"),
+    "error_sign": ("s * gamma * (f[o] - v[o])", "s * gamma * (v[o] - f[o])"),
+    "gelu_prime_dropped": ("d1[j] = back * gelu_prime(z[j]);", "d1[j] = back * gelu(z[j]);"),
+    "w2_transposed_in_backward": ("back += W2[(long)o * h + j] * d2[o];", "back += W2[(long)j * cfg->d_v + o] * d2[o];"),
+    "poly2_diagonal_dropped": ("for (int b = a; b < p; ++b)", "for (int b = a + 1; b < p; ++b)"),
+    "residual_dropped": ("double s = cfg->residual ? r[o] : 0.0;", "double s = 0.0;"),
+    "halo_ignored": ("if (lo < -halo_valid) lo = -halo_valid;", "if (lo < 0) lo = 0;"),
+    "dot_bias_sign": ("-s * gamma * v[o]", "s * gamma * v[o]"),
+    "tanh_gelu": ("return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));", "return 0.5 * z * (1.0 + tanh(z));"),
+    "stale_chunk_start_state": ("memcpy(Wc, W, sizeof(double) * P);", "if (t0 == 0) memcpy(Wc, W, sizeof(double) * P);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(O.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found"
+    mut = tmp_path / "atlas_oracle.c"
+    mut.write_text(src.replace(old, new))
+    (tmp_path / "atlas_oracle.h").write_text(open(os.path.join(os.path.dirname(O.SRC), "atlas_oracle.h")).read())
+    lib = O.build(str(mut), str(tmp_path / "liboracle_mut.so"))
+    env = dict(os.environ, ATLAS_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(HERE, "test_oracle_pins.py")],
+                       env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
