@@ -1,0 +1,190 @@
+"""Throughput of the test-time memory update + retrieval on one MI355X.
+
+One step = one atlas_mem_forward over the whole batch: every (batch, head)
+sequence, all seq_len tokens, through the gate-coefficient kernel and the
+recurrent chunk kernel.  Inputs are seeded synthetic tensors already resident
+in HBM; each step continues the memory from the previous step's state (the
+state is a stream, so no reset is needed and the work per step is fixed).
+
+Prints one JSON line.  `roofline` refers to the recurrent chunk kernel (the
+dominant kernel); its duration is measured live with HIP events recorded by
+the library around that kernel on the call's stream.  `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+
+
+def alg_flops_per_chunk(wl) -> float:
+    """FLOPs the method must do per chunk of one sequence (the chunked form;
+    per-token weights are never materialised): forward over the window,
+    backward, momentum+decay update, the state side of the retrieval and the
+    intra-chunk (token x token) terms."""
+    b, W, D, dv, h = wl.chunk, wl.chunk + wl.window - 1, wl.feature_dim, wl.d_v, wl.hidden
+    f = 2 if wl.momentum else 1
+    if wl.memory == "linear":
+        return 2 * W * D * dv + f * 2 * W * D * dv + f * 2 * b * D * dv + 2 * b * W * (D + dv)
+    P = h * D + dv * h
+    return (2 * W * (h * D + dv * h) + 2 * W * dv * h + f * 2 * W * P + f * 2 * b * P
+            + 2 * b * W * (D + 2 * h + dv))
+
+
+def alg_bytes_per_head_token(wl) -> int:
+    """q, k, v in, out back (io dtype), four fp32 gates."""
+    es = 4 if wl.io_dtype == "f32" else 2
+    return es * (2 * wl.d_k + 2 * wl.d_v) + 4 * 4
+
+
+def cpu_baseline(wl, inputs, w0, budget_s: float):
+    """The fp64 oracle on a bounded sample: one sequence per thread, the first
+    n tokens, n chunk-aligned and sized for about budget_s seconds."""
+    from oracle import oracle as O
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(16, os.cpu_count() or 1)
+    S = wl.batch * wl.heads
+    n_seq = min(S, threads)
+    P = wl.hidden * wl.feature_dim + wl.d_v * wl.hidden if wl.memory == "mlp" else wl.d_v * wl.feature_dim
+    cost = 2.0 * (wl.window + 8) * P            # flops per head-token, direct window sums
+    n = int(budget_s * 3.0e9 / cost) // wl.chunk * wl.chunk
+    n = max(wl.chunk, min(n, wl.seq_len))
+    seqs = [int(s) for s in range(0, S, max(1, S // n_seq))][:n_seq]
+    t = time.perf_counter()
+    _, _, used = O.run_workload(wl, inputs, w0, seqs=seqs, n_tokens=n, threads=threads)
+    dt = time.perf_counter() - t
+    head_tokens = len(seqs) * n
+    return {
+        "value": head_tokens / wl.heads / dt,
+        "unit": "tokens/s",
+        "cores": used,
+        "kind": "oracle",
+        "sample": f"{len(seqs)} of {S} (batch, head) sequences x first {n} tokens of {wl.name}, "
+                  f"fp64, {dt:.1f} s; value counts tokens as positions (head-tokens / {wl.heads})",
+        "head_tokens_per_s": head_tokens / dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="layer_scale")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the chunk kernel")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: every (batch, head) sequence is independent, "
+              "so a multi-GPU run is N copies of this one on a share of the sequences; "
+              "no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from test_memorization_sequence_amd import binding, synth
+    from test_memorization_sequence_amd.configs import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    print(f"[bench] {wl.name}: B={wl.batch} H={wl.heads} N={wl.seq_len} ({wl.note})", file=sys.stderr, flush=True)
+    inputs = synth.make_inputs(wl, 0)
+    w0 = synth.initial_weights_flat(wl, inputs)
+    dev = torch.device("cuda:0")
+    io = torch.float32 if wl.io_dtype == "f32" else torch.bfloat16
+    t_in = {k: torch.from_numpy(inputs[k]).to(dev, dtype=io) for k in ("q", "k", "v")}
+    g_in = {k: torch.from_numpy(inputs[k]).to(dev) for k in ("alpha", "eta", "theta", "gamma")}
+    mem = binding.AtlasMem(wl)
+    state = mem.new_state(torch.from_numpy(w0), device=dev)
+    out = torch.empty(wl.batch, wl.heads, wl.seq_len, wl.d_v, dtype=io, device=dev)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    ev1.record(stream)
+    mem.set_kernel_events(ev0, ev1)
+
+    def step():
+        mem.forward(t_in["q"], t_in["k"], t_in["v"], g_in["alpha"], g_in["eta"] if wl.momentum else None,
+                    g_in["theta"], g_in["gamma"], state, out, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    kernel_ms = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+        ev1.synchronize()
+        kernel_ms.append(ev0.elapsed_time(ev1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mem.set_kernel_events(None, None)
+    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    if not torch.isfinite(out.float()).all():
+        print("[bench] warning: non-finite outputs", file=sys.stderr)
+
+    S = wl.batch * wl.heads
+    nch = -(-wl.seq_len // wl.chunk)
+    flops = alg_flops_per_chunk(wl) * nch * S
+    k_ms = float(np.mean(kernel_ms))
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    peak = PEAK_FP32_TFLOPS if wl.io_dtype == "f32" else PEAK_BF16_TFLOPS
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get(wl.name)
+    tokens = wl.batch * wl.seq_len
+    res = {
+        "metric": "memory update+retrieve tokens/sec (1 GPU); MFMA util % of bf16 peak",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.io_dtype == "f32" else "bf16",
+        "data": "synthetic (seeded numpy: L2-normalised q,k; N(0,1) v; sigmoid gates)",
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seq_len,
+                   "d_k": wl.d_k, "d_v": wl.d_v, "memory": wl.memory, "hidden": wl.hidden,
+                   "feature_dim": wl.feature_dim, "window": wl.window, "chunk": wl.chunk,
+                   "momentum": wl.momentum},
+        "head_tokens_per_s": S * wl.seq_len / (ms_per_step * 1e-3),
+        "mfma_util_pct": 100.0 * (flops / (ms_per_step * 1e-3) / 1e12) / peak,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "chunk_kernel",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": traffic,
+            "alg_flops_per_launch": flops,
+            "kernel_ms": k_ms,
+        },
+        "hbm_alg_gbs": alg_bytes_per_head_token(wl) * S * wl.seq_len / (ms_per_step * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample) ...", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, inputs, w0, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * atlas_mem.h -- C ABI of the MI355X test-time memory (ATLAS / Titans
+ * long-term memory): chunked Omega-rule update with Titans momentum and
+ * decay, and retrieval from the updated memory.
+ *
+ * The operation (for every sequence s = (batch, head), tokens t in order):
+ *
+ *   x_t   = phi(k_t)      feature map: identity, [k, upper-tri(k k^T)], or
+ *                         [k, poly2(k[:p])]            (ATLAS review, sec. 3.1
+ *                         "Polynomial Feature Mapping"; raw monomials, each
+ *                         unordered pair once, diagonal included)
+ *   f(x)  = M x           (linear memory)   or   r + W2 gelu(W1 x)  (2-layer
+ *                         MLP memory, exact erf GELU, no biases, r the raw
+ *                         key/query; Titans review sec. 3.1 "Memory
+ *                         Architecture", ATLAS review sec. 2)
+ *   loss  = sum over the last c tokens i of gamma_i * s/2 * |f(x_i) - v_i|^2
+ *                         (Omega rule, ATLAS review sec. 3.2), or the
+ *                         dot-product bias -gamma_i * s * <f(x_i), v_i>
+ *   chunks of b tokens:   every gradient of a chunk is taken at the weights
+ *                         the previous chunk left (ATLAS review sec. 3.3
+ *                         "Parallelizing Omega Rule")
+ *   S_t   = eta_t S_{t-1} - theta_t grad_t   (Titans review sec. 3.1,
+ *                         momentum / "past surprise")
+ *   M_t   = (1 - alpha_t) M_{t-1} + S_t      (Titans review sec. 3.1,
+ *                         "Forgetting Mechanism")
+ *   y_t   = f_{M_t}(phi(q_t))                 (Titans review sec. 3.1
+ *                         "Retrieving a Memory": a forward pass, no update)
+ *
+ * where grad_t = sum_{i = t-c+1}^{t} grad of token i's term.  The window
+ * stops at the first token the sequence has seen.
+ *
+ * Every function returns an atlas_status (0 = success).  Nothing is thrown
+ * across the ABI and nothing aborts.  All device pointers are plain HIP
+ * device addresses owned by the caller; the library owns only its handle and
+ * the workspace it allocates in atlas_mem_init.
+ */
+#ifndef ATLAS_MEM_H
+#define ATLAS_MEM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATLAS_OK = 0,
+  ATLAS_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, aliasing   */
+  ATLAS_ERR_UNSUPPORTED = 2,      /* valid config with no kernel built for it      */
+  ATLAS_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed                   */
+  ATLAS_ERR_HIP = 4               /* a HIP call failed; see atlas_mem_last_hip_error */
+} atlas_status;
+
+enum { ATLAS_MEM_LINEAR = 0, ATLAS_MEM_MLP = 1 };
+enum { ATLAS_PHI_IDENTITY = 0, ATLAS_PHI_POLY2 = 1, ATLAS_PHI_RAW_POLY2 = 2 };
+enum { ATLAS_BIAS_L2 = 0, ATLAS_BIAS_DOT = 1 };
+enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
+
+typedef struct {
+  int batch, heads;   /* B, H: B*H independent sequences                        */
+  int seq_len;        /* N: tokens per sequence in every forward call (>= 0)    */
+  int d_k, d_v;       /* raw key/query width, value width                       */
+  int memory;         /* ATLAS_MEM_LINEAR | ATLAS_MEM_MLP                       */
+  int mlp_layers;     /* MLP depth L_M; 2 is the only depth built               */
+  int mlp_hidden;     /* MLP hidden width h                                     */
+  int mlp_residual;   /* 1: f(x) = r + W2 gelu(W1 x); needs d_k == d_v          */
+  int feature_map;    /* ATLAS_PHI_*                                            */
+  int poly_dims;      /* p for ATLAS_PHI_RAW_POLY2 (leading key dims)           */
+  int window;         /* c >= 1, c <= chunk                                     */
+  int chunk;          /* b                                                      */
+  int momentum;       /* 0: eta is ignored (treated as 0) and S is not stored   */
+  int bias;           /* ATLAS_BIAS_L2 | ATLAS_BIAS_DOT                         */
+  int io_dtype;       /* ATLAS_BF16 | ATLAS_F32 for q, k, v, out                */
+  float grad_scale;   /* s: 1 matches the printed update rules; 2 is the
+                         literal derivative of the squared norm                 */
+} atlas_mem_config;
+
+typedef struct atlas_mem_s* atlas_mem_t;
+
+/* Byte offsets inside ONE sequence's state block, and the block stride.
+ * The state buffer is [batch*heads] blocks of seq_stride bytes, sequence
+ * index s = b*heads + h, 256-byte aligned.  Inside a block:
+ *   weights  fp32  linear: M [d_v][D];  MLP: W1 [h][D] then W2 [d_v][h] (row-major)
+ *   momentum fp32  same shape as weights (only if momentum)
+ *   halo_k   fp32  [c-1][d_k]  raw keys of the last c-1 tokens seen, oldest first
+ *   halo_v   fp32  [c-1][d_v]
+ *   halo_g   fp32  [c-1]       their gamma
+ *   count    int64             tokens seen so far
+ * The caller writes the initial weights, zeroes everything else, and reads
+ * the final weights/momentum back.  D is the width of phi(k).              */
+typedef struct {
+  size_t seq_stride;
+  size_t weights, momentum, halo_k, halo_v, halo_g, count;
+  int feature_dim;    /* D */
+  long param_count;   /* P: number of weights (floats) */
+} atlas_mem_state_layout;
+
+/* Validates cfg, selects the kernels and allocates the device workspace on
+ * the current HIP device.  No kernel is launched.  On success *out holds a
+ * handle that must be released with atlas_mem_free.
+ * Errors: INVALID_ARGUMENT (bad or inconsistent sizes, null out),
+ * UNSUPPORTED (no kernel for this shape: see atlas_mem_supported),
+ * OUT_OF_MEMORY, HIP.                                                      */
+atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out);
+
+/* Same validation as atlas_mem_init without allocating anything:
+ * ATLAS_OK if a kernel exists for cfg.                                     */
+atlas_status atlas_mem_supported(const atlas_mem_config* cfg);
+
+/* Size in bytes of the state buffer (all sequences) and its layout.        */
+size_t atlas_mem_state_bytes(atlas_mem_t h);
+atlas_status atlas_mem_state_layout_of(atlas_mem_t h, atlas_mem_state_layout* out);
+
+/* Runs one call over seq_len tokens of every sequence, enqueued on `stream`
+ * (no host synchronisation, no allocation).  Chunks start at the call's
+ * first token, so a call split in two equals one call when the first part's
+ * length is a multiple of the chunk.
+ *   q, k   [B][H][N][d_k]   io_dtype, contiguous
+ *   v      [B][H][N][d_v]   io_dtype
+ *   alpha, eta, theta, gamma  [B][H][N] fp32 (eta may be NULL if !momentum)
+ *   state  in/out, layout above (device)
+ *   out    [B][H][N][d_v]   io_dtype, must not overlap any input or state
+ * All pointers are device pointers, 16-byte aligned (gates: 4-byte); with
+ * seq_len == 0 the call does nothing and accepts any pointer.  One handle serves one
+ * stream at a time (the workspace is shared by its calls).
+ * Errors: INVALID_ARGUMENT (null/misaligned/overlapping pointers, bad
+ * handle), HIP (launch failure).  NaN/Inf in the inputs propagate.         */
+atlas_status atlas_mem_forward(atlas_mem_t h,
+                               const void* q, const void* k, const void* v,
+                               const float* alpha, const float* eta,
+                               const float* theta, const float* gamma,
+                               void* state, void* out, void* stream /* hipStream_t */);
+
+/* Optional timing hook for profilers and benchmarks: while set, every
+ * atlas_mem_forward records `before` on its stream right before the
+ * recurrent chunk kernel and `after` right after it.  Both are hipEvent_t
+ * created by the caller, who keeps ownership; NULL, NULL clears the hook.
+ * Errors: INVALID_ARGUMENT (bad handle, exactly one event NULL).           */
+atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* after);
+
+/* Releases the workspace and the handle (NULL is accepted).                */
+atlas_status atlas_mem_free(atlas_mem_t h);
+
+/* Static description of a status code.                                     */
+const char* atlas_mem_error_string(int code);
+
+/* Text of the last HIP error seen by this thread, "" if none.              */
+const char* atlas_mem_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATLAS_MEM_H */

@@ -160,3 +160,36 @@ def forward(cfg: OracleConfig, q, k, v, alpha, eta, theta, gamma, state: dict,
     if used < 0:
         raise ValueError("oracle rejected the configuration")
     return out, used
+
+
+def config_for(wl) -> OracleConfig:
+    """Oracle configuration for a workload description (any object with the
+    workload fields: d_k, d_v, memory, hidden, residual, feature_map,
+    poly_dims, window, chunk, momentum, bias, grad_scale)."""
+    return make_config(d_k=wl.d_k, d_v=wl.d_v, memory=wl.memory, hidden=wl.hidden,
+                       residual=wl.residual, feature_map=wl.feature_map, poly_dims=wl.poly_dims,
+                       window=wl.window, chunk=wl.chunk, momentum=wl.momentum, bias=wl.bias,
+                       grad_scale=wl.grad_scale)
+
+
+def run_workload(wl, inputs: dict, weights0, seqs=None, n_tokens=None, state=None, threads=None):
+    """Runs the oracle on generator inputs ([B,H,N,...] float32 arrays).
+    weights0: [B*H, P] initial weights.  seqs: flat sequence indices to run
+    (default all); n_tokens: prefix length (default all).  Returns
+    (out [S, n, d_v] float64, state dict)."""
+    S_all = wl.batch * wl.heads
+    seqs = list(range(S_all)) if seqs is None else list(seqs)
+    n = wl.seq_len if n_tokens is None else n_tokens
+
+    def take(a):
+        a = a.reshape(S_all, a.shape[2], *a.shape[3:])
+        return np.ascontiguousarray(a[seqs, :n], dtype=np.float64)
+
+    cfg = config_for(wl)
+    cfg.n_seq = len(seqs)
+    if state is None:
+        state = empty_state(cfg)
+        state["mem"][:] = np.asarray(weights0, dtype=np.float64)[seqs]
+    out, used = forward(cfg, *(take(inputs[key]) for key in ("q", "k", "v", "alpha", "eta", "theta", "gamma")),
+                        state, threads=threads)
+    return out, state, used

@@ -70,7 +70,7 @@ WORKLOADS = {
     # matrix memory on phi(k) = [k, upper-tri(k k^T)] (32 -> 560), c = 16, momentum
     "linear_poly2": Workload(
         "linear_poly2", 2, 8, 4096, 32, 32, "linear", 0, False, "poly2", 32,
-        window=16, chunk=64, momentum=True, io_dtype="bf16",
+        window=16, chunk=64, momentum=True, io_dtype="bf16", theta_div=16.0,
         note="linear 560x32 poly2, c=16, momentum, bf16"),
     # 2-layer residual MLP 64-256-64, c = 1, momentum + decay
     "mlp64": Workload(
@@ -80,14 +80,31 @@ WORKLOADS = {
     # ATLAS-style: [k, poly2(k[:32])] (688) -> 512 -> 128 residual MLP, c = 64, N = 32768
     "atlas_long": Workload(
         "atlas_long", 1, 8, 32768, 128, 128, "mlp", 512, True, "raw_poly2", 32,
-        window=64, chunk=64, momentum=True, io_dtype="bf16", init_std=0.02,
+        window=64, chunk=64, momentum=True, io_dtype="bf16", init_std=0.02, theta_div=64.0,
         note="MLP 688-512-128 residual, raw+poly2 map, c=64, N=32768, bf16"),
     # layer scale: d_model 1536 = 12 heads x 128, MLP 128-512-128, c = 32, B = 8, N = 16384
     "layer_scale": Workload(
         "layer_scale", 8, 12, 16384, 128, 128, "mlp", 512, True, "identity", 0,
-        window=32, chunk=64, momentum=True, io_dtype="bf16", init_std=0.02,
+        window=32, chunk=64, momentum=True, io_dtype="bf16", init_std=0.02, theta_div=32.0,
         note="MLP 128-512-128 residual, c=32, 8x12 heads, N=16384, bf16"),
 }
+
+# Gate recipes under which the memory changes a lot over a few hundred tokens
+# and stays finite (small decay).  Used by the parity tests next to each
+# preset's own recipe, because several presets decay to the W = 0 fixed point
+# of the MLP memory within a few chunks.
+LIVELY = {
+    "linear64_delta": dict(alpha_u=(-8.0, -4.0)),
+    "linear_poly2": dict(alpha_u=(-8.0, -4.0), theta_div=16.0),
+    "mlp64": dict(alpha_u=(-8.0, -4.0), theta_u=(-6.0, -2.0)),
+    "atlas_long": dict(alpha_u=(-8.0, -4.0), theta_div=128.0),
+    "layer_scale": dict(alpha_u=(-8.0, -4.0), theta_div=64.0),
+}
+
+
+def lively(wl: Workload) -> Workload:
+    return replace(wl, **LIVELY[wl.name])
+
 
 # the order the five workloads are listed in
 ORDER = ["linear64_delta", "linear_poly2", "mlp64", "atlas_long", "layer_scale"]

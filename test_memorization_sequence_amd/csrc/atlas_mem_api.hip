@@ -1,0 +1,275 @@
+// atlas_mem_api.hip -- host side of the C ABI declared in include/atlas_mem.h:
+// configuration checks, kernel selection, workspace, state layout, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "atlas_mem.h"
+#include "atlas_mem_internal.h"
+
+namespace atlas {
+
+typedef hipError_t (*LaunchFn)(const ChunkParams&, const CoeffParams&, int, hipStream_t, hipEvent_t, hipEvent_t);
+
+struct Variant {
+  const char* name;
+  int io, mem, phi, dk, dv, h, bc, wp, pd;
+  size_t ws_bytes;
+  LaunchFn launch;
+};
+
+template <typename T> constexpr int io_code() { return sizeof(T) == 4 ? ATLAS_F32 : ATLAS_BF16; }
+
+#define ATLAS_VARIANT(NAME, T, TI, MEM, PHI, DK, DV, H, BC, WP, PD)                          \
+  {#NAME, io_code<TI>(), MEM, PHI, DK, DV, H, BC, WP, PD,                                     \
+   Shape<T, TI, MEM, PHI, DK, DV, H, BC, WP, PD>::WS::bytes,                                  \
+   &launch<Shape<T, TI, MEM, PHI, DK, DV, H, BC, WP, PD>>},
+static const Variant kVariants[] = {
+#include "atlas_mem_variants.inc"
+};
+#undef ATLAS_VARIANT
+
+}  // namespace atlas
+
+using namespace atlas;
+
+struct atlas_mem_s {
+  uint32_t magic;
+  atlas_mem_config cfg;
+  const Variant* var;
+  atlas_mem_state_layout lay;
+  int n_seq, nchunks, coef_stride, device;
+  char* ws;
+  float* coef;
+  hipEvent_t ev_before, ev_after;
+};
+
+static const uint32_t kMagic = 0xA7A5AE11u;
+static thread_local char g_hip_error[256] = "";
+
+static atlas_status hip_fail(hipError_t e) {
+  std::snprintf(g_hip_error, sizeof(g_hip_error), "%s", hipGetErrorString(e));
+  return ATLAS_ERR_HIP;
+}
+
+static int pd_of(const atlas_mem_config* c) {
+  return c->feature_map == ATLAS_PHI_POLY2 ? c->d_k : c->feature_map == ATLAS_PHI_RAW_POLY2 ? c->poly_dims : 0;
+}
+
+static atlas_status check_config(const atlas_mem_config* c, const Variant** out) {
+  if (!c) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->batch < 1 || c->heads < 1 || c->seq_len < 0 || c->d_k < 1 || c->d_v < 1) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->window < 1 || c->chunk < 1) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->memory != ATLAS_MEM_LINEAR && c->memory != ATLAS_MEM_MLP) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->feature_map < ATLAS_PHI_IDENTITY || c->feature_map > ATLAS_PHI_RAW_POLY2) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->io_dtype != ATLAS_BF16 && c->io_dtype != ATLAS_F32) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(c->grad_scale)) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->feature_map == ATLAS_PHI_RAW_POLY2 && (c->poly_dims < 1 || c->poly_dims > c->d_k)) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->memory == ATLAS_MEM_MLP) {
+    if (c->mlp_hidden < 1) return ATLAS_ERR_INVALID_ARGUMENT;
+    if (c->mlp_residual && c->d_k != c->d_v) return ATLAS_ERR_INVALID_ARGUMENT;
+    if (c->mlp_layers != 2) return ATLAS_ERR_UNSUPPORTED;
+  }
+  if (c->window > c->chunk) return ATLAS_ERR_UNSUPPORTED;
+  // sequences x chunks must fit one grid dimension of the coefficient kernel
+  const long n_seq = (long)c->batch * c->heads;
+  if (n_seq > (1L << 20) || n_seq * ((c->seq_len + c->chunk - 1) / c->chunk) > 0x7fffffffL) return ATLAS_ERR_INVALID_ARGUMENT;
+  const int h = c->memory == ATLAS_MEM_MLP ? c->mlp_hidden : 0;
+  const int need_w = c->chunk + c->window - 1;
+  const Variant* best = nullptr;
+  for (const Variant& v : kVariants) {
+    if (v.io != c->io_dtype || v.mem != c->memory || v.phi != c->feature_map || v.dk != c->d_k ||
+        v.dv != c->d_v || v.h != h || v.bc != c->chunk || v.pd != pd_of(c))
+      continue;
+    if (v.wp < need_w) continue;
+    if (!best || v.wp < best->wp) best = &v;
+  }
+  if (!best) return ATLAS_ERR_UNSUPPORTED;
+  if (out) *out = best;
+  return ATLAS_OK;
+}
+
+static atlas_mem_state_layout make_layout(const atlas_mem_config* c) {
+  atlas_mem_state_layout L;
+  const int pd = pd_of(c);
+  L.feature_dim = feature_dim(c->feature_map, c->d_k, pd);
+  const long D = L.feature_dim;
+  L.param_count = c->memory == ATLAS_MEM_MLP ? (long)c->mlp_hidden * D + (long)c->d_v * c->mlp_hidden : (long)c->d_v * D;
+  const size_t P = (size_t)L.param_count, halo = (size_t)(c->window - 1);
+  L.weights = 0;
+  L.momentum = align_up(L.weights + P * 4, 16);
+  L.halo_k = align_up(L.momentum + (c->momentum ? P * 4 : 0), 16);
+  L.halo_v = align_up(L.halo_k + halo * c->d_k * 4, 16);
+  L.halo_g = align_up(L.halo_v + halo * c->d_v * 4, 16);
+  L.count = align_up(L.halo_g + halo * 4, 16);
+  L.seq_stride = align_up(L.count + 8, 256);
+  return L;
+}
+
+extern "C" {
+
+atlas_status atlas_mem_supported(const atlas_mem_config* cfg) { return check_config(cfg, nullptr); }
+
+atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
+  if (!out) return ATLAS_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const Variant* var = nullptr;
+  atlas_status s = check_config(cfg, &var);
+  if (s != ATLAS_OK) return s;
+  atlas_mem_s* h = new (std::nothrow) atlas_mem_s();
+  if (!h) return ATLAS_ERR_OUT_OF_MEMORY;
+  h->magic = kMagic;
+  h->cfg = *cfg;
+  h->var = var;
+  h->lay = make_layout(cfg);
+  h->n_seq = cfg->batch * cfg->heads;
+  h->nchunks = (cfg->seq_len + cfg->chunk - 1) / cfg->chunk;
+  h->coef_stride = coef_stride(var->bc, var->wp);
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) { delete h; return hip_fail(e); }
+  h->ws = nullptr;
+  h->coef = nullptr;
+  h->ev_before = h->ev_after = nullptr;
+  const size_t ws_bytes = var->ws_bytes * (size_t)h->n_seq;
+  const size_t coef_bytes = (size_t)h->n_seq * h->nchunks * h->coef_stride * sizeof(float);
+  if (ws_bytes && hipMalloc(&h->ws, ws_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return ATLAS_ERR_OUT_OF_MEMORY;
+  }
+  if (coef_bytes && hipMalloc(&h->coef, coef_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(h->ws);
+    delete h;
+    return ATLAS_ERR_OUT_OF_MEMORY;
+  }
+  *out = h;
+  return ATLAS_OK;
+}
+
+size_t atlas_mem_state_bytes(atlas_mem_t h) {
+  if (!h || h->magic != kMagic) return 0;
+  return h->lay.seq_stride * (size_t)h->n_seq;
+}
+
+atlas_status atlas_mem_state_layout_of(atlas_mem_t h, atlas_mem_state_layout* out) {
+  if (!h || h->magic != kMagic || !out) return ATLAS_ERR_INVALID_ARGUMENT;
+  *out = h->lay;
+  return ATLAS_OK;
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, const void* v,
+                               const float* alpha, const float* eta, const float* theta,
+                               const float* gamma, void* state, void* out, void* stream) {
+  if (!h || h->magic != kMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+  const atlas_mem_config& c = h->cfg;
+  if (c.seq_len == 0) return ATLAS_OK;  // nothing to read or write; any pointer accepted
+  if (!q || !k || !v || !alpha || !theta || !gamma || !state || !out) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c.momentum && !eta) return ATLAS_ERR_INVALID_ARGUMENT;
+  const void* p16[] = {q, k, v, state, out};
+  for (const void* p : p16)
+    if ((uintptr_t)p % 16) return ATLAS_ERR_INVALID_ARGUMENT;
+  const void* p4[] = {alpha, eta, theta, gamma};
+  for (const void* p : p4)
+    if ((uintptr_t)p % 4) return ATLAS_ERR_INVALID_ARGUMENT;
+  const size_t es = c.io_dtype == ATLAS_F32 ? 4 : 2, S = (size_t)h->n_seq, N = (size_t)c.seq_len;
+  const size_t out_b = S * N * c.d_v * es;
+  const size_t st_b = atlas_mem_state_bytes(h);
+  if (overlaps(out, out_b, q, S * N * c.d_k * es) || overlaps(out, out_b, k, S * N * c.d_k * es) ||
+      overlaps(out, out_b, v, S * N * c.d_v * es) || overlaps(out, out_b, state, st_b) ||
+      overlaps(out, out_b, alpha, S * N * 4) || overlaps(out, out_b, theta, S * N * 4) ||
+      overlaps(out, out_b, gamma, S * N * 4) || (eta && overlaps(out, out_b, eta, S * N * 4)) ||
+      overlaps(state, st_b, q, S * N * c.d_k * es) || overlaps(state, st_b, k, S * N * c.d_k * es) ||
+      overlaps(state, st_b, v, S * N * c.d_v * es))
+    return ATLAS_ERR_INVALID_ARGUMENT;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev != h->device) return ATLAS_ERR_INVALID_ARGUMENT;
+
+  CoeffParams kp;
+  kp.alpha = alpha;
+  kp.eta = eta;
+  kp.theta = theta;
+  kp.state = (const char*)state;
+  kp.coef = h->coef;
+  kp.N = c.seq_len;
+  kp.c = c.window;
+  kp.nchunks = h->nchunks;
+  kp.coef_stride = h->coef_stride;
+  kp.momentum = c.momentum;
+  kp.seq_stride = h->lay.seq_stride;
+  kp.off_count = h->lay.count;
+
+  ChunkParams cp;
+  cp.q = q;
+  cp.k = k;
+  cp.v = v;
+  cp.gamma = gamma;
+  cp.state = (char*)state;
+  cp.out = out;
+  cp.ws = h->ws;
+  cp.coef = h->coef;
+  cp.N = c.seq_len;
+  cp.c = c.window;
+  cp.nchunks = h->nchunks;
+  cp.coef_stride = h->coef_stride;
+  cp.seq_stride = h->lay.seq_stride;
+  cp.off_weights = h->lay.weights;
+  cp.off_momentum = h->lay.momentum;
+  cp.off_halo_k = h->lay.halo_k;
+  cp.off_halo_v = h->lay.halo_v;
+  cp.off_halo_g = h->lay.halo_g;
+  cp.off_count = h->lay.count;
+  cp.grad_scale = c.grad_scale;
+  cp.momentum = c.momentum;
+  cp.bias = c.bias;
+  cp.residual = c.memory == ATLAS_MEM_MLP ? c.mlp_residual : 0;
+  e = h->var->launch(cp, kp, h->n_seq, (hipStream_t)stream, h->ev_before, h->ev_after);
+  if (e != hipSuccess) return hip_fail(e);
+  return ATLAS_OK;
+}
+
+atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* after) {
+  if (!h || h->magic != kMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+  if ((before == nullptr) != (after == nullptr)) return ATLAS_ERR_INVALID_ARGUMENT;
+  h->ev_before = (hipEvent_t)before;
+  h->ev_after = (hipEvent_t)after;
+  return ATLAS_OK;
+}
+
+atlas_status atlas_mem_free(atlas_mem_t h) {
+  if (!h) return ATLAS_OK;
+  if (h->magic != kMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+  h->magic = 0;
+  hipError_t e1 = h->ws ? hipFree(h->ws) : hipSuccess;
+  hipError_t e2 = h->coef ? hipFree(h->coef) : hipSuccess;
+  delete h;
+  if (e1 != hipSuccess) return hip_fail(e1);
+  if (e2 != hipSuccess) return hip_fail(e2);
+  return ATLAS_OK;
+}
+
+const char* atlas_mem_error_string(int code) {
+  switch (code) {
+    case ATLAS_OK: return "success";
+    case ATLAS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ATLAS_ERR_UNSUPPORTED: return "no kernel built for this configuration";
+    case ATLAS_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case ATLAS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* atlas_mem_last_hip_error(void) { return g_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// atlas_mem_internal.h -- shapes, workspace layout and launch parameters
+// shared by the kernels and the C ABI implementation of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace atlas {
+
+typedef __bf16 bf16;
+
+enum { MEM_LINEAR = 0, MEM_MLP = 1 };
+enum { PHI_IDENTITY = 0, PHI_POLY2 = 1, PHI_RAW_POLY2 = 2 };
+enum { BIAS_L2 = 0, BIAS_DOT = 1 };
+
+constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int feature_dim(int phi, int dk, int pd) {
+  return phi == PHI_IDENTITY ? dk
+       : phi == PHI_POLY2    ? dk + dk * (dk + 1) / 2
+                             : dk + pd + pd * (pd + 1) / 2;
+}
+
+// Per-sequence workspace of the chunk kernel (operand images of the state and
+// the per-chunk intermediates), byte offsets.
+template <class S>
+struct WsLayout {
+  typedef typename S::T T;
+  static constexpr bool MLP = S::MEM == MEM_MLP;
+  static constexpr size_t e = sizeof(T);
+  static constexpr size_t WP = S::WP, DP = S::DP, BC = S::BC, DV = S::DV, H = S::H;
+  static constexpr size_t Xw = 0;
+  static constexpr size_t XwT = align_up(Xw + WP * DP * e, 256);
+  static constexpr size_t Xq = align_up(XwT + DP * WP * e, 256);
+  static constexpr size_t Q1 = align_up(Xq + BC * DP * e, 256);
+  static constexpr size_t Q2 = align_up(Q1 + BC * WP * e, 256);
+  static constexpr size_t W1b = align_up(Q2 + BC * WP * e, 256);
+  static constexpr size_t S1b = align_up(W1b + (MLP ? H * DP : 0) * e, 256);
+  static constexpr size_t W2b = align_up(S1b + (MLP ? H * DP : 0) * e, 256);
+  static constexpr size_t S2b = align_up(W2b + (MLP ? DV * H : DV * DP) * e, 256);
+  static constexpr size_t W2T = align_up(S2b + (MLP ? DV * H : DV * DP) * e, 256);
+  static constexpr size_t Zf = align_up(W2T + (MLP ? H * DV : 0) * e, 256);
+  static constexpr size_t Ab = align_up(Zf + (MLP ? WP * H * 4 : 0), 256);
+  static constexpr size_t AT = align_up(Ab + (MLP ? WP * H : 0) * e, 256);
+  static constexpr size_t D2 = align_up(AT + (MLP ? H * WP : 0) * e, 256);
+  static constexpr size_t D2T = align_up(D2 + WP * DV * e, 256);
+  static constexpr size_t D2TM = align_up(D2T + DV * WP * e, 256);
+  static constexpr size_t D2TS = align_up(D2TM + DV * WP * e, 256);
+  static constexpr size_t D1T = align_up(D2TS + DV * WP * e, 256);
+  static constexpr size_t D1TM = align_up(D1T + (MLP ? H * WP : 0) * e, 256);
+  static constexpr size_t D1TS = align_up(D1TM + (MLP ? H * WP : 0) * e, 256);
+  static constexpr size_t Ah = align_up(D1TS + (MLP ? H * WP : 0) * e, 256);
+  static constexpr size_t bytes = align_up(Ah + (MLP ? BC * H : 0) * e, 256);
+};
+
+// T: MFMA operand type (bf16 or float); TI: io type of q, k, v, out.
+// H = 0 for a linear memory.  WP: window rows (chunk + c - 1) padded to 32.
+// PD: degree-2 map width (== DK for PHI_POLY2).
+template <typename T_, typename TI_, int MEM_, int PHI_, int DK_, int DV_, int H_, int BC_, int WP_, int PD_>
+struct Shape {
+  typedef T_ T;
+  typedef TI_ TI;
+  static constexpr int MEM = MEM_, PHI = PHI_, DK = DK_, DV = DV_, H = H_, BC = BC_, WP = WP_, PD = PD_;
+  static constexpr int D = feature_dim(PHI_, DK_, PD_);
+  static constexpr int DP = (D + 31) / 32 * 32;
+  typedef WsLayout<Shape> WS;
+  static_assert(WP % 32 == 0 && BC % 32 == 0 && DV % 32 == 0 && H % 32 == 0, "MFMA tile multiples");
+  static_assert(BC <= 64, "coefficient kernel handles chunks up to 64");
+};
+
+// Coefficient block of one chunk (floats):
+//   [0, BC)            A_t           [BC, 2BC)  B_t        [2BC] P (+3 pad)
+//   [2BC+4, +WP)       cM_i = C_{te,i}
+//   [2BC+4+WP, +WP)    cS_i
+//   [2BC+4+2WP, +BC*WP) C_{t,i} row-major
+constexpr int coef_stride(int bc, int wp) { return 2 * bc + 4 + 2 * wp + bc * wp; }
+
+struct CoeffParams {
+  const float* alpha;
+  const float* eta;
+  const float* theta;
+  const char* state;
+  float* coef;
+  int N, c, nchunks, coef_stride, momentum;
+  size_t seq_stride, off_count;
+};
+
+struct ChunkParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gamma;
+  char* state;
+  void* out;
+  char* ws;
+  const float* coef;
+  int N, c, nchunks, coef_stride;
+  size_t seq_stride, off_weights, off_momentum, off_halo_k, off_halo_v, off_halo_g, off_count;
+  float grad_scale;
+  int momentum, bias, residual;
+};
+
+// Enqueues the coefficient kernel, then the chunk kernel; ev0/ev1 (optional)
+// are recorded right before and right after the chunk kernel.
+template <class S>
+hipError_t launch(const ChunkParams& cp, const CoeffParams& kp, int n_seq, hipStream_t stream,
+                  hipEvent_t ev0, hipEvent_t ev1);
+
+}  // namespace atlas

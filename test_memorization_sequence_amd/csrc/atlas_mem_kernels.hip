@@ -1,0 +1,580 @@
+// atlas_mem_kernels.hip -- gfx950 kernels of the test-time memory.
+//
+// Two kernels per forward call:
+//
+//  coeff_kernel   one workgroup per (sequence, chunk), all chunks in parallel.
+//                 The gates alone fix how each token's gradient enters every
+//                 later weight of the chunk.  Unrolling the momentum/decay
+//                 recurrence (Titans review sec. 3.1, "Forgetting Mechanism")
+//                 over a chunk that starts at t0 with weights W0, momentum S0:
+//                   W_t = A_t W0 + B_t S0 - sum_i C_{t,i} G_i
+//                   S_te = P S0 - sum_i cS_i G_i
+//                 with G_i the gradient of window token i at W0 (ATLAS review
+//                 sec. 3.3: gradients at the previous chunk's final state) and
+//                   a_{m->t} = prod_{u=m+1..t} (1 - alpha_u),  e_{n->m} = prod_{u=n+1..m} eta_u
+//                   A_t = a_{t0-1->t},  B_t = sum_{m=t0..t} a_{m->t} e_{t0-1->m}
+//                   K_{t,n} = sum_{m=n..t} a_{m->t} e_{n->m}
+//                   C_{t,i} = sum_{n in [t0,t], i in window(n)} K_{t,n} theta_n
+//                   cS_i = sum_{n in chunk, i in window(n)} e_{n->te} theta_n,  P = e_{t0-1->te}
+//                 The window of n is [n-c+1, n] (Omega rule, ATLAS review
+//                 sec. 3.2); the band of C is the sliding-window mask.
+//
+//  chunk_kernel   one workgroup per sequence, persistent over the chunks
+//                 (the chunk chain is sequential).  Per chunk, as bf16 (or
+//                 fp32) MFMA GEMMs with fp32 accumulation:
+//                   MLP  Z = X W1^T, A = gelu(Z), E = R + A W2^T - V,
+//                        D2 = s*gamma*E, D1 = (D2 W2) .* gelu'(Z)
+//                        retrieval with the per-token weights W_t:
+//                          Zq = diag(A_t) Xq W1^T + diag(B_t) Xq S1^T - (C .* Xq X^T) D1
+//                          y  = Rq + diag(A_t) gelu(Zq) W2^T + diag(B_t) gelu(Zq) S2^T
+//                               - (C .* gelu(Zq) A^T) D2
+//                        (exact, because every gradient is a sum of outer
+//                        products; Titans review sec. 3.1 "Retrieving a Memory")
+//                        W1 <- A_te W1 + B_te S1 - (cM .* D1)^T X,  S1 <- P S1 - (cS .* D1)^T X
+//                        W2 <- A_te W2 + B_te S2 - (cM .* D2)^T A,  S2 <- P S2 - (cS .* D2)^T A
+//                   linear  the same with one layer and no gelu.
+//                 phi (ATLAS review sec. 3.1) is applied while staging.
+//
+// Every GEMM is "NT": C[m][n] = sum_k A[m][k] B[n][k], both operands stored
+// with k contiguous, so each lane's MFMA fragment is one 16-byte load.
+// Epilogues write each intermediate in the layouts its consumers need.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "atlas_mem_internal.h"
+
+namespace atlas {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_prime(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * expf(-0.5f * z * z) * 0.39894228040143268f;
+}
+
+// ----------------------------------------------------------------------------- MFMA
+template <typename T> struct Mma;
+template <> struct Mma<bf16> {
+  static constexpr int KSTEP = 32;
+  typedef bf16x8 frag;
+  // lane l: row (l & 15) of a 16-row block, k = k0 + 8*(l >> 4) .. +7
+  __device__ static frag load(const bf16* base, int ld, int row0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(base + (size_t)(row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+  }
+  __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  static constexpr int KSTEP = 4;
+  typedef float frag;
+  // lane l: row (l & 15), k = k0 + (l >> 4)
+  __device__ static frag load(const float* base, int ld, int row0, int k0, int lane) {
+    return base[(size_t)(row0 + (lane & 15)) * ld + k0 + (lane >> 4)];
+  }
+  __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename T> struct Op {
+  const T* A; int lda;  // [M][K], k contiguous
+  const T* B; int ldb;  // [N][K], k contiguous
+  int K;                // multiple of Mma<T>::KSTEP; A == nullptr disables the op
+};
+
+// C_o[m][n] = sum_k A_o[m][k] B_o[n][k] for each op o, over a 32x32 tile per
+// wave (2x2 MFMA blocks); epi(m, n, v[NOPS]) receives every element once.
+// M and N must be multiples of 32.
+template <typename T, int NOPS, typename Epi>
+__device__ __forceinline__ void gemm_nt(int M, int N, const Op<T> (&ops)[NOPS], Epi&& epi) {
+  typedef Mma<T> MM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int tn = N >> 5, ntiles = (M >> 5) * tn;
+  for (int t = wave; t < ntiles; t += nwaves) {
+    const int m0 = (t / tn) << 5, n0 = (t % tn) << 5;
+    f32x4 acc[NOPS][2][2];
+#pragma unroll
+    for (int o = 0; o < NOPS; ++o)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[o][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int o = 0; o < NOPS; ++o) {
+      const Op<T> op = ops[o];
+      if (op.A == nullptr) continue;
+      for (int k0 = 0; k0 < op.K; k0 += MM::KSTEP) {
+        typename MM::frag a0 = MM::load(op.A, op.lda, m0, k0, lane);
+        typename MM::frag a1 = MM::load(op.A, op.lda, m0 + 16, k0, lane);
+        typename MM::frag b0 = MM::load(op.B, op.ldb, n0, k0, lane);
+        typename MM::frag b1 = MM::load(op.B, op.ldb, n0 + 16, k0, lane);
+        acc[o][0][0] = MM::mma(a0, b0, acc[o][0][0]);
+        acc[o][0][1] = MM::mma(a0, b1, acc[o][0][1]);
+        acc[o][1][0] = MM::mma(a1, b0, acc[o][1][0]);
+        acc[o][1][1] = MM::mma(a1, b1, acc[o][1][1]);
+      }
+    }
+    // 16x16 MFMA output: lane l holds column (l & 15), rows 4*(l >> 4) + r
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v[NOPS];
+#pragma unroll
+          for (int o = 0; o < NOPS; ++o) v[o] = acc[o][i][j][r];
+          epi(m0 + 16 * i + 4 * (lane >> 4) + r, n0 + 16 * j + (lane & 15), v);
+        }
+  }
+}
+
+// ----------------------------------------------------------------------------- phi
+// Pair table for the degree-2 monomials x_a x_b, a <= b < p, row-major upper
+// triangle order (ATLAS review sec. 3.1, polynomial feature map).
+template <int P> struct PairTable {
+  static constexpr int NP = P * (P + 1) / 2;
+  uint8_t a[NP > 0 ? NP : 1], b[NP > 0 ? NP : 1];
+  __device__ void fill() {
+    for (int idx = threadIdx.x; idx < NP; idx += blockDim.x) {
+      int aa = 0, off = 0;
+      while (idx >= off + (P - aa)) { off += P - aa; ++aa; }
+      a[idx] = (uint8_t)aa;
+      b[idx] = (uint8_t)(aa + idx - off);
+    }
+  }
+};
+
+// feature f of phi(row); zero past the feature width (padding)
+template <class S, typename TI>
+__device__ __forceinline__ float phi_feature(const TI* row, int f, const PairTable<S::PD>& pt) {
+  if (f < S::DK) return to_f(row[f]);
+  if (S::PHI == PHI_POLY2) {
+    if (f < S::D) { const int p = f - S::DK; return to_f(row[pt.a[p]]) * to_f(row[pt.b[p]]); }
+    return 0.f;
+  }
+  if (S::PHI == PHI_RAW_POLY2) {
+    if (f < S::DK + S::PD) return to_f(row[f - S::DK]);
+    if (f < S::D) { const int p = f - S::DK - S::PD; return to_f(row[pt.a[p]]) * to_f(row[pt.b[p]]); }
+  }
+  return 0.f;
+}
+
+// ----------------------------------------------------------------------------- coefficients
+// One workgroup per (sequence, chunk), flattened on x.  256 threads; chunk <= 64.
+template <int BC, int WP>
+__global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
+  const int chunk = (int)(blockIdx.x % (unsigned)p.nchunks), seq = (int)(blockIdx.x / (unsigned)p.nchunks);
+  const int t0 = chunk * BC;
+  const int te = min(p.N, t0 + BC) - 1;
+  const int nb = te - t0 + 1;
+  const int c = p.c;
+  const size_t g0 = (size_t)seq * p.N;
+  const int64_t cnt = *reinterpret_cast<const int64_t*>(p.state + (size_t)seq * p.seq_stride + p.off_count);
+  const int halo_valid = (int)min<int64_t>(cnt, (int64_t)(c - 1));
+
+  __shared__ float al[BC], et[BC], th[BC];
+  __shared__ float F[BC][BC + 1];   // F[t][n] = K_{t,n} theta_n
+  __shared__ float G[BC];           // e_{n->te} theta_n
+  float* out = p.coef + ((size_t)seq * p.nchunks + chunk) * p.coef_stride;
+  float* oA = out;
+  float* oB = out + BC;
+  float* oP = out + 2 * BC;
+  float* ocM = out + 2 * BC + 4;
+  float* ocS = ocM + WP;
+  float* oC = ocS + WP;             // [BC][WP]
+
+  for (int n = threadIdx.x; n < BC; n += blockDim.x) {
+    const bool ok = n < nb;
+    al[n] = ok ? p.alpha[g0 + t0 + n] : 0.f;
+    et[n] = (ok && p.momentum) ? p.eta[g0 + t0 + n] : 0.f;
+    th[n] = ok ? p.theta[g0 + t0 + n] : 0.f;
+  }
+  __syncthreads();
+  if (threadIdx.x < BC) {
+    const int n = threadIdx.x;
+    for (int t = 0; t < BC; ++t) F[t][n] = 0.f;
+    if (n < nb) {
+      float K = 1.f, e = 1.f;
+      F[n][n] = th[n];
+      for (int t = n + 1; t < nb; ++t) {
+        e *= et[t];
+        K = (1.f - al[t]) * K + e;
+        F[t][n] = K * th[n];
+      }
+      G[n] = e * th[n];
+    } else {
+      G[n] = 0.f;
+    }
+  }
+  if (threadIdx.x == 64) {
+    float a = 1.f, b = 0.f, e0 = 1.f;
+    for (int t = 0; t < BC; ++t) {
+      if (t < nb) {
+        a *= 1.f - al[t];
+        e0 *= et[t];
+        b = (1.f - al[t]) * b + e0;
+        oA[t] = a;
+        oB[t] = b;
+      } else {
+        oA[t] = 0.f;
+        oB[t] = 0.f;
+      }
+    }
+    oP[0] = e0;
+  }
+  __syncthreads();
+  // window row w <-> token i = t0 - (c-1) + w (relative to the call start)
+  for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) {
+    const int tt = idx / WP, w = idx % WP;
+    const int i = t0 - (c - 1) + w;
+    float s = 0.f;
+    if (tt < nb && w < BC + c - 1 && i >= -halo_valid && i <= t0 + tt) {
+      const int lo = max(t0, i), hi = min(t0 + tt, i + c - 1);
+      for (int n = lo; n <= hi; ++n) s += F[tt][n - t0];
+    }
+    oC[tt * WP + w] = s;
+  }
+  for (int w = threadIdx.x; w < WP; w += blockDim.x) {
+    const int i = t0 - (c - 1) + w;
+    float sm = 0.f, ss = 0.f;
+    if (w < BC + c - 1 && i >= -halo_valid && i <= te) {
+      const int lo = max(t0, i), hi = min(te, i + c - 1);
+      for (int n = lo; n <= hi; ++n) { sm += F[nb - 1][n - t0]; ss += G[n - t0]; }
+    }
+    ocM[w] = sm;
+    ocS[w] = ss;
+  }
+}
+
+// ----------------------------------------------------------------------------- chunk kernel
+template <class S>
+__global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
+  typedef typename S::T T;    // MFMA operand type
+  typedef typename S::TI TI;  // io type of q, k, v, out
+  typedef typename S::WS WS;
+  constexpr int DK = S::DK, DV = S::DV, D = S::D, DP = S::DP, H = S::H, BC = S::BC, WP = S::WP;
+  const int seq = blockIdx.x;
+  const int N = p.N, c = p.c, W = BC + c - 1;
+  const float s_grad = p.grad_scale;
+  const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
+
+  char* st = p.state + (size_t)seq * p.seq_stride;
+  float* Wt = reinterpret_cast<float*>(st + p.off_weights);
+  float* Mo = reinterpret_cast<float*>(st + p.off_momentum);
+  float* hk = reinterpret_cast<float*>(st + p.off_halo_k);
+  float* hv = reinterpret_cast<float*>(st + p.off_halo_v);
+  float* hg = reinterpret_cast<float*>(st + p.off_halo_g);
+  int64_t* cnt = reinterpret_cast<int64_t*>(st + p.off_count);
+  const int halo_valid = (int)min<int64_t>(*cnt, (int64_t)(c - 1));
+
+  const TI* q = reinterpret_cast<const TI*>(p.q) + (size_t)seq * N * DK;
+  const TI* k = reinterpret_cast<const TI*>(p.k) + (size_t)seq * N * DK;
+  const TI* v = reinterpret_cast<const TI*>(p.v) + (size_t)seq * N * DV;
+  TI* out = reinterpret_cast<TI*>(p.out) + (size_t)seq * N * DV;
+  const float* gam_in = p.gamma + (size_t)seq * N;
+
+  char* ws = p.ws + (size_t)seq * WS::bytes;
+  T* Xw = reinterpret_cast<T*>(ws + WS::Xw);     // [WP][DP]  phi(k) of the window
+  T* XwT = reinterpret_cast<T*>(ws + WS::XwT);   // [DP][WP]
+  T* Xq = reinterpret_cast<T*>(ws + WS::Xq);     // [BC][DP]  phi(q) of the chunk
+  T* Q1 = reinterpret_cast<T*>(ws + WS::Q1);     // [BC][WP]  C .* (Xq X^T)
+  // MLP
+  T* W1b = reinterpret_cast<T*>(ws + WS::W1b);   // [H][DP]   operand image of W1
+  T* S1b = reinterpret_cast<T*>(ws + WS::S1b);   // [H][DP]
+  T* W2b = reinterpret_cast<T*>(ws + WS::W2b);   // [DV][H]
+  T* S2b = reinterpret_cast<T*>(ws + WS::S2b);   // [DV][H]
+  T* W2T = reinterpret_cast<T*>(ws + WS::W2T);   // [H][DV]
+  float* Zf = reinterpret_cast<float*>(ws + WS::Zf);  // [WP][H]
+  T* Ab = reinterpret_cast<T*>(ws + WS::Ab);     // [WP][H]   gelu(Z)
+  T* AT = reinterpret_cast<T*>(ws + WS::AT);     // [H][WP]
+  T* D2 = reinterpret_cast<T*>(ws + WS::D2);     // [WP][DV]
+  T* D2T = reinterpret_cast<T*>(ws + WS::D2T);   // [DV][WP]
+  T* D2TM = reinterpret_cast<T*>(ws + WS::D2TM); // [DV][WP]  cM-scaled
+  T* D2TS = reinterpret_cast<T*>(ws + WS::D2TS); // [DV][WP]  cS-scaled
+  T* D1T = reinterpret_cast<T*>(ws + WS::D1T);   // [H][WP]
+  T* D1TM = reinterpret_cast<T*>(ws + WS::D1TM);
+  T* D1TS = reinterpret_cast<T*>(ws + WS::D1TS);
+  T* Ah = reinterpret_cast<T*>(ws + WS::Ah);     // [BC][H]   gelu(Zq)
+  T* Q2 = reinterpret_cast<T*>(ws + WS::Q2);     // [BC][WP]  C .* (gelu(Zq) A^T)
+  // linear (aliases of the MLP names where the roles coincide)
+  T* Mb = W2b;   // [DV][DP]
+  T* Sb = S2b;   // [DV][DP]
+
+  __shared__ TI kr[WP][DK];   // raw keys of the window (residual path, phi input)
+  __shared__ TI qr[BC][DK];   // raw queries of the chunk
+  __shared__ float gw[WP], cMw[WP], cSw[WP], cA[BC], cB[BC];
+  __shared__ float cP;
+  __shared__ PairTable<S::PD> pt;
+  if (S::PHI != PHI_IDENTITY) pt.fill();
+
+  // operand images of the state
+  if (S::MEM == MEM_MLP) {
+    const float* W1 = Wt;
+    const float* W2 = Wt + (size_t)H * D;
+    for (int e = threadIdx.x; e < H * DP; e += blockDim.x) {
+      const int j = e / DP, f = e % DP;
+      W1b[e] = from_f<T>(f < D ? W1[j * D + f] : 0.f);
+      S1b[e] = from_f<T>((f < D && mom) ? Mo[j * D + f] : 0.f);
+    }
+    for (int e = threadIdx.x; e < DV * H; e += blockDim.x) {
+      const int o = e / H, j = e % H;
+      W2b[e] = from_f<T>(W2[e]);
+      S2b[e] = from_f<T>(mom ? Mo[(size_t)H * D + e] : 0.f);
+      W2T[j * DV + o] = from_f<T>(W2[e]);
+    }
+  } else {
+    for (int e = threadIdx.x; e < DV * DP; e += blockDim.x) {
+      const int o = e / DP, f = e % DP;
+      Mb[e] = from_f<T>(f < D ? Wt[o * D + f] : 0.f);
+      Sb[e] = from_f<T>((f < D && mom) ? Mo[o * D + f] : 0.f);
+    }
+  }
+  __syncthreads();
+
+  const int nchunks = (N + BC - 1) / BC;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int t0 = ch * BC;
+    const int te = min(N, t0 + BC) - 1;
+    const float* coef = p.coef + ((size_t)seq * p.nchunks + ch) * p.coef_stride;
+    const float* Cc = coef + 2 * BC + 4 + 2 * WP;   // [BC][WP]
+
+    // ---- stage raw rows, gates, coefficients
+    for (int e = threadIdx.x; e < WP * DK; e += blockDim.x) {
+      const int w = e / DK, d = e % DK;
+      const int i = t0 - (c - 1) + w;
+      float x = 0.f;
+      if (w < W && i >= -halo_valid && i <= te) x = i >= 0 ? to_f(k[(size_t)i * DK + d]) : hk[(c - 1 + i) * DK + d];
+      kr[w][d] = from_f<TI>(x);
+    }
+    for (int e = threadIdx.x; e < BC * DK; e += blockDim.x) {
+      const int n = e / DK, d = e % DK;
+      qr[n][d] = t0 + n <= te ? q[(size_t)(t0 + n) * DK + d] : from_f<TI>(0.f);
+    }
+    for (int w = threadIdx.x; w < WP; w += blockDim.x) {
+      const int i = t0 - (c - 1) + w;
+      float g = 0.f;
+      if (w < W && i >= -halo_valid && i <= te) g = i >= 0 ? gam_in[i] : hg[c - 1 + i];
+      gw[w] = g;
+      cMw[w] = coef[2 * BC + 4 + w];
+      cSw[w] = coef[2 * BC + 4 + WP + w];
+    }
+    for (int n = threadIdx.x; n < BC; n += blockDim.x) { cA[n] = coef[n]; cB[n] = coef[BC + n]; }
+    if (threadIdx.x == 0) cP = coef[2 * BC];
+    __syncthreads();
+
+    // ---- phi of window keys and chunk queries
+    for (int e = threadIdx.x; e < WP * DP; e += blockDim.x) {
+      const int w = e / DP, f = e % DP;
+      const T x = from_f<T>(phi_feature<S>(&kr[w][0], f, pt));
+      Xw[e] = x;
+      XwT[f * WP + w] = x;
+    }
+    for (int e = threadIdx.x; e < BC * DP; e += blockDim.x) {
+      const int n = e / DP, f = e % DP;
+      Xq[e] = from_f<T>(phi_feature<S>(&qr[n][0], f, pt));
+    }
+    __syncthreads();
+
+    // value of window row w, component o (input or halo); row valid <=> gw != 0 or in range
+    auto vrow = [&](int w, int o) -> float {
+      const int i = t0 - (c - 1) + w;
+      if (w >= W || i < -halo_valid || i > te) return 0.f;
+      return i >= 0 ? to_f(v[(size_t)i * DV + o]) : hv[(c - 1 + i) * DV + o];
+    };
+
+    // Q1 = C .* (Xq X^T)
+    {
+      Op<T> ops[1] = {{Xq, DP, Xw, DP, DP}};
+      gemm_nt(BC, WP, ops, [&](int n, int w, const float* a) { Q1[n * WP + w] = from_f<T>(Cc[n * WP + w] * a[0]); });
+    }
+
+    if (S::MEM == MEM_MLP) {
+      // Z = X W1^T ; A = gelu(Z)
+      {
+        Op<T> ops[1] = {{Xw, DP, W1b, DP, DP}};
+        gemm_nt(WP, H, ops, [&](int w, int j, const float* a) {
+          Zf[w * H + j] = a[0];
+          const T g = from_f<T>(gelu(a[0]));
+          Ab[w * H + j] = g;
+          AT[j * WP + w] = g;
+        });
+      }
+      __syncthreads();
+      // E = R + A W2^T - V ; D2 = s gamma E  (dot bias: D2 = -s gamma V)
+      {
+        Op<T> ops[1] = {{Ab, H, W2b, H, H}};
+        gemm_nt(WP, DV, ops, [&](int w, int o, const float* a) {
+          const float vv = vrow(w, o);
+          float d2;
+          if (dot) d2 = -s_grad * gw[w] * vv;
+          else d2 = s_grad * gw[w] * ((res ? to_f(kr[w][o]) : 0.f) + a[0] - vv);
+          D2[w * DV + o] = from_f<T>(d2);
+          D2T[o * WP + w] = from_f<T>(d2);
+          D2TM[o * WP + w] = from_f<T>(cMw[w] * d2);
+          D2TS[o * WP + w] = from_f<T>(cSw[w] * d2);
+        });
+      }
+      __syncthreads();
+      // D1 = (D2 W2) .* gelu'(Z)
+      {
+        Op<T> ops[1] = {{D2, DV, W2T, DV, DV}};
+        gemm_nt(WP, H, ops, [&](int w, int j, const float* a) {
+          const float d1 = a[0] * gelu_prime(Zf[w * H + j]);
+          D1T[j * WP + w] = from_f<T>(d1);
+          D1TM[j * WP + w] = from_f<T>(cMw[w] * d1);
+          D1TS[j * WP + w] = from_f<T>(cSw[w] * d1);
+        });
+      }
+      __syncthreads();
+      // Zq = A_t Xq W1^T + B_t Xq S1^T - Q1 D1 ; Ah = gelu(Zq)
+      {
+        Op<T> ops[3] = {{Xq, DP, W1b, DP, DP}, {mom ? Xq : nullptr, DP, S1b, DP, DP}, {Q1, WP, D1T, WP, WP}};
+        gemm_nt(BC, H, ops, [&](int n, int j, const float* a) {
+          Ah[n * H + j] = from_f<T>(gelu(cA[n] * a[0] + cB[n] * a[1] - a[2]));
+        });
+      }
+      __syncthreads();
+      // Q2 = C .* (Ah A^T)
+      {
+        Op<T> ops[1] = {{Ah, H, Ab, H, H}};
+        gemm_nt(BC, WP, ops, [&](int n, int w, const float* a) { Q2[n * WP + w] = from_f<T>(Cc[n * WP + w] * a[0]); });
+      }
+      __syncthreads();
+      // y = Rq + A_t Ah W2^T + B_t Ah S2^T - Q2 D2
+      {
+        Op<T> ops[3] = {{Ah, H, W2b, H, H}, {mom ? Ah : nullptr, H, S2b, H, H}, {Q2, WP, D2T, WP, WP}};
+        gemm_nt(BC, DV, ops, [&](int n, int o, const float* a) {
+          if (t0 + n <= te) {
+            const float y = (res ? to_f(qr[n][o]) : 0.f) + cA[n] * a[0] + cB[n] * a[1] - a[2];
+            out[(size_t)(t0 + n) * DV + o] = from_f<TI>(y);
+          }
+        });
+      }
+      __syncthreads();
+      // state update at the chunk end
+      const float Ate = cA[te - t0], Bte = cB[te - t0], Pc = cP;
+      {
+        Op<T> ops[2] = {{D1TM, WP, XwT, WP, WP}, {mom ? D1TS : nullptr, WP, XwT, WP, WP}};
+        gemm_nt(H, DP, ops, [&](int j, int f, const float* a) {
+          if (f < D) {
+            const size_t e = (size_t)j * D + f;
+            const float w1 = Wt[e], s1 = mom ? Mo[e] : 0.f;
+            const float nw = Ate * w1 + Bte * s1 - a[0];
+            Wt[e] = nw;
+            W1b[j * DP + f] = from_f<T>(nw);
+            if (mom) {
+              const float ns = Pc * s1 - a[1];
+              Mo[e] = ns;
+              S1b[j * DP + f] = from_f<T>(ns);
+            }
+          }
+        });
+      }
+      {
+        Op<T> ops[2] = {{D2TM, WP, AT, WP, WP}, {mom ? D2TS : nullptr, WP, AT, WP, WP}};
+        gemm_nt(DV, H, ops, [&](int o, int j, const float* a) {
+          const size_t e = (size_t)H * D + (size_t)o * H + j;
+          const float w2 = Wt[e], s2 = mom ? Mo[e] : 0.f;
+          const float nw = Ate * w2 + Bte * s2 - a[0];
+          Wt[e] = nw;
+          W2b[o * H + j] = from_f<T>(nw);
+          W2T[j * DV + o] = from_f<T>(nw);
+          if (mom) {
+            const float ns = Pc * s2 - a[1];
+            Mo[e] = ns;
+            S2b[o * H + j] = from_f<T>(ns);
+          }
+        });
+      }
+      __syncthreads();
+    } else {
+      // linear: D = s gamma (X M^T - V)  (dot bias: -s gamma V)
+      {
+        Op<T> ops[1] = {{Xw, DP, Mb, DP, DP}};
+        gemm_nt(WP, DV, ops, [&](int w, int o, const float* a) {
+          const float vv = vrow(w, o);
+          const float d = dot ? -s_grad * gw[w] * vv : s_grad * gw[w] * (a[0] - vv);
+          D2T[o * WP + w] = from_f<T>(d);
+          D2TM[o * WP + w] = from_f<T>(cMw[w] * d);
+          D2TS[o * WP + w] = from_f<T>(cSw[w] * d);
+        });
+      }
+      __syncthreads();
+      // y = A_t Xq M^T + B_t Xq S^T - Q1 D
+      {
+        Op<T> ops[3] = {{Xq, DP, Mb, DP, DP}, {mom ? Xq : nullptr, DP, Sb, DP, DP}, {Q1, WP, D2T, WP, WP}};
+        gemm_nt(BC, DV, ops, [&](int n, int o, const float* a) {
+          if (t0 + n <= te) out[(size_t)(t0 + n) * DV + o] = from_f<TI>(cA[n] * a[0] + cB[n] * a[1] - a[2]);
+        });
+      }
+      __syncthreads();
+      const float Ate = cA[te - t0], Bte = cB[te - t0], Pc = cP;
+      {
+        Op<T> ops[2] = {{D2TM, WP, XwT, WP, WP}, {mom ? D2TS : nullptr, WP, XwT, WP, WP}};
+        gemm_nt(DV, DP, ops, [&](int o, int f, const float* a) {
+          if (f < D) {
+            const size_t e = (size_t)o * D + f;
+            const float m = Wt[e], s = mom ? Mo[e] : 0.f;
+            const float nm = Ate * m + Bte * s - a[0];
+            Wt[e] = nm;
+            Mb[o * DP + f] = from_f<T>(nm);
+            if (mom) {
+              const float ns = Pc * s - a[1];
+              Mo[e] = ns;
+              Sb[o * DP + f] = from_f<T>(ns);
+            }
+          }
+        });
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- halo of the last c-1 tokens (oldest first) and the token count.
+  // Slot j takes token N-(c-1)+j: from this call if >= 0, else from old slot
+  // N+j >= j, which increasing-j order has not overwritten yet.
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    for (int j = 0; j < c - 1; ++j) {
+      const int i = N - (c - 1) + j;
+      for (int d = lane; d < DK; d += 64) hk[j * DK + d] = i >= 0 ? to_f(k[(size_t)i * DK + d]) : hk[(N + j) * DK + d];
+      for (int o = lane; o < DV; o += 64) hv[j * DV + o] = i >= 0 ? to_f(v[(size_t)i * DV + o]) : hv[(N + j) * DV + o];
+      if (lane == 0) hg[j] = i >= 0 ? gam_in[i] : hg[N + j];
+    }
+    if (lane == 0) *cnt += N;
+  }
+}
+
+// ----------------------------------------------------------------------------- launch
+template <class S>
+hipError_t launch(const ChunkParams& cp, const CoeffParams& kp, int n_seq, hipStream_t stream,
+                  hipEvent_t ev0, hipEvent_t ev1) {
+  if (cp.N == 0 || n_seq == 0) return hipSuccess;
+  hipLaunchKernelGGL((coeff_kernel<S::BC, S::WP>), dim3((unsigned)kp.nchunks * (unsigned)n_seq), dim3(256), 0, stream, kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((chunk_kernel<S>), dim3(n_seq), dim3(256), 0, stream, cp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+#define ATLAS_VARIANT(NAME, ...)                                                            \
+  typedef Shape<__VA_ARGS__> NAME;                                                          \
+  template hipError_t launch<NAME>(const ChunkParams&, const CoeffParams&, int, hipStream_t, \
+                                   hipEvent_t, hipEvent_t);
+
+#include "atlas_mem_variants.inc"
+
+}  // namespace atlas

@@ -1,0 +1,75 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/atlas_mem.h declares, and validates configurations.  No kernel is
+launched."""
+import ctypes
+from dataclasses import replace
+
+import pytest
+
+from test_memorization_sequence_amd import binding
+from test_memorization_sequence_amd.configs import ORDER, WORKLOADS
+
+
+def test_library_exports_every_declared_function():
+    L = binding.lib()
+    names = binding.declared_functions()
+    assert {"atlas_mem_init", "atlas_mem_forward", "atlas_mem_free"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("name", ORDER)
+def test_every_workload_has_a_kernel(name):
+    assert binding.supported(binding.config_of(WORKLOADS[name])) == binding.OK
+
+
+def _cfg(**kw):
+    return binding.config_of(replace(WORKLOADS["layer_scale"], **kw))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=65), binding.ERR_UNSUPPORTED),         # c > chunk
+    (dict(hidden=384), binding.ERR_UNSUPPORTED),        # no kernel for this width
+    (dict(d_k=64), binding.ERR_INVALID),                # residual needs d_k == d_v
+    (dict(batch=0), binding.ERR_INVALID),
+    (dict(seq_len=-1), binding.ERR_INVALID),
+    (dict(window=0), binding.ERR_INVALID),
+    (dict(feature_map="raw_poly2", poly_dims=0), binding.ERR_INVALID),
+    (dict(feature_map="raw_poly2", poly_dims=200), binding.ERR_INVALID),
+])
+def test_bad_configs(kw, code):
+    assert binding.supported(_cfg(**kw)) == code
+
+
+def test_enum_fields_are_checked():
+    for field, val in (("memory", 7), ("feature_map", 5), ("bias", 3), ("io_dtype", 9)):
+        c = _cfg()
+        setattr(c, field, val)
+        assert binding.supported(c) == binding.ERR_INVALID, field
+    c = _cfg()
+    c.mlp_layers = 3
+    assert binding.supported(c) == binding.ERR_UNSUPPORTED
+    c = _cfg()
+    c.grad_scale = float("nan")
+    assert binding.supported(c) == binding.ERR_INVALID
+
+
+def test_null_handle_and_strings():
+    L = binding.lib()
+    assert L.atlas_mem_forward(None, *[None] * 10) == binding.ERR_INVALID
+    assert L.atlas_mem_free(None) == binding.OK
+    assert L.atlas_mem_state_bytes(None) == 0
+    assert L.atlas_mem_init(ctypes.byref(_cfg()), None) == binding.ERR_INVALID
+    for code in range(5):
+        assert L.atlas_mem_error_string(code)
+    assert L.atlas_mem_supported(None) == binding.ERR_INVALID
+
+
+def test_init_without_a_device_fails_cleanly():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p(1234)
+    rc = binding.lib().atlas_mem_init(ctypes.byref(_cfg()), ctypes.byref(h))
+    assert rc in (binding.ERR_HIP, binding.ERR_OOM)
+    assert not h.value

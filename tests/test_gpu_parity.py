@@ -1,0 +1,213 @@
+"""Parity of the HIP library with the fp64 oracle (needs an MI355X).
+
+Inputs come from the seeded generator; the same bits feed both sides.
+Tolerances (relative L2): 2e-2 for bf16 io, 1e-4 for fp32 io, applied to the
+outputs, to the memory's own contribution y - r (MLP with residual, where the
+residual path would otherwise dominate y), to the final weights and to the
+final momentum.  Halo and token count must match exactly.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from test_memorization_sequence_amd.configs import ORDER, WORKLOADS, lively
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from test_memorization_sequence_amd import binding
+    import harness
+    return binding, harness
+
+
+def _run_both(B, wl, seqs=None, n_tokens=None):
+    binding, H = B
+    inputs, w0 = H.prepare(wl)
+    mem = binding.AtlasMem(wl)
+    dev = H.to_device(wl, inputs)
+    st = mem.new_state(torch.from_numpy(w0))
+    out = H.gpu_run(mem, wl, dev, st)
+    torch.cuda.synchronize()
+    st_g = H.gpu_state_np(mem, st)
+    out_g = out.float().cpu().numpy()
+    from oracle import oracle as O
+    out_o, st_o, _ = O.run_workload(wl, inputs, w0, seqs=seqs, n_tokens=n_tokens)
+    return inputs, out_g, st_g, out_o, st_o, mem
+
+
+SMALL_N = 3 * 64 + 17   # three full chunks and a ragged tail
+
+
+@pytest.mark.parametrize("recipe", ["preset", "lively"])
+@pytest.mark.parametrize("name", ORDER)
+def test_parity_small(B, name, recipe):
+    wl = WORKLOADS[name].with_shape(batch=1, heads=2, seq_len=SMALL_N)
+    if recipe == "lively":
+        wl = lively(wl)
+    _say(f"[parity] {name} {recipe} B=1 H=2 N={SMALL_N}")
+    binding, H = B
+    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl)
+    r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
+    _say(f"[parity] {name} {recipe}: {r}")
+    tol = H.tol_of(wl)
+    assert np.isfinite(out_g).all()
+    for key in ("out", "memory_part", "weights", "momentum"):
+        if key in r:
+            assert r[key] <= tol, (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
+
+
+@pytest.mark.parametrize("name", ["linear_poly2", "mlp64", "layer_scale", "atlas_long"])
+def test_streaming_split_is_bitwise_equal(B, name):
+    """Two calls with a chunk-aligned split equal one call, bit for bit."""
+    binding, H = B
+    wl = lively(WORKLOADS[name].with_shape(batch=1, heads=2, seq_len=SMALL_N))
+    _say(f"[split] {name}")
+    inputs, w0 = H.prepare(wl)
+    dev = H.to_device(wl, inputs)
+    one = binding.AtlasMem(wl)
+    st1 = one.new_state(torch.from_numpy(w0))
+    out1 = H.gpu_run(one, wl, dev, st1)
+    n1 = 128
+    wa, wb = wl.with_shape(seq_len=n1), wl.with_shape(seq_len=SMALL_N - n1)
+    ma, mb = binding.AtlasMem(wa), binding.AtlasMem(wb)
+    st2 = ma.new_state(torch.from_numpy(w0))
+    part = lambda t, a, b: t[:, :, a:b].contiguous()
+    da = {k_: part(t, 0, n1) for k_, t in dev.items()}
+    db = {k_: part(t, n1, SMALL_N) for k_, t in dev.items()}
+    oa = H.gpu_run(ma, wa, da, st2)
+    ob = H.gpu_run(mb, wb, db, st2)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([oa, ob], dim=2), out1)
+    assert torch.equal(st1, st2)
+
+
+def test_deterministic(B):
+    binding, H = B
+    wl = lively(WORKLOADS["layer_scale"].with_shape(batch=1, heads=3, seq_len=SMALL_N))
+    _say("[determinism] layer_scale")
+    inputs, w0 = H.prepare(wl)
+    dev = H.to_device(wl, inputs)
+    mem = binding.AtlasMem(wl)
+    outs, sts = [], []
+    for _ in range(2):
+        st = mem.new_state(torch.from_numpy(w0))
+        outs.append(H.gpu_run(mem, wl, dev, st).clone())
+        sts.append(st)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(sts[0], sts[1])
+
+
+@pytest.mark.parametrize("n", [0, 1, 37, 64])
+@pytest.mark.parametrize("name", ["linear64_delta", "mlp64", "layer_scale"])
+def test_short_and_empty_calls(B, name, n):
+    """N = 0 leaves the state alone; N < chunk is one partial chunk."""
+    binding, H = B
+    wl = lively(WORKLOADS[name].with_shape(batch=1, heads=2, seq_len=n))
+    _say(f"[short] {name} N={n}")
+    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl)
+    if n == 0:
+        assert out_g.size == 0
+        np.testing.assert_array_equal(st_g["weights"], st_o["mem"])
+        assert (st_g["count"] == 0).all()
+        return
+    r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
+    tol = H.tol_of(wl)
+    for key in ("out", "memory_part", "weights", "momentum"):
+        if key in r:
+            assert r[key] <= tol, (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
+
+
+def test_alpha_one_erases_exactly(B):
+    """alpha = 1, theta = 0: weights become exactly zero and y = q exactly."""
+    binding, H = B
+    wl = WORKLOADS["layer_scale"].with_shape(batch=1, heads=2, seq_len=SMALL_N)
+    _say("[alpha=1] layer_scale")
+    inputs, w0 = H.prepare(wl)
+    inputs["alpha"][:] = 1.0
+    inputs["theta"][:] = 0.0
+    dev = H.to_device(wl, inputs)
+    mem = binding.AtlasMem(wl)
+    st = mem.new_state(torch.from_numpy(w0))
+    out = H.gpu_run(mem, wl, dev, st)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dev["q"])
+    assert not mem.view(st, "weights").any()
+
+
+def test_theta_zero_keeps_weights_exactly(B):
+    binding, H = B
+    wl = WORKLOADS["atlas_long"].with_shape(batch=1, heads=1, seq_len=SMALL_N)
+    _say("[theta=0] atlas_long")
+    inputs, w0 = H.prepare(wl)
+    inputs["alpha"][:] = 0.0
+    inputs["theta"][:] = 0.0
+    dev = H.to_device(wl, inputs)
+    mem = binding.AtlasMem(wl)
+    st = mem.new_state(torch.from_numpy(w0))
+    out = H.gpu_run(mem, wl, dev, st)
+    torch.cuda.synchronize()
+    assert torch.equal(mem.view(st, "weights").cpu(), torch.from_numpy(w0))
+    from oracle import oracle as O
+    out_o, _, _ = O.run_workload(wl, inputs, w0)
+    assert H.rel_l2(out.float().cpu().numpy().reshape(out_o.shape), out_o) <= 2e-2
+
+
+@pytest.mark.parametrize("name", ORDER)
+def test_full_size_sampled(B, name):
+    """Full shapes in the benchmark's launch configuration; the oracle replays
+    the first two chunks of the first and last sequence."""
+    binding, H = B
+    wl = WORKLOADS[name]
+    S = wl.batch * wl.heads
+    seqs = sorted({0, S - 1})
+    n = 2 * wl.chunk
+    _say(f"[full] {name} B={wl.batch} H={wl.heads} N={wl.seq_len} sampled seqs={seqs} n={n}")
+    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl, seqs=seqs, n_tokens=n)
+    assert np.isfinite(out_g).all()
+    r = H.compare(wl, inputs, out_g, None, out_o, None, seqs=seqs, n_tokens=n)
+    _say(f"[full] {name}: {r}")
+    for key in ("out", "memory_part"):
+        if key in r:
+            assert r[key] <= H.tol_of(wl), (key, r)
+    assert (st_g["count"] == wl.seq_len).all()
+
+
+def test_forward_rejects_bad_arguments(B):
+    binding, H = B
+    import ctypes
+    wl = WORKLOADS["mlp64"].with_shape(batch=1, heads=1, seq_len=64)
+    inputs, w0 = H.prepare(wl)
+    dev = H.to_device(wl, inputs)
+    mem = binding.AtlasMem(wl)
+    st = mem.new_state(torch.from_numpy(w0))
+    out = torch.empty(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    L = binding.lib()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = [p(dev["q"]), p(dev["k"]), p(dev["v"]), p(dev["alpha"]), p(dev["eta"]), p(dev["theta"]),
+            p(dev["gamma"]), p(st), p(out), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)]
+    for i in (0, 1, 2, 3, 5, 6, 7, 8):
+        bad = list(args)
+        bad[i] = ctypes.c_void_p(0)
+        assert L.atlas_mem_forward(mem.handle, *bad) == binding.ERR_INVALID
+    bad = list(args)
+    bad[8] = ctypes.c_void_p(out.data_ptr() + 2)            # misaligned
+    assert L.atlas_mem_forward(mem.handle, *bad) == binding.ERR_INVALID
+    bad = list(args)
+    bad[8] = p(dev["q"])                                    # out aliases q
+    assert L.atlas_mem_forward(mem.handle, *bad) == binding.ERR_INVALID
+    assert L.atlas_mem_forward(mem.handle, *args) == binding.OK
+    torch.cuda.synchronize()
