@@ -56,6 +56,12 @@ enum { ATLAS_MEM_LINEAR = 0, ATLAS_MEM_MLP = 1 };
 enum { ATLAS_PHI_IDENTITY = 0, ATLAS_PHI_POLY2 = 1, ATLAS_PHI_RAW_POLY2 = 2 };
 enum { ATLAS_BIAS_L2 = 0, ATLAS_BIAS_DOT = 1 };
 enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
+/* Kernel family.  PER_SEQUENCE: one workgroup per sequence, weights streamed
+ * through the cache each chunk.  SHARDED: the hidden units of each sequence
+ * split over several workgroups of one XCD, weights resident in registers
+ * (MLP memory, identity feature map, bf16 io).  AUTO picks SHARDED when a
+ * kernel of that family exists for the shape.                              */
+enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2 };
 
 typedef struct {
   int batch, heads;   /* B, H: B*H independent sequences                        */
@@ -74,6 +80,7 @@ typedef struct {
   int io_dtype;       /* ATLAS_BF16 | ATLAS_F32 for q, k, v, out                */
   float grad_scale;   /* s: 1 matches the printed update rules; 2 is the
                          literal derivative of the squared norm                 */
+  int kernel;         /* ATLAS_KERNEL_*                                         */
 } atlas_mem_config;
 
 typedef struct atlas_mem_s* atlas_mem_t;
@@ -138,6 +145,11 @@ atlas_status atlas_mem_forward(atlas_mem_t h,
  * created by the caller, who keeps ownership; NULL, NULL clears the hook.
  * Errors: INVALID_ARGUMENT (bad handle, exactly one event NULL).           */
 atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* after);
+
+/* Device-side error word of the handle's last forward call (0: none; bit 0:
+ * a group barrier of the sharded kernel timed out, its outputs are invalid).
+ * Synchronises the device.  Errors: INVALID_ARGUMENT, HIP.                 */
+atlas_status atlas_mem_device_errors(atlas_mem_t h, unsigned* flags);
 
 /* Releases the workspace and the handle (NULL is accepted).                */
 atlas_status atlas_mem_free(atlas_mem_t h);

@@ -25,6 +25,7 @@ MEM = {"linear": 0, "mlp": 1}
 PHI = {"identity": 0, "poly2": 1, "raw_poly2": 2}
 BIAS = {"l2": 0, "dot": 1}
 IO = {"bf16": 0, "f32": 1}
+KERNEL = {"auto": 0, "per_sequence": 1, "sharded": 2}
 TORCH_IO = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
@@ -32,7 +33,7 @@ class AtlasMemConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "batch", "heads", "seq_len", "d_k", "d_v", "memory", "mlp_layers", "mlp_hidden",
         "mlp_residual", "feature_map", "poly_dims", "window", "chunk", "momentum", "bias",
-        "io_dtype")] + [("grad_scale", ctypes.c_float)]
+        "io_dtype")] + [("grad_scale", ctypes.c_float), ("kernel", ctypes.c_int)]
 
 
 class StateLayout(ctypes.Structure):
@@ -73,6 +74,8 @@ def lib():
         L.atlas_mem_forward.restype = ctypes.c_int
         L.atlas_mem_set_kernel_events.argtypes = [vp, vp, vp]
         L.atlas_mem_set_kernel_events.restype = ctypes.c_int
+        L.atlas_mem_device_errors.argtypes = [vp, ctypes.POINTER(ctypes.c_uint)]
+        L.atlas_mem_device_errors.restype = ctypes.c_int
         L.atlas_mem_free.argtypes = [vp]
         L.atlas_mem_free.restype = ctypes.c_int
         L.atlas_mem_error_string.argtypes = [ctypes.c_int]
@@ -89,8 +92,8 @@ def declared_functions() -> list[str]:
     return sorted(set(re.findall(r"\b(atlas_mem_\w+)\s*\(", text)))
 
 
-def config_of(wl: Workload) -> AtlasMemConfig:
-    return AtlasMemConfig(
+def config_of(wl: Workload, kernel: str = "auto") -> AtlasMemConfig:
+    return AtlasMemConfig(kernel=KERNEL[kernel],
         batch=wl.batch, heads=wl.heads, seq_len=wl.seq_len, d_k=wl.d_k, d_v=wl.d_v,
         memory=MEM[wl.memory], mlp_layers=2 if wl.memory == "mlp" else 0, mlp_hidden=wl.hidden,
         mlp_residual=int(wl.residual), feature_map=PHI[wl.feature_map], poly_dims=wl.poly_dims,
@@ -109,8 +112,8 @@ def _ptr(t):
 class AtlasMem:
     """One library handle (one workload shape, one stream at a time)."""
 
-    def __init__(self, wl: Workload | AtlasMemConfig):
-        self.cfg = config_of(wl) if isinstance(wl, Workload) else wl
+    def __init__(self, wl: Workload | AtlasMemConfig, kernel: str = "auto"):
+        self.cfg = config_of(wl, kernel) if isinstance(wl, Workload) else wl
         self.io_dtype = torch.float32 if self.cfg.io_dtype == IO["f32"] else torch.bfloat16
         h = ctypes.c_void_p()
         rc = lib().atlas_mem_init(ctypes.byref(self.cfg), ctypes.byref(h))
@@ -162,6 +165,14 @@ class AtlasMem:
         rc = lib().atlas_mem_set_kernel_events(self.handle, raw(before), raw(after))
         if rc != OK:
             raise AtlasError(rc, "atlas_mem_set_kernel_events")
+
+    def device_errors(self) -> int:
+        """Error word of the last call (synchronises the device)."""
+        f = ctypes.c_uint(0)
+        rc = lib().atlas_mem_device_errors(self.handle, ctypes.byref(f))
+        if rc != OK:
+            raise AtlasError(rc, "atlas_mem_device_errors")
+        return f.value
 
     # -- forward --------------------------------------------------------------------
     def forward(self, q, k, v, alpha, eta, theta, gamma, state, out, stream=None):

@@ -32,6 +32,22 @@ static const Variant kVariants[] = {
 };
 #undef ATLAS_VARIANT
 
+typedef hipError_t (*ShardedLaunchFn)(const ShardedParams&, const CoeffParams&, hipStream_t, hipEvent_t, hipEvent_t);
+
+struct ShardedVariant {
+  const char* name;
+  int d, dv, h, g, wp, bc;
+  size_t (*xbytes)();
+  ShardedLaunchFn launch;
+};
+
+#define ATLAS_SHARDED(NAME, D, DV, H, G, WP, BC) \
+  {#NAME, D, DV, H, G, WP, BC, &sharded_xbytes<D, DV, H, G, WP, BC>, &launch_sharded<D, DV, H, G, WP, BC>},
+static const ShardedVariant kSharded[] = {
+#include "atlas_mem_sharded_variants.inc"
+};
+#undef ATLAS_SHARDED
+
 }  // namespace atlas
 
 using namespace atlas;
@@ -39,7 +55,9 @@ using namespace atlas;
 struct atlas_mem_s {
   uint32_t magic;
   atlas_mem_config cfg;
-  const Variant* var;
+  const Variant* var;           // per-sequence kernel, or
+  const ShardedVariant* svar;   // sharded kernel
+  unsigned* ctrl;               // sharded: error word + barrier counters
   atlas_mem_state_layout lay;
   int n_seq, nchunks, coef_stride, device;
   char* ws;
@@ -59,7 +77,19 @@ static int pd_of(const atlas_mem_config* c) {
   return c->feature_map == ATLAS_PHI_POLY2 ? c->d_k : c->feature_map == ATLAS_PHI_RAW_POLY2 ? c->poly_dims : 0;
 }
 
-static atlas_status check_config(const atlas_mem_config* c, const Variant** out) {
+static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
+  if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
+  if (c->d_k != c->d_v) return nullptr;
+  const int need_w = c->chunk + c->window - 1;
+  const ShardedVariant* best = nullptr;
+  for (const ShardedVariant& v : kSharded) {
+    if (v.d != c->d_k || v.dv != c->d_v || v.h != c->mlp_hidden || v.bc != c->chunk || v.wp < need_w) continue;
+    if (!best || v.wp < best->wp) best = &v;
+  }
+  return best;
+}
+
+static atlas_status check_config(const atlas_mem_config* c, const Variant** out, const ShardedVariant** sout) {
   if (!c) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->batch < 1 || c->heads < 1 || c->seq_len < 0 || c->d_k < 1 || c->d_v < 1) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->window < 1 || c->chunk < 1) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -78,6 +108,17 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out)
   // sequences x chunks must fit one grid dimension of the coefficient kernel
   const long n_seq = (long)c->batch * c->heads;
   if (n_seq > (1L << 20) || n_seq * ((c->seq_len + c->chunk - 1) / c->chunk) > 0x7fffffffL) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->kernel < ATLAS_KERNEL_AUTO || c->kernel > ATLAS_KERNEL_SHARDED) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->kernel != ATLAS_KERNEL_PER_SEQUENCE) {
+    const ShardedVariant* sv = find_sharded(c);
+    if (sv) {
+      if (sout) *sout = sv;
+      if (out) *out = nullptr;
+      return ATLAS_OK;
+    }
+    if (c->kernel == ATLAS_KERNEL_SHARDED) return ATLAS_ERR_UNSUPPORTED;
+  }
+  if (sout) *sout = nullptr;
   const int h = c->memory == ATLAS_MEM_MLP ? c->mlp_hidden : 0;
   const int need_w = c->chunk + c->window - 1;
   const Variant* best = nullptr;
@@ -112,29 +153,34 @@ static atlas_mem_state_layout make_layout(const atlas_mem_config* c) {
 
 extern "C" {
 
-atlas_status atlas_mem_supported(const atlas_mem_config* cfg) { return check_config(cfg, nullptr); }
+atlas_status atlas_mem_supported(const atlas_mem_config* cfg) { return check_config(cfg, nullptr, nullptr); }
 
 atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   if (!out) return ATLAS_ERR_INVALID_ARGUMENT;
   *out = nullptr;
   const Variant* var = nullptr;
-  atlas_status s = check_config(cfg, &var);
+  const ShardedVariant* svar = nullptr;
+  atlas_status s = check_config(cfg, &var, &svar);
   if (s != ATLAS_OK) return s;
   atlas_mem_s* h = new (std::nothrow) atlas_mem_s();
   if (!h) return ATLAS_ERR_OUT_OF_MEMORY;
   h->magic = kMagic;
   h->cfg = *cfg;
   h->var = var;
+  h->svar = svar;
+  h->ctrl = nullptr;
   h->lay = make_layout(cfg);
   h->n_seq = cfg->batch * cfg->heads;
   h->nchunks = (cfg->seq_len + cfg->chunk - 1) / cfg->chunk;
-  h->coef_stride = coef_stride(var->bc, var->wp);
+  h->coef_stride = var ? coef_stride(var->bc, var->wp) : coef_stride(svar->bc, svar->wp);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { delete h; return hip_fail(e); }
   h->ws = nullptr;
   h->coef = nullptr;
   h->ev_before = h->ev_after = nullptr;
-  const size_t ws_bytes = var->ws_bytes * (size_t)h->n_seq;
+  // sharded: exchange buffers per sequence, then the control words
+  const size_t ctrl_off = svar ? align_up(svar->xbytes() * (size_t)h->n_seq, 256) : 0;
+  const size_t ws_bytes = var ? var->ws_bytes * (size_t)h->n_seq : ctrl_off + align_up((1 + (size_t)h->n_seq) * 4, 256);
   const size_t coef_bytes = (size_t)h->n_seq * h->nchunks * h->coef_stride * sizeof(float);
   if (ws_bytes && hipMalloc(&h->ws, ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -146,6 +192,15 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
     (void)hipFree(h->ws);
     delete h;
     return ATLAS_ERR_OUT_OF_MEMORY;
+  }
+  if (svar) {
+    h->ctrl = reinterpret_cast<unsigned*>(h->ws + ctrl_off);
+    if ((e = hipMemset(h->ctrl, 0, (1 + (size_t)h->n_seq) * 4)) != hipSuccess) {
+      (void)hipFree(h->ws);
+      (void)hipFree(h->coef);
+      delete h;
+      return hip_fail(e);
+    }
   }
   *out = h;
   return ATLAS_OK;
@@ -197,6 +252,7 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
   if (dev != h->device) return ATLAS_ERR_INVALID_ARGUMENT;
 
   CoeffParams kp;
+  kp.ctrl = h->ctrl;
   kp.alpha = alpha;
   kp.eta = eta;
   kp.theta = theta;
@@ -210,6 +266,37 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
   kp.seq_stride = h->lay.seq_stride;
   kp.off_count = h->lay.count;
 
+  if (h->svar) {
+    ShardedParams sp;
+    sp.q = q;
+    sp.k = k;
+    sp.v = v;
+    sp.gamma = gamma;
+    sp.state = (char*)state;
+    sp.out = out;
+    sp.xws = h->ws;
+    sp.ctrl = h->ctrl;
+    sp.coef = h->coef;
+    sp.n_seq = h->n_seq;
+    sp.N = c.seq_len;
+    sp.c = c.window;
+    sp.nchunks = h->nchunks;
+    sp.coef_stride = h->coef_stride;
+    sp.seq_stride = h->lay.seq_stride;
+    sp.off_weights = h->lay.weights;
+    sp.off_momentum = h->lay.momentum;
+    sp.off_halo_k = h->lay.halo_k;
+    sp.off_halo_v = h->lay.halo_v;
+    sp.off_halo_g = h->lay.halo_g;
+    sp.off_count = h->lay.count;
+    sp.grad_scale = c.grad_scale;
+    sp.momentum = c.momentum;
+    sp.bias = c.bias;
+    sp.residual = c.mlp_residual;
+    e = h->svar->launch(sp, kp, (hipStream_t)stream, h->ev_before, h->ev_after);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATLAS_OK;
+  }
   ChunkParams cp;
   cp.q = q;
   cp.k = k;
@@ -245,6 +332,15 @@ atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* afte
   h->ev_before = (hipEvent_t)before;
   h->ev_after = (hipEvent_t)after;
   return ATLAS_OK;
+}
+
+atlas_status atlas_mem_device_errors(atlas_mem_t h, unsigned* flags) {
+  if (!h || h->magic != kMagic || !flags) return ATLAS_ERR_INVALID_ARGUMENT;
+  *flags = 0;
+  if (!h->ctrl) return ATLAS_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(flags, h->ctrl, sizeof(unsigned), hipMemcpyDeviceToHost);
+  return e == hipSuccess ? ATLAS_OK : hip_fail(e);
 }
 
 atlas_status atlas_mem_free(atlas_mem_t h) {

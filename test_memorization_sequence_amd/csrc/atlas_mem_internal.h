@@ -82,6 +82,7 @@ struct CoeffParams {
   const float* theta;
   const char* state;
   float* coef;
+  unsigned* ctrl;   // sharded kernel: [0] error word, [1 + s] barrier counter of sequence s; else null
   int N, c, nchunks, coef_stride, momentum;
   size_t seq_stride, off_count;
 };
@@ -100,6 +101,28 @@ struct ChunkParams {
   float grad_scale;
   int momentum, bias, residual;
 };
+
+struct ShardedParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gamma;
+  char* state;
+  void* out;
+  char* xws;        // exchange workspace, per sequence
+  unsigned* ctrl;   // [0] error word, [1 + s] barrier counter of sequence s
+  const float* coef;
+  int n_seq, N, c, nchunks, coef_stride;
+  size_t seq_stride, off_weights, off_momentum, off_halo_k, off_halo_v, off_halo_g, off_count;
+  float grad_scale;
+  int momentum, bias, residual;
+};
+
+template <int D, int DV, int H, int G, int WP, int BC>
+hipError_t launch_sharded(const ShardedParams& sp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
+                          hipEvent_t ev1);
+template <int D, int DV, int H, int G, int WP, int BC>
+size_t sharded_xbytes();
 
 // Enqueues the coefficient kernel, then the chunk kernel; ev0/ev1 (optional)
 // are recorded right before and right after the chunk kernel.

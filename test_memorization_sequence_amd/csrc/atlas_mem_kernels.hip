@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include "atlas_mem_internal.h"
+#include "atlas_mem_coeff.h"
 
 namespace atlas {
 
@@ -167,93 +168,6 @@ __device__ __forceinline__ float phi_feature(const TI* row, int f, const PairTab
     if (f < S::D) { const int p = f - S::DK - S::PD; return to_f(row[pt.a[p]]) * to_f(row[pt.b[p]]); }
   }
   return 0.f;
-}
-
-// ----------------------------------------------------------------------------- coefficients
-// One workgroup per (sequence, chunk), flattened on x.  256 threads; chunk <= 64.
-template <int BC, int WP>
-__global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
-  const int chunk = (int)(blockIdx.x % (unsigned)p.nchunks), seq = (int)(blockIdx.x / (unsigned)p.nchunks);
-  const int t0 = chunk * BC;
-  const int te = min(p.N, t0 + BC) - 1;
-  const int nb = te - t0 + 1;
-  const int c = p.c;
-  const size_t g0 = (size_t)seq * p.N;
-  const int64_t cnt = *reinterpret_cast<const int64_t*>(p.state + (size_t)seq * p.seq_stride + p.off_count);
-  const int halo_valid = (int)min<int64_t>(cnt, (int64_t)(c - 1));
-
-  __shared__ float al[BC], et[BC], th[BC];
-  __shared__ float F[BC][BC + 1];   // F[t][n] = K_{t,n} theta_n
-  __shared__ float G[BC];           // e_{n->te} theta_n
-  float* out = p.coef + ((size_t)seq * p.nchunks + chunk) * p.coef_stride;
-  float* oA = out;
-  float* oB = out + BC;
-  float* oP = out + 2 * BC;
-  float* ocM = out + 2 * BC + 4;
-  float* ocS = ocM + WP;
-  float* oC = ocS + WP;             // [BC][WP]
-
-  for (int n = threadIdx.x; n < BC; n += blockDim.x) {
-    const bool ok = n < nb;
-    al[n] = ok ? p.alpha[g0 + t0 + n] : 0.f;
-    et[n] = (ok && p.momentum) ? p.eta[g0 + t0 + n] : 0.f;
-    th[n] = ok ? p.theta[g0 + t0 + n] : 0.f;
-  }
-  __syncthreads();
-  if (threadIdx.x < BC) {
-    const int n = threadIdx.x;
-    for (int t = 0; t < BC; ++t) F[t][n] = 0.f;
-    if (n < nb) {
-      float K = 1.f, e = 1.f;
-      F[n][n] = th[n];
-      for (int t = n + 1; t < nb; ++t) {
-        e *= et[t];
-        K = (1.f - al[t]) * K + e;
-        F[t][n] = K * th[n];
-      }
-      G[n] = e * th[n];
-    } else {
-      G[n] = 0.f;
-    }
-  }
-  if (threadIdx.x == 64) {
-    float a = 1.f, b = 0.f, e0 = 1.f;
-    for (int t = 0; t < BC; ++t) {
-      if (t < nb) {
-        a *= 1.f - al[t];
-        e0 *= et[t];
-        b = (1.f - al[t]) * b + e0;
-        oA[t] = a;
-        oB[t] = b;
-      } else {
-        oA[t] = 0.f;
-        oB[t] = 0.f;
-      }
-    }
-    oP[0] = e0;
-  }
-  __syncthreads();
-  // window row w <-> token i = t0 - (c-1) + w (relative to the call start)
-  for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) {
-    const int tt = idx / WP, w = idx % WP;
-    const int i = t0 - (c - 1) + w;
-    float s = 0.f;
-    if (tt < nb && w < BC + c - 1 && i >= -halo_valid && i <= t0 + tt) {
-      const int lo = max(t0, i), hi = min(t0 + tt, i + c - 1);
-      for (int n = lo; n <= hi; ++n) s += F[tt][n - t0];
-    }
-    oC[tt * WP + w] = s;
-  }
-  for (int w = threadIdx.x; w < WP; w += blockDim.x) {
-    const int i = t0 - (c - 1) + w;
-    float sm = 0.f, ss = 0.f;
-    if (w < BC + c - 1 && i >= -halo_valid && i <= te) {
-      const int lo = max(t0, i), hi = min(te, i + c - 1);
-      for (int n = lo; n <= hi; ++n) { sm += F[nb - 1][n - t0]; ss += G[n - t0]; }
-    }
-    ocM[w] = sm;
-    ocS[w] = ss;
-  }
 }
 
 // ----------------------------------------------------------------------------- chunk kernel

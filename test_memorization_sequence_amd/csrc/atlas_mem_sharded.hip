@@ -1,0 +1,658 @@
+// atlas_mem_sharded.hip -- MLP memory with the hidden units of every
+// sequence split over G workgroups ("a group"), the fp32 weights and momentum
+// resident in registers for the whole call.
+//
+// Method (as in atlas_mem_kernels.hip): per chunk of BC tokens, gradients of
+// the Omega-rule window loss (ATLAS review sec. 3.2-3.3) at the chunk-start
+// weights, folded into momentum and decay (Titans review sec. 3.1) through the
+// gate coefficients A_t, B_t, C_{t,i}, cM_i, cS_i, P, and the retrieval
+// y_t = f_{W_t}(q_t) with the per-token weights (Titans review sec. 3.1,
+// "Retrieving a Memory").
+//
+// Work split.  Workgroup p of a group owns hidden units [p*HL, (p+1)*HL) of W1
+// (rows) and W2 (columns); inside it wave w owns 16 hidden units of W1/S1 and
+// DVW value rows of W2/S2.  Everything that sums over the hidden units of one
+// workgroup stays local; the two sums over ALL hidden units are exchanged
+// through L2:
+//   * the window forward A W2^T (needed for the error E) - reduce-scatter of
+//     the per-group partials, then all-gather of D2 = s*gamma*E  (two group
+//     barriers per chunk, on the recurrence's critical path);
+//   * the retrieval output - written as partials and reduced by the group one
+//     chunk later, off the critical path.
+//
+// Register layout of the state.  A 16x16 MFMA result tile gives lane l the
+// column (l & 15) and rows 4*(l >> 4) + r, r = 0..3.  Two such tiles stacked
+// along a 32-wide block of the contraction dimension therefore hold, for
+// lane group g = l >> 4, exactly the indices {4g..4g+3} U {16+4g..16+4g+3}:
+// an MFMA operand fragment in a permuted k order ("perm32").  The weights are
+// kept as result tiles of their own update GEMMs and converted to bf16
+// operands in place; the other operand of those GEMMs is read from LDS in the
+// same perm32 order.  Every other GEMM uses the natural k order.
+//
+// Group membership is XCD-aware: block b runs on XCD b % 8, so the G members
+// of a group are blocks 8*(gi*G + p) + xcd and share one L2.  Members of the
+// first 8 groups are the first 8*G blocks, so groups are complete in dispatch
+// order and later groups wait only for earlier groups to finish.  Every
+// barrier wait is bounded: on timeout the call's error word is set, all
+// further waits return at once, and the kernel runs to completion.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "atlas_mem_internal.h"
+#include "atlas_mem_coeff.h"
+
+namespace atlas {
+namespace sharded {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_prime(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * expf(-0.5f * z * z) * 0.39894228040143268f;
+}
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// natural k order: lane (row l&15, group g) reads k0+8g .. k0+8g+7
+__device__ __forceinline__ bf16x8 ld_nat(const bf16* base, int ld, int row0, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+// perm32 k order: k0+4g .. +3, then k0+16+4g .. +3
+__device__ __forceinline__ bf16x8 ld_perm(const bf16* base, int ld, int row0, int k0, int lane) {
+  const bf16* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// natural order, element i scaled by s[k0 + 8g + i]
+__device__ __forceinline__ bf16x8 ld_nat_scaled(const bf16* base, int ld, int row0, int k0, int lane, const float* s) {
+  const bf16x8 v = ld_nat(base, ld, row0, k0, lane);
+  const float* sc = s + k0 + 8 * (lane >> 4);
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)((float)v[i] * sc[i]);
+  return r;
+}
+// two stacked result tiles -> perm32 operand
+__device__ __forceinline__ bf16x8 tiles_to_frag(const f32x4& lo, const f32x4& hi) {
+  return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3], (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+}
+
+// ----------------------------------------------------------------------------- group barrier
+// Monotonic arrival counter per group; barrier number `k` (1, 2, ...) waits
+// for G*k arrivals.  The members of a group share one XCD and its L2, so no
+// device-wide cache write-back or L2 invalidation is needed: every wave waits
+// until its own stores are complete (they write through the CU's L1), the
+// counter is a device-scope atomic, and after the wait every wave invalidates
+// its CU's L1 (vector cache) so that later loads read the partners' data from
+// L2.  Bounded: about 2^24 polls, then the call's error word is set and every
+// later wait returns at once.
+__device__ __forceinline__ void group_barrier(unsigned* ctr, unsigned target, unsigned* err) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(ctr, 1u);
+    unsigned polls = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+      if (++polls > (1u << 24)) {
+        atomicOr(err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  asm volatile("buffer_inv sc0" ::: "memory");
+}
+
+// ----------------------------------------------------------------------------- shape
+template <int D_, int DV_, int H_, int G_, int WP_, int BC_>
+struct SShape {
+  static constexpr int D = D_, DV = DV_, H = H_, G = G_, WP = WP_, BC = BC_;
+  static constexpr int NW = 4;                 // waves per workgroup
+  static constexpr int HL = H / G;             // hidden units per workgroup
+  static constexpr int DVW = DV / NW;          // W2 value rows per wave
+  static constexpr int NDT = DVW / 16;         // their 16-tiles
+  static constexpr int ND = D / 16;            // 16-tiles of W1 rows (feature dim)
+  static constexpr int NT = WP / 16;           // window token tiles
+  static constexpr int NQ = BC / 16;           // chunk (query) tiles
+  static constexpr int RW = WP / G;            // window rows reduced by each member
+  static constexpr int RQ = BC / G;            // output rows reduced by each member
+  static_assert(HL == 16 * NW, "each wave owns 16 hidden units");
+  static_assert(DVW % 16 == 0 && D % 32 == 0 && WP % 32 == 0 && BC % 16 == 0 && HL % 32 == 0, "tiles");
+  static_assert(WP % G == 0 && BC % G == 0, "reduce split");
+  // LDS row strides in bf16 elements (multiples of 8: 16-byte aligned rows)
+  static constexpr int LX = D + 8, LT = WP + 8, LH = HL + 8, LV = DV + 8;
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  // LDS regions (bytes); lifetimes inside one chunk:
+  //   RX : X [WP][LX] (stage..Z) -> D2 [WP][LV] (gather..D1) -> XT [D][LT] (U)
+  //   RXQ: Xq [BC][LX] (stage..Zq) -> Q2 [BC][LT] (G..Yo)
+  static constexpr size_t oRX = 0;
+  static constexpr size_t szRX = align_up(mx(mx(WP * LX, WP * LV), D * LT) * 2, 256);
+  static constexpr size_t oRXQ = oRX + szRX;
+  static constexpr size_t szRXQ = align_up(mx(BC * LX, BC * LT) * 2, 256);
+  static constexpr size_t oQ1 = oRXQ + szRXQ;                       // Q1 [BC][LT]
+  static constexpr size_t oA = oQ1 + align_up(BC * LT * 2, 256);    // A [WP][LH]
+  static constexpr size_t oAT = oA + align_up(WP * LH * 2, 256);    // AT [HL][LT]
+  static constexpr size_t oD2T = oAT + align_up(HL * LT * 2, 256);  // D2T [DV][LT]
+  static constexpr size_t oD1T = oD2T + align_up(DV * LT * 2, 256); // D1T [HL][LT]
+  static constexpr size_t oAh = oD1T + align_up(HL * LT * 2, 256);  // Ah [BC][LH]
+  static constexpr size_t oW2T = oAh + align_up(BC * LH * 2, 256);  // W2T [HL][LV] (bf16 image)
+  static constexpr size_t oF = oW2T + align_up(HL * LV * 2, 256);   // floats: cA, cB, cM, cS
+  static constexpr size_t lds = oF + (2 * BC + 2 * WP + 4) * 4;
+  static_assert(lds <= 163840, "LDS budget of one CU");
+  // exchange workspace per sequence (bytes)
+  static constexpr size_t xY = 0;                                             // [2][G][WP][DV] f32
+  static constexpr size_t xD2 = xY + 2ull * G * WP * DV * 4;                  // [2][WP][DV] bf16
+  static constexpr size_t xYo = align_up(xD2 + 2ull * WP * DV * 2, 256);      // [2][G][BC][DV] f32
+  static constexpr size_t xbytes = align_up(xYo + 2ull * G * BC * DV * 4, 256);
+};
+
+// ----------------------------------------------------------------------------- kernel
+template <class S>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+sharded_mlp_kernel(ShardedParams p) {
+  constexpr int D = S::D, DV = S::DV, H = S::H, G = S::G, WP = S::WP, BC = S::BC;
+  constexpr int HL = S::HL, DVW = S::DVW, NDT = S::NDT, ND = S::ND, NT = S::NT, NQ = S::NQ;
+  constexpr int LX = S::LX, LT = S::LT, LH = S::LH, LV = S::LV;
+  extern __shared__ __attribute__((aligned(256))) char smem[];
+
+  // ---- XCD-aware group membership
+  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  const int pm = slot % G, gi = slot / G;
+  const int seq = gi * 8 + xcd;
+  if (seq >= p.n_seq) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int N = p.N, c = p.c, W = BC + c - 1;
+  const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
+  const float s_grad = p.grad_scale;
+
+  char* st = p.state + (size_t)seq * p.seq_stride;
+  float* Wt = reinterpret_cast<float*>(st + p.off_weights);
+  float* Mo = reinterpret_cast<float*>(st + p.off_momentum);
+  float* hk = reinterpret_cast<float*>(st + p.off_halo_k);
+  float* hv = reinterpret_cast<float*>(st + p.off_halo_v);
+  float* hg = reinterpret_cast<float*>(st + p.off_halo_g);
+  int64_t* cnt = reinterpret_cast<int64_t*>(st + p.off_count);
+  const int halo_valid = (int)min<int64_t>(*cnt, (int64_t)(c - 1));
+  const bf16* q = reinterpret_cast<const bf16*>(p.q) + (size_t)seq * N * D;
+  const bf16* k = reinterpret_cast<const bf16*>(p.k) + (size_t)seq * N * D;
+  const bf16* v = reinterpret_cast<const bf16*>(p.v) + (size_t)seq * N * DV;
+  bf16* out = reinterpret_cast<bf16*>(p.out) + (size_t)seq * N * DV;
+  const float* gam_in = p.gamma + (size_t)seq * N;
+
+  char* xw = p.xws + (size_t)seq * S::xbytes;
+  float* ybuf = reinterpret_cast<float*>(xw + S::xY);
+  bf16* d2buf = reinterpret_cast<bf16*>(xw + S::xD2);
+  float* yobuf = reinterpret_cast<float*>(xw + S::xYo);
+  unsigned* ctr = p.ctrl + 1 + seq;
+  unsigned* err = p.ctrl;
+  unsigned nbar = 0;
+
+  bf16* RX = reinterpret_cast<bf16*>(smem + S::oRX);
+  bf16* RXQ = reinterpret_cast<bf16*>(smem + S::oRXQ);
+  bf16* Q1 = reinterpret_cast<bf16*>(smem + S::oQ1);
+  bf16* Al = reinterpret_cast<bf16*>(smem + S::oA);
+  bf16* AT = reinterpret_cast<bf16*>(smem + S::oAT);
+  bf16* D2T = reinterpret_cast<bf16*>(smem + S::oD2T);
+  bf16* D1T = reinterpret_cast<bf16*>(smem + S::oD1T);
+  bf16* Ah = reinterpret_cast<bf16*>(smem + S::oAh);
+  bf16* W2L = reinterpret_cast<bf16*>(smem + S::oW2T);
+  float* cA = reinterpret_cast<float*>(smem + S::oF);
+  float* cB = cA + BC;
+  float* cM = cB + BC;
+  float* cS = cM + WP;
+  bf16* X = RX;     // [WP][LX]
+  bf16* D2 = RX;    // [WP][LV]
+  bf16* XT = RX;    // [D][LT]
+  bf16* Xq = RXQ;   // [BC][LX]
+  bf16* Q2 = RXQ;   // [BC][LT]
+
+  // ---- state slices into registers
+  const int jw = pm * HL + 16 * wave;      // first hidden unit of this wave (W1 rows)
+  const int dvw = DVW * wave;              // first value row of this wave (W2 rows)
+  f32x4 W1T[ND], S1T[ND], W2T[HL / 16][NDT], S2T[HL / 16][NDT];
+  {
+    const float* W1 = Wt;
+    const float* W2 = Wt + (size_t)H * D;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      const size_t e = (size_t)(jw + c16) * D + 16 * t + 4 * g;
+      W1T[t] = *reinterpret_cast<const f32x4*>(W1 + e);
+      S1T[t] = mom ? *reinterpret_cast<const f32x4*>(Mo + e) : zero4();
+    }
+#pragma unroll
+    for (int a = 0; a < HL / 16; ++a)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        const size_t e = (size_t)(dvw + 16 * bb + c16) * H + pm * HL + 16 * a + 4 * g;
+        W2T[a][bb] = *reinterpret_cast<const f32x4*>(W2 + e);
+        S2T[a][bb] = mom ? *reinterpret_cast<const f32x4*>(Mo + (size_t)H * D + e) : zero4();
+      }
+  }
+  // bf16 image W2L[jl][dv] of this workgroup's W2 columns (all value rows)
+  auto write_w2l = [&]() {
+#pragma unroll
+    for (int a = 0; a < HL / 16; ++a)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) W2L[(16 * a + 4 * g + r) * LV + dvw + 16 * bb + c16] = (bf16)W2T[a][bb][r];
+  };
+  write_w2l();
+
+  // token i (relative to the call start) of window row w, and its validity
+  auto row_ok = [&](int w, int t0, int te) {
+    const int i = t0 - (c - 1) + w;
+    return w < W && i >= -halo_valid && i <= te;
+  };
+
+  // reduce the retrieval partials of chunk `pc` (rows owned by this member) into out
+  auto reduce_out = [&](int pc) {
+    const int pt0 = pc * BC, pte = min(N, pt0 + BC) - 1;
+    const float* yo = yobuf + (size_t)(pc & 1) * G * BC * DV;
+    for (int e = tid; e < S::RQ * DV; e += 256) {
+      const int qq = pm * S::RQ + e / DV, o = e % DV;
+      if (pt0 + qq > pte) continue;
+      float y = res ? (float)q[(size_t)(pt0 + qq) * D + o] : 0.f;
+#pragma unroll
+      for (int pp = 0; pp < G; ++pp) y += yo[((size_t)pp * BC + qq) * DV + o];
+      out[(size_t)(pt0 + qq) * DV + o] = (bf16)y;
+    }
+  };
+
+  const int nchunks = (N + BC - 1) / BC;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int t0 = ch * BC;
+    const int te = min(N, t0 + BC) - 1;
+    const int sl = ch & 1;
+    const float* coef = p.coef + ((size_t)seq * p.nchunks + ch) * p.coef_stride;
+    const float* Cc = coef + 2 * BC + 4 + 2 * WP;   // [BC][WP]
+
+    // ---- stage: window keys X (phi = identity), chunk queries Xq, coefficients
+    for (int e = tid; e < WP * (D / 8); e += 256) {
+      const int w = e / (D / 8), d8 = (e % (D / 8)) * 8;
+      const int i = t0 - (c - 1) + w;
+      bf16x8 x;
+      if (!row_ok(w, t0, te)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = (bf16)0.f;
+      } else if (i >= 0) {
+        x = *reinterpret_cast<const bf16x8*>(k + (size_t)i * D + d8);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = (bf16)hk[(c - 1 + i) * D + d8 + u];
+      }
+      *reinterpret_cast<bf16x8*>(X + w * LX + d8) = x;
+    }
+    for (int e = tid; e < BC * (D / 8); e += 256) {
+      const int n = e / (D / 8), d8 = (e % (D / 8)) * 8;
+      bf16x8 x;
+      if (t0 + n <= te) x = *reinterpret_cast<const bf16x8*>(q + (size_t)(t0 + n) * D + d8);
+      else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = (bf16)0.f;
+      }
+      *reinterpret_cast<bf16x8*>(Xq + n * LX + d8) = x;
+    }
+    for (int e = tid; e < BC; e += 256) { cA[e] = coef[e]; cB[e] = coef[BC + e]; }
+    for (int e = tid; e < WP; e += 256) { cM[e] = coef[2 * BC + 4 + e]; cS[e] = coef[2 * BC + 4 + WP + e]; }
+    __syncthreads();
+    const float Pc = coef[2 * BC];
+
+    // ---- Q1 = C .* (Xq X^T)   [BC x WP], K = D, natural order
+    for (int t = wave; t < NQ * NT; t += 4) {
+      const int m0 = 16 * (t / NT), n0 = 16 * (t % NT);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32) acc = mma(ld_nat(Xq, LX, m0, k0, lane), ld_nat(X, LX, n0, k0, lane), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qq = m0 + 4 * g + r, tok = n0 + c16;
+        Q1[qq * LT + tok] = (bf16)(Cc[qq * WP + tok] * acc[r]);
+      }
+    }
+    // ---- Z^T = W1_w X^T  [16 j x WP], K = D (perm32, A from registers)
+    f32x4 ZT[NT];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) ZT[m] = zero4();
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const bf16x8 a = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) ZT[m] = mma(a, ld_perm(X, LX, 16 * m, 32 * s, lane), ZT[m]);
+    }
+    // A = gelu(Z) -> Al [tok][jl], AT [jl][tok]
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int tok = 16 * m + c16;
+      bf16x4 a4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        a4[r] = (bf16)gelu(ZT[m][r]);
+        AT[(16 * wave + 4 * g + r) * LT + tok] = a4[r];
+      }
+      *reinterpret_cast<bf16x4*>(Al + tok * LH + 16 * wave + 4 * g) = a4;
+    }
+    __syncthreads();
+
+    // ---- partial window forward Y_p = A W2_p^T  [WP x DVW per wave], K = HL (perm32)
+    {
+      float* yb = ybuf + ((size_t)sl * G + pm) * WP * DV;
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        f32x4 acc[NT];
+#pragma unroll
+        for (int m = 0; m < NT; ++m) acc[m] = zero4();
+#pragma unroll
+        for (int s = 0; s < HL / 32; ++s) {
+          const bf16x8 bw = tiles_to_frag(W2T[2 * s][bb], W2T[2 * s + 1][bb]);
+#pragma unroll
+          for (int m = 0; m < NT; ++m) acc[m] = mma(ld_perm(Al, LH, 16 * m, 32 * s, lane), bw, acc[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yb[(size_t)(16 * m + 4 * g + r) * DV + dvw + 16 * bb + c16] = acc[m][r];
+      }
+    }
+    group_barrier(ctr, G * (++nbar), err);
+
+    // ---- reduce-scatter: this member's window rows -> D2 rows; previous chunk's outputs
+    {
+      const float* yb = ybuf + (size_t)sl * G * WP * DV;
+      bf16* d2b = d2buf + (size_t)sl * WP * DV;
+      for (int e = tid; e < S::RW * DV; e += 256) {
+        const int w = pm * S::RW + e / DV, o = e % DV;
+        float d2 = 0.f;
+        if (row_ok(w, t0, te)) {
+          const int i = t0 - (c - 1) + w;
+          const float vv = i >= 0 ? (float)v[(size_t)i * DV + o] : hv[(c - 1 + i) * DV + o];
+          const float gm = i >= 0 ? gam_in[i] : hg[c - 1 + i];
+          if (dot) {
+            d2 = -s_grad * gm * vv;
+          } else {
+            float y = 0.f;
+#pragma unroll
+            for (int pp = 0; pp < G; ++pp) y += yb[((size_t)pp * WP + w) * DV + o];
+            const float r0 = res ? (i >= 0 ? (float)k[(size_t)i * D + o] : hk[(c - 1 + i) * D + o]) : 0.f;
+            d2 = s_grad * gm * (r0 + y - vv);
+          }
+        }
+        d2b[(size_t)w * DV + o] = (bf16)d2;
+      }
+      if (ch > 0) reduce_out(ch - 1);
+    }
+    group_barrier(ctr, G * (++nbar), err);
+
+    // ---- all-gather D2 -> D2 [tok][dv], D2T [dv][tok]
+    {
+      const bf16* d2b = d2buf + (size_t)sl * WP * DV;
+      for (int e = tid; e < WP * (DV / 8); e += 256) {
+        const int w = e / (DV / 8), o8 = (e % (DV / 8)) * 8;
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(d2b + (size_t)w * DV + o8);
+        *reinterpret_cast<bf16x8*>(D2 + w * LV + o8) = x;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) D2T[(o8 + u) * LT + w] = x[u];
+      }
+    }
+    __syncthreads();
+
+    // ---- D1^T = (W2^T D2^T) .* gelu'(Z^T)  [16 j x WP], K = DV (natural, both LDS)
+    {
+      f32x4 acc[NT];
+#pragma unroll
+      for (int m = 0; m < NT; ++m) acc[m] = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < DV; k0 += 32) {
+        const bf16x8 a = ld_nat(W2L, LV, 16 * wave, k0, lane);
+#pragma unroll
+        for (int m = 0; m < NT; ++m) acc[m] = mma(a, ld_nat(D2, LV, 16 * m, k0, lane), acc[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          D1T[(16 * wave + 4 * g + r) * LT + 16 * m + c16] = (bf16)(acc[m][r] * gelu_prime(ZT[m][r]));
+    }
+    __syncthreads();
+
+    // ---- retrieval, layer 1: Zq^T = A_q W1 Xq^T + B_q S1 Xq^T - D1^T Q1^T  [16 j x BC]
+    {
+      f32x4 a1[NQ], a2[NQ], a3[NQ];
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) { a1[m] = zero4(); a2[m] = zero4(); a3[m] = zero4(); }
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const bf16x8 fw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
+        const bf16x8 fs = tiles_to_frag(S1T[2 * s], S1T[2 * s + 1]);
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+          const bf16x8 xb = ld_perm(Xq, LX, 16 * m, 32 * s, lane);
+          a1[m] = mma(fw, xb, a1[m]);
+          if (mom) a2[m] = mma(fs, xb, a2[m]);
+        }
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < WP; k0 += 32) {
+        const bf16x8 a = ld_nat(D1T, LT, 16 * wave, k0, lane);
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) a3[m] = mma(a, ld_nat(Q1, LT, 16 * m, k0, lane), a3[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) {
+        const int qq = 16 * m + c16;
+        bf16x4 h4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h4[r] = (bf16)gelu(cA[qq] * a1[m][r] + cB[qq] * a2[m][r] - a3[m][r]);
+        *reinterpret_cast<bf16x4*>(Ah + qq * LH + 16 * wave + 4 * g) = h4;
+      }
+    }
+    __syncthreads();
+
+    // ---- Q2 = C .* (Ah A^T)  [BC x WP], K = HL (natural, both LDS)
+    for (int t = wave; t < NQ * NT; t += 4) {
+      const int m0 = 16 * (t / NT), n0 = 16 * (t % NT);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < HL; k0 += 32) acc = mma(ld_nat(Ah, LH, m0, k0, lane), ld_nat(Al, LH, n0, k0, lane), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qq = m0 + 4 * g + r, tok = n0 + c16;
+        Q2[qq * LT + tok] = (bf16)(Cc[qq * WP + tok] * acc[r]);
+      }
+    }
+    __syncthreads();
+
+    // ---- retrieval, layer 2 partial: A_q Ah W2^T + B_q Ah S2^T - Q2 D2  [BC x DVW per wave]
+    {
+      float* yo = yobuf + ((size_t)sl * G + pm) * BC * DV;
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        f32x4 a1[NQ], a2[NQ], a3[NQ];
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) { a1[m] = zero4(); a2[m] = zero4(); a3[m] = zero4(); }
+#pragma unroll
+        for (int s = 0; s < HL / 32; ++s) {
+          const bf16x8 fw = tiles_to_frag(W2T[2 * s][bb], W2T[2 * s + 1][bb]);
+          const bf16x8 fs = tiles_to_frag(S2T[2 * s][bb], S2T[2 * s + 1][bb]);
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) {
+            const bf16x8 ah = ld_perm(Ah, LH, 16 * m, 32 * s, lane);
+            a1[m] = mma(ah, fw, a1[m]);
+            if (mom) a2[m] = mma(ah, fs, a2[m]);
+          }
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < WP; k0 += 32) {
+          const bf16x8 bd = ld_nat(D2T, LT, dvw + 16 * bb, k0, lane);
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) a3[m] = mma(ld_nat(Q2, LT, 16 * m, k0, lane), bd, a3[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < NQ; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int qq = 16 * m + 4 * g + r;
+            yo[(size_t)qq * DV + dvw + 16 * bb + c16] = cA[qq] * a1[m][r] + cB[qq] * a2[m][r] - a3[m][r];
+          }
+      }
+    }
+    __syncthreads();
+
+    // ---- stage X^T for the W1 update (the D2 tile in RX is dead)
+    for (int e = tid; e < WP * (D / 8); e += 256) {
+      const int w = e / (D / 8), d8 = (e % (D / 8)) * 8;
+      const int i = t0 - (c - 1) + w;
+      bf16x8 x;
+      if (!row_ok(w, t0, te)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = (bf16)0.f;
+      } else if (i >= 0) {
+        x = *reinterpret_cast<const bf16x8*>(k + (size_t)i * D + d8);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = (bf16)hk[(c - 1 + i) * D + d8 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) XT[(d8 + u) * LT + w] = x[u];
+    }
+    __syncthreads();
+
+    // ---- state update at the chunk end (registers)
+    {
+      const int ce = te - t0;
+      const float Ate = cA[ce], Bte = cB[ce];
+      // W1^T [D x 16 j]: X^T (cM .* D1)
+      bf16x8 bm[WP / 32], bs[WP / 32];
+#pragma unroll
+      for (int s = 0; s < WP / 32; ++s) {
+        bm[s] = ld_nat_scaled(D1T, LT, 16 * wave, 32 * s, lane, cM);
+        bs[s] = ld_nat_scaled(D1T, LT, 16 * wave, 32 * s, lane, cS);
+      }
+#pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        f32x4 um = zero4(), us = zero4();
+#pragma unroll
+        for (int s = 0; s < WP / 32; ++s) {
+          const bf16x8 xa = ld_nat(XT, LT, 16 * t, 32 * s, lane);
+          um = mma(xa, bm[s], um);
+          if (mom) us = mma(xa, bs[s], us);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float w1 = W1T[t][r], s1 = S1T[t][r];
+          W1T[t][r] = Ate * w1 + Bte * s1 - um[r];
+          S1T[t][r] = Pc * s1 - us[r];
+        }
+      }
+      // W2^T [HL j x DVW]: (cM .* A)^T D2
+#pragma unroll
+      for (int a = 0; a < HL / 16; ++a) {
+        bf16x8 am[WP / 32], as_[WP / 32];
+#pragma unroll
+        for (int s = 0; s < WP / 32; ++s) {
+          am[s] = ld_nat_scaled(AT, LT, 16 * a, 32 * s, lane, cM);
+          as_[s] = ld_nat_scaled(AT, LT, 16 * a, 32 * s, lane, cS);
+        }
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          f32x4 um = zero4(), us = zero4();
+#pragma unroll
+          for (int s = 0; s < WP / 32; ++s) {
+            const bf16x8 bd = ld_nat(D2T, LT, dvw + 16 * bb, 32 * s, lane);
+            um = mma(am[s], bd, um);
+            if (mom) us = mma(as_[s], bd, us);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float w2 = W2T[a][bb][r], s2 = S2T[a][bb][r];
+            W2T[a][bb][r] = Ate * w2 + Bte * s2 - um[r];
+            S2T[a][bb][r] = Pc * s2 - us[r];
+          }
+        }
+      }
+      write_w2l();
+    }
+    __syncthreads();
+  }
+
+  // ---- last chunk's outputs, then the state back to memory
+  group_barrier(ctr, G * (++nbar), err);
+  if (nchunks > 0) reduce_out(nchunks - 1);
+  {
+    float* W1 = Wt;
+    float* W2 = Wt + (size_t)H * D;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      const size_t e = (size_t)(jw + c16) * D + 16 * t + 4 * g;
+      *reinterpret_cast<f32x4*>(W1 + e) = W1T[t];
+      if (mom) *reinterpret_cast<f32x4*>(Mo + e) = S1T[t];
+    }
+#pragma unroll
+    for (int a = 0; a < HL / 16; ++a)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        const size_t e = (size_t)(dvw + 16 * bb + c16) * H + pm * HL + 16 * a + 4 * g;
+        *reinterpret_cast<f32x4*>(W2 + e) = W2T[a][bb];
+        if (mom) *reinterpret_cast<f32x4*>(Mo + (size_t)H * D + e) = S2T[a][bb];
+      }
+  }
+  // halo and count: member 0, after every member has staged chunk 0 (the
+  // barrier above orders it after all reads of the old halo)
+  if (pm == 0 && tid < 64) {
+    for (int j = 0; j < c - 1; ++j) {
+      const int i = N - (c - 1) + j;
+      for (int d = lane; d < D; d += 64) hk[j * D + d] = i >= 0 ? (float)k[(size_t)i * D + d] : hk[(N + j) * D + d];
+      for (int o = lane; o < DV; o += 64) hv[j * DV + o] = i >= 0 ? (float)v[(size_t)i * DV + o] : hv[(N + j) * DV + o];
+      if (lane == 0) hg[j] = i >= 0 ? gam_in[i] : hg[N + j];
+    }
+    if (lane == 0) *cnt += N;
+  }
+}
+
+}  // namespace sharded
+
+template <int D, int DV, int H, int G, int WP, int BC>
+hipError_t launch_sharded(const ShardedParams& sp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
+                          hipEvent_t ev1) {
+  typedef sharded::SShape<D, DV, H, G, WP, BC> S;
+  if (sp.N == 0 || sp.n_seq == 0) return hipSuccess;
+  hipLaunchKernelGGL((coeff_kernel<BC, WP>), dim3((unsigned)kp.nchunks * (unsigned)sp.n_seq), dim3(256), 0,
+                     stream, kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  static bool attr_set = false;
+  if (!attr_set) {
+    // allow more than the default dynamic LDS; a refusal shows up at launch
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&sharded::sharded_mlp_kernel<S>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
+    (void)hipGetLastError();
+    attr_set = true;
+  }
+  const unsigned groups8 = (unsigned)((sp.n_seq + 7) / 8);
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((sharded::sharded_mlp_kernel<S>), dim3(groups8 * 8u * G), dim3(256), S::lds, stream, sp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+template <int D, int DV, int H, int G, int WP, int BC>
+size_t sharded_xbytes() { return sharded::SShape<D, DV, H, G, WP, BC>::xbytes; }
+
+#define ATLAS_SHARDED(NAME, D, DV, H, G, WP, BC)                                                        \
+  template hipError_t launch_sharded<D, DV, H, G, WP, BC>(const ShardedParams&, const CoeffParams&,      \
+                                                          hipStream_t, hipEvent_t, hipEvent_t);          \
+  template size_t sharded_xbytes<D, DV, H, G, WP, BC>();
+#include "atlas_mem_sharded_variants.inc"
+#undef ATLAS_SHARDED
+
+}  // namespace atlas

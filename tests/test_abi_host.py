@@ -52,6 +52,20 @@ def test_enum_fields_are_checked():
     c = _cfg()
     c.grad_scale = float("nan")
     assert binding.supported(c) == binding.ERR_INVALID
+    c = _cfg()
+    c.kernel = 7
+    assert binding.supported(c) == binding.ERR_INVALID
+
+
+def test_kernel_family_selection():
+    ok = binding.OK
+    assert binding.supported(binding.config_of(WORKLOADS["layer_scale"], "sharded")) == ok
+    assert binding.supported(binding.config_of(WORKLOADS["layer_scale"], "per_sequence")) == ok
+    assert binding.supported(binding.config_of(WORKLOADS["mlp64"], "sharded")) == ok
+    # no sharded kernel for the raw+poly2 map or for linear memories
+    assert binding.supported(binding.config_of(WORKLOADS["atlas_long"], "sharded")) == binding.ERR_UNSUPPORTED
+    assert binding.supported(binding.config_of(WORKLOADS["linear_poly2"], "sharded")) == binding.ERR_UNSUPPORTED
+    assert binding.supported(binding.config_of(WORKLOADS["atlas_long"], "auto")) == ok
 
 
 def test_null_handle_and_strings():

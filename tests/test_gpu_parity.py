@@ -32,14 +32,15 @@ def B():
     return binding, harness
 
 
-def _run_both(B, wl, seqs=None, n_tokens=None):
+def _run_both(B, wl, seqs=None, n_tokens=None, kernel="auto"):
     binding, H = B
     inputs, w0 = H.prepare(wl)
-    mem = binding.AtlasMem(wl)
+    mem = binding.AtlasMem(wl, kernel)
     dev = H.to_device(wl, inputs)
     st = mem.new_state(torch.from_numpy(w0))
     out = H.gpu_run(mem, wl, dev, st)
     torch.cuda.synchronize()
+    assert mem.device_errors() == 0
     st_g = H.gpu_state_np(mem, st)
     out_g = out.float().cpu().numpy()
     from oracle import oracle as O
@@ -50,17 +51,21 @@ def _run_both(B, wl, seqs=None, n_tokens=None):
 SMALL_N = 3 * 64 + 17   # three full chunks and a ragged tail
 
 
+CASES = [(n, k) for n in ORDER for k in ("auto", "per_sequence")
+         if k == "auto" or WORKLOADS[n].memory == "mlp"]
+
+
 @pytest.mark.parametrize("recipe", ["preset", "lively"])
-@pytest.mark.parametrize("name", ORDER)
-def test_parity_small(B, name, recipe):
+@pytest.mark.parametrize("name,kernel", CASES)
+def test_parity_small(B, name, kernel, recipe):
     wl = WORKLOADS[name].with_shape(batch=1, heads=2, seq_len=SMALL_N)
     if recipe == "lively":
         wl = lively(wl)
-    _say(f"[parity] {name} {recipe} B=1 H=2 N={SMALL_N}")
+    _say(f"[parity] {name} kernel={kernel} {recipe} B=1 H=2 N={SMALL_N}")
     binding, H = B
-    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl)
+    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl, kernel=kernel)
     r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
-    _say(f"[parity] {name} {recipe}: {r}")
+    _say(f"[parity] {name} kernel={kernel} {recipe}: {r}")
     tol = H.tol_of(wl)
     assert np.isfinite(out_g).all()
     for key in ("out", "memory_part", "weights", "momentum"):
@@ -211,3 +216,40 @@ def test_forward_rejects_bad_arguments(B):
     assert L.atlas_mem_forward(mem.handle, *bad) == binding.ERR_INVALID
     assert L.atlas_mem_forward(mem.handle, *args) == binding.OK
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["mlp64", "layer_scale"])
+def test_window_wider_than_one_chunk_row_block(B, name):
+    """c = 33 on the mlp64 shape (window 96 rows) and c = 17 on layer_scale,
+    through the automatically chosen kernel."""
+    binding, H = B
+    c = 33 if name == "mlp64" else 17
+    wl = lively(WORKLOADS[name].with_shape(batch=1, heads=2, seq_len=SMALL_N))
+    from dataclasses import replace
+    wl = replace(wl, window=c, gamma_u=(-2.0, 2.0), theta_div=float(c))
+    _say(f"[window] {name} c={c}")
+    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl)
+    r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
+    _say(f"[window] {name}: {r}")
+    for key in ("out", "memory_part", "weights", "momentum"):
+        if key in r:
+            assert r[key] <= H.tol_of(wl), (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
+
+
+def test_kernel_families_agree(B):
+    """The sharded and per-sequence kernels compute the same thing (up to bf16
+    rounding order) on the same inputs."""
+    binding, H = B
+    wl = lively(WORKLOADS["layer_scale"].with_shape(batch=2, heads=3, seq_len=SMALL_N))
+    _say("[families] layer_scale")
+    inputs, w0 = H.prepare(wl)
+    dev = H.to_device(wl, inputs)
+    outs = []
+    for kernel in ("sharded", "per_sequence"):
+        mem = binding.AtlasMem(wl, kernel)
+        st = mem.new_state(torch.from_numpy(w0))
+        outs.append((H.gpu_run(mem, wl, dev, st).float().cpu().numpy(), H.gpu_state_np(mem, st)))
+        assert mem.device_errors() == 0
+    assert H.rel_l2(outs[0][0], outs[1][0]) < 5e-3
+    assert H.rel_l2(outs[0][1]["weights"], outs[1][1]["weights"]) < 1e-2
