@@ -172,7 +172,7 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   h->lay = make_layout(cfg);
   h->n_seq = cfg->batch * cfg->heads;
   h->nchunks = (cfg->seq_len + cfg->chunk - 1) / cfg->chunk;
-  h->coef_stride = var ? coef_stride(var->bc, var->wp) : coef_stride(svar->bc, svar->wp);
+  h->coef_stride = var ? coef_stride(var->bc, var->wp) : coef_stride(svar->bc, svar->wp, true);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { delete h; return hip_fail(e); }
   h->ws = nullptr;
@@ -253,6 +253,9 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
 
   CoeffParams kp;
   kp.ctrl = h->ctrl;
+  kp.q = q;
+  kp.k = k;
+  kp.off_halo_k = h->lay.halo_k;
   kp.alpha = alpha;
   kp.eta = eta;
   kp.theta = theta;

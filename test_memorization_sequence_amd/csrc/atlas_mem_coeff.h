@@ -10,7 +10,9 @@ namespace atlas {
 
 // ----------------------------------------------------------------------------- coefficients
 // One workgroup per (sequence, chunk), flattened on x.  256 threads; chunk <= 64.
-template <int BC, int WP>
+// QD > 0: also compute Q1 = C .* (Xq X^T) for an identity feature map of
+// width QD (window keys X, chunk queries Xq), stored as bf16 after C.
+template <int BC, int WP, int QD = 0>
 __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   const int chunk = (int)(blockIdx.x % (unsigned)p.nchunks), seq = (int)(blockIdx.x / (unsigned)p.nchunks);
   const int t0 = chunk * BC;
@@ -86,6 +88,52 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
       for (int n = lo; n <= hi; ++n) s += F[tt][n - t0];
     }
     oC[tt * WP + w] = s;
+  }
+  __syncthreads();
+  if constexpr (QD > 0) {
+    // Q1 = C .* (Xq X^T): bf16 MFMA, fp32 accumulation, 4 waves x 16x16 tiles
+    typedef __bf16 bx8 __attribute__((ext_vector_type(8)));
+    typedef float fx4 __attribute__((ext_vector_type(4)));
+    constexpr int L = QD + 8;
+    __shared__ __attribute__((aligned(16))) __bf16 Xs[WP * L];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[BC * L];
+    const __bf16* kk = reinterpret_cast<const __bf16*>(p.k) + (size_t)seq * p.N * QD;
+    const __bf16* qq = reinterpret_cast<const __bf16*>(p.q) + (size_t)seq * p.N * QD;
+    const float* hk = reinterpret_cast<const float*>(p.state + (size_t)seq * p.seq_stride + p.off_halo_k);
+    for (int e = threadIdx.x; e < WP * (QD / 8); e += blockDim.x) {
+      const int w = e / (QD / 8), d8 = (e % (QD / 8)) * 8, i = t0 - (c - 1) + w;
+      bx8 x;
+      for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
+      if (w < BC + c - 1 && i >= -halo_valid && i <= te) {
+        if (i >= 0) x = *reinterpret_cast<const bx8*>(kk + (size_t)i * QD + d8);
+        else
+          for (int z = 0; z < 8; ++z) x[z] = (__bf16)hk[(c - 1 + i) * QD + d8 + z];
+      }
+      *reinterpret_cast<bx8*>(Xs + w * L + d8) = x;
+    }
+    for (int e = threadIdx.x; e < BC * (QD / 8); e += blockDim.x) {
+      const int n = e / (QD / 8), d8 = (e % (QD / 8)) * 8;
+      bx8 x;
+      for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
+      if (n < nb) x = *reinterpret_cast<const bx8*>(qq + (size_t)(t0 + n) * QD + d8);
+      *reinterpret_cast<bx8*>(Qs + n * L + d8) = x;
+    }
+    __syncthreads();
+    __bf16* oQ = reinterpret_cast<__bf16*>(oC + BC * WP);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+    for (int t = wave; t < (BC / 16) * (WP / 16); t += 4) {
+      const int m0 = 16 * (t / (WP / 16)), n0 = 16 * (t % (WP / 16));
+      fx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < QD; k0 += 32) {
+        const bx8 a = *reinterpret_cast<const bx8*>(Qs + (m0 + c16) * L + k0 + 8 * g);
+        const bx8 b = *reinterpret_cast<const bx8*>(Xs + (n0 + c16) * L + k0 + 8 * g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+      }
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + 4 * g + r, col = n0 + c16;
+        oQ[row * WP + col] = (__bf16)(oC[row * WP + col] * acc[r]);
+      }
+    }
   }
   for (int w = threadIdx.x; w < WP; w += blockDim.x) {
     const int i = t0 - (c - 1) + w;

@@ -74,7 +74,9 @@ struct Shape {
 //   [2BC+4, +WP)       cM_i = C_{te,i}
 //   [2BC+4+WP, +WP)    cS_i
 //   [2BC+4+2WP, +BC*WP) C_{t,i} row-major
-constexpr int coef_stride(int bc, int wp) { return 2 * bc + 4 + 2 * wp + bc * wp; }
+//   with a precomputed Q1 (sharded kernel, identity feature map) the block
+//   continues with Q1 = C .* (Xq X^T) as bf16 [BC][WP] (BC*WP/2 floats).
+constexpr int coef_stride(int bc, int wp, bool q1 = false) { return 2 * bc + 4 + 2 * wp + bc * wp + (q1 ? bc * wp / 2 : 0); }
 
 struct CoeffParams {
   const float* alpha;
@@ -83,6 +85,9 @@ struct CoeffParams {
   const char* state;
   float* coef;
   unsigned* ctrl;   // sharded kernel: [0] error word, [1 + s] barrier counter of sequence s; else null
+  const void* q;    // Q1 precompute (sharded kernel): bf16 queries and keys [seq][N][d]
+  const void* k;
+  size_t off_halo_k;
   int N, c, nchunks, coef_stride, momentum;
   size_t seq_stride, off_count;
 };

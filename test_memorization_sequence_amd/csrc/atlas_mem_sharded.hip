@@ -258,15 +258,35 @@ sharded_mlp_kernel(ShardedParams p) {
   auto reduce_out = [&](int pc) {
     const int pt0 = pc * BC, pte = min(N, pt0 + BC) - 1;
     const float* yo = yobuf + (size_t)(pc & 1) * G * BC * DV;
-    for (int e = tid; e < S::RQ * DV; e += 256) {
-      const int qq = pm * S::RQ + e / DV, o = e % DV;
+    for (int e = tid; e < S::RQ * DV / 4; e += 256) {
+      const int qq = pm * S::RQ + e / (DV / 4), o4 = (e % (DV / 4)) * 4;
       if (pt0 + qq > pte) continue;
-      float y = res ? (float)q[(size_t)(pt0 + qq) * D + o] : 0.f;
+      float4 part[G];
 #pragma unroll
-      for (int pp = 0; pp < G; ++pp) y += yo[((size_t)pp * BC + qq) * DV + o];
-      out[(size_t)(pt0 + qq) * DV + o] = (bf16)y;
+      for (int pp = 0; pp < G; ++pp) part[pp] = *reinterpret_cast<const float4*>(yo + ((size_t)pp * BC + qq) * DV + o4);
+      float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (res) {
+        const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(q + (size_t)(pt0 + qq) * D + o4);
+        y = make_float4((float)r4[0], (float)r4[1], (float)r4[2], (float)r4[3]);
+      }
+#pragma unroll
+      for (int pp = 0; pp < G; ++pp) { y.x += part[pp].x; y.y += part[pp].y; y.z += part[pp].z; y.w += part[pp].w; }
+      *reinterpret_cast<bf16x4*>(out + (size_t)(pt0 + qq) * DV + o4) = bf16x4{(bf16)y.x, (bf16)y.y, (bf16)y.z, (bf16)y.w};
     }
   };
+
+  // L2 prefetch of the next chunk's inputs: one 4-byte load per 128-byte line
+  // into registers (compile-time indexed), folded into `sink` only at the end
+  // of the chunk, so nothing waits for them before the first group barrier.
+  constexpr int CSTR = coef_stride(BC, WP, true);
+  constexpr int NPK = (WP * D * 2 + 32767) / 32768, NPV = (WP * DV * 2 + 32767) / 32768;
+  constexpr int NPQ = (BC * D * 2 + 32767) / 32768, NPC = (CSTR * 4 + 32767) / 32768;
+  unsigned sink = 0, pfk[NPK], pfv[NPV], pfq[NPQ], pfc[NPC];
+#define ATLAS_TOUCH(arr, n, base, bytes)                                               \
+  _Pragma("unroll") for (int u = 0; u < n; ++u) {                                      \
+    const size_t off = ((size_t)tid + 256u * u) * 128u;                                \
+    arr[u] = off < (bytes) ? *reinterpret_cast<const unsigned*>((base) + off) : 0u;    \
+  }
 
   const int nchunks = (N + BC - 1) / BC;
   for (int ch = 0; ch < nchunks; ++ch) {
@@ -276,49 +296,75 @@ sharded_mlp_kernel(ShardedParams p) {
     const float* coef = p.coef + ((size_t)seq * p.nchunks + ch) * p.coef_stride;
     const float* Cc = coef + 2 * BC + 4 + 2 * WP;   // [BC][WP]
 
-    // ---- stage: window keys X (phi = identity), chunk queries Xq, coefficients
-    for (int e = tid; e < WP * (D / 8); e += 256) {
-      const int w = e / (D / 8), d8 = (e % (D / 8)) * 8;
-      const int i = t0 - (c - 1) + w;
-      bf16x8 x;
-      if (!row_ok(w, t0, te)) {
+    // ---- stage: window keys X (phi = identity), chunk queries Xq, coefficients.
+    // All global loads of a thread are issued before its LDS stores.
+    {
+      constexpr int NXV = (WP * (D / 8) + 255) / 256, NQV = (BC * (D / 8) + 255) / 256;
+      bf16x8 xv[NXV], qv[NQV];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = (bf16)0.f;
-      } else if (i >= 0) {
-        x = *reinterpret_cast<const bf16x8*>(k + (size_t)i * D + d8);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = (bf16)hk[(c - 1 + i) * D + d8 + u];
+      for (int u = 0; u < NXV; ++u) {
+        const int e = tid + 256 * u, w = e / (D / 8), d8 = (e % (D / 8)) * 8;
+        const int i = t0 - (c - 1) + w;
+        for (int z = 0; z < 8; ++z) xv[u][z] = (bf16)0.f;
+        if (e < WP * (D / 8) && row_ok(w, t0, te)) {
+          if (i >= 0) xv[u] = *reinterpret_cast<const bf16x8*>(k + (size_t)i * D + d8);
+          else
+            for (int z = 0; z < 8; ++z) xv[u][z] = (bf16)hk[(c - 1 + i) * D + d8 + z];
+        }
       }
-      *reinterpret_cast<bf16x8*>(X + w * LX + d8) = x;
-    }
-    for (int e = tid; e < BC * (D / 8); e += 256) {
-      const int n = e / (D / 8), d8 = (e % (D / 8)) * 8;
-      bf16x8 x;
-      if (t0 + n <= te) x = *reinterpret_cast<const bf16x8*>(q + (size_t)(t0 + n) * D + d8);
-      else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = (bf16)0.f;
+      for (int u = 0; u < NQV; ++u) {
+        const int e = tid + 256 * u, n = e / (D / 8), d8 = (e % (D / 8)) * 8;
+        for (int z = 0; z < 8; ++z) qv[u][z] = (bf16)0.f;
+        if (e < BC * (D / 8) && t0 + n <= te) qv[u] = *reinterpret_cast<const bf16x8*>(q + (size_t)(t0 + n) * D + d8);
       }
-      *reinterpret_cast<bf16x8*>(Xq + n * LX + d8) = x;
+      // Q1 = C .* (Xq X^T) from the coefficient block (bf16 [BC][WP])
+      const bf16* q1g = reinterpret_cast<const bf16*>(coef + 2 * BC + 4 + 2 * WP + BC * WP);
+      constexpr int NQ1 = (BC * WP / 8 + 255) / 256;
+      bf16x8 q1v[NQ1];
+#pragma unroll
+      for (int u = 0; u < NQ1; ++u) {
+        const int e = tid + 256 * u;
+        if (e < BC * WP / 8) q1v[u] = *reinterpret_cast<const bf16x8*>(q1g + 8 * e);
+      }
+      if (tid < BC) { cA[tid] = coef[tid]; cB[tid] = coef[BC + tid]; }
+      if (tid < WP) { cM[tid] = coef[2 * BC + 4 + tid]; cS[tid] = coef[2 * BC + 4 + WP + tid]; }
+#pragma unroll
+      for (int u = 0; u < NXV; ++u) {
+        const int e = tid + 256 * u;
+        if (e < WP * (D / 8)) *reinterpret_cast<bf16x8*>(X + (e / (D / 8)) * LX + (e % (D / 8)) * 8) = xv[u];
+      }
+#pragma unroll
+      for (int u = 0; u < NQV; ++u) {
+        const int e = tid + 256 * u;
+        if (e < BC * (D / 8)) *reinterpret_cast<bf16x8*>(Xq + (e / (D / 8)) * LX + (e % (D / 8)) * 8) = qv[u];
+      }
+#pragma unroll
+      for (int u = 0; u < NQ1; ++u) {
+        const int e = tid + 256 * u;
+        if (e < BC * WP / 8) *reinterpret_cast<bf16x8*>(Q1 + (8 * e / WP) * LT + (8 * e) % WP) = q1v[u];
+      }
     }
-    for (int e = tid; e < BC; e += 256) { cA[e] = coef[e]; cB[e] = coef[BC + e]; }
-    for (int e = tid; e < WP; e += 256) { cM[e] = coef[2 * BC + 4 + e]; cS[e] = coef[2 * BC + 4 + WP + e]; }
+    constexpr int NRG = (S::RW * DV / 4 + 255) / 256;
     __syncthreads();
     const float Pc = coef[2 * BC];
 
-    // ---- Q1 = C .* (Xq X^T)   [BC x WP], K = D, natural order
-    for (int t = wave; t < NQ * NT; t += 4) {
-      const int m0 = 16 * (t / NT), n0 = 16 * (t % NT);
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int k0 = 0; k0 < D; k0 += 32) acc = mma(ld_nat(Xq, LX, m0, k0, lane), ld_nat(X, LX, n0, k0, lane), acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = m0 + 4 * g + r, tok = n0 + c16;
-        Q1[qq * LT + tok] = (bf16)(Cc[qq * WP + tok] * acc[r]);
-      }
+    // ---- bring the next chunk's inputs into L2 while this chunk computes
+    {
+      const bool more = ch + 1 < nchunks;
+      const int n0 = t0 + BC, ne = more ? min(N, n0 + BC) - 1 : n0 - 1, lo = max(0, n0 - (c - 1));
+      const size_t bk = more ? (size_t)(ne - lo + 1) * D * 2 : 0, bv = more ? (size_t)(ne - lo + 1) * DV * 2 : 0;
+      const size_t bq = more ? (size_t)(ne - n0 + 1) * D * 2 : 0, bc = more ? (size_t)CSTR * 4 : 0;
+      const char* ck = reinterpret_cast<const char*>(k + (size_t)lo * D);
+      const char* cv = reinterpret_cast<const char*>(v + (size_t)lo * DV);
+      const char* cq = reinterpret_cast<const char*>(q + (size_t)n0 * D);
+      const char* cc = reinterpret_cast<const char*>(p.coef + ((size_t)seq * p.nchunks + (more ? ch + 1 : ch)) * p.coef_stride);
+      ATLAS_TOUCH(pfk, NPK, ck, bk)
+      ATLAS_TOUCH(pfv, NPV, cv, bv)
+      ATLAS_TOUCH(pfq, NPQ, cq, bq)
+      ATLAS_TOUCH(pfc, NPC, cc, bc)
     }
+
     // ---- Z^T = W1_w X^T  [16 j x WP], K = D (perm32, A from registers)
     f32x4 ZT[NT];
 #pragma unroll
@@ -369,24 +415,48 @@ sharded_mlp_kernel(ShardedParams p) {
     {
       const float* yb = ybuf + (size_t)sl * G * WP * DV;
       bf16* d2b = d2buf + (size_t)sl * WP * DV;
-      for (int e = tid; e < S::RW * DV; e += 256) {
-        const int w = pm * S::RW + e / DV, o = e % DV;
-        float d2 = 0.f;
+#pragma unroll
+      for (int u = 0; u < NRG; ++u) {
+        const int e = tid + 256 * u;
+        if (e >= S::RW * DV / 4) break;
+        const int w = pm * S::RW + e / (DV / 4), o4 = (e % (DV / 4)) * 4;
+        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!dot) {
+          float4 part[G];
+#pragma unroll
+          for (int pp = 0; pp < G; ++pp) part[pp] = *reinterpret_cast<const float4*>(yb + ((size_t)pp * WP + w) * DV + o4);
+#pragma unroll
+          for (int pp = 0; pp < G; ++pp) { y.x += part[pp].x; y.y += part[pp].y; y.z += part[pp].z; y.w += part[pp].w; }
+        }
+        // value row, residual row (raw key) and gamma of window row w
+        float4 pv = make_float4(0.f, 0.f, 0.f, 0.f), pr = pv;
+        float pg = 0.f;
         if (row_ok(w, t0, te)) {
           const int i = t0 - (c - 1) + w;
-          const float vv = i >= 0 ? (float)v[(size_t)i * DV + o] : hv[(c - 1 + i) * DV + o];
-          const float gm = i >= 0 ? gam_in[i] : hg[c - 1 + i];
-          if (dot) {
-            d2 = -s_grad * gm * vv;
+          if (i >= 0) {
+            const bf16x4 vv = *reinterpret_cast<const bf16x4*>(v + (size_t)i * DV + o4);
+            pv = make_float4((float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]);
+            if (res) {
+              const bf16x4 rr = *reinterpret_cast<const bf16x4*>(k + (size_t)i * D + o4);
+              pr = make_float4((float)rr[0], (float)rr[1], (float)rr[2], (float)rr[3]);
+            }
+            pg = gam_in[i];
           } else {
-            float y = 0.f;
-#pragma unroll
-            for (int pp = 0; pp < G; ++pp) y += yb[((size_t)pp * WP + w) * DV + o];
-            const float r0 = res ? (i >= 0 ? (float)k[(size_t)i * D + o] : hk[(c - 1 + i) * D + o]) : 0.f;
-            d2 = s_grad * gm * (r0 + y - vv);
+            pv = *reinterpret_cast<const float4*>(hv + (c - 1 + i) * DV + o4);
+            if (res) pr = *reinterpret_cast<const float4*>(hk + (c - 1 + i) * D + o4);
+            pg = hg[c - 1 + i];
           }
         }
-        d2b[(size_t)w * DV + o] = (bf16)d2;
+        const float sg = s_grad * pg;
+        bf16x4 d4;
+        if (dot) {
+          d4[0] = (bf16)(-sg * pv.x); d4[1] = (bf16)(-sg * pv.y);
+          d4[2] = (bf16)(-sg * pv.z); d4[3] = (bf16)(-sg * pv.w);
+        } else {
+          d4[0] = (bf16)(sg * (pr.x + y.x - pv.x)); d4[1] = (bf16)(sg * (pr.y + y.y - pv.y));
+          d4[2] = (bf16)(sg * (pr.z + y.z - pv.z)); d4[3] = (bf16)(sg * (pr.w + y.w - pv.w));
+        }
+        *reinterpret_cast<bf16x4*>(d2b + (size_t)w * DV + o4) = d4;
       }
       if (ch > 0) reduce_out(ch - 1);
     }
@@ -422,7 +492,8 @@ sharded_mlp_kernel(ShardedParams p) {
         for (int r = 0; r < 4; ++r)
           D1T[(16 * wave + 4 * g + r) * LT + 16 * m + c16] = (bf16)(acc[m][r] * gelu_prime(ZT[m][r]));
     }
-    __syncthreads();
+    // the next phase reads only this wave's own D1T rows, and Q1 / Xq were
+    // complete before the exchange: no workgroup barrier needed here
 
     // ---- retrieval, layer 1: Zq^T = A_q W1 Xq^T + B_q S1 Xq^T - D1^T Q1^T  [16 j x BC]
     {
@@ -460,14 +531,14 @@ sharded_mlp_kernel(ShardedParams p) {
     // ---- Q2 = C .* (Ah A^T)  [BC x WP], K = HL (natural, both LDS)
     for (int t = wave; t < NQ * NT; t += 4) {
       const int m0 = 16 * (t / NT), n0 = 16 * (t % NT);
+      float cc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cc[r] = Cc[(m0 + 4 * g + r) * WP + n0 + c16];
       f32x4 acc = zero4();
 #pragma unroll
       for (int k0 = 0; k0 < HL; k0 += 32) acc = mma(ld_nat(Ah, LH, m0, k0, lane), ld_nat(Al, LH, n0, k0, lane), acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = m0 + 4 * g + r, tok = n0 + c16;
-        Q2[qq * LT + tok] = (bf16)(Cc[qq * WP + tok] * acc[r]);
-      }
+      for (int r = 0; r < 4; ++r) Q2[(m0 + 4 * g + r) * LT + n0 + c16] = (bf16)(cc[r] * acc[r]);
     }
     __syncthreads();
 
@@ -581,10 +652,19 @@ sharded_mlp_kernel(ShardedParams p) {
       }
       write_w2l();
     }
+#pragma unroll
+    for (int u = 0; u < NPK; ++u) sink ^= pfk[u];
+#pragma unroll
+    for (int u = 0; u < NPV; ++u) sink ^= pfv[u];
+#pragma unroll
+    for (int u = 0; u < NPQ; ++u) sink ^= pfq[u];
+#pragma unroll
+    for (int u = 0; u < NPC; ++u) sink ^= pfc[u];
     __syncthreads();
   }
 
   // ---- last chunk's outputs, then the state back to memory
+  if (sink == 0x9e3779b9u && N < 0) out[0] = (bf16)0.f;   // keeps the prefetch loads
   group_barrier(ctr, G * (++nbar), err);
   if (nchunks > 0) reduce_out(nchunks - 1);
   {
@@ -625,7 +705,7 @@ hipError_t launch_sharded(const ShardedParams& sp, const CoeffParams& kp, hipStr
                           hipEvent_t ev1) {
   typedef sharded::SShape<D, DV, H, G, WP, BC> S;
   if (sp.N == 0 || sp.n_seq == 0) return hipSuccess;
-  hipLaunchKernelGGL((coeff_kernel<BC, WP>), dim3((unsigned)kp.nchunks * (unsigned)sp.n_seq), dim3(256), 0,
+  hipLaunchKernelGGL((coeff_kernel<BC, WP, D>), dim3((unsigned)kp.nchunks * (unsigned)sp.n_seq), dim3(256), 0,
                      stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
