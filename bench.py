@@ -26,6 +26,27 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0
 
+CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
+
+# HBM bytes per launch of the chunk kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes scaled by a plain-copy calibration (fetch x2.0, write
+# x1.0), keyed by the hash of the kernel sources they were taken on.  A
+# changed kernel reports null until it is measured again.
+MEASURED_TRAFFIC = {
+    "layer_scale": {"src": "16299ef06071595b", "bytes": 59.85e9},
+}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    m = hashlib.sha1()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h", ".inc")):
+            m.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                m.update(fh.read())
+    return m.hexdigest()[:16]
+
 
 def alg_flops_per_chunk(wl) -> float:
     """FLOPs the method must do per chunk of one sequence (the chunked form;
@@ -82,9 +103,19 @@ def main():
     ap.add_argument("--workload", default="layer_scale")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the chunk kernel")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only copy a buffer of this many bytes 3 times (HBM counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: every (batch, head) sequence is independent, "
@@ -144,9 +175,8 @@ def main():
     k_ms = float(np.mean(kernel_ms))
     achieved = flops / (k_ms * 1e-3) / 1e12
     peak = PEAK_FP32_TFLOPS if wl.io_dtype == "f32" else PEAK_BF16_TFLOPS
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get(wl.name)
+    meas = MEASURED_TRAFFIC.get(wl.name)
+    traffic = meas["bytes"] if meas and meas["src"] == kernel_source_hash() else None
     tokens = wl.batch * wl.seq_len
     res = {
         "metric": "memory update+retrieve tokens/sec (1 GPU); MFMA util % of bf16 peak",
@@ -169,12 +199,14 @@ def main():
         "mfma_util_pct": 100.0 * (flops / (ms_per_step * 1e-3) / 1e12) / peak,
         "roofline": {
             "bound": "mfma",
-            "kernel": "chunk_kernel",
+            "kernel": ("sharded_mlp_kernel" if binding.supported(binding.config_of(wl, "sharded")) == binding.OK
+                       else "chunk_kernel"),
             "achieved": achieved,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
             "traffic": traffic,
+            "traffic_unit": "bytes per launch",
             "alg_flops_per_launch": flops,
             "kernel_ms": k_ms,
         },
