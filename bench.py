@@ -33,7 +33,7 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 # x1.0), keyed by the hash of the kernel sources they were taken on.  A
 # changed kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    "layer_scale": {"src": "16299ef06071595b", "bytes": 59.85e9},
+    ("layer_scale", "sharded_mlp_kernel"): {"src": "16299ef06071595b", "bytes": 59.85e9},
 }
 
 
@@ -95,12 +95,20 @@ def cpu_baseline(wl, inputs, w0, budget_s: float):
     }
 
 
+def kernel_name(binding, wl, family):
+    """Name of the recurrent kernel a call runs for this workload and family."""
+    if family == "auto":
+        family = "sharded" if binding.supported(binding.config_of(wl, "sharded")) == binding.OK else "per_sequence"
+    return {"sharded": "sharded_mlp_kernel", "streamed": "stream_mlp_kernel", "per_sequence": "chunk_kernel"}[family]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="layer_scale")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "per_sequence", "sharded", "streamed"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -136,7 +144,7 @@ def main():
     io = torch.float32 if wl.io_dtype == "f32" else torch.bfloat16
     t_in = {k: torch.from_numpy(inputs[k]).to(dev, dtype=io) for k in ("q", "k", "v")}
     g_in = {k: torch.from_numpy(inputs[k]).to(dev) for k in ("alpha", "eta", "theta", "gamma")}
-    mem = binding.AtlasMem(wl)
+    mem = binding.AtlasMem(wl, args.kernel)
     state = mem.new_state(torch.from_numpy(w0), device=dev)
     out = torch.empty(wl.batch, wl.heads, wl.seq_len, wl.d_v, dtype=io, device=dev)
     stream = torch.cuda.current_stream()
@@ -175,7 +183,7 @@ def main():
     k_ms = float(np.mean(kernel_ms))
     achieved = flops / (k_ms * 1e-3) / 1e12
     peak = PEAK_FP32_TFLOPS if wl.io_dtype == "f32" else PEAK_BF16_TFLOPS
-    meas = MEASURED_TRAFFIC.get(wl.name)
+    meas = MEASURED_TRAFFIC.get((wl.name, kernel_name(binding, wl, args.kernel)))
     traffic = meas["bytes"] if meas and meas["src"] == kernel_source_hash() else None
     tokens = wl.batch * wl.seq_len
     res = {
@@ -191,7 +199,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if wl.io_dtype == "f32" else "bf16",
         "data": "synthetic (seeded numpy: L2-normalised q,k; N(0,1) v; sigmoid gates)",
-        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seq_len,
+        "config": {"workload": wl.name, "kernel_family": args.kernel, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seq_len,
                    "d_k": wl.d_k, "d_v": wl.d_v, "memory": wl.memory, "hidden": wl.hidden,
                    "feature_dim": wl.feature_dim, "window": wl.window, "chunk": wl.chunk,
                    "momentum": wl.momentum},
@@ -199,8 +207,7 @@ def main():
         "mfma_util_pct": 100.0 * (flops / (ms_per_step * 1e-3) / 1e12) / peak,
         "roofline": {
             "bound": "mfma",
-            "kernel": ("sharded_mlp_kernel" if binding.supported(binding.config_of(wl, "sharded")) == binding.OK
-                       else "chunk_kernel"),
+            "kernel": kernel_name(binding, wl, args.kernel),
             "achieved": achieved,
             "peak": peak,
             "unit": "TFLOP/s",

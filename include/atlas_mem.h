@@ -56,12 +56,15 @@ enum { ATLAS_MEM_LINEAR = 0, ATLAS_MEM_MLP = 1 };
 enum { ATLAS_PHI_IDENTITY = 0, ATLAS_PHI_POLY2 = 1, ATLAS_PHI_RAW_POLY2 = 2 };
 enum { ATLAS_BIAS_L2 = 0, ATLAS_BIAS_DOT = 1 };
 enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
-/* Kernel family.  PER_SEQUENCE: one workgroup per sequence, weights streamed
- * through the cache each chunk.  SHARDED: the hidden units of each sequence
- * split over several workgroups of one XCD, weights resident in registers
- * (MLP memory, identity feature map, bf16 io).  AUTO picks SHARDED when a
- * kernel of that family exists for the shape.                              */
-enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2 };
+/* Kernel family.  PER_SEQUENCE: one workgroup per sequence, every operand
+ * image kept in a global workspace (all memories and feature maps).
+ * SHARDED: the hidden units of each sequence split over several workgroups
+ * of one XCD, weights resident in registers.  STREAMED: one workgroup per
+ * sequence, the fp32 weights and momentum read and written once per chunk
+ * in one fused pass.  SHARDED and STREAMED serve the MLP memory with the
+ * identity feature map, d_k == d_v and bf16 io.  AUTO picks SHARDED, then
+ * PER_SEQUENCE, whichever has a kernel for the shape.                       */
+enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3 };
 
 typedef struct {
   int batch, heads;   /* B, H: B*H independent sequences                        */

@@ -25,7 +25,7 @@ MEM = {"linear": 0, "mlp": 1}
 PHI = {"identity": 0, "poly2": 1, "raw_poly2": 2}
 BIAS = {"l2": 0, "dot": 1}
 IO = {"bf16": 0, "f32": 1}
-KERNEL = {"auto": 0, "per_sequence": 1, "sharded": 2}
+KERNEL = {"auto": 0, "per_sequence": 1, "sharded": 2, "streamed": 3}
 TORCH_IO = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 

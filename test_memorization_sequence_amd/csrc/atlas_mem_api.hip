@@ -48,6 +48,18 @@ static const ShardedVariant kSharded[] = {
 };
 #undef ATLAS_SHARDED
 
+struct StreamVariant {
+  const char* name;
+  int d, dv, h, wp, bc;
+  ShardedLaunchFn launch;
+};
+
+#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC) {#NAME, D, DV, H, WP, BC, &launch_streamed<D, DV, H, WP, BC>},
+static const StreamVariant kStreamed[] = {
+#include "atlas_mem_stream_variants.inc"
+};
+#undef ATLAS_STREAMED
+
 }  // namespace atlas
 
 using namespace atlas;
@@ -56,7 +68,8 @@ struct atlas_mem_s {
   uint32_t magic;
   atlas_mem_config cfg;
   const Variant* var;           // per-sequence kernel, or
-  const ShardedVariant* svar;   // sharded kernel
+  const ShardedVariant* svar;   // sharded kernel, or
+  const StreamVariant* tvar;    // streamed-state kernel
   unsigned* ctrl;               // sharded: error word + barrier counters
   atlas_mem_state_layout lay;
   int n_seq, nchunks, coef_stride, device;
@@ -89,7 +102,21 @@ static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
   return best;
 }
 
-static atlas_status check_config(const atlas_mem_config* c, const Variant** out, const ShardedVariant** sout) {
+static const StreamVariant* find_streamed(const atlas_mem_config* c) {
+  if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
+  if (c->d_k != c->d_v) return nullptr;
+  const int need_w = c->chunk + c->window - 1;
+  const StreamVariant* best = nullptr;
+  for (const StreamVariant& v : kStreamed) {
+    if (v.d != c->d_k || v.dv != c->d_v || v.h != c->mlp_hidden || v.bc != c->chunk || v.wp < need_w) continue;
+    if (!best || v.wp < best->wp) best = &v;
+  }
+  return best;
+}
+
+// Exactly one of *out, *sout, *tout is set on success.
+static atlas_status check_config(const atlas_mem_config* c, const Variant** out, const ShardedVariant** sout,
+                                 const StreamVariant** tout) {
   if (!c) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->batch < 1 || c->heads < 1 || c->seq_len < 0 || c->d_k < 1 || c->d_v < 1) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->window < 1 || c->chunk < 1) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -108,17 +135,24 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   // sequences x chunks must fit one grid dimension of the coefficient kernel
   const long n_seq = (long)c->batch * c->heads;
   if (n_seq > (1L << 20) || n_seq * ((c->seq_len + c->chunk - 1) / c->chunk) > 0x7fffffffL) return ATLAS_ERR_INVALID_ARGUMENT;
-  if (c->kernel < ATLAS_KERNEL_AUTO || c->kernel > ATLAS_KERNEL_SHARDED) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->kernel < ATLAS_KERNEL_AUTO || c->kernel > ATLAS_KERNEL_STREAMED) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (out) *out = nullptr;
+  if (sout) *sout = nullptr;
+  if (tout) *tout = nullptr;
+  if (c->kernel == ATLAS_KERNEL_STREAMED) {
+    const StreamVariant* tv = find_streamed(c);
+    if (!tv) return ATLAS_ERR_UNSUPPORTED;
+    if (tout) *tout = tv;
+    return ATLAS_OK;
+  }
   if (c->kernel != ATLAS_KERNEL_PER_SEQUENCE) {
     const ShardedVariant* sv = find_sharded(c);
     if (sv) {
       if (sout) *sout = sv;
-      if (out) *out = nullptr;
       return ATLAS_OK;
     }
     if (c->kernel == ATLAS_KERNEL_SHARDED) return ATLAS_ERR_UNSUPPORTED;
   }
-  if (sout) *sout = nullptr;
   const int h = c->memory == ATLAS_MEM_MLP ? c->mlp_hidden : 0;
   const int need_w = c->chunk + c->window - 1;
   const Variant* best = nullptr;
@@ -153,14 +187,15 @@ static atlas_mem_state_layout make_layout(const atlas_mem_config* c) {
 
 extern "C" {
 
-atlas_status atlas_mem_supported(const atlas_mem_config* cfg) { return check_config(cfg, nullptr, nullptr); }
+atlas_status atlas_mem_supported(const atlas_mem_config* cfg) { return check_config(cfg, nullptr, nullptr, nullptr); }
 
 atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   if (!out) return ATLAS_ERR_INVALID_ARGUMENT;
   *out = nullptr;
   const Variant* var = nullptr;
   const ShardedVariant* svar = nullptr;
-  atlas_status s = check_config(cfg, &var, &svar);
+  const StreamVariant* tvar = nullptr;
+  atlas_status s = check_config(cfg, &var, &svar, &tvar);
   if (s != ATLAS_OK) return s;
   atlas_mem_s* h = new (std::nothrow) atlas_mem_s();
   if (!h) return ATLAS_ERR_OUT_OF_MEMORY;
@@ -168,11 +203,14 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   h->cfg = *cfg;
   h->var = var;
   h->svar = svar;
+  h->tvar = tvar;
   h->ctrl = nullptr;
   h->lay = make_layout(cfg);
   h->n_seq = cfg->batch * cfg->heads;
   h->nchunks = (cfg->seq_len + cfg->chunk - 1) / cfg->chunk;
-  h->coef_stride = var ? coef_stride(var->bc, var->wp) : coef_stride(svar->bc, svar->wp, true);
+  h->coef_stride = var ? coef_stride(var->bc, var->wp)
+                 : svar ? coef_stride(svar->bc, svar->wp, true)
+                        : coef_stride(tvar->bc, tvar->wp, true);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { delete h; return hip_fail(e); }
   h->ws = nullptr;
@@ -180,7 +218,9 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   h->ev_before = h->ev_after = nullptr;
   // sharded: exchange buffers per sequence, then the control words
   const size_t ctrl_off = svar ? align_up(svar->xbytes() * (size_t)h->n_seq, 256) : 0;
-  const size_t ws_bytes = var ? var->ws_bytes * (size_t)h->n_seq : ctrl_off + align_up((1 + (size_t)h->n_seq) * 4, 256);
+  const size_t ws_bytes = var    ? var->ws_bytes * (size_t)h->n_seq
+                          : svar ? ctrl_off + align_up((1 + (size_t)h->n_seq) * 4, 256)
+                                 : 0;   // streamed: the coefficient blocks only
   const size_t coef_bytes = (size_t)h->n_seq * h->nchunks * h->coef_stride * sizeof(float);
   if (ws_bytes && hipMalloc(&h->ws, ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -269,7 +309,7 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
   kp.seq_stride = h->lay.seq_stride;
   kp.off_count = h->lay.count;
 
-  if (h->svar) {
+  if (h->svar || h->tvar) {
     ShardedParams sp;
     sp.q = q;
     sp.k = k;
@@ -296,7 +336,7 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
     sp.momentum = c.momentum;
     sp.bias = c.bias;
     sp.residual = c.mlp_residual;
-    e = h->svar->launch(sp, kp, (hipStream_t)stream, h->ev_before, h->ev_after);
+    e = (h->svar ? h->svar->launch : h->tvar->launch)(sp, kp, (hipStream_t)stream, h->ev_before, h->ev_after);
     if (e != hipSuccess) return hip_fail(e);
     return ATLAS_OK;
   }

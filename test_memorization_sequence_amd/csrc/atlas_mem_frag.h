@@ -1,0 +1,92 @@
+// atlas_mem_frag.h -- MFMA operand helpers of the MLP kernels (device code).
+//
+// gfx950 v_mfma_f32_16x16x32_bf16: for both operands lane l supplies row
+// (l & 15) and the eight k values 8*(l >> 4) .. +7; the 16x16 fp32 result
+// gives lane l the column (l & 15) and rows 4*(l >> 4) + r, r = 0..3.
+//
+// "perm32" k order.  Two result tiles stacked along a 32-wide block of a
+// contraction dimension hold, for lane group g = l >> 4, the indices
+// {4g..4g+3} U {16+4g..16+4g+3}.  Used as an operand in that permuted k order
+// they need no data movement; the other operand is then read in the same
+// order (ld_perm, ld_tr_perm).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "atlas_mem_internal.h"
+#include "atlas_mem_gelu.h"
+
+namespace atlas {
+namespace mfma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row-major operand (k contiguous), natural k order: lane reads k0+8g .. +7 of row row0 + (l & 15).
+__device__ __forceinline__ bf16x8 ld_nat(const bf16* base, int ld, int row0, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+// Row-major operand, perm32 k order: k0+4g .. +3, then k0+16+4g .. +3.
+__device__ __forceinline__ bf16x8 ld_perm(const bf16* base, int ld, int row0, int k0, int lane) {
+  const bf16* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// Natural order, element i scaled by s[k0 + 8g + i].
+__device__ __forceinline__ bf16x8 ld_nat_scaled(const bf16* base, int ld, int row0, int k0, int lane, const float* s) {
+  const bf16x8 v = ld_nat(base, ld, row0, k0, lane);
+  const float* sc = s + k0 + 8 * (lane >> 4);
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)((float)v[i] * sc[i]);
+  return r;
+}
+// Every element scaled by one factor.
+__device__ __forceinline__ bf16x8 scaled(const bf16x8& v, float s) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)((float)v[i] * s);
+  return r;
+}
+// Two stacked result tiles -> perm32 operand.
+__device__ __forceinline__ bf16x8 tiles_to_frag(const f32x4& lo, const f32x4& hi) {
+  return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3], (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+}
+
+// Transposed reads from LDS (ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane s addresses row (s >> 2) and columns 4*(s & 3) .. +3 of a 4x16
+// block of a k-major matrix M[k][n]; the instruction returns to lane s the
+// column n = s, rows 0..3.  Two such reads give the operand of row
+// n0 + (l & 15) of the transposed matrix, so M needs no transposed copy.
+__device__ __forceinline__ i16x4 tr4(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// M[k][n] (n contiguous, row stride ld): operand row n0 + (l & 15), natural k order.
+__device__ __forceinline__ bf16x8 ld_tr_nat(const bf16* M, int ld, int n0, int k0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const bf16* p = M + (k0 + 8 * g + (s >> 2)) * ld + n0 + 4 * (s & 3);
+  return join(tr4(p), tr4(p + 4 * ld));
+}
+// Same, perm32 k order.
+__device__ __forceinline__ bf16x8 ld_tr_perm(const bf16* M, int ld, int n0, int k0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const bf16* p = M + (k0 + 4 * g + (s >> 2)) * ld + n0 + 4 * (s & 3);
+  return join(tr4(p), tr4(p + 16 * ld));
+}
+
+}  // namespace mfma
+}  // namespace atlas

@@ -44,6 +44,7 @@
 
 #include "atlas_mem_internal.h"
 #include "atlas_mem_coeff.h"
+#include "atlas_mem_gelu.h"
 
 namespace atlas {
 
@@ -56,10 +57,6 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
 
-__device__ __forceinline__ float gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
-__device__ __forceinline__ float gelu_prime(float z) {
-  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * expf(-0.5f * z * z) * 0.39894228040143268f;
-}
 
 // ----------------------------------------------------------------------------- MFMA
 template <typename T> struct Mma;

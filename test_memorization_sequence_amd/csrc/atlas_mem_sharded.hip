@@ -40,47 +40,12 @@
 
 #include "atlas_mem_internal.h"
 #include "atlas_mem_coeff.h"
+#include "atlas_mem_frag.h"
 
 namespace atlas {
 namespace sharded {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float gelu(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
-__device__ __forceinline__ float gelu_prime(float z) {
-  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * expf(-0.5f * z * z) * 0.39894228040143268f;
-}
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// natural k order: lane (row l&15, group g) reads k0+8g .. k0+8g+7
-__device__ __forceinline__ bf16x8 ld_nat(const bf16* base, int ld, int row0, int k0, int lane) {
-  return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
-}
-// perm32 k order: k0+4g .. +3, then k0+16+4g .. +3
-__device__ __forceinline__ bf16x8 ld_perm(const bf16* base, int ld, int row0, int k0, int lane) {
-  const bf16* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-// natural order, element i scaled by s[k0 + 8g + i]
-__device__ __forceinline__ bf16x8 ld_nat_scaled(const bf16* base, int ld, int row0, int k0, int lane, const float* s) {
-  const bf16x8 v = ld_nat(base, ld, row0, k0, lane);
-  const float* sc = s + k0 + 8 * (lane >> 4);
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)((float)v[i] * sc[i]);
-  return r;
-}
-// two stacked result tiles -> perm32 operand
-__device__ __forceinline__ bf16x8 tiles_to_frag(const f32x4& lo, const f32x4& hi) {
-  return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3], (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
-}
+using namespace mfma;
 
 // ----------------------------------------------------------------------------- group barrier
 // Monotonic arrival counter per group; barrier number `k` (1, 2, ...) waits

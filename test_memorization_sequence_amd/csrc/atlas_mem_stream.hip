@@ -1,0 +1,727 @@
+// atlas_mem_stream.hip -- MLP memory, one workgroup per sequence, the fp32
+// weights and momentum streamed through the workgroup once per chunk.
+//
+// Method (as in atlas_mem_kernels.hip): per chunk of BC tokens, gradients of
+// the Omega-rule window loss (ATLAS review sec. 3.2-3.3) at the chunk-start
+// weights, folded into momentum and decay (Titans review sec. 3.1) through the
+// gate coefficients A_t, B_t, C_{t,i}, cM_i, cS_i, P, and the retrieval
+// y_t = f_{W_t}(q_t) with the per-token weights (Titans review sec. 3.1,
+// "Retrieving a Memory").  Per chunk, with X the window keys, Xq the queries:
+//   Z = X W1^T, A = gelu(Z), D2 = s*gamma*(x + A W2^T - v)         (l2 bias)
+//   D1 = (D2 W2) .* gelu'(Z)
+//   Zq = A_q Xq W1^T + B_q Xq S1^T - Q1 D1,  Ah = gelu(Zq),  Q1 = C .* Xq X^T
+//   y  = q + A_q Ah W2^T + B_q Ah S2^T - (C .* Ah A^T) D2
+//   W1 <- a W1 + b S1 - (cM .* D1)^T X,   S1 <- P S1 - (cS .* D1)^T X
+//   W2 <- a W2 + b S2 - D2^T (cM .* A),   S2 <- P S2 - D2^T (cS .* A)
+//
+// Work split.  The hidden units are visited in super tiles of HJ = 64; wave w
+// owns units 16w..16w+15 of the tile for everything indexed by hidden unit
+// (Z, D1, Zq, the W1/S1 rows) and value rows DVW*w .. +DVW for everything
+// indexed by value row (the W2/S2 rows, the sums A W2^T and Ah W2^T, the
+// output).  One pass over the super tiles per chunk reads and writes the
+// state once; it also runs the NEXT chunk's forward (Z' = X' W1'^T and its
+// sum A' W2'^T) on each tile right after the tile's update, so the next
+// chunk's D2 is ready when the pass ends and no second pass is needed.  The
+// cross-tile sums (A' W2'^T, Ah W2^T, Ah A^T) stay in registers.
+//
+// The state tiles use the register layout of MFMA result tiles; as operands
+// they are read in perm32 order (atlas_mem_frag.h).  Transposed operands are
+// read from LDS with ds_read_b64_tr_b16, so every LDS matrix is stored once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "atlas_mem_internal.h"
+#include "atlas_mem_coeff.h"
+#include "atlas_mem_frag.h"
+
+namespace atlas {
+namespace streamed {
+
+using namespace mfma;
+
+template <int D_, int DV_, int H_, int WP_, int BC_>
+struct TShape {
+  static constexpr int D = D_, DV = DV_, H = H_, WP = WP_, BC = BC_;
+  static constexpr int NW = 4;                 // waves per workgroup
+  static constexpr int HJ = 16 * NW;           // hidden units per super tile
+  static constexpr int NJ = H / HJ;            // super tiles
+  static constexpr int DVW = DV / NW;          // value rows per wave
+  static constexpr int NDT = DVW / 16;
+  static constexpr int ND = D / 16;
+  static constexpr int NT = WP / 16;           // window token tiles
+  static constexpr int NQ = BC / 16;           // query tiles
+  static constexpr int NU = HJ / 16;           // unit tiles per super tile
+  static_assert(H % HJ == 0 && DVW % 16 == 0 && D % 32 == 0 && WP % 32 == 0 && BC % 32 == 0, "tiles");
+  // LDS row strides in bf16 elements (multiples of 8: 16-byte aligned rows)
+  static constexpr int LX = D + 8, LV = DV + 8, LT = WP + 8, LH = HJ + 8, LQ = BC + 4, L1Q = WP + 4;
+  static constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+  //   Xa, Xb : window keys of this chunk and the next [WP][LX] (ping-pong)
+  //   Xq     : queries [BC][LX];  Q1 [BC][L1Q] (read 8 bytes at a time);  D2 [WP][LV]
+  //   AT     : A^T of the super tile [HJ][LT];  at the end of a pass Q2^T [WP][LQ]
+  //   W2     : bf16 image W2^T [DV][LH];  after its use the next chunk's A' [WP][LH]
+  //   Ah     : retrieval activations of the super tile [BC][LH]
+  //   Cm     : the weights C_{t,i} of the chunk, bf16 [BC][WP]
+  static constexpr size_t szX = align_up((size_t)WP * LX * 2, 256);
+  static constexpr size_t oXa = 0, oXb = oXa + szX, oXq = oXb + szX;
+  static constexpr size_t oQ1 = oXq + align_up((size_t)BC * LX * 2, 256);
+  static constexpr size_t oD2 = oQ1 + align_up((size_t)BC * L1Q * 2, 256);
+  static constexpr size_t oAT = oD2 + align_up((size_t)WP * LV * 2, 256);
+  static constexpr size_t oW2 = oAT + align_up(mx((size_t)HJ * LT, (size_t)WP * LQ) * 2, 256);
+  static constexpr size_t oAh = oW2 + align_up(mx((size_t)DV * LH, (size_t)WP * LH) * 2, 256);
+  static constexpr size_t oCm = oAh + align_up((size_t)BC * LH * 2, 256);  // C [BC][WP] (bf16)
+  static constexpr size_t oF = oCm + align_up((size_t)BC * WP * 2, 256);   // cA, cB, cM, cS, P, sg
+  static constexpr size_t lds = oF + (2 * BC + 3 * WP + 4) * 4;   // + s*gamma of the window rows
+  static_assert(lds <= 163840, "LDS budget of one CU");
+  // state lines (128 B) of one super tile: W1/S1 rows, W2/S2 columns
+  static constexpr int L1 = HJ * D / 32, L2 = DV * (HJ / 32);
+};
+
+template <class S>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+stream_mlp_kernel(ShardedParams p) {
+  constexpr int D = S::D, DV = S::DV, H = S::H, WP = S::WP, BC = S::BC;
+  constexpr int HJ = S::HJ, NJ = S::NJ, NDT = S::NDT, ND = S::ND, NT = S::NT, NQ = S::NQ, NU = S::NU;
+  constexpr int LX = S::LX, LV = S::LV, LT = S::LT, LH = S::LH, LQ = S::LQ, L1Q = S::L1Q;
+  constexpr int oCM = 2 * BC + 4, oCS = oCM + WP, oCC = oCS + WP, oQ1g = oCC + BC * WP;
+  extern __shared__ __attribute__((aligned(256))) char smem[];
+
+  const int seq = blockIdx.x;
+  if (seq >= p.n_seq) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int N = p.N, c = p.c, W = BC + c - 1;
+  const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
+  const float s_grad = p.grad_scale;
+
+  char* st = p.state + (size_t)seq * p.seq_stride;
+  float* W1g = reinterpret_cast<float*>(st + p.off_weights);
+  float* W2g = W1g + (size_t)H * D;
+  float* S1g = reinterpret_cast<float*>(st + p.off_momentum);
+  float* S2g = S1g + (size_t)H * D;
+  float* hk = reinterpret_cast<float*>(st + p.off_halo_k);
+  float* hv = reinterpret_cast<float*>(st + p.off_halo_v);
+  float* hg = reinterpret_cast<float*>(st + p.off_halo_g);
+  int64_t* cnt = reinterpret_cast<int64_t*>(st + p.off_count);
+  const int halo_valid = (int)min<int64_t>(*cnt, (int64_t)(c - 1));
+  const bf16* q = reinterpret_cast<const bf16*>(p.q) + (size_t)seq * N * D;
+  const bf16* k = reinterpret_cast<const bf16*>(p.k) + (size_t)seq * N * D;
+  const bf16* v = reinterpret_cast<const bf16*>(p.v) + (size_t)seq * N * DV;
+  bf16* out = reinterpret_cast<bf16*>(p.out) + (size_t)seq * N * DV;
+  const float* gam_in = p.gamma + (size_t)seq * N;
+  const float* coef_seq = p.coef + (size_t)seq * p.nchunks * p.coef_stride;
+
+  bf16* Xc = reinterpret_cast<bf16*>(smem + S::oXa);   // window keys of the current chunk
+  bf16* Xn = reinterpret_cast<bf16*>(smem + S::oXb);   // ... and of the next one
+  bf16* Xq = reinterpret_cast<bf16*>(smem + S::oXq);
+  bf16* Q1 = reinterpret_cast<bf16*>(smem + S::oQ1);
+  bf16* D2 = reinterpret_cast<bf16*>(smem + S::oD2);
+  bf16* AT = reinterpret_cast<bf16*>(smem + S::oAT);
+  bf16* Q2T = AT;
+  bf16* W2L = reinterpret_cast<bf16*>(smem + S::oW2);
+  bf16* An = W2L;
+  bf16* Ah = reinterpret_cast<bf16*>(smem + S::oAh);
+  bf16* Cm = reinterpret_cast<bf16*>(smem + S::oCm);
+  float* cA = reinterpret_cast<float*>(smem + S::oF);
+  float* cB = cA + BC;
+  float* cM = cB + BC;
+  float* cS = cM + WP;
+  float* cP = cS + WP;
+  float* sgw = cP + 4;   // s * gamma of the window rows (0 outside the window)
+
+  const int dvw = S::DVW * wave;
+  const int nchunks = (N + BC - 1) / BC;
+
+  // token i (relative to the call start) of window row w, and its validity
+  auto row_ok = [&](int w, int t0, int te) {
+    const int i = t0 - (c - 1) + w;
+    return w < W && i >= -halo_valid && i <= te;
+  };
+
+  // Inputs of a chunk are moved in two halves: the loads into registers
+  // (issued early, so their latency overlaps other work), then the LDS stores.
+  // HALO = false for chunks >= 1, whose windows never reach before the call.
+  constexpr int NXV = (WP * (D / 8) + 255) / 256;   // window key vectors per thread
+  constexpr int NQV = (BC * (D / 8) + 255) / 256;   // query vectors per thread
+  constexpr int NQ1V = (BC * WP / 8 + 255) / 256;   // Q1 vectors per thread
+  constexpr int NCV = (BC * WP / 4 + 255) / 256;    // C float4 per thread
+  struct WinRegs { bf16x8 x[NXV]; };
+  struct ChunkRegs { bf16x8 q[NQV], q1[NQ1V]; f32x4 cc[NCV]; float ca, cb, cm, cs, cp, sg; };
+  struct D2Regs { bf16 vv[NT][4][NDT]; };
+
+  // window keys of chunk ch (halo rows from the state, invalid rows zero)
+  auto load_window = [&](int ch, WinRegs& R, auto halo_tag) {
+    constexpr bool HALO = decltype(halo_tag)::value;
+    const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
+#pragma unroll
+    for (int u = 0; u < NXV; ++u) {
+      const int e = tid + 256 * u, w = e / (D / 8), d8 = (e % (D / 8)) * 8, i = t0 - (c - 1) + w;
+      const bool ok = (WP * (D / 8) % 256 == 0 || e < WP * (D / 8)) && row_ok(w, t0, te);
+      if (HALO) {
+#pragma unroll
+        for (int z = 0; z < 8; ++z) R.x[u][z] = (bf16)0.f;
+        if (ok) {
+          if (i >= 0) R.x[u] = *reinterpret_cast<const bf16x8*>(k + (size_t)i * D + d8);
+          else
+#pragma unroll
+            for (int z = 0; z < 8; ++z) R.x[u][z] = (bf16)hk[(c - 1 + i) * D + d8 + z];
+        }
+      } else {
+        // branch-free: a clamped (always valid) row, then a select
+        const unsigned ic = (unsigned)min(max(i, 0), N - 1);
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(k + ic * D + d8);
+        bf16x8 zz;
+#pragma unroll
+        for (int z = 0; z < 8; ++z) zz[z] = (bf16)0.f;
+        R.x[u] = ok ? x : zz;
+      }
+    }
+  };
+  auto store_window = [&](bf16* Xdst, const WinRegs& R) {
+#pragma unroll
+    for (int u = 0; u < NXV; ++u) {
+      const int e = tid + 256 * u;
+      if (e < WP * (D / 8)) *reinterpret_cast<bf16x8*>(Xdst + (e / (D / 8)) * LX + (e % (D / 8)) * 8) = R.x[u];
+    }
+  };
+
+  // queries, Q1, the weights C, the gate coefficients and s*gamma of the
+  // window rows of chunk ch
+  auto load_chunk = [&](int ch, ChunkRegs& R, auto halo_tag) {
+    constexpr bool HALO = decltype(halo_tag)::value;
+    const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
+    const float* coef = coef_seq + (size_t)ch * p.coef_stride;
+#pragma unroll
+    for (int u = 0; u < NQV; ++u) {
+      const int e = tid + 256 * u, n = e / (D / 8), d8 = (e % (D / 8)) * 8;
+      const bool ok = (BC * (D / 8) % 256 == 0 || e < BC * (D / 8)) && t0 + n <= te;
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(q + (unsigned)min(t0 + n, N - 1) * D + d8);
+      bf16x8 zz;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) zz[z] = (bf16)0.f;
+      R.q[u] = ok ? x : zz;
+    }
+    const bf16* q1g = reinterpret_cast<const bf16*>(coef + oQ1g);
+#pragma unroll
+    for (int u = 0; u < NQ1V; ++u) {
+      const int e = tid + 256 * u;
+      if (e < BC * WP / 8) R.q1[u] = *reinterpret_cast<const bf16x8*>(q1g + 8 * e);
+    }
+#pragma unroll
+    for (int u = 0; u < NCV; ++u) {
+      const int e = tid + 256 * u;
+      if (e < BC * WP / 4) R.cc[u] = *reinterpret_cast<const f32x4*>(coef + oCC + 4 * e);
+    }
+    R.ca = tid < BC ? coef[tid] : 0.f;
+    R.cb = tid < BC ? coef[BC + tid] : 0.f;
+    R.cm = tid < WP ? coef[oCM + tid] : 0.f;
+    R.cs = tid < WP ? coef[oCS + tid] : 0.f;
+    R.cp = coef[2 * BC];
+    {
+      const int i = t0 - (c - 1) + tid;
+      const bool ok = tid < WP && row_ok(tid, t0, te);
+      if (HALO) R.sg = ok ? s_grad * (i >= 0 ? gam_in[i] : hg[c - 1 + i]) : 0.f;
+      else R.sg = ok ? s_grad * gam_in[(unsigned)min(max(i, 0), N - 1)] : 0.f;
+    }
+  };
+  auto store_chunk = [&](const ChunkRegs& R) {
+#pragma unroll
+    for (int u = 0; u < NQV; ++u) {
+      const int e = tid + 256 * u;
+      if (e < BC * (D / 8)) *reinterpret_cast<bf16x8*>(Xq + (e / (D / 8)) * LX + (e % (D / 8)) * 8) = R.q[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NQ1V; ++u) {
+      const int e = tid + 256 * u;
+      if (e < BC * WP / 8) {
+        const bf16x8 x = R.q1[u];
+        bf16* d = Q1 + (8 * e / WP) * L1Q + (8 * e) % WP;
+        *reinterpret_cast<bf16x4*>(d) = bf16x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<bf16x4*>(d + 4) = bf16x4{x[4], x[5], x[6], x[7]};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NCV; ++u) {
+      const int e = tid + 256 * u;
+      const f32x4 cv = R.cc[u];
+      if (e < BC * WP / 4) *reinterpret_cast<bf16x4*>(Cm + 4 * e) = bf16x4{(bf16)cv[0], (bf16)cv[1], (bf16)cv[2], (bf16)cv[3]};
+    }
+    if (tid < BC) { cA[tid] = R.ca; cB[tid] = R.cb; }
+    if (tid < WP) { cM[tid] = R.cm; cS[tid] = R.cs; }
+    if (tid == 0) cP[0] = R.cp;
+    if (tid < WP) sgw[tid] = R.sg;
+  };
+
+  // D2 of chunk ch from the sums yh = A W2^T of its window (Xw: its window keys)
+  f32x4 yh[NT][NDT];
+  auto load_d2 = [&](int ch, D2Regs& R, auto halo_tag) {
+    constexpr bool HALO = decltype(halo_tag)::value;
+    const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int w = 16 * m + 4 * g + r, i = t0 - (c - 1) + w;
+        const bool ok = row_ok(w, t0, te);
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          const int o = dvw + 16 * bb + c16;
+          if (HALO) {
+            R.vv[m][r][bb] = !ok ? (bf16)0.f : i >= 0 ? v[(size_t)i * DV + o] : (bf16)hv[(c - 1 + i) * DV + o];
+          } else {
+            const bf16 x = v[(unsigned)min(max(i, 0), N - 1) * DV + o];
+            R.vv[m][r][bb] = ok ? x : (bf16)0.f;
+          }
+        }
+      }
+  };
+  // needs sgw of chunk ch in LDS
+  auto finish_d2 = [&](int ch, const D2Regs& R, const bf16* Xw, auto halo_tag) {
+    constexpr bool HALO = decltype(halo_tag)::value;
+    const int t0 = ch * BC;
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int w = 16 * m + 4 * g + r, i = t0 - (c - 1) + w;
+        const float sg = sgw[w];
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          const int o = dvw + 16 * bb + c16;
+          const float vv = (float)R.vv[m][r][bb];
+          float val;
+          if (dot) {
+            val = -sg * vv;
+          } else {
+            // rows outside the window have sg = 0
+            const float rr = !res ? 0.f : !HALO || i >= 0 || sg == 0.f ? (float)Xw[w * LX + o] : hk[(c - 1 + i) * D + o];
+            val = sg * (rr + yh[m][bb][r] - vv);
+          }
+          D2[w * LV + o] = (bf16)val;
+        }
+      }
+  };
+
+  // state tiles of super tile J (see the layout notes at the top): uniform
+  // tile base + one lane offset + a compile-time offset per tile
+  const int l1 = (16 * wave + c16) * D + 4 * g, l2 = (dvw + c16) * H + 4 * g;
+  auto w1_at = [&](int J, int t) { return J * HJ * D + l1 + 16 * t; };
+  auto w2_at = [&](int J, int a, int bb) { return J * HJ + l2 + 16 * bb * H + 16 * a; };
+
+  // L2 prefetch of super tile J's state: one 4-byte load per 128-byte line,
+  // kept in registers until the end of the current tile so nothing waits on it
+  unsigned sink = 0;
+  constexpr int NP1 = (S::L1 + 255) / 256, NP2 = (S::L2 + 255) / 256, NPF = 2 * NP1 + 2 * NP2;
+  auto touch_state = [&](int J, unsigned (&pf)[NPF]) {
+    const float* w1 = W1g + J * HJ * D;
+    const float* s1 = S1g + J * HJ * D;
+    const float* w2 = W2g + J * HJ;
+    const float* s2 = S2g + J * HJ;
+#pragma unroll
+    for (int u = 0; u < NP1; ++u) {
+      const int L = tid + 256 * u;
+      const bool ok = S::L1 % 256 == 0 || L < S::L1;
+      pf[u] = ok ? *reinterpret_cast<const unsigned*>(w1 + 32 * L) : 0u;
+      pf[NP1 + u] = ok && mom ? *reinterpret_cast<const unsigned*>(s1 + 32 * L) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < NP2; ++u) {
+      const int L = tid + 256 * u, o = (L / (HJ / 32)) * H + 32 * (L % (HJ / 32));
+      const bool ok = S::L2 % 256 == 0 || L < S::L2;
+      pf[2 * NP1 + u] = ok ? *reinterpret_cast<const unsigned*>(w2 + o) : 0u;
+      pf[2 * NP1 + NP2 + u] = ok && mom ? *reinterpret_cast<const unsigned*>(s2 + o) : 0u;
+    }
+  };
+
+  // ---- prologue: inputs of chunk 0 (and the keys of chunk 1), then chunk 0's forward
+  if (nchunks > 0) {
+    WinRegs w0, w1;
+    ChunkRegs c0;
+    D2Regs d0;
+    load_window(0, w0, std::true_type{});
+    if (nchunks > 1) load_window(1, w1, std::false_type{});
+    load_chunk(0, c0, std::true_type{});
+    load_d2(0, d0, std::true_type{});
+    store_window(Xc, w0);
+    if (nchunks > 1) store_window(Xn, w1);
+    store_chunk(c0);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) yh[m][bb] = zero4();
+    for (int J = 0; J < NJ; ++J) {
+      f32x4 W1T[ND], W2T[NU][NDT];
+#pragma unroll
+      for (int t = 0; t < ND; ++t) W1T[t] = *reinterpret_cast<const f32x4*>(W1g + w1_at(J, t));
+#pragma unroll
+      for (int a = 0; a < NU; ++a)
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) W2T[a][bb] = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
+      f32x4 z[NT];
+#pragma unroll
+      for (int m = 0; m < NT; ++m) z[m] = zero4();
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const bf16x8 aw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
+#pragma unroll
+        for (int m = 0; m < NT; ++m) z[m] = mma(aw, ld_perm(Xc, LX, 16 * m, 32 * s, lane), z[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        bf16x4 a4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a4[r] = (bf16)gelu(z[m][r]);
+        *reinterpret_cast<bf16x4*>(An + (16 * m + c16) * LH + 16 * wave + 4 * g) = a4;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < HJ / 32; ++s)
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          const bf16x8 bw = tiles_to_frag(W2T[2 * s][bb], W2T[2 * s + 1][bb]);
+#pragma unroll
+          for (int m = 0; m < NT; ++m) yh[m][bb] = mma(ld_perm(An, LH, 16 * m, 32 * s, lane), bw, yh[m][bb]);
+        }
+      __syncthreads();
+    }
+    finish_d2(0, d0, Xc, std::true_type{});
+    __syncthreads();
+  }
+
+  // ---- one pass over the super tiles per chunk
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int t0 = ch * BC, te = min(N, t0 + BC) - 1, ce = te - t0;
+    const bool more = ch + 1 < nchunks;
+    const float Ate = cA[ce], Bte = cB[ce], Pc = cP[0];
+    f32x4 yo[NQ][NDT], q2[NT];
+#pragma unroll
+    for (int m = 0; m < NQ; ++m)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) yo[m][bb] = zero4();
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      q2[m] = zero4();
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) yh[m][bb] = zero4();
+    }
+
+    for (int J = 0; J < NJ; ++J) {
+      // ======== W1 side: W1/S1 in registers, W2 only long enough for its bf16 image
+      unsigned pf[NPF];
+      touch_state(J + 1 < NJ ? J + 1 : 0, pf);
+      f32x4 W1T[ND], S1T[ND];
+#pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        W1T[t] = *reinterpret_cast<const f32x4*>(W1g + w1_at(J, t));
+        S1T[t] = mom ? *reinterpret_cast<const f32x4*>(S1g + w1_at(J, t)) : zero4();
+      }
+      // ---- bf16 image W2^T [dv][unit] of the tile (this wave's value rows)
+#pragma unroll
+      for (int a = 0; a < NU; ++a)
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
+          *reinterpret_cast<bf16x4*>(W2L + (dvw + 16 * bb + c16) * LH + 16 * a + 4 * g) =
+              bf16x4{(bf16)w[0], (bf16)w[1], (bf16)w[2], (bf16)w[3]};
+        }
+      // ---- Z = X W1^T [tok x 16 units]; A -> AT [unit][tok]; z keeps gelu'(Z)
+      f32x4 z[NT];
+#pragma unroll
+      for (int m = 0; m < NT; ++m) z[m] = zero4();
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {
+        const bf16x8 bw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
+#pragma unroll
+        for (int m = 0; m < NT; ++m) z[m] = mma(ld_perm(Xc, LX, 16 * m, 32 * s, lane), bw, z[m]);
+      }
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        bf16x4 a4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a, da;
+          gelu_and_prime(z[m][r], a, da);
+          a4[r] = (bf16)a;
+          z[m][r] = da;
+        }
+        *reinterpret_cast<bf16x4*>(AT + (16 * wave + c16) * LT + 16 * m + 4 * g) = a4;
+      }
+      __syncthreads();   // W2 image, AT
+
+      // ---- D1 = (D2 W2) .* gelu'(Z) [tok x 16 units], then perm32 operands over tokens
+      bf16x8 fd[NT / 2], fm[NT / 2], fs[NT / 2];
+      {
+        f32x4 d1[NT];
+#pragma unroll
+        for (int m = 0; m < NT; ++m) d1[m] = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DV; k0 += 32) {
+          const bf16x8 bw = ld_tr_nat(W2L, LH, 16 * wave, k0, lane);
+#pragma unroll
+          for (int m = 0; m < NT; ++m) d1[m] = mma(ld_nat(D2, LV, 16 * m, k0, lane), bw, d1[m]);
+        }
+#pragma unroll
+        for (int s = 0; s < NT / 2; ++s)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tl = 32 * s + 4 * g + r, th = tl + 16;
+            const float lo = d1[2 * s][r] * z[2 * s][r], hi = d1[2 * s + 1][r] * z[2 * s + 1][r];
+            fd[s][r] = (bf16)(-lo);
+            fd[s][4 + r] = (bf16)(-hi);
+            fm[s][r] = (bf16)(lo * cM[tl]);
+            fm[s][4 + r] = (bf16)(hi * cM[th]);
+            fs[s][r] = (bf16)(lo * cS[tl]);
+            fs[s][4 + r] = (bf16)(hi * cS[th]);
+          }
+      }
+
+      // ---- Zq^T = W1 (A_q Xq)^T + S1 (B_q Xq)^T - D1^T Q1^T [16 units x q]; Ah = gelu
+      {
+        f32x4 zq[NQ];
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) zq[m] = zero4();
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+          const bf16x8 aw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
+          const bf16x8 as = tiles_to_frag(S1T[2 * s], S1T[2 * s + 1]);
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) {
+            const bf16x8 xb = ld_perm(Xq, LX, 16 * m, 32 * s, lane);
+            zq[m] = mma(aw, scaled(xb, cA[16 * m + c16]), zq[m]);
+            if (mom) zq[m] = mma(as, scaled(xb, cB[16 * m + c16]), zq[m]);
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < NT / 2; ++s)
+#pragma unroll
+          for (int m = 0; m < NQ; ++m) zq[m] = mma(fd[s], ld_perm(Q1, L1Q, 16 * m, 32 * s, lane), zq[m]);
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+          bf16x4 h4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h4[r] = (bf16)gelu(zq[m][r]);
+          *reinterpret_cast<bf16x4*>(Ah + (16 * m + c16) * LH + 16 * wave + 4 * g) = h4;
+        }
+      }
+
+      // ---- W1/S1 update [d x 16 units]; written back at once
+#pragma unroll
+      for (int t = 0; t < ND; ++t) {
+        f32x4 um = zero4(), us = zero4();
+#pragma unroll
+        for (int s = 0; s < NT / 2; ++s) {
+          const bf16x8 xa = ld_tr_perm(Xc, LX, 16 * t, 32 * s, lane);
+          um = mma(xa, fm[s], um);
+          if (mom) us = mma(xa, fs[s], us);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float w1 = W1T[t][r], s1 = S1T[t][r];
+          W1T[t][r] = Ate * w1 + Bte * s1 - um[r];
+          S1T[t][r] = Pc * s1 - us[r];
+        }
+        *reinterpret_cast<f32x4*>(W1g + w1_at(J, t)) = W1T[t];
+        if (mom) *reinterpret_cast<f32x4*>(S1g + w1_at(J, t)) = S1T[t];
+      }
+      __syncthreads();   // Ah complete; every wave is done with the W2 image
+
+      // ---- next chunk's forward on the updated rows: A' = gelu(X' W1'^T) -> An [tok][unit]
+      if (more) {
+        f32x4 z1[NT];
+#pragma unroll
+        for (int m = 0; m < NT; ++m) z1[m] = zero4();
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+          const bf16x8 aw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
+#pragma unroll
+          for (int m = 0; m < NT; ++m) z1[m] = mma(aw, ld_perm(Xn, LX, 16 * m, 32 * s, lane), z1[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+          bf16x4 a4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a4[r] = (bf16)gelu(z1[m][r]);
+          *reinterpret_cast<bf16x4*>(An + (16 * m + c16) * LH + 16 * wave + 4 * g) = a4;
+        }
+      }
+
+      // ======== W2 side: W2/S2 (this wave's value rows) back from L2
+      f32x4 W2T[NU][NDT], S2T[NU][NDT];
+#pragma unroll
+      for (int a = 0; a < NU; ++a)
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          W2T[a][bb] = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
+          S2T[a][bb] = mom ? *reinterpret_cast<const f32x4*>(S2g + w2_at(J, a, bb)) : zero4();
+        }
+      // ---- Q2 partial: Ah A^T, this wave's 16 query rows [q x tok]
+#pragma unroll
+      for (int k0 = 0; k0 < HJ; k0 += 32) {
+        const bf16x8 ah = ld_nat(Ah, LH, 16 * wave, k0, lane);
+#pragma unroll
+        for (int m = 0; m < NT; ++m) q2[m] = mma(ah, ld_tr_nat(AT, LT, 16 * m, k0, lane), q2[m]);
+      }
+      // ---- output partial: A_q Ah W2^T + B_q Ah S2^T [q x this wave's dv]
+#pragma unroll
+      for (int s = 0; s < HJ / 32; ++s) {
+        bf16x8 bw[NDT], bs[NDT];
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          bw[bb] = tiles_to_frag(W2T[2 * s][bb], W2T[2 * s + 1][bb]);
+          bs[bb] = tiles_to_frag(S2T[2 * s][bb], S2T[2 * s + 1][bb]);
+        }
+#pragma unroll
+        for (int m = 0; m < NQ; ++m) {
+          const bf16x8 ah = ld_perm(Ah, LH, 16 * m, 32 * s, lane);
+          const bf16x8 ha = scaled(ah, cA[16 * m + c16]);
+          const bf16x8 hb = scaled(ah, cB[16 * m + c16]);
+#pragma unroll
+          for (int bb = 0; bb < NDT; ++bb) {
+            yo[m][bb] = mma(ha, bw[bb], yo[m][bb]);
+            if (mom) yo[m][bb] = mma(hb, bs[bb], yo[m][bb]);
+          }
+        }
+      }
+      // ---- W2/S2 update [units x this wave's dv]; written back at once
+#pragma unroll
+      for (int a = 0; a < NU; ++a) {
+        bf16x8 am[NT / 2], as[NT / 2];
+#pragma unroll
+        for (int s = 0; s < NT / 2; ++s) {
+          am[s] = ld_nat_scaled(AT, LT, 16 * a, 32 * s, lane, cM);
+          as[s] = ld_nat_scaled(AT, LT, 16 * a, 32 * s, lane, cS);
+        }
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          f32x4 um = zero4(), us = zero4();
+#pragma unroll
+          for (int s = 0; s < NT / 2; ++s) {
+            const bf16x8 bd = ld_tr_nat(D2, LV, dvw + 16 * bb, 32 * s, lane);
+            um = mma(am[s], bd, um);
+            if (mom) us = mma(as[s], bd, us);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float w2 = W2T[a][bb][r], s2 = S2T[a][bb][r];
+            W2T[a][bb][r] = Ate * w2 + Bte * s2 - um[r];
+            S2T[a][bb][r] = Pc * s2 - us[r];
+          }
+          *reinterpret_cast<f32x4*>(W2g + w2_at(J, a, bb)) = W2T[a][bb];
+          if (mom) *reinterpret_cast<f32x4*>(S2g + w2_at(J, a, bb)) = S2T[a][bb];
+        }
+      }
+      // ---- next chunk's window sums A' W2'^T [tok x this wave's dv]
+      if (more) {
+        __syncthreads();   // An complete
+#pragma unroll
+        for (int s = 0; s < HJ / 32; ++s)
+#pragma unroll
+          for (int bb = 0; bb < NDT; ++bb) {
+            const bf16x8 bw = tiles_to_frag(W2T[2 * s][bb], W2T[2 * s + 1][bb]);
+#pragma unroll
+            for (int m = 0; m < NT; ++m) yh[m][bb] = mma(ld_perm(An, LH, 16 * m, 32 * s, lane), bw, yh[m][bb]);
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) sink ^= pf[u];
+      __syncthreads();
+    }
+
+    // ---- end of the pass.  The next chunk's inputs are requested first; they
+    // arrive while Q2 and the output rows are finished.
+    WinRegs wr;
+    ChunkRegs cr;
+    D2Regs dr;
+    if (more) {
+      load_d2(ch + 1, dr, std::false_type{});
+      load_chunk(ch + 1, cr, std::false_type{});
+      if (ch + 2 < nchunks) load_window(ch + 2, wr, std::false_type{});
+    }
+    // Q2 = C .* (Ah A^T) -> Q2^T [tok][q]
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      bf16x4 c4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c4[r] = (bf16)((float)Cm[(16 * wave + 4 * g + r) * WP + 16 * m + c16] * q2[m][r]);
+      *reinterpret_cast<bf16x4*>(Q2T + (16 * m + c16) * LQ + 16 * wave + 4 * g) = c4;
+    }
+    __syncthreads();
+    // y -= Q2 D2, then the output rows (+ the residual query)
+#pragma unroll
+    for (int m = 0; m < NQ; ++m)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < WP; k0 += 32)
+          acc = mma(ld_tr_nat(Q2T, LQ, 16 * m, k0, lane), ld_tr_nat(D2, LV, dvw + 16 * bb, k0, lane), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qq = 16 * m + 4 * g + r, o = dvw + 16 * bb + c16;
+          if (t0 + qq <= te) {
+            const float rr = res ? (float)Xq[qq * LX + o] : 0.f;
+            out[(size_t)(t0 + qq) * DV + o] = (bf16)(rr + yo[m][bb][r] - acc[r]);
+          }
+        }
+      }
+    __syncthreads();
+    if (more) {
+      store_chunk(cr);
+      if (ch + 2 < nchunks) store_window(Xc, wr);
+      __syncthreads();   // sgw of the next chunk
+      finish_d2(ch + 1, dr, Xn, std::false_type{});
+      bf16* tmp = Xc;
+      Xc = Xn;
+      Xn = tmp;
+      __syncthreads();
+    }
+  }
+
+  if (sink == 0x9e3779b9u && N < 0) out[0] = (bf16)0.f;   // keeps the prefetch loads
+  // ---- halo and count (every read of the old halo happened in the prologue)
+  if (tid < 64) {
+    for (int j = 0; j < c - 1; ++j) {
+      const int i = N - (c - 1) + j;
+      for (int d = lane; d < D; d += 64) hk[j * D + d] = i >= 0 ? (float)k[(size_t)i * D + d] : hk[(N + j) * D + d];
+      for (int o = lane; o < DV; o += 64) hv[j * DV + o] = i >= 0 ? (float)v[(size_t)i * DV + o] : hv[(N + j) * DV + o];
+      if (lane == 0) hg[j] = i >= 0 ? gam_in[i] : hg[N + j];
+    }
+    if (lane == 0) *cnt += N;
+  }
+}
+
+}  // namespace streamed
+
+template <int D, int DV, int H, int WP, int BC>
+hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
+                           hipEvent_t ev1) {
+  typedef streamed::TShape<D, DV, H, WP, BC> S;
+  if (sp.N == 0 || sp.n_seq == 0) return hipSuccess;
+  hipLaunchKernelGGL((coeff_kernel<BC, WP, D>), dim3((unsigned)kp.nchunks * (unsigned)sp.n_seq), dim3(256), 0,
+                     stream, kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  static bool attr_set = false;
+  if (!attr_set) {
+    // allow more than the default dynamic LDS; a refusal shows up at launch
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
+    (void)hipGetLastError();
+    attr_set = true;
+  }
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((streamed::stream_mlp_kernel<S>), dim3((unsigned)sp.n_seq), dim3(256), S::lds, stream, sp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC) \
+  template hipError_t launch_streamed<D, DV, H, WP, BC>(const ShardedParams&, const CoeffParams&, hipStream_t, \
+                                                        hipEvent_t, hipEvent_t);
+#include "atlas_mem_stream_variants.inc"
+#undef ATLAS_STREAMED
+
+}  // namespace atlas

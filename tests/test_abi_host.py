@@ -52,9 +52,10 @@ def test_enum_fields_are_checked():
     c = _cfg()
     c.grad_scale = float("nan")
     assert binding.supported(c) == binding.ERR_INVALID
-    c = _cfg()
-    c.kernel = 7
-    assert binding.supported(c) == binding.ERR_INVALID
+    for bad in (4, 7, -1):
+        c = _cfg()
+        c.kernel = bad
+        assert binding.supported(c) == binding.ERR_INVALID
 
 
 def test_kernel_family_selection():
@@ -66,6 +67,11 @@ def test_kernel_family_selection():
     assert binding.supported(binding.config_of(WORKLOADS["atlas_long"], "sharded")) == binding.ERR_UNSUPPORTED
     assert binding.supported(binding.config_of(WORKLOADS["linear_poly2"], "sharded")) == binding.ERR_UNSUPPORTED
     assert binding.supported(binding.config_of(WORKLOADS["atlas_long"], "auto")) == ok
+    # streamed-state family: the same shapes as the sharded one
+    for name in ("layer_scale", "mlp64"):
+        assert binding.supported(binding.config_of(WORKLOADS[name], "streamed")) == ok
+    for name in ("atlas_long", "linear_poly2", "linear64_delta"):
+        assert binding.supported(binding.config_of(WORKLOADS[name], "streamed")) == binding.ERR_UNSUPPORTED
 
 
 def test_null_handle_and_strings():

@@ -51,8 +51,12 @@ def _run_both(B, wl, seqs=None, n_tokens=None, kernel="auto"):
 SMALL_N = 3 * 64 + 17   # three full chunks and a ragged tail
 
 
-CASES = [(n, k) for n in ORDER for k in ("auto", "per_sequence")
-         if k == "auto" or WORKLOADS[n].memory == "mlp"]
+# kernel families per workload: every workload through "auto"; the MLP ones
+# also through the per-sequence family; the identity-map MLPs also through the
+# sharded and the streamed-state families
+GROUPED = [n for n in ORDER if WORKLOADS[n].memory == "mlp" and WORKLOADS[n].feature_map == "identity"]
+CASES = ([(n, "auto") for n in ORDER] + [(n, "per_sequence") for n in ORDER if WORKLOADS[n].memory == "mlp"]
+         + [(n, k) for n in GROUPED for k in ("sharded", "streamed")])
 
 
 @pytest.mark.parametrize("recipe", ["preset", "lively"])
@@ -74,20 +78,21 @@ def test_parity_small(B, name, kernel, recipe):
     assert r["halo_exact"] and r["count_exact"], r
 
 
-@pytest.mark.parametrize("name", ["linear_poly2", "mlp64", "layer_scale", "atlas_long"])
-def test_streaming_split_is_bitwise_equal(B, name):
+@pytest.mark.parametrize("name,kernel", [("linear_poly2", "auto"), ("mlp64", "auto"), ("layer_scale", "auto"),
+                                         ("atlas_long", "auto"), ("mlp64", "streamed"), ("layer_scale", "streamed")])
+def test_streaming_split_is_bitwise_equal(B, name, kernel):
     """Two calls with a chunk-aligned split equal one call, bit for bit."""
     binding, H = B
     wl = lively(WORKLOADS[name].with_shape(batch=1, heads=2, seq_len=SMALL_N))
-    _say(f"[split] {name}")
+    _say(f"[split] {name} kernel={kernel}")
     inputs, w0 = H.prepare(wl)
     dev = H.to_device(wl, inputs)
-    one = binding.AtlasMem(wl)
+    one = binding.AtlasMem(wl, kernel)
     st1 = one.new_state(torch.from_numpy(w0))
     out1 = H.gpu_run(one, wl, dev, st1)
     n1 = 128
     wa, wb = wl.with_shape(seq_len=n1), wl.with_shape(seq_len=SMALL_N - n1)
-    ma, mb = binding.AtlasMem(wa), binding.AtlasMem(wb)
+    ma, mb = binding.AtlasMem(wa, kernel), binding.AtlasMem(wb, kernel)
     st2 = ma.new_state(torch.from_numpy(w0))
     part = lambda t, a, b: t[:, :, a:b].contiguous()
     da = {k_: part(t, 0, n1) for k_, t in dev.items()}
@@ -99,13 +104,14 @@ def test_streaming_split_is_bitwise_equal(B, name):
     assert torch.equal(st1, st2)
 
 
-def test_deterministic(B):
+@pytest.mark.parametrize("kernel", ["sharded", "streamed"])
+def test_deterministic(B, kernel):
     binding, H = B
     wl = lively(WORKLOADS["layer_scale"].with_shape(batch=1, heads=3, seq_len=SMALL_N))
-    _say("[determinism] layer_scale")
+    _say(f"[determinism] layer_scale kernel={kernel}")
     inputs, w0 = H.prepare(wl)
     dev = H.to_device(wl, inputs)
-    mem = binding.AtlasMem(wl)
+    mem = binding.AtlasMem(wl, kernel)
     outs, sts = [], []
     for _ in range(2):
         st = mem.new_state(torch.from_numpy(w0))
@@ -115,14 +121,15 @@ def test_deterministic(B):
     assert torch.equal(outs[0], outs[1]) and torch.equal(sts[0], sts[1])
 
 
-@pytest.mark.parametrize("n", [0, 1, 37, 64])
-@pytest.mark.parametrize("name", ["linear64_delta", "mlp64", "layer_scale"])
-def test_short_and_empty_calls(B, name, n):
+@pytest.mark.parametrize("n", [0, 1, 37, 64, 65])
+@pytest.mark.parametrize("name,kernel", [("linear64_delta", "auto"), ("mlp64", "auto"), ("layer_scale", "auto"),
+                                         ("mlp64", "streamed"), ("layer_scale", "streamed")])
+def test_short_and_empty_calls(B, name, kernel, n):
     """N = 0 leaves the state alone; N < chunk is one partial chunk."""
     binding, H = B
     wl = lively(WORKLOADS[name].with_shape(batch=1, heads=2, seq_len=n))
-    _say(f"[short] {name} N={n}")
-    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl)
+    _say(f"[short] {name} kernel={kernel} N={n}")
+    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl, kernel=kernel)
     if n == 0:
         assert out_g.size == 0
         np.testing.assert_array_equal(st_g["weights"], st_o["mem"])
@@ -136,16 +143,17 @@ def test_short_and_empty_calls(B, name, n):
     assert r["halo_exact"] and r["count_exact"], r
 
 
-def test_alpha_one_erases_exactly(B):
+@pytest.mark.parametrize("kernel", ["sharded", "streamed"])
+def test_alpha_one_erases_exactly(B, kernel):
     """alpha = 1, theta = 0: weights become exactly zero and y = q exactly."""
     binding, H = B
     wl = WORKLOADS["layer_scale"].with_shape(batch=1, heads=2, seq_len=SMALL_N)
-    _say("[alpha=1] layer_scale")
+    _say(f"[alpha=1] layer_scale kernel={kernel}")
     inputs, w0 = H.prepare(wl)
     inputs["alpha"][:] = 1.0
     inputs["theta"][:] = 0.0
     dev = H.to_device(wl, inputs)
-    mem = binding.AtlasMem(wl)
+    mem = binding.AtlasMem(wl, kernel)
     st = mem.new_state(torch.from_numpy(w0))
     out = H.gpu_run(mem, wl, dev, st)
     torch.cuda.synchronize()
@@ -171,8 +179,8 @@ def test_theta_zero_keeps_weights_exactly(B):
     assert H.rel_l2(out.float().cpu().numpy().reshape(out_o.shape), out_o) <= 2e-2
 
 
-@pytest.mark.parametrize("name", ORDER)
-def test_full_size_sampled(B, name):
+@pytest.mark.parametrize("name,kernel", [(n, "auto") for n in ORDER] + [(n, "streamed") for n in GROUPED])
+def test_full_size_sampled(B, name, kernel):
     """Full shapes in the benchmark's launch configuration; the oracle replays
     the first two chunks of the first and last sequence."""
     binding, H = B
@@ -180,8 +188,8 @@ def test_full_size_sampled(B, name):
     S = wl.batch * wl.heads
     seqs = sorted({0, S - 1})
     n = 2 * wl.chunk
-    _say(f"[full] {name} B={wl.batch} H={wl.heads} N={wl.seq_len} sampled seqs={seqs} n={n}")
-    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl, seqs=seqs, n_tokens=n)
+    _say(f"[full] {name} kernel={kernel} B={wl.batch} H={wl.heads} N={wl.seq_len} sampled seqs={seqs} n={n}")
+    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl, seqs=seqs, n_tokens=n, kernel=kernel)
     assert np.isfinite(out_g).all()
     r = H.compare(wl, inputs, out_g, None, out_o, None, seqs=seqs, n_tokens=n)
     _say(f"[full] {name}: {r}")
@@ -218,17 +226,17 @@ def test_forward_rejects_bad_arguments(B):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("kernel", ["sharded", "streamed"])
 @pytest.mark.parametrize("name", ["mlp64", "layer_scale"])
-def test_window_wider_than_one_chunk_row_block(B, name):
-    """c = 33 on the mlp64 shape (window 96 rows) and c = 17 on layer_scale,
-    through the automatically chosen kernel."""
+def test_window_wider_than_one_chunk_row_block(B, name, kernel):
+    """c = 33 on the mlp64 shape (window 96 rows) and c = 17 on layer_scale."""
     binding, H = B
     c = 33 if name == "mlp64" else 17
     wl = lively(WORKLOADS[name].with_shape(batch=1, heads=2, seq_len=SMALL_N))
     from dataclasses import replace
     wl = replace(wl, window=c, gamma_u=(-2.0, 2.0), theta_div=float(c))
-    _say(f"[window] {name} c={c}")
-    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl)
+    _say(f"[window] {name} kernel={kernel} c={c}")
+    inputs, out_g, st_g, out_o, st_o, _ = _run_both(B, wl, kernel=kernel)
     r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
     _say(f"[window] {name}: {r}")
     for key in ("out", "memory_part", "weights", "momentum"):
@@ -246,10 +254,11 @@ def test_kernel_families_agree(B):
     inputs, w0 = H.prepare(wl)
     dev = H.to_device(wl, inputs)
     outs = []
-    for kernel in ("sharded", "per_sequence"):
+    for kernel in ("sharded", "per_sequence", "streamed"):
         mem = binding.AtlasMem(wl, kernel)
         st = mem.new_state(torch.from_numpy(w0))
         outs.append((H.gpu_run(mem, wl, dev, st).float().cpu().numpy(), H.gpu_state_np(mem, st)))
         assert mem.device_errors() == 0
-    assert H.rel_l2(outs[0][0], outs[1][0]) < 5e-3
-    assert H.rel_l2(outs[0][1]["weights"], outs[1][1]["weights"]) < 1e-2
+    for other in outs[1:]:
+        assert H.rel_l2(outs[0][0], other[0]) < 5e-3
+        assert H.rel_l2(outs[0][1]["weights"], other[1]["weights"]) < 1e-2
