@@ -98,7 +98,8 @@ def cpu_baseline(wl, inputs, w0, budget_s: float):
 def kernel_name(binding, wl, family):
     """Name of the recurrent kernel a call runs for this workload and family."""
     if family == "auto":
-        family = "sharded" if binding.supported(binding.config_of(wl, "sharded")) == binding.OK else "per_sequence"
+        family = next(f for f in ("streamed", "sharded", "per_sequence")
+                      if binding.supported(binding.config_of(wl, f)) == binding.OK)
     return {"sharded": "sharded_mlp_kernel", "streamed": "stream_mlp_kernel", "per_sequence": "chunk_kernel"}[family]
 
 

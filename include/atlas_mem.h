@@ -60,10 +60,11 @@ enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
  * image kept in a global workspace (all memories and feature maps).
  * SHARDED: the hidden units of each sequence split over several workgroups
  * of one XCD, weights resident in registers.  STREAMED: one workgroup per
- * sequence, the fp32 weights and momentum read and written once per chunk
- * in one fused pass.  SHARDED and STREAMED serve the MLP memory with the
- * identity feature map, d_k == d_v and bf16 io.  AUTO picks SHARDED, then
- * PER_SEQUENCE, whichever has a kernel for the shape.                       */
+ * sequence (or a pair of workgroups of one XCD, each with half of the hidden
+ * units), the fp32 weights and momentum read and written once per chunk in
+ * one fused pass.  SHARDED and STREAMED serve the MLP memory with the
+ * identity feature map, d_k == d_v and bf16 io.  AUTO picks STREAMED, then
+ * SHARDED, then PER_SEQUENCE, the first with a kernel for the shape.        */
 enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3 };
 
 typedef struct {

@@ -50,11 +50,13 @@ static const ShardedVariant kSharded[] = {
 
 struct StreamVariant {
   const char* name;
-  int d, dv, h, wp, bc;
+  int d, dv, h, wp, bc, g;
+  size_t (*xbytes)();
   ShardedLaunchFn launch;
 };
 
-#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC) {#NAME, D, DV, H, WP, BC, &launch_streamed<D, DV, H, WP, BC>},
+#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC, G) \
+  {#NAME, D, DV, H, WP, BC, G, &streamed_xbytes<D, DV, H, WP, BC, G>, &launch_streamed<D, DV, H, WP, BC, G>},
 static const StreamVariant kStreamed[] = {
 #include "atlas_mem_stream_variants.inc"
 };
@@ -139,11 +141,13 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   if (out) *out = nullptr;
   if (sout) *sout = nullptr;
   if (tout) *tout = nullptr;
-  if (c->kernel == ATLAS_KERNEL_STREAMED) {
+  if (c->kernel == ATLAS_KERNEL_STREAMED || c->kernel == ATLAS_KERNEL_AUTO) {
     const StreamVariant* tv = find_streamed(c);
-    if (!tv) return ATLAS_ERR_UNSUPPORTED;
-    if (tout) *tout = tv;
-    return ATLAS_OK;
+    if (tv) {
+      if (tout) *tout = tv;
+      return ATLAS_OK;
+    }
+    if (c->kernel == ATLAS_KERNEL_STREAMED) return ATLAS_ERR_UNSUPPORTED;
   }
   if (c->kernel != ATLAS_KERNEL_PER_SEQUENCE) {
     const ShardedVariant* sv = find_sharded(c);
@@ -216,11 +220,14 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   h->ws = nullptr;
   h->coef = nullptr;
   h->ev_before = h->ev_after = nullptr;
-  // sharded: exchange buffers per sequence, then the control words
-  const size_t ctrl_off = svar ? align_up(svar->xbytes() * (size_t)h->n_seq, 256) : 0;
-  const size_t ws_bytes = var    ? var->ws_bytes * (size_t)h->n_seq
-                          : svar ? ctrl_off + align_up((1 + (size_t)h->n_seq) * 4, 256)
-                                 : 0;   // streamed: the coefficient blocks only
+  // sharded, and streamed with G > 1: exchange buffers per sequence, then
+  // the control words (error word + one barrier counter per sequence)
+  const bool grouped = svar || (tvar && tvar->g > 1);
+  const size_t xbytes = svar ? svar->xbytes() : tvar ? tvar->xbytes() : 0;
+  const size_t ctrl_off = align_up(xbytes * (size_t)h->n_seq, 256);
+  const size_t ws_bytes = var       ? var->ws_bytes * (size_t)h->n_seq
+                          : grouped ? ctrl_off + align_up((1 + (size_t)h->n_seq) * 4, 256)
+                                    : 0;
   const size_t coef_bytes = (size_t)h->n_seq * h->nchunks * h->coef_stride * sizeof(float);
   if (ws_bytes && hipMalloc(&h->ws, ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -233,7 +240,7 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
     delete h;
     return ATLAS_ERR_OUT_OF_MEMORY;
   }
-  if (svar) {
+  if (grouped) {
     h->ctrl = reinterpret_cast<unsigned*>(h->ws + ctrl_off);
     if ((e = hipMemset(h->ctrl, 0, (1 + (size_t)h->n_seq) * 4)) != hipSuccess) {
       (void)hipFree(h->ws);

@@ -29,6 +29,13 @@ __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// The value x, opaque to the optimiser: index arithmetic derived from it is
+// recomputed where it is used instead of being hoisted out of loops (where
+// the compiler would keep it live, or spill it, for the whole loop).
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Row-major operand (k contiguous), natural k order: lane reads k0+8g .. +7 of row row0 + (l & 15).
 __device__ __forceinline__ bf16x8 ld_nat(const bf16* base, int ld, int row0, int k0, int lane) {
@@ -45,6 +52,13 @@ __device__ __forceinline__ bf16x8 ld_perm(const bf16* base, int ld, int row0, in
 __device__ __forceinline__ bf16x8 ld_nat_scaled(const bf16* base, int ld, int row0, int k0, int lane, const float* s) {
   const bf16x8 v = ld_nat(base, ld, row0, k0, lane);
   const float* sc = s + k0 + 8 * (lane >> 4);
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)((float)v[i] * sc[i]);
+  return r;
+}
+// Element i scaled by sc[i] (sc already offset to the lane's first k).
+__device__ __forceinline__ bf16x8 scaled_k(const bf16x8& v, const float* sc) {
   bf16x8 r;
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = (bf16)((float)v[i] * sc[i]);

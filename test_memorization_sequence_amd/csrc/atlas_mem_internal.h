@@ -128,10 +128,13 @@ hipError_t launch_sharded(const ShardedParams& sp, const CoeffParams& kp, hipStr
                           hipEvent_t ev1);
 template <int D, int DV, int H, int G, int WP, int BC>
 size_t sharded_xbytes();
-// Streamed-state MLP kernel; takes ShardedParams with xws and ctrl unused.
-template <int D, int DV, int H, int WP, int BC>
+// Streamed-state MLP kernel (G workgroups per sequence; for G = 1 xws and
+// ctrl are unused).
+template <int D, int DV, int H, int WP, int BC, int G>
 hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
                            hipEvent_t ev1);
+template <int D, int DV, int H, int WP, int BC, int G>
+size_t streamed_xbytes();
 
 // Enqueues the coefficient kernel, then the chunk kernel; ev0/ev1 (optional)
 // are recorded right before and right after the chunk kernel.

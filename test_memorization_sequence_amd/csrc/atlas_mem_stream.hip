@@ -35,18 +35,21 @@
 #include "atlas_mem_internal.h"
 #include "atlas_mem_coeff.h"
 #include "atlas_mem_frag.h"
+#include "atlas_mem_group.h"
 
 namespace atlas {
 namespace streamed {
 
 using namespace mfma;
 
-template <int D_, int DV_, int H_, int WP_, int BC_>
+template <int D_, int DV_, int H_, int WP_, int BC_, int G_>
 struct TShape {
-  static constexpr int D = D_, DV = DV_, H = H_, WP = WP_, BC = BC_;
+  static constexpr int D = D_, DV = DV_, H = H_, WP = WP_, BC = BC_, G = G_;
   static constexpr int NW = 4;                 // waves per workgroup
   static constexpr int HJ = 16 * NW;           // hidden units per super tile
-  static constexpr int NJ = H / HJ;            // super tiles
+  static constexpr int NJ = H / HJ / G;        // super tiles per member of a group
+  static_assert(G == 1 || G == 2, "groups of one or two workgroups");
+  static_assert((H / HJ) % G == 0, "super tiles split evenly");
   static constexpr int DVW = DV / NW;          // value rows per wave
   static constexpr int NDT = DVW / 16;
   static constexpr int ND = D / 16;
@@ -60,7 +63,8 @@ struct TShape {
   //   Xa, Xb : window keys of this chunk and the next [WP][LX] (ping-pong)
   //   Xq     : queries [BC][LX];  Q1 [BC][L1Q] (read 8 bytes at a time);  D2 [WP][LV]
   //   AT     : A^T of the super tile [HJ][LT];  at the end of a pass Q2^T [WP][LQ]
-  //   W2     : bf16 image W2^T [DV][LH];  after its use the next chunk's A' [WP][LH]
+  //   W2     : bf16 image W2^T [DV][LH];  after its use the next chunk's A' [WP][LH];
+  //            between passes, with Ah, the value rows of the next window [WP][LV]
   //   Ah     : retrieval activations of the super tile [BC][LH]
   //   Cm     : the weights C_{t,i} of the chunk, bf16 [BC][WP]
   static constexpr size_t szX = align_up((size_t)WP * LX * 2, 256);
@@ -74,8 +78,15 @@ struct TShape {
   static constexpr size_t oF = oCm + align_up((size_t)BC * WP * 2, 256);   // cA, cB, cM, cS, P, sg
   static constexpr size_t lds = oF + (2 * BC + 3 * WP + 4) * 4;   // + s*gamma of the window rows
   static_assert(lds <= 163840, "LDS budget of one CU");
-  // state lines (128 B) of one super tile: W1/S1 rows, W2/S2 columns
-  static constexpr int L1 = HJ * D / 32, L2 = DV * (HJ / 32);
+  static_assert(oAh - oW2 + align_up((size_t)BC * LH * 2, 256) >= (size_t)WP * LV * 2, "value rows fit W2 + Ah");
+  static_assert(oAh + align_up((size_t)BC * LH * 2, 256) == oCm, "W2 and Ah regions are contiguous");
+  // exchange workspace per sequence (G = 2): per chunk parity and member,
+  // the partial sums A' W2'^T [NT][NDT] and y [NQ][NDT] as per-lane f32x4
+  // tiles in lane order (both members use the same lane layout)
+  static constexpr size_t tile_bytes = 256 * 16;
+  static constexpr size_t xYh = 0;
+  static constexpr size_t xYp = xYh + 2ull * G * NT * NDT * tile_bytes;
+  static constexpr size_t xbytes = G == 1 ? 0 : xYp + 2ull * G * NQ * NDT * tile_bytes;
 };
 
 template <class S>
@@ -88,8 +99,21 @@ stream_mlp_kernel(ShardedParams p) {
   constexpr int oCM = 2 * BC + 4, oCS = oCM + WP, oCC = oCS + WP, oQ1g = oCC + BC * WP;
   extern __shared__ __attribute__((aligned(256))) char smem[];
 
-  const int seq = blockIdx.x;
+  // group membership (G = 2): XCD-aware, as in the sharded kernel: block b
+  // runs on XCD b % 8 and the members of a group are blocks 8*(gi*G + p) + xcd
+  constexpr int G = S::G;
+  int seq = blockIdx.x, pm = 0;
+  if constexpr (G > 1) {
+    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+    pm = slot % G;
+    seq = (slot / G) * 8 + xcd;
+  }
   if (seq >= p.n_seq) return;
+  const int J0 = pm * NJ;   // first super tile of this member
+  unsigned* ctr = G > 1 ? p.ctrl + 1 + seq : nullptr;
+  unsigned* err = p.ctrl;
+  unsigned nbar = 0;
+  char* xw = G > 1 ? p.xws + (size_t)seq * S::xbytes : nullptr;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int N = p.N, c = p.c, W = BC + c - 1;
   const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
@@ -152,6 +176,7 @@ stream_mlp_kernel(ShardedParams p) {
 
   // window keys of chunk ch (halo rows from the state, invalid rows zero)
   auto load_window = [&](int ch, WinRegs& R, auto halo_tag) {
+    const int tid = fresh(threadIdx.x);
     constexpr bool HALO = decltype(halo_tag)::value;
     const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
 #pragma unroll
@@ -179,6 +204,7 @@ stream_mlp_kernel(ShardedParams p) {
     }
   };
   auto store_window = [&](bf16* Xdst, const WinRegs& R) {
+    const int tid = fresh(threadIdx.x);
 #pragma unroll
     for (int u = 0; u < NXV; ++u) {
       const int e = tid + 256 * u;
@@ -189,6 +215,7 @@ stream_mlp_kernel(ShardedParams p) {
   // queries, Q1, the weights C, the gate coefficients and s*gamma of the
   // window rows of chunk ch
   auto load_chunk = [&](int ch, ChunkRegs& R, auto halo_tag) {
+    const int tid = fresh(threadIdx.x);
     constexpr bool HALO = decltype(halo_tag)::value;
     const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
     const float* coef = coef_seq + (size_t)ch * p.coef_stride;
@@ -226,6 +253,7 @@ stream_mlp_kernel(ShardedParams p) {
     }
   };
   auto store_chunk = [&](const ChunkRegs& R) {
+    const int tid = fresh(threadIdx.x);
 #pragma unroll
     for (int u = 0; u < NQV; ++u) {
       const int e = tid + 256 * u;
@@ -253,9 +281,37 @@ stream_mlp_kernel(ShardedParams p) {
     if (tid < WP) sgw[tid] = R.sg;
   };
 
+  // value rows of chunk ch's window (chunks >= 1: no halo), staged through LDS
+  constexpr int NVV = (WP * (DV / 8) + 255) / 256;
+  struct VRegs { bf16x8 x[NVV]; };
+  auto load_vwin = [&](int ch, VRegs& R) {
+    const int tid = fresh(threadIdx.x);
+    const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+      const int e = tid + 256 * u, w = e / (DV / 8), d8 = (e % (DV / 8)) * 8, i = t0 - (c - 1) + w;
+      const bool ok = (WP * (DV / 8) % 256 == 0 || e < WP * (DV / 8)) && row_ok(w, t0, te);
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(v + (unsigned)min(max(i, 0), N - 1) * DV + d8);
+      bf16x8 zz;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) zz[z] = (bf16)0.f;
+      R.x[u] = ok ? x : zz;
+    }
+  };
+  auto store_vwin = [&](bf16* Vdst, const VRegs& R) {
+    const int tid = fresh(threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+      const int e = tid + 256 * u;
+      if (WP * (DV / 8) % 256 == 0 || e < WP * (DV / 8))
+        *reinterpret_cast<bf16x8*>(Vdst + (e / (DV / 8)) * LV + (e % (DV / 8)) * 8) = R.x[u];
+    }
+  };
+
   // D2 of chunk ch from the sums yh = A W2^T of its window (Xw: its window keys)
   f32x4 yh[NT][NDT];
   auto load_d2 = [&](int ch, D2Regs& R, auto halo_tag) {
+    const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
     constexpr bool HALO = decltype(halo_tag)::value;
     const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
 #pragma unroll
@@ -278,6 +334,7 @@ stream_mlp_kernel(ShardedParams p) {
   };
   // needs sgw of chunk ch in LDS
   auto finish_d2 = [&](int ch, const D2Regs& R, const bf16* Xw, auto halo_tag) {
+    const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
     constexpr bool HALO = decltype(halo_tag)::value;
     const int t0 = ch * BC;
 #pragma unroll
@@ -303,35 +360,70 @@ stream_mlp_kernel(ShardedParams p) {
       }
   };
 
+  // the same from the staged value rows Vw (chunks >= 1)
+  auto finish_d2_lds = [&](const bf16* Vw, const bf16* Xw) {
+    const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int w = 16 * m + 4 * g + r;
+        const float sg = sgw[w];
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          const int o = dvw + 16 * bb + c16;
+          const float vv = (float)Vw[w * LV + o];
+          const float val = dot ? -sg * vv : sg * ((res ? (float)Xw[w * LX + o] : 0.f) + yh[m][bb][r] - vv);
+          D2[w * LV + o] = (bf16)val;
+        }
+      }
+  };
+
   // state tiles of super tile J (see the layout notes at the top): uniform
   // tile base + one lane offset + a compile-time offset per tile
-  const int l1 = (16 * wave + c16) * D + 4 * g, l2 = (dvw + c16) * H + 4 * g;
-  auto w1_at = [&](int J, int t) { return J * HJ * D + l1 + 16 * t; };
-  auto w2_at = [&](int J, int a, int bb) { return J * HJ + l2 + 16 * bb * H + 16 * a; };
+  auto w1_at = [&](int J, int t) {
+    const int l = fresh(threadIdx.x);
+    return J * HJ * D + (l >> 2 & ~15 | (l & 15)) * D + 4 * (l >> 4 & 3) + 16 * t;
+  };
+  auto w2_at = [&](int J, int a, int bb) {
+    const int l = fresh(threadIdx.x);
+    return J * HJ + (S::DVW * (l >> 6) + (l & 15)) * H + 4 * (l >> 4 & 3) + 16 * bb * H + 16 * a;
+  };
 
-  // L2 prefetch of super tile J's state: one 4-byte load per 128-byte line,
-  // kept in registers until the end of the current tile so nothing waits on it
-  unsigned sink = 0;
-  constexpr int NP1 = (S::L1 + 255) / 256, NP2 = (S::L2 + 255) / 256, NPF = 2 * NP1 + 2 * NP2;
-  auto touch_state = [&](int J, unsigned (&pf)[NPF]) {
-    const float* w1 = W1g + J * HJ * D;
-    const float* s1 = S1g + J * HJ * D;
-    const float* w2 = W2g + J * HJ;
-    const float* s2 = S2g + J * HJ;
+  // State prefetch, one super tile ahead, into loop-carried registers: the
+  // W1/S1 rows of the tile and the W2 values of its bf16 image.  They are
+  // issued after the loads the current tile still waits for (vmcnt retires in
+  // order), so no wait in the current tile covers them.
+  f32x4 pW1[ND], pS1[ND], pW2[NU][NDT];
+  auto prefetch = [&](int J) {
 #pragma unroll
-    for (int u = 0; u < NP1; ++u) {
-      const int L = tid + 256 * u;
-      const bool ok = S::L1 % 256 == 0 || L < S::L1;
-      pf[u] = ok ? *reinterpret_cast<const unsigned*>(w1 + 32 * L) : 0u;
-      pf[NP1 + u] = ok && mom ? *reinterpret_cast<const unsigned*>(s1 + 32 * L) : 0u;
+    for (int t = 0; t < ND; ++t) {
+      pW1[t] = *reinterpret_cast<const f32x4*>(W1g + w1_at(J, t));
+      pS1[t] = mom ? *reinterpret_cast<const f32x4*>(S1g + w1_at(J, t)) : zero4();
     }
 #pragma unroll
-    for (int u = 0; u < NP2; ++u) {
-      const int L = tid + 256 * u, o = (L / (HJ / 32)) * H + 32 * (L % (HJ / 32));
-      const bool ok = S::L2 % 256 == 0 || L < S::L2;
-      pf[2 * NP1 + u] = ok ? *reinterpret_cast<const unsigned*>(w2 + o) : 0u;
-      pf[2 * NP1 + NP2 + u] = ok && mom ? *reinterpret_cast<const unsigned*>(s2 + o) : 0u;
-    }
+    for (int a = 0; a < NU; ++a)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) pW2[a][bb] = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
+  };
+
+  // lane-ordered exchange of per-lane accumulator tiles with the partner
+  // (G = 2): tile i of member m at xw + base + (i * 256 + tid) * 16
+  auto xYh_at = [&](int par, int m) { return S::xYh + ((size_t)par * G + m) * NT * NDT * S::tile_bytes; };
+  auto xYp_at = [&](int par, int m) { return S::xYp + ((size_t)par * G + m) * NQ * NDT * S::tile_bytes; };
+  auto xput = [&](size_t off, const f32x4 (&a)[NT][NDT]) {
+    f32x4* d = reinterpret_cast<f32x4*>(xw + off) + threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) d[(m * NDT + bb) * 256] = a[m][bb];
+  };
+  auto xadd = [&](size_t off, f32x4 (&a)[NT][NDT]) {
+    const f32x4* d = reinterpret_cast<const f32x4*>(xw + off) + threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) a[m][bb] += d[(m * NDT + bb) * 256];
   };
 
   // ---- prologue: inputs of chunk 0 (and the keys of chunk 1), then chunk 0's forward
@@ -351,7 +443,7 @@ stream_mlp_kernel(ShardedParams p) {
     for (int m = 0; m < NT; ++m)
 #pragma unroll
       for (int bb = 0; bb < NDT; ++bb) yh[m][bb] = zero4();
-    for (int J = 0; J < NJ; ++J) {
+    for (int J = J0; J < J0 + NJ; ++J) {
       f32x4 W1T[ND], W2T[NU][NDT];
 #pragma unroll
       for (int t = 0; t < ND; ++t) W1T[t] = *reinterpret_cast<const f32x4*>(W1g + w1_at(J, t));
@@ -386,6 +478,14 @@ stream_mlp_kernel(ShardedParams p) {
         }
       __syncthreads();
     }
+    if constexpr (G > 1) {
+      // the partner's partial sums of the window forward
+      const int par = 1;   // chunk 0 uses parity 0; the prologue the other slot
+      xput(xYh_at(par, pm), yh);
+      group_barrier(ctr, G * (++nbar), err);
+      xadd(xYh_at(par, 1 - pm), yh);
+    }
+    prefetch(J0);
     finish_d2(0, d0, Xc, std::true_type{});
     __syncthreads();
   }
@@ -395,11 +495,14 @@ stream_mlp_kernel(ShardedParams p) {
     const int t0 = ch * BC, te = min(N, t0 + BC) - 1, ce = te - t0;
     const bool more = ch + 1 < nchunks;
     const float Ate = cA[ce], Bte = cB[ce], Pc = cP[0];
-    f32x4 yo[NQ][NDT], q2[NT];
+    f32x4 yw[NQ][NDT], ys[NQ][NDT], q2[NT];   // Ah W2^T, Ah S2^T (scaled by A_q, B_q at the end)
 #pragma unroll
     for (int m = 0; m < NQ; ++m)
 #pragma unroll
-      for (int bb = 0; bb < NDT; ++bb) yo[m][bb] = zero4();
+      for (int bb = 0; bb < NDT; ++bb) {
+        yw[m][bb] = zero4();
+        ys[m][bb] = zero4();
+      }
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       q2[m] = zero4();
@@ -407,22 +510,20 @@ stream_mlp_kernel(ShardedParams p) {
       for (int bb = 0; bb < NDT; ++bb) yh[m][bb] = zero4();
     }
 
-    for (int J = 0; J < NJ; ++J) {
+    for (int J = J0; J < J0 + NJ; ++J) {
       // ======== W1 side: W1/S1 in registers, W2 only long enough for its bf16 image
-      unsigned pf[NPF];
-      touch_state(J + 1 < NJ ? J + 1 : 0, pf);
       f32x4 W1T[ND], S1T[ND];
 #pragma unroll
       for (int t = 0; t < ND; ++t) {
-        W1T[t] = *reinterpret_cast<const f32x4*>(W1g + w1_at(J, t));
-        S1T[t] = mom ? *reinterpret_cast<const f32x4*>(S1g + w1_at(J, t)) : zero4();
+        W1T[t] = pW1[t];
+        S1T[t] = pS1[t];
       }
       // ---- bf16 image W2^T [dv][unit] of the tile (this wave's value rows)
 #pragma unroll
       for (int a = 0; a < NU; ++a)
 #pragma unroll
         for (int bb = 0; bb < NDT; ++bb) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
+          const f32x4 w = pW2[a][bb];
           *reinterpret_cast<bf16x4*>(W2L + (dvw + 16 * bb + c16) * LH + 16 * a + 4 * g) =
               bf16x4{(bf16)w[0], (bf16)w[1], (bf16)w[2], (bf16)w[3]};
         }
@@ -477,11 +578,15 @@ stream_mlp_kernel(ShardedParams p) {
           }
       }
 
-      // ---- Zq^T = W1 (A_q Xq)^T + S1 (B_q Xq)^T - D1^T Q1^T [16 units x q]; Ah = gelu
+      // ---- Zq^T = A_q (W1 Xq^T) + B_q (S1 Xq^T) - D1^T Q1^T [16 units x q]; Ah = gelu
       {
-        f32x4 zq[NQ];
+        f32x4 a1[NQ], a2[NQ], a3[NQ];
 #pragma unroll
-        for (int m = 0; m < NQ; ++m) zq[m] = zero4();
+        for (int m = 0; m < NQ; ++m) {
+          a1[m] = zero4();
+          a2[m] = zero4();
+          a3[m] = zero4();
+        }
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) {
           const bf16x8 aw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
@@ -489,19 +594,20 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
           for (int m = 0; m < NQ; ++m) {
             const bf16x8 xb = ld_perm(Xq, LX, 16 * m, 32 * s, lane);
-            zq[m] = mma(aw, scaled(xb, cA[16 * m + c16]), zq[m]);
-            if (mom) zq[m] = mma(as, scaled(xb, cB[16 * m + c16]), zq[m]);
+            a1[m] = mma(aw, xb, a1[m]);
+            if (mom) a2[m] = mma(as, xb, a2[m]);
           }
         }
 #pragma unroll
         for (int s = 0; s < NT / 2; ++s)
 #pragma unroll
-          for (int m = 0; m < NQ; ++m) zq[m] = mma(fd[s], ld_perm(Q1, L1Q, 16 * m, 32 * s, lane), zq[m]);
+          for (int m = 0; m < NQ; ++m) a3[m] = mma(fd[s], ld_perm(Q1, L1Q, 16 * m, 32 * s, lane), a3[m]);
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
+          const float qa = cA[16 * m + c16], qb = cB[16 * m + c16];
           bf16x4 h4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h4[r] = (bf16)gelu(zq[m][r]);
+          for (int r = 0; r < 4; ++r) h4[r] = (bf16)gelu(fmaf(qa, a1[m][r], fmaf(qb, a2[m][r], a3[m][r])));
           *reinterpret_cast<bf16x4*>(Ah + (16 * m + c16) * LH + 16 * wave + 4 * g) = h4;
         }
       }
@@ -547,7 +653,8 @@ stream_mlp_kernel(ShardedParams p) {
         }
       }
 
-      // ======== W2 side: W2/S2 (this wave's value rows) back from L2
+      // ======== W2 side: W2/S2 (this wave's value rows, recently loaded: in L2),
+      // then the next tile's prefetch
       f32x4 W2T[NU][NDT], S2T[NU][NDT];
 #pragma unroll
       for (int a = 0; a < NU; ++a)
@@ -556,6 +663,7 @@ stream_mlp_kernel(ShardedParams p) {
           W2T[a][bb] = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
           S2T[a][bb] = mom ? *reinterpret_cast<const f32x4*>(S2g + w2_at(J, a, bb)) : zero4();
         }
+      prefetch(J + 1 < J0 + NJ ? J + 1 : J0);   // (the last pass fetches, unused, its first tile)
       // ---- Q2 partial: Ah A^T, this wave's 16 query rows [q x tok]
 #pragma unroll
       for (int k0 = 0; k0 < HJ; k0 += 32) {
@@ -563,7 +671,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
         for (int m = 0; m < NT; ++m) q2[m] = mma(ah, ld_tr_nat(AT, LT, 16 * m, k0, lane), q2[m]);
       }
-      // ---- output partial: A_q Ah W2^T + B_q Ah S2^T [q x this wave's dv]
+      // ---- output partials: Ah W2^T and Ah S2^T [q x this wave's dv]
 #pragma unroll
       for (int s = 0; s < HJ / 32; ++s) {
         bf16x8 bw[NDT], bs[NDT];
@@ -575,41 +683,47 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
         for (int m = 0; m < NQ; ++m) {
           const bf16x8 ah = ld_perm(Ah, LH, 16 * m, 32 * s, lane);
-          const bf16x8 ha = scaled(ah, cA[16 * m + c16]);
-          const bf16x8 hb = scaled(ah, cB[16 * m + c16]);
 #pragma unroll
           for (int bb = 0; bb < NDT; ++bb) {
-            yo[m][bb] = mma(ha, bw[bb], yo[m][bb]);
-            if (mom) yo[m][bb] = mma(hb, bs[bb], yo[m][bb]);
+            yw[m][bb] = mma(ah, bw[bb], yw[m][bb]);
+            if (mom) ys[m][bb] = mma(ah, bs[bb], ys[m][bb]);
           }
         }
       }
-      // ---- W2/S2 update [units x this wave's dv]; written back at once
+      // ---- W2/S2 update [units x this wave's dv]: A^T (cM .* D2), the D2
+      // operand scaled along the tokens; written back at once
+      {
+        bf16x8 dm[NDT][NT / 2], ds[NDT][NT / 2];
 #pragma unroll
-      for (int a = 0; a < NU; ++a) {
-        bf16x8 am[NT / 2], as[NT / 2];
-#pragma unroll
-        for (int s = 0; s < NT / 2; ++s) {
-          am[s] = ld_nat_scaled(AT, LT, 16 * a, 32 * s, lane, cM);
-          as[s] = ld_nat_scaled(AT, LT, 16 * a, 32 * s, lane, cS);
-        }
-#pragma unroll
-        for (int bb = 0; bb < NDT; ++bb) {
-          f32x4 um = zero4(), us = zero4();
+        for (int bb = 0; bb < NDT; ++bb)
 #pragma unroll
           for (int s = 0; s < NT / 2; ++s) {
             const bf16x8 bd = ld_tr_nat(D2, LV, dvw + 16 * bb, 32 * s, lane);
-            um = mma(am[s], bd, um);
-            if (mom) us = mma(as[s], bd, us);
+            dm[bb][s] = scaled_k(bd, cM + 32 * s + 8 * g);
+            ds[bb][s] = scaled_k(bd, cS + 32 * s + 8 * g);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float w2 = W2T[a][bb][r], s2 = S2T[a][bb][r];
-            W2T[a][bb][r] = Ate * w2 + Bte * s2 - um[r];
-            S2T[a][bb][r] = Pc * s2 - us[r];
+        for (int a = 0; a < NU; ++a) {
+          bf16x8 at[NT / 2];
+#pragma unroll
+          for (int s = 0; s < NT / 2; ++s) at[s] = ld_nat(AT, LT, 16 * a, 32 * s, lane);
+#pragma unroll
+          for (int bb = 0; bb < NDT; ++bb) {
+            f32x4 um = zero4(), us = zero4();
+#pragma unroll
+            for (int s = 0; s < NT / 2; ++s) {
+              um = mma(at[s], dm[bb][s], um);
+              if (mom) us = mma(at[s], ds[bb][s], us);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float w2 = W2T[a][bb][r], s2 = S2T[a][bb][r];
+              W2T[a][bb][r] = Ate * w2 + Bte * s2 - um[r];
+              S2T[a][bb][r] = Pc * s2 - us[r];
+            }
+            *reinterpret_cast<f32x4*>(W2g + w2_at(J, a, bb)) = W2T[a][bb];
+            if (mom) *reinterpret_cast<f32x4*>(S2g + w2_at(J, a, bb)) = S2T[a][bb];
           }
-          *reinterpret_cast<f32x4*>(W2g + w2_at(J, a, bb)) = W2T[a][bb];
-          if (mom) *reinterpret_cast<f32x4*>(S2g + w2_at(J, a, bb)) = S2T[a][bb];
         }
       }
       // ---- next chunk's window sums A' W2'^T [tok x this wave's dv]
@@ -624,22 +738,10 @@ stream_mlp_kernel(ShardedParams p) {
             for (int m = 0; m < NT; ++m) yh[m][bb] = mma(ld_perm(An, LH, 16 * m, 32 * s, lane), bw, yh[m][bb]);
           }
       }
-#pragma unroll
-      for (int u = 0; u < NPF; ++u) sink ^= pf[u];
       __syncthreads();
     }
 
-    // ---- end of the pass.  The next chunk's inputs are requested first; they
-    // arrive while Q2 and the output rows are finished.
-    WinRegs wr;
-    ChunkRegs cr;
-    D2Regs dr;
-    if (more) {
-      load_d2(ch + 1, dr, std::false_type{});
-      load_chunk(ch + 1, cr, std::false_type{});
-      if (ch + 2 < nchunks) load_window(ch + 2, wr, std::false_type{});
-    }
-    // Q2 = C .* (Ah A^T) -> Q2^T [tok][q]
+    // ---- end of the pass: Q2 = C .* (Ah A^T) -> Q2^T [tok][q]
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       bf16x4 c4;
@@ -648,30 +750,79 @@ stream_mlp_kernel(ShardedParams p) {
       *reinterpret_cast<bf16x4*>(Q2T + (16 * m + c16) * LQ + 16 * wave + 4 * g) = c4;
     }
     __syncthreads();
-    // y -= Q2 D2, then the output rows (+ the residual query)
+    // this member's part of y - q = A_q Ah W2^T + B_q Ah S2^T - Q2 D2
+    f32x4 yp[NQ][NDT];
+    {
+      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4;
 #pragma unroll
-    for (int m = 0; m < NQ; ++m)
+      for (int m = 0; m < NQ; ++m)
 #pragma unroll
-      for (int bb = 0; bb < NDT; ++bb) {
-        f32x4 acc = zero4();
+        for (int bb = 0; bb < NDT; ++bb) {
+          f32x4 acc = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < WP; k0 += 32)
-          acc = mma(ld_tr_nat(Q2T, LQ, 16 * m, k0, lane), ld_tr_nat(D2, LV, dvw + 16 * bb, k0, lane), acc);
+          for (int k0 = 0; k0 < WP; k0 += 32)
+            acc = mma(ld_tr_nat(Q2T, LQ, 16 * m, k0, lane), ld_tr_nat(D2, LV, dvw + 16 * bb, k0, lane), acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qq = 16 * m + 4 * g + r, o = dvw + 16 * bb + c16;
-          if (t0 + qq <= te) {
-            const float rr = res ? (float)Xq[qq * LX + o] : 0.f;
-            out[(size_t)(t0 + qq) * DV + o] = (bf16)(rr + yo[m][bb][r] - acc[r]);
+          for (int r = 0; r < 4; ++r) {
+            const int qq = 16 * m + 4 * g + r;
+            yp[m][bb][r] = fmaf(cA[qq], yw[m][bb][r], fmaf(cB[qq], ys[m][bb][r], -acc[r]));
           }
         }
+    }
+    // G = 2: exchange the partial sums; each member writes half of the output rows
+    constexpr int MQ = NQ / G;
+    const int mlo = pm * MQ;
+    if constexpr (G > 1) {
+      const int par = ch & 1;
+      {
+        f32x4* d = reinterpret_cast<f32x4*>(xw + xYp_at(par, pm)) + threadIdx.x;
+#pragma unroll
+        for (int m = 0; m < NQ; ++m)
+#pragma unroll
+          for (int bb = 0; bb < NDT; ++bb) d[(m * NDT + bb) * 256] = yp[m][bb];
       }
+      if (more) xput(xYh_at(par, pm), yh);
+      group_barrier(ctr, G * (++nbar), err);
+      if (more) xadd(xYh_at(par, 1 - pm), yh);
+      const f32x4* d = reinterpret_cast<const f32x4*>(xw + xYp_at(par, 1 - pm)) + threadIdx.x;
+#pragma unroll
+      for (int m = 0; m < NQ; ++m)
+        if (m >= mlo && m < mlo + MQ)
+#pragma unroll
+          for (int bb = 0; bb < NDT; ++bb) yp[m][bb] += d[(m * NDT + bb) * 256];
+    }
+    {
+      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) {
+        if (m < mlo || m >= mlo + MQ) continue;
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int qq = 16 * m + 4 * g + r, o = dvw + 16 * bb + c16;
+            if (t0 + qq <= te) {
+              const float rr = res ? (float)Xq[qq * LX + o] : 0.f;
+              out[(size_t)(t0 + qq) * DV + o] = (bf16)(yp[m][bb][r] + rr);
+            }
+          }
+      }
+    }
     __syncthreads();
+    // ---- the next chunk's inputs, requested together (one round trip); its
+    // value rows go through the tile buffers, free now, to form D2
     if (more) {
+      VRegs vr;
+      ChunkRegs cr;
+      WinRegs wr;
+      load_vwin(ch + 1, vr);
+      load_chunk(ch + 1, cr, std::false_type{});
+      if (ch + 2 < nchunks) load_window(ch + 2, wr, std::false_type{});
+      store_vwin(W2L, vr);
       store_chunk(cr);
       if (ch + 2 < nchunks) store_window(Xc, wr);
-      __syncthreads();   // sgw of the next chunk
-      finish_d2(ch + 1, dr, Xn, std::false_type{});
+      __syncthreads();
+      finish_d2_lds(W2L, Xn);
       bf16* tmp = Xc;
       Xc = Xn;
       Xn = tmp;
@@ -679,9 +830,10 @@ stream_mlp_kernel(ShardedParams p) {
     }
   }
 
-  if (sink == 0x9e3779b9u && N < 0) out[0] = (bf16)0.f;   // keeps the prefetch loads
-  // ---- halo and count (every read of the old halo happened in the prologue)
-  if (tid < 64) {
+  // ---- halo and count (every read of the old halo happened in the
+  // prologue; with G = 2 the barrier orders it after the partner's reads)
+  if constexpr (G > 1) group_barrier(ctr, G * (++nbar), err);
+  if (pm == 0 && tid < 64) {
     for (int j = 0; j < c - 1; ++j) {
       const int i = N - (c - 1) + j;
       for (int d = lane; d < D; d += 64) hk[j * D + d] = i >= 0 ? (float)k[(size_t)i * D + d] : hk[(N + j) * D + d];
@@ -694,10 +846,10 @@ stream_mlp_kernel(ShardedParams p) {
 
 }  // namespace streamed
 
-template <int D, int DV, int H, int WP, int BC>
+template <int D, int DV, int H, int WP, int BC, int G>
 hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
                            hipEvent_t ev1) {
-  typedef streamed::TShape<D, DV, H, WP, BC> S;
+  typedef streamed::TShape<D, DV, H, WP, BC, G> S;
   if (sp.N == 0 || sp.n_seq == 0) return hipSuccess;
   hipLaunchKernelGGL((coeff_kernel<BC, WP, D>), dim3((unsigned)kp.nchunks * (unsigned)sp.n_seq), dim3(256), 0,
                      stream, kp);
@@ -711,16 +863,21 @@ hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipSt
     (void)hipGetLastError();
     attr_set = true;
   }
+  const unsigned blocks = G == 1 ? (unsigned)sp.n_seq : (unsigned)((sp.n_seq + 7) / 8) * 8u * G;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((streamed::stream_mlp_kernel<S>), dim3((unsigned)sp.n_seq), dim3(256), S::lds, stream, sp);
+  hipLaunchKernelGGL((streamed::stream_mlp_kernel<S>), dim3(blocks), dim3(256), S::lds, stream, sp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 
-#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC) \
-  template hipError_t launch_streamed<D, DV, H, WP, BC>(const ShardedParams&, const CoeffParams&, hipStream_t, \
-                                                        hipEvent_t, hipEvent_t);
+template <int D, int DV, int H, int WP, int BC, int G>
+size_t streamed_xbytes() { return streamed::TShape<D, DV, H, WP, BC, G>::xbytes; }
+
+#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC, G)                                                        \
+  template hipError_t launch_streamed<D, DV, H, WP, BC, G>(const ShardedParams&, const CoeffParams&,      \
+                                                           hipStream_t, hipEvent_t, hipEvent_t);          \
+  template size_t streamed_xbytes<D, DV, H, WP, BC, G>();
 #include "atlas_mem_stream_variants.inc"
 #undef ATLAS_STREAMED
 

@@ -51,9 +51,10 @@ def _run_both(B, wl, seqs=None, n_tokens=None, kernel="auto"):
 SMALL_N = 3 * 64 + 17   # three full chunks and a ragged tail
 
 
-# kernel families per workload: every workload through "auto"; the MLP ones
-# also through the per-sequence family; the identity-map MLPs also through the
-# sharded and the streamed-state families
+# kernel families per workload: every workload through "auto" (the streamed
+# family for the identity-map MLPs); the MLP ones also through the
+# per-sequence family; the identity-map MLPs also through the sharded and,
+# explicitly, the streamed families
 GROUPED = [n for n in ORDER if WORKLOADS[n].memory == "mlp" and WORKLOADS[n].feature_map == "identity"]
 CASES = ([(n, "auto") for n in ORDER] + [(n, "per_sequence") for n in ORDER if WORKLOADS[n].memory == "mlp"]
          + [(n, k) for n in GROUPED for k in ("sharded", "streamed")])
@@ -78,7 +79,7 @@ def test_parity_small(B, name, kernel, recipe):
     assert r["halo_exact"] and r["count_exact"], r
 
 
-@pytest.mark.parametrize("name,kernel", [("linear_poly2", "auto"), ("mlp64", "auto"), ("layer_scale", "auto"),
+@pytest.mark.parametrize("name,kernel", [("linear_poly2", "auto"), ("mlp64", "sharded"), ("layer_scale", "sharded"),
                                          ("atlas_long", "auto"), ("mlp64", "streamed"), ("layer_scale", "streamed")])
 def test_streaming_split_is_bitwise_equal(B, name, kernel):
     """Two calls with a chunk-aligned split equal one call, bit for bit."""
@@ -122,7 +123,7 @@ def test_deterministic(B, kernel):
 
 
 @pytest.mark.parametrize("n", [0, 1, 37, 64, 65])
-@pytest.mark.parametrize("name,kernel", [("linear64_delta", "auto"), ("mlp64", "auto"), ("layer_scale", "auto"),
+@pytest.mark.parametrize("name,kernel", [("linear64_delta", "auto"), ("mlp64", "sharded"), ("layer_scale", "sharded"),
                                          ("mlp64", "streamed"), ("layer_scale", "streamed")])
 def test_short_and_empty_calls(B, name, kernel, n):
     """N = 0 leaves the state alone; N < chunk is one partial chunk."""
@@ -179,7 +180,7 @@ def test_theta_zero_keeps_weights_exactly(B):
     assert H.rel_l2(out.float().cpu().numpy().reshape(out_o.shape), out_o) <= 2e-2
 
 
-@pytest.mark.parametrize("name,kernel", [(n, "auto") for n in ORDER] + [(n, "streamed") for n in GROUPED])
+@pytest.mark.parametrize("name,kernel", [(n, "auto") for n in ORDER] + [(n, "sharded") for n in GROUPED])
 def test_full_size_sampled(B, name, kernel):
     """Full shapes in the benchmark's launch configuration; the oracle replays
     the first two chunks of the first and last sequence."""
