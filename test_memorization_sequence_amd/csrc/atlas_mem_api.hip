@@ -214,7 +214,7 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   h->nchunks = (cfg->seq_len + cfg->chunk - 1) / cfg->chunk;
   h->coef_stride = var ? coef_stride(var->bc, var->wp)
                  : svar ? coef_stride(svar->bc, svar->wp, true)
-                        : coef_stride(tvar->bc, tvar->wp, true);
+                        : coef_stride(tvar->bc, tvar->wp, true, true);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { delete h; return hip_fail(e); }
   h->ws = nullptr;

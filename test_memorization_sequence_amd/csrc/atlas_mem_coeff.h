@@ -12,7 +12,8 @@ namespace atlas {
 // One workgroup per (sequence, chunk), flattened on x.  256 threads; chunk <= 64.
 // QD > 0: also compute Q1 = C .* (Xq X^T) for an identity feature map of
 // width QD (window keys X, chunk queries Xq), stored as bf16 after C.
-template <int BC, int WP, int QD = 0>
+// CB16: then also C itself as bf16.
+template <int BC, int WP, int QD = 0, bool CB16 = false>
 __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   const int chunk = (int)(blockIdx.x % (unsigned)p.nchunks), seq = (int)(blockIdx.x / (unsigned)p.nchunks);
   const int t0 = chunk * BC;
@@ -134,6 +135,10 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
         oQ[row * WP + col] = (__bf16)(oC[row * WP + col] * acc[r]);
       }
     }
+  }
+  if constexpr (CB16) {
+    __bf16* oCb = reinterpret_cast<__bf16*>(oC + BC * WP) + BC * WP;
+    for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) oCb[idx] = (__bf16)oC[idx];
   }
   for (int w = threadIdx.x; w < WP; w += blockDim.x) {
     const int i = t0 - (c - 1) + w;

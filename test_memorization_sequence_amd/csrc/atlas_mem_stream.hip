@@ -96,7 +96,7 @@ stream_mlp_kernel(ShardedParams p) {
   constexpr int D = S::D, DV = S::DV, H = S::H, WP = S::WP, BC = S::BC;
   constexpr int HJ = S::HJ, NJ = S::NJ, NDT = S::NDT, ND = S::ND, NT = S::NT, NQ = S::NQ, NU = S::NU;
   constexpr int LX = S::LX, LV = S::LV, LT = S::LT, LH = S::LH, LQ = S::LQ, L1Q = S::L1Q;
-  constexpr int oCM = 2 * BC + 4, oCS = oCM + WP, oCC = oCS + WP, oQ1g = oCC + BC * WP;
+  constexpr int oCM = 2 * BC + 4, oCS = oCM + WP, oCC = oCS + WP, oQ1g = oCC + BC * WP, oCbg = oQ1g + BC * WP / 2;
   extern __shared__ __attribute__((aligned(256))) char smem[];
 
   // group membership (G = 2): XCD-aware, as in the sharded kernel: block b
@@ -169,9 +169,9 @@ stream_mlp_kernel(ShardedParams p) {
   constexpr int NXV = (WP * (D / 8) + 255) / 256;   // window key vectors per thread
   constexpr int NQV = (BC * (D / 8) + 255) / 256;   // query vectors per thread
   constexpr int NQ1V = (BC * WP / 8 + 255) / 256;   // Q1 vectors per thread
-  constexpr int NCV = (BC * WP / 4 + 255) / 256;    // C float4 per thread
+  constexpr int NCV = (BC * WP / 8 + 255) / 256;    // C (bf16) vectors per thread
   struct WinRegs { bf16x8 x[NXV]; };
-  struct ChunkRegs { bf16x8 q[NQV], q1[NQ1V]; f32x4 cc[NCV]; float ca, cb, cm, cs, cp, sg; };
+  struct ChunkRegs { bf16x8 q[NQV], q1[NQ1V], cc[NCV]; float ca, cb, cm, cs, cp, sg; };
   struct D2Regs { bf16 vv[NT][4][NDT]; };
 
   // window keys of chunk ch (halo rows from the state, invalid rows zero)
@@ -235,10 +235,11 @@ stream_mlp_kernel(ShardedParams p) {
       const int e = tid + 256 * u;
       if (e < BC * WP / 8) R.q1[u] = *reinterpret_cast<const bf16x8*>(q1g + 8 * e);
     }
+    const bf16* cbg = reinterpret_cast<const bf16*>(coef + oCbg);
 #pragma unroll
     for (int u = 0; u < NCV; ++u) {
       const int e = tid + 256 * u;
-      if (e < BC * WP / 4) R.cc[u] = *reinterpret_cast<const f32x4*>(coef + oCC + 4 * e);
+      if (e < BC * WP / 8) R.cc[u] = *reinterpret_cast<const bf16x8*>(cbg + 8 * e);
     }
     R.ca = tid < BC ? coef[tid] : 0.f;
     R.cb = tid < BC ? coef[BC + tid] : 0.f;
@@ -272,8 +273,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
     for (int u = 0; u < NCV; ++u) {
       const int e = tid + 256 * u;
-      const f32x4 cv = R.cc[u];
-      if (e < BC * WP / 4) *reinterpret_cast<bf16x4*>(Cm + 4 * e) = bf16x4{(bf16)cv[0], (bf16)cv[1], (bf16)cv[2], (bf16)cv[3]};
+      if (e < BC * WP / 8) *reinterpret_cast<bf16x8*>(Cm + 8 * e) = R.cc[u];
     }
     if (tid < BC) { cA[tid] = R.ca; cB[tid] = R.cb; }
     if (tid < WP) { cM[tid] = R.cm; cS[tid] = R.cs; }
@@ -420,10 +420,16 @@ stream_mlp_kernel(ShardedParams p) {
   };
   auto xadd = [&](size_t off, f32x4 (&a)[NT][NDT]) {
     const f32x4* d = reinterpret_cast<const f32x4*>(xw + off) + threadIdx.x;
+    f32x4 t[NT][NDT];
 #pragma unroll
     for (int m = 0; m < NT; ++m)
 #pragma unroll
-      for (int bb = 0; bb < NDT; ++bb) a[m][bb] += d[(m * NDT + bb) * 256];
+      for (int bb = 0; bb < NDT; ++bb) t[m][bb] = d[(m * NDT + bb) * 256];
+    __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first add
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) a[m][bb] += t[m][bb];
   };
 
   // ---- prologue: inputs of chunk 0 (and the keys of chunk 1), then chunk 0's forward
@@ -511,6 +517,10 @@ stream_mlp_kernel(ShardedParams p) {
     }
 
     for (int J = J0; J < J0 + NJ; ++J) {
+      // per-iteration lane ids: keeps the lane-dependent LDS address
+      // arithmetic inside the loop instead of in registers across the call
+      const int tid = fresh(threadIdx.x), lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+      const int dvw = S::DVW * wave;
       // ======== W1 side: W1/S1 in registers, W2 only long enough for its bf16 image
       f32x4 W1T[ND], S1T[ND];
 #pragma unroll
@@ -663,7 +673,8 @@ stream_mlp_kernel(ShardedParams p) {
           W2T[a][bb] = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
           S2T[a][bb] = mom ? *reinterpret_cast<const f32x4*>(S2g + w2_at(J, a, bb)) : zero4();
         }
-      prefetch(J + 1 < J0 + NJ ? J + 1 : J0);   // (the last pass fetches, unused, its first tile)
+      // (the next pass's first tile is fetched after the chunk inputs are staged)
+      if (J + 1 < J0 + NJ) prefetch(J + 1);
       // ---- Q2 partial: Ah A^T, this wave's 16 query rows [q x tok]
 #pragma unroll
       for (int k0 = 0; k0 < HJ; k0 += 32) {
@@ -742,6 +753,8 @@ stream_mlp_kernel(ShardedParams p) {
     }
 
     // ---- end of the pass: Q2 = C .* (Ah A^T) -> Q2^T [tok][q]
+    {
+    const int tid = fresh(threadIdx.x), lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       bf16x4 c4;
@@ -749,11 +762,12 @@ stream_mlp_kernel(ShardedParams p) {
       for (int r = 0; r < 4; ++r) c4[r] = (bf16)((float)Cm[(16 * wave + 4 * g + r) * WP + 16 * m + c16] * q2[m][r]);
       *reinterpret_cast<bf16x4*>(Q2T + (16 * m + c16) * LQ + 16 * wave + 4 * g) = c4;
     }
+    }
     __syncthreads();
     // this member's part of y - q = A_q Ah W2^T + B_q Ah S2^T - Q2 D2
     f32x4 yp[NQ][NDT];
     {
-      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4;
+      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, dvw = S::DVW * (threadIdx.x >> 6);
 #pragma unroll
       for (int m = 0; m < NQ; ++m)
 #pragma unroll
@@ -792,7 +806,7 @@ stream_mlp_kernel(ShardedParams p) {
           for (int bb = 0; bb < NDT; ++bb) yp[m][bb] += d[(m * NDT + bb) * 256];
     }
     {
-      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15;
+      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
 #pragma unroll
       for (int m = 0; m < NQ; ++m) {
         if (m < mlo || m >= mlo + MQ) continue;
@@ -812,17 +826,24 @@ stream_mlp_kernel(ShardedParams p) {
     // ---- the next chunk's inputs, requested together (one round trip); its
     // value rows go through the tile buffers, free now, to form D2
     if (more) {
-      VRegs vr;
-      ChunkRegs cr;
-      WinRegs wr;
-      load_vwin(ch + 1, vr);
-      load_chunk(ch + 1, cr, std::false_type{});
-      if (ch + 2 < nchunks) load_window(ch + 2, wr, std::false_type{});
-      store_vwin(W2L, vr);
-      store_chunk(cr);
-      if (ch + 2 < nchunks) store_window(Xc, wr);
+      {
+        VRegs vr;
+        WinRegs wr;
+        load_vwin(ch + 1, vr);
+        if (ch + 2 < nchunks) load_window(ch + 2, wr, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        store_vwin(W2L, vr);
+        if (ch + 2 < nchunks) store_window(Xc, wr);
+      }
+      {
+        ChunkRegs cr;
+        load_chunk(ch + 1, cr, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        store_chunk(cr);
+      }
       __syncthreads();
       finish_d2_lds(W2L, Xn);
+      prefetch(J0);
       bf16* tmp = Xc;
       Xc = Xn;
       Xn = tmp;
@@ -851,7 +872,7 @@ hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipSt
                            hipEvent_t ev1) {
   typedef streamed::TShape<D, DV, H, WP, BC, G> S;
   if (sp.N == 0 || sp.n_seq == 0) return hipSuccess;
-  hipLaunchKernelGGL((coeff_kernel<BC, WP, D>), dim3((unsigned)kp.nchunks * (unsigned)sp.n_seq), dim3(256), 0,
+  hipLaunchKernelGGL((coeff_kernel<BC, WP, D, true>), dim3((unsigned)kp.nchunks * (unsigned)sp.n_seq), dim3(256), 0,
                      stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
