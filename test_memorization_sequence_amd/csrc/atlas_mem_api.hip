@@ -222,7 +222,7 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   h->ev_before = h->ev_after = nullptr;
   // sharded, and streamed with G > 1: exchange buffers per sequence, then
   // the control words (error word + one barrier counter per sequence)
-  const bool grouped = svar || (tvar && tvar->g > 1);
+  const bool grouped = svar || tvar;   // streamed: tile-major state copy (+ exchange for G = 2)
   const size_t xbytes = svar ? svar->xbytes() : tvar ? tvar->xbytes() : 0;
   const size_t ctrl_off = align_up(xbytes * (size_t)h->n_seq, 256);
   const size_t ws_bytes = var       ? var->ws_bytes * (size_t)h->n_seq

@@ -84,9 +84,13 @@ struct TShape {
   // the partial sums A' W2'^T [NT][NDT] and y [NQ][NDT] as per-lane f32x4
   // tiles in lane order (both members use the same lane layout)
   static constexpr size_t tile_bytes = 256 * 16;
-  static constexpr size_t xYh = 0;
+  // the state between passes, tile-major: W1, S1, W2, S2 (fp32), each wave's
+  // f32x4 tile 1 KB contiguous
+  static constexpr size_t xTS = 0;
+  static constexpr size_t xYh = xTS + 4ull * H * D * 4;
   static constexpr size_t xYp = xYh + 2ull * G * NT * NDT * tile_bytes;
-  static constexpr size_t xbytes = G == 1 ? 0 : xYp + 2ull * G * NQ * NDT * tile_bytes;
+  static constexpr size_t xbytes = G == 1 ? xYh : xYp + 2ull * G * NQ * NDT * tile_bytes;
+  static_assert(D == DV, "one tile-major stride for both layers");
 };
 
 template <class S>
@@ -113,7 +117,7 @@ stream_mlp_kernel(ShardedParams p) {
   unsigned* ctr = G > 1 ? p.ctrl + 1 + seq : nullptr;
   unsigned* err = p.ctrl;
   unsigned nbar = 0;
-  char* xw = G > 1 ? p.xws + (size_t)seq * S::xbytes : nullptr;
+  char* xw = p.xws + (size_t)seq * S::xbytes;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int N = p.N, c = p.c, W = BC + c - 1;
   const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
@@ -381,6 +385,28 @@ stream_mlp_kernel(ShardedParams p) {
 
   // state tiles of super tile J (see the layout notes at the top): uniform
   // tile base + one lane offset + a compile-time offset per tile
+  // Two layouts of the state: the row-major one of the call's state buffer
+  // (W1 [H][D], W2 [DV][H], the momentum alike), read by the first pass and
+  // written by the last, and the tile-major copy in the workspace used by the
+  // passes in between, in which every access of a wave is one contiguous
+  // 1 KB block.  tiled = true selects the copy.
+  float* T1 = reinterpret_cast<float*>(xw + S::xTS);
+  float* TS1 = T1 + (size_t)H * D;
+  float* T2 = TS1 + (size_t)H * D;
+  float* TS2 = T2 + (size_t)H * D;
+  auto at1 = [&](float* rowmajor, float* tiles, bool tiled, int J, int t) -> f32x4* {
+    const int l = fresh(threadIdx.x);
+    f32x4* a = reinterpret_cast<f32x4*>(tiles) + ((J * 4 + (l >> 6)) * ND + t) * 64 + (l & 63);
+    f32x4* b = reinterpret_cast<f32x4*>(rowmajor + J * HJ * D + (l >> 2 & ~15 | (l & 15)) * D + 4 * (l >> 4 & 3) + 16 * t);
+    return tiled ? a : b;
+  };
+  auto at2 = [&](float* rowmajor, float* tiles, bool tiled, int J, int a_, int bb) -> f32x4* {
+    const int l = fresh(threadIdx.x);
+    f32x4* a = reinterpret_cast<f32x4*>(tiles) + ((J * 4 + (l >> 6)) * (NU * NDT) + a_ * NDT + bb) * 64 + (l & 63);
+    f32x4* b = reinterpret_cast<f32x4*>(rowmajor + J * HJ + (S::DVW * (l >> 6) + (l & 15)) * H + 4 * (l >> 4 & 3) +
+                                        16 * bb * H + 16 * a_);
+    return tiled ? a : b;
+  };
   auto w1_at = [&](int J, int t) {
     const int l = fresh(threadIdx.x);
     return J * HJ * D + (l >> 2 & ~15 | (l & 15)) * D + 4 * (l >> 4 & 3) + 16 * t;
@@ -395,16 +421,16 @@ stream_mlp_kernel(ShardedParams p) {
   // issued after the loads the current tile still waits for (vmcnt retires in
   // order), so no wait in the current tile covers them.
   f32x4 pW1[ND], pS1[ND], pW2[NU][NDT];
-  auto prefetch = [&](int J) {
+  auto prefetch = [&](int J, bool tiled) {
 #pragma unroll
     for (int t = 0; t < ND; ++t) {
-      pW1[t] = *reinterpret_cast<const f32x4*>(W1g + w1_at(J, t));
-      pS1[t] = mom ? *reinterpret_cast<const f32x4*>(S1g + w1_at(J, t)) : zero4();
+      pW1[t] = *at1(W1g, T1, tiled, J, t);
+      pS1[t] = mom ? *at1(S1g, TS1, tiled, J, t) : zero4();
     }
 #pragma unroll
     for (int a = 0; a < NU; ++a)
 #pragma unroll
-      for (int bb = 0; bb < NDT; ++bb) pW2[a][bb] = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
+      for (int bb = 0; bb < NDT; ++bb) pW2[a][bb] = *at2(W2g, T2, tiled, J, a, bb);
   };
 
   // lane-ordered exchange of per-lane accumulator tiles with the partner
@@ -491,7 +517,7 @@ stream_mlp_kernel(ShardedParams p) {
       group_barrier(ctr, G * (++nbar), err);
       xadd(xYh_at(par, 1 - pm), yh);
     }
-    prefetch(J0);
+    prefetch(J0, false);
     finish_d2(0, d0, Xc, std::true_type{});
     __syncthreads();
   }
@@ -500,6 +526,7 @@ stream_mlp_kernel(ShardedParams p) {
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t0 = ch * BC, te = min(N, t0 + BC) - 1, ce = te - t0;
     const bool more = ch + 1 < nchunks;
+    const bool src_t = ch > 0, dst_t = more;   // state layouts read and written by this pass
     const float Ate = cA[ce], Bte = cB[ce], Pc = cP[0];
     f32x4 yw[NQ][NDT], ys[NQ][NDT], q2[NT];   // Ah W2^T, Ah S2^T (scaled by A_q, B_q at the end)
 #pragma unroll
@@ -638,8 +665,8 @@ stream_mlp_kernel(ShardedParams p) {
           W1T[t][r] = Ate * w1 + Bte * s1 - um[r];
           S1T[t][r] = Pc * s1 - us[r];
         }
-        *reinterpret_cast<f32x4*>(W1g + w1_at(J, t)) = W1T[t];
-        if (mom) *reinterpret_cast<f32x4*>(S1g + w1_at(J, t)) = S1T[t];
+        *at1(W1g, T1, dst_t, J, t) = W1T[t];
+        if (mom) *at1(S1g, TS1, dst_t, J, t) = S1T[t];
       }
       __syncthreads();   // Ah complete; every wave is done with the W2 image
 
@@ -670,11 +697,11 @@ stream_mlp_kernel(ShardedParams p) {
       for (int a = 0; a < NU; ++a)
 #pragma unroll
         for (int bb = 0; bb < NDT; ++bb) {
-          W2T[a][bb] = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
-          S2T[a][bb] = mom ? *reinterpret_cast<const f32x4*>(S2g + w2_at(J, a, bb)) : zero4();
+          W2T[a][bb] = *at2(W2g, T2, src_t, J, a, bb);
+          S2T[a][bb] = mom ? *at2(S2g, TS2, src_t, J, a, bb) : zero4();
         }
       // (the next pass's first tile is fetched after the chunk inputs are staged)
-      if (J + 1 < J0 + NJ) prefetch(J + 1);
+      if (J + 1 < J0 + NJ) prefetch(J + 1, src_t);
       // ---- Q2 partial: Ah A^T, this wave's 16 query rows [q x tok]
 #pragma unroll
       for (int k0 = 0; k0 < HJ; k0 += 32) {
@@ -732,8 +759,8 @@ stream_mlp_kernel(ShardedParams p) {
               W2T[a][bb][r] = Ate * w2 + Bte * s2 - um[r];
               S2T[a][bb][r] = Pc * s2 - us[r];
             }
-            *reinterpret_cast<f32x4*>(W2g + w2_at(J, a, bb)) = W2T[a][bb];
-            if (mom) *reinterpret_cast<f32x4*>(S2g + w2_at(J, a, bb)) = S2T[a][bb];
+            *at2(W2g, T2, dst_t, J, a, bb) = W2T[a][bb];
+            if (mom) *at2(S2g, TS2, dst_t, J, a, bb) = S2T[a][bb];
           }
         }
       }
@@ -843,7 +870,7 @@ stream_mlp_kernel(ShardedParams p) {
       }
       __syncthreads();
       finish_d2_lds(W2L, Xn);
-      prefetch(J0);
+      prefetch(J0, dst_t);
       bf16* tmp = Xc;
       Xc = Xn;
       Xn = tmp;
