@@ -63,8 +63,9 @@ enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
  * sequence (or a pair of workgroups of one XCD, each with half of the hidden
  * units), the fp32 weights and momentum read and written once per chunk in
  * one fused pass.  SHARDED and STREAMED serve the MLP memory with the
- * identity feature map, d_k == d_v and bf16 io.  AUTO picks STREAMED, then
- * SHARDED, then PER_SEQUENCE, the first with a kernel for the shape.        */
+ * identity feature map, d_k == d_v and bf16 io.  AUTO picks the fastest
+ * family measured for the shape: STREAMED where marked so (large hidden
+ * layers), else SHARDED, else PER_SEQUENCE.                                 */
 enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3 };
 
 typedef struct {
@@ -150,8 +151,13 @@ atlas_status atlas_mem_forward(atlas_mem_t h,
  * Errors: INVALID_ARGUMENT (bad handle, exactly one event NULL).           */
 atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* after);
 
+/* Kernel family the handle runs (ATLAS_KERNEL_PER_SEQUENCE, _SHARDED or
+ * _STREAMED; AUTO is resolved at init).  Returns -1 for an invalid handle.  */
+int atlas_mem_kernel_family(atlas_mem_t h);
+
 /* Device-side error word of the handle's last forward call (0: none; bit 0:
- * a group barrier of the sharded kernel timed out, its outputs are invalid).
+ * a group barrier of the sharded or the streamed kernel timed out, its
+ * outputs are invalid).
  * Synchronises the device.  Errors: INVALID_ARGUMENT, HIP.                 */
 atlas_status atlas_mem_device_errors(atlas_mem_t h, unsigned* flags);
 

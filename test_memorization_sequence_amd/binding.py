@@ -74,6 +74,8 @@ def lib():
         L.atlas_mem_forward.restype = ctypes.c_int
         L.atlas_mem_set_kernel_events.argtypes = [vp, vp, vp]
         L.atlas_mem_set_kernel_events.restype = ctypes.c_int
+        L.atlas_mem_kernel_family.argtypes = [vp]
+        L.atlas_mem_kernel_family.restype = ctypes.c_int
         L.atlas_mem_device_errors.argtypes = [vp, ctypes.POINTER(ctypes.c_uint)]
         L.atlas_mem_device_errors.restype = ctypes.c_int
         L.atlas_mem_free.argtypes = [vp]
@@ -165,6 +167,11 @@ class AtlasMem:
         rc = lib().atlas_mem_set_kernel_events(self.handle, raw(before), raw(after))
         if rc != OK:
             raise AtlasError(rc, "atlas_mem_set_kernel_events")
+
+    def family(self) -> str:
+        """Kernel family this handle runs ("per_sequence", "sharded", "streamed")."""
+        code = lib().atlas_mem_kernel_family(self.handle)
+        return {v: k for k, v in KERNEL.items()}[code]
 
     def device_errors(self) -> int:
         """Error word of the last call (synchronises the device)."""

@@ -50,13 +50,13 @@ static const ShardedVariant kSharded[] = {
 
 struct StreamVariant {
   const char* name;
-  int d, dv, h, wp, bc, g;
+  int d, dv, h, wp, bc, g, autopick;
   size_t (*xbytes)();
   ShardedLaunchFn launch;
 };
 
-#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC, G) \
-  {#NAME, D, DV, H, WP, BC, G, &streamed_xbytes<D, DV, H, WP, BC, G>, &launch_streamed<D, DV, H, WP, BC, G>},
+#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC, G, AUTO) \
+  {#NAME, D, DV, H, WP, BC, G, AUTO, &streamed_xbytes<D, DV, H, WP, BC, G>, &launch_streamed<D, DV, H, WP, BC, G>},
 static const StreamVariant kStreamed[] = {
 #include "atlas_mem_stream_variants.inc"
 };
@@ -143,7 +143,7 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   if (tout) *tout = nullptr;
   if (c->kernel == ATLAS_KERNEL_STREAMED || c->kernel == ATLAS_KERNEL_AUTO) {
     const StreamVariant* tv = find_streamed(c);
-    if (tv) {
+    if (tv && (c->kernel == ATLAS_KERNEL_STREAMED || tv->autopick)) {
       if (tout) *tout = tv;
       return ATLAS_OK;
     }
@@ -382,6 +382,11 @@ atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* afte
   h->ev_before = (hipEvent_t)before;
   h->ev_after = (hipEvent_t)after;
   return ATLAS_OK;
+}
+
+int atlas_mem_kernel_family(atlas_mem_t h) {
+  if (!h || h->magic != kMagic) return -1;
+  return h->var ? ATLAS_KERNEL_PER_SEQUENCE : h->svar ? ATLAS_KERNEL_SHARDED : ATLAS_KERNEL_STREAMED;
 }
 
 atlas_status atlas_mem_device_errors(atlas_mem_t h, unsigned* flags) {

@@ -922,7 +922,7 @@ hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipSt
 template <int D, int DV, int H, int WP, int BC, int G>
 size_t streamed_xbytes() { return streamed::TShape<D, DV, H, WP, BC, G>::xbytes; }
 
-#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC, G)                                                        \
+#define ATLAS_STREAMED(NAME, D, DV, H, WP, BC, G, AUTO)                                                  \
   template hipError_t launch_streamed<D, DV, H, WP, BC, G>(const ShardedParams&, const CoeffParams&,      \
                                                            hipStream_t, hipEvent_t, hipEvent_t);          \
   template size_t streamed_xbytes<D, DV, H, WP, BC, G>();

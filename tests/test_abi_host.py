@@ -83,6 +83,7 @@ def test_null_handle_and_strings():
     for code in range(5):
         assert L.atlas_mem_error_string(code)
     assert L.atlas_mem_supported(None) == binding.ERR_INVALID
+    assert L.atlas_mem_kernel_family(None) == -1
 
 
 def test_init_without_a_device_fails_cleanly():

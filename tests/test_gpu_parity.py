@@ -36,6 +36,7 @@ def _run_both(B, wl, seqs=None, n_tokens=None, kernel="auto"):
     binding, H = B
     inputs, w0 = H.prepare(wl)
     mem = binding.AtlasMem(wl, kernel)
+    assert kernel == "auto" or mem.family() == kernel
     dev = H.to_device(wl, inputs)
     st = mem.new_state(torch.from_numpy(w0))
     out = H.gpu_run(mem, wl, dev, st)
@@ -257,6 +258,7 @@ def test_kernel_families_agree(B):
     outs = []
     for kernel in ("sharded", "per_sequence", "streamed"):
         mem = binding.AtlasMem(wl, kernel)
+        assert mem.family() == kernel
         st = mem.new_state(torch.from_numpy(w0))
         outs.append((H.gpu_run(mem, wl, dev, st).float().cpu().numpy(), H.gpu_state_np(mem, st)))
         assert mem.device_errors() == 0
