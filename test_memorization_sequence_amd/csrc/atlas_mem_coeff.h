@@ -25,8 +25,10 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   const int halo_valid = (int)min<int64_t>(cnt, (int64_t)(c - 1));
 
   __shared__ float al[BC], et[BC], th[BC];
-  __shared__ float F[BC][BC + 1];   // F[t][n] = K_{t,n} theta_n
-  __shared__ float G[BC];           // e_{n->te} theta_n
+  // F[t][n] = K_{t,n} theta_n, turned into row prefix sums over n (fp64), so
+  // that every window sum of C, cM, cS is one difference
+  __shared__ double F[BC][BC + 1];
+  __shared__ double G[BC + 1];      // prefix sums of e_{n->te} theta_n
   if (p.ctrl != nullptr && chunk == 0 && threadIdx.x == 0) {
     p.ctrl[1 + seq] = 0u;            // group barrier counter of this sequence
     if (seq == 0) p.ctrl[0] = 0u;    // error word of the call
@@ -46,9 +48,10 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
     th[n] = ok ? p.theta[g0 + t0 + n] : 0.f;
   }
   __syncthreads();
+  __shared__ float Gv[BC];
   if (threadIdx.x < BC) {
     const int n = threadIdx.x;
-    for (int t = 0; t < BC; ++t) F[t][n] = 0.f;
+    for (int t = 0; t < BC; ++t) F[t][n] = 0.0;
     if (n < nb) {
       float K = 1.f, e = 1.f;
       F[n][n] = th[n];
@@ -57,9 +60,9 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
         K = (1.f - al[t]) * K + e;
         F[t][n] = K * th[n];
       }
-      G[n] = e * th[n];
+      Gv[n] = e * th[n];
     } else {
-      G[n] = 0.f;
+      Gv[n] = 0.f;
     }
   }
   if (threadIdx.x == 64) {
@@ -79,14 +82,32 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
     oP[0] = e0;
   }
   __syncthreads();
-  // window row w <-> token i = t0 - (c-1) + w (relative to the call start)
+  // row prefix sums: F[t][n] <- sum_{m <= n} F[t][m];  G[n + 1] = sum_{m <= n} Gv[m]
+  if (threadIdx.x < BC) {
+    const int t = threadIdx.x;
+    double acc = 0.0;
+    for (int n = 0; n < BC; ++n) {
+      acc += F[t][n];
+      F[t][n] = acc;
+    }
+  } else if (threadIdx.x == BC) {
+    double acc = 0.0;
+    G[0] = 0.0;
+    for (int n = 0; n < BC; ++n) {
+      acc += (double)Gv[n];
+      G[n + 1] = acc;
+    }
+  }
+  __syncthreads();
+  // window row w <-> token i = t0 - (c-1) + w (relative to the call start):
+  // C_{tt,w} = sum of F[tt][n] over n in [max(t0, i), min(t0 + tt, i + c - 1)]
   for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) {
     const int tt = idx / WP, w = idx % WP;
     const int i = t0 - (c - 1) + w;
     float s = 0.f;
     if (tt < nb && w < BC + c - 1 && i >= -halo_valid && i <= t0 + tt) {
-      const int lo = max(t0, i), hi = min(t0 + tt, i + c - 1);
-      for (int n = lo; n <= hi; ++n) s += F[tt][n - t0];
+      const int lo = max(t0, i) - t0, hi = min(t0 + tt, i + c - 1) - t0;
+      s = (float)(F[tt][hi] - (lo > 0 ? F[tt][lo - 1] : 0.0));
     }
     oC[tt * WP + w] = s;
   }
@@ -144,8 +165,9 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
     const int i = t0 - (c - 1) + w;
     float sm = 0.f, ss = 0.f;
     if (w < BC + c - 1 && i >= -halo_valid && i <= te) {
-      const int lo = max(t0, i), hi = min(te, i + c - 1);
-      for (int n = lo; n <= hi; ++n) { sm += F[nb - 1][n - t0]; ss += G[n - t0]; }
+      const int lo = max(t0, i) - t0, hi = min(te, i + c - 1) - t0;
+      sm = (float)(F[nb - 1][hi] - (lo > 0 ? F[nb - 1][lo - 1] : 0.0));
+      ss = (float)(G[hi + 1] - G[lo]);
     }
     ocM[w] = sm;
     ocS[w] = ss;
