@@ -37,6 +37,22 @@ __device__ __forceinline__ int fresh(int x) {
   return x;
 }
 
+// Raw buffer access (gfx9 descriptor: base, no stride, byte size; the third
+// config dword 0x00020000 is the plain 32-bit raw-buffer format of gfx9
+// parts).  Out-of-range accesses return zero / are dropped by the hardware.
+// A per-lane byte offset in a VGPR plus a wave-uniform one in an SGPR keeps
+// the address arithmetic off the vector ALU.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store4(const f32x4& v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
+}
+
 // Row-major operand (k contiguous), natural k order: lane reads k0+8g .. +7 of row row0 + (l & 15).
 __device__ __forceinline__ bf16x8 ld_nat(const bf16* base, int ld, int row0, int k0, int lane) {
   return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));

@@ -389,31 +389,37 @@ stream_mlp_kernel(ShardedParams p) {
   // (W1 [H][D], W2 [DV][H], the momentum alike), read by the first pass and
   // written by the last, and the tile-major copy in the workspace used by the
   // passes in between, in which every access of a wave is one contiguous
-  // 1 KB block.  tiled = true selects the copy.
-  float* T1 = reinterpret_cast<float*>(xw + S::xTS);
-  float* TS1 = T1 + (size_t)H * D;
-  float* T2 = TS1 + (size_t)H * D;
-  float* TS2 = T2 + (size_t)H * D;
-  auto at1 = [&](float* rowmajor, float* tiles, bool tiled, int J, int t) -> f32x4* {
-    const int l = fresh(threadIdx.x);
-    f32x4* a = reinterpret_cast<f32x4*>(tiles) + ((J * 4 + (l >> 6)) * ND + t) * 64 + (l & 63);
-    f32x4* b = reinterpret_cast<f32x4*>(rowmajor + J * HJ * D + (l >> 2 & ~15 | (l & 15)) * D + 4 * (l >> 4 & 3) + 16 * t);
-    return tiled ? a : b;
+  // 1 KB block.  Buffer accesses: a per-lane byte offset (constant for the
+  // call) and a wave-uniform scalar offset; the layout is chosen by selecting
+  // descriptor and offsets, so exactly one access is issued.
+  const int wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rT = buffer_of(xw + S::xTS, 4u * H * D * 4);
+  const __amdgpu_buffer_rsrc_t rW = buffer_of(W1g, 2u * H * D * 4);
+  const __amdgpu_buffer_rsrc_t rM = buffer_of(S1g, mom ? 2u * H * D * 4 : 0u);
+  const int vT = (threadIdx.x & 63) * 16;                                   // tile-major
+  const int vW1 = (threadIdx.x & 15) * D * 4 + ((threadIdx.x >> 4) & 3) * 16;  // row-major W1 / S1
+  const int vW2 = (threadIdx.x & 15) * H * 4 + ((threadIdx.x >> 4) & 3) * 16;  // row-major W2 / S2
+  // which: 0 = W1, 1 = S1
+  auto ld1 = [&](int which, bool tiled, int J, int t) -> f32x4 {
+    const int so_t = ((J * 4 + wave_s) * ND + t) * 1024 + which * H * D * 4;
+    const int so_r = (J * HJ + 16 * wave_s) * D * 4 + 64 * t;
+    return buf_load4(tiled ? rT : which ? rM : rW, tiled ? vT : vW1, tiled ? so_t : so_r);
   };
-  auto at2 = [&](float* rowmajor, float* tiles, bool tiled, int J, int a_, int bb) -> f32x4* {
-    const int l = fresh(threadIdx.x);
-    f32x4* a = reinterpret_cast<f32x4*>(tiles) + ((J * 4 + (l >> 6)) * (NU * NDT) + a_ * NDT + bb) * 64 + (l & 63);
-    f32x4* b = reinterpret_cast<f32x4*>(rowmajor + J * HJ + (S::DVW * (l >> 6) + (l & 15)) * H + 4 * (l >> 4 & 3) +
-                                        16 * bb * H + 16 * a_);
-    return tiled ? a : b;
+  auto st1 = [&](const f32x4& v, int which, bool tiled, int J, int t) {
+    const int so_t = ((J * 4 + wave_s) * ND + t) * 1024 + which * H * D * 4;
+    const int so_r = (J * HJ + 16 * wave_s) * D * 4 + 64 * t;
+    buf_store4(v, tiled ? rT : which ? rM : rW, tiled ? vT : vW1, tiled ? so_t : so_r);
   };
-  auto w1_at = [&](int J, int t) {
-    const int l = fresh(threadIdx.x);
-    return J * HJ * D + (l >> 2 & ~15 | (l & 15)) * D + 4 * (l >> 4 & 3) + 16 * t;
+  // which: 0 = W2, 1 = S2
+  auto ld2 = [&](int which, bool tiled, int J, int a, int bb) -> f32x4 {
+    const int so_t = ((J * 4 + wave_s) * (NU * NDT) + a * NDT + bb) * 1024 + (2 + which) * H * D * 4;
+    const int so_r = H * D * 4 + (S::DVW * wave_s + 16 * bb) * H * 4 + (J * HJ + 16 * a) * 4;
+    return buf_load4(tiled ? rT : which ? rM : rW, tiled ? vT : vW2, tiled ? so_t : so_r);
   };
-  auto w2_at = [&](int J, int a, int bb) {
-    const int l = fresh(threadIdx.x);
-    return J * HJ + (S::DVW * (l >> 6) + (l & 15)) * H + 4 * (l >> 4 & 3) + 16 * bb * H + 16 * a;
+  auto st2 = [&](const f32x4& v, int which, bool tiled, int J, int a, int bb) {
+    const int so_t = ((J * 4 + wave_s) * (NU * NDT) + a * NDT + bb) * 1024 + (2 + which) * H * D * 4;
+    const int so_r = H * D * 4 + (S::DVW * wave_s + 16 * bb) * H * 4 + (J * HJ + 16 * a) * 4;
+    buf_store4(v, tiled ? rT : which ? rM : rW, tiled ? vT : vW2, tiled ? so_t : so_r);
   };
 
   // State prefetch, one super tile ahead, into loop-carried registers: the
@@ -424,13 +430,13 @@ stream_mlp_kernel(ShardedParams p) {
   auto prefetch = [&](int J, bool tiled) {
 #pragma unroll
     for (int t = 0; t < ND; ++t) {
-      pW1[t] = *at1(W1g, T1, tiled, J, t);
-      pS1[t] = mom ? *at1(S1g, TS1, tiled, J, t) : zero4();
+      pW1[t] = ld1(0, tiled, J, t);
+      pS1[t] = mom ? ld1(1, tiled, J, t) : zero4();
     }
 #pragma unroll
     for (int a = 0; a < NU; ++a)
 #pragma unroll
-      for (int bb = 0; bb < NDT; ++bb) pW2[a][bb] = *at2(W2g, T2, tiled, J, a, bb);
+      for (int bb = 0; bb < NDT; ++bb) pW2[a][bb] = ld2(0, tiled, J, a, bb);
   };
 
   // lane-ordered exchange of per-lane accumulator tiles with the partner
@@ -478,11 +484,11 @@ stream_mlp_kernel(ShardedParams p) {
     for (int J = J0; J < J0 + NJ; ++J) {
       f32x4 W1T[ND], W2T[NU][NDT];
 #pragma unroll
-      for (int t = 0; t < ND; ++t) W1T[t] = *reinterpret_cast<const f32x4*>(W1g + w1_at(J, t));
+      for (int t = 0; t < ND; ++t) W1T[t] = ld1(0, false, J, t);
 #pragma unroll
       for (int a = 0; a < NU; ++a)
 #pragma unroll
-        for (int bb = 0; bb < NDT; ++bb) W2T[a][bb] = *reinterpret_cast<const f32x4*>(W2g + w2_at(J, a, bb));
+        for (int bb = 0; bb < NDT; ++bb) W2T[a][bb] = ld2(0, false, J, a, bb);
       f32x4 z[NT];
 #pragma unroll
       for (int m = 0; m < NT; ++m) z[m] = zero4();
@@ -665,8 +671,8 @@ stream_mlp_kernel(ShardedParams p) {
           W1T[t][r] = Ate * w1 + Bte * s1 - um[r];
           S1T[t][r] = Pc * s1 - us[r];
         }
-        *at1(W1g, T1, dst_t, J, t) = W1T[t];
-        if (mom) *at1(S1g, TS1, dst_t, J, t) = S1T[t];
+        st1(W1T[t], 0, dst_t, J, t);
+        if (mom) st1(S1T[t], 1, dst_t, J, t);
       }
       __syncthreads();   // Ah complete; every wave is done with the W2 image
 
@@ -697,8 +703,8 @@ stream_mlp_kernel(ShardedParams p) {
       for (int a = 0; a < NU; ++a)
 #pragma unroll
         for (int bb = 0; bb < NDT; ++bb) {
-          W2T[a][bb] = *at2(W2g, T2, src_t, J, a, bb);
-          S2T[a][bb] = mom ? *at2(S2g, TS2, src_t, J, a, bb) : zero4();
+          W2T[a][bb] = ld2(0, src_t, J, a, bb);
+          S2T[a][bb] = mom ? ld2(1, src_t, J, a, bb) : zero4();
         }
       // (the next pass's first tile is fetched after the chunk inputs are staged)
       if (J + 1 < J0 + NJ) prefetch(J + 1, src_t);
@@ -759,8 +765,8 @@ stream_mlp_kernel(ShardedParams p) {
               W2T[a][bb][r] = Ate * w2 + Bte * s2 - um[r];
               S2T[a][bb][r] = Pc * s2 - us[r];
             }
-            *at2(W2g, T2, dst_t, J, a, bb) = W2T[a][bb];
-            if (mom) *at2(S2g, TS2, dst_t, J, a, bb) = S2T[a][bb];
+            st2(W2T[a][bb], 0, dst_t, J, a, bb);
+            if (mom) st2(S2T[a][bb], 1, dst_t, J, a, bb);
           }
         }
       }
