@@ -63,7 +63,7 @@ struct TShape {
   //   Xa, Xb : window keys of this chunk and the next [WP][LX] (ping-pong)
   //   Xq     : queries [BC][LX];  Q1 [BC][L1Q] (read 8 bytes at a time);  D2 [WP][LV]
   //   AT     : A^T of the super tile [HJ][LT];  at the end of a pass Q2^T [WP][LQ]
-  //   W2     : bf16 image W2^T [DV][LH];  after its use the next chunk's A' [WP][LH];
+  //   W2     : bf16 image W2^T [DV][LH];  after its use the next chunk's A'^T [HJ][LT];
   //            between passes, with Ah, the value rows of the next window [WP][LV]
   //   Ah     : retrieval activations of the super tile [BC][LH]
   //   Cm     : the weights C_{t,i} of the chunk, bf16 [BC][WP]
@@ -73,7 +73,7 @@ struct TShape {
   static constexpr size_t oD2 = oQ1 + align_up((size_t)BC * L1Q * 2, 256);
   static constexpr size_t oAT = oD2 + align_up((size_t)WP * LV * 2, 256);
   static constexpr size_t oW2 = oAT + align_up(mx((size_t)HJ * LT, (size_t)WP * LQ) * 2, 256);
-  static constexpr size_t oAh = oW2 + align_up(mx((size_t)DV * LH, (size_t)WP * LH) * 2, 256);
+  static constexpr size_t oAh = oW2 + align_up(mx((size_t)DV * LH, (size_t)HJ * LT) * 2, 256);
   static constexpr size_t oCm = oAh + align_up((size_t)BC * LH * 2, 256);  // C [BC][WP] (bf16)
   static constexpr size_t oF = oCm + align_up((size_t)BC * WP * 2, 256);   // cA, cB, cM, cS, P, sg
   static constexpr size_t lds = oF + (2 * BC + 3 * WP + 4) * 4;   // + s*gamma of the window rows
@@ -87,7 +87,12 @@ struct TShape {
   // the state between passes, tile-major: W1, S1, W2, S2 (fp32), each wave's
   // f32x4 tile 1 KB contiguous
   static constexpr size_t xTS = 0;
-  static constexpr size_t xYh = xTS + 4ull * H * D * 4;
+  // A = gelu(Z) and gelu'(Z) of every super tile for the next pass (bf16,
+  // NT lane-ordered 1 KB chunks per wave and tile): saves the next pass the
+  // recomputation of Z
+  static constexpr size_t xAG = xTS + 4ull * H * D * 4;
+  static constexpr size_t ag_bytes = (size_t)(H / HJ) * NW * NT * 1024;
+  static constexpr size_t xYh = xAG + ag_bytes;
   static constexpr size_t xYp = xYh + 2ull * G * NT * NDT * tile_bytes;
   static constexpr size_t xbytes = G == 1 ? xYh : xYp + 2ull * G * NQ * NDT * tile_bytes;
   static_assert(D == DV, "one tile-major stride for both layers");
@@ -396,6 +401,7 @@ stream_mlp_kernel(ShardedParams p) {
   const __amdgpu_buffer_rsrc_t rT = buffer_of(xw + S::xTS, 4u * H * D * 4);
   const __amdgpu_buffer_rsrc_t rW = buffer_of(W1g, 2u * H * D * 4);
   const __amdgpu_buffer_rsrc_t rM = buffer_of(S1g, mom ? 2u * H * D * 4 : 0u);
+  const __amdgpu_buffer_rsrc_t rAG = buffer_of(xw + S::xAG, (unsigned)S::ag_bytes);
   const int vT = (threadIdx.x & 63) * 16;                                   // tile-major
   const int vW1 = (threadIdx.x & 15) * D * 4 + ((threadIdx.x >> 4) & 3) * 16;  // row-major W1 / S1
   const int vW2 = (threadIdx.x & 15) * H * 4 + ((threadIdx.x >> 4) & 3) * 16;  // row-major W2 / S2
@@ -426,8 +432,10 @@ stream_mlp_kernel(ShardedParams p) {
   // W1/S1 rows of the tile and the W2 values of its bf16 image.  They are
   // issued after the loads the current tile still waits for (vmcnt retires in
   // order), so no wait in the current tile covers them.
-  f32x4 pW1[ND], pS1[ND], pW2[NU][NDT];
+  f32x4 pW1[ND], pS1[ND], pW2[NU][NDT], pAG[NT];
   auto prefetch = [&](int J, bool tiled) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) pAG[i] = buf_load4(rAG, vT, ((J * 4 + wave_s) * NT + i) * 1024);
 #pragma unroll
     for (int t = 0; t < ND; ++t) {
       pW1[t] = ld1(0, tiled, J, t);
@@ -437,6 +445,54 @@ stream_mlp_kernel(ShardedParams p) {
     for (int a = 0; a < NU; ++a)
 #pragma unroll
       for (int bb = 0; bb < NDT; ++bb) pW2[a][bb] = ld2(0, tiled, J, a, bb);
+  };
+
+  // Forward of super tile J on a window Xs with first-layer rows W1 (this
+  // wave's 16 units): Z [tok x unit] = Xs W1^T, A = gelu(Z) -> An^T [unit][tok]
+  // in LDS, and A, gelu'(Z) saved (bf16, lane order) for the pass that will
+  // update this tile with this window.
+  auto forward_tile = [&](const bf16* Xs, const f32x4 (&W1)[ND], int J) {
+    const int lane = fresh(threadIdx.x) & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+    f32x4 z1[NT];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) z1[m] = zero4();
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      const bf16x8 bw = tiles_to_frag(W1[2 * s], W1[2 * s + 1]);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) z1[m] = mma(ld_perm(Xs, LX, 16 * m, 32 * s, lane), bw, z1[m]);
+    }
+    bf16x8 ca[NT / 2], cd[NT / 2];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      bf16x4 a4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a, da;
+        gelu_and_prime(z1[m][r], a, da);
+        a4[r] = (bf16)a;
+        ca[m / 2][4 * (m % 2) + r] = a4[r];
+        cd[m / 2][4 * (m % 2) + r] = (bf16)da;
+      }
+      *reinterpret_cast<bf16x4*>(An + (16 * wave + c16) * LT + 16 * m + 4 * g) = a4;
+    }
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) {
+      buf_store4(__builtin_bit_cast(f32x4, ca[i]), rAG, vT, ((J * 4 + wave_s) * NT + i) * 1024);
+      buf_store4(__builtin_bit_cast(f32x4, cd[i]), rAG, vT, ((J * 4 + wave_s) * NT + NT / 2 + i) * 1024);
+    }
+  };
+  // A' W2'^T of the tile into the window sums (after An^T is complete)
+  auto window_sums = [&](const f32x4 (&W2)[NU][NDT]) {
+    const int lane = fresh(threadIdx.x) & 63;
+#pragma unroll
+    for (int s = 0; s < HJ / 32; ++s)
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        const bf16x8 bw = tiles_to_frag(W2[2 * s][bb], W2[2 * s + 1][bb]);
+#pragma unroll
+        for (int m = 0; m < NT; ++m) yh[m][bb] = mma(ld_tr_perm(An, LT, 16 * m, 32 * s, lane), bw, yh[m][bb]);
+      }
   };
 
   // lane-ordered exchange of per-lane accumulator tiles with the partner
@@ -489,31 +545,9 @@ stream_mlp_kernel(ShardedParams p) {
       for (int a = 0; a < NU; ++a)
 #pragma unroll
         for (int bb = 0; bb < NDT; ++bb) W2T[a][bb] = ld2(0, false, J, a, bb);
-      f32x4 z[NT];
-#pragma unroll
-      for (int m = 0; m < NT; ++m) z[m] = zero4();
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        const bf16x8 aw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
-#pragma unroll
-        for (int m = 0; m < NT; ++m) z[m] = mma(aw, ld_perm(Xc, LX, 16 * m, 32 * s, lane), z[m]);
-      }
-#pragma unroll
-      for (int m = 0; m < NT; ++m) {
-        bf16x4 a4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a4[r] = (bf16)gelu(z[m][r]);
-        *reinterpret_cast<bf16x4*>(An + (16 * m + c16) * LH + 16 * wave + 4 * g) = a4;
-      }
+      forward_tile(Xc, W1T, J);
       __syncthreads();
-#pragma unroll
-      for (int s = 0; s < HJ / 32; ++s)
-#pragma unroll
-        for (int bb = 0; bb < NDT; ++bb) {
-          const bf16x8 bw = tiles_to_frag(W2T[2 * s][bb], W2T[2 * s + 1][bb]);
-#pragma unroll
-          for (int m = 0; m < NT; ++m) yh[m][bb] = mma(ld_perm(An, LH, 16 * m, 32 * s, lane), bw, yh[m][bb]);
-        }
+      window_sums(W2T);
       __syncthreads();
     }
     if constexpr (G > 1) {
@@ -570,25 +604,18 @@ stream_mlp_kernel(ShardedParams p) {
           *reinterpret_cast<bf16x4*>(W2L + (dvw + 16 * bb + c16) * LH + 16 * a + 4 * g) =
               bf16x4{(bf16)w[0], (bf16)w[1], (bf16)w[2], (bf16)w[3]};
         }
-      // ---- Z = X W1^T [tok x 16 units]; A -> AT [unit][tok]; z keeps gelu'(Z)
+      // ---- A = gelu(Z) and gelu'(Z) of this tile at this chunk's window, saved
+      // by the previous pass (or the prologue): A -> AT [unit][tok], z = gelu'
       f32x4 z[NT];
 #pragma unroll
-      for (int m = 0; m < NT; ++m) z[m] = zero4();
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        const bf16x8 bw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
-#pragma unroll
-        for (int m = 0; m < NT; ++m) z[m] = mma(ld_perm(Xc, LX, 16 * m, 32 * s, lane), bw, z[m]);
-      }
-#pragma unroll
       for (int m = 0; m < NT; ++m) {
+        const bf16x8 ca = __builtin_bit_cast(bf16x8, pAG[m / 2]);
+        const bf16x8 cd = __builtin_bit_cast(bf16x8, pAG[NT / 2 + m / 2]);
         bf16x4 a4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float a, da;
-          gelu_and_prime(z[m][r], a, da);
-          a4[r] = (bf16)a;
-          z[m][r] = da;
+          a4[r] = ca[4 * (m % 2) + r];
+          z[m][r] = (float)cd[4 * (m % 2) + r];
         }
         *reinterpret_cast<bf16x4*>(AT + (16 * wave + c16) * LT + 16 * m + 4 * g) = a4;
       }
@@ -676,25 +703,8 @@ stream_mlp_kernel(ShardedParams p) {
       }
       __syncthreads();   // Ah complete; every wave is done with the W2 image
 
-      // ---- next chunk's forward on the updated rows: A' = gelu(X' W1'^T) -> An [tok][unit]
-      if (more) {
-        f32x4 z1[NT];
-#pragma unroll
-        for (int m = 0; m < NT; ++m) z1[m] = zero4();
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-          const bf16x8 aw = tiles_to_frag(W1T[2 * s], W1T[2 * s + 1]);
-#pragma unroll
-          for (int m = 0; m < NT; ++m) z1[m] = mma(aw, ld_perm(Xn, LX, 16 * m, 32 * s, lane), z1[m]);
-        }
-#pragma unroll
-        for (int m = 0; m < NT; ++m) {
-          bf16x4 a4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) a4[r] = (bf16)gelu(z1[m][r]);
-          *reinterpret_cast<bf16x4*>(An + (16 * m + c16) * LH + 16 * wave + 4 * g) = a4;
-        }
-      }
+      // ---- next chunk's forward on the updated rows: A' -> An^T, saved for the next pass
+      if (more) forward_tile(Xn, W1T, J);
 
       // ======== W2 side: W2/S2 (this wave's value rows, recently loaded: in L2),
       // then the next tile's prefetch
@@ -772,15 +782,8 @@ stream_mlp_kernel(ShardedParams p) {
       }
       // ---- next chunk's window sums A' W2'^T [tok x this wave's dv]
       if (more) {
-        __syncthreads();   // An complete
-#pragma unroll
-        for (int s = 0; s < HJ / 32; ++s)
-#pragma unroll
-          for (int bb = 0; bb < NDT; ++bb) {
-            const bf16x8 bw = tiles_to_frag(W2T[2 * s][bb], W2T[2 * s + 1][bb]);
-#pragma unroll
-            for (int m = 0; m < NT; ++m) yh[m][bb] = mma(ld_perm(An, LH, 16 * m, 32 * s, lane), bw, yh[m][bb]);
-          }
+        __syncthreads();   // An^T complete
+        window_sums(W2T);
       }
       __syncthreads();
     }
