@@ -17,6 +17,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the kernels read every accumulator back
+    # into vector arithmetic, and accumulation registers only add copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 
