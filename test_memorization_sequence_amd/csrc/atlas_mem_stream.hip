@@ -181,7 +181,7 @@ stream_mlp_kernel(ShardedParams p) {
   constexpr int NCV = (BC * WP / 8 + 255) / 256;    // C (bf16) vectors per thread
   struct WinRegs { bf16x8 x[NXV]; };
   struct ChunkRegs { bf16x8 q[NQV], q1[NQ1V], cc[NCV]; float ca, cb, cm, cs, cp, sg; };
-  struct D2Regs { bf16 vv[NT][4][NDT]; };
+  struct D2Regs { bf16x4 vv[NT][NDT]; };
 
   // window keys of chunk ch (halo rows from the state, invalid rows zero)
   auto load_window = [&](int ch, WinRegs& R, auto halo_tag) {
@@ -317,75 +317,86 @@ stream_mlp_kernel(ShardedParams p) {
     }
   };
 
-  // D2 of chunk ch from the sums yh = A W2^T of its window (Xw: its window keys)
+  // D2 of chunk ch from the sums yh = A W2^T of its window (Xw: its window
+  // keys).  yh is held transposed: tile [m][bb] gives lane l the window row
+  // w = 16 m + (l & 15) and the four value columns o = dvw + 16 bb + 4 (l >> 4) + r,
+  // so every access below moves four adjacent bf16.
   f32x4 yh[NT][NDT];
-  auto load_d2 = [&](int ch, D2Regs& R, auto halo_tag) {
+  auto load_d2 = [&](int ch, D2Regs& R) {
     const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
-    constexpr bool HALO = decltype(halo_tag)::value;
     const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
 #pragma unroll
-    for (int m = 0; m < NT; ++m)
+    for (int m = 0; m < NT; ++m) {
+      const int w = 16 * m + c16, i = t0 - (c - 1) + w;
+      const bool ok = row_ok(w, t0, te);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int w = 16 * m + 4 * g + r, i = t0 - (c - 1) + w;
-        const bool ok = row_ok(w, t0, te);
+      for (int bb = 0; bb < NDT; ++bb) {
+        const int o = dvw + 16 * bb + 4 * g;
+        bf16x4 x = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+        if (ok) {
+          if (i >= 0) x = *reinterpret_cast<const bf16x4*>(v + (size_t)i * DV + o);
+          else
 #pragma unroll
-        for (int bb = 0; bb < NDT; ++bb) {
-          const int o = dvw + 16 * bb + c16;
-          if (HALO) {
-            R.vv[m][r][bb] = !ok ? (bf16)0.f : i >= 0 ? v[(size_t)i * DV + o] : (bf16)hv[(c - 1 + i) * DV + o];
-          } else {
-            const bf16 x = v[(unsigned)min(max(i, 0), N - 1) * DV + o];
-            R.vv[m][r][bb] = ok ? x : (bf16)0.f;
-          }
+            for (int r = 0; r < 4; ++r) x[r] = (bf16)hv[(c - 1 + i) * DV + o + r];
         }
+        R.vv[m][bb] = x;
       }
+    }
   };
-  // needs sgw of chunk ch in LDS
-  auto finish_d2 = [&](int ch, const D2Regs& R, const bf16* Xw, auto halo_tag) {
+  // one element of D2 (rows outside the window have sg = 0)
+  auto d2_of = [&](float sg, float x, float y, float vv) {
+    float t = y + (res ? x : 0.f);
+    t = dot ? 0.f : t;
+    return (bf16)(sg * (t - vv));
+  };
+  // chunk 0 (window rows may come from the halo); needs sgw of the chunk in LDS
+  auto finish_d2 = [&](int ch, const D2Regs& R, const bf16* Xw) {
     const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
-    constexpr bool HALO = decltype(halo_tag)::value;
     const int t0 = ch * BC;
 #pragma unroll
-    for (int m = 0; m < NT; ++m)
+    for (int m = 0; m < NT; ++m) {
+      const int w = 16 * m + c16, i = t0 - (c - 1) + w;
+      const float sg = sgw[w];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int w = 16 * m + 4 * g + r, i = t0 - (c - 1) + w;
-        const float sg = sgw[w];
+      for (int bb = 0; bb < NDT; ++bb) {
+        const int o = dvw + 16 * bb + 4 * g;
+        float xr[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (D == DV) {
+          if (i >= 0 || sg == 0.f) {
+            const bf16x4 x4 = *reinterpret_cast<const bf16x4*>(Xw + w * LX + o);
 #pragma unroll
-        for (int bb = 0; bb < NDT; ++bb) {
-          const int o = dvw + 16 * bb + c16;
-          const float vv = (float)R.vv[m][r][bb];
-          float val;
-          if (dot) {
-            val = -sg * vv;
+            for (int r = 0; r < 4; ++r) xr[r] = (float)x4[r];
           } else {
-            // rows outside the window have sg = 0
-            const float rr = !res ? 0.f : !HALO || i >= 0 || sg == 0.f ? (float)Xw[w * LX + o] : hk[(c - 1 + i) * D + o];
-            val = sg * (rr + yh[m][bb][r] - vv);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xr[r] = hk[(c - 1 + i) * D + o + r];
           }
-          D2[w * LV + o] = (bf16)val;
         }
+        bf16x4 d;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[r] = d2_of(sg, xr[r], yh[m][bb][r], (float)R.vv[m][bb][r]);
+        *reinterpret_cast<bf16x4*>(D2 + w * LV + o) = d;
       }
+    }
   };
-
-  // the same from the staged value rows Vw (chunks >= 1)
+  // chunks >= 1: from the staged value rows Vw, branch-free
   auto finish_d2_lds = [&](const bf16* Vw, const bf16* Xw) {
     const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
 #pragma unroll
-    for (int m = 0; m < NT; ++m)
+    for (int m = 0; m < NT; ++m) {
+      const int w = 16 * m + c16;
+      const float sg = sgw[w];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int w = 16 * m + 4 * g + r;
-        const float sg = sgw[w];
+      for (int bb = 0; bb < NDT; ++bb) {
+        const int o = dvw + 16 * bb + 4 * g;
+        const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(Vw + w * LV + o);
+        bf16x4 x4 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+        if constexpr (D == DV) x4 = *reinterpret_cast<const bf16x4*>(Xw + w * LX + o);
+        bf16x4 d;
 #pragma unroll
-        for (int bb = 0; bb < NDT; ++bb) {
-          const int o = dvw + 16 * bb + c16;
-          const float vv = (float)Vw[w * LV + o];
-          const float val = dot ? -sg * vv : sg * ((res ? (float)Xw[w * LX + o] : 0.f) + yh[m][bb][r] - vv);
-          D2[w * LV + o] = (bf16)val;
-        }
+        for (int r = 0; r < 4; ++r) d[r] = d2_of(sg, (float)x4[r], yh[m][bb][r], (float)v4[r]);
+        *reinterpret_cast<bf16x4*>(D2 + w * LV + o) = d;
       }
+    }
   };
 
   // state tiles of super tile J (see the layout notes at the top): uniform
@@ -491,7 +502,7 @@ stream_mlp_kernel(ShardedParams p) {
       for (int bb = 0; bb < NDT; ++bb) {
         const bf16x8 bw = tiles_to_frag(W2[2 * s][bb], W2[2 * s + 1][bb]);
 #pragma unroll
-        for (int m = 0; m < NT; ++m) yh[m][bb] = mma(ld_tr_perm(An, LT, 16 * m, 32 * s, lane), bw, yh[m][bb]);
+        for (int m = 0; m < NT; ++m) yh[m][bb] = mma(bw, ld_tr_perm(An, LT, 16 * m, 32 * s, lane), yh[m][bb]);
       }
   };
 
@@ -528,7 +539,7 @@ stream_mlp_kernel(ShardedParams p) {
     load_window(0, w0, std::true_type{});
     if (nchunks > 1) load_window(1, w1, std::false_type{});
     load_chunk(0, c0, std::true_type{});
-    load_d2(0, d0, std::true_type{});
+    load_d2(0, d0);
     store_window(Xc, w0);
     if (nchunks > 1) store_window(Xn, w1);
     store_chunk(c0);
@@ -558,7 +569,7 @@ stream_mlp_kernel(ShardedParams p) {
       xadd(xYh_at(par, 1 - pm), yh);
     }
     prefetch(J0, false);
-    finish_d2(0, d0, Xc, std::true_type{});
+    finish_d2(0, d0, Xc);
     __syncthreads();
   }
 
@@ -568,7 +579,10 @@ stream_mlp_kernel(ShardedParams p) {
     const bool more = ch + 1 < nchunks;
     const bool src_t = ch > 0, dst_t = more;   // state layouts read and written by this pass
     const float Ate = cA[ce], Bte = cB[ce], Pc = cP[0];
-    f32x4 yw[NQ][NDT], ys[NQ][NDT], q2[NT];   // Ah W2^T, Ah S2^T (scaled by A_q, B_q at the end)
+    // Ah W2^T, Ah S2^T (scaled by A_q, B_q at the end), held transposed like
+    // yh: tile [m][bb] gives lane l the query row 16 m + (l & 15) and the value
+    // columns dvw + 16 bb + 4 (l >> 4) + r
+    f32x4 yw[NQ][NDT], ys[NQ][NDT], q2[NT];
 #pragma unroll
     for (int m = 0; m < NQ; ++m)
 #pragma unroll
@@ -739,8 +753,8 @@ stream_mlp_kernel(ShardedParams p) {
           const bf16x8 ah = ld_perm(Ah, LH, 16 * m, 32 * s, lane);
 #pragma unroll
           for (int bb = 0; bb < NDT; ++bb) {
-            yw[m][bb] = mma(ah, bw[bb], yw[m][bb]);
-            if (mom) ys[m][bb] = mma(ah, bs[bb], ys[m][bb]);
+            yw[m][bb] = mma(bw[bb], ah, yw[m][bb]);
+            if (mom) ys[m][bb] = mma(bs[bb], ah, ys[m][bb]);
           }
         }
       }
@@ -800,26 +814,26 @@ stream_mlp_kernel(ShardedParams p) {
     }
     }
     __syncthreads();
-    // this member's part of y - q = A_q Ah W2^T + B_q Ah S2^T - Q2 D2
+    // this member's part of y - q = A_q Ah W2^T + B_q Ah S2^T - Q2 D2 (transposed tiles)
     f32x4 yp[NQ][NDT];
     {
-      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, dvw = S::DVW * (threadIdx.x >> 6);
+      const int lane = fresh(threadIdx.x) & 63, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
 #pragma unroll
-      for (int m = 0; m < NQ; ++m)
+      for (int m = 0; m < NQ; ++m) {
+        const float a = cA[16 * m + c16], b = cB[16 * m + c16];
 #pragma unroll
         for (int bb = 0; bb < NDT; ++bb) {
           f32x4 acc = zero4();
 #pragma unroll
           for (int k0 = 0; k0 < WP; k0 += 32)
-            acc = mma(ld_tr_nat(Q2T, LQ, 16 * m, k0, lane), ld_tr_nat(D2, LV, dvw + 16 * bb, k0, lane), acc);
+            acc = mma(ld_tr_nat(D2, LV, dvw + 16 * bb, k0, lane), ld_tr_nat(Q2T, LQ, 16 * m, k0, lane), acc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int qq = 16 * m + 4 * g + r;
-            yp[m][bb][r] = fmaf(cA[qq], yw[m][bb][r], fmaf(cB[qq], ys[m][bb][r], -acc[r]));
-          }
+          for (int r = 0; r < 4; ++r) yp[m][bb][r] = fmaf(a, yw[m][bb][r], fmaf(b, ys[m][bb][r], -acc[r]));
         }
+      }
     }
-    // G = 2: exchange the partial sums; each member writes half of the output rows
+    // G = 2: exchange the partial sums; each member writes half of the output
+    // rows, and hands the partner only the tiles of the partner's half
     constexpr int MQ = NQ / G;
     const int mlo = pm * MQ;
     if constexpr (G > 1) {
@@ -828,8 +842,9 @@ stream_mlp_kernel(ShardedParams p) {
         f32x4* d = reinterpret_cast<f32x4*>(xw + xYp_at(par, pm)) + threadIdx.x;
 #pragma unroll
         for (int m = 0; m < NQ; ++m)
+          if (m < mlo || m >= mlo + MQ)
 #pragma unroll
-          for (int bb = 0; bb < NDT; ++bb) d[(m * NDT + bb) * 256] = yp[m][bb];
+            for (int bb = 0; bb < NDT; ++bb) d[(m * NDT + bb) * 256] = yp[m][bb];
       }
       if (more) xput(xYh_at(par, pm), yh);
       group_barrier(ctr, G * (++nbar), err);
@@ -842,20 +857,22 @@ stream_mlp_kernel(ShardedParams p) {
           for (int bb = 0; bb < NDT; ++bb) yp[m][bb] += d[(m * NDT + bb) * 256];
     }
     {
+      // four adjacent values of one output row per lane and tile
       const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
 #pragma unroll
       for (int m = 0; m < NQ; ++m) {
-        if (m < mlo || m >= mlo + MQ) continue;
+        const int qq = 16 * m + c16;
+        if (m < mlo || m >= mlo + MQ || t0 + qq > te) continue;
 #pragma unroll
-        for (int bb = 0; bb < NDT; ++bb)
+        for (int bb = 0; bb < NDT; ++bb) {
+          const int o = dvw + 16 * bb + 4 * g;
+          bf16x4 x4 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+          if constexpr (D == DV) x4 = *reinterpret_cast<const bf16x4*>(Xq + qq * LX + o);
+          bf16x4 y4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int qq = 16 * m + 4 * g + r, o = dvw + 16 * bb + c16;
-            if (t0 + qq <= te) {
-              const float rr = res ? (float)Xq[qq * LX + o] : 0.f;
-              out[(size_t)(t0 + qq) * DV + o] = (bf16)(yp[m][bb][r] + rr);
-            }
-          }
+          for (int r = 0; r < 4; ++r) y4[r] = (bf16)(yp[m][bb][r] + (res ? (float)x4[r] : 0.f));
+          *reinterpret_cast<bf16x4*>(out + (size_t)(t0 + qq) * DV + o) = y4;
+        }
       }
     }
     __syncthreads();
