@@ -107,6 +107,11 @@ static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
 static const StreamVariant* find_streamed(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
+  // the kernel addresses one sequence's inputs and coefficients through
+  // 32-bit buffer offsets (below 1 GiB each)
+  const size_t nch = ((size_t)c->seq_len + c->chunk - 1) / c->chunk;
+  if ((size_t)c->seq_len * c->d_k * 2 > (1u << 30) || nch * coef_stride(c->chunk, c->chunk + c->window - 1 + 31, true, true) * 4 > (1u << 30))
+    return nullptr;
   const int need_w = c->chunk + c->window - 1;
   const StreamVariant* best = nullptr;
   for (const StreamVariant& v : kStreamed) {

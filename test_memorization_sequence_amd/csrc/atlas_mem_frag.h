@@ -53,6 +53,39 @@ __device__ __forceinline__ void buf_store4(const f32x4& v, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
 }
 
+// Buffer load that writes LDS directly (no registers): lane l's BYTES (4 or
+// 16) go to LDS at dst + l * BYTES, dst wave-uniform.  A voff beyond the
+// buffer's size reads zeros.  Completion is counted by vmcnt like any load:
+// wait for it (s_waitcnt vmcnt) before a barrier after which other waves read.
+template <int BYTES>
+__device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 4, voff, 0, 0, 0);
+}
+// wait for every vector-memory access of this wave (loads to LDS included)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
+constexpr int kZeroOffset = 0x7FFFFF00;   // beyond every buffer the kernels address
+// Copy of NR rows into LDS by direct loads: row r lands at dst + r * LP
+// (bytes), its first RB bytes read from byte src(r) of buffer rs (src < 0:
+// zeros), the padding bytes LP - RB zeroed.  The region is cut into
+// 64 * GR-byte blocks, one load per block, spread over the NW waves.
+template <int GR, int NR, int RB, int LP, int NW, class Src>
+__device__ __forceinline__ void rows_to_lds(__amdgpu_buffer_rsrc_t rs, char* dst, int wave_s, int lane, Src src) {
+  static_assert((GR == 4 || GR == 16) && LP % GR == 0 && RB % GR == 0 && RB <= LP, "granules");
+  constexpr int TOTAL = NR * LP, BLK = 64 * GR, NB = (TOTAL + BLK - 1) / BLK;
+#pragma unroll
+  for (int b0 = 0; b0 < NB; b0 += NW) {
+    const int b = b0 + wave_s;
+    if (b < NB) {
+      const int off = b * BLK + lane * GR, row = off / LP, cb = off - row * LP;
+      const int so = src(row);
+      const int voff = cb < RB && so >= 0 ? so + cb : kZeroOffset;
+      if (TOTAL % BLK == 0 || off < TOTAL) buf_load_lds<GR>(rs, dst + b * BLK, voff);
+    }
+  }
+}
+
 // Row-major operand (k contiguous), natural k order: lane reads k0+8g .. +7 of row row0 + (l & 15).
 __device__ __forceinline__ bf16x8 ld_nat(const bf16* base, int ld, int row0, int k0, int lane) {
   return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));

@@ -75,7 +75,9 @@ struct TShape {
   static constexpr size_t oW2 = oAT + align_up(mx((size_t)HJ * LT, (size_t)WP * LQ) * 2, 256);
   static constexpr size_t oAh = oW2 + align_up(mx((size_t)DV * LH, (size_t)HJ * LT) * 2, 256);
   static constexpr size_t oCm = oAh + align_up((size_t)BC * LH * 2, 256);  // C [BC][WP] (bf16)
-  static constexpr size_t oF = oCm + align_up((size_t)BC * WP * 2, 256);   // cA, cB, cM, cS, P, sg
+  // gate coefficients in the order of the coefficient kernel's block (A, B,
+  // P and 3 spare words, cM, cS), then gamma of the window rows
+  static constexpr size_t oF = oCm + align_up((size_t)BC * WP * 2, 256);
   static constexpr size_t lds = oF + (2 * BC + 3 * WP + 4) * 4;   // + s*gamma of the window rows
   static_assert(lds <= 163840, "LDS budget of one CU");
   static_assert(oAh - oW2 + align_up((size_t)BC * LH * 2, 256) >= (size_t)WP * LV * 2, "value rows fit W2 + Ah");
@@ -96,6 +98,7 @@ struct TShape {
   static constexpr size_t xYp = xYh + 2ull * G * NT * NDT * tile_bytes;
   static constexpr size_t xbytes = G == 1 ? xYh : xYp + 2ull * G * NQ * NDT * tile_bytes;
   static_assert(D == DV, "one tile-major stride for both layers");
+  static_assert(WP <= 2 * BC, "windows of chunks >= 1 start inside the call");
 };
 
 template <class S>
@@ -158,10 +161,10 @@ stream_mlp_kernel(ShardedParams p) {
   bf16* Cm = reinterpret_cast<bf16*>(smem + S::oCm);
   float* cA = reinterpret_cast<float*>(smem + S::oF);
   float* cB = cA + BC;
-  float* cM = cB + BC;
+  float* cP = cB + BC;
+  float* cM = cP + 4;
   float* cS = cM + WP;
-  float* cP = cS + WP;
-  float* sgw = cP + 4;   // s * gamma of the window rows (0 outside the window)
+  float* sgw = cS + WP;   // gamma of the window rows (0 outside the window)
 
   const int dvw = S::DVW * wave;
   const int nchunks = (N + BC - 1) / BC;
@@ -258,8 +261,8 @@ stream_mlp_kernel(ShardedParams p) {
     {
       const int i = t0 - (c - 1) + tid;
       const bool ok = tid < WP && row_ok(tid, t0, te);
-      if (HALO) R.sg = ok ? s_grad * (i >= 0 ? gam_in[i] : hg[c - 1 + i]) : 0.f;
-      else R.sg = ok ? s_grad * gam_in[(unsigned)min(max(i, 0), N - 1)] : 0.f;
+      if (HALO) R.sg = ok ? (i >= 0 ? gam_in[i] : hg[c - 1 + i]) : 0.f;
+      else R.sg = ok ? gam_in[(unsigned)min(max(i, 0), N - 1)] : 0.f;
     }
   };
   auto store_chunk = [&](const ChunkRegs& R) {
@@ -288,33 +291,6 @@ stream_mlp_kernel(ShardedParams p) {
     if (tid < WP) { cM[tid] = R.cm; cS[tid] = R.cs; }
     if (tid == 0) cP[0] = R.cp;
     if (tid < WP) sgw[tid] = R.sg;
-  };
-
-  // value rows of chunk ch's window (chunks >= 1: no halo), staged through LDS
-  constexpr int NVV = (WP * (DV / 8) + 255) / 256;
-  struct VRegs { bf16x8 x[NVV]; };
-  auto load_vwin = [&](int ch, VRegs& R) {
-    const int tid = fresh(threadIdx.x);
-    const int t0 = ch * BC, te = min(N, t0 + BC) - 1;
-#pragma unroll
-    for (int u = 0; u < NVV; ++u) {
-      const int e = tid + 256 * u, w = e / (DV / 8), d8 = (e % (DV / 8)) * 8, i = t0 - (c - 1) + w;
-      const bool ok = (WP * (DV / 8) % 256 == 0 || e < WP * (DV / 8)) && row_ok(w, t0, te);
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(v + (unsigned)min(max(i, 0), N - 1) * DV + d8);
-      bf16x8 zz;
-#pragma unroll
-      for (int z = 0; z < 8; ++z) zz[z] = (bf16)0.f;
-      R.x[u] = ok ? x : zz;
-    }
-  };
-  auto store_vwin = [&](bf16* Vdst, const VRegs& R) {
-    const int tid = fresh(threadIdx.x);
-#pragma unroll
-    for (int u = 0; u < NVV; ++u) {
-      const int e = tid + 256 * u;
-      if (WP * (DV / 8) % 256 == 0 || e < WP * (DV / 8))
-        *reinterpret_cast<bf16x8*>(Vdst + (e / (DV / 8)) * LV + (e % (DV / 8)) * 8) = R.x[u];
-    }
   };
 
   // D2 of chunk ch from the sums yh = A W2^T of its window (Xw: its window
@@ -356,7 +332,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       const int w = 16 * m + c16, i = t0 - (c - 1) + w;
-      const float sg = sgw[w];
+      const float sg = s_grad * sgw[w];
 #pragma unroll
       for (int bb = 0; bb < NDT; ++bb) {
         const int o = dvw + 16 * bb + 4 * g;
@@ -384,7 +360,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       const int w = 16 * m + c16;
-      const float sg = sgw[w];
+      const float sg = s_grad * sgw[w];
 #pragma unroll
       for (int bb = 0; bb < NDT; ++bb) {
         const int o = dvw + 16 * bb + 4 * g;
@@ -529,6 +505,48 @@ stream_mlp_kernel(ShardedParams p) {
     for (int m = 0; m < NT; ++m)
 #pragma unroll
       for (int bb = 0; bb < NDT; ++bb) a[m][bb] += t[m][bb];
+  };
+
+  // The inputs of chunk cn (cn >= 1) that the passes read from LDS, and the
+  // keys of chunk cn + 1's window, loaded straight into LDS (no registers), so
+  // the loads overlap the exchange with the partner; invalid rows read zeros.
+  // Needs every wave past its last read of the target regions.
+  auto stage_next = [&](int cn) {
+    const int lane = fresh(threadIdx.x) & 63;
+    const int t0n = cn * BC, ten = min(N, t0n + BC) - 1, wb = t0n - (c - 1);
+    const __amdgpu_buffer_rsrc_t rV = buffer_of(v, (unsigned)N * DV * 2);
+    const __amdgpu_buffer_rsrc_t rK = buffer_of(k, (unsigned)N * D * 2);
+    const __amdgpu_buffer_rsrc_t rQ = buffer_of(q, (unsigned)N * D * 2);
+    const __amdgpu_buffer_rsrc_t rG = buffer_of(gam_in, (unsigned)N * 4);
+    const __amdgpu_buffer_rsrc_t rC = buffer_of(coef_seq, (unsigned)nchunks * p.coef_stride * 4);
+    const int cb = cn * p.coef_stride * 4;   // byte offset of the chunk's coefficient block
+    // value rows of the window -> W2L [WP][LV] (with the Ah region)
+    // (window rows of chunks >= 1 start at token >= 0: valid iff w < W and token <= te)
+    auto win = [&](int w, int wb_, int te_) { return (w < W) & (wb_ + w <= te_); };
+    rows_to_lds<16, WP, DV * 2, LV * 2, S::NW>(rV, reinterpret_cast<char*>(W2L), wave_s, lane,
+                                               [&](int w) { return win(w, wb, ten) ? (wb + w) * DV * 2 : -1; });
+    // keys of the window of chunk cn + 1 -> Xc (free: the pass is done with it)
+    if (cn + 1 < nchunks) {
+      const int t0w = t0n + BC, tew = min(N, t0w + BC) - 1;
+      rows_to_lds<16, WP, D * 2, LX * 2, S::NW>(rK, reinterpret_cast<char*>(Xc), wave_s, lane, [&](int w) {
+        return win(w, t0w - (c - 1), tew) ? (t0w - (c - 1) + w) * D * 2 : -1;
+      });
+    }
+    // queries -> Xq [BC][LX]
+    rows_to_lds<16, BC, D * 2, LX * 2, S::NW>(rQ, reinterpret_cast<char*>(Xq), wave_s, lane,
+                                              [&](int n) { return t0n + n <= ten ? (t0n + n) * D * 2 : -1; });
+    // A, B, P, cM, cS (fp32, the block's layout) -> cA ..
+    constexpr int NCF = (2 * BC + 4 + 2 * WP) * 4;
+    rows_to_lds<16, 1, NCF, NCF, S::NW>(rC, reinterpret_cast<char*>(cA), wave_s, lane, [&](int) { return cb; });
+    // Q1 (bf16 [BC][WP]) -> [BC][L1Q]
+    rows_to_lds<4, BC, WP * 2, L1Q * 2, S::NW>(rC, reinterpret_cast<char*>(Q1), wave_s, lane,
+                                               [&](int n) { return cb + oQ1g * 4 + n * WP * 2; });
+    // C (bf16 [BC][WP]) -> Cm
+    rows_to_lds<16, 1, BC * WP * 2, BC * WP * 2, S::NW>(rC, reinterpret_cast<char*>(Cm), wave_s, lane,
+                                                        [&](int) { return cb + oCbg * 4; });
+    // gamma of the window rows
+    rows_to_lds<4, WP, 4, 4, S::NW>(rG, reinterpret_cast<char*>(sgw), wave_s, lane,
+                                    [&](int w) { return win(w, wb, ten) ? (wb + w) * 4 : -1; });
   };
 
   // ---- prologue: inputs of chunk 0 (and the keys of chunk 1), then chunk 0's forward
@@ -836,8 +854,22 @@ stream_mlp_kernel(ShardedParams p) {
     // rows, and hands the partner only the tiles of the partner's half
     constexpr int MQ = NQ / G;
     const int mlo = pm * MQ;
+    // the residual part of this member's output rows, read before the next
+    // chunk's queries replace Xq
+    bf16x4 xres[MQ][NDT];
+    {
+      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
+#pragma unroll
+      for (int mi = 0; mi < MQ; ++mi)
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb) {
+          xres[mi][bb] = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+          if constexpr (D == DV)
+            xres[mi][bb] = *reinterpret_cast<const bf16x4*>(Xq + (16 * (mlo + mi) + c16) * LX + dvw + 16 * bb + 4 * g);
+        }
+    }
+    const int par = ch & 1;
     if constexpr (G > 1) {
-      const int par = ch & 1;
       {
         f32x4* d = reinterpret_cast<f32x4*>(xw + xYp_at(par, pm)) + threadIdx.x;
 #pragma unroll
@@ -848,6 +880,13 @@ stream_mlp_kernel(ShardedParams p) {
       }
       if (more) xput(xYh_at(par, pm), yh);
       group_barrier(ctr, G * (++nbar), err);
+    } else {
+      __syncthreads();
+    }
+    // ---- the next chunk's inputs into LDS, in flight during the partner's
+    // reads and the output stores
+    if (more) stage_next(ch + 1);
+    if constexpr (G > 1) {
       if (more) xadd(xYh_at(par, 1 - pm), yh);
       const f32x4* d = reinterpret_cast<const f32x4*>(xw + xYp_at(par, 1 - pm)) + threadIdx.x;
 #pragma unroll
@@ -860,41 +899,22 @@ stream_mlp_kernel(ShardedParams p) {
       // four adjacent values of one output row per lane and tile
       const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
 #pragma unroll
-      for (int m = 0; m < NQ; ++m) {
-        const int qq = 16 * m + c16;
-        if (m < mlo || m >= mlo + MQ || t0 + qq > te) continue;
+      for (int mi = 0; mi < MQ; ++mi) {
+        const int m = mlo + mi, qq = 16 * m + c16;
+        if (t0 + qq > te) continue;
 #pragma unroll
         for (int bb = 0; bb < NDT; ++bb) {
           const int o = dvw + 16 * bb + 4 * g;
-          bf16x4 x4 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-          if constexpr (D == DV) x4 = *reinterpret_cast<const bf16x4*>(Xq + qq * LX + o);
           bf16x4 y4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) y4[r] = (bf16)(yp[m][bb][r] + (res ? (float)x4[r] : 0.f));
+          for (int r = 0; r < 4; ++r) y4[r] = (bf16)(yp[m][bb][r] + (res ? (float)xres[mi][bb][r] : 0.f));
           *reinterpret_cast<bf16x4*>(out + (size_t)(t0 + qq) * DV + o) = y4;
         }
       }
     }
-    __syncthreads();
-    // ---- the next chunk's inputs, requested together (one round trip); its
-    // value rows go through the tile buffers, free now, to form D2
     if (more) {
-      {
-        VRegs vr;
-        WinRegs wr;
-        load_vwin(ch + 1, vr);
-        if (ch + 2 < nchunks) load_window(ch + 2, wr, std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        store_vwin(W2L, vr);
-        if (ch + 2 < nchunks) store_window(Xc, wr);
-      }
-      {
-        ChunkRegs cr;
-        load_chunk(ch + 1, cr, std::false_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        store_chunk(cr);
-      }
-      __syncthreads();
+      wait_vmem();       // this wave's loads into LDS have landed
+      __syncthreads();   // and everyone's
       finish_d2_lds(W2L, Xn);
       prefetch(J0, dst_t);
       bf16* tmp = Xc;
