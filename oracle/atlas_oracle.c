@@ -26,6 +26,11 @@
  * sec. 2 "Deep Memory Module"): linear f(x) = M x, or the two-layer MLP
  * f(x) = [r +] W2 gelu(W1 x) with the exact erf GELU and no biases.
  * phi follows ATLAS review sec. 3.1 "Polynomial Feature Mapping".
+ * Attentional biases (the loss of one token, e = f - v): squared error, the
+ * dot product, and from the Miras review, "Alternative Attentional Biases",
+ * the l_p loss |e|_p^p / p and the Huber loss with a threshold delta_t per
+ * token (squared error while |e|_2 <= delta_t, else delta_t times the l1
+ * error; the choice is made for the token as a whole).
  *
  * The per-token gradient is written out from the chain rule; its
  * factors are the per-token error and hidden activations.  No blocking,
@@ -131,20 +136,38 @@ void oracle_memory_apply(const oracle_config* cfg, const double* theta,
   apply(cfg, theta, x, r, y, NULL);
 }
 
+static double sgn(double x) { return x > 0.0 ? 1.0 : x < 0.0 ? -1.0 : 0.0; }
+
+/* derivative of |e|^p / p: sign(e) |e|^(p-1)  (p >= 1; zero at e = 0) */
+static double lp_slope(double e, double p) { return e == 0.0 ? 0.0 : sgn(e) * pow(fabs(e), p - 1.0); }
+
 /* Factors of one token's gradient at theta:
  *   linear: dY (d_v)            G = dY x^T
  *   MLP   : d1 (h), d2 (d_v), a (h)   G = { d1 x^T , d2 a^T }
- * dY / d2 = dLoss/df: L2 -> s*gamma*(f - v);  DOT -> -s*gamma*v.          */
+ * dY / d2 = dLoss/df, with e = f - v:
+ *   L2 -> s*gamma*e;  DOT -> -s*gamma*v;  LP -> s*gamma*sign(e)|e|^(p-1)
+ *   (elementwise);  HUBER -> s*gamma*e while |e|_2 <= delta, else
+ *   s*gamma*delta*sign(e): one choice for the whole token.                 */
 static void grad_factors(const oracle_config* cfg, const double* th,
                          const double* x, const double* r, const double* v,
-                         double gamma, double* d1, double* d2, double* a) {
+                         double gamma, double delta, double* d1, double* d2, double* a) {
   const int D = oracle_feature_dim(cfg), dv = cfg->d_v, h = cfg->hidden;
   const double s = cfg->grad_scale;
   double* f = (double*)malloc(sizeof(double) * dv);
   double* z = cfg->memory == ORC_MLP ? (double*)malloc(sizeof(double) * h) : NULL;
   apply(cfg, th, x, r, f, z);
-  for (int o = 0; o < dv; ++o)
-    d2[o] = cfg->bias == ORC_BIAS_L2 ? s * gamma * (f[o] - v[o]) : -s * gamma * v[o];
+  int huber_small = 0;
+  if (cfg->bias == ORC_BIAS_HUBER) {
+    double n2 = 0.0;
+    for (int o = 0; o < dv; ++o) n2 += (f[o] - v[o]) * (f[o] - v[o]);
+    huber_small = sqrt(n2) <= delta;
+  }
+  for (int o = 0; o < dv; ++o) {
+    if (cfg->bias == ORC_BIAS_L2) d2[o] = s * gamma * (f[o] - v[o]);
+    else if (cfg->bias == ORC_BIAS_DOT) d2[o] = -s * gamma * v[o];
+    else if (cfg->bias == ORC_BIAS_LP) d2[o] = s * gamma * lp_slope(f[o] - v[o], cfg->bias_p);
+    else d2[o] = s * gamma * (huber_small ? f[o] - v[o] : delta * sgn(f[o] - v[o]));
+  }
   if (cfg->memory == ORC_MLP) {
     const double* W2 = th + (long)h * D;
     for (int j = 0; j < h; ++j) {
@@ -174,17 +197,23 @@ static void add_grad(const oracle_config* cfg, const double* x, const double* d1
     for (int j = 0; j < h; ++j) gW2[(long)o * h + j] += d2[o] * a[j];
 }
 
-void oracle_token_grad(const oracle_config* cfg, const double* theta,
-                       const double* x, const double* r, const double* v,
-                       double gamma, double* grad) {
+void oracle_token_grad_ex(const oracle_config* cfg, const double* theta,
+                          const double* x, const double* r, const double* v,
+                          double gamma, double delta, double* grad) {
   const int dv = cfg->d_v, h = cfg->hidden > 0 ? cfg->hidden : 1;
   double* d1 = (double*)malloc(sizeof(double) * h);
   double* d2 = (double*)malloc(sizeof(double) * dv);
   double* a = (double*)malloc(sizeof(double) * h);
   memset(grad, 0, sizeof(double) * oracle_param_count(cfg));
-  grad_factors(cfg, theta, x, r, v, gamma, d1, d2, a);
+  grad_factors(cfg, theta, x, r, v, gamma, delta, d1, d2, a);
   add_grad(cfg, x, d1, d2, a, grad);
   free(d1); free(d2); free(a);
+}
+
+void oracle_token_grad(const oracle_config* cfg, const double* theta,
+                       const double* x, const double* r, const double* v,
+                       double gamma, double* grad) {
+  oracle_token_grad_ex(cfg, theta, x, r, v, gamma, 0.0, grad);
 }
 
 static int config_ok(const oracle_config* c) {
@@ -198,20 +227,22 @@ static int config_ok(const oracle_config* c) {
   } else if (c->memory != ORC_LINEAR) {
     return 0;
   }
-  return c->bias == ORC_BIAS_L2 || c->bias == ORC_BIAS_DOT;
+  if (c->bias == ORC_BIAS_LP) return c->bias_p >= 1.0 && c->bias_p < 1e6;
+  return c->bias == ORC_BIAS_L2 || c->bias == ORC_BIAS_DOT || c->bias == ORC_BIAS_HUBER;
 }
 
 /* One sequence. */
 static void run_sequence(const oracle_config* cfg, const double* q, const double* k,
                          const double* v, const double* al, const double* et,
-                         const double* th, const double* ga, double* W, double* S,
-                         double* hk, double* hv, double* hg, int64_t* count,
+                         const double* th, const double* ga, const double* dl, double* W, double* S,
+                         double* hk, double* hv, double* hg, double* hd, int64_t* count,
                          double* out) {
   const int N = cfg->seq_len, dk = cfg->d_k, dv = cfg->d_v, c = cfg->window;
   const int b = cfg->chunk, h = cfg->hidden > 0 ? cfg->hidden : 1;
   const int D = oracle_feature_dim(cfg);
   const long P = oracle_param_count(cfg);
   const int halo = c - 1;
+  const int huber = cfg->bias == ORC_BIAS_HUBER;
   /* tokens before this call that still exist (sequence start truncates) */
   const int halo_valid = (int)(*count < halo ? *count : halo);
 
@@ -233,15 +264,17 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
     if (lo < -halo_valid) lo = -halo_valid;
     for (int i = lo; i <= te; ++i) {
       const double *ki, *vi;
-      double gi;
+      double gi, di = 0.0;
       if (i >= 0) {
         ki = k + (long)i * dk; vi = v + (long)i * dv; gi = ga[i];
+        if (huber) di = dl[i];
       } else {
         ki = hk + (long)(halo + i) * dk; vi = hv + (long)(halo + i) * dv; gi = hg[halo + i];
+        if (huber) di = hd[halo + i];
       }
       const int w = i - lo;
       oracle_phi(cfg, ki, X + (long)w * D);
-      grad_factors(cfg, Wc, X + (long)w * D, ki, vi, gi, D1 + (long)w * h,
+      grad_factors(cfg, Wc, X + (long)w * D, ki, vi, gi, di, D1 + (long)w * h,
                    D2 + (long)w * dv, A + (long)w * h);
     }
     for (int n = t0; n <= te; ++n) {
@@ -269,36 +302,41 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
     double* nk = (double*)malloc(sizeof(double) * halo * dk);
     double* nv = (double*)malloc(sizeof(double) * halo * dv);
     double* ng = (double*)malloc(sizeof(double) * halo);
+    double* nd = (double*)malloc(sizeof(double) * halo);
     for (int j = 0; j < halo; ++j) {
       const int i = N - halo + j;
       if (i >= 0) {
         memcpy(nk + (long)j * dk, k + (long)i * dk, sizeof(double) * dk);
         memcpy(nv + (long)j * dv, v + (long)i * dv, sizeof(double) * dv);
         ng[j] = ga[i];
+        nd[j] = huber ? dl[i] : 0.0;
       } else {
         memcpy(nk + (long)j * dk, hk + (long)(halo + i) * dk, sizeof(double) * dk);
         memcpy(nv + (long)j * dv, hv + (long)(halo + i) * dv, sizeof(double) * dv);
         ng[j] = hg[halo + i];
+        nd[j] = huber ? hd[halo + i] : 0.0;
       }
     }
     memcpy(hk, nk, sizeof(double) * halo * dk);
     memcpy(hv, nv, sizeof(double) * halo * dv);
     memcpy(hg, ng, sizeof(double) * halo);
-    free(nk); free(nv); free(ng);
+    if (huber) memcpy(hd, nd, sizeof(double) * halo);
+    free(nk); free(nv); free(ng); free(nd);
   }
   *count += N;
 
   free(Wc); free(g); free(X); free(D1); free(D2); free(A); free(xq); free(Sloc);
 }
 
-int oracle_forward(const oracle_config* cfg,
-                   const double* q, const double* k, const double* v,
-                   const double* alpha, const double* eta,
-                   const double* theta, const double* gamma,
-                   double* mem, double* mom,
-                   double* halo_k, double* halo_v, double* halo_g,
-                   int64_t* count, double* out) {
+int oracle_forward_ex(const oracle_config* cfg,
+                      const double* q, const double* k, const double* v,
+                      const double* alpha, const double* eta,
+                      const double* theta, const double* gamma, const double* delta,
+                      double* mem, double* mom,
+                      double* halo_k, double* halo_v, double* halo_g, double* halo_d,
+                      int64_t* count, double* out) {
   if (!config_ok(cfg)) return -1;
+  if (cfg->bias == ORC_BIAS_HUBER && (!delta || (cfg->window > 1 && !halo_d))) return -1;
   const long N = cfg->seq_len, dk = cfg->d_k, dv = cfg->d_v, halo = cfg->window - 1;
   const long P = oracle_param_count(cfg);
   int threads = 1;
@@ -312,10 +350,24 @@ int oracle_forward(const oracle_config* cfg,
     for (int s = 0; s < cfg->n_seq; ++s) {
       run_sequence(cfg, q + s * N * dk, k + s * N * dk, v + s * N * dv,
                    alpha + s * N, eta + s * N, theta + s * N, gamma + s * N,
+                   delta ? delta + s * N : NULL,
                    mem + s * P, mom + s * P,
                    halo_k + s * halo * dk, halo_v + s * halo * dv, halo_g + s * halo,
+                   halo_d ? halo_d + s * halo : NULL,
                    count + s, out + s * N * dv);
     }
   }
   return threads;
+}
+
+int oracle_forward(const oracle_config* cfg,
+                   const double* q, const double* k, const double* v,
+                   const double* alpha, const double* eta,
+                   const double* theta, const double* gamma,
+                   double* mem, double* mom,
+                   double* halo_k, double* halo_v, double* halo_g,
+                   int64_t* count, double* out) {
+  if (cfg->bias == ORC_BIAS_HUBER) return -1;   /* needs the thresholds */
+  return oracle_forward_ex(cfg, q, k, v, alpha, eta, theta, gamma, NULL, mem, mom,
+                           halo_k, halo_v, halo_g, NULL, count, out);
 }

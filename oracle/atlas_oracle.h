@@ -24,6 +24,11 @@
  *     after token t's update (Titans review, section 3.1 "Retrieving a
  *     Memory").
  *
+ * Attentional biases besides the squared error (Miras review, "Alternative
+ * Attentional Biases"): the l_p loss, and the Huber loss whose threshold
+ * delta_t is an input per token and which picks, per token, the squared
+ * error or delta_t times the absolute (l1) error.
+ *
  * Parity unpinned: the combination MLP memory + window c > 1 + chunk b > 1 +
  * momentum is fixed by no closed form on the pages; it is pinned only through
  * the special cases that reduce to one (see tests/test_oracle_pins.py).
@@ -39,7 +44,7 @@ extern "C" {
 
 enum { ORC_LINEAR = 0, ORC_MLP = 1 };
 enum { ORC_PHI_ID = 0, ORC_PHI_POLY2 = 1, ORC_PHI_RAW_POLY2 = 2 };
-enum { ORC_BIAS_L2 = 0, ORC_BIAS_DOT = 1 };
+enum { ORC_BIAS_L2 = 0, ORC_BIAS_DOT = 1, ORC_BIAS_LP = 2, ORC_BIAS_HUBER = 3 };
 
 typedef struct {
   int n_seq;        /* independent sequences (batch * heads)                 */
@@ -53,8 +58,14 @@ typedef struct {
   int window;       /* c >= 1                                                 */
   int chunk;        /* b >= 1                                                 */
   int momentum;     /* 0: eta treated as 0 and S not carried                  */
-  int bias;         /* ORC_BIAS_L2: gamma/2*s*|f-v|^2 ; ORC_BIAS_DOT: -s*gamma*<f,v> */
+  int bias;         /* attentional bias of one token (e = f - v), times s*gamma:
+                       ORC_BIAS_L2   : |e|_2^2 / 2
+                       ORC_BIAS_DOT  : -<f, v>
+                       ORC_BIAS_LP   : sum_o |e_o|^p / p
+                       ORC_BIAS_HUBER: |e|_2^2 / 2 if |e|_2 <= delta, else
+                                       delta * (|e|_1 - delta / 2)          */
   double grad_scale;/* s                                                      */
+  double bias_p;    /* p >= 1 of ORC_BIAS_LP                                  */
 } oracle_config;
 
 /* Sets the OpenMP thread count used by oracle_forward (n <= 0: default). */
@@ -80,6 +91,10 @@ void oracle_memory_apply(const oracle_config* cfg, const double* theta,
 void oracle_token_grad(const oracle_config* cfg, const double* theta,
                        const double* x, const double* r, const double* v,
                        double gamma, double* grad);
+/* The same with the token's Huber threshold delta (ORC_BIAS_HUBER).       */
+void oracle_token_grad_ex(const oracle_config* cfg, const double* theta,
+                          const double* x, const double* r, const double* v,
+                          double gamma, double delta, double* grad);
 
 /* Run the memory over one call's tokens for every sequence.
  *   q, k   [n_seq][seq_len][d_k]     v [n_seq][seq_len][d_v]
@@ -100,6 +115,16 @@ int oracle_forward(const oracle_config* cfg,
                    double* mem, double* mom,
                    double* halo_k, double* halo_v, double* halo_g,
                    int64_t* count, double* out);
+/* The same with the per-token Huber thresholds delta [n_seq][seq_len] and
+ * their halo halo_d [n_seq][c-1] (in/out), both used only by
+ * ORC_BIAS_HUBER (which oracle_forward rejects); NULL otherwise.          */
+int oracle_forward_ex(const oracle_config* cfg,
+                      const double* q, const double* k, const double* v,
+                      const double* alpha, const double* eta,
+                      const double* theta, const double* gamma, const double* delta,
+                      double* mem, double* mom,
+                      double* halo_k, double* halo_v, double* halo_g, double* halo_d,
+                      int64_t* count, double* out);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ LIB_PATH = os.environ.get("ATLAS_ORACLE_LIB") or os.path.join(HERE, "liboracle.s
 
 LINEAR, MLP = 0, 1
 PHI = {"identity": 0, "poly2": 1, "raw_poly2": 2}
-BIAS = {"l2": 0, "dot": 1}
+BIAS = {"l2": 0, "dot": 1, "lp": 2, "huber": 3}
 
 
 def build(src: str = SRC, out: str | None = None) -> str:
@@ -49,6 +49,7 @@ class OracleConfig(ctypes.Structure):
         ("momentum", ctypes.c_int),
         ("bias", ctypes.c_int),
         ("grad_scale", ctypes.c_double),
+        ("bias_p", ctypes.c_double),
     ]
 
 
@@ -71,20 +72,24 @@ def lib():
         L.oracle_phi.argtypes = [cp, dp, dp]
         L.oracle_memory_apply.argtypes = [cp, dp, dp, dp, dp]
         L.oracle_token_grad.argtypes = [cp, dp, dp, dp, dp, ctypes.c_double, dp]
+        L.oracle_token_grad_ex.argtypes = [cp, dp, dp, dp, dp, ctypes.c_double, ctypes.c_double, dp]
         L.oracle_forward.argtypes = [cp] + [dp] * 7 + [dp] * 5 + [ctypes.POINTER(ctypes.c_int64), dp]
         L.oracle_forward.restype = ctypes.c_int
+        L.oracle_forward_ex.argtypes = [cp] + [dp] * 8 + [dp] * 6 + [ctypes.POINTER(ctypes.c_int64), dp]
+        L.oracle_forward_ex.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
 def make_config(*, n_seq=1, seq_len=0, d_k, d_v, memory="linear", hidden=0, residual=False,
                 feature_map="identity", poly_dims=0, window=1, chunk=1, momentum=False,
-                bias="l2", grad_scale=1.0) -> OracleConfig:
+                bias="l2", grad_scale=1.0, bias_p=2.0) -> OracleConfig:
     return OracleConfig(
         n_seq=n_seq, seq_len=seq_len, d_k=d_k, d_v=d_v,
         memory=MLP if memory == "mlp" else LINEAR, hidden=hidden, residual=int(bool(residual)),
         feature_map=PHI[feature_map], poly_dims=poly_dims, window=window, chunk=chunk,
-        momentum=int(bool(momentum)), bias=BIAS[bias], grad_scale=float(grad_scale))
+        momentum=int(bool(momentum)), bias=BIAS[bias], grad_scale=float(grad_scale),
+        bias_p=float(bias_p))
 
 
 def _p(a: np.ndarray):
@@ -116,10 +121,11 @@ def memory_apply(cfg: OracleConfig, theta, x, r) -> np.ndarray:
     return y
 
 
-def token_grad(cfg: OracleConfig, theta, x, r, v, gamma) -> np.ndarray:
+def token_grad(cfg: OracleConfig, theta, x, r, v, gamma, delta=0.0) -> np.ndarray:
+    """Gradient of one token's weighted loss; delta: its Huber threshold."""
     arrs = [np.ascontiguousarray(a, dtype=np.float64) for a in (theta, x, r, v)]
     g = np.zeros(param_count(cfg))
-    lib().oracle_token_grad(ctypes.byref(cfg), *[_p(a) for a in arrs], float(gamma), _p(g))
+    lib().oracle_token_grad_ex(ctypes.byref(cfg), *[_p(a) for a in arrs], float(gamma), float(delta), _p(g))
     return g
 
 
@@ -132,30 +138,35 @@ def empty_state(cfg: OracleConfig) -> dict:
         "halo_k": np.zeros((S, max(c - 1, 0), cfg.d_k)),
         "halo_v": np.zeros((S, max(c - 1, 0), cfg.d_v)),
         "halo_g": np.zeros((S, max(c - 1, 0))),
+        "halo_d": np.zeros((S, max(c - 1, 0))),
         "count": np.zeros(S, dtype=np.int64),
     }
 
 
 def forward(cfg: OracleConfig, q, k, v, alpha, eta, theta, gamma, state: dict,
-            threads: int | None = None):
-    """Runs one call.  q,k: [S,N,d_k]; v: [S,N,d_v]; gates: [S,N].
+            threads: int | None = None, delta=None):
+    """Runs one call.  q,k: [S,N,d_k]; v: [S,N,d_v]; gates (and delta, the
+    Huber thresholds, needed by that bias only): [S,N].
     `state` (from empty_state or a previous call) is updated in place.
     Returns (out [S,N,d_v], threads_used)."""
     S, N = q.shape[0], q.shape[1]
     cfg = OracleConfig.from_buffer_copy(cfg)
     cfg.n_seq, cfg.seq_len = S, N
-    ins = [np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, alpha, eta, theta, gamma)]
-    for key in ("mem", "mom", "halo_k", "halo_v", "halo_g"):
+    if delta is None:
+        delta = np.zeros((S, N))
+    ins = [np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, alpha, eta, theta, gamma, delta)]
+    state.setdefault("halo_d", np.zeros((S, max(cfg.window - 1, 0))))
+    for key in ("mem", "mom", "halo_k", "halo_v", "halo_g", "halo_d"):
         assert state[key].dtype == np.float64 and state[key].flags["C_CONTIGUOUS"], key
         assert state[key].shape[0] == S, key
     assert state["count"].dtype == np.int64
     out = np.zeros((S, N, cfg.d_v))
     if threads:
         lib().oracle_set_threads(int(threads))
-    used = lib().oracle_forward(
+    used = lib().oracle_forward_ex(
         ctypes.byref(cfg), *[_p(a) for a in ins],
         _p(state["mem"]), _p(state["mom"]), _p(state["halo_k"]), _p(state["halo_v"]),
-        _p(state["halo_g"]), state["count"].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        _p(state["halo_g"]), _p(state["halo_d"]), state["count"].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
         _p(out))
     if used < 0:
         raise ValueError("oracle rejected the configuration")
@@ -165,11 +176,11 @@ def forward(cfg: OracleConfig, q, k, v, alpha, eta, theta, gamma, state: dict,
 def config_for(wl) -> OracleConfig:
     """Oracle configuration for a workload description (any object with the
     workload fields: d_k, d_v, memory, hidden, residual, feature_map,
-    poly_dims, window, chunk, momentum, bias, grad_scale)."""
+    poly_dims, window, chunk, momentum, bias, grad_scale; bias_p if present)."""
     return make_config(d_k=wl.d_k, d_v=wl.d_v, memory=wl.memory, hidden=wl.hidden,
                        residual=wl.residual, feature_map=wl.feature_map, poly_dims=wl.poly_dims,
                        window=wl.window, chunk=wl.chunk, momentum=wl.momentum, bias=wl.bias,
-                       grad_scale=wl.grad_scale)
+                       grad_scale=wl.grad_scale, bias_p=getattr(wl, "bias_p", 2.0))
 
 
 def run_workload(wl, inputs: dict, weights0, seqs=None, n_tokens=None, state=None, threads=None):
@@ -190,6 +201,7 @@ def run_workload(wl, inputs: dict, weights0, seqs=None, n_tokens=None, state=Non
     if state is None:
         state = empty_state(cfg)
         state["mem"][:] = np.asarray(weights0, dtype=np.float64)[seqs]
+    delta = take(inputs["delta"]) if "delta" in inputs else None
     out, used = forward(cfg, *(take(inputs[key]) for key in ("q", "k", "v", "alpha", "eta", "theta", "gamma")),
-                        state, threads=threads)
+                        state, threads=threads, delta=delta)
     return out, state, used

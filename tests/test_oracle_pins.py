@@ -18,14 +18,15 @@ from oracle import oracle as O
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def run(cfg, q, k, v, alpha, eta, theta, gamma, mem0=None, state=None):
+def run(cfg, q, k, v, alpha, eta, theta, gamma, mem0=None, state=None, delta=None):
     """Single-sequence convenience wrapper: arrays without the sequence axis."""
     cfg.n_seq = 1
     st = state if state is not None else O.empty_state(cfg)
     if mem0 is not None:
         st["mem"][0] = np.asarray(mem0, dtype=np.float64).ravel()
     add = lambda a: np.asarray(a, dtype=np.float64)[None]
-    out, _ = O.forward(cfg, add(q), add(k), add(v), add(alpha), add(eta), add(theta), add(gamma), st)
+    out, _ = O.forward(cfg, add(q), add(k), add(v), add(alpha), add(eta), add(theta), add(gamma), st,
+                       delta=None if delta is None else add(delta))
     return out[0], st
 
 
@@ -380,3 +381,147 @@ def test_bad_configs_are_rejected():
     z = np.zeros((1, 2, 3))
     with pytest.raises(ValueError):
         O.forward(cfg, z, z, np.zeros((1, 2, 4)), *[np.zeros((1, 2))] * 4, st)
+
+
+# --------------------------------------------------------------------------- other attentional biases
+# Miras review, "Alternative Attentional Biases": the l_p loss |M(k) - v|_p^p
+# and the Huber loss (squared error below a per-token threshold delta_t, the
+# absolute error above it).  Readings: the l_p loss carries the 1/p that the
+# squared error's 1/2 convention generalises to, so p = 2 is the squared
+# error; the Huber choice is made per token on |e|_2, its large-error branch
+# is delta_t * |e|_1.
+
+def huber_loss(e, delta):
+    n = np.linalg.norm(e)
+    return 0.5 * n * n if n <= delta else delta * (np.sum(np.abs(e)) - 0.5 * delta)
+
+
+@pytest.mark.parametrize("p", [3.0, 1.5])
+@pytest.mark.parametrize("residual", [True, False])
+def test_lp_gradient_matches_finite_differences(p, residual):
+    """Central differences of gamma*s * sum_o |f_o - v_o|^p / p."""
+    rng = np.random.default_rng(40)
+    d, h, gamma, s = 3, 5, 0.7, 1.3
+    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=h, residual=residual, bias="lp",
+                        bias_p=p, grad_scale=s)
+    theta = rng.standard_normal(h * d + d * h)
+    x, v = rng.standard_normal(d), rng.standard_normal(d)
+
+    def loss(th):
+        W1, W2 = th[:h * d].reshape(h, d), th[h * d:].reshape(d, h)
+        f = (x if residual else 0) + W2 @ gelu(W1 @ x)
+        return gamma * s * np.sum(np.abs(f - v) ** p) / p
+
+    g = O.token_grad(cfg, theta, x, x, v, gamma)
+    eps = 1e-6
+    fd = np.array([(loss(theta + eps * e) - loss(theta - eps * e)) / (2 * eps)
+                   for e in np.eye(theta.size)])
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("regime", ["squared", "absolute", "between_norms"])
+def test_huber_gradient_matches_finite_differences(regime):
+    """Central differences of gamma*s * huber(f - v; delta), on both branches
+    and with delta between |e|_2 and |e|_1 (the test uses the l2 norm)."""
+    rng = np.random.default_rng(41)
+    d, h, gamma, s = 3, 5, 0.8, 1.0
+    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=h, residual=True, bias="huber", grad_scale=s)
+    theta = rng.standard_normal(h * d + d * h)
+    x, v = rng.standard_normal(d), rng.standard_normal(d)
+    W1, W2 = theta[:h * d].reshape(h, d), theta[h * d:].reshape(d, h)
+    e = x + W2 @ gelu(W1 @ x) - v
+    n2, n1 = np.linalg.norm(e), np.sum(np.abs(e))
+    delta = {"squared": 2.0 * n1, "absolute": 0.3 * n2, "between_norms": 0.5 * (n1 + n2)}[regime]
+    assert n2 < n1
+
+    def loss(th):
+        W1, W2 = th[:h * d].reshape(h, d), th[h * d:].reshape(d, h)
+        return gamma * s * huber_loss(x + W2 @ gelu(W1 @ x) - v, delta)
+
+    g = O.token_grad(cfg, theta, x, x, v, gamma, delta)
+    eps = 1e-6
+    fd = np.array([(loss(theta + eps * e) - loss(theta - eps * e)) / (2 * eps)
+                   for e in np.eye(theta.size)])
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+def _mixed_run(bias, rng_seed=42, **kw):
+    rng = np.random.default_rng(rng_seed)
+    N, d = 37, 4
+    q, k, v = rand_unit(rng, N, d), rand_unit(rng, N, d), rng.standard_normal((N, d))
+    g = [rng.uniform(0, 0.3, N), rng.uniform(0.3, 0.9, N), rng.uniform(0.05, 0.4, N), rng.uniform(0.2, 1, N)]
+    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=6, residual=True, window=3, chunk=5,
+                        momentum=True, bias=bias, **kw)
+    W0 = np.random.default_rng(rng_seed + 1).standard_normal(O.param_count(cfg)) * 0.5
+    return cfg, (q, k, v, *g), W0
+
+
+def test_lp_with_p2_is_the_squared_error():
+    """|e|_2^2 / 2 is the l_p loss at p = 2: the whole run (MLP, window,
+    chunks, momentum) matches the squared-error bias."""
+    cfg2, args, W0 = _mixed_run("l2")
+    cfgp, _, _ = _mixed_run("lp", bias_p=2.0)
+    want, st2 = run(cfg2, *args, W0)
+    got, stp = run(cfgp, *args, W0)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(stp["mem"], st2["mem"], rtol=1e-12, atol=1e-14)
+
+
+def test_huber_limits():
+    """delta = +inf: always the squared error; delta = 0: the absolute branch
+    times 0, so nothing is ever written and retrieval is the plain forward
+    pass at the initial weights (as with theta = 0)."""
+    cfg2, args, W0 = _mixed_run("l2")
+    cfgh, _, _ = _mixed_run("huber")
+    N = args[0].shape[0]
+    want, st2 = run(cfg2, *args, W0)
+    got, sth = run(cfgh, *args, W0, delta=np.full(N, 1e300))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+    q, k, v, al, et, th, ga = args
+    frozen, _ = run(cfg2, q, k, v, np.zeros(N), et, np.zeros(N), ga, W0)
+    got0, st0 = run(cfgh, q, k, v, np.zeros(N), et, th, ga, W0, delta=np.zeros(N))
+    np.testing.assert_allclose(got0, frozen, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(st0["mem"][0], W0)
+
+
+@pytest.mark.parametrize("bias", ["lp1", "lp3", "huber"])
+def test_scalar_memory_sign_rules(bias):
+    """A 1x1 linear memory, b = c = 1, no decay or momentum: each token does
+    m <- m - theta*gamma*g(m k - v) k, with g(e) = sign(e) (p = 1),
+    e|e| (p = 3), or e if |e| <= delta else delta*sign(e) (Huber); y = m q."""
+    rng = np.random.default_rng(43)
+    N = 30
+    q, k, v = rng.standard_normal((N, 1)), rng.standard_normal((N, 1)), rng.standard_normal((N, 1)) * 2
+    th, ga, dl = rng.uniform(0.05, 0.5, N), rng.uniform(0.3, 1.0, N), rng.uniform(0.2, 2.0, N)
+    kw = {"lp1": dict(bias="lp", bias_p=1.0), "lp3": dict(bias="lp", bias_p=3.0), "huber": dict(bias="huber")}[bias]
+    cfg = O.make_config(d_k=1, d_v=1, window=1, chunk=1, **kw)
+    m, want = 0.4, []
+    for t in range(N):
+        e = m * k[t, 0] - v[t, 0]
+        gx = {"lp1": np.sign(e), "lp3": e * abs(e), "huber": e if abs(e) <= dl[t] else dl[t] * np.sign(e)}[bias]
+        m = m - th[t] * ga[t] * gx * k[t, 0]
+        want.append(m * q[t, 0])
+    out, st = run(cfg, q, k, v, np.zeros(N), np.zeros(N), th, ga, [0.4], delta=dl)
+    np.testing.assert_allclose(out[:, 0], want, rtol=1e-12, atol=1e-14)
+
+
+def test_huber_thresholds_of_the_halo_carry_over():
+    """The last c-1 thresholds travel in the state like the keys, values and
+    gammas: two chunk-aligned calls equal one."""
+    cfg, args, W0 = _mixed_run("huber")
+    N = args[0].shape[0]
+    dl = np.random.default_rng(44).uniform(0.3, 3.0, N)
+    full, st_full = run(cfg, *args, W0, delta=dl)
+    st = O.empty_state(cfg)
+    st["mem"][0] = W0
+    s1 = 15
+    o1, st = run(cfg, *[a[:s1] for a in args], state=st, delta=dl[:s1])
+    o2, st = run(cfg, *[a[s1:] for a in args], state=st, delta=dl[s1:])
+    np.testing.assert_allclose(np.concatenate([o1, o2]), full, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(st["halo_d"], st_full["halo_d"], rtol=0, atol=0)
+
+
+def test_huber_needs_thresholds_and_lp_needs_p_at_least_one():
+    cfg, args, W0 = _mixed_run("lp", bias_p=0.5)
+    with pytest.raises(ValueError):
+        run(cfg, *args, W0)
