@@ -13,9 +13,14 @@
  *                         MLP memory, exact erf GELU, no biases, r the raw
  *                         key/query; Titans review sec. 3.1 "Memory
  *                         Architecture", ATLAS review sec. 2)
- *   loss  = sum over the last c tokens i of gamma_i * s/2 * |f(x_i) - v_i|^2
- *                         (Omega rule, ATLAS review sec. 3.2), or the
- *                         dot-product bias -gamma_i * s * <f(x_i), v_i>
+ *   loss  = sum over the last c tokens i of gamma_i * s * l(f(x_i) - v_i)
+ *                         (Omega rule, ATLAS review sec. 3.2) with the
+ *                         attentional bias l(e) = |e|^2 / 2, or the
+ *                         dot-product bias -gamma_i * s * <f(x_i), v_i>, or
+ *                         (Miras review, "Alternative Attentional Biases")
+ *                         l(e) = sum_o |e_o|^p / p, or the Huber loss with a
+ *                         threshold delta_i per token: |e|_2^2 / 2 while
+ *                         |e|_2 <= delta_i, else delta_i (|e|_1 - delta_i / 2)
  *   chunks of b tokens:   every gradient of a chunk is taken at the weights
  *                         the previous chunk left (ATLAS review sec. 3.3
  *                         "Parallelizing Omega Rule")
@@ -54,7 +59,7 @@ typedef enum {
 
 enum { ATLAS_MEM_LINEAR = 0, ATLAS_MEM_MLP = 1 };
 enum { ATLAS_PHI_IDENTITY = 0, ATLAS_PHI_POLY2 = 1, ATLAS_PHI_RAW_POLY2 = 2 };
-enum { ATLAS_BIAS_L2 = 0, ATLAS_BIAS_DOT = 1 };
+enum { ATLAS_BIAS_L2 = 0, ATLAS_BIAS_DOT = 1, ATLAS_BIAS_LP = 2, ATLAS_BIAS_HUBER = 3 };
 enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
 /* Kernel family.  PER_SEQUENCE: one workgroup per sequence, every operand
  * image kept in a global workspace (all memories and feature maps).
@@ -63,7 +68,8 @@ enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
  * sequence (or a pair of workgroups of one XCD, each with half of the hidden
  * units), the fp32 weights and momentum read and written once per chunk in
  * one fused pass.  SHARDED and STREAMED serve the MLP memory with the
- * identity feature map, d_k == d_v and bf16 io.  AUTO picks the fastest
+ * identity feature map, d_k == d_v and bf16 io (SHARDED: the l2 and
+ * dot-product biases only).  AUTO picks the fastest
  * family measured for the shape: STREAMED where marked so (large hidden
  * layers), else SHARDED, else PER_SEQUENCE.                                 */
 enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3 };
@@ -81,11 +87,16 @@ typedef struct {
   int window;         /* c >= 1, c <= chunk                                     */
   int chunk;          /* b                                                      */
   int momentum;       /* 0: eta is ignored (treated as 0) and S is not stored   */
-  int bias;           /* ATLAS_BIAS_L2 | ATLAS_BIAS_DOT                         */
+  int bias;           /* ATLAS_BIAS_L2 | _DOT | _LP | _HUBER                    */
   int io_dtype;       /* ATLAS_BF16 | ATLAS_F32 for q, k, v, out                */
   float grad_scale;   /* s: 1 matches the printed update rules; 2 is the
                          literal derivative of the squared norm                 */
   int kernel;         /* ATLAS_KERNEL_*                                         */
+  float bias_p;       /* p >= 1 of ATLAS_BIAS_LP (ignored otherwise)            */
+  float sign_alpha;   /* sign(e) in the l_p and Huber slopes: 0 exact; > 0
+                         tanh(sign_alpha * e), the smooth sign of the Miras
+                         review (Remark 5 under "Alternative Attentional
+                         Biases"), which keeps the result continuous in e    */
 } atlas_mem_config;
 
 typedef struct atlas_mem_s* atlas_mem_t;
@@ -98,6 +109,7 @@ typedef struct atlas_mem_s* atlas_mem_t;
  *   halo_k   fp32  [c-1][d_k]  raw keys of the last c-1 tokens seen, oldest first
  *   halo_v   fp32  [c-1][d_v]
  *   halo_g   fp32  [c-1]       their gamma
+ *   halo_d   fp32  [c-1]       their Huber threshold (ATLAS_BIAS_HUBER only)
  *   count    int64             tokens seen so far
  * The caller writes the initial weights, zeroes everything else, and reads
  * the final weights/momentum back.  D is the width of phi(k).              */
@@ -106,6 +118,7 @@ typedef struct {
   size_t weights, momentum, halo_k, halo_v, halo_g, count;
   int feature_dim;    /* D */
   long param_count;   /* P: number of weights (floats) */
+  size_t halo_d;      /* equal to count when the bias has no threshold */
 } atlas_mem_state_layout;
 
 /* Validates cfg, selects the kernels and allocates the device workspace on
@@ -137,12 +150,24 @@ atlas_status atlas_mem_state_layout_of(atlas_mem_t h, atlas_mem_state_layout* ou
  * seq_len == 0 the call does nothing and accepts any pointer.  One handle serves one
  * stream at a time (the workspace is shared by its calls).
  * Errors: INVALID_ARGUMENT (null/misaligned/overlapping pointers, bad
- * handle), HIP (launch failure).  NaN/Inf in the inputs propagate.         */
+ * handle, a handle with ATLAS_BIAS_HUBER: it needs atlas_mem_forward_ex),
+ * HIP (launch failure).  NaN/Inf in the inputs propagate.                  */
 atlas_status atlas_mem_forward(atlas_mem_t h,
                                const void* q, const void* k, const void* v,
                                const float* alpha, const float* eta,
                                const float* theta, const float* gamma,
                                void* state, void* out, void* stream /* hipStream_t */);
+
+/* atlas_mem_forward with the per-token Huber thresholds delta [B][H][N]
+ * fp32 (device, 4-byte aligned; required with ATLAS_BIAS_HUBER, ignored
+ * and may be NULL otherwise).  The Huber bias of the Miras review ("Yaad"):
+ * per token, the squared-error gradient while |f(x_i) - v_i|_2 <= delta_i,
+ * else delta_i * sign(f(x_i) - v_i).  Same semantics and errors otherwise. */
+atlas_status atlas_mem_forward_ex(atlas_mem_t h,
+                                  const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* eta,
+                                  const float* theta, const float* gamma, const float* delta,
+                                  void* state, void* out, void* stream /* hipStream_t */);
 
 /* Optional timing hook for profilers and benchmarks: while set, every
  * atlas_mem_forward records `before` on its stream right before the

@@ -138,8 +138,13 @@ void oracle_memory_apply(const oracle_config* cfg, const double* theta,
 
 static double sgn(double x) { return x > 0.0 ? 1.0 : x < 0.0 ? -1.0 : 0.0; }
 
+/* the sign factor of the l_p and Huber slopes: exact, or tanh(alpha e) */
+static double sign_a(double e, double alpha) { return alpha > 0.0 ? tanh(alpha * e) : sgn(e); }
+
 /* derivative of |e|^p / p: sign(e) |e|^(p-1)  (p >= 1; zero at e = 0) */
-static double lp_slope(double e, double p) { return e == 0.0 ? 0.0 : sgn(e) * pow(fabs(e), p - 1.0); }
+static double lp_slope(double e, double p, double alpha) {
+  return e == 0.0 ? 0.0 : sign_a(e, alpha) * pow(fabs(e), p - 1.0);
+}
 
 /* Factors of one token's gradient at theta:
  *   linear: dY (d_v)            G = dY x^T
@@ -165,8 +170,8 @@ static void grad_factors(const oracle_config* cfg, const double* th,
   for (int o = 0; o < dv; ++o) {
     if (cfg->bias == ORC_BIAS_L2) d2[o] = s * gamma * (f[o] - v[o]);
     else if (cfg->bias == ORC_BIAS_DOT) d2[o] = -s * gamma * v[o];
-    else if (cfg->bias == ORC_BIAS_LP) d2[o] = s * gamma * lp_slope(f[o] - v[o], cfg->bias_p);
-    else d2[o] = s * gamma * (huber_small ? f[o] - v[o] : delta * sgn(f[o] - v[o]));
+    else if (cfg->bias == ORC_BIAS_LP) d2[o] = s * gamma * lp_slope(f[o] - v[o], cfg->bias_p, cfg->sign_alpha);
+    else d2[o] = s * gamma * (huber_small ? f[o] - v[o] : delta * sign_a(f[o] - v[o], cfg->sign_alpha));
   }
   if (cfg->memory == ORC_MLP) {
     const double* W2 = th + (long)h * D;
@@ -227,6 +232,7 @@ static int config_ok(const oracle_config* c) {
   } else if (c->memory != ORC_LINEAR) {
     return 0;
   }
+  if (!(c->sign_alpha >= 0.0 && c->sign_alpha < 1e30)) return 0;
   if (c->bias == ORC_BIAS_LP) return c->bias_p >= 1.0 && c->bias_p < 1e6;
   return c->bias == ORC_BIAS_L2 || c->bias == ORC_BIAS_DOT || c->bias == ORC_BIAS_HUBER;
 }

@@ -66,6 +66,10 @@ typedef struct {
                                        delta * (|e|_1 - delta / 2)          */
   double grad_scale;/* s                                                      */
   double bias_p;    /* p >= 1 of ORC_BIAS_LP                                  */
+  double sign_alpha;/* 0: sign(e) exact in the l_p and Huber slopes; > 0:
+                       tanh(sign_alpha * e), the smooth sign of the Miras
+                       review (Remark 5 under "Alternative Attentional
+                       Biases")                                              */
 } oracle_config;
 
 /* Sets the OpenMP thread count used by oracle_forward (n <= 0: default). */

@@ -50,6 +50,7 @@ class OracleConfig(ctypes.Structure):
         ("bias", ctypes.c_int),
         ("grad_scale", ctypes.c_double),
         ("bias_p", ctypes.c_double),
+        ("sign_alpha", ctypes.c_double),
     ]
 
 
@@ -83,13 +84,13 @@ def lib():
 
 def make_config(*, n_seq=1, seq_len=0, d_k, d_v, memory="linear", hidden=0, residual=False,
                 feature_map="identity", poly_dims=0, window=1, chunk=1, momentum=False,
-                bias="l2", grad_scale=1.0, bias_p=2.0) -> OracleConfig:
+                bias="l2", grad_scale=1.0, bias_p=2.0, sign_alpha=0.0) -> OracleConfig:
     return OracleConfig(
         n_seq=n_seq, seq_len=seq_len, d_k=d_k, d_v=d_v,
         memory=MLP if memory == "mlp" else LINEAR, hidden=hidden, residual=int(bool(residual)),
         feature_map=PHI[feature_map], poly_dims=poly_dims, window=window, chunk=chunk,
         momentum=int(bool(momentum)), bias=BIAS[bias], grad_scale=float(grad_scale),
-        bias_p=float(bias_p))
+        bias_p=float(bias_p), sign_alpha=float(sign_alpha))
 
 
 def _p(a: np.ndarray):
@@ -180,7 +181,8 @@ def config_for(wl) -> OracleConfig:
     return make_config(d_k=wl.d_k, d_v=wl.d_v, memory=wl.memory, hidden=wl.hidden,
                        residual=wl.residual, feature_map=wl.feature_map, poly_dims=wl.poly_dims,
                        window=wl.window, chunk=wl.chunk, momentum=wl.momentum, bias=wl.bias,
-                       grad_scale=wl.grad_scale, bias_p=getattr(wl, "bias_p", 2.0))
+                       grad_scale=wl.grad_scale, bias_p=getattr(wl, "bias_p", 2.0),
+                       sign_alpha=getattr(wl, "sign_alpha", 0.0))
 
 
 def run_workload(wl, inputs: dict, weights0, seqs=None, n_tokens=None, state=None, threads=None):

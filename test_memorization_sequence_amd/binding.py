@@ -23,7 +23,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "atlas_mem.h")
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_OOM, ERR_HIP = 0, 1, 2, 3, 4
 MEM = {"linear": 0, "mlp": 1}
 PHI = {"identity": 0, "poly2": 1, "raw_poly2": 2}
-BIAS = {"l2": 0, "dot": 1}
+BIAS = {"l2": 0, "dot": 1, "lp": 2, "huber": 3}
 IO = {"bf16": 0, "f32": 1}
 KERNEL = {"auto": 0, "per_sequence": 1, "sharded": 2, "streamed": 3}
 TORCH_IO = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -33,13 +33,14 @@ class AtlasMemConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "batch", "heads", "seq_len", "d_k", "d_v", "memory", "mlp_layers", "mlp_hidden",
         "mlp_residual", "feature_map", "poly_dims", "window", "chunk", "momentum", "bias",
-        "io_dtype")] + [("grad_scale", ctypes.c_float), ("kernel", ctypes.c_int)]
+        "io_dtype")] + [("grad_scale", ctypes.c_float), ("kernel", ctypes.c_int), ("bias_p", ctypes.c_float),
+                       ("sign_alpha", ctypes.c_float)]
 
 
 class StateLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "seq_stride", "weights", "momentum", "halo_k", "halo_v", "halo_g", "count")] + [
-        ("feature_dim", ctypes.c_int), ("param_count", ctypes.c_long)]
+        ("feature_dim", ctypes.c_int), ("param_count", ctypes.c_long), ("halo_d", ctypes.c_size_t)]
 
 
 class AtlasError(RuntimeError):
@@ -72,6 +73,8 @@ def lib():
         L.atlas_mem_state_layout_of.restype = ctypes.c_int
         L.atlas_mem_forward.argtypes = [vp] * 11
         L.atlas_mem_forward.restype = ctypes.c_int
+        L.atlas_mem_forward_ex.argtypes = [vp] * 12
+        L.atlas_mem_forward_ex.restype = ctypes.c_int
         L.atlas_mem_set_kernel_events.argtypes = [vp, vp, vp]
         L.atlas_mem_set_kernel_events.restype = ctypes.c_int
         L.atlas_mem_kernel_family.argtypes = [vp]
@@ -100,7 +103,8 @@ def config_of(wl: Workload, kernel: str = "auto") -> AtlasMemConfig:
         memory=MEM[wl.memory], mlp_layers=2 if wl.memory == "mlp" else 0, mlp_hidden=wl.hidden,
         mlp_residual=int(wl.residual), feature_map=PHI[wl.feature_map], poly_dims=wl.poly_dims,
         window=wl.window, chunk=wl.chunk, momentum=int(wl.momentum), bias=BIAS[wl.bias],
-        io_dtype=IO[wl.io_dtype], grad_scale=wl.grad_scale)
+        io_dtype=IO[wl.io_dtype], grad_scale=wl.grad_scale, bias_p=getattr(wl, "bias_p", 2.0),
+        sign_alpha=getattr(wl, "sign_alpha", 0.0))
 
 
 def supported(cfg: AtlasMemConfig) -> int:
@@ -154,7 +158,8 @@ class AtlasMem:
         rows = state.view(self.n_seq, L.seq_stride)
         halo = c.window - 1
         sizes = {"weights": L.param_count, "momentum": L.param_count if c.momentum else 0,
-                 "halo_k": halo * c.d_k, "halo_v": halo * c.d_v, "halo_g": halo}
+                 "halo_k": halo * c.d_k, "halo_v": halo * c.d_v, "halo_g": halo,
+                 "halo_d": halo if c.bias == BIAS["huber"] else 0}
         if field == "count":
             return rows[:, L.count:L.count + 8].view(torch.int64)[:, 0]
         off = getattr(L, field)
@@ -182,13 +187,21 @@ class AtlasMem:
         return f.value
 
     # -- forward --------------------------------------------------------------------
-    def forward(self, q, k, v, alpha, eta, theta, gamma, state, out, stream=None):
-        """Enqueues one call on `stream` (default: torch's current stream)."""
+    def forward(self, q, k, v, alpha, eta, theta, gamma, state, out, stream=None, delta=None):
+        """Enqueues one call on `stream` (default: torch's current stream).
+        delta: the per-token Huber thresholds (that bias only)."""
         if stream is None:
             stream = torch.cuda.current_stream()
-        rc = lib().atlas_mem_forward(
-            self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(theta),
-            _ptr(gamma), _ptr(state), _ptr(out), ctypes.c_void_p(stream.cuda_stream))
+        if delta is None and self.cfg.bias != BIAS["huber"]:
+            rc = lib().atlas_mem_forward(
+                self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(theta),
+                _ptr(gamma), _ptr(state), _ptr(out), ctypes.c_void_p(stream.cuda_stream))
+            what = "atlas_mem_forward"
+        else:
+            rc = lib().atlas_mem_forward_ex(
+                self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(theta),
+                _ptr(gamma), _ptr(delta), _ptr(state), _ptr(out), ctypes.c_void_p(stream.cuda_stream))
+            what = "atlas_mem_forward_ex"
         if rc != OK:
-            raise AtlasError(rc, "atlas_mem_forward")
+            raise AtlasError(rc, what)
         return out

@@ -31,8 +31,10 @@ class Workload:
     chunk: int             # chunk b
     momentum: bool
     io_dtype: str          # "bf16" | "f32" for q, k, v, out
-    bias: str = "l2"       # "l2" | "dot"
+    bias: str = "l2"       # "l2" | "dot" | "lp" | "huber"
     grad_scale: float = 1.0
+    bias_p: float = 2.0    # p of the l_p bias
+    sign_alpha: float = 0.0  # l_p / Huber: 0 exact sign(e), > 0 tanh(sign_alpha * e)
     alpha_u: tuple | None = (-4.0, 0.0)
     theta_u: tuple | None = (-4.0, 0.0)
     eta_u: tuple | None = (0.0, 3.0)

@@ -94,6 +94,7 @@ static int pd_of(const atlas_mem_config* c) {
 
 static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
+  if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
   const int need_w = c->chunk + c->window - 1;
   const ShardedVariant* best = nullptr;
@@ -106,6 +107,7 @@ static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
 
 static const StreamVariant* find_streamed(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
+  if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
   // the kernel addresses one sequence's inputs and coefficients through
   // 32-bit buffer offsets (below 1 GiB each)
@@ -129,7 +131,10 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   if (c->window < 1 || c->chunk < 1) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->memory != ATLAS_MEM_LINEAR && c->memory != ATLAS_MEM_MLP) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->feature_map < ATLAS_PHI_IDENTITY || c->feature_map > ATLAS_PHI_RAW_POLY2) return ATLAS_ERR_INVALID_ARGUMENT;
-  if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->bias < ATLAS_BIAS_L2 || c->bias > ATLAS_BIAS_HUBER) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->bias == ATLAS_BIAS_LP && !(c->bias_p >= 1.f && c->bias_p < 1e6f)) return ATLAS_ERR_INVALID_ARGUMENT;
+  if ((c->bias == ATLAS_BIAS_LP || c->bias == ATLAS_BIAS_HUBER) && !(c->sign_alpha >= 0.f && c->sign_alpha < 1e30f))
+    return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->io_dtype != ATLAS_BF16 && c->io_dtype != ATLAS_F32) return ATLAS_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(c->grad_scale)) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->feature_map == ATLAS_PHI_RAW_POLY2 && (c->poly_dims < 1 || c->poly_dims > c->d_k)) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -189,7 +194,8 @@ static atlas_mem_state_layout make_layout(const atlas_mem_config* c) {
   L.halo_k = align_up(L.momentum + (c->momentum ? P * 4 : 0), 16);
   L.halo_v = align_up(L.halo_k + halo * c->d_k * 4, 16);
   L.halo_g = align_up(L.halo_v + halo * c->d_v * 4, 16);
-  L.count = align_up(L.halo_g + halo * 4, 16);
+  L.halo_d = align_up(L.halo_g + halo * 4, 16);
+  L.count = align_up(L.halo_d + (c->bias == ATLAS_BIAS_HUBER ? halo * 4 : 0), 16);
   L.seq_stride = align_up(L.count + 8, 256);
   return L;
 }
@@ -277,11 +283,21 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, const void* v,
                                const float* alpha, const float* eta, const float* theta,
                                const float* gamma, void* state, void* out, void* stream) {
+  if (!h || h->magic != kMagic || h->cfg.bias == ATLAS_BIAS_HUBER) return ATLAS_ERR_INVALID_ARGUMENT;
+  return atlas_mem_forward_ex(h, q, k, v, alpha, eta, theta, gamma, nullptr, state, out, stream);
+}
+
+atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* eta, const float* theta,
+                                  const float* gamma, const float* delta, void* state, void* out, void* stream) {
   if (!h || h->magic != kMagic) return ATLAS_ERR_INVALID_ARGUMENT;
   const atlas_mem_config& c = h->cfg;
   if (c.seq_len == 0) return ATLAS_OK;  // nothing to read or write; any pointer accepted
   if (!q || !k || !v || !alpha || !theta || !gamma || !state || !out) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c.momentum && !eta) return ATLAS_ERR_INVALID_ARGUMENT;
+  const bool huber = c.bias == ATLAS_BIAS_HUBER;
+  if (huber && (!delta || (uintptr_t)delta % 4)) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (!huber) delta = nullptr;
   const void* p16[] = {q, k, v, state, out};
   for (const void* p : p16)
     if ((uintptr_t)p % 16) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -295,6 +311,7 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
       overlaps(out, out_b, v, S * N * c.d_v * es) || overlaps(out, out_b, state, st_b) ||
       overlaps(out, out_b, alpha, S * N * 4) || overlaps(out, out_b, theta, S * N * 4) ||
       overlaps(out, out_b, gamma, S * N * 4) || (eta && overlaps(out, out_b, eta, S * N * 4)) ||
+      (delta && overlaps(out, out_b, delta, S * N * 4)) || (delta && overlaps(state, st_b, delta, S * N * 4)) ||
       overlaps(state, st_b, q, S * N * c.d_k * es) || overlaps(state, st_b, k, S * N * c.d_k * es) ||
       overlaps(state, st_b, v, S * N * c.d_v * es))
     return ATLAS_ERR_INVALID_ARGUMENT;
@@ -347,6 +364,10 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
     sp.grad_scale = c.grad_scale;
     sp.momentum = c.momentum;
     sp.bias = c.bias;
+    sp.bias_p = c.bias_p;
+    sp.sign_alpha = c.sign_alpha;
+    sp.delta = delta;
+    sp.off_halo_d = h->lay.halo_d;
     sp.residual = c.mlp_residual;
     e = (h->svar ? h->svar->launch : h->tvar->launch)(sp, kp, (hipStream_t)stream, h->ev_before, h->ev_after);
     if (e != hipSuccess) return hip_fail(e);
@@ -375,6 +396,10 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
   cp.grad_scale = c.grad_scale;
   cp.momentum = c.momentum;
   cp.bias = c.bias;
+  cp.bias_p = c.bias_p;
+  cp.sign_alpha = c.sign_alpha;
+  cp.delta = delta;
+  cp.off_halo_d = h->lay.halo_d;
   cp.residual = c.memory == ATLAS_MEM_MLP ? c.mlp_residual : 0;
   e = h->var->launch(cp, kp, h->n_seq, (hipStream_t)stream, h->ev_before, h->ev_after);
   if (e != hipSuccess) return hip_fail(e);

@@ -12,7 +12,7 @@ typedef __bf16 bf16;
 
 enum { MEM_LINEAR = 0, MEM_MLP = 1 };
 enum { PHI_IDENTITY = 0, PHI_POLY2 = 1, PHI_RAW_POLY2 = 2 };
-enum { BIAS_L2 = 0, BIAS_DOT = 1 };
+enum { BIAS_L2 = 0, BIAS_DOT = 1, BIAS_LP = 2, BIAS_HUBER = 3 };
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -51,7 +51,9 @@ struct WsLayout {
   static constexpr size_t D1TM = align_up(D1T + (MLP ? H * WP : 0) * e, 256);
   static constexpr size_t D1TS = align_up(D1TM + (MLP ? H * WP : 0) * e, 256);
   static constexpr size_t Ah = align_up(D1TS + (MLP ? H * WP : 0) * e, 256);
-  static constexpr size_t bytes = align_up(Ah + (MLP ? BC * H : 0) * e, 256);
+  // raw errors E [WP][DV] (fp32) for the biases that shape them per token
+  static constexpr size_t Ef = align_up(Ah + (MLP ? BC * H : 0) * e, 256);
+  static constexpr size_t bytes = align_up(Ef + WP * DV * 4, 256);
 };
 
 // T: MFMA operand type (bf16 or float); TI: io type of q, k, v, out.
@@ -109,6 +111,11 @@ struct ChunkParams {
   size_t seq_stride, off_weights, off_momentum, off_halo_k, off_halo_v, off_halo_g, off_count;
   float grad_scale;
   int momentum, bias, residual;
+  // l_p exponent; Huber thresholds of the call [n_seq][N] (else null) and the
+  // state offset of the thresholds of the halo
+  float bias_p, sign_alpha;
+  const float* delta;
+  size_t off_halo_d;
 };
 
 struct ShardedParams {
@@ -125,6 +132,11 @@ struct ShardedParams {
   size_t seq_stride, off_weights, off_momentum, off_halo_k, off_halo_v, off_halo_g, off_count;
   float grad_scale;
   int momentum, bias, residual;
+  // l_p exponent; Huber thresholds of the call [n_seq][N] (else null) and the
+  // state offset of the thresholds of the halo
+  float bias_p, sign_alpha;
+  const float* delta;
+  size_t off_halo_d;
 };
 
 template <int D, int DV, int H, int G, int WP, int BC>

@@ -23,7 +23,8 @@
 //                 (the chunk chain is sequential).  Per chunk, as bf16 (or
 //                 fp32) MFMA GEMMs with fp32 accumulation:
 //                   MLP  Z = X W1^T, A = gelu(Z), E = R + A W2^T - V,
-//                        D2 = s*gamma*E, D1 = (D2 W2) .* gelu'(Z)
+//                        D2 = s*gamma*E (l_p, Huber: s*gamma*slope(E), see
+//                        atlas_mem_bias.h), D1 = (D2 W2) .* gelu'(Z)
 //                        retrieval with the per-token weights W_t:
 //                          Zq = diag(A_t) Xq W1^T + diag(B_t) Xq S1^T - (C .* Xq X^T) D1
 //                          y  = Rq + diag(A_t) gelu(Zq) W2^T + diag(B_t) gelu(Zq) S2^T
@@ -45,6 +46,7 @@
 #include "atlas_mem_internal.h"
 #include "atlas_mem_coeff.h"
 #include "atlas_mem_gelu.h"
+#include "atlas_mem_bias.h"
 
 namespace atlas {
 
@@ -178,6 +180,9 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   const int N = p.N, c = p.c, W = BC + c - 1;
   const float s_grad = p.grad_scale;
   const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
+  // l_p and Huber biases: D2 from the raw errors once whole rows are known
+  const bool shaped = p.bias == BIAS_LP || p.bias == BIAS_HUBER, huber = p.bias == BIAS_HUBER;
+  const float bias_p = p.bias_p, sign_alpha = p.sign_alpha;
 
   char* st = p.state + (size_t)seq * p.seq_stride;
   float* Wt = reinterpret_cast<float*>(st + p.off_weights);
@@ -185,8 +190,10 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   float* hk = reinterpret_cast<float*>(st + p.off_halo_k);
   float* hv = reinterpret_cast<float*>(st + p.off_halo_v);
   float* hg = reinterpret_cast<float*>(st + p.off_halo_g);
+  float* hd = reinterpret_cast<float*>(st + p.off_halo_d);   // Huber only
   int64_t* cnt = reinterpret_cast<int64_t*>(st + p.off_count);
   const int halo_valid = (int)min<int64_t>(*cnt, (int64_t)(c - 1));
+  const float* dl_in = huber ? p.delta + (size_t)seq * N : nullptr;
 
   const TI* q = reinterpret_cast<const TI*>(p.q) + (size_t)seq * N * DK;
   const TI* k = reinterpret_cast<const TI*>(p.k) + (size_t)seq * N * DK;
@@ -217,6 +224,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   T* D1TS = reinterpret_cast<T*>(ws + WS::D1TS);
   T* Ah = reinterpret_cast<T*>(ws + WS::Ah);     // [BC][H]   gelu(Zq)
   T* Q2 = reinterpret_cast<T*>(ws + WS::Q2);     // [BC][WP]  C .* (gelu(Zq) A^T)
+  float* Ef = reinterpret_cast<float*>(ws + WS::Ef);  // [WP][DV] raw errors (l_p, Huber)
   // linear (aliases of the MLP names where the roles coincide)
   T* Mb = W2b;   // [DV][DP]
   T* Sb = S2b;   // [DV][DP]
@@ -224,6 +232,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   __shared__ TI kr[WP][DK];   // raw keys of the window (residual path, phi input)
   __shared__ TI qr[BC][DK];   // raw queries of the chunk
   __shared__ float gw[WP], cMw[WP], cSw[WP], cA[BC], cB[BC];
+  __shared__ float dw[WP], rsel[WP];   // Huber: thresholds of the window rows, their choice
   __shared__ float cP;
   __shared__ PairTable<S::PD> pt;
   if (S::PHI != PHI_IDENTITY) pt.fill();
@@ -274,8 +283,13 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
     for (int w = threadIdx.x; w < WP; w += blockDim.x) {
       const int i = t0 - (c - 1) + w;
       float g = 0.f;
-      if (w < W && i >= -halo_valid && i <= te) g = i >= 0 ? gam_in[i] : hg[c - 1 + i];
+      float dd = 0.f;
+      if (w < W && i >= -halo_valid && i <= te) {
+        g = i >= 0 ? gam_in[i] : hg[c - 1 + i];
+        if (huber) dd = i >= 0 ? dl_in[i] : hd[c - 1 + i];
+      }
       gw[w] = g;
+      dw[w] = dd;
       cMw[w] = coef[2 * BC + 4 + w];
       cSw[w] = coef[2 * BC + 4 + WP + w];
     }
@@ -302,6 +316,32 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
       if (w >= W || i < -halo_valid || i > te) return 0.f;
       return i >= 0 ? to_f(v[(size_t)i * DV + o]) : hv[(c - 1 + i) * DV + o];
     };
+    // D2 element (w, o) in every layout its consumers read
+    auto put_d2 = [&](int w, int o, float d2) {
+      if (S::MEM == MEM_MLP) D2[w * DV + o] = from_f<T>(d2);
+      D2T[o * WP + w] = from_f<T>(d2);
+      D2TM[o * WP + w] = from_f<T>(cMw[w] * d2);
+      D2TS[o * WP + w] = from_f<T>(cSw[w] * d2);
+    };
+    // l_p / Huber: D2 = s gamma slope(E) from the raw errors in Ef; the
+    // Huber choice needs each row's |E|_2 first
+    auto shape_rows = [&]() {
+      __syncthreads();
+      if (huber) {
+        for (int w = threadIdx.x; w < WP; w += blockDim.x) {
+          float n2 = 0.f;
+          for (int o = 0; o < DV; ++o) n2 += Ef[w * DV + o] * Ef[w * DV + o];
+          rsel[w] = sqrtf(n2) <= dw[w] ? 1.f : 0.f;
+        }
+        __syncthreads();
+      }
+      for (int e = threadIdx.x; e < WP * DV; e += blockDim.x) {
+        const int w = e / DV, o = e % DV;
+        const float x = Ef[e];
+        const float g = huber ? huber_slope(x, rsel[w] != 0.f, dw[w], sign_alpha) : lp_slope(x, bias_p, sign_alpha);
+        put_d2(w, o, s_grad * gw[w] * g);
+      }
+    };
 
     // Q1 = C .* (Xq X^T)
     {
@@ -326,14 +366,11 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
         Op<T> ops[1] = {{Ab, H, W2b, H, H}};
         gemm_nt(WP, DV, ops, [&](int w, int o, const float* a) {
           const float vv = vrow(w, o);
-          float d2;
-          if (dot) d2 = -s_grad * gw[w] * vv;
-          else d2 = s_grad * gw[w] * ((res ? to_f(kr[w][o]) : 0.f) + a[0] - vv);
-          D2[w * DV + o] = from_f<T>(d2);
-          D2T[o * WP + w] = from_f<T>(d2);
-          D2TM[o * WP + w] = from_f<T>(cMw[w] * d2);
-          D2TS[o * WP + w] = from_f<T>(cSw[w] * d2);
+          const float err = (res ? to_f(kr[w][o]) : 0.f) + a[0] - vv;
+          if (shaped) Ef[w * DV + o] = err;
+          else put_d2(w, o, dot ? -s_grad * gw[w] * vv : s_grad * gw[w] * err);
         });
+        if (shaped) shape_rows();
       }
       __syncthreads();
       // D1 = (D2 W2) .* gelu'(Z)
@@ -414,11 +451,11 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
         Op<T> ops[1] = {{Xw, DP, Mb, DP, DP}};
         gemm_nt(WP, DV, ops, [&](int w, int o, const float* a) {
           const float vv = vrow(w, o);
-          const float d = dot ? -s_grad * gw[w] * vv : s_grad * gw[w] * (a[0] - vv);
-          D2T[o * WP + w] = from_f<T>(d);
-          D2TM[o * WP + w] = from_f<T>(cMw[w] * d);
-          D2TS[o * WP + w] = from_f<T>(cSw[w] * d);
+          const float err = a[0] - vv;
+          if (shaped) Ef[w * DV + o] = err;
+          else put_d2(w, o, dot ? -s_grad * gw[w] * vv : s_grad * gw[w] * err);
         });
+        if (shaped) shape_rows();
       }
       __syncthreads();
       // y = A_t Xq M^T + B_t Xq S^T - Q1 D
@@ -461,6 +498,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
       for (int d = lane; d < DK; d += 64) hk[j * DK + d] = i >= 0 ? to_f(k[(size_t)i * DK + d]) : hk[(N + j) * DK + d];
       for (int o = lane; o < DV; o += 64) hv[j * DV + o] = i >= 0 ? to_f(v[(size_t)i * DV + o]) : hv[(N + j) * DV + o];
       if (lane == 0) hg[j] = i >= 0 ? gam_in[i] : hg[N + j];
+      if (lane == 0 && huber) hd[j] = i >= 0 ? dl_in[i] : hd[N + j];
     }
     if (lane == 0) *cnt += N;
   }

@@ -13,7 +13,10 @@ Recipe (one numpy Generator, default_rng(seed), draws in this order):
          stored as fp32 (eta = 0 without momentum, gamma = 1 when constant);
   initial MLP weights ~ N(0, init_std^2), one draw per head, shared by every
          batch entry (W1 [H, hidden, D] then W2 [H, d_v, hidden]); zero for a
-         linear memory.
+         linear memory;
+  Huber bias only, drawn last: delta_t = m_t * |v_t|_2 [B, H, N] fp32 with
+         m_t = 1/4 or 4, each with probability 1/2 (a threshold per token that
+         depends on the input, far from the token's error norm either way).
 bf16 values are held in float32 arrays whose low 16 bits are zero.
 """
 from __future__ import annotations
@@ -75,6 +78,10 @@ def make_inputs(wl: Workload, seed: int = 0) -> dict:
             out["w2"] = np.zeros((H, wl.d_v, wl.hidden), np.float32)
     else:
         out["m"] = np.zeros((H, wl.d_v, D), np.float32)
+    if wl.bias == "huber":
+        vn = np.sqrt(np.sum(v.astype(np.float64) ** 2, axis=-1))
+        m = np.where(rng.uniform(size=g) < 0.5, 0.25, 4.0)
+        out["delta"] = (m * vn).astype(np.float32)
     return out
 
 

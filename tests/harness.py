@@ -24,8 +24,9 @@ def to_device(wl, inputs, device="cuda"):
     d = {}
     for key in ("q", "k", "v"):
         d[key] = torch.from_numpy(inputs[key]).to(device=device, dtype=io).contiguous()
-    for key in ("alpha", "eta", "theta", "gamma"):
-        d[key] = torch.from_numpy(inputs[key]).to(device=device).contiguous()
+    for key in ("alpha", "eta", "theta", "gamma", "delta"):
+        if key in inputs:
+            d[key] = torch.from_numpy(inputs[key]).to(device=device).contiguous()
     return d
 
 
@@ -35,13 +36,13 @@ def gpu_run(mem, wl, dev_inputs, state, out=None):
         out = torch.empty(wl.batch, wl.heads, wl.seq_len, wl.d_v, dtype=mem.io_dtype, device="cuda")
     mem.forward(dev_inputs["q"], dev_inputs["k"], dev_inputs["v"], dev_inputs["alpha"],
                 dev_inputs["eta"] if wl.momentum else None, dev_inputs["theta"], dev_inputs["gamma"],
-                state, out)
+                state, out, delta=dev_inputs.get("delta"))
     return out
 
 
 def gpu_state_np(mem, state):
     return {f: mem.view(state, f).cpu().numpy().astype(np.float64 if f != "count" else np.int64)
-            for f in ("weights", "momentum", "halo_k", "halo_v", "halo_g", "count")}
+            for f in ("weights", "momentum", "halo_k", "halo_v", "halo_g", "halo_d", "count")}
 
 
 def compare(wl, inputs, out_gpu, st_gpu, out_or, st_or, seqs=None, n_tokens=None):
@@ -68,7 +69,8 @@ def compare(wl, inputs, out_gpu, st_gpu, out_or, st_or, seqs=None, n_tokens=None
             res["momentum"] = rel_l2(st_gpu["momentum"][seqs], st_or["mom"])
         res["halo_exact"] = bool(np.array_equal(st_gpu["halo_k"][seqs].reshape(st_or["halo_k"].shape), st_or["halo_k"])
                                  and np.array_equal(st_gpu["halo_v"][seqs].reshape(st_or["halo_v"].shape), st_or["halo_v"])
-                                 and np.array_equal(st_gpu["halo_g"][seqs], st_or["halo_g"]))
+                                 and np.array_equal(st_gpu["halo_g"][seqs], st_or["halo_g"])
+                                 and (wl.bias != "huber" or np.array_equal(st_gpu["halo_d"][seqs], st_or["halo_d"])))
         res["count_exact"] = bool(np.array_equal(st_gpu["count"][seqs], st_or["count"]))
     return res
 

@@ -42,7 +42,7 @@ def test_bad_configs(kw, code):
 
 
 def test_enum_fields_are_checked():
-    for field, val in (("memory", 7), ("feature_map", 5), ("bias", 3), ("io_dtype", 9)):
+    for field, val in (("memory", 7), ("feature_map", 5), ("bias", 4), ("io_dtype", 9)):
         c = _cfg()
         setattr(c, field, val)
         assert binding.supported(c) == binding.ERR_INVALID, field
@@ -72,6 +72,27 @@ def test_kernel_family_selection():
         assert binding.supported(binding.config_of(WORKLOADS[name], "streamed")) == ok
     for name in ("atlas_long", "linear_poly2", "linear64_delta"):
         assert binding.supported(binding.config_of(WORKLOADS[name], "streamed")) == binding.ERR_UNSUPPORTED
+
+
+def test_other_attentional_biases():
+    """l_p needs p >= 1; l_p and Huber run on the per-sequence family (AUTO
+    picks it), not on the sharded one."""
+    ok, inv, uns = binding.OK, binding.ERR_INVALID, binding.ERR_UNSUPPORTED
+    for p, code in ((0.5, inv), (float("nan"), inv), (1.0, ok), (3.0, ok)):
+        assert binding.supported(binding.config_of(replace(WORKLOADS["mlp64"], bias="lp", bias_p=p))) == code, p
+    for name in ORDER:
+        for bias in ("lp", "huber"):
+            wl = replace(WORKLOADS[name], bias=bias, bias_p=3.0)
+            assert binding.supported(binding.config_of(wl, "auto")) == ok, (name, bias)
+            assert binding.supported(binding.config_of(wl, "per_sequence")) == ok, (name, bias)
+            if wl.memory == "mlp" and wl.feature_map == "identity":
+                assert binding.supported(binding.config_of(wl, "sharded")) == uns, (name, bias)
+
+
+def test_forward_ex_is_declared_and_checks_its_handle():
+    L = binding.lib()
+    assert "atlas_mem_forward_ex" in binding.declared_functions()
+    assert L.atlas_mem_forward_ex(None, *[None] * 11) == binding.ERR_INVALID
 
 
 def test_null_handle_and_strings():

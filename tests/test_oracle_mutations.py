@@ -27,13 +27,14 @@ MUTANTS = {
     "dot_bias_sign": ("-s * gamma * v[o]", "s * gamma * v[o]"),
     "tanh_gelu": ("return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));", "return 0.5 * z * (1.0 + tanh(z));"),
     "stale_chunk_start_state": ("memcpy(Wc, W, sizeof(double) * P);", "if (t0 == 0) memcpy(Wc, W, sizeof(double) * P);"),
-    "lp_exponent_p": ("sgn(e) * pow(fabs(e), p - 1.0)", "sgn(e) * pow(fabs(e), p)"),
-    "lp_sign_dropped": ("sgn(e) * pow(fabs(e), p - 1.0)", "pow(fabs(e), p - 1.0)"),
+    "lp_exponent_p": ("sign_a(e, alpha) * pow(fabs(e), p - 1.0)", "sign_a(e, alpha) * pow(fabs(e), p)"),
+    "lp_sign_dropped": ("sign_a(e, alpha) * pow(fabs(e), p - 1.0)", "pow(fabs(e), p - 1.0)"),
+    "smooth_sign_slope": ("alpha > 0.0 ? tanh(alpha * e) : sgn(e)", "alpha > 0.0 ? tanh(e) : sgn(e)"),
     "huber_l1_norm_test": ("n2 += (f[o] - v[o]) * (f[o] - v[o]);", "n2 += fabs(f[o] - v[o]); n2 *= 1.0;"),
-    "huber_branches_swapped": ("huber_small ? f[o] - v[o] : delta * sgn(f[o] - v[o])",
-                               "huber_small ? delta * sgn(f[o] - v[o]) : f[o] - v[o]"),
-    "huber_delta_dropped": ("huber_small ? f[o] - v[o] : delta * sgn(f[o] - v[o])",
-                            "huber_small ? f[o] - v[o] : sgn(f[o] - v[o])"),
+    "huber_branches_swapped": ("huber_small ? f[o] - v[o] : delta * sign_a(f[o] - v[o], cfg->sign_alpha)",
+                               "huber_small ? delta * sign_a(f[o] - v[o], cfg->sign_alpha) : f[o] - v[o]"),
+    "huber_delta_dropped": ("huber_small ? f[o] - v[o] : delta * sign_a(f[o] - v[o], cfg->sign_alpha)",
+                            "huber_small ? f[o] - v[o] : sign_a(f[o] - v[o], cfg->sign_alpha)"),
     "huber_halo_threshold_lost": ("nd[j] = huber ? dl[i] : 0.0;", "nd[j] = 0.0;"),
     "huber_squared_norm_test": ("huber_small = sqrt(n2) <= delta;", "huber_small = n2 <= delta;"),
 }

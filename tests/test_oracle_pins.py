@@ -419,13 +419,17 @@ def test_lp_gradient_matches_finite_differences(p, residual):
     np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
 
 
+@pytest.mark.parametrize("alpha", [0.0, 3.0])
 @pytest.mark.parametrize("regime", ["squared", "absolute", "between_norms"])
-def test_huber_gradient_matches_finite_differences(regime):
+def test_huber_gradient_matches_finite_differences(regime, alpha):
     """Central differences of gamma*s * huber(f - v; delta), on both branches
-    and with delta between |e|_2 and |e|_1 (the test uses the l2 norm)."""
+    and with delta between |e|_2 and |e|_1 (the test uses the l2 norm).  With
+    the smooth sign tanh(alpha e) the large-error branch is
+    delta * sum_o log(cosh(alpha e_o)) / alpha."""
     rng = np.random.default_rng(41)
     d, h, gamma, s = 3, 5, 0.8, 1.0
-    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=h, residual=True, bias="huber", grad_scale=s)
+    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=h, residual=True, bias="huber", grad_scale=s,
+                        sign_alpha=alpha)
     theta = rng.standard_normal(h * d + d * h)
     x, v = rng.standard_normal(d), rng.standard_normal(d)
     W1, W2 = theta[:h * d].reshape(h, d), theta[h * d:].reshape(d, h)
@@ -436,7 +440,10 @@ def test_huber_gradient_matches_finite_differences(regime):
 
     def loss(th):
         W1, W2 = th[:h * d].reshape(h, d), th[h * d:].reshape(d, h)
-        return gamma * s * huber_loss(x + W2 @ gelu(W1 @ x) - v, delta)
+        e = x + W2 @ gelu(W1 @ x) - v
+        if alpha > 0 and np.linalg.norm(e) > delta:
+            return gamma * s * delta * np.sum(np.log(np.cosh(alpha * e))) / alpha
+        return gamma * s * huber_loss(e, delta)
 
     g = O.token_grad(cfg, theta, x, x, v, gamma, delta)
     eps = 1e-6
@@ -484,21 +491,24 @@ def test_huber_limits():
     np.testing.assert_array_equal(st0["mem"][0], W0)
 
 
+@pytest.mark.parametrize("alpha", [0.0, 2.5])
 @pytest.mark.parametrize("bias", ["lp1", "lp3", "huber"])
-def test_scalar_memory_sign_rules(bias):
+def test_scalar_memory_sign_rules(bias, alpha):
     """A 1x1 linear memory, b = c = 1, no decay or momentum: each token does
     m <- m - theta*gamma*g(m k - v) k, with g(e) = sign(e) (p = 1),
-    e|e| (p = 3), or e if |e| <= delta else delta*sign(e) (Huber); y = m q."""
+    e|e| (p = 3), or e if |e| <= delta else delta*sign(e) (Huber); y = m q.
+    With alpha > 0, sign(e) is tanh(alpha e)."""
     rng = np.random.default_rng(43)
     N = 30
     q, k, v = rng.standard_normal((N, 1)), rng.standard_normal((N, 1)), rng.standard_normal((N, 1)) * 2
     th, ga, dl = rng.uniform(0.05, 0.5, N), rng.uniform(0.3, 1.0, N), rng.uniform(0.2, 2.0, N)
     kw = {"lp1": dict(bias="lp", bias_p=1.0), "lp3": dict(bias="lp", bias_p=3.0), "huber": dict(bias="huber")}[bias]
-    cfg = O.make_config(d_k=1, d_v=1, window=1, chunk=1, **kw)
+    cfg = O.make_config(d_k=1, d_v=1, window=1, chunk=1, sign_alpha=alpha, **kw)
+    sg = (lambda e: np.tanh(alpha * e)) if alpha > 0 else np.sign
     m, want = 0.4, []
     for t in range(N):
         e = m * k[t, 0] - v[t, 0]
-        gx = {"lp1": np.sign(e), "lp3": e * abs(e), "huber": e if abs(e) <= dl[t] else dl[t] * np.sign(e)}[bias]
+        gx = {"lp1": sg(e), "lp3": sg(e) * e * e, "huber": e if abs(e) <= dl[t] else dl[t] * sg(e)}[bias]
         m = m - th[t] * ga[t] * gx * k[t, 0]
         want.append(m * q[t, 0])
     out, st = run(cfg, q, k, v, np.zeros(N), np.zeros(N), th, ga, [0.4], delta=dl)
