@@ -110,6 +110,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="layer_scale")
     ap.add_argument("--kernel", default="auto", choices=["auto", "per_sequence", "sharded", "streamed"])
+    ap.add_argument("--bias", default=None, choices=["l2", "dot", "lp", "huber"],
+                    help="attentional bias (default: the workload's own)")
+    ap.add_argument("--bias-p", type=float, default=3.0, help="p of the l_p bias")
+    ap.add_argument("--sign-alpha", type=float, default=0.0, help="l_p / Huber: 0 exact sign, > 0 tanh(alpha e)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -138,13 +142,16 @@ def main():
     from test_memorization_sequence_amd.configs import WORKLOADS
 
     wl = WORKLOADS[args.workload]
-    print(f"[bench] {wl.name}: B={wl.batch} H={wl.heads} N={wl.seq_len} ({wl.note})", file=sys.stderr, flush=True)
+    if args.bias is not None:
+        from dataclasses import replace
+        wl = replace(wl, bias=args.bias, bias_p=args.bias_p, sign_alpha=args.sign_alpha)
+    print(f"[bench] {wl.name} bias={wl.bias}: B={wl.batch} H={wl.heads} N={wl.seq_len} ({wl.note})", file=sys.stderr, flush=True)
     inputs = synth.make_inputs(wl, 0)
     w0 = synth.initial_weights_flat(wl, inputs)
     dev = torch.device("cuda:0")
     io = torch.float32 if wl.io_dtype == "f32" else torch.bfloat16
     t_in = {k: torch.from_numpy(inputs[k]).to(dev, dtype=io) for k in ("q", "k", "v")}
-    g_in = {k: torch.from_numpy(inputs[k]).to(dev) for k in ("alpha", "eta", "theta", "gamma")}
+    g_in = {k: torch.from_numpy(inputs[k]).to(dev) for k in ("alpha", "eta", "theta", "gamma", "delta") if k in inputs}
     mem = binding.AtlasMem(wl, args.kernel)
     state = mem.new_state(torch.from_numpy(w0), device=dev)
     out = torch.empty(wl.batch, wl.heads, wl.seq_len, wl.d_v, dtype=io, device=dev)
@@ -156,7 +163,7 @@ def main():
 
     def step():
         mem.forward(t_in["q"], t_in["k"], t_in["v"], g_in["alpha"], g_in["eta"] if wl.momentum else None,
-                    g_in["theta"], g_in["gamma"], state, out, stream)
+                    g_in["theta"], g_in["gamma"], state, out, stream, delta=g_in.get("delta"))
 
     for _ in range(args.warmup):
         step()
@@ -184,7 +191,7 @@ def main():
     k_ms = float(np.mean(kernel_ms))
     achieved = flops / (k_ms * 1e-3) / 1e12
     peak = PEAK_FP32_TFLOPS if wl.io_dtype == "f32" else PEAK_BF16_TFLOPS
-    meas = MEASURED_TRAFFIC.get((wl.name, kernel_name(binding, wl, args.kernel)))
+    meas = MEASURED_TRAFFIC.get((wl.name, kernel_name(binding, wl, args.kernel))) if wl.bias == "l2" else None
     traffic = meas["bytes"] if meas and meas["src"] == kernel_source_hash() else None
     tokens = wl.batch * wl.seq_len
     res = {
@@ -203,7 +210,9 @@ def main():
         "config": {"workload": wl.name, "kernel_family": args.kernel, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seq_len,
                    "d_k": wl.d_k, "d_v": wl.d_v, "memory": wl.memory, "hidden": wl.hidden,
                    "feature_dim": wl.feature_dim, "window": wl.window, "chunk": wl.chunk,
-                   "momentum": wl.momentum},
+                   "momentum": wl.momentum, "bias": wl.bias,
+                   **({"bias_p": wl.bias_p} if wl.bias == "lp" else {}),
+                   **({"sign_alpha": wl.sign_alpha} if wl.bias in ("lp", "huber") else {})},
         "head_tokens_per_s": S * wl.seq_len / (ms_per_step * 1e-3),
         "mfma_util_pct": 100.0 * (flops / (ms_per_step * 1e-3) / 1e12) / peak,
         "roofline": {

@@ -71,7 +71,7 @@ enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
  * identity feature map, d_k == d_v and bf16 io (SHARDED: the l2 and
  * dot-product biases only).  AUTO picks the fastest
  * family measured for the shape: STREAMED where marked so (large hidden
- * layers), else SHARDED, else PER_SEQUENCE.                                 */
+ * layers), else SHARDED, else STREAMED, else PER_SEQUENCE.                 */
 enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3 };
 
 typedef struct {

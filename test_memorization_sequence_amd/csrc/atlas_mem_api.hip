@@ -107,7 +107,6 @@ static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
 
 static const StreamVariant* find_streamed(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
-  if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
   // the kernel addresses one sequence's inputs and coefficients through
   // 32-bit buffer offsets (below 1 GiB each)
@@ -151,8 +150,9 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   if (out) *out = nullptr;
   if (sout) *sout = nullptr;
   if (tout) *tout = nullptr;
+  const StreamVariant* tv = nullptr;
   if (c->kernel == ATLAS_KERNEL_STREAMED || c->kernel == ATLAS_KERNEL_AUTO) {
-    const StreamVariant* tv = find_streamed(c);
+    tv = find_streamed(c);
     if (tv && (c->kernel == ATLAS_KERNEL_STREAMED || tv->autopick)) {
       if (tout) *tout = tv;
       return ATLAS_OK;
@@ -166,6 +166,12 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
       return ATLAS_OK;
     }
     if (c->kernel == ATLAS_KERNEL_SHARDED) return ATLAS_ERR_UNSUPPORTED;
+  }
+  // AUTO without a sharded kernel (l_p, Huber): a streamed one still beats
+  // the per-sequence family
+  if (c->kernel == ATLAS_KERNEL_AUTO && tv) {
+    if (tout) *tout = tv;
+    return ATLAS_OK;
   }
   const int h = c->memory == ATLAS_MEM_MLP ? c->mlp_hidden : 0;
   const int need_w = c->chunk + c->window - 1;

@@ -35,6 +35,7 @@
 #include "atlas_mem_internal.h"
 #include "atlas_mem_coeff.h"
 #include "atlas_mem_frag.h"
+#include "atlas_mem_bias.h"
 #include "atlas_mem_group.h"
 
 namespace atlas {
@@ -99,9 +100,13 @@ struct TShape {
   static constexpr size_t xbytes = G == 1 ? xYh : xYp + 2ull * G * NQ * NDT * tile_bytes;
   static_assert(D == DV, "one tile-major stride for both layers");
   static_assert(WP <= 2 * BC, "windows of chunks >= 1 start inside the call");
+  static_assert((size_t)(1 + NW) * WP * 4 <= mx((size_t)HJ * LT, (size_t)WP * LQ) * 2, "Huber scratch fits AT");
 };
 
-template <class S>
+// SHAPE: 0 for the l2 and dot-product biases, BIAS_LP or BIAS_HUBER for the
+// biases that form D2 from whole error rows; each instance holds only its own
+// bias's code.
+template <class S, int SHAPE>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 stream_mlp_kernel(ShardedParams p) {
@@ -130,6 +135,9 @@ stream_mlp_kernel(ShardedParams p) {
   const int N = p.N, c = p.c, W = BC + c - 1;
   const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
   const float s_grad = p.grad_scale;
+  // l_p and Huber biases reshape the errors once whole rows are known
+  constexpr bool shaped = SHAPE != 0, huber = SHAPE == BIAS_HUBER;
+  const float bias_p = p.bias_p, sign_alpha = p.sign_alpha;
 
   char* st = p.state + (size_t)seq * p.seq_stride;
   float* W1g = reinterpret_cast<float*>(st + p.off_weights);
@@ -139,6 +147,7 @@ stream_mlp_kernel(ShardedParams p) {
   float* hk = reinterpret_cast<float*>(st + p.off_halo_k);
   float* hv = reinterpret_cast<float*>(st + p.off_halo_v);
   float* hg = reinterpret_cast<float*>(st + p.off_halo_g);
+  float* hd = reinterpret_cast<float*>(st + p.off_halo_d);   // Huber only
   int64_t* cnt = reinterpret_cast<int64_t*>(st + p.off_count);
   const int halo_valid = (int)min<int64_t>(*cnt, (int64_t)(c - 1));
   const bf16* q = reinterpret_cast<const bf16*>(p.q) + (size_t)seq * N * D;
@@ -146,6 +155,7 @@ stream_mlp_kernel(ShardedParams p) {
   const bf16* v = reinterpret_cast<const bf16*>(p.v) + (size_t)seq * N * DV;
   bf16* out = reinterpret_cast<bf16*>(p.out) + (size_t)seq * N * DV;
   const float* gam_in = p.gamma + (size_t)seq * N;
+  const float* dl_in = huber ? p.delta + (size_t)seq * N : nullptr;
   const float* coef_seq = p.coef + (size_t)seq * p.nchunks * p.coef_stride;
 
   bf16* Xc = reinterpret_cast<bf16*>(smem + S::oXa);   // window keys of the current chunk
@@ -155,6 +165,11 @@ stream_mlp_kernel(ShardedParams p) {
   bf16* D2 = reinterpret_cast<bf16*>(smem + S::oD2);
   bf16* AT = reinterpret_cast<bf16*>(smem + S::oAT);
   bf16* Q2T = AT;
+  // Huber: thresholds of the window rows and the four waves' partial |e|^2
+  // per row, in the AT region (free from the end of a pass's exchange to its
+  // next tile, and in the prologue)
+  float* dlw = reinterpret_cast<float*>(smem + S::oAT);
+  float* rn = dlw + WP;
   bf16* W2L = reinterpret_cast<bf16*>(smem + S::oW2);
   bf16* An = W2L;
   bf16* Ah = reinterpret_cast<bf16*>(smem + S::oAh);
@@ -325,6 +340,50 @@ stream_mlp_kernel(ShardedParams p) {
     t = dot ? 0.f : t;
     return (bf16)(sg * (t - vv));
   };
+  // l_p / Huber: D2 = s gamma slope(e) from the errors e, which have replaced
+  // the window sums in yh.  The Huber choice needs each row's |e|_2: the
+  // lanes of a row within a wave add over xor-shuffles, the four waves
+  // through rn.  Needs sgw (and for Huber dlw) of the chunk in LDS.
+  auto shape_d2 = [&]() __attribute__((always_inline)) {
+    const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, wv = threadIdx.x >> 6;
+    const int dvw = S::DVW * wv;
+    if (huber) {
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        float s2 = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s2 = fmaf(yh[m][bb][r], yh[m][bb][r], s2);
+        s2 += __shfl_xor(s2, 16);
+        s2 += __shfl_xor(s2, 32);
+        if (g == 0) rn[wv * WP + 16 * m + c16] = s2;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int w = 16 * m + c16;
+      const float sg = s_grad * sgw[w];
+      bool small = true;
+      float dl = 0.f;
+      if (huber) {
+        const float n2 = ((rn[w] + rn[WP + w]) + rn[2 * WP + w]) + rn[3 * WP + w];
+        dl = dlw[w];
+        small = sqrtf(n2) <= dl;
+      }
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        bf16x4 d;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = yh[m][bb][r];
+          d[r] = (bf16)(sg * (huber ? huber_slope(e, small, dl, sign_alpha) : lp_slope(e, bias_p, sign_alpha)));
+        }
+        *reinterpret_cast<bf16x4*>(D2 + w * LV + dvw + 16 * bb + 4 * g) = d;
+      }
+    }
+  };
   // chunk 0 (window rows may come from the halo); needs sgw of the chunk in LDS
   auto finish_d2 = [&](int ch, const D2Regs& R, const bf16* Xw) {
     const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
@@ -347,12 +406,36 @@ stream_mlp_kernel(ShardedParams p) {
             for (int r = 0; r < 4; ++r) xr[r] = hk[(c - 1 + i) * D + o + r];
           }
         }
-        bf16x4 d;
+        if constexpr (shaped) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] = d2_of(sg, xr[r], yh[m][bb][r], (float)R.vv[m][bb][r]);
-        *reinterpret_cast<bf16x4*>(D2 + w * LV + o) = d;
+          for (int r = 0; r < 4; ++r) yh[m][bb][r] += (res ? xr[r] : 0.f) - (float)R.vv[m][bb][r];
+        } else {
+          bf16x4 d;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d[r] = d2_of(sg, xr[r], yh[m][bb][r], (float)R.vv[m][bb][r]);
+          *reinterpret_cast<bf16x4*>(D2 + w * LV + o) = d;
+        }
       }
     }
+    if constexpr (shaped) shape_d2();
+  };
+  // chunks >= 1, l_p / Huber: the errors from the staged value rows Vw
+  auto shaped_d2_lds = [&](const bf16* Vw, const bf16* Xw) {
+    const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int w = 16 * m + c16;
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        const int o = dvw + 16 * bb + 4 * g;
+        const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(Vw + w * LV + o);
+        bf16x4 x4 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+        if constexpr (D == DV) x4 = *reinterpret_cast<const bf16x4*>(Xw + w * LX + o);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yh[m][bb][r] += (res ? (float)x4[r] : 0.f) - (float)v4[r];
+      }
+    }
+    shape_d2();
   };
   // chunks >= 1: from the staged value rows Vw, branch-free
   auto finish_d2_lds = [&](const bf16* Vw, const bf16* Xw) {
@@ -547,6 +630,12 @@ stream_mlp_kernel(ShardedParams p) {
     // gamma of the window rows
     rows_to_lds<4, WP, 4, 4, S::NW>(rG, reinterpret_cast<char*>(sgw), wave_s, lane,
                                     [&](int w) { return win(w, wb, ten) ? (wb + w) * 4 : -1; });
+    // Huber: their thresholds (AT region, free now)
+    if (huber) {
+      const __amdgpu_buffer_rsrc_t rD = buffer_of(dl_in, (unsigned)N * 4);
+      rows_to_lds<4, WP, 4, 4, S::NW>(rD, reinterpret_cast<char*>(dlw), wave_s, lane,
+                                      [&](int w) { return win(w, wb, ten) ? (wb + w) * 4 : -1; });
+    }
   };
 
   // ---- prologue: inputs of chunk 0 (and the keys of chunk 1), then chunk 0's forward
@@ -561,6 +650,10 @@ stream_mlp_kernel(ShardedParams p) {
     store_window(Xc, w0);
     if (nchunks > 1) store_window(Xn, w1);
     store_chunk(c0);
+    if (huber && tid < WP) {
+      const int i = -(c - 1) + tid;
+      dlw[tid] = row_ok(tid, 0, min(N, BC) - 1) ? (i >= 0 ? dl_in[i] : hd[c - 1 + i]) : 0.f;
+    }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < NT; ++m)
@@ -915,7 +1008,8 @@ stream_mlp_kernel(ShardedParams p) {
     if (more) {
       wait_vmem();       // this wave's loads into LDS have landed
       __syncthreads();   // and everyone's
-      finish_d2_lds(W2L, Xn);
+      if constexpr (shaped) shaped_d2_lds(W2L, Xn);
+      else finish_d2_lds(W2L, Xn);
       prefetch(J0, dst_t);
       bf16* tmp = Xc;
       Xc = Xn;
@@ -933,6 +1027,7 @@ stream_mlp_kernel(ShardedParams p) {
       for (int d = lane; d < D; d += 64) hk[j * D + d] = i >= 0 ? (float)k[(size_t)i * D + d] : hk[(N + j) * D + d];
       for (int o = lane; o < DV; o += 64) hv[j * DV + o] = i >= 0 ? (float)v[(size_t)i * DV + o] : hv[(N + j) * DV + o];
       if (lane == 0) hg[j] = i >= 0 ? gam_in[i] : hg[N + j];
+      if (lane == 0 && huber) hd[j] = i >= 0 ? dl_in[i] : hd[N + j];
     }
     if (lane == 0) *cnt += N;
   }
@@ -949,17 +1044,25 @@ hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipSt
                      stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static bool attr_set = false;
-  if (!attr_set) {
+  const int shape = sp.bias == BIAS_LP || sp.bias == BIAS_HUBER ? sp.bias : 0;
+  const void* fn = shape == BIAS_LP      ? reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_LP>)
+                   : shape == BIAS_HUBER ? reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_HUBER>)
+                                         : reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, 0>);
+  static bool attr_set[4] = {false, false, false, false};
+  if (!attr_set[shape]) {
     // allow more than the default dynamic LDS; a refusal shows up at launch
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
     (void)hipGetLastError();
-    attr_set = true;
+    attr_set[shape] = true;
   }
   const unsigned blocks = G == 1 ? (unsigned)sp.n_seq : (unsigned)((sp.n_seq + 7) / 8) * 8u * G;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((streamed::stream_mlp_kernel<S>), dim3(blocks), dim3(256), S::lds, stream, sp);
+  if (shape == BIAS_LP)
+    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_LP>), dim3(blocks), dim3(256), S::lds, stream, sp);
+  else if (shape == BIAS_HUBER)
+    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_HUBER>), dim3(blocks), dim3(256), S::lds, stream, sp);
+  else
+    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, 0>), dim3(blocks), dim3(256), S::lds, stream, sp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;

@@ -75,8 +75,8 @@ def test_kernel_family_selection():
 
 
 def test_other_attentional_biases():
-    """l_p needs p >= 1; l_p and Huber run on the per-sequence family (AUTO
-    picks it), not on the sharded one."""
+    """l_p needs p >= 1; l_p and Huber run on the per-sequence and streamed
+    families, not on the sharded one."""
     ok, inv, uns = binding.OK, binding.ERR_INVALID, binding.ERR_UNSUPPORTED
     for p, code in ((0.5, inv), (float("nan"), inv), (1.0, ok), (3.0, ok)):
         assert binding.supported(binding.config_of(replace(WORKLOADS["mlp64"], bias="lp", bias_p=p))) == code, p
@@ -87,6 +87,7 @@ def test_other_attentional_biases():
             assert binding.supported(binding.config_of(wl, "per_sequence")) == ok, (name, bias)
             if wl.memory == "mlp" and wl.feature_map == "identity":
                 assert binding.supported(binding.config_of(wl, "sharded")) == uns, (name, bias)
+                assert binding.supported(binding.config_of(wl, "streamed")) == ok, (name, bias)
 
 
 def test_forward_ex_is_declared_and_checks_its_handle():

@@ -282,8 +282,10 @@ BIAS_SPECS = {
     "huber_smooth": dict(bias="huber", sign_alpha=16.0),
     "huber": dict(bias="huber"),
 }
-BIAS_CASES = ([(n, b) for n in ORDER for b in ("lp3", "lp1.5", "huber_smooth")]
-              + [("mlp64", "huber"), ("layer_scale", "lp1_smooth"), ("mlp64", "lp1_smooth")])
+BIAS_CASES = ([(n, b, "auto") for n in ORDER for b in ("lp3", "lp1.5", "huber_smooth")]
+              + [(n, b, "per_sequence") for n in GROUPED for b in ("lp3", "lp1.5", "huber_smooth")]
+              + [("mlp64", "huber", k) for k in ("per_sequence", "streamed")]
+              + [(n, "lp1_smooth", "auto") for n in ("layer_scale", "mlp64")])
 
 
 def _with_bias(wl, bias):
@@ -292,17 +294,19 @@ def _with_bias(wl, bias):
 
 
 @pytest.mark.parametrize("recipe", ["preset", "lively"])
-@pytest.mark.parametrize("name,bias", BIAS_CASES)
-def test_parity_other_biases(B, name, bias, recipe):
+@pytest.mark.parametrize("name,bias,kernel", BIAS_CASES)
+def test_parity_other_biases(B, name, bias, kernel, recipe):
     wl = _with_bias(WORKLOADS[name], bias).with_shape(batch=1, heads=2, seq_len=SMALL_N)
     if recipe == "lively":
         wl = lively(wl)
-    _say(f"[parity-bias] {name} {bias} {recipe} B=1 H=2 N={SMALL_N}")
+    _say(f"[parity-bias] {name} {bias} {kernel} {recipe} B=1 H=2 N={SMALL_N}")
     binding, H = B
-    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl)
-    assert mem.family() == "per_sequence"
+    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl, kernel=kernel)
+    # AUTO: the streamed family for the identity-map MLPs, else per-sequence
+    want = kernel if kernel != "auto" else "streamed" if name in GROUPED else "per_sequence"
+    assert mem.family() == want
     r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
-    _say(f"[parity-bias] {name} {bias} {recipe}: {r}")
+    _say(f"[parity-bias] {name} {bias} {kernel} {recipe}: {r}")
     tol = H.tol_of(wl)
     assert np.isfinite(out_g).all()
     for key in ("out", "memory_part", "weights", "momentum"):
@@ -311,20 +315,21 @@ def test_parity_other_biases(B, name, bias, recipe):
     assert r["halo_exact"] and r["count_exact"], r
 
 
-def test_huber_split_is_bitwise_equal(B):
+@pytest.mark.parametrize("kernel", ["per_sequence", "streamed"])
+def test_huber_split_is_bitwise_equal(B, kernel):
     """The thresholds of the halo travel in the state: two chunk-aligned calls
     equal one, bit for bit."""
     binding, H = B
     wl = lively(_with_bias(WORKLOADS["layer_scale"], "huber").with_shape(batch=1, heads=2, seq_len=SMALL_N))
-    _say("[split-huber] layer_scale")
+    _say(f"[split-huber] layer_scale kernel={kernel}")
     inputs, w0 = H.prepare(wl)
     dev = H.to_device(wl, inputs)
-    one = binding.AtlasMem(wl)
+    one = binding.AtlasMem(wl, kernel)
     st1 = one.new_state(torch.from_numpy(w0))
     out1 = H.gpu_run(one, wl, dev, st1)
     n1 = 128
     wa, wb = wl.with_shape(seq_len=n1), wl.with_shape(seq_len=SMALL_N - n1)
-    ma, mb = binding.AtlasMem(wa), binding.AtlasMem(wb)
+    ma, mb = binding.AtlasMem(wa, kernel), binding.AtlasMem(wb, kernel)
     st2 = ma.new_state(torch.from_numpy(w0))
     part = lambda t, a, b: t[:, :, a:b].contiguous()
     oa = H.gpu_run(ma, wa, {k_: part(t, 0, n1) for k_, t in dev.items()}, st2)
@@ -349,3 +354,19 @@ def test_huber_needs_its_thresholds(B):
     with pytest.raises(binding.AtlasError):
         mem.forward(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["eta"], dev["theta"], dev["gamma"], st, out,
                     delta=None)
+
+
+@pytest.mark.parametrize("n", [1, 37, 65])
+@pytest.mark.parametrize("bias", ["lp3", "huber_smooth"])
+def test_short_calls_other_biases(B, bias, n):
+    """One partial chunk, and a full chunk plus one token, on the streamed family."""
+    binding, H = B
+    wl = lively(_with_bias(WORKLOADS["layer_scale"], bias).with_shape(batch=1, heads=2, seq_len=n))
+    _say(f"[short-bias] layer_scale {bias} streamed N={n}")
+    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl, kernel="streamed")
+    r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
+    _say(f"[short-bias] {bias} N={n}: {r}")
+    for key in ("out", "memory_part", "weights", "momentum"):
+        if key in r:
+            assert r[key] <= H.tol_of(wl), (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
