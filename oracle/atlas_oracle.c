@@ -100,9 +100,29 @@ static double gelu_prime(double z) {
   return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * exp(-0.5 * z * z) / sqrt(2.0 * pi);
 }
 
-/* Forward pass; keeps the hidden pre-activation z when asked (MLP only). */
+/* Layer norm of u (n entries) without gain or shift: nhat = (u - mean) / sd,
+ * sd = sqrt(var + eps), var the biased variance.  Returns sd.              */
+static double layer_norm(const double* u, int n, double eps, double* nhat) {
+  double mean = 0.0, var = 0.0;
+  for (int o = 0; o < n; ++o) mean += u[o];
+  mean /= n;
+  for (int o = 0; o < n; ++o) var += (u[o] - mean) * (u[o] - mean);
+  var /= n;
+  const double sd = sqrt(var + eps);
+  for (int o = 0; o < n; ++o) nhat[o] = (u[o] - mean) / sd;
+  return sd;
+}
+
+/* Forward pass; keeps the hidden pre-activation z when asked (MLP only),
+ * and with layer norm the normalised branch nhat and its sd.               */
+static void apply_ln(const oracle_config* cfg, const double* th, const double* x,
+                     const double* r, double* y, double* z_keep, double* nhat_keep, double* sd_keep);
 static void apply(const oracle_config* cfg, const double* th, const double* x,
                   const double* r, double* y, double* z_keep) {
+  apply_ln(cfg, th, x, r, y, z_keep, NULL, NULL);
+}
+static void apply_ln(const oracle_config* cfg, const double* th, const double* x,
+                     const double* r, double* y, double* z_keep, double* nhat_keep, double* sd_keep) {
   const int D = oracle_feature_dim(cfg), dv = cfg->d_v, h = cfg->hidden;
   if (cfg->memory == ORC_LINEAR) {
     for (int o = 0; o < dv; ++o) {
@@ -123,10 +143,18 @@ static void apply(const oracle_config* cfg, const double* th, const double* x,
     a[j] = gelu(s);
   }
   for (int o = 0; o < dv; ++o) {
-    double s = cfg->residual ? r[o] : 0.0;
+    double s = 0.0;
     for (int j = 0; j < h; ++j) s += W2[(long)o * h + j] * a[j];
-    y[o] = s;
+    y[o] = s;   /* the branch u = W2 gelu(W1 x) */
   }
+  if (cfg->layernorm) {
+    double* nh = nhat_keep ? nhat_keep : (double*)malloc(sizeof(double) * dv);
+    const double sd = layer_norm(y, dv, cfg->ln_eps, nh);
+    for (int o = 0; o < dv; ++o) y[o] = nh[o];
+    if (sd_keep) *sd_keep = sd;
+    if (!nhat_keep) free(nh);
+  }
+  for (int o = 0; o < dv; ++o) y[o] += cfg->residual ? r[o] : 0.0;
   free(a);
   if (!z_keep) free(z);
 }
@@ -149,7 +177,8 @@ static double lp_slope(double e, double p, double alpha) {
 /* Factors of one token's gradient at theta:
  *   linear: dY (d_v)            G = dY x^T
  *   MLP   : d1 (h), d2 (d_v), a (h)   G = { d1 x^T , d2 a^T }
- * dY / d2 = dLoss/df, with e = f - v:
+ * dY / d2 = dLoss/df (with layer norm: dLoss/du of the branch u, through
+ * the LN Jacobian (g - mean(g) - nhat mean(g nhat)) / sd), with e = f - v:
  *   L2 -> s*gamma*e;  DOT -> -s*gamma*v;  LP -> s*gamma*sign(e)|e|^(p-1)
  *   (elementwise);  HUBER -> s*gamma*e while |e|_2 <= delta, else
  *   s*gamma*delta*sign(e): one choice for the whole token.                 */
@@ -160,7 +189,10 @@ static void grad_factors(const oracle_config* cfg, const double* th,
   const double s = cfg->grad_scale;
   double* f = (double*)malloc(sizeof(double) * dv);
   double* z = cfg->memory == ORC_MLP ? (double*)malloc(sizeof(double) * h) : NULL;
-  apply(cfg, th, x, r, f, z);
+  const int ln = cfg->memory == ORC_MLP && cfg->layernorm;
+  double* nh = ln ? (double*)malloc(sizeof(double) * dv) : NULL;
+  double sd = 1.0;
+  apply_ln(cfg, th, x, r, f, z, nh, &sd);
   int huber_small = 0;
   if (cfg->bias == ORC_BIAS_HUBER) {
     double n2 = 0.0;
@@ -172,6 +204,14 @@ static void grad_factors(const oracle_config* cfg, const double* th,
     else if (cfg->bias == ORC_BIAS_DOT) d2[o] = -s * gamma * v[o];
     else if (cfg->bias == ORC_BIAS_LP) d2[o] = s * gamma * lp_slope(f[o] - v[o], cfg->bias_p, cfg->sign_alpha);
     else d2[o] = s * gamma * (huber_small ? f[o] - v[o] : delta * sign_a(f[o] - v[o], cfg->sign_alpha));
+  }
+  if (ln) {
+    double mg = 0.0, mgn = 0.0;
+    for (int o = 0; o < dv; ++o) { mg += d2[o]; mgn += d2[o] * nh[o]; }
+    mg /= dv;
+    mgn /= dv;
+    for (int o = 0; o < dv; ++o) d2[o] = (d2[o] - mg - nh[o] * mgn) / sd;
+    free(nh);
   }
   if (cfg->memory == ORC_MLP) {
     const double* W2 = th + (long)h * D;
@@ -233,6 +273,7 @@ static int config_ok(const oracle_config* c) {
     return 0;
   }
   if (!(c->sign_alpha >= 0.0 && c->sign_alpha < 1e30)) return 0;
+  if (c->layernorm && (c->memory != ORC_MLP || !(c->ln_eps > 0.0 && c->ln_eps < 1.0))) return 0;
   if (c->bias == ORC_BIAS_LP) return c->bias_p >= 1.0 && c->bias_p < 1e6;
   return c->bias == ORC_BIAS_L2 || c->bias == ORC_BIAS_DOT || c->bias == ORC_BIAS_HUBER;
 }

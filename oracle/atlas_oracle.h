@@ -70,6 +70,10 @@ typedef struct {
                        tanh(sign_alpha * e), the smooth sign of the Miras
                        review (Remark 5 under "Alternative Attentional
                        Biases")                                              */
+  int layernorm;    /* MLP only: f(x) = [r +] LN(W2 gelu(W1 x)), LN over the
+                       d_v outputs without gain or shift (Miras review, the
+                       memory of its three models)                           */
+  double ln_eps;    /* LN: (u - mean) / sqrt(var + ln_eps)                    */
 } oracle_config;
 
 /* Sets the OpenMP thread count used by oracle_forward (n <= 0: default). */

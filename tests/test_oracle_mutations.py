@@ -22,7 +22,7 @@ MUTANTS = {
     "gelu_prime_dropped": ("d1[j] = back * gelu_prime(z[j]);", "d1[j] = back * gelu(z[j]);"),
     "w2_transposed_in_backward": ("back += W2[(long)o * h + j] * d2[o];", "back += W2[(long)j * cfg->d_v + o] * d2[o];"),
     "poly2_diagonal_dropped": ("for (int b = a; b < p; ++b)", "for (int b = a + 1; b < p; ++b)"),
-    "residual_dropped": ("double s = cfg->residual ? r[o] : 0.0;", "double s = 0.0;"),
+    "residual_dropped": ("y[o] += cfg->residual ? r[o] : 0.0;", "y[o] += 0.0;"),
     "halo_ignored": ("if (lo < -halo_valid) lo = -halo_valid;", "if (lo < 0) lo = 0;"),
     "dot_bias_sign": ("-s * gamma * v[o]", "s * gamma * v[o]"),
     "tanh_gelu": ("return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));", "return 0.5 * z * (1.0 + tanh(z));"),
@@ -37,6 +37,12 @@ MUTANTS = {
                             "huber_small ? f[o] - v[o] : sign_a(f[o] - v[o], cfg->sign_alpha)"),
     "huber_halo_threshold_lost": ("nd[j] = huber ? dl[i] : 0.0;", "nd[j] = 0.0;"),
     "huber_squared_norm_test": ("huber_small = sqrt(n2) <= delta;", "huber_small = n2 <= delta;"),
+    "ln_mean_term_dropped": ("(d2[o] - mg - nh[o] * mgn) / sd", "(d2[o] - nh[o] * mgn) / sd"),
+    "ln_nhat_term_dropped": ("(d2[o] - mg - nh[o] * mgn) / sd", "(d2[o] - mg) / sd"),
+    "ln_sd_dropped": ("(d2[o] - mg - nh[o] * mgn) / sd", "(d2[o] - mg - nh[o] * mgn)"),
+    "ln_unbiased_variance": ("  var /= n;", "  var /= n - 1;"),
+    "ln_eps_outside_sqrt": ("const double sd = sqrt(var + eps);", "const double sd = sqrt(var) + eps;"),
+    "ln_residual_dropped": ("y[o] += cfg->residual ? r[o] : 0.0;", "y[o] += cfg->residual && !cfg->layernorm ? r[o] : 0.0;"),
 }
 
 

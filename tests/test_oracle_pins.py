@@ -535,3 +535,69 @@ def test_huber_needs_thresholds_and_lp_needs_p_at_least_one():
     cfg, args, W0 = _mixed_run("lp", bias_p=0.5)
     with pytest.raises(ValueError):
         run(cfg, *args, W0)
+
+
+# --------------------------------------------------------------------------- layer-norm memory
+# Miras review, the memory of its three models: M(x) = x + LN(W sigma(W' x)).
+# Here f(x) = r + LN(W2 gelu(W1 x)), LN over the d_v outputs without gain or
+# shift, (u - mean) / sqrt(var + eps) with the biased variance.
+
+def ln_np(u, eps):
+    return (u - u.mean()) / np.sqrt(u.var() + eps)
+
+
+@pytest.mark.parametrize("bias", ["l2", "dot", "lp", "huber"])
+def test_layernorm_gradient_matches_finite_differences(bias):
+    rng = np.random.default_rng(50)
+    d, h, gamma, s, eps = 4, 5, 0.7, 1.2, 0.05   # eps large enough that its placement matters
+    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=h, residual=True, bias=bias, grad_scale=s,
+                        bias_p=3.0, layernorm=True, ln_eps=eps)
+    theta = rng.standard_normal(h * d + d * h)
+    x, v = rng.standard_normal(d), rng.standard_normal(d) * 2
+    delta = 1.5
+
+    def loss(th):
+        W1, W2 = th[:h * d].reshape(h, d), th[h * d:].reshape(d, h)
+        f = x + ln_np(W2 @ gelu(W1 @ x), eps)
+        e = f - v
+        if bias == "l2":
+            return gamma * s * 0.5 * e @ e
+        if bias == "dot":
+            return -gamma * s * f @ v
+        if bias == "lp":
+            return gamma * s * np.sum(np.abs(e) ** 3) / 3
+        return gamma * s * huber_loss(e, delta)
+
+    g = O.token_grad(cfg, theta, x, x, v, gamma, delta)
+    eps_fd = 1e-6
+    fd = np.array([(loss(theta + eps_fd * e) - loss(theta - eps_fd * e)) / (2 * eps_fd)
+                   for e in np.eye(theta.size)])
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_layernorm_retrieval_is_the_plain_forward_and_scale_free():
+    """theta = alpha = 0: y = q + LN(W2 gelu(W1 q)); LN removes any positive
+    scale of W2 (eps small against the variance)."""
+    rng = np.random.default_rng(51)
+    N, d, h, eps = 13, 6, 7, 1e-12
+    q, k, v = rand_unit(rng, N, d), rand_unit(rng, N, d), rng.standard_normal((N, d))
+    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=h, residual=True, window=2, chunk=4,
+                        momentum=True, layernorm=True, ln_eps=eps)
+    W1, W2 = rng.standard_normal((h, d)), rng.standard_normal((d, h))
+    out, _ = run(cfg, q, k, v, np.zeros(N), rng.uniform(size=N), np.zeros(N), np.ones(N),
+                 np.concatenate([W1.ravel(), W2.ravel()]))
+    want = np.array([q[t] + ln_np(W2 @ gelu(W1 @ q[t]), eps) for t in range(N)])
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-13)
+    out3, _ = run(cfg, q, k, v, np.zeros(N), rng.uniform(size=N), np.zeros(N), np.ones(N),
+                  np.concatenate([W1.ravel(), 3.0 * W2.ravel()]))
+    np.testing.assert_allclose(out3, out, rtol=1e-8, atol=1e-9)
+    branch = out - q
+    np.testing.assert_allclose(branch.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose(branch.var(axis=1), 1.0, rtol=1e-7)
+
+
+def test_layernorm_needs_an_mlp_and_a_positive_eps():
+    for kw in (dict(memory="linear", layernorm=True), dict(memory="mlp", hidden=4, layernorm=True, ln_eps=0.0)):
+        cfg = O.make_config(d_k=3, d_v=3, window=1, chunk=2, **kw)
+        with pytest.raises(ValueError):
+            run(cfg, np.zeros((2, 3)), np.zeros((2, 3)), np.zeros((2, 3)), *[np.zeros(2)] * 4)
