@@ -12,7 +12,10 @@
  *   f(x)  = M x           (linear memory)   or   r + W2 gelu(W1 x)  (2-layer
  *                         MLP memory, exact erf GELU, no biases, r the raw
  *                         key/query; Titans review sec. 3.1 "Memory
- *                         Architecture", ATLAS review sec. 2)
+ *                         Architecture", ATLAS review sec. 2), optionally
+ *                         r + LN(W2 gelu(W1 x)) with a layer norm over the
+ *                         d_v outputs, without gain or shift (Miras review,
+ *                         the memory of its three models)
  *   loss  = sum over the last c tokens i of gamma_i * s * l(f(x_i) - v_i)
  *                         (Omega rule, ATLAS review sec. 3.2) with the
  *                         attentional bias l(e) = |e|^2 / 2, or the
@@ -69,7 +72,7 @@ enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
  * units), the fp32 weights and momentum read and written once per chunk in
  * one fused pass.  SHARDED and STREAMED serve the MLP memory with the
  * identity feature map, d_k == d_v and bf16 io (SHARDED: the l2 and
- * dot-product biases only).  AUTO picks the fastest
+ * dot-product biases and no layer norm).  AUTO picks the fastest
  * family measured for the shape: STREAMED where marked so (large hidden
  * layers), else SHARDED, else STREAMED, else PER_SEQUENCE.                 */
 enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3 };
@@ -97,6 +100,8 @@ typedef struct {
                          tanh(sign_alpha * e), the smooth sign of the Miras
                          review (Remark 5 under "Alternative Attentional
                          Biases"), which keeps the result continuous in e    */
+  int mlp_layernorm;  /* MLP only, 1: f(x) = r + LN(W2 gelu(W1 x))               */
+  float ln_eps;       /* LN: (u - mean) / sqrt(var + ln_eps), 0 < ln_eps < 1    */
 } atlas_mem_config;
 
 typedef struct atlas_mem_s* atlas_mem_t;

@@ -35,6 +35,8 @@ class Workload:
     grad_scale: float = 1.0
     bias_p: float = 2.0    # p of the l_p bias
     sign_alpha: float = 0.0  # l_p / Huber: 0 exact sign(e), > 0 tanh(sign_alpha * e)
+    layernorm: bool = False  # MLP: f = r + LN(W2 gelu(W1 x))
+    ln_eps: float = 1e-5
     alpha_u: tuple | None = (-4.0, 0.0)
     theta_u: tuple | None = (-4.0, 0.0)
     eta_u: tuple | None = (0.0, 3.0)

@@ -95,6 +95,7 @@ static int pd_of(const atlas_mem_config* c) {
 static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
   if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
+  if (c->mlp_layernorm) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
   const int need_w = c->chunk + c->window - 1;
   const ShardedVariant* best = nullptr;
@@ -107,6 +108,7 @@ static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
 
 static const StreamVariant* find_streamed(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
+  if (c->mlp_layernorm) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
   // the kernel addresses one sequence's inputs and coefficients through
   // 32-bit buffer offsets (below 1 GiB each)
@@ -133,6 +135,9 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   if (c->bias < ATLAS_BIAS_L2 || c->bias > ATLAS_BIAS_HUBER) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->bias == ATLAS_BIAS_LP && !(c->bias_p >= 1.f && c->bias_p < 1e6f)) return ATLAS_ERR_INVALID_ARGUMENT;
   if ((c->bias == ATLAS_BIAS_LP || c->bias == ATLAS_BIAS_HUBER) && !(c->sign_alpha >= 0.f && c->sign_alpha < 1e30f))
+    return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->mlp_layernorm != 0 && c->mlp_layernorm != 1) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->mlp_layernorm && (c->memory != ATLAS_MEM_MLP || !(c->ln_eps > 0.f && c->ln_eps < 1.f)))
     return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->io_dtype != ATLAS_BF16 && c->io_dtype != ATLAS_F32) return ATLAS_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(c->grad_scale)) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -372,6 +377,8 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, c
     sp.bias = c.bias;
     sp.bias_p = c.bias_p;
     sp.sign_alpha = c.sign_alpha;
+    sp.layernorm = c.mlp_layernorm;
+    sp.ln_eps = c.ln_eps;
     sp.delta = delta;
     sp.off_halo_d = h->lay.halo_d;
     sp.residual = c.mlp_residual;
@@ -404,6 +411,8 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, c
   cp.bias = c.bias;
   cp.bias_p = c.bias_p;
   cp.sign_alpha = c.sign_alpha;
+  cp.layernorm = c.memory == ATLAS_MEM_MLP ? c.mlp_layernorm : 0;
+  cp.ln_eps = c.ln_eps;
   cp.delta = delta;
   cp.off_halo_d = h->lay.halo_d;
   cp.residual = c.memory == ATLAS_MEM_MLP ? c.mlp_residual : 0;

@@ -51,9 +51,12 @@ struct WsLayout {
   static constexpr size_t D1TM = align_up(D1T + (MLP ? H * WP : 0) * e, 256);
   static constexpr size_t D1TS = align_up(D1TM + (MLP ? H * WP : 0) * e, 256);
   static constexpr size_t Ah = align_up(D1TS + (MLP ? H * WP : 0) * e, 256);
-  // raw errors E [WP][DV] (fp32) for the biases that shape them per token
+  // rows that need whole-row statistics (fp32 [WP][DV]): raw errors for the
+  // l_p / Huber biases, the pre-norm branch u with the layer norm; En keeps
+  // the normalised branch for the LN backward
   static constexpr size_t Ef = align_up(Ah + (MLP ? BC * H : 0) * e, 256);
-  static constexpr size_t bytes = align_up(Ef + WP * DV * 4, 256);
+  static constexpr size_t En = align_up(Ef + WP * DV * 4, 256);
+  static constexpr size_t bytes = align_up(En + (MLP ? WP * DV * 4 : 0), 256);
 };
 
 // T: MFMA operand type (bf16 or float); TI: io type of q, k, v, out.
@@ -116,6 +119,8 @@ struct ChunkParams {
   float bias_p, sign_alpha;
   const float* delta;
   size_t off_halo_d;
+  int layernorm;   // MLP: f = r + LN(W2 gelu(W1 x)), no gain or shift
+  float ln_eps;
 };
 
 struct ShardedParams {
@@ -137,6 +142,8 @@ struct ShardedParams {
   float bias_p, sign_alpha;
   const float* delta;
   size_t off_halo_d;
+  int layernorm;   // MLP: f = r + LN(W2 gelu(W1 x)), no gain or shift
+  float ln_eps;
 };
 
 template <int D, int DV, int H, int G, int WP, int BC>

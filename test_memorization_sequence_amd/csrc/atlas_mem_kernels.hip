@@ -183,6 +183,10 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   // l_p and Huber biases: D2 from the raw errors once whole rows are known
   const bool shaped = p.bias == BIAS_LP || p.bias == BIAS_HUBER, huber = p.bias == BIAS_HUBER;
   const float bias_p = p.bias_p, sign_alpha = p.sign_alpha;
+  // MLP with a layer norm on the branch: D2 and y need whole-row statistics too
+  const bool ln = S::MEM == MEM_MLP && p.layernorm != 0;
+  const float ln_eps = p.ln_eps;
+  const bool rowwise = shaped || ln;
 
   char* st = p.state + (size_t)seq * p.seq_stride;
   float* Wt = reinterpret_cast<float*>(st + p.off_weights);
@@ -224,7 +228,8 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   T* D1TS = reinterpret_cast<T*>(ws + WS::D1TS);
   T* Ah = reinterpret_cast<T*>(ws + WS::Ah);     // [BC][H]   gelu(Zq)
   T* Q2 = reinterpret_cast<T*>(ws + WS::Q2);     // [BC][WP]  C .* (gelu(Zq) A^T)
-  float* Ef = reinterpret_cast<float*>(ws + WS::Ef);  // [WP][DV] raw errors (l_p, Huber)
+  float* Ef = reinterpret_cast<float*>(ws + WS::Ef);  // [WP][DV] raw errors (l_p, Huber) or u (LN)
+  float* En = reinterpret_cast<float*>(ws + WS::En);  // [WP][DV] LN: the normalised branch
   // linear (aliases of the MLP names where the roles coincide)
   T* Mb = W2b;   // [DV][DP]
   T* Sb = S2b;   // [DV][DP]
@@ -323,23 +328,51 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
       D2TM[o * WP + w] = from_f<T>(cMw[w] * d2);
       D2TS[o * WP + w] = from_f<T>(cSw[w] * d2);
     };
-    // l_p / Huber: D2 = s gamma slope(E) from the raw errors in Ef; the
-    // Huber choice needs each row's |E|_2 first
+    // D2 from whole rows, one thread per window row.  In Ef: the raw errors
+    // (l_p, Huber) or, with the layer norm, the branch u = A W2^T.  LN
+    // forward (e = r + (u - mean)/sd - v), the bias's slope g (per token for
+    // Huber), then the LN backward (g - mean(g) - nhat mean(g nhat)) / sd.
     auto shape_rows = [&]() {
       __syncthreads();
-      if (huber) {
-        for (int w = threadIdx.x; w < WP; w += blockDim.x) {
-          float n2 = 0.f;
-          for (int o = 0; o < DV; ++o) n2 += Ef[w * DV + o] * Ef[w * DV + o];
-          rsel[w] = sqrtf(n2) <= dw[w] ? 1.f : 0.f;
+      for (int w = threadIdx.x; w < WP; w += blockDim.x) {
+        float* E = Ef + w * DV;
+        float* Nh = En + w * DV;
+        float sd = 1.f;
+        if (ln) {
+          float mu = 0.f, var = 0.f;
+          for (int o = 0; o < DV; ++o) mu += E[o];
+          mu /= DV;
+          for (int o = 0; o < DV; ++o) var += (E[o] - mu) * (E[o] - mu);
+          var /= DV;
+          sd = sqrtf(var + ln_eps);
+          for (int o = 0; o < DV; ++o) {
+            const float nh = (E[o] - mu) / sd;
+            Nh[o] = nh;
+            E[o] = (res ? to_f(kr[w][o]) : 0.f) + nh - vrow(w, o);
+          }
         }
-        __syncthreads();
-      }
-      for (int e = threadIdx.x; e < WP * DV; e += blockDim.x) {
-        const int w = e / DV, o = e % DV;
-        const float x = Ef[e];
-        const float g = huber ? huber_slope(x, rsel[w] != 0.f, dw[w], sign_alpha) : lp_slope(x, bias_p, sign_alpha);
-        put_d2(w, o, s_grad * gw[w] * g);
+        bool small = true;
+        if (huber) {
+          float n2 = 0.f;
+          for (int o = 0; o < DV; ++o) n2 += E[o] * E[o];
+          small = sqrtf(n2) <= dw[w];
+        }
+        for (int o = 0; o < DV; ++o)
+          E[o] = dot     ? -vrow(w, o)
+               : huber   ? huber_slope(E[o], small, dw[w], sign_alpha)
+               : shaped  ? lp_slope(E[o], bias_p, sign_alpha)
+                         : E[o];
+        if (ln) {
+          float mg = 0.f, mgn = 0.f;
+          for (int o = 0; o < DV; ++o) {
+            mg += E[o];
+            mgn += E[o] * Nh[o];
+          }
+          mg /= DV;
+          mgn /= DV;
+          for (int o = 0; o < DV; ++o) E[o] = (E[o] - mg - Nh[o] * mgn) / sd;
+        }
+        for (int o = 0; o < DV; ++o) put_d2(w, o, s_grad * gw[w] * E[o]);
       }
     };
 
@@ -367,10 +400,11 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
         gemm_nt(WP, DV, ops, [&](int w, int o, const float* a) {
           const float vv = vrow(w, o);
           const float err = (res ? to_f(kr[w][o]) : 0.f) + a[0] - vv;
-          if (shaped) Ef[w * DV + o] = err;
+          if (ln) Ef[w * DV + o] = a[0];
+          else if (shaped) Ef[w * DV + o] = err;
           else put_d2(w, o, dot ? -s_grad * gw[w] * vv : s_grad * gw[w] * err);
         });
-        if (shaped) shape_rows();
+        if (rowwise) shape_rows();
       }
       __syncthreads();
       // D1 = (D2 W2) .* gelu'(Z)
@@ -402,11 +436,26 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
       {
         Op<T> ops[3] = {{Ah, H, W2b, H, H}, {mom ? Ah : nullptr, H, S2b, H, H}, {Q2, WP, D2T, WP, WP}};
         gemm_nt(BC, DV, ops, [&](int n, int o, const float* a) {
-          if (t0 + n <= te) {
-            const float y = (res ? to_f(qr[n][o]) : 0.f) + cA[n] * a[0] + cB[n] * a[1] - a[2];
-            out[(size_t)(t0 + n) * DV + o] = from_f<TI>(y);
-          }
+          const float u = cA[n] * a[0] + cB[n] * a[1] - a[2];
+          if (ln) Ef[n * DV + o] = u;
+          else if (t0 + n <= te) out[(size_t)(t0 + n) * DV + o] = from_f<TI>((res ? to_f(qr[n][o]) : 0.f) + u);
         });
+        if (ln) {
+          // y = r + LN(u), one thread per query row
+          __syncthreads();
+          for (int n = threadIdx.x; n < BC; n += blockDim.x) {
+            if (t0 + n > te) continue;
+            const float* U = Ef + n * DV;
+            float mu = 0.f, var = 0.f;
+            for (int o = 0; o < DV; ++o) mu += U[o];
+            mu /= DV;
+            for (int o = 0; o < DV; ++o) var += (U[o] - mu) * (U[o] - mu);
+            var /= DV;
+            const float sd = sqrtf(var + ln_eps);
+            for (int o = 0; o < DV; ++o)
+              out[(size_t)(t0 + n) * DV + o] = from_f<TI>((res ? to_f(qr[n][o]) : 0.f) + (U[o] - mu) / sd);
+          }
+        }
       }
       __syncthreads();
       // state update at the chunk end

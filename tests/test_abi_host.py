@@ -90,6 +90,25 @@ def test_other_attentional_biases():
                 assert binding.supported(binding.config_of(wl, "streamed")) == ok, (name, bias)
 
 
+def test_layernorm_memory_configs():
+    """The LN variant needs an MLP and 0 < eps < 1; the per-sequence family
+    serves it (AUTO picks it), the sharded family does not."""
+    ok, inv, uns = binding.OK, binding.ERR_INVALID, binding.ERR_UNSUPPORTED
+    ln = lambda name, **kw: replace(WORKLOADS[name], layernorm=True, **kw)
+    assert binding.supported(binding.config_of(ln("linear_poly2"))) == inv
+    assert binding.supported(binding.config_of(ln("mlp64", ln_eps=0.0))) == inv
+    assert binding.supported(binding.config_of(ln("mlp64", ln_eps=1.0))) == inv
+    for name in ("mlp64", "atlas_long", "layer_scale"):
+        for bias in ("l2", "dot", "lp", "huber"):
+            wl = ln(name, bias=bias, bias_p=3.0)
+            assert binding.supported(binding.config_of(wl, "auto")) == ok, (name, bias)
+            assert binding.supported(binding.config_of(wl, "per_sequence")) == ok, (name, bias)
+    assert binding.supported(binding.config_of(ln("layer_scale"), "sharded")) == uns
+    c = binding.config_of(WORKLOADS["mlp64"])
+    c.mlp_layernorm = 2
+    assert binding.supported(c) == inv
+
+
 def test_forward_ex_is_declared_and_checks_its_handle():
     L = binding.lib()
     assert "atlas_mem_forward_ex" in binding.declared_functions()
