@@ -101,12 +101,13 @@ struct TShape {
   static_assert(D == DV, "one tile-major stride for both layers");
   static_assert(WP <= 2 * BC, "windows of chunks >= 1 start inside the call");
   static_assert((size_t)(1 + NW) * WP * 4 <= mx((size_t)HJ * LT, (size_t)WP * LQ) * 2, "Huber scratch fits AT");
+  static_assert((size_t)(4 * WP + 2 * BC) * NW * 4 <= mx((size_t)HJ * LT, (size_t)WP * LQ) * 2, "LN scratch fits AT");
 };
 
 // SHAPE: 0 for the l2 and dot-product biases, BIAS_LP or BIAS_HUBER for the
-// biases that form D2 from whole error rows; each instance holds only its own
-// bias's code.
-template <class S, int SHAPE>
+// biases that form D2 from whole error rows; LNORM: the layer-norm memory
+// r + LN(W2 gelu(W1 x)) (with SHAPE 0).  Each instance holds only its own code.
+template <class S, int SHAPE, bool LNORM>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 stream_mlp_kernel(ShardedParams p) {
@@ -136,7 +137,9 @@ stream_mlp_kernel(ShardedParams p) {
   const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
   const float s_grad = p.grad_scale;
   // l_p and Huber biases reshape the errors once whole rows are known
-  constexpr bool shaped = SHAPE != 0, huber = SHAPE == BIAS_HUBER;
+  constexpr bool shaped = SHAPE != 0, huber = SHAPE == BIAS_HUBER, lnorm = LNORM;
+  static_assert(!(LNORM && SHAPE != 0), "layer norm with the l2 / dot biases");
+  const float ln_eps = p.ln_eps;
   const float bias_p = p.bias_p, sign_alpha = p.sign_alpha;
 
   char* st = p.state + (size_t)seq * p.seq_stride;
@@ -170,6 +173,9 @@ stream_mlp_kernel(ShardedParams p) {
   // next tile, and in the prologue)
   float* dlw = reinterpret_cast<float*>(smem + S::oAT);
   float* rn = dlw + WP;
+  // layer norm: per-wave partial row sums in the same region, four arrays
+  // [NW][WP] for the window rows, two [NW][BC] for the output rows
+  float* lnS = reinterpret_cast<float*>(smem + S::oAT);
   bf16* W2L = reinterpret_cast<bf16*>(smem + S::oW2);
   bf16* An = W2L;
   bf16* Ah = reinterpret_cast<bf16*>(smem + S::oAh);
@@ -384,10 +390,94 @@ stream_mlp_kernel(ShardedParams p) {
       }
     }
   };
+  // sum over the four lane groups that hold one row of a transposed tile
+  auto rowsum = [&](float v) {
+    v += __shfl_xor(v, 16);
+    return v + __shfl_xor(v, 32);
+  };
+  auto across = [&](const float* P, int n, int w) { return ((P[w] + P[n + w]) + P[2 * n + w]) + P[3 * n + w]; };
+  // Layer norm (l2 / dot biases): the branch u is in yh (window sums), t
+  // holds v - r (l2) or v (dot).  Mean and variance of u per row (two
+  // passes), nhat = (u - mean) / sd, the slope g = nhat - t (l2) or -t (dot),
+  // then D2 = s gamma (g - mean(g) - nhat mean(g nhat)) / sd.
+  auto ln_d2 = [&](const float (&t)[NT][NDT][4]) __attribute__((always_inline)) {
+    const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, wv = threadIdx.x >> 6;
+    const int dvw = S::DVW * wv;
+    float* A_ = lnS;
+    float* B_ = A_ + S::NW * WP;
+    float* C_ = B_ + S::NW * WP;
+    float* E_ = C_ + S::NW * WP;
+    float mu[NT], rs[NT];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      float sum = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sum += yh[m][bb][r];
+      sum = rowsum(sum);
+      if (g == 0) A_[wv * WP + 16 * m + c16] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      mu[m] = across(A_, WP, 16 * m + c16) * (1.f / DV);
+      float sum = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float d = yh[m][bb][r] - mu[m];
+          sum = fmaf(d, d, sum);
+        }
+      sum = rowsum(sum);
+      if (g == 0) B_[wv * WP + 16 * m + c16] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      rs[m] = 1.f / sqrtf(across(B_, WP, 16 * m + c16) * (1.f / DV) + ln_eps);
+      float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float nh = (yh[m][bb][r] - mu[m]) * rs[m];
+          const float gg = dot ? -t[m][bb][r] : nh - t[m][bb][r];
+          s1 += gg;
+          s2 = fmaf(gg, nh, s2);
+        }
+      s1 = rowsum(s1);
+      s2 = rowsum(s2);
+      if (g == 0) {
+        C_[wv * WP + 16 * m + c16] = s1;
+        E_[wv * WP + 16 * m + c16] = s2;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int w = 16 * m + c16;
+      const float sg = s_grad * sgw[w];
+      const float mg = across(C_, WP, w) * (1.f / DV), mgn = across(E_, WP, w) * (1.f / DV);
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        bf16x4 d;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float nh = (yh[m][bb][r] - mu[m]) * rs[m];
+          const float gg = dot ? -t[m][bb][r] : nh - t[m][bb][r];
+          d[r] = (bf16)(sg * (gg - mg - nh * mgn) * rs[m]);
+        }
+        *reinterpret_cast<bf16x4*>(D2 + w * LV + dvw + 16 * bb + 4 * g) = d;
+      }
+    }
+  };
   // chunk 0 (window rows may come from the halo); needs sgw of the chunk in LDS
   auto finish_d2 = [&](int ch, const D2Regs& R, const bf16* Xw) {
     const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
     const int t0 = ch * BC;
+    float tln[lnorm ? NT : 1][NDT][4];
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       const int w = 16 * m + c16, i = t0 - (c - 1) + w;
@@ -406,7 +496,10 @@ stream_mlp_kernel(ShardedParams p) {
             for (int r = 0; r < 4; ++r) xr[r] = hk[(c - 1 + i) * D + o + r];
           }
         }
-        if constexpr (shaped) {
+        if constexpr (lnorm) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tln[m][bb][r] = (float)R.vv[m][bb][r] - (res && !dot ? xr[r] : 0.f);
+        } else if constexpr (shaped) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) yh[m][bb][r] += (res ? xr[r] : 0.f) - (float)R.vv[m][bb][r];
         } else {
@@ -418,6 +511,7 @@ stream_mlp_kernel(ShardedParams p) {
       }
     }
     if constexpr (shaped) shape_d2();
+    if constexpr (lnorm) ln_d2(tln);
   };
   // chunks >= 1, l_p / Huber: the errors from the staged value rows Vw
   auto shaped_d2_lds = [&](const bf16* Vw, const bf16* Xw) {
@@ -436,6 +530,25 @@ stream_mlp_kernel(ShardedParams p) {
       }
     }
     shape_d2();
+  };
+  // chunks >= 1, layer norm: the targets from the staged value rows Vw
+  auto ln_d2_lds = [&](const bf16* Vw, const bf16* Xw) {
+    const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
+    float t[NT][NDT][4];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int w = 16 * m + c16;
+#pragma unroll
+      for (int bb = 0; bb < NDT; ++bb) {
+        const int o = dvw + 16 * bb + 4 * g;
+        const bf16x4 v4 = *reinterpret_cast<const bf16x4*>(Vw + w * LV + o);
+        bf16x4 x4 = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+        if constexpr (D == DV) x4 = *reinterpret_cast<const bf16x4*>(Xw + w * LX + o);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[m][bb][r] = (float)v4[r] - (res && !dot ? (float)x4[r] : 0.f);
+      }
+    }
+    ln_d2(t);
   };
   // chunks >= 1: from the staged value rows Vw, branch-free
   auto finish_d2_lds = [&](const bf16* Vw, const bf16* Xw) {
@@ -988,6 +1101,48 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
           for (int bb = 0; bb < NDT; ++bb) yp[m][bb] += d[(m * NDT + bb) * 256];
     }
+    if constexpr (lnorm) {
+      // y = r + LN(u) on this member's rows: mean and variance of each row of
+      // u (yp) over the four lane groups and the four waves
+      const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, wv = threadIdx.x >> 6;
+      float* OA = lnS + 4 * S::NW * WP;
+      float* OB = OA + S::NW * BC;
+      float mu[MQ], rs[MQ];
+#pragma unroll
+      for (int mi = 0; mi < MQ; ++mi) {
+        float sum = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum += yp[mlo + mi][bb][r];
+        sum = rowsum(sum);
+        if (g == 0) OA[wv * BC + 16 * mi + c16] = sum;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int mi = 0; mi < MQ; ++mi) {
+        mu[mi] = across(OA, BC, 16 * mi + c16) * (1.f / DV);
+        float sum = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float d = yp[mlo + mi][bb][r] - mu[mi];
+            sum = fmaf(d, d, sum);
+          }
+        sum = rowsum(sum);
+        if (g == 0) OB[wv * BC + 16 * mi + c16] = sum;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int mi = 0; mi < MQ; ++mi) {
+        rs[mi] = 1.f / sqrtf(across(OB, BC, 16 * mi + c16) * (1.f / DV) + ln_eps);
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yp[mlo + mi][bb][r] = (yp[mlo + mi][bb][r] - mu[mi]) * rs[mi];
+      }
+    }
     {
       // four adjacent values of one output row per lane and tile
       const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, dvw = S::DVW * (threadIdx.x >> 6);
@@ -1009,6 +1164,7 @@ stream_mlp_kernel(ShardedParams p) {
       wait_vmem();       // this wave's loads into LDS have landed
       __syncthreads();   // and everyone's
       if constexpr (shaped) shaped_d2_lds(W2L, Xn);
+      else if constexpr (lnorm) ln_d2_lds(W2L, Xn);
       else finish_d2_lds(W2L, Xn);
       prefetch(J0, dst_t);
       bf16* tmp = Xc;
@@ -1044,25 +1200,29 @@ hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipSt
                      stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int shape = sp.bias == BIAS_LP || sp.bias == BIAS_HUBER ? sp.bias : 0;
-  const void* fn = shape == BIAS_LP      ? reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_LP>)
-                   : shape == BIAS_HUBER ? reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_HUBER>)
-                                         : reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, 0>);
+  // instance: 0 plain, 1 l_p, 2 Huber, 3 layer norm
+  const int inst = sp.layernorm ? 3 : sp.bias == BIAS_LP ? 1 : sp.bias == BIAS_HUBER ? 2 : 0;
+  const void* fns[4] = {reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, 0, false>),
+                        reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_LP, false>),
+                        reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_HUBER, false>),
+                        reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, 0, true>)};
   static bool attr_set[4] = {false, false, false, false};
-  if (!attr_set[shape]) {
+  if (!attr_set[inst]) {
     // allow more than the default dynamic LDS; a refusal shows up at launch
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
+    (void)hipFuncSetAttribute(fns[inst], hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
     (void)hipGetLastError();
-    attr_set[shape] = true;
+    attr_set[inst] = true;
   }
   const unsigned blocks = G == 1 ? (unsigned)sp.n_seq : (unsigned)((sp.n_seq + 7) / 8) * 8u * G;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  if (shape == BIAS_LP)
-    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_LP>), dim3(blocks), dim3(256), S::lds, stream, sp);
-  else if (shape == BIAS_HUBER)
-    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_HUBER>), dim3(blocks), dim3(256), S::lds, stream, sp);
+  if (inst == 1)
+    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_LP, false>), dim3(blocks), dim3(256), S::lds, stream, sp);
+  else if (inst == 2)
+    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_HUBER, false>), dim3(blocks), dim3(256), S::lds, stream, sp);
+  else if (inst == 3)
+    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, 0, true>), dim3(blocks), dim3(256), S::lds, stream, sp);
   else
-    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, 0>), dim3(blocks), dim3(256), S::lds, stream, sp);
+    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, 0, false>), dim3(blocks), dim3(256), S::lds, stream, sp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;

@@ -384,18 +384,24 @@ def test_short_calls_other_biases(B, bias, n):
 LN_MLPS = [n for n in ORDER if WORKLOADS[n].memory == "mlp"]
 LN_CASES = ([(n, b, "lively") for n in LN_MLPS for b in ("l2", "dot", "lp3")] + [("mlp64", "huber_smooth", "lively")]
             + [(n, b, "preset") for n in ("atlas_long", "layer_scale") for b in ("l2", "dot")])
+# AUTO: the streamed family for the identity-map MLPs with the l2 / dot
+# biases, the per-sequence family otherwise; the former also per-sequence
+LN_RUNS = ([(n, b, r, "auto") for n, b, r in LN_CASES]
+           + [(n, b, r, "per_sequence") for n, b, r in LN_CASES if n in GROUPED and b in ("l2", "dot")])
 
 
-@pytest.mark.parametrize("name,bias,recipe", LN_CASES)
-def test_parity_layernorm_memory(B, name, bias, recipe):
+@pytest.mark.parametrize("name,bias,recipe,kernel", LN_RUNS)
+def test_parity_layernorm_memory(B, name, bias, recipe, kernel):
     from dataclasses import replace
     wl = WORKLOADS[name] if bias in ("l2", "dot") else _with_bias(WORKLOADS[name], bias)
     wl = replace(wl, layernorm=True, bias=wl.bias if bias != "dot" else "dot").with_shape(batch=1, heads=2, seq_len=SMALL_N)
     if recipe == "lively":
         wl = lively(wl)
-    _say(f"[parity-ln] {name} {bias} {recipe} B=1 H=2 N={SMALL_N}")
+    _say(f"[parity-ln] {name} {bias} {recipe} {kernel} B=1 H=2 N={SMALL_N}")
     binding, H = B
-    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl)
+    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl, kernel=kernel)
+    want = kernel if kernel != "auto" else "streamed" if name in GROUPED and bias in ("l2", "dot") else "per_sequence"
+    assert mem.family() == want
     r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
     _say(f"[parity-ln] {name} {bias} {recipe} ({mem.family()}): {r}")
     tol = H.tol_of(wl)
@@ -404,3 +410,41 @@ def test_parity_layernorm_memory(B, name, bias, recipe):
         if key in r:
             assert r[key] <= tol, (key, r)
     assert r["halo_exact"] and r["count_exact"], r
+
+
+
+@pytest.mark.parametrize("n", [1, 37, 65])
+def test_short_calls_layernorm_streamed(B, n):
+    binding, H = B
+    from dataclasses import replace
+    wl = lively(replace(WORKLOADS["layer_scale"], layernorm=True).with_shape(batch=1, heads=2, seq_len=n))
+    _say(f"[short-ln] layer_scale streamed N={n}")
+    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl, kernel="streamed")
+    r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
+    _say(f"[short-ln] N={n}: {r}")
+    for key in ("out", "memory_part", "weights", "momentum"):
+        if key in r:
+            assert r[key] <= H.tol_of(wl), (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
+
+
+def test_layernorm_split_is_bitwise_equal_streamed(B):
+    binding, H = B
+    from dataclasses import replace
+    wl = lively(replace(WORKLOADS["layer_scale"], layernorm=True).with_shape(batch=1, heads=2, seq_len=SMALL_N))
+    _say("[split-ln] layer_scale streamed")
+    inputs, w0 = H.prepare(wl)
+    dev = H.to_device(wl, inputs)
+    one = binding.AtlasMem(wl, "streamed")
+    st1 = one.new_state(torch.from_numpy(w0))
+    out1 = H.gpu_run(one, wl, dev, st1)
+    n1 = 128
+    wa, wb = wl.with_shape(seq_len=n1), wl.with_shape(seq_len=SMALL_N - n1)
+    ma, mb = binding.AtlasMem(wa, "streamed"), binding.AtlasMem(wb, "streamed")
+    st2 = ma.new_state(torch.from_numpy(w0))
+    part = lambda t, a, b: t[:, :, a:b].contiguous()
+    oa = H.gpu_run(ma, wa, {k_: part(t, 0, n1) for k_, t in dev.items()}, st2)
+    ob = H.gpu_run(mb, wb, {k_: part(t, n1, SMALL_N) for k_, t in dev.items()}, st2)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([oa, ob], dim=2), out1)
+    assert torch.equal(st1, st2)
