@@ -67,7 +67,7 @@ int oracle_feature_dim(const oracle_config* cfg) {
 long oracle_param_count(const oracle_config* cfg) {
   long D = oracle_feature_dim(cfg);
   if (cfg->memory == ORC_LINEAR) return (long)cfg->d_v * D;
-  return (long)cfg->hidden * D + (long)cfg->d_v * cfg->hidden;
+  return (long)cfg->hidden * D * (cfg->gated ? 2 : 1) + (long)cfg->d_v * cfg->hidden;
 }
 
 /* [x_0..x_{p-1}, then x_a*x_b for a <= b in row-major upper-triangle order] */
@@ -132,15 +132,24 @@ static void apply_ln(const oracle_config* cfg, const double* th, const double* x
     }
     return;
   }
+  /* gated: z keeps W1 x then W3 x (2h entries), a = gelu(W1 x) .* (W3 x) */
+  const int gt = cfg->gated;
   const double* W1 = th;
   const double* W2 = th + (long)h * D;
-  double* z = z_keep ? z_keep : (double*)malloc(sizeof(double) * h);
+  const double* W3 = W2 + (long)dv * h;
+  double* z = z_keep ? z_keep : (double*)malloc(sizeof(double) * h * (gt ? 2 : 1));
   double* a = (double*)malloc(sizeof(double) * h);
   for (int j = 0; j < h; ++j) {
     double s = 0.0;
     for (int d = 0; d < D; ++d) s += W1[(long)j * D + d] * x[d];
     z[j] = s;
     a[j] = gelu(s);
+    if (gt) {
+      double s3 = 0.0;
+      for (int d = 0; d < D; ++d) s3 += W3[(long)j * D + d] * x[d];
+      z[h + j] = s3;
+      a[j] *= s3;
+    }
   }
   for (int o = 0; o < dv; ++o) {
     double s = 0.0;
@@ -177,6 +186,9 @@ static double lp_slope(double e, double p, double alpha) {
 /* Factors of one token's gradient at theta:
  *   linear: dY (d_v)            G = dY x^T
  *   MLP   : d1 (h), d2 (d_v), a (h)   G = { d1 x^T , d2 a^T }
+ *   gated : d1 holds 2h entries, the second half d3 for W3: G = { d1 x^T,
+ *           d2 a^T, d3 x^T } with back = W2^T d2, d1 = back .* gelu'(z1) .* z3,
+ *           d3 = back .* gelu(z1), a = gelu(z1) .* z3
  * dY / d2 = dLoss/df (with layer norm: dLoss/du of the branch u, through
  * the LN Jacobian (g - mean(g) - nhat mean(g nhat)) / sd), with e = f - v:
  *   L2 -> s*gamma*e;  DOT -> -s*gamma*v;  LP -> s*gamma*sign(e)|e|^(p-1)
@@ -188,7 +200,8 @@ static void grad_factors(const oracle_config* cfg, const double* th,
   const int D = oracle_feature_dim(cfg), dv = cfg->d_v, h = cfg->hidden;
   const double s = cfg->grad_scale;
   double* f = (double*)malloc(sizeof(double) * dv);
-  double* z = cfg->memory == ORC_MLP ? (double*)malloc(sizeof(double) * h) : NULL;
+  const int gt = cfg->memory == ORC_MLP && cfg->gated;
+  double* z = cfg->memory == ORC_MLP ? (double*)malloc(sizeof(double) * h * (gt ? 2 : 1)) : NULL;
   const int ln = cfg->memory == ORC_MLP && cfg->layernorm;
   double* nh = ln ? (double*)malloc(sizeof(double) * dv) : NULL;
   double sd = 1.0;
@@ -218,8 +231,9 @@ static void grad_factors(const oracle_config* cfg, const double* th,
     for (int j = 0; j < h; ++j) {
       double back = 0.0;
       for (int o = 0; o < dv; ++o) back += W2[(long)o * h + j] * d2[o];
-      d1[j] = back * gelu_prime(z[j]);
-      a[j] = gelu(z[j]);
+      d1[j] = back * gelu_prime(z[j]) * (gt ? z[h + j] : 1.0);
+      a[j] = gelu(z[j]) * (gt ? z[h + j] : 1.0);
+      if (gt) d1[h + j] = back * gelu(z[j]);
     }
     free(z);
   }
@@ -240,13 +254,18 @@ static void add_grad(const oracle_config* cfg, const double* x, const double* d1
     for (int d = 0; d < D; ++d) g[(long)j * D + d] += d1[j] * x[d];
   for (int o = 0; o < dv; ++o)
     for (int j = 0; j < h; ++j) gW2[(long)o * h + j] += d2[o] * a[j];
+  if (cfg->gated) {
+    double* gW3 = gW2 + (long)dv * h;
+    for (int j = 0; j < h; ++j)
+      for (int d = 0; d < D; ++d) gW3[(long)j * D + d] += d1[h + j] * x[d];
+  }
 }
 
 void oracle_token_grad_ex(const oracle_config* cfg, const double* theta,
                           const double* x, const double* r, const double* v,
                           double gamma, double delta, double* grad) {
   const int dv = cfg->d_v, h = cfg->hidden > 0 ? cfg->hidden : 1;
-  double* d1 = (double*)malloc(sizeof(double) * h);
+  double* d1 = (double*)malloc(sizeof(double) * h * 2);
   double* d2 = (double*)malloc(sizeof(double) * dv);
   double* a = (double*)malloc(sizeof(double) * h);
   memset(grad, 0, sizeof(double) * oracle_param_count(cfg));
@@ -274,6 +293,7 @@ static int config_ok(const oracle_config* c) {
   }
   if (!(c->sign_alpha >= 0.0 && c->sign_alpha < 1e30)) return 0;
   if (c->layernorm && (c->memory != ORC_MLP || !(c->ln_eps > 0.0 && c->ln_eps < 1.0))) return 0;
+  if (c->gated && c->memory != ORC_MLP) return 0;
   if (c->bias == ORC_BIAS_LP) return c->bias_p >= 1.0 && c->bias_p < 1e6;
   return c->bias == ORC_BIAS_L2 || c->bias == ORC_BIAS_DOT || c->bias == ORC_BIAS_HUBER;
 }
@@ -297,7 +317,8 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
   double* g = (double*)malloc(sizeof(double) * P);
   const int win = b + c - 1;
   double* X = (double*)malloc(sizeof(double) * win * D);
-  double* D1 = (double*)malloc(sizeof(double) * win * h);
+  const int h1 = cfg->gated ? 2 * h : h;   /* d1 (and d3) per window token */
+  double* D1 = (double*)malloc(sizeof(double) * win * h1);
   double* D2 = (double*)malloc(sizeof(double) * win * dv);
   double* A = (double*)malloc(sizeof(double) * win * h);
   double* xq = (double*)malloc(sizeof(double) * D);
@@ -321,7 +342,7 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
       }
       const int w = i - lo;
       oracle_phi(cfg, ki, X + (long)w * D);
-      grad_factors(cfg, Wc, X + (long)w * D, ki, vi, gi, di, D1 + (long)w * h,
+      grad_factors(cfg, Wc, X + (long)w * D, ki, vi, gi, di, D1 + (long)w * h1,
                    D2 + (long)w * dv, A + (long)w * h);
     }
     for (int n = t0; n <= te; ++n) {
@@ -330,7 +351,7 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
       if (i0 < lo) i0 = lo;
       for (int i = i0; i <= n; ++i) {
         const int w = i - lo;
-        add_grad(cfg, X + (long)w * D, D1 + (long)w * h, D2 + (long)w * dv,
+        add_grad(cfg, X + (long)w * D, D1 + (long)w * h1, D2 + (long)w * dv,
                  A + (long)w * h, g);
       }
       const double eta_n = cfg->momentum ? et[n] : 0.0;

@@ -74,6 +74,9 @@ typedef struct {
                        d_v outputs without gain or shift (Miras review, the
                        memory of its three models)                           */
   double ln_eps;    /* LN: (u - mean) / sqrt(var + ln_eps)                    */
+  int gated;        /* MLP only: the gated memory of three matrices,
+                       f(x) = [r +] W2 (gelu(W1 x) .* (W3 x)) (ATLAS summary,
+                       Atlas++); weights W1 [h][D], W2 [d_v][h], W3 [h][D]    */
 } oracle_config;
 
 /* Sets the OpenMP thread count used by oracle_forward (n <= 0: default). */

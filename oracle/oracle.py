@@ -53,6 +53,7 @@ class OracleConfig(ctypes.Structure):
         ("sign_alpha", ctypes.c_double),
         ("layernorm", ctypes.c_int),
         ("ln_eps", ctypes.c_double),
+        ("gated", ctypes.c_int),
     ]
 
 
@@ -87,14 +88,14 @@ def lib():
 def make_config(*, n_seq=1, seq_len=0, d_k, d_v, memory="linear", hidden=0, residual=False,
                 feature_map="identity", poly_dims=0, window=1, chunk=1, momentum=False,
                 bias="l2", grad_scale=1.0, bias_p=2.0, sign_alpha=0.0, layernorm=False,
-                ln_eps=1e-5) -> OracleConfig:
+                ln_eps=1e-5, gated=False) -> OracleConfig:
     return OracleConfig(
         n_seq=n_seq, seq_len=seq_len, d_k=d_k, d_v=d_v,
         memory=MLP if memory == "mlp" else LINEAR, hidden=hidden, residual=int(bool(residual)),
         feature_map=PHI[feature_map], poly_dims=poly_dims, window=window, chunk=chunk,
         momentum=int(bool(momentum)), bias=BIAS[bias], grad_scale=float(grad_scale),
         bias_p=float(bias_p), sign_alpha=float(sign_alpha), layernorm=int(bool(layernorm)),
-        ln_eps=float(ln_eps))
+        ln_eps=float(ln_eps), gated=int(bool(gated)))
 
 
 def _p(a: np.ndarray):
@@ -187,7 +188,7 @@ def config_for(wl) -> OracleConfig:
                        window=wl.window, chunk=wl.chunk, momentum=wl.momentum, bias=wl.bias,
                        grad_scale=wl.grad_scale, bias_p=getattr(wl, "bias_p", 2.0),
                        sign_alpha=getattr(wl, "sign_alpha", 0.0), layernorm=getattr(wl, "layernorm", False),
-                       ln_eps=getattr(wl, "ln_eps", 1e-5))
+                       ln_eps=getattr(wl, "ln_eps", 1e-5), gated=getattr(wl, "gated", False))
 
 
 def run_workload(wl, inputs: dict, weights0, seqs=None, n_tokens=None, state=None, threads=None):

@@ -19,7 +19,7 @@ MUTANTS = {
     "keep_factor_for_forget": ("W[p] = (1.0 - al[n]) * W[p] + Sx[p];", "W[p] = al[n] * W[p] + Sx[p];"),
     "window_off_by_one": ("int i0 = n - c + 1;", "int i0 = n - c;"),
     "error_sign": ("s * gamma * (f[o] - v[o])", "s * gamma * (v[o] - f[o])"),
-    "gelu_prime_dropped": ("d1[j] = back * gelu_prime(z[j]);", "d1[j] = back * gelu(z[j]);"),
+    "gelu_prime_dropped": ("d1[j] = back * gelu_prime(z[j]) * (gt", "d1[j] = back * gelu(z[j]) * (gt"),
     "w2_transposed_in_backward": ("back += W2[(long)o * h + j] * d2[o];", "back += W2[(long)j * cfg->d_v + o] * d2[o];"),
     "poly2_diagonal_dropped": ("for (int b = a; b < p; ++b)", "for (int b = a + 1; b < p; ++b)"),
     "residual_dropped": ("y[o] += cfg->residual ? r[o] : 0.0;", "y[o] += 0.0;"),
@@ -42,6 +42,9 @@ MUTANTS = {
     "ln_sd_dropped": ("(d2[o] - mg - nh[o] * mgn) / sd", "(d2[o] - mg - nh[o] * mgn)"),
     "ln_unbiased_variance": ("  var /= n;", "  var /= n - 1;"),
     "ln_eps_outside_sqrt": ("const double sd = sqrt(var + eps);", "const double sd = sqrt(var) + eps;"),
+    "gated_z3_dropped_in_d1": ("d1[j] = back * gelu_prime(z[j]) * (gt ? z[h + j] : 1.0);", "d1[j] = back * gelu_prime(z[j]);"),
+    "gated_d3_with_gelu_prime": ("if (gt) d1[h + j] = back * gelu(z[j]);", "if (gt) d1[h + j] = back * gelu_prime(z[j]);"),
+    "gated_w3_block_misplaced": ("double* gW3 = gW2 + (long)dv * h;", "double* gW3 = g;"),
     "ln_residual_dropped": ("y[o] += cfg->residual ? r[o] : 0.0;", "y[o] += cfg->residual && !cfg->layernorm ? r[o] : 0.0;"),
 }
 

@@ -601,3 +601,61 @@ def test_layernorm_needs_an_mlp_and_a_positive_eps():
         cfg = O.make_config(d_k=3, d_v=3, window=1, chunk=2, **kw)
         with pytest.raises(ValueError):
             run(cfg, np.zeros((2, 3)), np.zeros((2, 3)), np.zeros((2, 3)), *[np.zeros(2)] * 4)
+
+
+# --------------------------------------------------------------------------- gated memory
+# ATLAS summary, Atlas++: a gated MLP of three matrices.  Reading:
+# f(x) = r + W2 (gelu(W1 x) .* (W3 x)), the GLU form with the memory's
+# activation; weights W1 [h][D], W2 [d_v][h], W3 [h][D] in that order.
+
+def gated_np(th, x, d, h, residual=True, ln_eps=None):
+    W1 = th[:h * d].reshape(h, d)
+    W2 = th[h * d:h * d + d * h].reshape(d, h)
+    W3 = th[h * d + d * h:].reshape(h, d)
+    u = W2 @ (gelu(W1 @ x) * (W3 @ x))
+    if ln_eps is not None:
+        u = ln_np(u, ln_eps)
+    return (x if residual else 0) + u
+
+
+@pytest.mark.parametrize("bias,residual,ln", [("l2", True, False), ("dot", True, False), ("l2", False, False),
+                                              ("lp", True, False), ("l2", True, True)])
+def test_gated_gradient_matches_finite_differences(bias, residual, ln):
+    rng = np.random.default_rng(60)
+    d, h, gamma, s = 3, 5, 0.6, 1.1
+    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=h, residual=residual, bias=bias, grad_scale=s,
+                        bias_p=3.0, gated=True, layernorm=ln, ln_eps=0.05)
+    assert O.param_count(cfg) == 2 * h * d + d * h
+    theta = rng.standard_normal(2 * h * d + d * h)
+    x, v = rng.standard_normal(d), rng.standard_normal(d)
+
+    def loss(th):
+        f = gated_np(th, x, d, h, residual, 0.05 if ln else None)
+        e = f - v
+        if bias == "l2":
+            return gamma * s * 0.5 * e @ e
+        if bias == "dot":
+            return -gamma * s * f @ v
+        return gamma * s * np.sum(np.abs(e) ** 3) / 3
+
+    g = O.token_grad(cfg, theta, x, x, v, gamma)
+    eps = 1e-6
+    fd = np.array([(loss(theta + eps * e) - loss(theta - eps * e)) / (2 * eps) for e in np.eye(theta.size)])
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_gated_retrieval_is_the_plain_forward_and_w3_zero_blocks_w1():
+    rng = np.random.default_rng(61)
+    N, d, h = 11, 4, 6
+    q, k, v = rand_unit(rng, N, d), rand_unit(rng, N, d), rng.standard_normal((N, d))
+    cfg = O.make_config(d_k=d, d_v=d, memory="mlp", hidden=h, residual=True, window=2, chunk=3,
+                        momentum=True, gated=True)
+    th = rng.standard_normal(2 * h * d + d * h)
+    out, _ = run(cfg, q, k, v, np.zeros(N), rng.uniform(size=N), np.zeros(N), np.ones(N), th)
+    want = np.array([gated_np(th, q[t], d, h) for t in range(N)])
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-13)
+    # W3 = 0: the branch is zero, so W1 and W2 get no gradient; W3 does
+    th0 = th.copy()
+    th0[h * d + d * h:] = 0.0
+    g = O.token_grad(cfg, th0, k[0], k[0], v[0], 1.0)
+    assert not g[:h * d + d * h].any() and g[h * d + d * h:].any()
