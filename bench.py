@@ -115,6 +115,7 @@ def main():
     ap.add_argument("--bias-p", type=float, default=3.0, help="p of the l_p bias")
     ap.add_argument("--sign-alpha", type=float, default=0.0, help="l_p / Huber: 0 exact sign, > 0 tanh(alpha e)")
     ap.add_argument("--layernorm", action="store_true", help="MLP memory r + LN(W2 gelu(W1 x))")
+    ap.add_argument("--gated", action="store_true", help="MLP memory r + W2 (gelu(W1 x) .* (W3 x))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -146,9 +147,9 @@ def main():
     if args.bias is not None:
         from dataclasses import replace
         wl = replace(wl, bias=args.bias, bias_p=args.bias_p, sign_alpha=args.sign_alpha)
-    if args.layernorm:
+    if args.layernorm or args.gated:
         from dataclasses import replace
-        wl = replace(wl, layernorm=True)
+        wl = replace(wl, layernorm=wl.layernorm or args.layernorm, gated=args.gated)
     print(f"[bench] {wl.name} bias={wl.bias}: B={wl.batch} H={wl.heads} N={wl.seq_len} ({wl.note})", file=sys.stderr, flush=True)
     inputs = synth.make_inputs(wl, 0)
     w0 = synth.initial_weights_flat(wl, inputs)
@@ -196,7 +197,7 @@ def main():
     achieved = flops / (k_ms * 1e-3) / 1e12
     peak = PEAK_FP32_TFLOPS if wl.io_dtype == "f32" else PEAK_BF16_TFLOPS
     meas = (MEASURED_TRAFFIC.get((wl.name, kernel_name(binding, wl, args.kernel)))
-            if wl.bias == "l2" and not wl.layernorm else None)
+            if wl.bias == "l2" and not wl.layernorm and not wl.gated else None)
     traffic = meas["bytes"] if meas and meas["src"] == kernel_source_hash() else None
     tokens = wl.batch * wl.seq_len
     res = {
@@ -215,7 +216,7 @@ def main():
         "config": {"workload": wl.name, "kernel_family": args.kernel, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seq_len,
                    "d_k": wl.d_k, "d_v": wl.d_v, "memory": wl.memory, "hidden": wl.hidden,
                    "feature_dim": wl.feature_dim, "window": wl.window, "chunk": wl.chunk,
-                   "momentum": wl.momentum, "bias": wl.bias, "layernorm": wl.layernorm,
+                   "momentum": wl.momentum, "bias": wl.bias, "layernorm": wl.layernorm, "gated": wl.gated,
                    **({"bias_p": wl.bias_p} if wl.bias == "lp" else {}),
                    **({"sign_alpha": wl.sign_alpha} if wl.bias in ("lp", "huber") else {})},
         "head_tokens_per_s": S * wl.seq_len / (ms_per_step * 1e-3),

@@ -15,7 +15,9 @@
  *                         Architecture", ATLAS review sec. 2), optionally
  *                         r + LN(W2 gelu(W1 x)) with a layer norm over the
  *                         d_v outputs, without gain or shift (Miras review,
- *                         the memory of its three models)
+ *                         the memory of its three models), or the gated
+ *                         memory r + W2 (gelu(W1 x) .* (W3 x)) (ATLAS
+ *                         summary, Atlas++)
  *   loss  = sum over the last c tokens i of gamma_i * s * l(f(x_i) - v_i)
  *                         (Omega rule, ATLAS review sec. 3.2) with the
  *                         attentional bias l(e) = |e|^2 / 2, or the
@@ -102,6 +104,9 @@ typedef struct {
                          Biases"), which keeps the result continuous in e    */
   int mlp_layernorm;  /* MLP only, 1: f(x) = r + LN(W2 gelu(W1 x))               */
   float ln_eps;       /* LN: (u - mean) / sqrt(var + ln_eps), 0 < ln_eps < 1    */
+  int mlp_gated;      /* MLP only, 1: gated memory of three matrices (weights
+                         W1 [h][D], W2 [d_v][h], W3 [h][D]); per-sequence
+                         family only                                          */
 } atlas_mem_config;
 
 typedef struct atlas_mem_s* atlas_mem_t;
@@ -109,7 +114,8 @@ typedef struct atlas_mem_s* atlas_mem_t;
 /* Byte offsets inside ONE sequence's state block, and the block stride.
  * The state buffer is [batch*heads] blocks of seq_stride bytes, sequence
  * index s = b*heads + h, 256-byte aligned.  Inside a block:
- *   weights  fp32  linear: M [d_v][D];  MLP: W1 [h][D] then W2 [d_v][h] (row-major)
+ *   weights  fp32  linear: M [d_v][D];  MLP: W1 [h][D] then W2 [d_v][h] (row-major),
+ *                  then W3 [h][D] for the gated memory
  *   momentum fp32  same shape as weights (only if momentum)
  *   halo_k   fp32  [c-1][d_k]  raw keys of the last c-1 tokens seen, oldest first
  *   halo_v   fp32  [c-1][d_v]

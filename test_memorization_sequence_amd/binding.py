@@ -34,7 +34,8 @@ class AtlasMemConfig(ctypes.Structure):
         "batch", "heads", "seq_len", "d_k", "d_v", "memory", "mlp_layers", "mlp_hidden",
         "mlp_residual", "feature_map", "poly_dims", "window", "chunk", "momentum", "bias",
         "io_dtype")] + [("grad_scale", ctypes.c_float), ("kernel", ctypes.c_int), ("bias_p", ctypes.c_float),
-                       ("sign_alpha", ctypes.c_float), ("mlp_layernorm", ctypes.c_int), ("ln_eps", ctypes.c_float)]
+                       ("sign_alpha", ctypes.c_float), ("mlp_layernorm", ctypes.c_int), ("ln_eps", ctypes.c_float),
+                       ("mlp_gated", ctypes.c_int)]
 
 
 class StateLayout(ctypes.Structure):
@@ -105,7 +106,7 @@ def config_of(wl: Workload, kernel: str = "auto") -> AtlasMemConfig:
         window=wl.window, chunk=wl.chunk, momentum=int(wl.momentum), bias=BIAS[wl.bias],
         io_dtype=IO[wl.io_dtype], grad_scale=wl.grad_scale, bias_p=getattr(wl, "bias_p", 2.0),
         sign_alpha=getattr(wl, "sign_alpha", 0.0), mlp_layernorm=int(getattr(wl, "layernorm", False)),
-        ln_eps=getattr(wl, "ln_eps", 1e-5))
+        ln_eps=getattr(wl, "ln_eps", 1e-5), mlp_gated=int(getattr(wl, "gated", False)))
 
 
 def supported(cfg: AtlasMemConfig) -> int:

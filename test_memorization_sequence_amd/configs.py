@@ -37,6 +37,7 @@ class Workload:
     sign_alpha: float = 0.0  # l_p / Huber: 0 exact sign(e), > 0 tanh(sign_alpha * e)
     layernorm: bool = False  # MLP: f = r + LN(W2 gelu(W1 x))
     ln_eps: float = 1e-5
+    gated: bool = False    # MLP: f = r + W2 (gelu(W1 x) .* (W3 x))
     alpha_u: tuple | None = (-4.0, 0.0)
     theta_u: tuple | None = (-4.0, 0.0)
     eta_u: tuple | None = (0.0, 3.0)

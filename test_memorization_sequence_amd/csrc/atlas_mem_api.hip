@@ -95,7 +95,7 @@ static int pd_of(const atlas_mem_config* c) {
 static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
   if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
-  if (c->mlp_layernorm) return nullptr;
+  if (c->mlp_layernorm || c->mlp_gated) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
   const int need_w = c->chunk + c->window - 1;
   const ShardedVariant* best = nullptr;
@@ -109,6 +109,7 @@ static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
 static const StreamVariant* find_streamed(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
   if (c->mlp_layernorm && c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
+  if (c->mlp_gated) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
   // the kernel addresses one sequence's inputs and coefficients through
   // 32-bit buffer offsets (below 1 GiB each)
@@ -138,6 +139,8 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
     return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->mlp_layernorm != 0 && c->mlp_layernorm != 1) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->mlp_layernorm && (c->memory != ATLAS_MEM_MLP || !(c->ln_eps > 0.f && c->ln_eps < 1.f)))
+    return ATLAS_ERR_INVALID_ARGUMENT;
+  if ((c->mlp_gated != 0 && c->mlp_gated != 1) || (c->mlp_gated && c->memory != ATLAS_MEM_MLP))
     return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->io_dtype != ATLAS_BF16 && c->io_dtype != ATLAS_F32) return ATLAS_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(c->grad_scale)) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -198,7 +201,9 @@ static atlas_mem_state_layout make_layout(const atlas_mem_config* c) {
   const int pd = pd_of(c);
   L.feature_dim = feature_dim(c->feature_map, c->d_k, pd);
   const long D = L.feature_dim;
-  L.param_count = c->memory == ATLAS_MEM_MLP ? (long)c->mlp_hidden * D + (long)c->d_v * c->mlp_hidden : (long)c->d_v * D;
+  L.param_count = c->memory == ATLAS_MEM_MLP
+                      ? (long)c->mlp_hidden * D * (c->mlp_gated ? 2 : 1) + (long)c->d_v * c->mlp_hidden
+                      : (long)c->d_v * D;
   const size_t P = (size_t)L.param_count, halo = (size_t)(c->window - 1);
   L.weights = 0;
   L.momentum = align_up(L.weights + P * 4, 16);
@@ -412,6 +417,7 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, c
   cp.bias_p = c.bias_p;
   cp.sign_alpha = c.sign_alpha;
   cp.layernorm = c.memory == ATLAS_MEM_MLP ? c.mlp_layernorm : 0;
+  cp.gated = c.memory == ATLAS_MEM_MLP ? c.mlp_gated : 0;
   cp.ln_eps = c.ln_eps;
   cp.delta = delta;
   cp.off_halo_d = h->lay.halo_d;

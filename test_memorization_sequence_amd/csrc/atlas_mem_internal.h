@@ -56,7 +56,15 @@ struct WsLayout {
   // the normalised branch for the LN backward
   static constexpr size_t Ef = align_up(Ah + (MLP ? BC * H : 0) * e, 256);
   static constexpr size_t En = align_up(Ef + WP * DV * 4, 256);
-  static constexpr size_t bytes = align_up(En + (MLP ? WP * DV * 4 : 0), 256);
+  // gated memory: images of W3, S3, the pre-activation X W3^T, and D3 in the
+  // layouts of D1
+  static constexpr size_t W3b = align_up(En + (MLP ? WP * DV * 4 : 0), 256);
+  static constexpr size_t S3b = align_up(W3b + (MLP ? H * DP : 0) * e, 256);
+  static constexpr size_t Z3f = align_up(S3b + (MLP ? H * DP : 0) * e, 256);
+  static constexpr size_t D3T = align_up(Z3f + (MLP ? WP * H * 4 : 0), 256);
+  static constexpr size_t D3TM = align_up(D3T + (MLP ? H * WP : 0) * e, 256);
+  static constexpr size_t D3TS = align_up(D3TM + (MLP ? H * WP : 0) * e, 256);
+  static constexpr size_t bytes = align_up(D3TS + (MLP ? H * WP : 0) * e, 256);
 };
 
 // T: MFMA operand type (bf16 or float); TI: io type of q, k, v, out.
@@ -121,6 +129,7 @@ struct ChunkParams {
   size_t off_halo_d;
   int layernorm;   // MLP: f = r + LN(W2 gelu(W1 x)), no gain or shift
   float ln_eps;
+  int gated;       // MLP: f = r + W2 (gelu(W1 x) .* (W3 x)) (per-sequence kernel)
 };
 
 struct ShardedParams {
@@ -144,6 +153,7 @@ struct ShardedParams {
   size_t off_halo_d;
   int layernorm;   // MLP: f = r + LN(W2 gelu(W1 x)), no gain or shift
   float ln_eps;
+  int gated;       // MLP: f = r + W2 (gelu(W1 x) .* (W3 x)) (per-sequence kernel)
 };
 
 template <int D, int DV, int H, int G, int WP, int BC>

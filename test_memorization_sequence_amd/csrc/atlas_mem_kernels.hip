@@ -185,6 +185,8 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   const float bias_p = p.bias_p, sign_alpha = p.sign_alpha;
   // MLP with a layer norm on the branch: D2 and y need whole-row statistics too
   const bool ln = S::MEM == MEM_MLP && p.layernorm != 0;
+  // gated memory: A = gelu(X W1^T) .* (X W3^T), a third weight matrix W3
+  const bool gated = S::MEM == MEM_MLP && p.gated != 0;
   const float ln_eps = p.ln_eps;
   const bool rowwise = shaped || ln;
 
@@ -230,6 +232,12 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   T* Q2 = reinterpret_cast<T*>(ws + WS::Q2);     // [BC][WP]  C .* (gelu(Zq) A^T)
   float* Ef = reinterpret_cast<float*>(ws + WS::Ef);  // [WP][DV] raw errors (l_p, Huber) or u (LN)
   float* En = reinterpret_cast<float*>(ws + WS::En);  // [WP][DV] LN: the normalised branch
+  T* W3b = reinterpret_cast<T*>(ws + WS::W3b);   // [H][DP]   gated: image of W3
+  T* S3b = reinterpret_cast<T*>(ws + WS::S3b);   // [H][DP]
+  float* Z3f = reinterpret_cast<float*>(ws + WS::Z3f);  // [WP][H] X W3^T
+  T* D3T = reinterpret_cast<T*>(ws + WS::D3T);   // [H][WP]
+  T* D3TM = reinterpret_cast<T*>(ws + WS::D3TM);
+  T* D3TS = reinterpret_cast<T*>(ws + WS::D3TS);
   // linear (aliases of the MLP names where the roles coincide)
   T* Mb = W2b;   // [DV][DP]
   T* Sb = S2b;   // [DV][DP]
@@ -256,6 +264,15 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
       W2b[e] = from_f<T>(W2[e]);
       S2b[e] = from_f<T>(mom ? Mo[(size_t)H * D + e] : 0.f);
       W2T[j * DV + o] = from_f<T>(W2[e]);
+    }
+    if (gated) {
+      const float* W3 = Wt + (size_t)H * D + (size_t)DV * H;
+      const float* S3 = Mo + (size_t)H * D + (size_t)DV * H;
+      for (int e = threadIdx.x; e < H * DP; e += blockDim.x) {
+        const int j = e / DP, f = e % DP;
+        W3b[e] = from_f<T>(f < D ? W3[j * D + f] : 0.f);
+        S3b[e] = from_f<T>((f < D && mom) ? S3[j * D + f] : 0.f);
+      }
     }
   } else {
     for (int e = threadIdx.x; e < DV * DP; e += blockDim.x) {
@@ -383,12 +400,13 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
     }
 
     if (S::MEM == MEM_MLP) {
-      // Z = X W1^T ; A = gelu(Z)
+      // Z = X W1^T ; A = gelu(Z)   (gated: A = gelu(Z) .* (X W3^T))
       {
-        Op<T> ops[1] = {{Xw, DP, W1b, DP, DP}};
+        Op<T> ops[2] = {{Xw, DP, W1b, DP, DP}, {gated ? Xw : nullptr, DP, W3b, DP, DP}};
         gemm_nt(WP, H, ops, [&](int w, int j, const float* a) {
           Zf[w * H + j] = a[0];
-          const T g = from_f<T>(gelu(a[0]));
+          if (gated) Z3f[w * H + j] = a[1];
+          const T g = from_f<T>(gated ? gelu(a[0]) * a[1] : gelu(a[0]));
           Ab[w * H + j] = g;
           AT[j * WP + w] = g;
         });
@@ -407,22 +425,33 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
         if (rowwise) shape_rows();
       }
       __syncthreads();
-      // D1 = (D2 W2) .* gelu'(Z)
+      // D1 = (D2 W2) .* gelu'(Z)   (gated: .* (X W3^T), and D3 = (D2 W2) .* gelu(Z))
       {
         Op<T> ops[1] = {{D2, DV, W2T, DV, DV}};
         gemm_nt(WP, H, ops, [&](int w, int j, const float* a) {
-          const float d1 = a[0] * gelu_prime(Zf[w * H + j]);
+          const float z = Zf[w * H + j];
+          const float d1 = a[0] * gelu_prime(z) * (gated ? Z3f[w * H + j] : 1.f);
           D1T[j * WP + w] = from_f<T>(d1);
           D1TM[j * WP + w] = from_f<T>(cMw[w] * d1);
           D1TS[j * WP + w] = from_f<T>(cSw[w] * d1);
+          if (gated) {
+            const float d3 = a[0] * gelu(z);
+            D3T[j * WP + w] = from_f<T>(d3);
+            D3TM[j * WP + w] = from_f<T>(cMw[w] * d3);
+            D3TS[j * WP + w] = from_f<T>(cSw[w] * d3);
+          }
         });
       }
       __syncthreads();
       // Zq = A_t Xq W1^T + B_t Xq S1^T - Q1 D1 ; Ah = gelu(Zq)
+      // (gated: .* (A_t Xq W3^T + B_t Xq S3^T - Q1 D3))
       {
-        Op<T> ops[3] = {{Xq, DP, W1b, DP, DP}, {mom ? Xq : nullptr, DP, S1b, DP, DP}, {Q1, WP, D1T, WP, WP}};
+        Op<T> ops[6] = {{Xq, DP, W1b, DP, DP}, {mom ? Xq : nullptr, DP, S1b, DP, DP}, {Q1, WP, D1T, WP, WP},
+                        {gated ? Xq : nullptr, DP, W3b, DP, DP}, {gated && mom ? Xq : nullptr, DP, S3b, DP, DP},
+                        {gated ? Q1 : nullptr, WP, D3T, WP, WP}};
         gemm_nt(BC, H, ops, [&](int n, int j, const float* a) {
-          Ah[n * H + j] = from_f<T>(gelu(cA[n] * a[0] + cB[n] * a[1] - a[2]));
+          const float g1 = gelu(cA[n] * a[0] + cB[n] * a[1] - a[2]);
+          Ah[n * H + j] = from_f<T>(gated ? g1 * (cA[n] * a[3] + cB[n] * a[4] - a[5]) : g1);
         });
       }
       __syncthreads();
@@ -490,6 +519,24 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
             const float ns = Pc * s2 - a[1];
             Mo[e] = ns;
             S2b[o * H + j] = from_f<T>(ns);
+          }
+        });
+      }
+      if (gated) {
+        // W3 <- A_te W3 + B_te S3 - (cM .* D3)^T X,  S3 <- P S3 - (cS .* D3)^T X
+        Op<T> ops[2] = {{D3TM, WP, XwT, WP, WP}, {mom ? D3TS : nullptr, WP, XwT, WP, WP}};
+        gemm_nt(H, DP, ops, [&](int j, int f, const float* a) {
+          if (f < D) {
+            const size_t e = (size_t)H * D + (size_t)DV * H + (size_t)j * D + f;
+            const float w3 = Wt[e], s3 = mom ? Mo[e] : 0.f;
+            const float nw = Ate * w3 + Bte * s3 - a[0];
+            Wt[e] = nw;
+            W3b[j * DP + f] = from_f<T>(nw);
+            if (mom) {
+              const float ns = Pc * s3 - a[1];
+              Mo[e] = ns;
+              S3b[j * DP + f] = from_f<T>(ns);
+            }
           }
         });
       }

@@ -14,9 +14,10 @@ Recipe (one numpy Generator, default_rng(seed), draws in this order):
   initial MLP weights ~ N(0, init_std^2), one draw per head, shared by every
          batch entry (W1 [H, hidden, D] then W2 [H, d_v, hidden]); zero for a
          linear memory;
-  Huber bias only, drawn last: delta_t = m_t * |v_t|_2 [B, H, N] fp32 with
-         m_t = 1/4 or 4, each with probability 1/2 (a threshold per token that
-         depends on the input, far from the token's error norm either way).
+  Huber bias only, drawn after those: delta_t = m_t * |v_t|_2 [B, H, N] fp32
+         with m_t = 1/4 or 4, each with probability 1/2 (a threshold per token
+         that depends on the input, far from the token's error norm either way);
+  gated MLP memory only, drawn last: W3 [H, hidden, D] ~ N(0, init_std^2).
 bf16 values are held in float32 arrays whose low 16 bits are zero.
 """
 from __future__ import annotations
@@ -82,15 +83,21 @@ def make_inputs(wl: Workload, seed: int = 0) -> dict:
         vn = np.sqrt(np.sum(v.astype(np.float64) ** 2, axis=-1))
         m = np.where(rng.uniform(size=g) < 0.5, 0.25, 4.0)
         out["delta"] = (m * vn).astype(np.float32)
+    if wl.memory == "mlp" and wl.gated:
+        out["w3"] = (_normal(rng, (H, wl.hidden, D)) * np.float32(wl.init_std)).astype(np.float32)
     return out
 
 
 def initial_weights_flat(wl: Workload, inputs: dict) -> np.ndarray:
     """[B*H, P] float32: each sequence's initial weights in the order W1 then W2
-    (MLP, both row-major) or M (linear, row-major [d_v][D])."""
+    (MLP, both row-major; then W3 for the gated memory) or M (linear,
+    row-major [d_v][D])."""
     B, H = wl.batch, wl.heads
     if wl.memory == "mlp":
-        per_head = np.concatenate([inputs["w1"].reshape(H, -1), inputs["w2"].reshape(H, -1)], axis=1)
+        parts = [inputs["w1"].reshape(H, -1), inputs["w2"].reshape(H, -1)]
+        if wl.gated:
+            parts.append(inputs["w3"].reshape(H, -1))
+        per_head = np.concatenate(parts, axis=1)
     else:
         per_head = inputs["m"].reshape(H, -1)
     return np.ascontiguousarray(np.broadcast_to(per_head[None], (B, H, per_head.shape[1]))

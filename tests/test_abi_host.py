@@ -113,6 +113,23 @@ def test_layernorm_memory_configs():
     assert binding.supported(c) == inv
 
 
+def test_gated_memory_configs():
+    """The gated memory needs an MLP and runs on the per-sequence family
+    (AUTO picks it); its state holds W1, W2 and W3."""
+    ok, inv, uns = binding.OK, binding.ERR_INVALID, binding.ERR_UNSUPPORTED
+    g = lambda name, **kw: replace(WORKLOADS[name], gated=True, **kw)
+    assert binding.supported(binding.config_of(g("linear_poly2"))) == inv
+    for name in ("mlp64", "atlas_long", "layer_scale"):
+        assert binding.supported(binding.config_of(g(name), "auto")) == ok
+        assert binding.supported(binding.config_of(g(name), "per_sequence")) == ok
+        assert binding.supported(binding.config_of(g(name, layernorm=True, bias="lp", bias_p=3.0))) == ok
+    for fam in ("sharded", "streamed"):
+        assert binding.supported(binding.config_of(g("layer_scale"), fam)) == uns
+    c = binding.config_of(WORKLOADS["mlp64"])
+    c.mlp_gated = 3
+    assert binding.supported(c) == inv
+
+
 def test_forward_ex_is_declared_and_checks_its_handle():
     L = binding.lib()
     assert "atlas_mem_forward_ex" in binding.declared_functions()

@@ -448,3 +448,41 @@ def test_layernorm_split_is_bitwise_equal_streamed(B):
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([oa, ob], dim=2), out1)
     assert torch.equal(st1, st2)
+
+
+
+# --------------------------------------------------------------------------- gated memory
+# Atlas++ (ATLAS summary): f(x) = r + W2 (gelu(W1 x) .* (W3 x)), on the
+# per-sequence family; at the workloads' own init (0.02, where the branch is
+# small) and at 0.2 (where it is a visible part of y).
+GATED_CASES = ([(n, "l2", r, std) for n in LN_MLPS for r in ("preset", "lively") for std in (None, 0.2)]
+               + [("mlp64", "dot", "lively", 0.2), ("mlp64", "lp3", "lively", 0.2),
+                  ("layer_scale", "ln", "lively", 0.2), ("layer_scale", "huber_smooth", "lively", 0.2)])
+
+
+@pytest.mark.parametrize("name,bias,recipe,std", GATED_CASES)
+def test_parity_gated_memory(B, name, bias, recipe, std):
+    from dataclasses import replace
+    wl = WORKLOADS[name]
+    if bias in BIAS_SPECS:
+        wl = _with_bias(wl, bias)
+    elif bias == "dot":
+        wl = replace(wl, bias="dot")
+    elif bias == "ln":
+        wl = replace(wl, layernorm=True)
+    wl = replace(wl, gated=True, init_std=std if std is not None else wl.init_std)
+    wl = wl.with_shape(batch=1, heads=2, seq_len=SMALL_N)
+    if recipe == "lively":
+        wl = lively(wl)
+    _say(f"[parity-gated] {name} {bias} {recipe} init={wl.init_std} B=1 H=2 N={SMALL_N}")
+    binding, H = B
+    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl)
+    assert mem.family() == "per_sequence"
+    r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
+    _say(f"[parity-gated] {name} {bias} {recipe} init={wl.init_std}: {r}")
+    tol = H.tol_of(wl)
+    assert np.isfinite(out_g).all()
+    for key in ("out", "memory_part", "weights", "momentum"):
+        if key in r:
+            assert r[key] <= tol, (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
