@@ -103,6 +103,62 @@ def kernel_name(binding, wl, family):
     return {"sharded": "sharded_mlp_kernel", "streamed": "stream_mlp_kernel", "per_sequence": "chunk_kernel"}[family]
 
 
+def bench_prologue(args, wl):
+    """The fused prologue on the workload's shape: d_model = heads * d_k,
+    K = 4 taps, gate rank 16.  One JSON line; the projection GEMM (rocBLAS)
+    and the fused kernel are timed apart with HIP events on the call's
+    stream.  The kernel is HBM-bound: it reads the projections once and
+    writes q, k, v and the gates once."""
+    import numpy as np
+    import torch
+    from test_memorization_sequence_amd import binding, synth
+    B, N, H, d, K, r = wl.batch, wl.seq_len, wl.heads, wl.d_k, 4, 16
+    dm = H * d
+    print(f"[bench] prologue of {wl.name}: B={B} N={N} d_model={dm} H={H} d={d}", file=sys.stderr, flush=True)
+    inp = synth.make_prologue_inputs(B, N, dm, H, d, K, r, 0)
+    dev = lambda a, dt: torch.from_numpy(a).to("cuda", dtype=dt).contiguous()
+    x, w = dev(inp["x"], torch.bfloat16), dev(inp["w"], torch.bfloat16)
+    wc, gv, gb = dev(inp["w_conv"], torch.float32), dev(inp["gate_v"], torch.float32), dev(inp["gate_b"], torch.float32)
+    q, k, v = [torch.empty(B, H, N, d, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    gates = [torch.empty(B, H, N, dtype=torch.float32, device="cuda") for _ in range(4)]
+    pro = binding.AtlasPrologue(B, N, dm, H, d, K, r)
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in evs:
+        e.record(stream)
+    pro.set_events(*evs)
+    for _ in range(args.warmup):
+        pro.forward(x, w, wc, gv, gb, q, k, v, *gates, stream=stream)
+    torch.cuda.synchronize()
+    gemm_ms, kern_ms = [], []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pro.forward(x, w, wc, gv, gb, q, k, v, *gates, stream=stream)
+        evs[2].synchronize()
+        gemm_ms.append(evs[0].elapsed_time(evs[1]))
+        kern_ms.append(evs[1].elapsed_time(evs[2]))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    rows, ncol = B * N, 3 * H * d + 4 * r
+    flops = 2.0 * rows * ncol * dm
+    kbytes = rows * ncol * 2 + 3 * rows * H * d * 2 + 4 * rows * H * 4
+    g_ms, k_ms = float(np.mean(gemm_ms)), float(np.mean(kern_ms))
+    res = {
+        "metric": "prologue tokens/sec (1 GPU): x -> q, k, v, gates",
+        "value": rows / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy)",
+        "config": {"workload": f"prologue of {wl.name}", "batch": B, "seq_len": N, "d_model": dm, "heads": H,
+                   "d_head": d, "conv_taps": K, "gate_rank": r},
+        "gemm": {"ms": g_ms, "tflops": flops / (g_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                 "frac": flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "roofline": {"bound": "hbm", "kernel": "prologue_kernel", "achieved": kbytes / (k_ms * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kbytes / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None, "alg_bytes_per_launch": kbytes, "kernel_ms": k_ms},
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +172,8 @@ def main():
     ap.add_argument("--sign-alpha", type=float, default=0.0, help="l_p / Huber: 0 exact sign, > 0 tanh(alpha e)")
     ap.add_argument("--layernorm", action="store_true", help="MLP memory r + LN(W2 gelu(W1 x))")
     ap.add_argument("--gated", action="store_true", help="MLP memory r + W2 (gelu(W1 x) .* (W3 x))")
+    ap.add_argument("--prologue", action="store_true",
+                    help="time the fused prologue (x -> q, k, v, gates) on the workload's shape instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -144,6 +202,8 @@ def main():
     from test_memorization_sequence_amd.configs import WORKLOADS
 
     wl = WORKLOADS[args.workload]
+    if args.prologue:
+        return bench_prologue(args, wl)
     if args.bias is not None:
         from dataclasses import replace
         wl = replace(wl, bias=args.bias, bias_p=args.bias_p, sign_alpha=args.sign_alpha)

@@ -18,7 +18,8 @@ from .configs import Workload
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libatlas_mem.so")
-HEADER = os.path.join(os.path.dirname(_PKG), "include", "atlas_mem.h")
+INCLUDE = os.path.join(os.path.dirname(_PKG), "include")
+HEADER = os.path.join(INCLUDE, "atlas_mem.h")
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_OOM, ERR_HIP = 0, 1, 2, 3, 4
 MEM = {"linear": 0, "mlp": 1}
@@ -42,6 +43,11 @@ class StateLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "seq_stride", "weights", "momentum", "halo_k", "halo_v", "halo_g", "count")] + [
         ("feature_dim", ctypes.c_int), ("param_count", ctypes.c_long), ("halo_d", ctypes.c_size_t)]
+
+
+class PrologueConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "batch", "seq_len", "d_model", "heads", "d_head", "conv_taps", "gate_rank")]
 
 
 class AtlasError(RuntimeError):
@@ -88,14 +94,26 @@ def lib():
         L.atlas_mem_error_string.restype = ctypes.c_char_p
         L.atlas_mem_last_hip_error.argtypes = []
         L.atlas_mem_last_hip_error.restype = ctypes.c_char_p
+        pc = ctypes.POINTER(PrologueConfig)
+        L.atlas_prologue_init.argtypes = [pc, ctypes.POINTER(vp)]
+        L.atlas_prologue_init.restype = ctypes.c_int
+        L.atlas_prologue_forward.argtypes = [vp] * 14
+        L.atlas_prologue_forward.restype = ctypes.c_int
+        L.atlas_prologue_set_events.argtypes = [vp] * 4
+        L.atlas_prologue_set_events.restype = ctypes.c_int
+        L.atlas_prologue_free.argtypes = [vp]
+        L.atlas_prologue_free.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
 def declared_functions() -> list[str]:
-    """Names of the functions include/atlas_mem.h declares."""
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(atlas_mem_\w+)\s*\(", text)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            names |= set(re.findall(r"\b(atlas_(?:mem|prologue)_\w+)\s*\(", open(os.path.join(INCLUDE, f)).read()))
+    return sorted(names)
 
 
 def config_of(wl: Workload, kernel: str = "auto") -> AtlasMemConfig:
@@ -207,3 +225,43 @@ class AtlasMem:
         if rc != OK:
             raise AtlasError(rc, what)
         return out
+
+
+class AtlasPrologue:
+    """The fused prologue (include/atlas_prologue.h): x -> q, k, v and the
+    four gates in the layouts AtlasMem.forward takes."""
+
+    def __init__(self, batch, seq_len, d_model, heads, d_head, conv_taps=4, gate_rank=16):
+        self.cfg = PrologueConfig(batch=batch, seq_len=seq_len, d_model=d_model, heads=heads, d_head=d_head,
+                                  conv_taps=conv_taps, gate_rank=gate_rank)
+        h = ctypes.c_void_p()
+        rc = lib().atlas_prologue_init(ctypes.byref(self.cfg), ctypes.byref(h))
+        if rc != OK:
+            raise AtlasError(rc, "atlas_prologue_init")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().atlas_prologue_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_events(self, gemm_before=None, before=None, after=None):
+        raw = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)
+        rc = lib().atlas_prologue_set_events(self.handle, raw(gemm_before), raw(before), raw(after))
+        if rc != OK:
+            raise AtlasError(rc, "atlas_prologue_set_events")
+
+    def forward(self, x, w, w_conv, gate_v, gate_b, q, k, v, alpha, eta, theta, gamma, stream=None):
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        rc = lib().atlas_prologue_forward(
+            self.handle, *[_ptr(t) for t in (x, w, w_conv, gate_v, gate_b, q, k, v, alpha, eta, theta, gamma)],
+            ctypes.c_void_p(stream.cuda_stream))
+        if rc != OK:
+            raise AtlasError(rc, "atlas_prologue_forward")

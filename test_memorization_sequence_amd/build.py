@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libatlas_mem.so")
-SOURCES = ["atlas_mem_kernels.hip", "atlas_mem_sharded.hip", "atlas_mem_stream.hip", "atlas_mem_api.hip"]
+SOURCES = ["atlas_mem_kernels.hip", "atlas_mem_sharded.hip", "atlas_mem_stream.hip", "atlas_mem_api.hip",
+           "atlas_prologue.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -37,7 +38,8 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    # rocBLAS for the prologue's projection GEMM (a plain library GEMM)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp, "-lrocblas"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

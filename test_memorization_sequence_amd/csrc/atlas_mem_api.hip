@@ -88,6 +88,11 @@ static atlas_status hip_fail(hipError_t e) {
   return ATLAS_ERR_HIP;
 }
 
+namespace atlas {
+// the message atlas_mem_last_hip_error returns (other translation units)
+void record_hip_error(const char* what) { std::snprintf(g_hip_error, sizeof(g_hip_error), "%s", what); }
+}  // namespace atlas
+
 static int pd_of(const atlas_mem_config* c) {
   return c->feature_map == ATLAS_PHI_POLY2 ? c->d_k : c->feature_map == ATLAS_PHI_RAW_POLY2 ? c->poly_dims : 0;
 }

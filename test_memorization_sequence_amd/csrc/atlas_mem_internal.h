@@ -16,6 +16,9 @@ enum { BIAS_L2 = 0, BIAS_DOT = 1, BIAS_LP = 2, BIAS_HUBER = 3 };
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// sets the message of atlas_mem_last_hip_error (defined with the C ABI)
+void record_hip_error(const char* what);
+
 constexpr int feature_dim(int phi, int dk, int pd) {
   return phi == PHI_IDENTITY ? dk
        : phi == PHI_POLY2    ? dk + dk * (dk + 1) / 2

@@ -1,0 +1,293 @@
+// atlas_prologue.hip -- the fused prologue (include/atlas_prologue.h): one
+// rocBLAS GEMM for every projection of x, then one gfx950 kernel for the
+// rest of each token's work.
+//
+// Kernel layout: one wave per (run of TOK consecutive tokens of one sequence,
+// head), head fastest, so the waves of a workgroup share the tokens'
+// projection rows (their gate columns) in cache.  Lane l owns DPL = d / 64
+// adjacent channels of the head in each of q, k, v and keeps their conv taps
+// and the last K-1 projection rows in registers while it walks the run: each
+// projection value is loaded once.  SiLU follows the causal depthwise
+// convolution, and the L2 norm of q and k is a wave reduction.  The gate
+// projections V_g (U_g x) run on 4 r lanes: lane g*r + j multiplies the
+// token's j-th U_g output by V_g[h][j]; a reduction over r lanes and a
+// sigmoid give the gate.  HBM-bound: P is read once, q, k, v and the gates
+// are written once.
+
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+
+#include <cstdio>
+#include <new>
+
+#include "atlas_prologue.h"
+#include "atlas_mem_internal.h"
+
+namespace atlas {
+namespace prologue {
+
+struct Params {
+  const bf16* P;       // [B*N][ncol] projections
+  const float* w_conv; // [3*H*d][K]
+  const float* gv;     // [4][H][r]
+  const float* gb;     // [4][H]
+  bf16* q;
+  bf16* k;
+  bf16* v;
+  float* gate[4];
+  int B, N, H, K, r, ncol;
+};
+
+__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+__device__ __forceinline__ float sigm(float z) { return 1.f / (1.f + __expf(-z)); }
+
+constexpr int TOK = 32;   // tokens per wave
+
+template <int D, int K>
+__global__ void __launch_bounds__(256) prologue_kernel(Params p) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int tiles = (p.N + TOK - 1) / TOK;
+  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long items = (long)p.B * tiles * p.H;
+  if (item >= items) return;
+  const int h = (int)(item % p.H);
+  const long bt = item / p.H;
+  const int tile = (int)(bt % tiles);
+  const long b = bt / tiles;
+  const int n0 = tile * TOK, n1 = min(p.N, n0 + TOK);
+  const int HD = p.H * D;
+  bf16* outs[3] = {p.q, p.k, p.v};
+  // taps and the sliding window (oldest first) of this lane's channels
+  float tap[3][DPL][K], win[3][DPL][K];
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int ch = m * HD + h * D + lane * DPL + i;
+#pragma unroll
+      for (int j = 0; j < K; ++j) tap[m][i][j] = p.w_conv[(size_t)ch * K + j];
+#pragma unroll
+      for (int j = 0; j + 1 < K; ++j) {
+        const int src = n0 - (K - 1) + j;
+        win[m][i][j] = src >= 0 ? (float)p.P[(size_t)(b * p.N + src) * p.ncol + ch] : 0.f;
+      }
+    }
+  const int g = lane / p.r, jj = lane - g * p.r;
+  const float gvv = g < 4 ? p.gv[(g * p.H + h) * p.r + jj] : 0.f;
+  const float gbb = g < 4 ? p.gb[g * p.H + h] : 0.f;
+  for (int n = n0; n < n1; ++n) {
+    const bf16* row = p.P + (size_t)(b * p.N + n) * p.ncol;
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const bf16* src = row + m * HD + h * D + lane * DPL;
+      float acc[DPL];
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        win[m][i][K - 1] = (float)src[i];
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) a = fmaf(tap[m][i][j], win[m][i][j], a);
+#pragma unroll
+        for (int j = 0; j + 1 < K; ++j) win[m][i][j] = win[m][i][j + 1];
+        acc[i] = silu(a);
+        ss = fmaf(acc[i], acc[i], ss);
+      }
+      float scale = 1.f;
+      if (m < 2) {
+#pragma unroll
+        for (int s2 = 32; s2 >= 1; s2 >>= 1) ss += __shfl_xor(ss, s2);
+        scale = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+      }
+      bf16* o = outs[m] + ((size_t)(b * p.H + h) * p.N + n) * D + lane * DPL;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) o[i] = (bf16)(acc[i] * scale);
+    }
+    float u = g < 4 ? (float)row[3 * HD + lane] * gvv : 0.f;
+    for (int s2 = 1; s2 < p.r; s2 <<= 1) u += __shfl_xor(u, s2);   // within aligned groups of r lanes
+    if (g < 4 && jj == 0) p.gate[g][(size_t)(b * p.H + h) * p.N + n] = sigm(u + gbb);
+  }
+}
+
+template <int D>
+void launch_d(const Params& p, int K, unsigned blocks, hipStream_t st) {
+  switch (K) {
+    case 1: hipLaunchKernelGGL((prologue_kernel<D, 1>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((prologue_kernel<D, 2>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 3: hipLaunchKernelGGL((prologue_kernel<D, 3>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((prologue_kernel<D, 4>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 5: hipLaunchKernelGGL((prologue_kernel<D, 5>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 6: hipLaunchKernelGGL((prologue_kernel<D, 6>), dim3(blocks), dim3(256), 0, st, p); break;
+    case 7: hipLaunchKernelGGL((prologue_kernel<D, 7>), dim3(blocks), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((prologue_kernel<D, 8>), dim3(blocks), dim3(256), 0, st, p); break;
+  }
+}
+
+}  // namespace prologue
+}  // namespace atlas
+
+struct atlas_prologue_s {
+  uint32_t magic;
+  atlas_prologue_config cfg;
+  int device;
+  rocblas_handle blas;
+  atlas::bf16* P;
+  hipEvent_t ev_gemm, ev_before, ev_after;
+};
+
+static const uint32_t kProMagic = 0xA7A5F10Bu;
+
+static atlas_status check(const atlas_prologue_config* c) {
+  if (!c || c->batch < 1 || c->seq_len < 0 || c->d_model < 8 || c->d_model % 8 || c->heads < 1 || c->d_head < 1 ||
+      c->conv_taps < 1 || c->gate_rank < 1)
+    return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->d_head != 64 && c->d_head != 128 && c->d_head != 256) return ATLAS_ERR_UNSUPPORTED;
+  if (c->conv_taps > 8) return ATLAS_ERR_UNSUPPORTED;
+  if (c->gate_rank != 1 && c->gate_rank != 2 && c->gate_rank != 4 && c->gate_rank != 8 && c->gate_rank != 16)
+    return ATLAS_ERR_UNSUPPORTED;
+  const long rows = (long)c->batch * c->seq_len, ncol = 3L * c->heads * c->d_head + 4L * c->gate_rank;
+  if (rows > 0x7fffffffL || ncol > 0x7fffffffL || rows * c->heads > (1L << 40)) return ATLAS_ERR_INVALID_ARGUMENT;
+  return ATLAS_OK;
+}
+
+extern "C" {
+
+atlas_status atlas_prologue_init(const atlas_prologue_config* cfg, atlas_prologue_t* out) {
+  if (!out) return ATLAS_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  atlas_status s = check(cfg);
+  if (s != ATLAS_OK) return s;
+  atlas_prologue_s* h = new (std::nothrow) atlas_prologue_s();
+  if (!h) return ATLAS_ERR_OUT_OF_MEMORY;
+  h->magic = kProMagic;
+  h->cfg = *cfg;
+  h->P = nullptr;
+  h->blas = nullptr;
+  h->ev_gemm = h->ev_before = h->ev_after = nullptr;
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    atlas::record_hip_error(hipGetErrorString(e));
+    delete h;
+    return ATLAS_ERR_HIP;
+  }
+  const size_t rows = (size_t)cfg->batch * cfg->seq_len;
+  const size_t ncol = 3 * (size_t)cfg->heads * cfg->d_head + 4 * (size_t)cfg->gate_rank;
+  if (rows && hipMalloc(&h->P, rows * ncol * sizeof(atlas::bf16)) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return ATLAS_ERR_OUT_OF_MEMORY;
+  }
+  if (rocblas_create_handle(&h->blas) != rocblas_status_success) {
+    atlas::record_hip_error("rocblas_create_handle failed");
+    (void)hipFree(h->P);
+    delete h;
+    return ATLAS_ERR_HIP;
+  }
+  *out = h;
+  return ATLAS_OK;
+}
+
+atlas_status atlas_prologue_forward(atlas_prologue_t h, const void* x, const void* w, const float* w_conv,
+                                    const float* gate_v, const float* gate_b, void* q, void* k, void* v,
+                                    float* alpha, float* eta, float* theta, float* gamma, void* stream) {
+  if (!h || h->magic != kProMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+  const atlas_prologue_config& c = h->cfg;
+  if (c.seq_len == 0) return ATLAS_OK;
+  const void* p16[] = {x, w, q, k, v};
+  for (const void* p : p16)
+    if (!p || (uintptr_t)p % 16) return ATLAS_ERR_INVALID_ARGUMENT;
+  const void* p4[] = {w_conv, gate_v, gate_b, alpha, eta, theta, gamma};
+  for (const void* p : p4)
+    if (!p || (uintptr_t)p % 4) return ATLAS_ERR_INVALID_ARGUMENT;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev != h->device) return e != hipSuccess ? (atlas::record_hip_error(hipGetErrorString(e)), ATLAS_ERR_HIP)
+                                                                  : ATLAS_ERR_INVALID_ARGUMENT;
+  hipStream_t st = (hipStream_t)stream;
+  const int rows = c.batch * c.seq_len;
+  const int ncol = 3 * c.heads * c.d_head + 4 * c.gate_rank;
+  if (h->ev_gemm && (e = hipEventRecord(h->ev_gemm, st)) != hipSuccess) {
+    atlas::record_hip_error(hipGetErrorString(e));
+    return ATLAS_ERR_HIP;
+  }
+  // P^T [ncol][rows] (column-major) = W [ncol][d_model] . x^T:  op(A) = W from
+  // its column-major view [d_model][ncol] transposed, B = x^T [d_model][rows]
+  const float one = 1.f, zero = 0.f;
+  rocblas_status bs = rocblas_set_stream(h->blas, st);
+  if (bs == rocblas_status_success)
+    bs = rocblas_gemm_ex(h->blas, rocblas_operation_transpose, rocblas_operation_none, ncol, rows, c.d_model, &one, w,
+                         rocblas_datatype_bf16_r, c.d_model, x, rocblas_datatype_bf16_r, c.d_model, &zero, h->P,
+                         rocblas_datatype_bf16_r, ncol, h->P, rocblas_datatype_bf16_r, ncol, rocblas_datatype_f32_r,
+                         rocblas_gemm_algo_standard, 0, 0);
+  if (bs != rocblas_status_success) {
+    char msg[96];
+    std::snprintf(msg, sizeof msg, "rocblas_gemm_ex failed (status %d)", (int)bs);
+    atlas::record_hip_error(msg);
+    return ATLAS_ERR_HIP;
+  }
+  atlas::prologue::Params p;
+  p.P = h->P;
+  p.w_conv = w_conv;
+  p.gv = gate_v;
+  p.gb = gate_b;
+  p.q = (atlas::bf16*)q;
+  p.k = (atlas::bf16*)k;
+  p.v = (atlas::bf16*)v;
+  p.gate[0] = alpha;
+  p.gate[1] = eta;
+  p.gate[2] = theta;
+  p.gate[3] = gamma;
+  p.B = c.batch;
+  p.N = c.seq_len;
+  p.H = c.heads;
+  p.K = c.conv_taps;
+  p.r = c.gate_rank;
+  p.ncol = ncol;
+  const long tiles = (c.seq_len + atlas::prologue::TOK - 1) / atlas::prologue::TOK;
+  const long items = (long)c.batch * tiles * c.heads;
+  const unsigned blocks = (unsigned)((items + 3) / 4);
+  if (h->ev_before && (e = hipEventRecord(h->ev_before, st)) != hipSuccess) {
+    atlas::record_hip_error(hipGetErrorString(e));
+    return ATLAS_ERR_HIP;
+  }
+  switch (c.d_head) {
+    case 64: atlas::prologue::launch_d<64>(p, c.conv_taps, blocks, st); break;
+    case 128: atlas::prologue::launch_d<128>(p, c.conv_taps, blocks, st); break;
+    default: atlas::prologue::launch_d<256>(p, c.conv_taps, blocks, st); break;
+  }
+  if ((e = hipGetLastError()) != hipSuccess ||
+      (h->ev_after && (e = hipEventRecord(h->ev_after, st)) != hipSuccess)) {
+    atlas::record_hip_error(hipGetErrorString(e));
+    return ATLAS_ERR_HIP;
+  }
+  return ATLAS_OK;
+}
+
+atlas_status atlas_prologue_set_events(atlas_prologue_t h, void* gemm_before, void* before, void* after) {
+  if (!h || h->magic != kProMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+  h->ev_gemm = (hipEvent_t)gemm_before;
+  h->ev_before = (hipEvent_t)before;
+  h->ev_after = (hipEvent_t)after;
+  return ATLAS_OK;
+}
+
+atlas_status atlas_prologue_free(atlas_prologue_t h) {
+  if (!h) return ATLAS_OK;
+  if (h->magic != kProMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+  h->magic = 0;
+  const rocblas_status bs = h->blas ? rocblas_destroy_handle(h->blas) : rocblas_status_success;
+  const hipError_t e = h->P ? hipFree(h->P) : hipSuccess;
+  delete h;
+  if (bs != rocblas_status_success) {
+    atlas::record_hip_error("rocblas_destroy_handle failed");
+    return ATLAS_ERR_HIP;
+  }
+  if (e != hipSuccess) {
+    atlas::record_hip_error(hipGetErrorString(e));
+    return ATLAS_ERR_HIP;
+  }
+  return ATLAS_OK;
+}
+
+}  // extern "C"

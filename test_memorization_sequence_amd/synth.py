@@ -102,3 +102,18 @@ def initial_weights_flat(wl: Workload, inputs: dict) -> np.ndarray:
         per_head = inputs["m"].reshape(H, -1)
     return np.ascontiguousarray(np.broadcast_to(per_head[None], (B, H, per_head.shape[1]))
                                 .reshape(B * H, -1))
+
+
+def make_prologue_inputs(batch, seq_len, d_model, heads, d_head, conv_taps=4, gate_rank=16, seed=0) -> dict:
+    """Seeded inputs of the fused prologue (float32 arrays; x and w hold bf16
+    values): x ~ N(0, 1) [B, N, d_model]; w ~ N(0, 1/d_model) [3*H*d + 4*r,
+    d_model]; w_conv ~ N(0, 1/K) [3*H*d, K]; gate_v ~ N(0, 1/r) [4, H, r];
+    gate_b ~ N(0, 1) [4, H]; drawn in that order."""
+    rng = np.random.default_rng(seed)
+    C = 3 * heads * d_head
+    x = round_to_bf16(_normal(rng, (batch, seq_len, d_model)))
+    w = round_to_bf16((_normal(rng, (C + 4 * gate_rank, d_model)) / np.float32(np.sqrt(d_model))).astype(np.float32))
+    w_conv = (_normal(rng, (C, conv_taps)) / np.float32(np.sqrt(conv_taps))).astype(np.float32)
+    gate_v = (_normal(rng, (4, heads, gate_rank)) / np.float32(np.sqrt(gate_rank))).astype(np.float32)
+    gate_b = _normal(rng, (4, heads))
+    return dict(x=x, w=w, w_conv=w_conv, gate_v=gate_v, gate_b=gate_b)
