@@ -14,7 +14,7 @@ L2-normalised q and k, gates as per-token values from low-rank projections):
   c_t        = sum_{j=0}^{K-1} w_conv[ch, j] * P_{t-(K-1)+j}[ch]     (q, k, v channels;
                rows before the sequence's first token count as zero)
   q, k, v    = SiLU(c), SiLU(z) = z * sigmoid(z)
-  q, k       <- q / |q|_2, k / |k|_2 per head (over the head's d channels)
+  q, k       <- q / max(|q|_2, 1e-12), likewise k, per head (over its d channels)
   gate_g     = sigmoid(V_g (U_g x_t) + b_g) per head, g in alpha, eta, theta, gamma
 
 Shapes: x [B][N][d_model]; W [3*H*d + 4*r][d_model]; w_conv [3*H*d][K];
@@ -55,8 +55,8 @@ def prologue(x, W, w_conv, V, b, heads: int, d_head: int, rank: int):
     q = act[..., 0 * H * d:1 * H * d].reshape(B, N, H, d)
     k = act[..., 1 * H * d:2 * H * d].reshape(B, N, H, d)
     v = act[..., 2 * H * d:3 * H * d].reshape(B, N, H, d)
-    q = q / np.linalg.norm(q, axis=-1, keepdims=True)
-    k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    q = q / np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), 1e-12)
+    k = k / np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), 1e-12)
     gates = np.zeros((4, B, H, N))
     for g in range(4):
         u = P[..., C + g * r:C + (g + 1) * r]        # [B][N][r]
