@@ -11,8 +11,8 @@ namespace atlas {
 // ----------------------------------------------------------------------------- coefficients
 // One workgroup per (sequence, chunk), flattened on x.  256 threads; chunk <= 64.
 // QD > 0: also compute Q1 = C .* (Xq X^T) for an identity feature map of
-// width QD (window keys X, chunk queries Xq), stored as bf16 after C.
-// CB16: then also C itself as bf16.
+// width QD (window keys X, chunk queries Xq), stored as bf16 after C with
+// row pitch q1_pitch(WP, CB16).  CB16: then also C itself as bf16.
 template <int BC, int WP, int QD = 0, bool CB16 = false>
 __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   const int chunk = (int)(blockIdx.x % (unsigned)p.nchunks), seq = (int)(blockIdx.x / (unsigned)p.nchunks);
@@ -142,6 +142,7 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
     }
     __syncthreads();
     __bf16* oQ = reinterpret_cast<__bf16*>(oC + BC * WP);
+    constexpr int QP = q1_pitch(WP, CB16);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
     for (int t = wave; t < (BC / 16) * (WP / 16); t += 4) {
       const int m0 = 16 * (t / (WP / 16)), n0 = 16 * (t % (WP / 16));
@@ -153,12 +154,12 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
       }
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + 4 * g + r, col = n0 + c16;
-        oQ[row * WP + col] = (__bf16)(oC[row * WP + col] * acc[r]);
+        oQ[row * QP + col] = (__bf16)(oC[row * WP + col] * acc[r]);
       }
     }
   }
   if constexpr (CB16) {
-    __bf16* oCb = reinterpret_cast<__bf16*>(oC + BC * WP) + BC * WP;
+    __bf16* oCb = reinterpret_cast<__bf16*>(oC + BC * WP) + BC * q1_pitch(WP, CB16);
     for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) oCb[idx] = (__bf16)oC[idx];
   }
   for (int w = threadIdx.x; w < WP; w += blockDim.x) {

@@ -91,11 +91,13 @@ struct Shape {
 //   [2BC+4+WP, +WP)    cS_i
 //   [2BC+4+2WP, +BC*WP) C_{t,i} row-major
 //   with a precomputed Q1 (sharded and streamed kernels, identity feature
-//   map) the block continues with Q1 = C .* (Xq X^T) as bf16 [BC][WP]
-//   (BC*WP/2 floats), and for the streamed kernel then with C itself as bf16
-//   [BC][WP].
+//   map) the block continues with Q1 = C .* (Xq X^T) as bf16 [BC][pitch]
+//   (pitch WP; WP + 4 for the streamed kernel, its LDS pitch, so that the
+//   block is the LDS image), and for the streamed kernel then with C itself
+//   as bf16 [BC][WP].
+constexpr int q1_pitch(int wp, bool cb16) { return cb16 ? wp + 4 : wp; }
 constexpr int coef_stride(int bc, int wp, bool q1 = false, bool cb16 = false) {
-  return 2 * bc + 4 + 2 * wp + bc * wp + (q1 ? bc * wp / 2 : 0) + (cb16 ? bc * wp / 2 : 0);
+  return 2 * bc + 4 + 2 * wp + bc * wp + (q1 ? bc * q1_pitch(wp, cb16) / 2 : 0) + (cb16 ? bc * wp / 2 : 0);
 }
 
 struct CoeffParams {

@@ -114,7 +114,8 @@ stream_mlp_kernel(ShardedParams p) {
   constexpr int D = S::D, DV = S::DV, H = S::H, WP = S::WP, BC = S::BC;
   constexpr int HJ = S::HJ, NJ = S::NJ, NDT = S::NDT, ND = S::ND, NT = S::NT, NQ = S::NQ, NU = S::NU;
   constexpr int LX = S::LX, LV = S::LV, LT = S::LT, LH = S::LH, LQ = S::LQ, L1Q = S::L1Q;
-  constexpr int oCM = 2 * BC + 4, oCS = oCM + WP, oCC = oCS + WP, oQ1g = oCC + BC * WP, oCbg = oQ1g + BC * WP / 2;
+  constexpr int oCM = 2 * BC + 4, oCS = oCM + WP, oCC = oCS + WP, oQ1g = oCC + BC * WP, oCbg = oQ1g + BC * L1Q / 2;
+  static_assert(L1Q == q1_pitch(WP, true), "Q1 of the coefficient block is the LDS image");
   extern __shared__ __attribute__((aligned(256))) char smem[];
 
   // group membership (G = 2): XCD-aware, as in the sharded kernel: block b
@@ -201,7 +202,7 @@ stream_mlp_kernel(ShardedParams p) {
   // HALO = false for chunks >= 1, whose windows never reach before the call.
   constexpr int NXV = (WP * (D / 8) + 255) / 256;   // window key vectors per thread
   constexpr int NQV = (BC * (D / 8) + 255) / 256;   // query vectors per thread
-  constexpr int NQ1V = (BC * WP / 8 + 255) / 256;   // Q1 vectors per thread
+  constexpr int NQ1V = (BC * L1Q / 8 + 255) / 256;  // Q1 vectors per thread (LDS image, pitch L1Q)
   constexpr int NCV = (BC * WP / 8 + 255) / 256;    // C (bf16) vectors per thread
   struct WinRegs { bf16x8 x[NXV]; };
   struct ChunkRegs { bf16x8 q[NQV], q1[NQ1V], cc[NCV]; float ca, cb, cm, cs, cp, sg; };
@@ -266,7 +267,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
     for (int u = 0; u < NQ1V; ++u) {
       const int e = tid + 256 * u;
-      if (e < BC * WP / 8) R.q1[u] = *reinterpret_cast<const bf16x8*>(q1g + 8 * e);
+      if (e < BC * L1Q / 8) R.q1[u] = *reinterpret_cast<const bf16x8*>(q1g + 8 * e);
     }
     const bf16* cbg = reinterpret_cast<const bf16*>(coef + oCbg);
 #pragma unroll
@@ -296,12 +297,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
     for (int u = 0; u < NQ1V; ++u) {
       const int e = tid + 256 * u;
-      if (e < BC * WP / 8) {
-        const bf16x8 x = R.q1[u];
-        bf16* d = Q1 + (8 * e / WP) * L1Q + (8 * e) % WP;
-        *reinterpret_cast<bf16x4*>(d) = bf16x4{x[0], x[1], x[2], x[3]};
-        *reinterpret_cast<bf16x4*>(d + 4) = bf16x4{x[4], x[5], x[6], x[7]};
-      }
+      if (e < BC * L1Q / 8) *reinterpret_cast<bf16x8*>(Q1 + 8 * e) = R.q1[u];
     }
 #pragma unroll
     for (int u = 0; u < NCV; ++u) {
@@ -734,9 +730,9 @@ stream_mlp_kernel(ShardedParams p) {
     // A, B, P, cM, cS (fp32, the block's layout) -> cA ..
     constexpr int NCF = (2 * BC + 4 + 2 * WP) * 4;
     rows_to_lds<16, 1, NCF, NCF, S::NW>(rC, reinterpret_cast<char*>(cA), wave_s, lane, [&](int) { return cb; });
-    // Q1 (bf16 [BC][WP]) -> [BC][L1Q]
-    rows_to_lds<4, BC, WP * 2, L1Q * 2, S::NW>(rC, reinterpret_cast<char*>(Q1), wave_s, lane,
-                                               [&](int n) { return cb + oQ1g * 4 + n * WP * 2; });
+    // Q1 (bf16, already in the LDS image [BC][L1Q]): one contiguous block
+    rows_to_lds<16, 1, BC * L1Q * 2, BC * L1Q * 2, S::NW>(rC, reinterpret_cast<char*>(Q1), wave_s, lane,
+                                                          [&](int) { return cb + oQ1g * 4; });
     // C (bf16 [BC][WP]) -> Cm
     rows_to_lds<16, 1, BC * WP * 2, BC * WP * 2, S::NW>(rC, reinterpret_cast<char*>(Cm), wave_s, lane,
                                                         [&](int) { return cb + oCbg * 4; });
