@@ -33,7 +33,7 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 # x1.0), keyed by the hash of the kernel sources they were taken on.  A
 # changed kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    ("layer_scale", "stream_mlp_kernel"): {"src": "1ae1cccec8f901b4", "bytes": 74.94e9},
+    ("layer_scale", "stream_mlp_kernel"): {"src": "62247ceee7bd7ba4", "bytes": 74.96e9},
 }
 
 
