@@ -486,3 +486,78 @@ def test_parity_gated_memory(B, name, bias, recipe, std):
         if key in r:
             assert r[key] <= tol, (key, r)
     assert r["halo_exact"] and r["count_exact"], r
+
+
+@pytest.mark.parametrize("variant", ["lp3", "huber_smooth", "huber", "layernorm", "layernorm_dot", "gated"])
+def test_full_size_sampled_variants(B, variant):
+    """The layer-scale shape in the benchmark's launch configuration
+    (AUTO: streamed for l_p, Huber and the LN memory; per-sequence for the
+    gated memory) with each variant; the oracle replays the first two chunks
+    of the first and last sequence."""
+    from dataclasses import replace
+    binding, H = B
+    wl = WORKLOADS["layer_scale"]
+    if variant in BIAS_SPECS:
+        wl = _with_bias(wl, variant)
+    elif variant == "layernorm":
+        wl = replace(wl, layernorm=True)
+    elif variant == "layernorm_dot":
+        wl = replace(wl, layernorm=True, bias="dot")
+    else:
+        wl = replace(wl, gated=True)
+    S = wl.batch * wl.heads
+    seqs = sorted({0, S - 1})
+    n = 2 * wl.chunk
+    _say(f"[full-variant] layer_scale {variant} B={wl.batch} H={wl.heads} N={wl.seq_len} sampled seqs={seqs} n={n}")
+    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl, seqs=seqs, n_tokens=n)
+    assert mem.family() == ("per_sequence" if variant == "gated" else "streamed")
+    assert np.isfinite(out_g).all()
+    r = H.compare(wl, inputs, out_g, None, out_o, None, seqs=seqs, n_tokens=n)
+    _say(f"[full-variant] {variant}: {r}")
+    for key in ("out", "memory_part"):
+        if key in r:
+            assert r[key] <= H.tol_of(wl), (key, r)
+    assert (st_g["count"] == wl.seq_len).all()
+
+
+@pytest.mark.parametrize("recipe", ["preset", "lively"])
+@pytest.mark.parametrize("variant", ["l2", "lp3", "huber_smooth", "layernorm", "gated"])
+def test_full_grid_state(B, variant, recipe):
+    """Every sequence of the layer-scale shape (8 x 12 heads) in one call of
+    two chunks and a ragged tail, so that the final state of sampled
+    sequences can be replayed by the oracle.  The weights are compared as
+    the update W - W0 as well (the preset gates decay W towards zero, so the
+    update is mostly that decay; the remaining weights carry the rest)."""
+    from dataclasses import replace
+    binding, H = B
+    wl = WORKLOADS["layer_scale"].with_shape(batch=8, heads=12, seq_len=2 * 64 + 17)
+    if variant in BIAS_SPECS:
+        wl = _with_bias(wl, variant)
+    elif variant == "layernorm":
+        wl = replace(wl, layernorm=True)
+    elif variant == "gated":
+        wl = replace(wl, gated=True)
+    if recipe == "lively":
+        wl = lively(wl)
+    S = wl.batch * wl.heads
+    seqs = [0, S // 2 + 5, S - 1]
+    _say(f"[full-grid] layer_scale {variant} {recipe} B={wl.batch} H={wl.heads} N={wl.seq_len} seqs={seqs}")
+    inputs, w0 = H.prepare(wl)
+    mem = binding.AtlasMem(wl, "auto")
+    dev = H.to_device(wl, inputs)
+    st = mem.new_state(torch.from_numpy(w0))
+    out = H.gpu_run(mem, wl, dev, st)
+    torch.cuda.synchronize()
+    assert mem.device_errors() == 0
+    st_g = H.gpu_state_np(mem, st)
+    from oracle import oracle as O
+    out_o, st_o, _ = O.run_workload(wl, inputs, w0, seqs=seqs)
+    r = H.compare(wl, inputs, out.float().cpu().numpy(), st_g, out_o, st_o, seqs=seqs)
+    w0s = np.asarray(w0, dtype=np.float64)[seqs]
+    r["update"] = H.rel_l2(st_g["weights"][seqs] - w0s, st_o["mem"] - w0s)
+    _say(f"[full-grid] {variant} {recipe} family={mem.family()}: {r}")
+    tol = H.tol_of(wl)
+    for key in ("out", "memory_part", "weights", "update", "momentum"):
+        if key in r:
+            assert r[key] <= tol, (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
