@@ -280,6 +280,65 @@ void oracle_token_grad(const oracle_config* cfg, const double* theta,
   oracle_token_grad_ex(cfg, theta, x, r, v, gamma, 0.0, grad);
 }
 
+/* Muon's orthogonalisation (K. Jordan et al., 2024): X = G / (|G|_F + 1e-7),
+ * taken with fewer rows than columns (transposed if needed); then each step
+ * X <- a X + (b A + c A A) X with A = X X^T, a, b, c = 3.4445, -4.7750,
+ * 2.0315.  Plain triple loops; out is row-major rows x cols like G. */
+void oracle_newton_schulz(const double* G, int rows, int cols, int steps, double* out) {
+  const double a = 3.4445, b = -4.7750, c = 2.0315;
+  const int tr = rows > cols;
+  const int r = tr ? cols : rows, n = tr ? rows : cols;
+  double* X = (double*)malloc(sizeof(double) * r * n);
+  double* Y = (double*)malloc(sizeof(double) * r * n);
+  double* A = (double*)malloc(sizeof(double) * r * r);
+  double* B = (double*)malloc(sizeof(double) * r * r);
+  double nrm = 0.0;
+  for (long e = 0; e < (long)rows * cols; ++e) nrm += G[e] * G[e];
+  nrm = sqrt(nrm) + 1e-7;
+  for (int i = 0; i < rows; ++i)
+    for (int j = 0; j < cols; ++j) {
+      const double x = G[(long)i * cols + j] / nrm;
+      if (tr) X[(long)j * n + i] = x;
+      else X[(long)i * n + j] = x;
+    }
+  for (int s = 0; s < steps; ++s) {
+    for (int i = 0; i < r; ++i)
+      for (int j = 0; j < r; ++j) {
+        double acc = 0.0;
+        for (int l = 0; l < n; ++l) acc += X[(long)i * n + l] * X[(long)j * n + l];
+        A[i * r + j] = acc;
+      }
+    for (int i = 0; i < r; ++i)
+      for (int j = 0; j < r; ++j) {
+        double acc = 0.0;
+        for (int l = 0; l < r; ++l) acc += A[i * r + l] * A[l * r + j];
+        B[i * r + j] = b * A[i * r + j] + c * acc;
+      }
+    for (int i = 0; i < r; ++i)
+      for (int j = 0; j < n; ++j) {
+        double acc = 0.0;
+        for (int l = 0; l < r; ++l) acc += B[i * r + l] * X[(long)l * n + j];
+        Y[(long)i * n + j] = a * X[(long)i * n + j] + acc;
+      }
+    memcpy(X, Y, sizeof(double) * r * n);
+  }
+  for (int i = 0; i < rows; ++i)
+    for (int j = 0; j < cols; ++j)
+      out[(long)i * cols + j] = tr ? X[(long)j * n + i] : X[(long)i * n + j];
+  free(X); free(Y); free(A); free(B);
+}
+
+/* The weight matrices of the memory, in their order in theta. */
+static int weight_matrices(const oracle_config* cfg, int rows[3], int cols[3]) {
+  const int D = oracle_feature_dim(cfg);
+  if (cfg->memory == ORC_LINEAR) { rows[0] = cfg->d_v; cols[0] = D; return 1; }
+  rows[0] = cfg->hidden; cols[0] = D;
+  rows[1] = cfg->d_v; cols[1] = cfg->hidden;
+  if (!cfg->gated) return 2;
+  rows[2] = cfg->hidden; cols[2] = D;
+  return 3;
+}
+
 static int config_ok(const oracle_config* c) {
   if (c->n_seq < 0 || c->seq_len < 0 || c->d_k <= 0 || c->d_v <= 0) return 0;
   if (c->window < 1 || c->chunk < 1) return 0;
@@ -294,6 +353,8 @@ static int config_ok(const oracle_config* c) {
   if (!(c->sign_alpha >= 0.0 && c->sign_alpha < 1e30)) return 0;
   if (c->layernorm && (c->memory != ORC_MLP || !(c->ln_eps > 0.0 && c->ln_eps < 1.0))) return 0;
   if (c->gated && c->memory != ORC_MLP) return 0;
+  if (c->optimizer != ORC_OPT_GD && c->optimizer != ORC_OPT_MUON) return 0;
+  if (c->optimizer == ORC_OPT_MUON && c->ns_steps < 1) return 0;
   if (c->bias == ORC_BIAS_LP) return c->bias_p >= 1.0 && c->bias_p < 1e6;
   return c->bias == ORC_BIAS_L2 || c->bias == ORC_BIAS_DOT || c->bias == ORC_BIAS_HUBER;
 }
@@ -323,6 +384,7 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
   double* A = (double*)malloc(sizeof(double) * win * h);
   double* xq = (double*)malloc(sizeof(double) * D);
   double* Sloc = (double*)calloc(P, sizeof(double));
+  double* O = cfg->optimizer == ORC_OPT_MUON ? (double*)malloc(sizeof(double) * P) : NULL;
 
   for (int t0 = 0; t0 < N; t0 += b) {
     const int te = (t0 + b < N ? t0 + b : N) - 1;
@@ -356,9 +418,21 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
       }
       const double eta_n = cfg->momentum ? et[n] : 0.0;
       double* Sx = cfg->momentum ? S : Sloc;
-      for (long p = 0; p < P; ++p) {
-        Sx[p] = eta_n * Sx[p] - th[n] * g[p];
-        W[p] = (1.0 - al[n]) * W[p] + Sx[p];
+      if (cfg->optimizer == ORC_OPT_MUON) {
+        for (long p = 0; p < P; ++p) Sx[p] = eta_n * Sx[p] + g[p];
+        int rows[3], cols[3];
+        const int nm = weight_matrices(cfg, rows, cols);
+        long off = 0;
+        for (int m = 0; m < nm; ++m) {
+          oracle_newton_schulz(Sx + off, rows[m], cols[m], cfg->ns_steps, O + off);
+          off += (long)rows[m] * cols[m];
+        }
+        for (long p = 0; p < P; ++p) W[p] = (1.0 - al[n]) * W[p] - th[n] * O[p];
+      } else {
+        for (long p = 0; p < P; ++p) {
+          Sx[p] = eta_n * Sx[p] - th[n] * g[p];
+          W[p] = (1.0 - al[n]) * W[p] + Sx[p];
+        }
       }
       oracle_phi(cfg, q + (long)n * dk, xq);
       apply(cfg, W, xq, q + (long)n * dk, out + (long)n * dv, NULL);
@@ -393,7 +467,7 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
   }
   *count += N;
 
-  free(Wc); free(g); free(X); free(D1); free(D2); free(A); free(xq); free(Sloc);
+  free(Wc); free(g); free(X); free(D1); free(D2); free(A); free(xq); free(Sloc); free(O);
 }
 
 int oracle_forward_ex(const oracle_config* cfg,

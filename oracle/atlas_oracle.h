@@ -24,6 +24,19 @@
  *     after token t's update (Titans review, section 3.1 "Retrieving a
  *     Memory").
  *
+ * Memory optimizer Muon (ATLAS review, section 5 "Memory Optimization": Muon
+ * takes the place of plain gradient descent on the memory).  Read as the
+ * published Muon optimizer (K. Jordan et al., 2024, "Muon: An optimizer for
+ * hidden layers in neural networks"), with the memory's gates in its roles:
+ * momentum of the raw window gradients S_t = eta_t S_{t-1} + grad, each
+ * weight matrix's S_t orthogonalised by the quintic Newton-Schulz iteration
+ * of that optimizer (Frobenius normalisation with eps 1e-7, then ns_steps
+ * steps X <- a X + (b A + c A^2) X, A = X X^T, on the orientation with fewer
+ * rows; a, b, c = 3.4445, -4.7750, 2.0315), and the step
+ * M_t = (1 - alpha_t) M_{t-1} - theta_t NS(S_t).  The learning rate theta
+ * scales the orthogonalised step because NS is invariant to the scale of
+ * its input.
+ *
  * Attentional biases besides the squared error (Miras review, "Alternative
  * Attentional Biases"): the l_p loss, and the Huber loss whose threshold
  * delta_t is an input per token and which picks, per token, the squared
@@ -45,6 +58,7 @@ extern "C" {
 enum { ORC_LINEAR = 0, ORC_MLP = 1 };
 enum { ORC_PHI_ID = 0, ORC_PHI_POLY2 = 1, ORC_PHI_RAW_POLY2 = 2 };
 enum { ORC_BIAS_L2 = 0, ORC_BIAS_DOT = 1, ORC_BIAS_LP = 2, ORC_BIAS_HUBER = 3 };
+enum { ORC_OPT_GD = 0, ORC_OPT_MUON = 1 };
 
 typedef struct {
   int n_seq;        /* independent sequences (batch * heads)                 */
@@ -77,6 +91,10 @@ typedef struct {
   int gated;        /* MLP only: the gated memory of three matrices,
                        f(x) = [r +] W2 (gelu(W1 x) .* (W3 x)) (ATLAS summary,
                        Atlas++); weights W1 [h][D], W2 [d_v][h], W3 [h][D]    */
+  int optimizer;    /* ORC_OPT_GD: S = eta S - theta g, M = (1-alpha) M + S;
+                       ORC_OPT_MUON: S = eta S + g, M = (1-alpha) M - theta NS(S),
+                       NS per weight matrix                                    */
+  int ns_steps;     /* Muon: Newton-Schulz steps (>= 1)                       */
 } oracle_config;
 
 /* Sets the OpenMP thread count used by oracle_forward (n <= 0: default). */
@@ -136,6 +154,10 @@ int oracle_forward_ex(const oracle_config* cfg,
                       double* mem, double* mom,
                       double* halo_k, double* halo_v, double* halo_g, double* halo_d,
                       int64_t* count, double* out);
+
+/* Muon's Newton-Schulz orthogonalisation of one rows x cols matrix G
+ * (row-major) into out; steps >= 0 (0: the normalised input). */
+void oracle_newton_schulz(const double* G, int rows, int cols, int steps, double* out);
 
 #ifdef __cplusplus
 }

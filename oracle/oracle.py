@@ -23,6 +23,7 @@ LIB_PATH = os.environ.get("ATLAS_ORACLE_LIB") or os.path.join(HERE, "liboracle.s
 LINEAR, MLP = 0, 1
 PHI = {"identity": 0, "poly2": 1, "raw_poly2": 2}
 BIAS = {"l2": 0, "dot": 1, "lp": 2, "huber": 3}
+OPTIMIZER = {"gd": 0, "muon": 1}
 
 
 def build(src: str = SRC, out: str | None = None) -> str:
@@ -54,6 +55,8 @@ class OracleConfig(ctypes.Structure):
         ("layernorm", ctypes.c_int),
         ("ln_eps", ctypes.c_double),
         ("gated", ctypes.c_int),
+        ("optimizer", ctypes.c_int),
+        ("ns_steps", ctypes.c_int),
     ]
 
 
@@ -81,6 +84,7 @@ def lib():
         L.oracle_forward.restype = ctypes.c_int
         L.oracle_forward_ex.argtypes = [cp] + [dp] * 8 + [dp] * 6 + [ctypes.POINTER(ctypes.c_int64), dp]
         L.oracle_forward_ex.restype = ctypes.c_int
+        L.oracle_newton_schulz.argtypes = [dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp]
         _lib = L
     return _lib
 
@@ -88,14 +92,15 @@ def lib():
 def make_config(*, n_seq=1, seq_len=0, d_k, d_v, memory="linear", hidden=0, residual=False,
                 feature_map="identity", poly_dims=0, window=1, chunk=1, momentum=False,
                 bias="l2", grad_scale=1.0, bias_p=2.0, sign_alpha=0.0, layernorm=False,
-                ln_eps=1e-5, gated=False) -> OracleConfig:
+                ln_eps=1e-5, gated=False, optimizer="gd", ns_steps=5) -> OracleConfig:
     return OracleConfig(
         n_seq=n_seq, seq_len=seq_len, d_k=d_k, d_v=d_v,
         memory=MLP if memory == "mlp" else LINEAR, hidden=hidden, residual=int(bool(residual)),
         feature_map=PHI[feature_map], poly_dims=poly_dims, window=window, chunk=chunk,
         momentum=int(bool(momentum)), bias=BIAS[bias], grad_scale=float(grad_scale),
         bias_p=float(bias_p), sign_alpha=float(sign_alpha), layernorm=int(bool(layernorm)),
-        ln_eps=float(ln_eps), gated=int(bool(gated)))
+        ln_eps=float(ln_eps), gated=int(bool(gated)), optimizer=OPTIMIZER[optimizer],
+        ns_steps=int(ns_steps))
 
 
 def _p(a: np.ndarray):
@@ -115,6 +120,14 @@ def phi(cfg: OracleConfig, x) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float64)
     out = np.zeros(feature_dim(cfg))
     lib().oracle_phi(ctypes.byref(cfg), _p(x), _p(out))
+    return out
+
+
+def newton_schulz(G, steps: int = 5) -> np.ndarray:
+    """Muon's orthogonalisation of one matrix (atlas_oracle.c)."""
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    out = np.zeros_like(G)
+    lib().oracle_newton_schulz(_p(G), G.shape[0], G.shape[1], int(steps), _p(out))
     return out
 
 
@@ -188,7 +201,8 @@ def config_for(wl) -> OracleConfig:
                        window=wl.window, chunk=wl.chunk, momentum=wl.momentum, bias=wl.bias,
                        grad_scale=wl.grad_scale, bias_p=getattr(wl, "bias_p", 2.0),
                        sign_alpha=getattr(wl, "sign_alpha", 0.0), layernorm=getattr(wl, "layernorm", False),
-                       ln_eps=getattr(wl, "ln_eps", 1e-5), gated=getattr(wl, "gated", False))
+                       ln_eps=getattr(wl, "ln_eps", 1e-5), gated=getattr(wl, "gated", False),
+                       optimizer=getattr(wl, "optimizer", "gd"), ns_steps=getattr(wl, "ns_steps", 5))
 
 
 def run_workload(wl, inputs: dict, weights0, seqs=None, n_tokens=None, state=None, threads=None):

@@ -38,6 +38,8 @@ class Workload:
     layernorm: bool = False  # MLP: f = r + LN(W2 gelu(W1 x))
     ln_eps: float = 1e-5
     gated: bool = False    # MLP: f = r + W2 (gelu(W1 x) .* (W3 x))
+    optimizer: str = "gd"  # "gd": momentum + decay; "muon": Newton-Schulz on the momentum
+    ns_steps: int = 5      # Muon: Newton-Schulz steps
     alpha_u: tuple | None = (-4.0, 0.0)
     theta_u: tuple | None = (-4.0, 0.0)
     eta_u: tuple | None = (0.0, 3.0)

@@ -45,6 +45,14 @@ MUTANTS = {
     "gated_z3_dropped_in_d1": ("d1[j] = back * gelu_prime(z[j]) * (gt ? z[h + j] : 1.0);", "d1[j] = back * gelu_prime(z[j]);"),
     "gated_d3_with_gelu_prime": ("if (gt) d1[h + j] = back * gelu(z[j]);", "if (gt) d1[h + j] = back * gelu_prime(z[j]);"),
     "gated_w3_block_misplaced": ("double* gW3 = gW2 + (long)dv * h;", "double* gW3 = g;"),
+    "muon_ns_coefficient": ("const double a = 3.4445, b = -4.7750, c = 2.0315;", "const double a = 3.4445, b = -4.7750, c = 2.0;"),
+    "muon_frobenius_norm_dropped": ("nrm = sqrt(nrm) + 1e-7;", "nrm = 1.0;"),
+    "muon_steps_off_by_one": ("for (int s = 0; s < steps; ++s) {", "for (int s = 0; s <= steps; ++s) {"),
+    "muon_theta_inside_momentum": ("Sx[p] = eta_n * Sx[p] + g[p];", "Sx[p] = eta_n * Sx[p] + th[n] * g[p];"),
+    "muon_momentum_sign": ("Sx[p] = eta_n * Sx[p] + g[p];", "Sx[p] = eta_n * Sx[p] - g[p];"),
+    "muon_decay_on_step": ("W[p] = (1.0 - al[n]) * W[p] - th[n] * O[p];", "W[p] = (1.0 - al[n]) * (W[p] - th[n] * O[p]);"),
+    "muon_one_matrix_for_the_mlp": ("const int nm = weight_matrices(cfg, rows, cols);",
+                                    "int nm = weight_matrices(cfg, rows, cols); nm = 1; rows[0] = 1; cols[0] = (int)P;"),
     "ln_residual_dropped": ("y[o] += cfg->residual ? r[o] : 0.0;", "y[o] += cfg->residual && !cfg->layernorm ? r[o] : 0.0;"),
 }
 

@@ -659,3 +659,138 @@ def test_gated_retrieval_is_the_plain_forward_and_w3_zero_blocks_w1():
     th0[h * d + d * h:] = 0.0
     g = O.token_grad(cfg, th0, k[0], k[0], v[0], 1.0)
     assert not g[:h * d + d * h].any() and g[h * d + d * h:].any()
+
+
+# --------------------------------------------------------------------------- Muon
+# ATLAS review, sec. 5 "Memory Optimization": Muon replaces gradient descent
+# on the memory.  The oracle follows the published Muon optimizer (quintic
+# Newton-Schulz, a, b, c = 3.4445, -4.7750, 2.0315, Frobenius normalisation).
+NS_ABC = (3.4445, -4.7750, 2.0315)
+
+
+def ns_by_svd(G, steps=5):
+    """Newton-Schulz acts on the singular values alone: U f^steps(s/|G|_F) V^T
+    with the scalar quintic f(x) = a x + b x^3 + c x^5."""
+    U, s, Vt = np.linalg.svd(G, full_matrices=False)
+    x = s / (np.linalg.norm(G) + 1e-7)
+    a, b, c = NS_ABC
+    for _ in range(steps):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return (U * x) @ Vt
+
+
+@pytest.mark.parametrize("shape", [(4, 9), (9, 4), (6, 6), (1, 5), (32, 560)])
+@pytest.mark.parametrize("steps", [1, 5])
+def test_newton_schulz_is_the_singular_value_map(shape, steps):
+    rng = np.random.default_rng(101)
+    G = rng.standard_normal(shape) * 3.0
+    np.testing.assert_allclose(O.newton_schulz(G, steps), ns_by_svd(G, steps), rtol=0, atol=1e-12)
+
+
+def test_newton_schulz_of_a_rank_one_matrix():
+    """u w^T has one singular value |u||w|, so NS gives f^5(1 - tiny) u^ w^^T."""
+    rng = np.random.default_rng(102)
+    u, w = rng.standard_normal(7), rng.standard_normal(11)
+    G = np.outer(u, w)
+    x = np.linalg.norm(G) / (np.linalg.norm(G) + 1e-7)
+    a, b, c = NS_ABC
+    for _ in range(5):
+        x = a * x + b * x ** 3 + c * x ** 5
+    want = x * np.outer(u / np.linalg.norm(u), w / np.linalg.norm(w))
+    np.testing.assert_allclose(O.newton_schulz(G, 5), want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("b", [1, 4])
+@pytest.mark.parametrize("bias", ["l2", "dot"])
+def test_muon_without_momentum_is_a_normalised_delta_rule(b, bias):
+    """Linear memory, c = 1, no momentum: each token's gradient is the rank-one
+    (M0 k - v) k^T (l2; -v k^T for the dot bias) at the chunk-start memory M0,
+    so Muon moves M by -theta f^5(~1) e^ k^^T."""
+    rng = np.random.default_rng(103)
+    N, dk, dv = 23, 6, 4
+    cfg = O.make_config(d_k=dk, d_v=dv, window=1, chunk=b, bias=bias, optimizer="muon")
+    q, k, v = rand_unit(rng, N, dk), rng.standard_normal((N, dk)) * 0.7, rng.standard_normal((N, dv))
+    alpha, theta, gamma = rng.uniform(0, 0.2, N), rng.uniform(0.05, 0.3, N), rng.uniform(0.5, 1.5, N)
+    M = rng.standard_normal((dv, dk)) * 0.3
+    out, st = run(cfg, q, k, v, alpha, np.zeros(N), theta, gamma, M)
+    a_, b_, c_ = NS_ABC
+    for t0 in range(0, N, b):
+        M0 = M.copy()
+        for t in range(t0, min(N, t0 + b)):
+            e = (M0 @ k[t] - v[t]) if bias == "l2" else -v[t]
+            g = gamma[t] * np.outer(e, k[t])
+            x = np.linalg.norm(g) / (np.linalg.norm(g) + 1e-7)
+            for _ in range(5):
+                x = a_ * x + b_ * x ** 3 + c_ * x ** 5
+            M = (1 - alpha[t]) * M - theta[t] * x * np.outer(e / np.linalg.norm(e), k[t] / np.linalg.norm(k[t]))
+            np.testing.assert_allclose(out[t], M @ q[t], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(st["mem"][0].reshape(dv, dk), M, rtol=1e-11, atol=1e-13)
+
+
+def test_muon_scalar_memory():
+    """A 1x1 memory with momentum, window c = 2 and chunk b = 3: NS of a
+    scalar s is f^5(|s| / (|s| + 1e-7)) sign(s)."""
+    rng = np.random.default_rng(104)
+    N, c, b = 31, 2, 3
+    q, k, v = rng.standard_normal((N, 1)), rng.standard_normal((N, 1)), rng.standard_normal((N, 1))
+    al, et, th, ga = rng.uniform(0, 0.3, N), rng.uniform(0.2, 0.9, N), rng.uniform(0.05, 0.4, N), rng.uniform(0.3, 1.2, N)
+    cfg = O.make_config(d_k=1, d_v=1, window=c, chunk=b, momentum=True, optimizer="muon")
+    a_, b_, c_ = NS_ABC
+
+    def ns(s):
+        x = abs(s) / (abs(s) + 1e-7)
+        for _ in range(5):
+            x = a_ * x + b_ * x ** 3 + c_ * x ** 5
+        return x * np.sign(s)
+
+    m, S, want = 0.5, 0.0, []
+    for t0 in range(0, N, b):
+        m0 = m
+        for t in range(t0, min(N, t0 + b)):
+            g = sum(ga[i] * (m0 * k[i, 0] - v[i, 0]) * k[i, 0] for i in range(max(0, t - c + 1), t + 1))
+            S = et[t] * S + g
+            m = (1 - al[t]) * m - th[t] * ns(S)
+            want.append(m * q[t, 0])
+    out, st = run(cfg, q, k, v, al, et, th, ga, [0.5])
+    np.testing.assert_allclose(out[:, 0], want, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(st["mom"][0, 0], S, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("memory", ["linear", "mlp"])
+def test_muon_orthogonalises_each_weight_matrix(memory):
+    """Window c = 2, chunk b = 3, momentum: the replay keeps S per weight
+    matrix, takes each matrix's NS through its SVD, and uses the oracle's
+    token gradient (itself pinned against finite differences)."""
+    rng = np.random.default_rng(105)
+    N, dk, dv, h, c, b = 17, 4, 4, 5, 2, 3
+    kw = dict(memory="mlp", hidden=h, residual=True) if memory == "mlp" else {}
+    cfg = O.make_config(d_k=dk, d_v=dv, window=c, chunk=b, momentum=True, optimizer="muon", **kw)
+    P = O.param_count(cfg)
+    q, k, v = rand_unit(rng, N, dk), rand_unit(rng, N, dk), rng.standard_normal((N, dv))
+    al, et, th, ga = rng.uniform(0, 0.2, N), rng.uniform(0.3, 0.9, N), rng.uniform(0.05, 0.3, N), rng.uniform(0.5, 1.5, N)
+    W = rng.standard_normal(P) * 0.4
+    out, st = run(cfg, q, k, v, al, et, th, ga, W)
+    shapes = [(dv, dk)] if memory == "linear" else [(h, dk), (dv, h)]
+    S = np.zeros(P)
+    for t0 in range(0, N, b):
+        W0 = W.copy()
+        for t in range(t0, min(N, t0 + b)):
+            g = sum(O.token_grad(cfg, W0, k[i], k[i], v[i], ga[i]) for i in range(max(0, t - c + 1), t + 1))
+            S = et[t] * S + g
+            O_, off = np.zeros(P), 0
+            for r_, c_ in shapes:
+                O_[off:off + r_ * c_] = ns_by_svd(S[off:off + r_ * c_].reshape(r_, c_)).ravel()
+                off += r_ * c_
+            W = (1 - al[t]) * W - th[t] * O_
+            np.testing.assert_allclose(out[t], O.memory_apply(cfg, W, q[t], q[t]), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(st["mem"][0], W, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(st["mom"][0], S, rtol=1e-10, atol=1e-12)
+
+
+def test_muon_config_checks():
+    cfg = O.make_config(d_k=2, d_v=2, optimizer="muon", ns_steps=0)
+    cfg.n_seq, cfg.seq_len = 1, 0
+    st = O.empty_state(cfg)
+    z = np.zeros((1, 0))
+    with pytest.raises(Exception):
+        O.forward(cfg, np.zeros((1, 0, 2)), np.zeros((1, 0, 2)), np.zeros((1, 0, 2)), z, z, z, z, st)
