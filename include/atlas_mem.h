@@ -36,6 +36,18 @@
  *   y_t   = f_{M_t}(phi(q_t))                 (Titans review sec. 3.1
  *                         "Retrieving a Memory": a forward pass, no update)
  *
+ * With the Muon memory optimizer (ATLAS review sec. 5 "Memory Optimization":
+ * Muon in place of plain gradient descent on the memory; per-sequence family,
+ * plain linear or 2-layer MLP memory) the two middle lines become
+ *   S_t   = eta_t S_{t-1} + grad_t
+ *   M_t   = (1 - alpha_t) M_{t-1} - theta_t NS(S_t)
+ * per weight matrix, NS the quintic Newton-Schulz orthogonalisation of the
+ * published Muon optimizer (K. Jordan et al., 2024): X = S / (|S|_F + 1e-7)
+ * on the orientation with fewer rows, then ns_steps times
+ * X <- a X + (b A + c A A) X, A = X X^T, (a, b, c) = (3.4445, -4.7750, 2.0315).
+ * The gradients keep the chunked semantics (taken at the chunk-start weights);
+ * NS runs for every token, in fp32.
+ *
  * where grad_t = sum_{i = t-c+1}^{t} grad of token i's term.  The window
  * stops at the first token the sequence has seen.
  *
@@ -66,6 +78,7 @@ enum { ATLAS_MEM_LINEAR = 0, ATLAS_MEM_MLP = 1 };
 enum { ATLAS_PHI_IDENTITY = 0, ATLAS_PHI_POLY2 = 1, ATLAS_PHI_RAW_POLY2 = 2 };
 enum { ATLAS_BIAS_L2 = 0, ATLAS_BIAS_DOT = 1, ATLAS_BIAS_LP = 2, ATLAS_BIAS_HUBER = 3 };
 enum { ATLAS_BF16 = 0, ATLAS_F32 = 1 };
+enum { ATLAS_OPT_GD = 0, ATLAS_OPT_MUON = 1 };
 /* Kernel family.  PER_SEQUENCE: one workgroup per sequence, every operand
  * image kept in a global workspace (all memories and feature maps).
  * SHARDED: the hidden units of each sequence split over several workgroups
@@ -107,6 +120,11 @@ typedef struct {
   int mlp_gated;      /* MLP only, 1: gated memory of three matrices (weights
                          W1 [h][D], W2 [d_v][h], W3 [h][D]); per-sequence
                          family only                                          */
+  int optimizer;      /* ATLAS_OPT_GD (momentum + decay, above) or
+                         ATLAS_OPT_MUON (per-sequence family; no layer norm,
+                         no gated memory; the momentum slot of the state holds
+                         S_t = eta S + grad when momentum is on)              */
+  int ns_steps;       /* Muon: Newton-Schulz steps, 1..64 (ignored for GD)   */
 } atlas_mem_config;
 
 typedef struct atlas_mem_s* atlas_mem_t;

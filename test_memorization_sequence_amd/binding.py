@@ -27,6 +27,7 @@ PHI = {"identity": 0, "poly2": 1, "raw_poly2": 2}
 BIAS = {"l2": 0, "dot": 1, "lp": 2, "huber": 3}
 IO = {"bf16": 0, "f32": 1}
 KERNEL = {"auto": 0, "per_sequence": 1, "sharded": 2, "streamed": 3}
+OPTIMIZER = {"gd": 0, "muon": 1}
 TORCH_IO = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
@@ -36,7 +37,7 @@ class AtlasMemConfig(ctypes.Structure):
         "mlp_residual", "feature_map", "poly_dims", "window", "chunk", "momentum", "bias",
         "io_dtype")] + [("grad_scale", ctypes.c_float), ("kernel", ctypes.c_int), ("bias_p", ctypes.c_float),
                        ("sign_alpha", ctypes.c_float), ("mlp_layernorm", ctypes.c_int), ("ln_eps", ctypes.c_float),
-                       ("mlp_gated", ctypes.c_int)]
+                       ("mlp_gated", ctypes.c_int), ("optimizer", ctypes.c_int), ("ns_steps", ctypes.c_int)]
 
 
 class StateLayout(ctypes.Structure):
@@ -124,7 +125,8 @@ def config_of(wl: Workload, kernel: str = "auto") -> AtlasMemConfig:
         window=wl.window, chunk=wl.chunk, momentum=int(wl.momentum), bias=BIAS[wl.bias],
         io_dtype=IO[wl.io_dtype], grad_scale=wl.grad_scale, bias_p=getattr(wl, "bias_p", 2.0),
         sign_alpha=getattr(wl, "sign_alpha", 0.0), mlp_layernorm=int(getattr(wl, "layernorm", False)),
-        ln_eps=getattr(wl, "ln_eps", 1e-5), mlp_gated=int(getattr(wl, "gated", False)))
+        ln_eps=getattr(wl, "ln_eps", 1e-5), mlp_gated=int(getattr(wl, "gated", False)),
+        optimizer=OPTIMIZER[getattr(wl, "optimizer", "gd")], ns_steps=getattr(wl, "ns_steps", 5))
 
 
 def supported(cfg: AtlasMemConfig) -> int:

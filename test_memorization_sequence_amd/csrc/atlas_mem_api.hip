@@ -78,6 +78,8 @@ struct atlas_mem_s {
   char* ws;
   float* coef;
   hipEvent_t ev_before, ev_after;
+  char* mws;           // Muon: per-sequence workspace inside ws (else null)
+  size_t mws_stride;
 };
 
 static const uint32_t kMagic = 0xA7A5AE11u;
@@ -149,6 +151,9 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
     return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->io_dtype != ATLAS_BF16 && c->io_dtype != ATLAS_F32) return ATLAS_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(c->grad_scale)) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->optimizer != ATLAS_OPT_GD && c->optimizer != ATLAS_OPT_MUON) return ATLAS_ERR_INVALID_ARGUMENT;
+  const bool muon = c->optimizer == ATLAS_OPT_MUON;
+  if (muon && (c->ns_steps < 1 || c->ns_steps > 64)) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->feature_map == ATLAS_PHI_RAW_POLY2 && (c->poly_dims < 1 || c->poly_dims > c->d_k)) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->memory == ATLAS_MEM_MLP) {
     if (c->mlp_hidden < 1) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -163,8 +168,11 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   if (out) *out = nullptr;
   if (sout) *sout = nullptr;
   if (tout) *tout = nullptr;
+  // Muon: the per-sequence family, plain linear or MLP memory
+  if (muon && (c->mlp_layernorm || c->mlp_gated || (c->kernel != ATLAS_KERNEL_AUTO && c->kernel != ATLAS_KERNEL_PER_SEQUENCE)))
+    return ATLAS_ERR_UNSUPPORTED;
   const StreamVariant* tv = nullptr;
-  if (c->kernel == ATLAS_KERNEL_STREAMED || c->kernel == ATLAS_KERNEL_AUTO) {
+  if (!muon && (c->kernel == ATLAS_KERNEL_STREAMED || c->kernel == ATLAS_KERNEL_AUTO)) {
     tv = find_streamed(c);
     if (tv && (c->kernel == ATLAS_KERNEL_STREAMED || tv->autopick)) {
       if (tout) *tout = tv;
@@ -172,7 +180,7 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
     }
     if (c->kernel == ATLAS_KERNEL_STREAMED) return ATLAS_ERR_UNSUPPORTED;
   }
-  if (c->kernel != ATLAS_KERNEL_PER_SEQUENCE) {
+  if (!muon && c->kernel != ATLAS_KERNEL_PER_SEQUENCE) {
     const ShardedVariant* sv = find_sharded(c);
     if (sv) {
       if (sout) *sout = sv;
@@ -257,9 +265,13 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   const bool grouped = svar || tvar;   // streamed: tile-major state copy (+ exchange for G = 2)
   const size_t xbytes = svar ? svar->xbytes() : tvar ? tvar->xbytes() : 0;
   const size_t ctrl_off = align_up(xbytes * (size_t)h->n_seq, 256);
-  const size_t ws_bytes = var       ? var->ws_bytes * (size_t)h->n_seq
+  const bool muon = cfg->optimizer == ATLAS_OPT_MUON;
+  h->mws_stride = muon ? muon_ws_of(cfg->memory == ATLAS_MEM_MLP, h->lay.feature_dim, cfg->d_v, cfg->mlp_hidden).bytes : 0;
+  const size_t mws_off = var ? align_up(var->ws_bytes * (size_t)h->n_seq, 256) : 0;
+  const size_t ws_bytes = var       ? mws_off + h->mws_stride * (size_t)h->n_seq
                           : grouped ? ctrl_off + align_up((1 + (size_t)h->n_seq) * 4, 256)
                                     : 0;
+  h->mws = nullptr;
   const size_t coef_bytes = (size_t)h->n_seq * h->nchunks * h->coef_stride * sizeof(float);
   if (ws_bytes && hipMalloc(&h->ws, ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -272,6 +284,7 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
     delete h;
     return ATLAS_ERR_OUT_OF_MEMORY;
   }
+  if (muon) h->mws = h->ws + mws_off;
   if (grouped) {
     h->ctrl = reinterpret_cast<unsigned*>(h->ws + ctrl_off);
     if ((e = hipMemset(h->ctrl, 0, (1 + (size_t)h->n_seq) * 4)) != hipSuccess) {
@@ -427,6 +440,13 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, c
   cp.delta = delta;
   cp.off_halo_d = h->lay.halo_d;
   cp.residual = c.memory == ATLAS_MEM_MLP ? c.mlp_residual : 0;
+  cp.alpha = alpha;
+  cp.eta = c.momentum ? eta : nullptr;
+  cp.theta = theta;
+  cp.muon = c.optimizer == ATLAS_OPT_MUON;
+  cp.ns_steps = c.ns_steps;
+  cp.mws = h->mws;
+  cp.mws_stride = h->mws_stride;
   e = h->var->launch(cp, kp, h->n_seq, (hipStream_t)stream, h->ev_before, h->ev_after);
   if (e != hipSuccess) return hip_fail(e);
   return ATLAS_OK;

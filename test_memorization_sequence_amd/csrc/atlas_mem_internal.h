@@ -70,6 +70,36 @@ struct WsLayout {
   static constexpr size_t bytes = align_up(D3TS + (MLP ? H * WP : 0) * e, 256);
 };
 
+// Muon (per-sequence kernel): Newton-Schulz runs on the orientation of a
+// rows x cols weight matrix with fewer rows, r x n (r <= n), both padded to
+// multiples of 32 with zeros, which the iteration keeps zero.
+constexpr long ns_r(long rows, long cols) { return ((rows > cols ? cols : rows) + 31) / 32 * 32; }
+constexpr long ns_n(long rows, long cols) { return ((rows > cols ? rows : cols) + 31) / 32 * 32; }
+constexpr long lmax(long a, long b) { return a > b ? a : b; }
+
+// Per-sequence Muon workspace (fp32, byte offsets): the momentum of a call
+// without momentum in the state (P floats), two ping-pong iterates X and
+// their transposes (r x n each, the largest matrix of the memory), and the
+// r x r products A = X X^T and B = b A + c A A.
+struct MuonWs {
+  size_t sloc, x0, x1, xt0, xt1, am, bm, bytes;
+};
+constexpr MuonWs muon_ws(long P, long rn, long rr) {
+  const size_t x0 = align_up((size_t)P * 4, 256);
+  const size_t x1 = align_up(x0 + (size_t)rn * 4, 256);
+  const size_t xt0 = align_up(x1 + (size_t)rn * 4, 256);
+  const size_t xt1 = align_up(xt0 + (size_t)rn * 4, 256);
+  const size_t am = align_up(xt1 + (size_t)rn * 4, 256);
+  const size_t bm = align_up(am + (size_t)rr * 4, 256);
+  return MuonWs{0, x0, x1, xt0, xt1, am, bm, align_up(bm + (size_t)rr * 4, 256)};
+}
+// linear memory: M [dv][D]; MLP: W1 [h][D], W2 [dv][h]
+constexpr MuonWs muon_ws_of(bool mlp, long D, long dv, long h) {
+  return mlp ? muon_ws(h * D + dv * h, lmax(ns_r(h, D) * ns_n(h, D), ns_r(dv, h) * ns_n(dv, h)),
+                       lmax(ns_r(h, D) * ns_r(h, D), ns_r(dv, h) * ns_r(dv, h)))
+             : muon_ws(dv * D, ns_r(dv, D) * ns_n(dv, D), ns_r(dv, D) * ns_r(dv, D));
+}
+
 // T: MFMA operand type (bf16 or float); TI: io type of q, k, v, out.
 // H = 0 for a linear memory.  WP: window rows (chunk + c - 1) padded to 32.
 // PD: degree-2 map width (== DK for PHI_POLY2).
@@ -135,6 +165,14 @@ struct ChunkParams {
   int layernorm;   // MLP: f = r + LN(W2 gelu(W1 x)), no gain or shift
   float ln_eps;
   int gated;       // MLP: f = r + W2 (gelu(W1 x) .* (W3 x)) (per-sequence kernel)
+  // Muon: raw gates per token, Newton-Schulz steps, workspace (MuonWs per
+  // sequence, mws_stride bytes apart); muon == 0 for gradient descent
+  const float* alpha;
+  const float* eta;
+  const float* theta;
+  int muon, ns_steps;
+  char* mws;
+  size_t mws_stride;
 };
 
 struct ShardedParams {

@@ -169,6 +169,12 @@ __device__ __forceinline__ float phi_feature(const TI* row, int f, const PairTab
   return 0.f;
 }
 
+}  // namespace atlas
+
+#include "atlas_mem_muon.h"
+
+namespace atlas {
+
 // ----------------------------------------------------------------------------- chunk kernel
 template <class S>
 __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
@@ -189,6 +195,9 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   const bool gated = S::MEM == MEM_MLP && p.gated != 0;
   const float ln_eps = p.ln_eps;
   const bool rowwise = shaped || ln;
+  // Muon memory optimizer: per-token Newton-Schulz steps after the window
+  // gradients (atlas_mem_muon.h); no layer norm, no gated memory
+  const bool muon = p.muon != 0;
 
   char* st = p.state + (size_t)seq * p.seq_stride;
   float* Wt = reinterpret_cast<float*>(st + p.off_weights);
@@ -248,7 +257,16 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   __shared__ float dw[WP], rsel[WP];   // Huber: thresholds of the window rows, their choice
   __shared__ float cP;
   __shared__ PairTable<S::PD> pt;
+  __shared__ float mu_red[4];                          // Muon: block sums
+  __shared__ float mu_ah[S::MEM == MEM_MLP ? H : 1];   // Muon: gelu(W1 phi(q_n))
   if (S::PHI != PHI_IDENTITY) pt.fill();
+  char* mws = muon ? p.mws + (size_t)seq * p.mws_stride : nullptr;
+  constexpr long P_W = S::MEM == MEM_MLP ? (long)H * D + (long)DV * H : (long)DV * D;
+  // Muon without momentum in the state: S = g every token (eta = 0) in a
+  // workspace buffer, zeroed so that 0 * S stays 0
+  float* Smu = muon ? (mom ? Mo : reinterpret_cast<float*>(mws)) : nullptr;
+  if (muon && !mom)
+    for (long e = threadIdx.x; e < P_W; e += blockDim.x) Smu[e] = 0.f;
 
   // operand images of the state
   if (S::MEM == MEM_MLP) {
@@ -338,6 +356,59 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
       if (w >= W || i < -halo_valid || i > te) return 0.f;
       return i >= 0 ? to_f(v[(size_t)i * DV + o]) : hv[(c - 1 + i) * DV + o];
     };
+    // Muon: per token, the Newton-Schulz step of every weight matrix, then
+    // y_n = f_{W_n}(phi(q_n)) from the fp32 weights; afterwards the operand
+    // images of the chunk-end weights for the next chunk's gradients
+    auto muon_chunk = [&]() {
+      for (int n = t0; n <= te; ++n) {
+        const size_t gi = (size_t)seq * N + n;
+        const float al = p.alpha[gi], th = p.theta[gi], et = mom ? p.eta[gi] : 0.f;
+        const int w0 = n - t0;
+        const T* xq = Xq + (size_t)(n - t0) * DP;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+        if constexpr (S::MEM == MEM_MLP) {
+          muon_matrix<S, H, D>(Wt, Smu, et, D1T, XwT, w0, c, al, th, p.ns_steps, mws, mu_red);
+          muon_matrix<S, DV, H>(Wt + (size_t)H * D, Smu + (size_t)H * D, et, D2T, AT, w0, c, al, th, p.ns_steps, mws,
+                                mu_red);
+          const float* W1 = Wt;
+          const float* W2 = Wt + (size_t)H * D;
+          for (int j = wave; j < H; j += nwaves) {
+            float acc = 0.f;
+            for (int f = lane; f < D; f += 64) acc += W1[(size_t)j * D + f] * to_f(xq[f]);
+            acc = muon_wave_sum(acc);
+            if (lane == 0) mu_ah[j] = gelu(acc);
+          }
+          __syncthreads();
+          for (int o = wave; o < DV; o += nwaves) {
+            float acc = 0.f;
+            for (int j = lane; j < H; j += 64) acc += W2[(size_t)o * H + j] * mu_ah[j];
+            acc = muon_wave_sum(acc);
+            if (lane == 0) out[(size_t)n * DV + o] = from_f<TI>((res ? to_f(qr[n - t0][o]) : 0.f) + acc);
+          }
+        } else {
+          muon_matrix<S, DV, D>(Wt, Smu, et, D2T, XwT, w0, c, al, th, p.ns_steps, mws, mu_red);
+          for (int o = wave; o < DV; o += nwaves) {
+            float acc = 0.f;
+            for (int f = lane; f < D; f += 64) acc += Wt[(size_t)o * D + f] * to_f(xq[f]);
+            acc = muon_wave_sum(acc);
+            if (lane == 0) out[(size_t)n * DV + o] = from_f<TI>(acc);
+          }
+        }
+        __syncthreads();
+      }
+      if (S::MEM == MEM_MLP) {
+        for (int e = threadIdx.x; e < H * D; e += blockDim.x) W1b[(e / D) * DP + e % D] = from_f<T>(Wt[e]);
+        for (int e = threadIdx.x; e < DV * H; e += blockDim.x) {
+          const float w2 = Wt[(size_t)H * D + e];
+          W2b[e] = from_f<T>(w2);
+          W2T[(e % H) * DV + e / H] = from_f<T>(w2);
+        }
+      } else {
+        for (int e = threadIdx.x; e < DV * D; e += blockDim.x) Mb[(e / D) * DP + e % D] = from_f<T>(Wt[e]);
+      }
+      __syncthreads();
+    };
+
     // D2 element (w, o) in every layout its consumers read
     auto put_d2 = [&](int w, int o, float d2) {
       if (S::MEM == MEM_MLP) D2[w * DV + o] = from_f<T>(d2);
@@ -394,7 +465,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
     };
 
     // Q1 = C .* (Xq X^T)
-    {
+    if (!muon) {
       Op<T> ops[1] = {{Xq, DP, Xw, DP, DP}};
       gemm_nt(BC, WP, ops, [&](int n, int w, const float* a) { Q1[n * WP + w] = from_f<T>(Cc[n * WP + w] * a[0]); });
     }
@@ -443,6 +514,10 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
         });
       }
       __syncthreads();
+      if (muon) {
+        muon_chunk();
+        continue;
+      }
       // Zq = A_t Xq W1^T + B_t Xq S1^T - Q1 D1 ; Ah = gelu(Zq)
       // (gated: .* (A_t Xq W3^T + B_t Xq S3^T - Q1 D3))
       {
@@ -554,6 +629,10 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
         if (shaped) shape_rows();
       }
       __syncthreads();
+      if (muon) {
+        muon_chunk();
+        continue;
+      }
       // y = A_t Xq M^T + B_t Xq S^T - Q1 D
       {
         Op<T> ops[3] = {{Xq, DP, Mb, DP, DP}, {mom ? Xq : nullptr, DP, Sb, DP, DP}, {Q1, WP, D2T, WP, WP}};

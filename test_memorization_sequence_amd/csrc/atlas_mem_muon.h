@@ -1,0 +1,120 @@
+// atlas_mem_muon.h -- the Muon memory optimizer inside the per-sequence chunk
+// kernel (included by atlas_mem_kernels.hip after gemm_nt and the MFMA types).
+//
+// ATLAS review sec. 5 "Memory Optimization": Muon takes the place of plain
+// gradient descent on the memory.  Read as the published Muon optimizer
+// (K. Jordan et al., 2024) with the memory's gates in its roles.  For every
+// token n of a chunk and every weight matrix W of the memory, with the
+// gradients of the window tokens taken at the chunk-start weights exactly as
+// for gradient descent (ATLAS review sec. 3.3):
+//   S <- eta_n S + g_n,    g_n = sum_{i = n-c+1..n} D_i x_i^T
+//   O  = NS(S):  X = S / (|S|_F + 1e-7), on the orientation with fewer rows;
+//                then ns_steps times X <- a X + (b A + c A A) X, A = X X^T,
+//                (a, b, c) = (3.4445, -4.7750, 2.0315)
+//   W <- (1 - alpha_n) W - theta_n O
+// and then y_n = f_W(phi(q_n)) with the token's own weights.
+//
+// O is a nonlinear function of S, so unlike gradient descent the per-token
+// weights are not sums of outer products and the chunk's dual form does not
+// apply: every token materialises S and W (fp32, in the state and an
+// L2-resident workspace) and runs the iteration.  Its three GEMMs per step are
+// fp32 MFMA (16x16x4) through gemm_nt, in fp32 because the iteration
+// amplifies noise along the near-null directions of S (about 3.4x per step),
+// which a low-rank momentum has many of.
+#pragma once
+
+namespace atlas {
+
+__device__ __forceinline__ float muon_wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One token's Muon step on the weight matrix Wm [ROWS][COLS] (fp32, row
+// major) with momentum Sm of the same shape.  The window gradient is
+// sum_{w0 <= w < w0 + cw} Dt[r][w] Xc[col][w]  (Dt [ROWS][WP], Xc [>= COLS][WP]).
+// Every thread of the workgroup calls this; it ends on a barrier.
+template <class S, int ROWS, int COLS, typename T>
+__device__ void muon_matrix(float* Wm, float* Sm, float eta, const T* Dt, const T* Xc, int w0, int cw, float alpha,
+                            float theta, int steps, char* mws, float* red) {
+  constexpr int WP = S::WP;
+  constexpr bool TR = ROWS > COLS;
+  constexpr int R = (int)ns_r(ROWS, COLS), NN = (int)ns_n(ROWS, COLS);
+  constexpr MuonWs L = muon_ws_of(S::MEM == MEM_MLP, S::D, S::DV, S::H);
+  float* X[2] = {reinterpret_cast<float*>(mws + L.x0), reinterpret_cast<float*>(mws + L.x1)};
+  float* Xt[2] = {reinterpret_cast<float*>(mws + L.xt0), reinterpret_cast<float*>(mws + L.xt1)};
+  float* Am = reinterpret_cast<float*>(mws + L.am);
+  float* Bm = reinterpret_cast<float*>(mws + L.bm);
+
+  // S <- eta S + g; |S|_F^2; S into X[0] in the R x NN orientation, zero padded
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < R * NN; e += blockDim.x) {
+    const int i = e / NN, j = e % NN;
+    const int r = TR ? j : i, c = TR ? i : j;
+    float s = 0.f;
+    if (r < ROWS && c < COLS) {
+      float g = 0.f;
+      for (int w = w0; w < w0 + cw; ++w) g += to_f(Dt[r * WP + w]) * to_f(Xc[c * WP + w]);
+      const size_t idx = (size_t)r * COLS + c;
+      s = eta * Sm[idx] + g;
+      Sm[idx] = s;
+      ss += s * s;
+    }
+    X[0][e] = s;
+  }
+  ss = muon_wave_sum(ss);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
+  const float inv = 1.f / (sqrtf(tot) + 1e-7f);
+  for (int e = threadIdx.x; e < R * NN; e += blockDim.x) {
+    const int i = e / NN, j = e % NN;
+    const float x = X[0][e] * inv;
+    X[0][e] = x;
+    Xt[0][j * R + i] = x;
+  }
+  __syncthreads();
+
+  const float ca = 3.4445f, cb = -4.7750f, cc = 2.0315f;
+  int cur = 0;
+  for (int it = 0; it < steps; ++it) {
+    const float* Xc_ = X[cur];
+    float* Xn = X[cur ^ 1];
+    float* Xtn = Xt[cur ^ 1];
+    {  // A = X X^T
+      Op<float> ops[1] = {{Xc_, NN, Xc_, NN, NN}};
+      gemm_nt(R, R, ops, [&](int i, int j, const float* a) { Am[i * R + j] = a[0]; });
+    }
+    __syncthreads();
+    {  // B = b A + c A A  (A symmetric: A A = A A^T)
+      Op<float> ops[1] = {{Am, R, Am, R, R}};
+      gemm_nt(R, R, ops, [&](int i, int j, const float* a) { Bm[i * R + j] = cb * Am[i * R + j] + cc * a[0]; });
+    }
+    __syncthreads();
+    {  // X <- a X + B X, also transposed for the next step's B X
+      Op<float> ops[1] = {{Bm, R, Xt[cur], R, R}};
+      gemm_nt(R, NN, ops, [&](int i, int j, const float* a) {
+        const float y = ca * Xc_[i * NN + j] + a[0];
+        Xn[i * NN + j] = y;
+        Xtn[j * R + i] = y;
+      });
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // W <- (1 - alpha) W - theta O
+  const float* O = X[cur];
+  const float keep = 1.f - alpha;
+  for (int e = threadIdx.x; e < ROWS * COLS; e += blockDim.x) {
+    const int r = e / COLS, c = e % COLS;
+    const float o = TR ? O[c * NN + r] : O[r * NN + c];
+    Wm[e] = keep * Wm[e] - theta * o;
+  }
+  __syncthreads();
+}
+
+}  // namespace atlas

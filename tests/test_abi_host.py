@@ -156,3 +156,24 @@ def test_init_without_a_device_fails_cleanly():
     rc = binding.lib().atlas_mem_init(ctypes.byref(_cfg()), ctypes.byref(h))
     assert rc in (binding.ERR_HIP, binding.ERR_OOM)
     assert not h.value
+
+
+def test_muon_configs():
+    """The Muon optimizer runs on the per-sequence family for the plain linear
+    and MLP memories; layer-norm and gated memories have no Muon kernel."""
+    for name in ORDER:
+        assert binding.supported(binding.config_of(replace(WORKLOADS[name], optimizer="muon"))) == binding.OK, name
+    for kernel in ("auto", "per_sequence"):
+        c = binding.config_of(replace(WORKLOADS["layer_scale"], optimizer="muon"), kernel)
+        assert binding.supported(c) == binding.OK, kernel
+    for kernel in ("sharded", "streamed"):
+        c = binding.config_of(replace(WORKLOADS["layer_scale"], optimizer="muon"), kernel)
+        assert binding.supported(c) == binding.ERR_UNSUPPORTED, kernel
+    for kw, code in [(dict(layernorm=True), binding.ERR_UNSUPPORTED), (dict(gated=True), binding.ERR_UNSUPPORTED),
+                     (dict(ns_steps=0), binding.ERR_INVALID), (dict(ns_steps=65), binding.ERR_INVALID)]:
+        assert binding.supported(_cfg(optimizer="muon", **kw)) == code, kw
+    c = _cfg()
+    c.optimizer = 2
+    assert binding.supported(c) == binding.ERR_INVALID
+    c = _cfg(ns_steps=0)          # ignored by gradient descent
+    assert binding.supported(c) == binding.OK
