@@ -37,15 +37,29 @@ MEASURED_TRAFFIC = {
 }
 
 
-def kernel_source_hash() -> str:
-    """Hash of the device-code sources (the host-side API file excluded)."""
+# translation unit of each recurrent kernel
+KERNEL_SOURCE = {"stream_mlp_kernel": "atlas_mem_stream.hip", "sharded_mlp_kernel": "atlas_mem_sharded.hip",
+                 "chunk_kernel": "atlas_mem_kernels.hip"}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the source file that holds the kernel and of every local header
+    it includes, directly or not."""
     import hashlib
+    import re
+    seen, todo = [], [KERNEL_SOURCE[kernel]]
+    while todo:
+        f = todo.pop(0)
+        if f in seen or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        seen.append(f)
+        with open(os.path.join(CSRC, f)) as fh:
+            todo += re.findall(r'#include "([^"]+)"', fh.read())
     m = hashlib.sha1()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h", ".inc")) and f != "atlas_mem_api.hip":
-            m.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                m.update(fh.read())
+    for f in sorted(seen):
+        m.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            m.update(fh.read())
     return m.hexdigest()[:16]
 
 
@@ -63,6 +77,33 @@ def alg_flops_per_chunk(wl) -> float:
             + 2 * b * W * (D + 2 * h + dv))
 
 
+def weight_matrices(wl):
+    """(rows, cols) of each weight matrix of the memory."""
+    D, dv, h = wl.feature_dim, wl.d_v, wl.hidden
+    return [(dv, D)] if wl.memory == "linear" else [(h, D), (dv, h)]
+
+
+def alg_flops_muon(wl, n_tokens: int) -> float:
+    """FLOPs of one sequence under the Muon optimizer over n_tokens: the
+    window forward and backward at each chunk-start state, and per token the
+    window gradient of every matrix (one rank-one term for c = 1, else the
+    running sum's entering and leaving terms: 2 or 4 rows cols), ns_steps
+    Newton-Schulz steps on the r x n orientation (the symmetric A = X X^T:
+    r r n, the symmetric A A: r^3, B X: 2 r r n), the update and the
+    retrieval (2 P)."""
+    b, W, D, dv, h, c = wl.chunk, wl.chunk + wl.window - 1, wl.feature_dim, wl.d_v, wl.hidden, wl.window
+    nch = -(-n_tokens // b)
+    if wl.memory == "linear":
+        per_chunk = 2 * W * D * dv
+    else:
+        per_chunk = 2 * W * (h * D + dv * h) + 2 * W * dv * h
+    per_token = 0.0
+    for rows, cols in weight_matrices(wl):
+        r, n = min(rows, cols), max(rows, cols)
+        per_token += 2 * min(c, 2) * rows * cols + wl.ns_steps * (3 * r * r * n + r ** 3) + 2 * rows * cols
+    return nch * per_chunk + n_tokens * per_token
+
+
 def alg_bytes_per_head_token(wl) -> int:
     """q, k, v in, out back (io dtype), four fp32 gates."""
     es = 4 if wl.io_dtype == "f32" else 2
@@ -78,6 +119,8 @@ def cpu_baseline(wl, inputs, w0, budget_s: float):
     n_seq = min(S, threads)
     P = wl.hidden * wl.feature_dim + wl.d_v * wl.hidden if wl.memory == "mlp" else wl.d_v * wl.feature_dim
     cost = 2.0 * (wl.window + 8) * P            # flops per head-token, direct window sums
+    if wl.optimizer == "muon":                   # plus the per-token Newton-Schulz steps
+        cost += sum(wl.ns_steps * (4 * min(r, c) ** 2 * max(r, c) + 2 * min(r, c) ** 3) for r, c in weight_matrices(wl))
     n = int(budget_s * 3.0e9 / cost) // wl.chunk * wl.chunk
     n = max(wl.chunk, min(n, wl.seq_len))
     seqs = [int(s) for s in range(0, S, max(1, S // n_seq))][:n_seq]
@@ -172,6 +215,10 @@ def main():
     ap.add_argument("--sign-alpha", type=float, default=0.0, help="l_p / Huber: 0 exact sign, > 0 tanh(alpha e)")
     ap.add_argument("--layernorm", action="store_true", help="MLP memory r + LN(W2 gelu(W1 x))")
     ap.add_argument("--gated", action="store_true", help="MLP memory r + W2 (gelu(W1 x) .* (W3 x))")
+    ap.add_argument("--muon", action="store_true",
+                    help="Muon memory optimizer (per-token Newton-Schulz; per-sequence family)")
+    ap.add_argument("--ns-steps", type=int, default=5, help="Muon: Newton-Schulz steps")
+    ap.add_argument("--seq-len", type=int, default=None, help="override the workload's tokens per sequence")
     ap.add_argument("--prologue", action="store_true",
                     help="time the fused prologue (x -> q, k, v, gates) on the workload's shape instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,6 +257,11 @@ def main():
     if args.layernorm or args.gated:
         from dataclasses import replace
         wl = replace(wl, layernorm=wl.layernorm or args.layernorm, gated=args.gated)
+    if args.muon:
+        from dataclasses import replace
+        wl = replace(wl, optimizer="muon", ns_steps=args.ns_steps)
+    if args.seq_len is not None:
+        wl = wl.with_shape(seq_len=args.seq_len)
     print(f"[bench] {wl.name} bias={wl.bias}: B={wl.batch} H={wl.heads} N={wl.seq_len} ({wl.note})", file=sys.stderr, flush=True)
     inputs = synth.make_inputs(wl, 0)
     w0 = synth.initial_weights_flat(wl, inputs)
@@ -252,13 +304,16 @@ def main():
 
     S = wl.batch * wl.heads
     nch = -(-wl.seq_len // wl.chunk)
-    flops = alg_flops_per_chunk(wl) * nch * S
+    muon = wl.optimizer == "muon"
+    flops = alg_flops_muon(wl, wl.seq_len) * S if muon else alg_flops_per_chunk(wl) * nch * S
     k_ms = float(np.mean(kernel_ms))
     achieved = flops / (k_ms * 1e-3) / 1e12
-    peak = PEAK_FP32_TFLOPS if wl.io_dtype == "f32" else PEAK_BF16_TFLOPS
+    # Muon's Newton-Schulz GEMMs run as fp32 MFMA
+    peak = PEAK_FP32_TFLOPS if wl.io_dtype == "f32" or muon else PEAK_BF16_TFLOPS
     meas = (MEASURED_TRAFFIC.get((wl.name, kernel_name(binding, wl, args.kernel)))
-            if wl.bias == "l2" and not wl.layernorm and not wl.gated else None)
-    traffic = meas["bytes"] if meas and meas["src"] == kernel_source_hash() else None
+            if wl.bias == "l2" and not wl.layernorm and not wl.gated and not muon and wl.seq_len == WORKLOADS[wl.name].seq_len
+            else None)
+    traffic = meas["bytes"] if meas and meas["src"] == kernel_source_hash(kernel_name(binding, wl, args.kernel)) else None
     tokens = wl.batch * wl.seq_len
     res = {
         "metric": "memory update+retrieve tokens/sec (1 GPU); MFMA util % of bf16 peak",
@@ -277,6 +332,7 @@ def main():
                    "d_k": wl.d_k, "d_v": wl.d_v, "memory": wl.memory, "hidden": wl.hidden,
                    "feature_dim": wl.feature_dim, "window": wl.window, "chunk": wl.chunk,
                    "momentum": wl.momentum, "bias": wl.bias, "layernorm": wl.layernorm, "gated": wl.gated,
+                   **({"optimizer": "muon", "ns_steps": wl.ns_steps} if muon else {}),
                    **({"bias_p": wl.bias_p} if wl.bias == "lp" else {}),
                    **({"sign_alpha": wl.sign_alpha} if wl.bias in ("lp", "huber") else {})},
         "head_tokens_per_s": S * wl.seq_len / (ms_per_step * 1e-3),

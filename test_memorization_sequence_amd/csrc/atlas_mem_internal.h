@@ -78,20 +78,22 @@ constexpr long ns_n(long rows, long cols) { return ((rows > cols ? rows : cols) 
 constexpr long lmax(long a, long b) { return a > b ? a : b; }
 
 // Per-sequence Muon workspace (fp32, byte offsets): the momentum of a call
-// without momentum in the state (P floats), two ping-pong iterates X and
-// their transposes (r x n each, the largest matrix of the memory), and the
-// r x r products A = X X^T and B = b A + c A A.
+// without momentum in the state (P floats), the running window gradient
+// (P floats), two ping-pong iterates X and their transposes (r x n each, the
+// largest matrix of the memory), and the r x r products A = X X^T and
+// B = b A + c A A.
 struct MuonWs {
-  size_t sloc, x0, x1, xt0, xt1, am, bm, bytes;
+  size_t sloc, g, x0, x1, xt0, xt1, am, bm, bytes;
 };
 constexpr MuonWs muon_ws(long P, long rn, long rr) {
-  const size_t x0 = align_up((size_t)P * 4, 256);
+  const size_t g = align_up((size_t)P * 4, 256);
+  const size_t x0 = align_up(g + (size_t)P * 4, 256);
   const size_t x1 = align_up(x0 + (size_t)rn * 4, 256);
   const size_t xt0 = align_up(x1 + (size_t)rn * 4, 256);
   const size_t xt1 = align_up(xt0 + (size_t)rn * 4, 256);
   const size_t am = align_up(xt1 + (size_t)rn * 4, 256);
   const size_t bm = align_up(am + (size_t)rr * 4, 256);
-  return MuonWs{0, x0, x1, xt0, xt1, am, bm, align_up(bm + (size_t)rr * 4, 256)};
+  return MuonWs{0, g, x0, x1, xt0, xt1, am, bm, align_up(bm + (size_t)rr * 4, 256)};
 }
 // linear memory: M [dv][D]; MLP: W1 [h][D], W2 [dv][h]
 constexpr MuonWs muon_ws_of(bool mlp, long D, long dv, long h) {

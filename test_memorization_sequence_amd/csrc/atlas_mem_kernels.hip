@@ -74,14 +74,19 @@ template <> struct Mma<bf16> {
   }
 };
 template <> struct Mma<float> {
-  static constexpr int KSTEP = 4;
-  typedef float frag;
-  // lane l: row (l & 15), k = k0 + (l >> 4)
+  static constexpr int KSTEP = 16;
+  typedef f32x4 frag;
+  // lane l: row (l & 15), k = k0 + 4*(l >> 4) .. +3, one 16-byte load.  MFMA
+  // step e contracts k0 + 4g + e over the four lane groups g: a permutation
+  // of the 16 k's, the same for both operands, so the sum is unchanged.
   __device__ static frag load(const float* base, int ld, int row0, int k0, int lane) {
-    return base[(size_t)(row0 + (lane & 15)) * ld + k0 + (lane >> 4)];
+    return *reinterpret_cast<const f32x4*>(base + (size_t)(row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
   }
   __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
   }
 };
 
@@ -93,14 +98,22 @@ template <typename T> struct Op {
 
 // C_o[m][n] = sum_k A_o[m][k] B_o[n][k] for each op o, over a 32x32 tile per
 // wave (2x2 MFMA blocks); epi(m, n, v[NOPS]) receives every element once.
-// M and N must be multiples of 32.
+// M and N must be multiples of 32.  upper (M == N, a symmetric result): only
+// the tiles on and above the diagonal, spread evenly over the waves; the
+// epilogue mirrors them.
 template <typename T, int NOPS, typename Epi>
-__device__ __forceinline__ void gemm_nt(int M, int N, const Op<T> (&ops)[NOPS], Epi&& epi) {
+__device__ __forceinline__ void gemm_nt(int M, int N, const Op<T> (&ops)[NOPS], Epi&& epi, bool upper = false) {
   typedef Mma<T> MM;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  const int tn = N >> 5, ntiles = (M >> 5) * tn;
+  const int tn = N >> 5, ntiles = upper ? tn * (tn + 1) / 2 : (M >> 5) * tn;
   for (int t = wave; t < ntiles; t += nwaves) {
-    const int m0 = (t / tn) << 5, n0 = (t % tn) << 5;
+    int m0 = (t / tn) << 5, n0 = (t % tn) << 5;
+    if (upper) {  // t-th tile of the upper triangle, row by row
+      int mt = 0, rem = t;
+      while (rem >= tn - mt) { rem -= tn - mt; ++mt; }
+      m0 = mt << 5;
+      n0 = (mt + rem) << 5;
+    }
     f32x4 acc[NOPS][2][2];
 #pragma unroll
     for (int o = 0; o < NOPS; ++o)
@@ -257,14 +270,19 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   __shared__ float dw[WP], rsel[WP];   // Huber: thresholds of the window rows, their choice
   __shared__ float cP;
   __shared__ PairTable<S::PD> pt;
-  __shared__ float mu_red[4];                          // Muon: block sums
-  __shared__ float mu_ah[S::MEM == MEM_MLP ? H : 1];   // Muon: gelu(W1 phi(q_n))
+  // Muon: block sums; the factors of the window rows entering and leaving
+  // (2 (rows + cols) floats of the largest matrix), then gelu(W1 phi(q_n))
+  constexpr int MU_STAGE = S::MEM == MEM_MLP ? 2 * ((H > DV ? H : DV) + (D > H ? D : H)) : 2 * (DV + D);
+  __shared__ float mu_red[4];
+  __shared__ float mu_stage[MU_STAGE];
+  float* mu_ah = mu_stage;
   if (S::PHI != PHI_IDENTITY) pt.fill();
   char* mws = muon ? p.mws + (size_t)seq * p.mws_stride : nullptr;
   constexpr long P_W = S::MEM == MEM_MLP ? (long)H * D + (long)DV * H : (long)DV * D;
   // Muon without momentum in the state: S = g every token (eta = 0) in a
   // workspace buffer, zeroed so that 0 * S stays 0
   float* Smu = muon ? (mom ? Mo : reinterpret_cast<float*>(mws)) : nullptr;
+  float* Gmu = muon ? reinterpret_cast<float*>(mws + muon_ws_of(S::MEM == MEM_MLP, D, DV, H).g) : nullptr;
   if (muon && !mom)
     for (long e = threadIdx.x; e < P_W; e += blockDim.x) Smu[e] = 0.f;
 
@@ -367,9 +385,9 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
         const T* xq = Xq + (size_t)(n - t0) * DP;
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
         if constexpr (S::MEM == MEM_MLP) {
-          muon_matrix<S, H, D>(Wt, Smu, et, D1T, XwT, w0, c, al, th, p.ns_steps, mws, mu_red);
-          muon_matrix<S, DV, H>(Wt + (size_t)H * D, Smu + (size_t)H * D, et, D2T, AT, w0, c, al, th, p.ns_steps, mws,
-                                mu_red);
+          muon_matrix<S, H, D>(Wt, Smu, Gmu, et, D1T, XwT, w0, c, n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage);
+          muon_matrix<S, DV, H>(Wt + (size_t)H * D, Smu + (size_t)H * D, Gmu + (size_t)H * D, et, D2T, AT, w0, c,
+                                n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage);
           const float* W1 = Wt;
           const float* W2 = Wt + (size_t)H * D;
           for (int j = wave; j < H; j += nwaves) {
@@ -386,7 +404,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
             if (lane == 0) out[(size_t)n * DV + o] = from_f<TI>((res ? to_f(qr[n - t0][o]) : 0.f) + acc);
           }
         } else {
-          muon_matrix<S, DV, D>(Wt, Smu, et, D2T, XwT, w0, c, al, th, p.ns_steps, mws, mu_red);
+          muon_matrix<S, DV, D>(Wt, Smu, Gmu, et, D2T, XwT, w0, c, n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage);
           for (int o = wave; o < DV; o += nwaves) {
             float acc = 0.f;
             for (int f = lane; f < D; f += 64) acc += Wt[(size_t)o * D + f] * to_f(xq[f]);

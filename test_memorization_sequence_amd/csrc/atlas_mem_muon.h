@@ -32,12 +32,17 @@ __device__ __forceinline__ float muon_wave_sum(float v) {
 }
 
 // One token's Muon step on the weight matrix Wm [ROWS][COLS] (fp32, row
-// major) with momentum Sm of the same shape.  The window gradient is
-// sum_{w0 <= w < w0 + cw} Dt[r][w] Xc[col][w]  (Dt [ROWS][WP], Xc [>= COLS][WP]).
+// major) with momentum Sm of the same shape and the running window gradient
+// Gm (workspace, same shape).  Dt [ROWS][WP] and Xc [>= COLS][WP] hold the
+// gradient factors of the window rows: G_w = Dt[:, w] Xc[:, w]^T.  The
+// window of the token is rows w0 .. w0 + c - 1.  first: the chunk's first
+// token (the window sum is formed directly); later tokens add row w0 + c - 1
+// and drop row w0 - 1, with both rows' factors staged in `stage` (LDS,
+// 2 (ROWS + COLS) floats).  c == 1 takes G_{w0} itself.
 // Every thread of the workgroup calls this; it ends on a barrier.
 template <class S, int ROWS, int COLS, typename T>
-__device__ void muon_matrix(float* Wm, float* Sm, float eta, const T* Dt, const T* Xc, int w0, int cw, float alpha,
-                            float theta, int steps, char* mws, float* red) {
+__device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T* Dt, const T* Xc, int w0, int c,
+                            bool first, float alpha, float theta, int steps, char* mws, float* red, float* stage) {
   constexpr int WP = S::WP;
   constexpr bool TR = ROWS > COLS;
   constexpr int R = (int)ns_r(ROWS, COLS), NN = (int)ns_n(ROWS, COLS);
@@ -47,36 +52,64 @@ __device__ void muon_matrix(float* Wm, float* Sm, float eta, const T* Dt, const 
   float* Am = reinterpret_cast<float*>(mws + L.am);
   float* Bm = reinterpret_cast<float*>(mws + L.bm);
 
-  // S <- eta S + g; |S|_F^2; S into X[0] in the R x NN orientation, zero padded
-  float ss = 0.f;
-  for (int e = threadIdx.x; e < R * NN; e += blockDim.x) {
-    const int i = e / NN, j = e % NN;
-    const int r = TR ? j : i, c = TR ? i : j;
-    float s = 0.f;
-    if (r < ROWS && c < COLS) {
-      float g = 0.f;
-      for (int w = w0; w < w0 + cw; ++w) g += to_f(Dt[r * WP + w]) * to_f(Xc[c * WP + w]);
-      const size_t idx = (size_t)r * COLS + c;
-      s = eta * Sm[idx] + g;
-      Sm[idx] = s;
-      ss += s * s;
-    }
-    X[0][e] = s;
+  // factors of the rows entering (dn, xn) and leaving (dd, xd) the window
+  float* dn = stage;
+  float* dd = stage + ROWS;
+  float* xn = stage + 2 * ROWS;
+  float* xd = stage + 2 * ROWS + COLS;
+  const bool running = c > 1 && !first;
+  const int wn = c == 1 ? w0 : w0 + c - 1, wd = w0 - 1;
+  for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
+    dn[r] = to_f(Dt[r * WP + wn]);
+    dd[r] = running ? to_f(Dt[r * WP + wd]) : 0.f;
   }
+  for (int q = threadIdx.x; q < COLS; q += blockDim.x) {
+    xn[q] = to_f(Xc[q * WP + wn]);
+    xd[q] = running ? to_f(Xc[q * WP + wd]) : 0.f;
+  }
+  __syncthreads();
+
+  // g, S <- eta S + g, |S|_F^2; S into X[0] and X[0]^T (unscaled), walking S
+  // in its own row-major order
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < ROWS * COLS; e += blockDim.x) {
+    const int r = e / COLS, q = e % COLS;
+    float g;
+    if (c == 1) {
+      g = dn[r] * xn[q];
+    } else if (first) {
+      g = 0.f;
+      for (int w = w0; w < w0 + c; ++w) g += to_f(Dt[r * WP + w]) * to_f(Xc[q * WP + w]);
+      Gm[e] = g;
+    } else {
+      g = Gm[e] + dn[r] * xn[q] - dd[r] * xd[q];
+      Gm[e] = g;
+    }
+    const float s = eta * Sm[e] + g;
+    Sm[e] = s;
+    ss += s * s;
+    const int i = TR ? q : r, j = TR ? r : q;   // position in the R x NN orientation
+    X[0][i * NN + j] = s;
+    Xt[0][j * R + i] = s;
+  }
+  // zero padding of the R x NN orientation (a no-op when both are multiples of 32)
+  constexpr int RR = TR ? COLS : ROWS, NR = TR ? ROWS : COLS;
+  if (RR != R || NR != NN)
+    for (int e = threadIdx.x; e < R * NN; e += blockDim.x) {
+      const int i = e / NN, j = e % NN;
+      if (i >= RR || j >= NR) {
+        X[0][e] = 0.f;
+        Xt[0][j * R + i] = 0.f;
+      }
+    }
   ss = muon_wave_sum(ss);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
+  // X_0 = S / (|S|_F + 1e-7): the scale is folded into the first step
   const float inv = 1.f / (sqrtf(tot) + 1e-7f);
-  for (int e = threadIdx.x; e < R * NN; e += blockDim.x) {
-    const int i = e / NN, j = e % NN;
-    const float x = X[0][e] * inv;
-    X[0][e] = x;
-    Xt[0][j * R + i] = x;
-  }
-  __syncthreads();
 
   const float ca = 3.4445f, cb = -4.7750f, cc = 2.0315f;
   int cur = 0;
@@ -84,20 +117,29 @@ __device__ void muon_matrix(float* Wm, float* Sm, float eta, const T* Dt, const 
     const float* Xc_ = X[cur];
     float* Xn = X[cur ^ 1];
     float* Xtn = Xt[cur ^ 1];
-    {  // A = X X^T
+    const float sa = it == 0 ? inv * inv : 1.f, sx = it == 0 ? inv : 1.f;
+    {  // A = X X^T (symmetric: upper tiles, mirrored)
       Op<float> ops[1] = {{Xc_, NN, Xc_, NN, NN}};
-      gemm_nt(R, R, ops, [&](int i, int j, const float* a) { Am[i * R + j] = a[0]; });
+      gemm_nt(R, R, ops, [&](int i, int j, const float* a) {
+        const float v = sa * a[0];
+        Am[i * R + j] = v;
+        if ((i >> 5) != (j >> 5)) Am[j * R + i] = v;
+      }, true);
     }
     __syncthreads();
-    {  // B = b A + c A A  (A symmetric: A A = A A^T)
+    {  // B = b A + c A A  (A symmetric: A A = A A^T, and B is symmetric)
       Op<float> ops[1] = {{Am, R, Am, R, R}};
-      gemm_nt(R, R, ops, [&](int i, int j, const float* a) { Bm[i * R + j] = cb * Am[i * R + j] + cc * a[0]; });
+      gemm_nt(R, R, ops, [&](int i, int j, const float* a) {
+        const float v = cb * Am[i * R + j] + cc * a[0];
+        Bm[i * R + j] = v;
+        if ((i >> 5) != (j >> 5)) Bm[j * R + i] = v;
+      }, true);
     }
     __syncthreads();
     {  // X <- a X + B X, also transposed for the next step's B X
       Op<float> ops[1] = {{Bm, R, Xt[cur], R, R}};
       gemm_nt(R, NN, ops, [&](int i, int j, const float* a) {
-        const float y = ca * Xc_[i * NN + j] + a[0];
+        const float y = sx * (ca * Xc_[i * NN + j] + a[0]);
         Xn[i * NN + j] = y;
         Xtn[j * R + i] = y;
       });
@@ -110,8 +152,8 @@ __device__ void muon_matrix(float* Wm, float* Sm, float eta, const T* Dt, const 
   const float* O = X[cur];
   const float keep = 1.f - alpha;
   for (int e = threadIdx.x; e < ROWS * COLS; e += blockDim.x) {
-    const int r = e / COLS, c = e % COLS;
-    const float o = TR ? O[c * NN + r] : O[r * NN + c];
+    const int r = e / COLS, q = e % COLS;
+    const float o = TR ? O[q * NN + r] : O[r * NN + q];
     Wm[e] = keep * Wm[e] - theta * o;
   }
   __syncthreads();
