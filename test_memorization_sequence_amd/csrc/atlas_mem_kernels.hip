@@ -189,8 +189,12 @@ __device__ __forceinline__ float phi_feature(const TI* row, int f, const PairTab
 namespace atlas {
 
 // ----------------------------------------------------------------------------- chunk kernel
-template <class S>
-__global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
+// NT threads: 256 for gradient descent; 512 for Muon, whose per-token
+// Newton-Schulz GEMMs are latency-bound and gain from a second wave per SIMD
+// (the chunk-start part then runs with fewer registers, which it can afford
+// once per chunk).
+template <class S, int NT>
+__global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
   typedef typename S::T T;    // MFMA operand type
   typedef typename S::TI TI;  // io type of q, k, v, out
   typedef typename S::WS WS;
@@ -273,7 +277,7 @@ __global__ void __launch_bounds__(256) chunk_kernel(ChunkParams p) {
   // Muon: block sums; the factors of the window rows entering and leaving
   // (2 (rows + cols) floats of the largest matrix), then gelu(W1 phi(q_n))
   constexpr int MU_STAGE = S::MEM == MEM_MLP ? 2 * ((H > DV ? H : DV) + (D > H ? D : H)) : 2 * (DV + D);
-  __shared__ float mu_red[4];
+  __shared__ float mu_red[NT / 64];
   __shared__ float mu_stage[MU_STAGE];
   float* mu_ah = mu_stage;
   if (S::PHI != PHI_IDENTITY) pt.fill();
@@ -706,7 +710,10 @@ hipError_t launch(const ChunkParams& cp, const CoeffParams& kp, int n_seq, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_kernel<S>), dim3(n_seq), dim3(256), 0, stream, cp);
+  if (cp.muon)
+    hipLaunchKernelGGL((chunk_kernel<S, 512>), dim3(n_seq), dim3(512), 0, stream, cp);
+  else
+    hipLaunchKernelGGL((chunk_kernel<S, 256>), dim3(n_seq), dim3(256), 0, stream, cp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
