@@ -78,8 +78,9 @@ struct atlas_mem_s {
   char* ws;
   float* coef;
   hipEvent_t ev_before, ev_after;
-  char* mws;           // Muon: per-sequence workspace inside ws (else null)
+  char* mws;           // Muon: per-workgroup workspace inside ws (else null)
   size_t mws_stride;
+  int group;           // workgroups per sequence of the per-sequence family (2: Muon on an MLP)
 };
 
 static const uint32_t kMagic = 0xA7A5AE11u;
@@ -266,9 +267,16 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   const size_t xbytes = svar ? svar->xbytes() : tvar ? tvar->xbytes() : 0;
   const size_t ctrl_off = align_up(xbytes * (size_t)h->n_seq, 256);
   const bool muon = cfg->optimizer == ATLAS_OPT_MUON;
-  h->mws_stride = muon ? muon_ws_of(cfg->memory == ATLAS_MEM_MLP, h->lay.feature_dim, cfg->d_v, cfg->mlp_hidden).bytes : 0;
-  const size_t mws_off = var ? align_up(var->ws_bytes * (size_t)h->n_seq, 256) : 0;
-  const size_t ws_bytes = var       ? mws_off + h->mws_stride * (size_t)h->n_seq
+  // Muon on the MLP memory: a pair of workgroups per sequence, each with its
+  // own chunk and Muon workspaces, and the pair's counters after them
+  h->group = muon && cfg->memory == ATLAS_MEM_MLP ? 2 : 1;
+  const size_t members = (size_t)h->n_seq * h->group;
+  h->mws_stride = muon ? muon_ws_of(cfg->memory == ATLAS_MEM_MLP, h->lay.feature_dim, cfg->d_v, cfg->mlp_hidden,
+                                    cfg->chunk).bytes
+                       : 0;
+  const size_t mws_off = var ? align_up(var->ws_bytes * members, 256) : 0;
+  const size_t pctrl_off = align_up(mws_off + h->mws_stride * members, 256);
+  const size_t ws_bytes = var       ? pctrl_off + (h->group > 1 ? align_up((1 + (size_t)h->n_seq) * 4, 256) : 0)
                           : grouped ? ctrl_off + align_up((1 + (size_t)h->n_seq) * 4, 256)
                                     : 0;
   h->mws = nullptr;
@@ -285,8 +293,9 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
     return ATLAS_ERR_OUT_OF_MEMORY;
   }
   if (muon) h->mws = h->ws + mws_off;
-  if (grouped) {
-    h->ctrl = reinterpret_cast<unsigned*>(h->ws + ctrl_off);
+  if (h->group > 1) h->ctrl = reinterpret_cast<unsigned*>(h->ws + pctrl_off);
+  if (grouped) h->ctrl = reinterpret_cast<unsigned*>(h->ws + ctrl_off);
+  if (h->ctrl) {
     if ((e = hipMemset(h->ctrl, 0, (1 + (size_t)h->n_seq) * 4)) != hipSuccess) {
       (void)hipFree(h->ws);
       (void)hipFree(h->coef);
@@ -447,6 +456,9 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, c
   cp.ns_steps = c.ns_steps;
   cp.mws = h->mws;
   cp.mws_stride = h->mws_stride;
+  cp.ctrl = h->ctrl;
+  cp.n_seq = h->n_seq;
+  cp.group = h->group;
   e = h->var->launch(cp, kp, h->n_seq, (hipStream_t)stream, h->ev_before, h->ev_after);
   if (e != hipSuccess) return hip_fail(e);
   return ATLAS_OK;

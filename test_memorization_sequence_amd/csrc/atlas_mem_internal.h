@@ -77,15 +77,17 @@ constexpr long ns_r(long rows, long cols) { return ((rows > cols ? cols : rows) 
 constexpr long ns_n(long rows, long cols) { return ((rows > cols ? rows : cols) + 31) / 32 * 32; }
 constexpr long lmax(long a, long b) { return a > b ? a : b; }
 
-// Per-sequence Muon workspace (fp32, byte offsets): the momentum of a call
-// without momentum in the state (P floats), the running window gradient
+// Muon workspace of one workgroup (fp32, byte offsets): the momentum of a
+// call without momentum in the state (P floats), the running window gradient
 // (P floats), two ping-pong iterates X and their transposes (r x n each, the
-// largest matrix of the memory), and the r x r products A = X X^T and
-// B = b A + c A A.
+// largest matrix of the memory), the r x r products A = X X^T and
+// B = b A + c A A, and (MLP) the hidden activations gelu(W1_t phi(q_t)) of
+// the chunk's tokens [chunk][h], which the W1 workgroup of a pair hands to the
+// W2 workgroup.
 struct MuonWs {
-  size_t sloc, g, x0, x1, xt0, xt1, am, bm, bytes;
+  size_t sloc, g, x0, x1, xt0, xt1, am, bm, ab, bytes;
 };
-constexpr MuonWs muon_ws(long P, long rn, long rr) {
+constexpr MuonWs muon_ws(long P, long rn, long rr, long nab) {
   const size_t g = align_up((size_t)P * 4, 256);
   const size_t x0 = align_up(g + (size_t)P * 4, 256);
   const size_t x1 = align_up(x0 + (size_t)rn * 4, 256);
@@ -93,13 +95,14 @@ constexpr MuonWs muon_ws(long P, long rn, long rr) {
   const size_t xt1 = align_up(xt0 + (size_t)rn * 4, 256);
   const size_t am = align_up(xt1 + (size_t)rn * 4, 256);
   const size_t bm = align_up(am + (size_t)rr * 4, 256);
-  return MuonWs{0, g, x0, x1, xt0, xt1, am, bm, align_up(bm + (size_t)rr * 4, 256)};
+  const size_t ab = align_up(bm + (size_t)rr * 4, 256);
+  return MuonWs{0, g, x0, x1, xt0, xt1, am, bm, ab, align_up(ab + (size_t)nab * 4, 256)};
 }
-// linear memory: M [dv][D]; MLP: W1 [h][D], W2 [dv][h]
-constexpr MuonWs muon_ws_of(bool mlp, long D, long dv, long h) {
+// linear memory: M [dv][D]; MLP: W1 [h][D], W2 [dv][h]; bc the chunk
+constexpr MuonWs muon_ws_of(bool mlp, long D, long dv, long h, long bc) {
   return mlp ? muon_ws(h * D + dv * h, lmax(ns_r(h, D) * ns_n(h, D), ns_r(dv, h) * ns_n(dv, h)),
-                       lmax(ns_r(h, D) * ns_r(h, D), ns_r(dv, h) * ns_r(dv, h)))
-             : muon_ws(dv * D, ns_r(dv, D) * ns_n(dv, D), ns_r(dv, D) * ns_r(dv, D));
+                       lmax(ns_r(h, D) * ns_r(h, D), ns_r(dv, h) * ns_r(dv, h)), bc * h)
+             : muon_ws(dv * D, ns_r(dv, D) * ns_n(dv, D), ns_r(dv, D) * ns_r(dv, D), 0);
 }
 
 // T: MFMA operand type (bf16 or float); TI: io type of q, k, v, out.
@@ -168,13 +171,19 @@ struct ChunkParams {
   float ln_eps;
   int gated;       // MLP: f = r + W2 (gelu(W1 x) .* (W3 x)) (per-sequence kernel)
   // Muon: raw gates per token, Newton-Schulz steps, workspace (MuonWs per
-  // sequence, mws_stride bytes apart); muon == 0 for gradient descent
+  // workgroup, mws_stride bytes apart); muon == 0 for gradient descent.
+  // group = 2 (MLP memory): a pair of workgroups of one XCD per sequence,
+  // one per weight matrix, synchronised through ctrl ([0] error word,
+  // [1 + s] counter of sequence s, reset by the coefficient kernel); the
+  // chunk workspace (ws) is then per workgroup as well.
   const float* alpha;
   const float* eta;
   const float* theta;
   int muon, ns_steps;
   char* mws;
   size_t mws_stride;
+  unsigned* ctrl;
+  int n_seq, group;
 };
 
 struct ShardedParams {

@@ -47,6 +47,7 @@
 #include "atlas_mem_coeff.h"
 #include "atlas_mem_gelu.h"
 #include "atlas_mem_bias.h"
+#include "atlas_mem_group.h"
 
 namespace atlas {
 
@@ -199,7 +200,18 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
   typedef typename S::TI TI;  // io type of q, k, v, out
   typedef typename S::WS WS;
   constexpr int DK = S::DK, DV = S::DV, D = S::D, DP = S::DP, H = S::H, BC = S::BC, WP = S::WP;
-  const int seq = blockIdx.x;
+  // Muon on the MLP memory: a pair of workgroups per sequence (pm 0: W1,
+  // pm 1: W2), XCD-aware: block b runs on XCD b % 8, and the pair is blocks
+  // 8 (2 i + pm) + xcd, so both members share that XCD's L2
+  int seq = blockIdx.x, pm = 0;
+  const bool pair = p.group > 1;
+  if (pair) {
+    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+    pm = slot & 1;
+    seq = (slot >> 1) * 8 + xcd;
+    if (seq >= p.n_seq) return;
+  }
+  const int member = pair ? 2 * seq + pm : seq;   // index of this workgroup's workspaces
   const int N = p.N, c = p.c, W = BC + c - 1;
   const float s_grad = p.grad_scale;
   const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
@@ -233,7 +245,7 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
   TI* out = reinterpret_cast<TI*>(p.out) + (size_t)seq * N * DV;
   const float* gam_in = p.gamma + (size_t)seq * N;
 
-  char* ws = p.ws + (size_t)seq * WS::bytes;
+  char* ws = p.ws + (size_t)member * WS::bytes;
   T* Xw = reinterpret_cast<T*>(ws + WS::Xw);     // [WP][DP]  phi(k) of the window
   T* XwT = reinterpret_cast<T*>(ws + WS::XwT);   // [DP][WP]
   T* Xq = reinterpret_cast<T*>(ws + WS::Xq);     // [BC][DP]  phi(q) of the chunk
@@ -281,12 +293,19 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
   __shared__ float mu_stage[MU_STAGE];
   float* mu_ah = mu_stage;
   if (S::PHI != PHI_IDENTITY) pt.fill();
-  char* mws = muon ? p.mws + (size_t)seq * p.mws_stride : nullptr;
+  char* mws = muon ? p.mws + (size_t)member * p.mws_stride : nullptr;
+  constexpr MuonWs MUL = muon_ws_of(S::MEM == MEM_MLP, D, DV, H, BC);
+  // pair: counter and error word, the barrier count so far, and the hidden
+  // activations the W1 member hands over (in that member's workspace)
+  unsigned* gctr = pair ? p.ctrl + 1 + seq : nullptr;
+  unsigned* gerr = pair ? p.ctrl : nullptr;
+  unsigned gbase = 0;
+  float* abuf = pair ? reinterpret_cast<float*>(p.mws + (size_t)(2 * seq) * p.mws_stride + MUL.ab) : nullptr;
   constexpr long P_W = S::MEM == MEM_MLP ? (long)H * D + (long)DV * H : (long)DV * D;
   // Muon without momentum in the state: S = g every token (eta = 0) in a
   // workspace buffer, zeroed so that 0 * S stays 0
   float* Smu = muon ? (mom ? Mo : reinterpret_cast<float*>(mws)) : nullptr;
-  float* Gmu = muon ? reinterpret_cast<float*>(mws + muon_ws_of(S::MEM == MEM_MLP, D, DV, H).g) : nullptr;
+  float* Gmu = muon ? reinterpret_cast<float*>(mws + MUL.g) : nullptr;
   if (muon && !mom)
     for (long e = threadIdx.x; e < P_W; e += blockDim.x) Smu[e] = 0.f;
 
@@ -382,6 +401,55 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
     // y_n = f_{W_n}(phi(q_n)) from the fp32 weights; afterwards the operand
     // images of the chunk-end weights for the next chunk's gradients
     auto muon_chunk = [&]() {
+      if constexpr (S::MEM == MEM_MLP) {
+        if (pair) {
+          // counter per chunk: both arrive (2), then one signal per token
+          // from member 0, then both arrive again (2)
+          const unsigned m = (unsigned)(te - t0 + 1);
+          group_barrier(gctr, gbase + 2u, gerr);   // the partner's image refresh is done
+          for (int n = t0; n <= te; ++n) {
+            const size_t gi = (size_t)seq * N + n;
+            const float al = p.alpha[gi], th = p.theta[gi], et = mom ? p.eta[gi] : 0.f;
+            const int w0 = n - t0;
+            const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+            float* an = abuf + (size_t)(n - t0) * H;
+            if (pm == 0) {
+              muon_matrix<S, H, D>(Wt, Smu, Gmu, et, D1T, XwT, w0, c, n == t0, al, th, p.ns_steps, mws, mu_red,
+                                   mu_stage);
+              const T* xq = Xq + (size_t)(n - t0) * DP;
+              for (int j = wave; j < H; j += nwaves) {
+                float acc = 0.f;
+                for (int f = lane; f < D; f += 64) acc += Wt[(size_t)j * D + f] * to_f(xq[f]);
+                acc = muon_wave_sum(acc);
+                if (lane == 0) an[j] = gelu(acc);
+              }
+              pair_signal(gctr);
+            } else {
+              muon_matrix<S, DV, H>(Wt + (size_t)H * D, Smu + (size_t)H * D, Gmu + (size_t)H * D, et, D2T, AT, w0, c,
+                                    n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage);
+              pair_wait(gctr, gbase + 2u + (unsigned)(n - t0 + 1), gerr);
+              const float* W2 = Wt + (size_t)H * D;
+              for (int o = wave; o < DV; o += nwaves) {
+                float acc = 0.f;
+                for (int j = lane; j < H; j += 64) acc += W2[(size_t)o * H + j] * an[j];
+                acc = muon_wave_sum(acc);
+                if (lane == 0) out[(size_t)n * DV + o] = from_f<TI>((res ? to_f(qr[n - t0][o]) : 0.f) + acc);
+              }
+              __syncthreads();
+            }
+          }
+          group_barrier(gctr, gbase + 4u + m, gerr);   // both matrices are at the chunk end
+          gbase += 4u + m;
+          for (int e = threadIdx.x; e < H * D; e += blockDim.x) W1b[(e / D) * DP + e % D] = from_f<T>(Wt[e]);
+          for (int e = threadIdx.x; e < DV * H; e += blockDim.x) {
+            const float w2 = Wt[(size_t)H * D + e];
+            W2b[e] = from_f<T>(w2);
+            W2T[(e % H) * DV + e / H] = from_f<T>(w2);
+          }
+          __syncthreads();
+          return;
+        }
+      }
       for (int n = t0; n <= te; ++n) {
         const size_t gi = (size_t)seq * N + n;
         const float al = p.alpha[gi], th = p.theta[gi], et = mom ? p.eta[gi] : 0.f;
@@ -688,7 +756,7 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
   // ---- halo of the last c-1 tokens (oldest first) and the token count.
   // Slot j takes token N-(c-1)+j: from this call if >= 0, else from old slot
   // N+j >= j, which increasing-j order has not overwritten yet.
-  if (threadIdx.x < 64) {
+  if (threadIdx.x < 64 && pm == 0) {
     const int lane = threadIdx.x;
     for (int j = 0; j < c - 1; ++j) {
       const int i = N - (c - 1) + j;
@@ -711,7 +779,8 @@ hipError_t launch(const ChunkParams& cp, const CoeffParams& kp, int n_seq, hipSt
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
   if (cp.muon)
-    hipLaunchKernelGGL((chunk_kernel<S, 512>), dim3(n_seq), dim3(512), 0, stream, cp);
+    hipLaunchKernelGGL((chunk_kernel<S, 512>), dim3(cp.group > 1 ? (unsigned)((n_seq + 7) / 8) * 16u : (unsigned)n_seq),
+                       dim3(512), 0, stream, cp);
   else
     hipLaunchKernelGGL((chunk_kernel<S, 256>), dim3(n_seq), dim3(256), 0, stream, cp);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -25,6 +25,33 @@
 
 namespace atlas {
 
+// Hand-off inside a pair of workgroups of one XCD (the counter is the pair's
+// group-barrier counter; see atlas_mem_group.h).  signal: every wave's stores
+// are complete (they write through the CU's L1 to the shared L2), then one
+// arrival.  wait: bounded poll until the counter reaches target, then the
+// CU's L1 is invalidated so that later loads see the partner's stores.
+__device__ __forceinline__ void pair_signal(unsigned* ctr) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(ctr, 1u);
+}
+
+__device__ __forceinline__ void pair_wait(unsigned* ctr, unsigned target, unsigned* err) {
+  if (threadIdx.x == 0) {
+    unsigned polls = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+      if (++polls > (1u << 24)) {
+        atomicOr(err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  asm volatile("buffer_inv sc0" ::: "memory");
+}
+
 __device__ __forceinline__ float muon_wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -46,7 +73,7 @@ __device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T*
   constexpr int WP = S::WP;
   constexpr bool TR = ROWS > COLS;
   constexpr int R = (int)ns_r(ROWS, COLS), NN = (int)ns_n(ROWS, COLS);
-  constexpr MuonWs L = muon_ws_of(S::MEM == MEM_MLP, S::D, S::DV, S::H);
+  constexpr MuonWs L = muon_ws_of(S::MEM == MEM_MLP, S::D, S::DV, S::H, S::BC);
   float* X[2] = {reinterpret_cast<float*>(mws + L.x0), reinterpret_cast<float*>(mws + L.x1)};
   float* Xt[2] = {reinterpret_cast<float*>(mws + L.xt0), reinterpret_cast<float*>(mws + L.xt1)};
   float* Am = reinterpret_cast<float*>(mws + L.am);

@@ -52,6 +52,7 @@ def _parity(B, wl):
     st = mem.new_state(torch.from_numpy(w0))
     out = H.gpu_run(mem, wl, dev, st)
     torch.cuda.synchronize()
+    assert mem.device_errors() == 0   # the pair's waits all completed
     st_g = H.gpu_state_np(mem, st)
     out_g = out.float().cpu().numpy()
     from oracle import oracle as O
