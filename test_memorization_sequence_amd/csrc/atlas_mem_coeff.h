@@ -101,16 +101,19 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   __syncthreads();
   // window row w <-> token i = t0 - (c-1) + w (relative to the call start):
   // C_{tt,w} = sum of F[tt][n] over n in [max(t0, i), min(t0 + tt, i + c - 1)]
-  for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) {
-    const int tt = idx / WP, w = idx % WP;
+  auto cval = [&](int tt, int w) -> float {
     const int i = t0 - (c - 1) + w;
     float s = 0.f;
     if (tt < nb && w < BC + c - 1 && i >= -halo_valid && i <= t0 + tt) {
       const int lo = max(t0, i) - t0, hi = min(t0 + tt, i + c - 1) - t0;
       s = (float)(F[tt][hi] - (lo > 0 ? F[tt][lo - 1] : 0.0));
     }
-    oC[tt * WP + w] = s;
-  }
+    return s;
+  };
+  // the fp32 C; its only reader with a bf16 copy (CB16) is this kernel, which
+  // then takes every value straight from the prefix sums instead
+  if constexpr (!CB16)
+    for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) oC[idx] = cval(idx / WP, idx % WP);
   __syncthreads();
   if constexpr (QD > 0) {
     // Q1 = C .* (Xq X^T): bf16 MFMA, fp32 accumulation, 4 waves x 16x16 tiles
@@ -154,13 +157,13 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
       }
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + 4 * g + r, col = n0 + c16;
-        oQ[row * QP + col] = (__bf16)(oC[row * WP + col] * acc[r]);
+        oQ[row * QP + col] = (__bf16)((CB16 ? cval(row, col) : oC[row * WP + col]) * acc[r]);
       }
     }
   }
   if constexpr (CB16) {
     __bf16* oCb = reinterpret_cast<__bf16*>(oC + BC * WP) + BC * q1_pitch(WP, CB16);
-    for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) oCb[idx] = (__bf16)oC[idx];
+    for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) oCb[idx] = (__bf16)cval(idx / WP, idx % WP);
   }
   for (int w = threadIdx.x; w < WP; w += blockDim.x) {
     const int i = t0 - (c - 1) + w;

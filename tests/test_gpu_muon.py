@@ -135,3 +135,29 @@ def test_muon_theta_zero_keeps_weights_and_alpha_one_erases(B):
     assert not mem.view(st, "weights").any()
     assert torch.equal(out.cpu(), dev["q"].cpu())
 
+
+
+def test_muon_bench_shape_sampled(B):
+    """The benchmark's Muon launch: all 96 sequences of the 128-512-128
+    memory (8 x 12 heads, c = 32) in one call, here of one chunk and a
+    ragged tail; the oracle replays three sequences (first, middle, last),
+    outputs and final weights and momentum."""
+    binding, H = B
+    n = 64 + 9
+    wl = replace(WORKLOADS["layer_scale"].with_shape(seq_len=n), optimizer="muon")
+    _say(f"[muon full grid] layer_scale B={wl.batch} H={wl.heads} N={n}")
+    inputs, w0 = H.prepare(wl)
+    mem = binding.AtlasMem(wl)
+    dev = H.to_device(wl, inputs)
+    st = mem.new_state(torch.from_numpy(w0))
+    out = H.gpu_run(mem, wl, dev, st)
+    torch.cuda.synchronize()
+    assert mem.device_errors() == 0
+    seqs = [0, 47, 95]
+    from oracle import oracle as O
+    out_o, st_o, _ = O.run_workload(wl, inputs, w0, seqs=seqs)
+    r = H.compare(wl, inputs, out.float().cpu().numpy(), H.gpu_state_np(mem, st), out_o, st_o, seqs=seqs)
+    _say(f"[muon full grid] {r}")
+    for key in ("out", "memory_part", "weights", "momentum"):
+        assert r[key] <= H.tol_of(wl), (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
