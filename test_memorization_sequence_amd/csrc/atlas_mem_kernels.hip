@@ -290,6 +290,7 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
   // (2 (rows + cols) floats of the largest matrix), then gelu(W1 phi(q_n))
   constexpr int MU_STAGE = S::MEM == MEM_MLP ? 2 * ((H > DV ? H : DV) + (D > H ? D : H)) : 2 * (DV + D);
   __shared__ float mu_red[NT / 64];
+  extern __shared__ __attribute__((aligned(16))) float mu_bs[];   // Muon: B of Newton-Schulz (launch-sized)
   __shared__ float mu_stage[MU_STAGE];
   float* mu_ah = mu_stage;
   if (S::PHI != PHI_IDENTITY) pt.fill();
@@ -415,7 +416,7 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
             float* an = abuf + (size_t)(n - t0) * H;
             if (pm == 0) {
               muon_matrix<S, H, D>(Wt, Smu, Gmu, et, D1T, XwT, w0, c, n == t0, al, th, p.ns_steps, mws, mu_red,
-                                   mu_stage);
+                                   mu_stage, mu_bs);
               const T* xq = Xq + (size_t)(n - t0) * DP;
               for (int j = wave; j < H; j += nwaves) {
                 float acc = 0.f;
@@ -426,7 +427,7 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
               pair_signal(gctr);
             } else {
               muon_matrix<S, DV, H>(Wt + (size_t)H * D, Smu + (size_t)H * D, Gmu + (size_t)H * D, et, D2T, AT, w0, c,
-                                    n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage);
+                                    n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage, mu_bs);
               pair_wait(gctr, gbase + 2u + (unsigned)(n - t0 + 1), gerr);
               const float* W2 = Wt + (size_t)H * D;
               for (int o = wave; o < DV; o += nwaves) {
@@ -457,9 +458,9 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
         const T* xq = Xq + (size_t)(n - t0) * DP;
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
         if constexpr (S::MEM == MEM_MLP) {
-          muon_matrix<S, H, D>(Wt, Smu, Gmu, et, D1T, XwT, w0, c, n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage);
+          muon_matrix<S, H, D>(Wt, Smu, Gmu, et, D1T, XwT, w0, c, n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage, mu_bs);
           muon_matrix<S, DV, H>(Wt + (size_t)H * D, Smu + (size_t)H * D, Gmu + (size_t)H * D, et, D2T, AT, w0, c,
-                                n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage);
+                                n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage, mu_bs);
           const float* W1 = Wt;
           const float* W2 = Wt + (size_t)H * D;
           for (int j = wave; j < H; j += nwaves) {
@@ -476,7 +477,7 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
             if (lane == 0) out[(size_t)n * DV + o] = from_f<TI>((res ? to_f(qr[n - t0][o]) : 0.f) + acc);
           }
         } else {
-          muon_matrix<S, DV, D>(Wt, Smu, Gmu, et, D2T, XwT, w0, c, n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage);
+          muon_matrix<S, DV, D>(Wt, Smu, Gmu, et, D2T, XwT, w0, c, n == t0, al, th, p.ns_steps, mws, mu_red, mu_stage, mu_bs);
           for (int o = wave; o < DV; o += nwaves) {
             float acc = 0.f;
             for (int f = lane; f < D; f += 64) acc += Wt[(size_t)o * D + f] * to_f(xq[f]);
@@ -778,9 +779,19 @@ hipError_t launch(const ChunkParams& cp, const CoeffParams& kp, int n_seq, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  if (cp.muon)
+  if (cp.muon) {
+    // LDS for Newton-Schulz's B when every orientation has at most 128 rows
+    constexpr long r1 = S::MEM == MEM_MLP ? lmax(ns_r(S::H, S::D), ns_r(S::DV, S::H)) : ns_r(S::DV, S::D);
+    constexpr size_t bs = r1 <= 128 ? (size_t)r1 * (r1 + 4) * 4 : 0;
+    static bool attr = false;
+    if (!attr) {
+      attr = true;
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_kernel<S, 512>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bs);
+    }
     hipLaunchKernelGGL((chunk_kernel<S, 512>), dim3(cp.group > 1 ? (unsigned)((n_seq + 7) / 8) * 16u : (unsigned)n_seq),
-                       dim3(512), 0, stream, cp);
+                       dim3(512), bs, stream, cp);
+  }
   else
     hipLaunchKernelGGL((chunk_kernel<S, 256>), dim3(n_seq), dim3(256), 0, stream, cp);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -58,6 +58,57 @@ __device__ __forceinline__ float muon_wave_sum(float v) {
   return v;
 }
 
+// B X step for an orientation with R <= 128 rows: B (R x R) sits in LDS at
+// pitch R + 4 (16-byte fragment reads without bank conflicts), X is read
+// straight from the workspace as the MFMA's B operand (lane l: row k, column
+// l & 15, so 16 lanes read 64 contiguous bytes), and each wave owns whole
+// 32-column strips of Y = sx (a X + B X) over all R / 32 row blocks.  Every
+// X element is read once, and no transposed copy of X is needed.
+template <int R, int NN>
+__device__ void ns_bx(const float* Bs, const float* X, float* Y, float ca, float sx) {
+  constexpr int BP = R + 4, RB = R / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll 1
+  for (int n0 = 32 * wave; n0 < NN; n0 += 32 * nwaves) {
+    f32x4 acc[RB][2][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[rb][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int k0 = 0; k0 < R; k0 += 16) {
+      // MFMA step e contracts k = k0 + 4 g + e (the fragment order of Mma<float>)
+      f32x4 b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[j][e] = X[(size_t)(k0 + 4 * g + e) * NN + n0 + 16 * j + c16];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(Bs + (32 * rb + 16 * i + c16) * BP + k0 + 4 * g);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[rb][i][j] = Mma<float>::mma(a, b[j], acc[rb][i][j]);
+        }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const size_t e = (size_t)(32 * rb + 16 * i + 4 * g + r) * NN + n0 + 16 * j + c16;
+            Y[e] = sx * (ca * X[e] + acc[rb][i][j][r]);
+          }
+  }
+}
+
 // One token's Muon step on the weight matrix Wm [ROWS][COLS] (fp32, row
 // major) with momentum Sm of the same shape and the running window gradient
 // Gm (workspace, same shape).  Dt [ROWS][WP] and Xc [>= COLS][WP] hold the
@@ -65,14 +116,21 @@ __device__ __forceinline__ float muon_wave_sum(float v) {
 // window of the token is rows w0 .. w0 + c - 1.  first: the chunk's first
 // token (the window sum is formed directly); later tokens add row w0 + c - 1
 // and drop row w0 - 1, with both rows' factors staged in `stage` (LDS,
-// 2 (ROWS + COLS) floats).  c == 1 takes G_{w0} itself.
+// 2 (ROWS + COLS) floats).  c == 1 takes G_{w0} itself.  bs: LDS for B
+// (R (R + 4) floats) when R <= 128; larger orientations keep B and a
+// transposed copy of X in the workspace.
 // Every thread of the workgroup calls this; it ends on a barrier.
 template <class S, int ROWS, int COLS, typename T>
 __device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T* Dt, const T* Xc, int w0, int c,
-                            bool first, float alpha, float theta, int steps, char* mws, float* red, float* stage) {
+                            bool first, float alpha, float theta, int steps, char* mws, float* red, float* stage,
+                            float* bs) {
   constexpr int WP = S::WP;
   constexpr bool TR = ROWS > COLS;
   constexpr int R = (int)ns_r(ROWS, COLS), NN = (int)ns_n(ROWS, COLS);
+  // B in LDS when every orientation of the memory has at most 128 rows (the
+  // launch sizes the LDS by the largest)
+  constexpr long RMAX = S::MEM == MEM_MLP ? lmax(ns_r(S::H, S::D), ns_r(S::DV, S::H)) : ns_r(S::DV, S::D);
+  constexpr bool LDSB = RMAX <= 128;
   constexpr MuonWs L = muon_ws_of(S::MEM == MEM_MLP, S::D, S::DV, S::H, S::BC);
   float* X[2] = {reinterpret_cast<float*>(mws + L.x0), reinterpret_cast<float*>(mws + L.x1)};
   float* Xt[2] = {reinterpret_cast<float*>(mws + L.xt0), reinterpret_cast<float*>(mws + L.xt1)};
@@ -117,7 +175,7 @@ __device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T*
     ss += s * s;
     const int i = TR ? q : r, j = TR ? r : q;   // position in the R x NN orientation
     X[0][i * NN + j] = s;
-    Xt[0][j * R + i] = s;
+    if (!LDSB) Xt[0][j * R + i] = s;
   }
   // zero padding of the R x NN orientation (a no-op when both are multiples of 32)
   constexpr int RR = TR ? COLS : ROWS, NR = TR ? ROWS : COLS;
@@ -126,7 +184,7 @@ __device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T*
       const int i = e / NN, j = e % NN;
       if (i >= RR || j >= NR) {
         X[0][e] = 0.f;
-        Xt[0][j * R + i] = 0.f;
+        if (!LDSB) Xt[0][j * R + i] = 0.f;
       }
     }
   ss = muon_wave_sum(ss);
@@ -156,14 +214,18 @@ __device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T*
     __syncthreads();
     {  // B = b A + c A A  (A symmetric: A A = A A^T, and B is symmetric)
       Op<float> ops[1] = {{Am, R, Am, R, R}};
+      float* Bd = LDSB ? bs : Bm;
+      constexpr int BP = LDSB ? R + 4 : R;
       gemm_nt(R, R, ops, [&](int i, int j, const float* a) {
         const float v = cb * Am[i * R + j] + cc * a[0];
-        Bm[i * R + j] = v;
-        if ((i >> 5) != (j >> 5)) Bm[j * R + i] = v;
+        Bd[i * BP + j] = v;
+        if ((i >> 5) != (j >> 5)) Bd[j * BP + i] = v;
       }, true);
     }
     __syncthreads();
-    {  // X <- a X + B X, also transposed for the next step's B X
+    if constexpr (LDSB) {  // X <- a X + B X
+      ns_bx<R, NN>(bs, Xc_, Xn, ca, sx);
+    } else {  // X <- a X + B X, also transposed for the next step's B X
       Op<float> ops[1] = {{Bm, R, Xt[cur], R, R}};
       gemm_nt(R, NN, ops, [&](int i, int j, const float* a) {
         const float y = sx * (ca * Xc_[i * NN + j] + a[0]);
