@@ -226,7 +226,8 @@ __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
   const bool rowwise = shaped || ln;
   // Muon memory optimizer: per-token Newton-Schulz steps after the window
   // gradients (atlas_mem_muon.h); no layer norm, no gated memory
-  const bool muon = p.muon != 0;
+  // (only the 512-thread instance carries the Muon code; the launcher picks it)
+  const bool muon = NT == 512 && p.muon != 0;
 
   char* st = p.state + (size_t)seq * p.seq_stride;
   float* Wt = reinterpret_cast<float*>(st + p.off_weights);

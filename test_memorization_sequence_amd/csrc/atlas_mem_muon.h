@@ -109,6 +109,74 @@ __device__ void ns_bx(const float* Bs, const float* X, float* Y, float ca, float
   }
 }
 
+// A = sa X X^T for R <= 128: X passes through LDS (the region of B, R x (R + 4)
+// floats) one block of R columns at a time, so every X element is read from
+// the workspace once; the upper tiles of A (32 x 32, at most two per wave)
+// keep their accumulators across the blocks, and the epilogue mirrors them.
+template <int R, int NN>
+__device__ void ns_xxt(const float* X, float* Am, float* Ls, float sa) {
+  constexpr int BP = R + 4, TN = R / 32, NTL = TN * (TN + 1) / 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  int tm[2], tn[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {   // the wave's tiles, row by row of the upper triangle
+    int t = wave + s * nwaves, mt = 0;
+    while (mt < TN && t >= TN - mt) { t -= TN - mt; ++mt; }
+    tm[s] = mt;
+    tn[s] = mt + t;
+  }
+  f32x4 acc[2][2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[s][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = 0; kb < NN; kb += R) {
+    const int kw = NN - kb < R ? NN - kb : R;   // a multiple of 32
+    __syncthreads();   // the previous block is consumed
+    for (int e = threadIdx.x; e < R * (kw / 4); e += blockDim.x) {
+      const int row = e / (kw / 4), q4 = e % (kw / 4);
+      *reinterpret_cast<f32x4*>(Ls + row * BP + 4 * q4) =
+          *reinterpret_cast<const f32x4*>(X + (size_t)row * NN + kb + 4 * q4);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (wave + s * nwaves >= NTL) break;
+      const float* ra = Ls + (32 * tm[s] + c16) * BP + 4 * g;
+      const float* rb = Ls + (32 * tn[s] + c16) * BP + 4 * g;
+#pragma unroll 1
+      for (int k0 = 0; k0 < kw; k0 += 16) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ra + k0);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ra + 16 * BP + k0);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(rb + k0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(rb + 16 * BP + k0);
+        acc[s][0][0] = Mma<float>::mma(a0, b0, acc[s][0][0]);
+        acc[s][0][1] = Mma<float>::mma(a0, b1, acc[s][0][1]);
+        acc[s][1][0] = Mma<float>::mma(a1, b0, acc[s][1][0]);
+        acc[s][1][1] = Mma<float>::mma(a1, b1, acc[s][1][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (wave + s * nwaves >= NTL) break;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 32 * tm[s] + 16 * i + 4 * g + r, col = 32 * tn[s] + 16 * j + c16;
+          const float v = sa * acc[s][i][j][r];
+          Am[row * R + col] = v;
+          if (tm[s] != tn[s]) Am[col * R + row] = v;
+        }
+  }
+}
+
 // One token's Muon step on the weight matrix Wm [ROWS][COLS] (fp32, row
 // major) with momentum Sm of the same shape and the running window gradient
 // Gm (workspace, same shape).  Dt [ROWS][WP] and Xc [>= COLS][WP] hold the
@@ -203,7 +271,10 @@ __device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T*
     float* Xn = X[cur ^ 1];
     float* Xtn = Xt[cur ^ 1];
     const float sa = it == 0 ? inv * inv : 1.f, sx = it == 0 ? inv : 1.f;
-    {  // A = X X^T (symmetric: upper tiles, mirrored)
+    if constexpr (LDSB) {  // A = X X^T, X staged through LDS
+      static_assert((R / 32) * (R / 32 + 1) / 2 <= 2 * 8, "at most two tiles of A per wave");
+      ns_xxt<R, NN>(Xc_, Am, bs, sa);
+    } else {  // A = X X^T (symmetric: upper tiles, mirrored)
       Op<float> ops[1] = {{Xc_, NN, Xc_, NN, NN}};
       gemm_nt(R, R, ops, [&](int i, int j, const float* a) {
         const float v = sa * a[0];
