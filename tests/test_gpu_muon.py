@@ -73,6 +73,8 @@ def _parity(B, wl):
 MUON_CASES = [("linear64_delta", 3 * 64 + 17, {}), ("linear_poly2", 3 * 64 + 17, {}), ("mlp64", 3 * 64 + 17, {}),
               ("mlp64", 2 * 64 + 5, {"momentum": False}), ("mlp64", 2 * 64 + 5, {"bias": "dot"}),
               ("mlp64", 2 * 64 + 5, {"window": 8}), ("mlp64", 2 * 64 + 5, {"ns_steps": 2}),
+              ("mlp64", 2 * 64 + 5, {"bias": "lp", "bias_p": 3.0}),
+              ("mlp64", 2 * 64 + 5, {"bias": "huber", "sign_alpha": 16.0}),
               ("layer_scale", 64 + 9, {})]
 
 
@@ -83,6 +85,17 @@ def test_muon_parity(B, name, n, kw, recipe):
     _say(f"[muon] {name} {kw} {recipe} B=1 H=2 N={n}")
     r = _parity(B, wl)
     _say(f"[muon] {name} {kw} {recipe}: {r}")
+
+
+def test_muon_wide_feature_map(B):
+    """The 688-512-128 memory on [k, poly2(k[:32])] (c = 64): W1's orientation
+    has 512 rows, past the LDS path, so Newton-Schulz keeps B and a transposed
+    copy of X in the workspace.  One sequence, ten tokens: the oracle needs
+    about 4 s per token of this memory."""
+    wl = replace(lively(WORKLOADS["atlas_long"]).with_shape(batch=1, heads=1, seq_len=10), optimizer="muon")
+    _say("[muon] atlas_long B=1 H=1 N=10")
+    r = _parity(B, wl)
+    _say(f"[muon] atlas_long: {r}")
 
 
 def test_muon_split_is_bitwise_equal(B):
