@@ -190,10 +190,10 @@ __device__ __forceinline__ float phi_feature(const TI* row, int f, const PairTab
 namespace atlas {
 
 // ----------------------------------------------------------------------------- chunk kernel
-// NT threads: 256 for gradient descent; 512 for Muon, whose per-token
-// Newton-Schulz GEMMs are latency-bound and gain from a second wave per SIMD
-// (the chunk-start part then runs with fewer registers, which it can afford
-// once per chunk).
+// NT threads: 256 for gradient descent on narrow memories; 512 for Muon,
+// whose per-token Newton-Schulz GEMMs are latency-bound and gain from a
+// second wave per SIMD, and for gradient descent on wide memories (h >= 512
+// or D >= 256), where the same holds for the chunk's GEMMs.
 template <class S, int NT>
 __global__ void __launch_bounds__(NT) chunk_kernel(ChunkParams p) {
   typedef typename S::T T;    // MFMA operand type
@@ -793,6 +793,11 @@ hipError_t launch(const ChunkParams& cp, const CoeffParams& kp, int n_seq, hipSt
     hipLaunchKernelGGL((chunk_kernel<S, 512>), dim3(cp.group > 1 ? (unsigned)((n_seq + 7) / 8) * 16u : (unsigned)n_seq),
                        dim3(512), bs, stream, cp);
   }
+  else if constexpr (S::H >= 512 || S::D >= 256)
+    // wide memories: a second wave per SIMD hides more of the GEMMs' load
+    // latency (atlas-style 688-512-128: 836 -> 617 ms per call; linear on
+    // 560 features: 7.48 -> 6.67 ms)
+    hipLaunchKernelGGL((chunk_kernel<S, 512>), dim3(n_seq), dim3(512), 0, stream, cp);
   else
     hipLaunchKernelGGL((chunk_kernel<S, 256>), dim3(n_seq), dim3(256), 0, stream, cp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
