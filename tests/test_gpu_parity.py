@@ -380,7 +380,7 @@ def test_short_calls_other_biases(B, bias, n):
 # decays to W = 0) and which gives W no restoring force: there a single
 # bf16-level perturbation of the initial weights moves the fp64 oracle by up
 # to 22 % (tests/test_layernorm_conditioning.py measures it).  Parity is
-# judged on the cases whose own sensitivity is small.
+# checked on the cases whose own sensitivity is small.
 LN_MLPS = [n for n in ORDER if WORKLOADS[n].memory == "mlp"]
 LN_CASES = ([(n, b, "lively") for n in LN_MLPS for b in ("l2", "dot", "lp3")] + [("mlp64", "huber_smooth", "lively")]
             + [(n, b, "preset") for n in ("atlas_long", "layer_scale") for b in ("l2", "dot")])
