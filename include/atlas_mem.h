@@ -36,7 +36,7 @@
  *   y_t   = f_{M_t}(phi(q_t))                 (Titans review sec. 3.1
  *                         "Retrieving a Memory": a forward pass, no update)
  *
- * With the Muon memory optimizer (ATLAS review sec. 5 "Memory Optimization":
+ * With the Muon memory optimizer (ATLAS summary sec. 5, "Memory Optimization":
  * Muon in place of plain gradient descent on the memory; per-sequence family,
  * plain linear or 2-layer MLP memory) the two middle lines become
  *   S_t   = eta_t S_{t-1} + grad_t

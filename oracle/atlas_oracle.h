@@ -24,7 +24,7 @@
  *     after token t's update (Titans review, section 3.1 "Retrieving a
  *     Memory").
  *
- * Memory optimizer Muon (ATLAS review, section 5 "Memory Optimization": Muon
+ * Memory optimizer Muon (ATLAS summary, section 5, "Memory Optimization": Muon
  * takes the place of plain gradient descent on the memory).  Read as the
  * published Muon optimizer (K. Jordan et al., 2024, "Muon: An optimizer for
  * hidden layers in neural networks"), with the memory's gates in its roles:

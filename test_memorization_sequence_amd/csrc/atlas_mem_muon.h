@@ -1,7 +1,7 @@
 // atlas_mem_muon.h -- the Muon memory optimizer inside the per-sequence chunk
 // kernel (included by atlas_mem_kernels.hip after gemm_nt and the MFMA types).
 //
-// ATLAS review sec. 5 "Memory Optimization": Muon takes the place of plain
+// ATLAS summary sec. 5, "Memory Optimization": Muon takes the place of plain
 // gradient descent on the memory.  Read as the published Muon optimizer
 // (K. Jordan et al., 2024) with the memory's gates in its roles.  For every
 // token n of a chunk and every weight matrix W of the memory, with the

@@ -1,7 +1,7 @@
 """Parity of the library's Muon memory optimizer with the fp64 oracle (needs
 an MI355X).
 
-Muon (ATLAS review sec. 5 "Memory Optimization") replaces gradient descent
+Muon (ATLAS summary sec. 5, "Memory Optimization") replaces gradient descent
 on the memory: per token, S = eta S + grad, each weight matrix moves by
 -theta NS(S) after the decay, NS the quintic Newton-Schulz iteration of the
 published Muon optimizer.  It runs on the per-sequence family.  Same inputs,
