@@ -222,6 +222,16 @@ __device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T*
   }
   __syncthreads();
 
+  // the chunk's first window sum as one GEMM (bf16 MFMA, fp32 sums) when the
+  // window is a whole number of MFMA k-steps and the matrix whole tiles;
+  // otherwise each element sums its c terms below
+  const bool gemm_first = c > 1 && first && c % Mma<T>::KSTEP == 0 && ROWS % 32 == 0 && COLS % 32 == 0;
+  if (gemm_first) {
+    Op<T> ops[1] = {{Dt + w0, WP, Xc + w0, WP, c}};
+    gemm_nt(ROWS, COLS, ops, [&](int r, int q, const float* a) { Gm[r * COLS + q] = a[0]; });
+    __syncthreads();
+  }
+
   // g, S <- eta S + g, |S|_F^2; S into X[0] and X[0]^T (unscaled), walking S
   // in its own row-major order
   float ss = 0.f;
@@ -230,6 +240,8 @@ __device__ void muon_matrix(float* Wm, float* Sm, float* Gm, float eta, const T*
     float g;
     if (c == 1) {
       g = dn[r] * xn[q];
+    } else if (gemm_first) {
+      g = Gm[e];
     } else if (first) {
       g = 0.f;
       for (int w = w0; w < w0 + c; ++w) g += to_f(Dt[r * WP + w]) * to_f(Xc[q * WP + w]);
