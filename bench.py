@@ -35,7 +35,7 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 MEASURED_TRAFFIC = {
     # (workload, kernel, optimizer, tokens per sequence), l2 bias, plain memory
     ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "b6b4b5a95dd1b0ba", "bytes": 75.03e9},
-    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "c782ba315e1e21a0", "bytes": 91.67e9},
+    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "e306d11cfb24f55e", "bytes": 91.84e9},
 }
 
 
