@@ -174,3 +174,27 @@ def test_muon_bench_shape_sampled(B):
     for key in ("out", "memory_part", "weights", "momentum"):
         assert r[key] <= H.tol_of(wl), (key, r)
     assert r["halo_exact"] and r["count_exact"], r
+
+
+@pytest.mark.parametrize("n", [0, 1, 37])
+def test_muon_short_and_empty_calls(B, n):
+    """Calls shorter than one chunk (and the empty call, which leaves the
+    state as it is) on the pair of workgroups (64-256-64) and on the linear
+    memory."""
+    binding, H = B
+    for name in ("mlp64", "linear_poly2"):
+        wl = _muon(name, n, "lively")
+        _say(f"[muon short] {name} N={n}")
+        if n == 0:
+            inputs, w0 = H.prepare(wl.with_shape(seq_len=1))
+            mem = binding.AtlasMem(wl)
+            st = mem.new_state(torch.from_numpy(w0))
+            before = st.clone()
+            dev = H.to_device(wl.with_shape(seq_len=1), inputs)
+            out = torch.empty(wl.batch, wl.heads, 0, wl.d_v, dtype=mem.io_dtype, device="cuda")
+            mem.forward(dev["q"][:, :, :0], dev["k"][:, :, :0], dev["v"][:, :, :0], dev["alpha"][:, :, :0],
+                        dev["eta"][:, :, :0], dev["theta"][:, :, :0], dev["gamma"][:, :, :0], st, out)
+            torch.cuda.synchronize()
+            assert torch.equal(st, before)
+            continue
+        _parity(B, wl)
