@@ -116,48 +116,65 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
     for (int idx = threadIdx.x; idx < BC * WP; idx += blockDim.x) oC[idx] = cval(idx / WP, idx % WP);
   __syncthreads();
   if constexpr (QD > 0) {
-    // Q1 = C .* (Xq X^T): bf16 MFMA, fp32 accumulation, 4 waves x 16x16 tiles
+    // Q1 = C .* (Xq X^T): bf16 MFMA, fp32 accumulation, 4 waves x 16x16
+    // tiles.  Keys and queries pass through LDS one block of KB columns at a
+    // time (a small footprint: three workgroups fit a CU instead of two), the
+    // tile accumulators staying in registers across the blocks.
     typedef __bf16 bx8 __attribute__((ext_vector_type(8)));
     typedef float fx4 __attribute__((ext_vector_type(4)));
-    constexpr int L = QD + 8;
+    constexpr int KB = 32, L = KB + 8;
+    static_assert(QD % KB == 0, "whole column blocks");
     __shared__ __attribute__((aligned(16))) __bf16 Xs[WP * L];
     __shared__ __attribute__((aligned(16))) __bf16 Qs[BC * L];
     const __bf16* kk = reinterpret_cast<const __bf16*>(p.k) + (size_t)seq * p.N * QD;
     const __bf16* qq = reinterpret_cast<const __bf16*>(p.q) + (size_t)seq * p.N * QD;
     const float* hk = reinterpret_cast<const float*>(p.state + (size_t)seq * p.seq_stride + p.off_halo_k);
-    for (int e = threadIdx.x; e < WP * (QD / 8); e += blockDim.x) {
-      const int w = e / (QD / 8), d8 = (e % (QD / 8)) * 8, i = t0 - (c - 1) + w;
-      bx8 x;
-      for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
-      if (w < BC + c - 1 && i >= -halo_valid && i <= te) {
-        if (i >= 0) x = *reinterpret_cast<const bx8*>(kk + (size_t)i * QD + d8);
-        else
-          for (int z = 0; z < 8; ++z) x[z] = (__bf16)hk[(c - 1 + i) * QD + d8 + z];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+    constexpr int NTL = (BC / 16) * (WP / 16), TPW = (NTL + 3) / 4;   // tiles, per wave
+    fx4 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) acc[u] = fx4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < QD; kb += KB) {
+      if (kb) __syncthreads();   // every wave is done with the previous block
+      for (int e = threadIdx.x; e < WP * (KB / 8); e += blockDim.x) {
+        const int w = e / (KB / 8), d8 = (e % (KB / 8)) * 8, i = t0 - (c - 1) + w;
+        bx8 x;
+        for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
+        if (w < BC + c - 1 && i >= -halo_valid && i <= te) {
+          if (i >= 0) x = *reinterpret_cast<const bx8*>(kk + (size_t)i * QD + kb + d8);
+          else
+            for (int z = 0; z < 8; ++z) x[z] = (__bf16)hk[(c - 1 + i) * QD + kb + d8 + z];
+        }
+        *reinterpret_cast<bx8*>(Xs + w * L + d8) = x;
       }
-      *reinterpret_cast<bx8*>(Xs + w * L + d8) = x;
+      for (int e = threadIdx.x; e < BC * (KB / 8); e += blockDim.x) {
+        const int n = e / (KB / 8), d8 = (e % (KB / 8)) * 8;
+        bx8 x;
+        for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
+        if (n < nb) x = *reinterpret_cast<const bx8*>(qq + (size_t)(t0 + n) * QD + kb + d8);
+        *reinterpret_cast<bx8*>(Qs + n * L + d8) = x;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int t = wave + 4 * u;
+        if (t >= NTL) break;
+        const int m0 = 16 * (t / (WP / 16)), n0 = 16 * (t % (WP / 16));
+        const bx8 a = *reinterpret_cast<const bx8*>(Qs + (m0 + c16) * L + 8 * g);
+        const bx8 b = *reinterpret_cast<const bx8*>(Xs + (n0 + c16) * L + 8 * g);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[u], 0, 0, 0);
+      }
     }
-    for (int e = threadIdx.x; e < BC * (QD / 8); e += blockDim.x) {
-      const int n = e / (QD / 8), d8 = (e % (QD / 8)) * 8;
-      bx8 x;
-      for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
-      if (n < nb) x = *reinterpret_cast<const bx8*>(qq + (size_t)(t0 + n) * QD + d8);
-      *reinterpret_cast<bx8*>(Qs + n * L + d8) = x;
-    }
-    __syncthreads();
     __bf16* oQ = reinterpret_cast<__bf16*>(oC + BC * WP);
     constexpr int QP = q1_pitch(WP, CB16);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
-    for (int t = wave; t < (BC / 16) * (WP / 16); t += 4) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave + 4 * u;
+      if (t >= NTL) break;
       const int m0 = 16 * (t / (WP / 16)), n0 = 16 * (t % (WP / 16));
-      fx4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < QD; k0 += 32) {
-        const bx8 a = *reinterpret_cast<const bx8*>(Qs + (m0 + c16) * L + k0 + 8 * g);
-        const bx8 b = *reinterpret_cast<const bx8*>(Xs + (n0 + c16) * L + k0 + 8 * g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-      }
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + 4 * g + r, col = n0 + c16;
-        oQ[row * QP + col] = (__bf16)((CB16 ? cval(row, col) : oC[row * WP + col]) * acc[r]);
+        oQ[row * QP + col] = (__bf16)((CB16 ? cval(row, col) : oC[row * WP + col]) * acc[u][r]);
       }
     }
   }
