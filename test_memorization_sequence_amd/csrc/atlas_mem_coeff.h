@@ -41,6 +41,47 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   float* ocS = ocM + WP;
   float* oC = ocS + WP;             // [BC][WP]
 
+  // Q1's operands (keys of the window, queries of the chunk; bf16, 8 at a
+  // time) are loaded into registers here, so that their latency passes while
+  // the recurrences below run; they go to LDS one block of KB columns at a
+  // time further down
+  typedef __bf16 bx8 __attribute__((ext_vector_type(8)));
+  constexpr int KB = 32, NKB = QD > 0 ? QD / KB : 1;
+  // (256 threads: the launch size of this kernel)
+  constexpr int NXE = (WP * (KB / 8) + 255) / 256, NQE = (BC * (KB / 8) + 255) / 256;   // per thread and block
+  bx8 xr[NKB][NXE], qr[NKB][NQE];
+  if constexpr (QD > 0) {
+    static_assert(QD % KB == 0, "whole column blocks");
+    const __bf16* kk = reinterpret_cast<const __bf16*>(p.k) + (size_t)seq * p.N * QD;
+    const __bf16* qq = reinterpret_cast<const __bf16*>(p.q) + (size_t)seq * p.N * QD;
+    const float* hk = reinterpret_cast<const float*>(p.state + (size_t)seq * p.seq_stride + p.off_halo_k);
+#pragma unroll
+    for (int b = 0; b < NKB; ++b) {
+#pragma unroll
+      for (int j = 0; j < NXE; ++j) {
+        const int e = (int)threadIdx.x + 256 * j;
+        const int w = e / (KB / 8), d = b * KB + (e % (KB / 8)) * 8, i = t0 - (c - 1) + w;
+        bx8 x;
+        for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
+        if (e < WP * (KB / 8) && w < BC + c - 1 && i >= -halo_valid && i <= te) {
+          if (i >= 0) x = *reinterpret_cast<const bx8*>(kk + (size_t)i * QD + d);
+          else
+            for (int z = 0; z < 8; ++z) x[z] = (__bf16)hk[(c - 1 + i) * QD + d + z];
+        }
+        xr[b][j] = x;
+      }
+#pragma unroll
+      for (int j = 0; j < NQE; ++j) {
+        const int e = (int)threadIdx.x + 256 * j;
+        const int n = e / (KB / 8), d = b * KB + (e % (KB / 8)) * 8;
+        bx8 x;
+        for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
+        if (e < BC * (KB / 8) && n < nb) x = *reinterpret_cast<const bx8*>(qq + (size_t)(t0 + n) * QD + d);
+        qr[b][j] = x;
+      }
+    }
+  }
+
   for (int n = threadIdx.x; n < BC; n += blockDim.x) {
     const bool ok = n < nb;
     al[n] = ok ? p.alpha[g0 + t0 + n] : 0.f;
@@ -120,39 +161,27 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
     // tiles.  Keys and queries pass through LDS one block of KB columns at a
     // time (a small footprint: three workgroups fit a CU instead of two), the
     // tile accumulators staying in registers across the blocks.
-    typedef __bf16 bx8 __attribute__((ext_vector_type(8)));
     typedef float fx4 __attribute__((ext_vector_type(4)));
-    constexpr int KB = 32, L = KB + 8;
-    static_assert(QD % KB == 0, "whole column blocks");
+    constexpr int L = KB + 8;
     __shared__ __attribute__((aligned(16))) __bf16 Xs[WP * L];
     __shared__ __attribute__((aligned(16))) __bf16 Qs[BC * L];
-    const __bf16* kk = reinterpret_cast<const __bf16*>(p.k) + (size_t)seq * p.N * QD;
-    const __bf16* qq = reinterpret_cast<const __bf16*>(p.q) + (size_t)seq * p.N * QD;
-    const float* hk = reinterpret_cast<const float*>(p.state + (size_t)seq * p.seq_stride + p.off_halo_k);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
     constexpr int NTL = (BC / 16) * (WP / 16), TPW = (NTL + 3) / 4;   // tiles, per wave
     fx4 acc[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) acc[u] = fx4{0.f, 0.f, 0.f, 0.f};
-    for (int kb = 0; kb < QD; kb += KB) {
-      if (kb) __syncthreads();   // every wave is done with the previous block
-      for (int e = threadIdx.x; e < WP * (KB / 8); e += blockDim.x) {
-        const int w = e / (KB / 8), d8 = (e % (KB / 8)) * 8, i = t0 - (c - 1) + w;
-        bx8 x;
-        for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
-        if (w < BC + c - 1 && i >= -halo_valid && i <= te) {
-          if (i >= 0) x = *reinterpret_cast<const bx8*>(kk + (size_t)i * QD + kb + d8);
-          else
-            for (int z = 0; z < 8; ++z) x[z] = (__bf16)hk[(c - 1 + i) * QD + kb + d8 + z];
-        }
-        *reinterpret_cast<bx8*>(Xs + w * L + d8) = x;
+#pragma unroll
+    for (int blk = 0; blk < NKB; ++blk) {
+      if (blk) __syncthreads();   // every wave is done with the previous block
+#pragma unroll
+      for (int jj = 0; jj < NXE; ++jj) {
+        const int e = (int)threadIdx.x + 256 * jj;
+        if (e < WP * (KB / 8)) *reinterpret_cast<bx8*>(Xs + (e / (KB / 8)) * L + (e % (KB / 8)) * 8) = xr[blk][jj];
       }
-      for (int e = threadIdx.x; e < BC * (KB / 8); e += blockDim.x) {
-        const int n = e / (KB / 8), d8 = (e % (KB / 8)) * 8;
-        bx8 x;
-        for (int z = 0; z < 8; ++z) x[z] = (__bf16)0.f;
-        if (n < nb) x = *reinterpret_cast<const bx8*>(qq + (size_t)(t0 + n) * QD + kb + d8);
-        *reinterpret_cast<bx8*>(Qs + n * L + d8) = x;
+#pragma unroll
+      for (int jj = 0; jj < NQE; ++jj) {
+        const int e = (int)threadIdx.x + 256 * jj;
+        if (e < BC * (KB / 8)) *reinterpret_cast<bx8*>(Qs + (e / (KB / 8)) * L + (e % (KB / 8)) * 8) = qr[blk][jj];
       }
       __syncthreads();
 #pragma unroll
