@@ -34,8 +34,8 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 # changed kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
     # (workload, kernel, optimizer, tokens per sequence), l2 bias, plain memory
-    ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "284f70ea11b54c92", "bytes": 75.02e9},
-    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "70050f644e7fbf52", "bytes": 91.77e9},
+    ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "978e86c51e1e3528", "bytes": 74.97e9},
+    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "9aa8cf83d3cedd91", "bytes": 91.84e9},
 }
 
 
