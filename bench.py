@@ -224,7 +224,7 @@ def main():
     ap.add_argument("--prologue", action="store_true",
                     help="time the fused prologue (x -> q, k, v, gates) on the workload's shape instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=24.0, help="seconds of oracle work (estimated)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only copy a buffer of this many bytes 3 times (HBM counter calibration)")
     args = ap.parse_args()
