@@ -221,6 +221,9 @@ def main():
                     help="Muon memory optimizer (per-token Newton-Schulz; per-sequence family)")
     ap.add_argument("--ns-steps", type=int, default=5, help="Muon: Newton-Schulz steps")
     ap.add_argument("--seq-len", type=int, default=None, help="override the workload's tokens per sequence")
+    ap.add_argument("--theta-as-stated", action="store_true",
+                    help="theta = sigmoid(U(-4, 0)) without the division by the window c (the recipe as "
+                         "stated, whose memory diverges to inf/NaN within a few chunks); throughput only")
     ap.add_argument("--prologue", action="store_true",
                     help="time the fused prologue (x -> q, k, v, gates) on the workload's shape instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -264,6 +267,9 @@ def main():
         wl = replace(wl, optimizer="muon", ns_steps=args.ns_steps)
     if args.seq_len is not None:
         wl = wl.with_shape(seq_len=args.seq_len)
+    if args.theta_as_stated:
+        from dataclasses import replace
+        wl = replace(wl, theta_div=1.0)
     print(f"[bench] {wl.name} bias={wl.bias}: B={wl.batch} H={wl.heads} N={wl.seq_len} ({wl.note})", file=sys.stderr, flush=True)
     inputs = synth.make_inputs(wl, 0)
     w0 = synth.initial_weights_flat(wl, inputs)
@@ -301,8 +307,15 @@ def main():
     mem.set_kernel_events(None, None)
     ms_per_step = wall * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
-    if not torch.isfinite(out.float()).all():
-        print("[bench] warning: non-finite outputs", file=sys.stderr)
+    flags = mem.device_errors()
+    finite = bool(torch.isfinite(out.float()).all())
+    if flags != 0:
+        print(f"[bench] error: device error word {flags:#x} (a group barrier timed out; outputs invalid)",
+              file=sys.stderr)
+        sys.exit(3)
+    if not finite and not args.theta_as_stated:
+        print("[bench] error: non-finite outputs", file=sys.stderr)
+        sys.exit(3)
 
     S = wl.batch * wl.heads
     nch = -(-wl.seq_len // wl.chunk)
@@ -328,7 +341,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if wl.io_dtype == "f32" else "bf16",
-        "data": "synthetic (seeded numpy: L2-normalised q,k; N(0,1) v; sigmoid gates)",
+        "data": "synthetic (seeded numpy: L2-normalised q,k; N(0,1) v; sigmoid gates"
+                + (", theta as stated: the memory diverges, outputs non-finite)" if args.theta_as_stated
+                   else f", theta / {wl.theta_div:g})" if wl.theta_div != 1.0 else ")"),
         "config": {"workload": wl.name, "kernel_family": args.kernel, "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seq_len,
                    "d_k": wl.d_k, "d_v": wl.d_v, "memory": wl.memory, "hidden": wl.hidden,
                    "feature_dim": wl.feature_dim, "window": wl.window, "chunk": wl.chunk,

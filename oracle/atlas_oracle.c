@@ -240,26 +240,47 @@ static void grad_factors(const oracle_config* cfg, const double* th,
   free(f);
 }
 
-/* g += G(d1, d2, a, x), the outer-product form of one token's gradient. */
-static void add_grad(const oracle_config* cfg, const double* x, const double* d1,
-                     const double* d2, const double* a, double* g) {
+/* g += G(d1, d2, a, x), the outer-product form of one token's gradient,
+ * restricted to the weight rows [r0, r1) of the row list W1 (h rows), W2 (d_v
+ * rows), W3 (h rows), or M (d_v rows) for a linear memory.  Splitting the rows
+ * between threads leaves every element's sum in the same order.            */
+static long grad_rows(const oracle_config* cfg) {
+  if (cfg->memory == ORC_LINEAR) return cfg->d_v;
+  return (long)cfg->hidden * (cfg->gated ? 2 : 1) + cfg->d_v;
+}
+
+static void add_grad_rows(const oracle_config* cfg, const double* x, const double* d1,
+                          const double* d2, const double* a, double* g, long r0, long r1) {
   const int D = oracle_feature_dim(cfg), dv = cfg->d_v, h = cfg->hidden;
   if (cfg->memory == ORC_LINEAR) {
-    for (int o = 0; o < dv; ++o)
-      for (int d = 0; d < D; ++d) g[(long)o * D + d] += d2[o] * x[d];
+    for (long o = r0; o < r1; ++o)
+      for (int d = 0; d < D; ++d) g[o * D + d] += d2[o] * x[d];
     return;
   }
   double* gW2 = g + (long)h * D;
-  for (int j = 0; j < h; ++j)
-    for (int d = 0; d < D; ++d) g[(long)j * D + d] += d1[j] * x[d];
-  for (int o = 0; o < dv; ++o)
-    for (int j = 0; j < h; ++j) gW2[(long)o * h + j] += d2[o] * a[j];
-  if (cfg->gated) {
-    double* gW3 = gW2 + (long)dv * h;
-    for (int j = 0; j < h; ++j)
-      for (int d = 0; d < D; ++d) gW3[(long)j * D + d] += d1[h + j] * x[d];
+  double* gW3 = gW2 + (long)dv * h;
+  for (long r = r0; r < r1; ++r) {
+    if (r < h) {
+      const long j = r;
+      for (int d = 0; d < D; ++d) g[j * D + d] += d1[j] * x[d];
+    } else if (r < h + dv) {
+      const long o = r - h;
+      for (int j = 0; j < h; ++j) gW2[o * h + j] += d2[o] * a[j];
+    } else {
+      const long j = r - h - dv;
+      for (int d = 0; d < D; ++d) gW3[j * D + d] += d1[h + j] * x[d];
+    }
   }
 }
+
+static void add_grad(const oracle_config* cfg, const double* x, const double* d1,
+                     const double* d2, const double* a, double* g) {
+  add_grad_rows(cfg, x, d1, d2, a, g, 0, grad_rows(cfg));
+}
+
+/* Threads that work inside one sequence (set per call by oracle_forward_ex
+ * when there are fewer sequences than threads).                            */
+static int g_inner_threads = 1;
 
 void oracle_token_grad_ex(const oracle_config* cfg, const double* theta,
                           const double* x, const double* r, const double* v,
@@ -392,6 +413,8 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
     /* window tokens i in [lo, te], relative to the call start; i < 0 is halo */
     int lo = t0 - (c - 1);
     if (lo < -halo_valid) lo = -halo_valid;
+    /* each window token's factors are independent of the others' */
+#pragma omp parallel for num_threads(g_inner_threads) if (g_inner_threads > 1) schedule(dynamic, 1)
     for (int i = lo; i <= te; ++i) {
       const double *ki, *vi;
       double gi, di = 0.0;
@@ -411,10 +434,22 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
       memset(g, 0, sizeof(double) * P);
       int i0 = n - c + 1;
       if (i0 < lo) i0 = lo;
-      for (int i = i0; i <= n; ++i) {
-        const int w = i - lo;
-        add_grad(cfg, X + (long)w * D, D1 + (long)w * h1, D2 + (long)w * dv,
-                 A + (long)w * h, g);
+      /* g_n = sum over the window, oldest token first; threads split the
+         weight rows, each row summed in that same order */
+      const long nrows = grad_rows(cfg);
+#pragma omp parallel num_threads(g_inner_threads) if (g_inner_threads > 1)
+      {
+        long r0 = 0, r1 = nrows;
+#ifdef _OPENMP
+        const int nt = omp_get_num_threads(), it = omp_get_thread_num();
+        r0 = nrows * it / nt;
+        r1 = nrows * (it + 1) / nt;
+#endif
+        for (int i = i0; i <= n; ++i) {
+          const int w = i - lo;
+          add_grad_rows(cfg, X + (long)w * D, D1 + (long)w * h1, D2 + (long)w * dv,
+                        A + (long)w * h, g, r0, r1);
+        }
       }
       const double eta_n = cfg->momentum ? et[n] : 0.0;
       double* Sx = cfg->momentum ? S : Sloc;
@@ -429,6 +464,7 @@ static void run_sequence(const oracle_config* cfg, const double* q, const double
         }
         for (long p = 0; p < P; ++p) W[p] = (1.0 - al[n]) * W[p] - th[n] * O[p];
       } else {
+#pragma omp parallel for num_threads(g_inner_threads) if (g_inner_threads > 1) schedule(static)
         for (long p = 0; p < P; ++p) {
           Sx[p] = eta_n * Sx[p] - th[n] * g[p];
           W[p] = (1.0 - al[n]) * W[p] + Sx[p];
@@ -482,6 +518,25 @@ int oracle_forward_ex(const oracle_config* cfg,
   const long N = cfg->seq_len, dk = cfg->d_k, dv = cfg->d_v, halo = cfg->window - 1;
   const long P = oracle_param_count(cfg);
   int threads = 1;
+  g_inner_threads = 1;
+#ifdef _OPENMP
+  /* Fewer sequences than threads and large per-token window sums: the
+     sequences run one after another, each with every thread splitting the
+     weight rows of its window sums and updates.                          */
+  const int avail = omp_get_max_threads();
+  if (cfg->n_seq < avail && (double)P * cfg->window >= 1.0e6) g_inner_threads = avail;
+#endif
+  if (g_inner_threads > 1) {
+    for (int s = 0; s < cfg->n_seq; ++s)
+      run_sequence(cfg, q + s * N * dk, k + s * N * dk, v + s * N * dv,
+                   alpha + s * N, eta + s * N, theta + s * N, gamma + s * N,
+                   delta ? delta + s * N : NULL,
+                   mem + s * P, mom + s * P,
+                   halo_k + s * halo * dk, halo_v + s * halo * dv, halo_g + s * halo,
+                   halo_d ? halo_d + s * halo : NULL,
+                   count + s, out + s * N * dv);
+    return g_inner_threads;
+  }
 #pragma omp parallel
   {
 #ifdef _OPENMP

@@ -25,15 +25,24 @@ FLAGS = [
 ]
 
 
+def _compile(src: str) -> tuple[str, str]:
+    obj = os.path.join(CSRC, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops' is not a recognized" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+    return obj, err
+
+
 def build(verbose: bool = False) -> str:
+    # one hipcc per translation unit, run side by side
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_compile, SOURCES))
     objs = []
-    for src in SOURCES:
-        obj = os.path.join(CSRC, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops' is not a recognized" not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+    for obj, err in results:
         if verbose and err.strip():
             print(err, file=sys.stderr)
         objs.append(obj)
