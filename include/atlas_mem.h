@@ -71,7 +71,9 @@ typedef enum {
   ATLAS_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, aliasing   */
   ATLAS_ERR_UNSUPPORTED = 2,      /* valid config with no kernel built for it      */
   ATLAS_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed                   */
-  ATLAS_ERR_HIP = 4               /* a HIP call failed; see atlas_mem_last_hip_error */
+  ATLAS_ERR_HIP = 4,              /* a HIP call failed; see atlas_mem_last_hip_error */
+  ATLAS_ERR_SCRATCH_TOO_SMALL = 5 /* atlas_mem_forward_noalloc: the call needs more
+                                     workspace than the static scratch buffer     */
 } atlas_status;
 
 enum { ATLAS_MEM_LINEAR = 0, ATLAS_MEM_MLP = 1 };
@@ -197,6 +199,30 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h,
                                   const float* alpha, const float* eta,
                                   const float* theta, const float* gamma, const float* delta,
                                   void* state, void* out, void* stream /* hipStream_t */);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * call as atlas_mem_forward_ex (same kernels, same results bit for bit, same
+ * argument rules), configured by *cfg directly: no handle and no allocation.
+ * Its workspace (coefficient blocks, operand images, exchange buffers and
+ * control words) lives in one static device buffer of the library, 32 MiB
+ * per device, which each device that runs such a call holds until the
+ * process ends.  A call whose workspace does not fit returns
+ * ATLAS_ERR_SCRATCH_TOO_SMALL and enqueues nothing (for a size, the
+ * handle's workspace is what atlas_mem_init would allocate).  Every call on
+ * one device shares that buffer, which keeps the last call's contents: calls
+ * that overlap on one device (two streams, two threads) race and give wrong
+ * results.  errors (device, optional, 4-byte aligned) receives the call's
+ * device error word after its kernels (0: none; bit 0: a group barrier timed
+ * out and the outputs are invalid); it replaces atlas_mem_device_errors.
+ * Errors: as atlas_mem_forward_ex, plus SCRATCH_TOO_SMALL; UNSUPPORTED /
+ * INVALID_ARGUMENT for a config atlas_mem_init would reject.               */
+atlas_status atlas_mem_forward_noalloc(const atlas_mem_config* cfg,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* eta,
+                                       const float* theta, const float* gamma, const float* delta,
+                                       void* state, void* out, unsigned* errors,
+                                       void* stream /* hipStream_t */);
 
 /* Optional timing hook for profilers and benchmarks: while set, every
  * atlas_mem_forward records `before` on its stream right before the

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libatlas_mem.so")
 INCLUDE = os.path.join(os.path.dirname(_PKG), "include")
 HEADER = os.path.join(INCLUDE, "atlas_mem.h")
 
-OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_OOM, ERR_HIP = 0, 1, 2, 3, 4
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_OOM, ERR_HIP, ERR_SCRATCH = 0, 1, 2, 3, 4, 5
 MEM = {"linear": 0, "mlp": 1}
 PHI = {"identity": 0, "poly2": 1, "raw_poly2": 2}
 BIAS = {"l2": 0, "dot": 1, "lp": 2, "huber": 3}
@@ -83,6 +83,8 @@ def lib():
         L.atlas_mem_forward.restype = ctypes.c_int
         L.atlas_mem_forward_ex.argtypes = [vp] * 12
         L.atlas_mem_forward_ex.restype = ctypes.c_int
+        L.atlas_mem_forward_noalloc.argtypes = [cp] + [vp] * 12
+        L.atlas_mem_forward_noalloc.restype = ctypes.c_int
         L.atlas_mem_set_kernel_events.argtypes = [vp, vp, vp]
         L.atlas_mem_set_kernel_events.restype = ctypes.c_int
         L.atlas_mem_kernel_family.argtypes = [vp]
@@ -227,6 +229,21 @@ class AtlasMem:
         if rc != OK:
             raise AtlasError(rc, what)
         return out
+
+
+def forward_noalloc(wl: Workload | AtlasMemConfig, q, k, v, alpha, eta, theta, gamma, state, out,
+                    errors=None, stream=None, delta=None, kernel: str = "auto") -> None:
+    """atlas_mem_forward_noalloc: the call of AtlasMem.forward without a
+    handle, on the library's static scratch buffer.  errors: optional int32
+    device tensor of one element that receives the call's error word."""
+    cfg = config_of(wl, kernel) if isinstance(wl, Workload) else wl
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = lib().atlas_mem_forward_noalloc(
+        ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(theta), _ptr(gamma),
+        _ptr(delta), _ptr(state), _ptr(out), _ptr(errors), ctypes.c_void_p(stream.cuda_stream))
+    if rc != OK:
+        raise AtlasError(rc, "atlas_mem_forward_noalloc")
 
 
 class AtlasPrologue:

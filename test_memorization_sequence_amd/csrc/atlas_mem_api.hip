@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "atlas_mem.h"
@@ -230,20 +231,14 @@ static atlas_mem_state_layout make_layout(const atlas_mem_config* c) {
   return L;
 }
 
-extern "C" {
-
-atlas_status atlas_mem_supported(const atlas_mem_config* cfg) { return check_config(cfg, nullptr, nullptr, nullptr); }
-
-atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
-  if (!out) return ATLAS_ERR_INVALID_ARGUMENT;
-  *out = nullptr;
+// Fields of a handle that depend on the configuration only.
+static atlas_status setup_handle(const atlas_mem_config* cfg, atlas_mem_s* h) {
   const Variant* var = nullptr;
   const ShardedVariant* svar = nullptr;
   const StreamVariant* tvar = nullptr;
   atlas_status s = check_config(cfg, &var, &svar, &tvar);
   if (s != ATLAS_OK) return s;
-  atlas_mem_s* h = new (std::nothrow) atlas_mem_s();
-  if (!h) return ATLAS_ERR_OUT_OF_MEMORY;
+  *h = atlas_mem_s();
   h->magic = kMagic;
   h->cfg = *cfg;
   h->var = var;
@@ -256,52 +251,120 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   h->coef_stride = var ? coef_stride(var->bc, var->wp)
                  : svar ? coef_stride(svar->bc, svar->wp, true)
                         : coef_stride(tvar->bc, tvar->wp, true, true);
-  hipError_t e = hipGetDevice(&h->device);
-  if (e != hipSuccess) { delete h; return hip_fail(e); }
+  h->device = -1;
   h->ws = nullptr;
   h->coef = nullptr;
   h->ev_before = h->ev_after = nullptr;
-  // sharded, and streamed with G > 1: exchange buffers per sequence, then
-  // the control words (error word + one barrier counter per sequence)
-  const bool grouped = svar || tvar;   // streamed: tile-major state copy (+ exchange for G = 2)
-  const size_t xbytes = svar ? svar->xbytes() : tvar ? tvar->xbytes() : 0;
-  const size_t ctrl_off = align_up(xbytes * (size_t)h->n_seq, 256);
+  h->mws = nullptr;
   const bool muon = cfg->optimizer == ATLAS_OPT_MUON;
   // Muon on the MLP memory: a pair of workgroups per sequence, each with its
   // own chunk and Muon workspaces, and the pair's counters after them
   h->group = muon && cfg->memory == ATLAS_MEM_MLP ? 2 : 1;
-  const size_t members = (size_t)h->n_seq * h->group;
   h->mws_stride = muon ? muon_ws_of(cfg->memory == ATLAS_MEM_MLP, h->lay.feature_dim, cfg->d_v, cfg->mlp_hidden,
                                     cfg->chunk).bytes
                        : 0;
-  const size_t mws_off = var ? align_up(var->ws_bytes * members, 256) : 0;
-  const size_t pctrl_off = align_up(mws_off + h->mws_stride * members, 256);
-  const size_t ws_bytes = var       ? pctrl_off + (h->group > 1 ? align_up((1 + (size_t)h->n_seq) * 4, 256) : 0)
-                          : grouped ? ctrl_off + align_up((1 + (size_t)h->n_seq) * 4, 256)
-                                    : 0;
-  h->mws = nullptr;
-  const size_t coef_bytes = (size_t)h->n_seq * h->nchunks * h->coef_stride * sizeof(float);
-  if (ws_bytes && hipMalloc(&h->ws, ws_bytes) != hipSuccess) {
+  return ATLAS_OK;
+}
+
+// Device memory a handle's calls use besides their arguments: the kernel
+// workspace (ws_bytes, with the control words inside it at ctrl_off) and the
+// coefficient blocks (coef_bytes).
+struct WsPlan {
+  size_t ws_bytes, coef_bytes, ctrl_off, mws_off;
+  bool has_ctrl;
+};
+
+static WsPlan plan_workspace(const atlas_mem_s* h) {
+  WsPlan pl;
+  // sharded, and streamed: exchange buffers / tile-major state per sequence,
+  // then the control words (error word + one barrier counter per sequence)
+  const bool grouped = h->svar || h->tvar;
+  const size_t xbytes = h->svar ? h->svar->xbytes() : h->tvar ? h->tvar->xbytes() : 0;
+  const size_t ctrl_grouped = align_up(xbytes * (size_t)h->n_seq, 256);
+  const size_t members = (size_t)h->n_seq * h->group;
+  pl.mws_off = h->var ? align_up(h->var->ws_bytes * members, 256) : 0;
+  const size_t pctrl_off = align_up(pl.mws_off + h->mws_stride * members, 256);
+  const size_t ctrl_bytes = align_up((1 + (size_t)h->n_seq) * 4, 256);
+  pl.ws_bytes = h->var ? pctrl_off + (h->group > 1 ? ctrl_bytes : 0) : grouped ? ctrl_grouped + ctrl_bytes : 0;
+  pl.ctrl_off = h->var ? pctrl_off : ctrl_grouped;
+  pl.has_ctrl = grouped || h->group > 1;
+  pl.coef_bytes = (size_t)h->n_seq * h->nchunks * h->coef_stride * sizeof(float);
+  return pl;
+}
+
+static void bind_workspace(atlas_mem_s* h, const WsPlan& pl, char* ws, float* coef) {
+  h->ws = ws;
+  h->coef = coef;
+  h->mws = h->cfg.optimizer == ATLAS_OPT_MUON ? ws + pl.mws_off : nullptr;
+  h->ctrl = pl.has_ctrl ? reinterpret_cast<unsigned*>(ws + pl.ctrl_off) : nullptr;
+}
+
+// ---- workspace of the allocation-free entry point
+// One static buffer per device; host code never passes its name to a kernel:
+// the address comes from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static char* g_scratch_ptr[kMaxDevices] = {};
+
+static hipError_t scratch_of(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// *dst = the call's error word, or 0 when the call has none
+__global__ void copy_error_word(unsigned* dst, const unsigned* ctrl) {
+  if (threadIdx.x == 0) *dst = ctrl ? ctrl[0] : 0u;
+}
+
+extern "C" {
+
+atlas_status atlas_mem_supported(const atlas_mem_config* cfg) { return check_config(cfg, nullptr, nullptr, nullptr); }
+
+atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
+  if (!out) return ATLAS_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  atlas_mem_s tmp;
+  atlas_status s = setup_handle(cfg, &tmp);
+  if (s != ATLAS_OK) return s;
+  hipError_t e = hipGetDevice(&tmp.device);
+  if (e != hipSuccess) return hip_fail(e);
+  const WsPlan pl = plan_workspace(&tmp);
+  char* ws = nullptr;
+  float* coef = nullptr;
+  if (pl.ws_bytes && hipMalloc(&ws, pl.ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
-    delete h;
     return ATLAS_ERR_OUT_OF_MEMORY;
   }
-  if (coef_bytes && hipMalloc(&h->coef, coef_bytes) != hipSuccess) {
+  if (pl.coef_bytes && hipMalloc(&coef, pl.coef_bytes) != hipSuccess) {
     (void)hipGetLastError();
-    (void)hipFree(h->ws);
-    delete h;
+    (void)hipFree(ws);
     return ATLAS_ERR_OUT_OF_MEMORY;
   }
-  if (muon) h->mws = h->ws + mws_off;
-  if (h->group > 1) h->ctrl = reinterpret_cast<unsigned*>(h->ws + pctrl_off);
-  if (grouped) h->ctrl = reinterpret_cast<unsigned*>(h->ws + ctrl_off);
-  if (h->ctrl) {
-    if ((e = hipMemset(h->ctrl, 0, (1 + (size_t)h->n_seq) * 4)) != hipSuccess) {
-      (void)hipFree(h->ws);
-      (void)hipFree(h->coef);
-      delete h;
+  bind_workspace(&tmp, pl, ws, coef);
+  if (tmp.ctrl) {
+    if ((e = hipMemset(tmp.ctrl, 0, (1 + (size_t)tmp.n_seq) * 4)) != hipSuccess) {
+      (void)hipFree(ws);
+      (void)hipFree(coef);
       return hip_fail(e);
     }
+  }
+  atlas_mem_s* h = new (std::nothrow) atlas_mem_s(tmp);
+  if (!h) {
+    (void)hipFree(ws);
+    (void)hipFree(coef);
+    return ATLAS_ERR_OUT_OF_MEMORY;
   }
   *out = h;
   return ATLAS_OK;
@@ -330,10 +393,11 @@ atlas_status atlas_mem_forward(atlas_mem_t h, const void* q, const void* k, cons
   return atlas_mem_forward_ex(h, q, k, v, alpha, eta, theta, gamma, nullptr, state, out, stream);
 }
 
-atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, const void* v,
-                                  const float* alpha, const float* eta, const float* theta,
-                                  const float* gamma, const float* delta, void* state, void* out, void* stream) {
-  if (!h || h->magic != kMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+// Checks the arguments of one call and enqueues its kernels on the workspace
+// bound to h.
+static atlas_status forward_impl(const atlas_mem_s* h, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* eta, const float* theta,
+                                 const float* gamma, const float* delta, void* state, void* out, void* stream) {
   const atlas_mem_config& c = h->cfg;
   if (c.seq_len == 0) return ATLAS_OK;  // nothing to read or write; any pointer accepted
   if (!q || !k || !v || !alpha || !theta || !gamma || !state || !out) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -349,7 +413,7 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, c
     if ((uintptr_t)p % 4) return ATLAS_ERR_INVALID_ARGUMENT;
   const size_t es = c.io_dtype == ATLAS_F32 ? 4 : 2, S = (size_t)h->n_seq, N = (size_t)c.seq_len;
   const size_t out_b = S * N * c.d_v * es;
-  const size_t st_b = atlas_mem_state_bytes(h);
+  const size_t st_b = h->lay.seq_stride * (size_t)h->n_seq;
   if (overlaps(out, out_b, q, S * N * c.d_k * es) || overlaps(out, out_b, k, S * N * c.d_k * es) ||
       overlaps(out, out_b, v, S * N * c.d_v * es) || overlaps(out, out_b, state, st_b) ||
       overlaps(out, out_b, alpha, S * N * 4) || overlaps(out, out_b, theta, S * N * 4) ||
@@ -464,6 +528,38 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, c
   return ATLAS_OK;
 }
 
+atlas_status atlas_mem_forward_ex(atlas_mem_t h, const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* eta, const float* theta,
+                                  const float* gamma, const float* delta, void* state, void* out, void* stream) {
+  if (!h || h->magic != kMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+  return forward_impl(h, q, k, v, alpha, eta, theta, gamma, delta, state, out, stream);
+}
+
+atlas_status atlas_mem_forward_noalloc(const atlas_mem_config* cfg, const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* eta, const float* theta,
+                                       const float* gamma, const float* delta, void* state, void* out,
+                                       unsigned* errors, void* stream) {
+  atlas_mem_s h;
+  atlas_status s = setup_handle(cfg, &h);
+  if (s != ATLAS_OK) return s;
+  if (cfg->seq_len == 0) return ATLAS_OK;
+  if (errors && (uintptr_t)errors % 4) return ATLAS_ERR_INVALID_ARGUMENT;
+  hipError_t e = hipGetDevice(&h.device);
+  if (e != hipSuccess) return hip_fail(e);
+  const WsPlan pl = plan_workspace(&h);
+  const size_t coef_off = align_up(pl.ws_bytes, 256);
+  if (coef_off + pl.coef_bytes > kScratchBytes) return ATLAS_ERR_SCRATCH_TOO_SMALL;
+  char* base = nullptr;
+  if ((e = scratch_of(h.device, &base)) != hipSuccess) return hip_fail(e);
+  bind_workspace(&h, pl, base, reinterpret_cast<float*>(base + coef_off));
+  // the coefficient kernel clears the control words at the start of the call
+  s = forward_impl(&h, q, k, v, alpha, eta, theta, gamma, delta, state, out, stream);
+  if (s != ATLAS_OK || !errors) return s;
+  hipLaunchKernelGGL(copy_error_word, dim3(1), dim3(64), 0, (hipStream_t)stream, errors, (const unsigned*)h.ctrl);
+  e = hipGetLastError();
+  return e == hipSuccess ? ATLAS_OK : hip_fail(e);
+}
+
 atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* after) {
   if (!h || h->magic != kMagic) return ATLAS_ERR_INVALID_ARGUMENT;
   if ((before == nullptr) != (after == nullptr)) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -505,6 +601,7 @@ const char* atlas_mem_error_string(int code) {
     case ATLAS_ERR_UNSUPPORTED: return "no kernel built for this configuration";
     case ATLAS_ERR_OUT_OF_MEMORY: return "out of device memory";
     case ATLAS_ERR_HIP: return "HIP runtime error";
+    case ATLAS_ERR_SCRATCH_TOO_SMALL: return "the call needs more workspace than the static scratch buffer holds";
     default: return "unknown status";
   }
 }
