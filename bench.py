@@ -41,7 +41,7 @@ MEASURED_TRAFFIC = {
 
 # translation unit of each recurrent kernel
 KERNEL_SOURCE = {"stream_mlp_kernel": "atlas_mem_stream.hip", "sharded_mlp_kernel": "atlas_mem_sharded.hip",
-                 "chunk_kernel": "atlas_mem_kernels.hip"}
+                 "chunk_kernel": "atlas_mem_kernels.hip", "grouped_kernel": "atlas_mem_grouped.hip"}
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -145,7 +145,8 @@ def kernel_name(binding, wl, family):
     """Name of the recurrent kernel a call runs for this workload and family."""
     if family == "auto":
         family = binding.AtlasMem(wl, "auto").family()
-    return {"sharded": "sharded_mlp_kernel", "streamed": "stream_mlp_kernel", "per_sequence": "chunk_kernel"}[family]
+    return {"sharded": "sharded_mlp_kernel", "streamed": "stream_mlp_kernel", "per_sequence": "chunk_kernel",
+            "grouped": "grouped_kernel"}[family]
 
 
 def bench_prologue(args, wl):
@@ -210,7 +211,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="layer_scale")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "per_sequence", "sharded", "streamed"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "per_sequence", "sharded", "streamed", "grouped"])
     ap.add_argument("--bias", default=None, choices=["l2", "dot", "lp", "huber"],
                     help="attentional bias (default: the workload's own)")
     ap.add_argument("--bias-p", type=float, default=3.0, help="p of the l_p bias")

@@ -89,10 +89,16 @@ enum { ATLAS_OPT_GD = 0, ATLAS_OPT_MUON = 1 };
  * units), the fp32 weights and momentum read and written once per chunk in
  * one fused pass.  SHARDED and STREAMED serve the MLP memory with the
  * identity feature map, d_k == d_v and bf16 io (SHARDED: the l2 and
- * dot-product biases and no layer norm).  AUTO picks the fastest
- * family measured for the shape: STREAMED where marked so (large hidden
- * layers), else SHARDED, else STREAMED, else PER_SEQUENCE.                 */
-enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3 };
+ * dot-product biases and no layer norm).  GROUPED: the hidden units of each
+ * sequence split over a group of workgroups of one XCD (16 per workgroup),
+ * weights resident in registers, phi of every key and query computed once
+ * per call into the workspace; the MLP memory on any feature map with the
+ * l2 or dot-product bias, bf16 io, chunk 64, c <= 64, no layer norm, no
+ * gated memory, gradient descent.  AUTO picks the fastest family measured
+ * for the shape: STREAMED where marked so (large hidden layers), else
+ * SHARDED, else STREAMED, else GROUPED, else PER_SEQUENCE.                 */
+enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3,
+       ATLAS_KERNEL_GROUPED = 4 };
 
 typedef struct {
   int batch, heads;   /* B, H: B*H independent sequences                        */
@@ -231,13 +237,15 @@ atlas_status atlas_mem_forward_noalloc(const atlas_mem_config* cfg,
  * Errors: INVALID_ARGUMENT (bad handle, exactly one event NULL).           */
 atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* after);
 
-/* Kernel family the handle runs (ATLAS_KERNEL_PER_SEQUENCE, _SHARDED or
- * _STREAMED; AUTO is resolved at init).  Returns -1 for an invalid handle.  */
+/* Kernel family the handle runs (ATLAS_KERNEL_PER_SEQUENCE, _SHARDED,
+ * _STREAMED or _GROUPED; AUTO is resolved at init).  Returns -1 for an
+ * invalid handle.                                                           */
 int atlas_mem_kernel_family(atlas_mem_t h);
 
 /* Device-side error word of the handle's last forward call (0: none; bit 0:
- * a group barrier of the sharded or the streamed kernel timed out, its
- * outputs are invalid).
+ * a group barrier of the sharded, streamed or grouped kernel timed out, its
+ * outputs are invalid; bit 1: the workgroups of one grouped-kernel sequence
+ * did not all run on one XCD, so their exchanges were not ordered).
  * Synchronises the device.  Errors: INVALID_ARGUMENT, HIP.                 */
 atlas_status atlas_mem_device_errors(atlas_mem_t h, unsigned* flags);
 

@@ -26,7 +26,7 @@ MEM = {"linear": 0, "mlp": 1}
 PHI = {"identity": 0, "poly2": 1, "raw_poly2": 2}
 BIAS = {"l2": 0, "dot": 1, "lp": 2, "huber": 3}
 IO = {"bf16": 0, "f32": 1}
-KERNEL = {"auto": 0, "per_sequence": 1, "sharded": 2, "streamed": 3}
+KERNEL = {"auto": 0, "per_sequence": 1, "sharded": 2, "streamed": 3, "grouped": 4}
 OPTIMIZER = {"gd": 0, "muon": 1}
 TORCH_IO = {"bf16": torch.bfloat16, "f32": torch.float32}
 

@@ -63,6 +63,22 @@ static const StreamVariant kStreamed[] = {
 };
 #undef ATLAS_STREAMED
 
+typedef hipError_t (*GroupedLaunchFn)(const GroupedParams&, const CoeffParams&, hipStream_t, hipEvent_t, hipEvent_t);
+
+struct GroupedVariant {
+  const char* name;
+  int phi, dk, pd, dv, h, g;
+  size_t (*seq_bytes)(int);
+  GroupedLaunchFn launch;
+};
+
+#define ATLAS_GROUPED(NAME, PHI, DK, PD, DV, H, G) \
+  {#NAME, PHI, DK, PD, DV, H, G, &grouped_seq_bytes<PHI, DK, PD, DV, H, G>, &launch_grouped<PHI, DK, PD, DV, H, G>},
+static const GroupedVariant kGrouped[] = {
+#include "atlas_mem_grouped_variants.inc"
+};
+#undef ATLAS_GROUPED
+
 }  // namespace atlas
 
 using namespace atlas;
@@ -72,7 +88,8 @@ struct atlas_mem_s {
   atlas_mem_config cfg;
   const Variant* var;           // per-sequence kernel, or
   const ShardedVariant* svar;   // sharded kernel, or
-  const StreamVariant* tvar;    // streamed-state kernel
+  const StreamVariant* tvar;    // streamed-state kernel, or
+  const GroupedVariant* gvar;   // grouped kernel (wide feature maps)
   unsigned* ctrl;               // sharded: error word + barrier counters
   atlas_mem_state_layout lay;
   int n_seq, nchunks, coef_stride, device;
@@ -134,9 +151,25 @@ static const StreamVariant* find_streamed(const atlas_mem_config* c) {
   return best;
 }
 
-// Exactly one of *out, *sout, *tout is set on success.
+static const GroupedVariant* find_grouped(const atlas_mem_config* c) {
+  if (c->memory != ATLAS_MEM_MLP || c->io_dtype != ATLAS_BF16 || c->optimizer != ATLAS_OPT_GD) return nullptr;
+  if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
+  if (c->mlp_layernorm || c->mlp_gated) return nullptr;
+  if (c->chunk != 64 || c->window > 64) return nullptr;
+  for (const GroupedVariant& v : kGrouped) {
+    if (v.phi != c->feature_map || v.dk != c->d_k || v.pd != pd_of(c) || v.dv != c->d_v || v.h != c->mlp_hidden)
+      continue;
+    // the kernels address one sequence's workspace through 32-bit offsets
+    const int nch = (c->seq_len + c->chunk - 1) / c->chunk;
+    if (v.seq_bytes(nch) >= (1u << 31)) return nullptr;
+    return &v;
+  }
+  return nullptr;
+}
+
+// Exactly one of *out, *sout, *tout, *gout is set on success.
 static atlas_status check_config(const atlas_mem_config* c, const Variant** out, const ShardedVariant** sout,
-                                 const StreamVariant** tout) {
+                                 const StreamVariant** tout, const GroupedVariant** gout) {
   if (!c) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->batch < 1 || c->heads < 1 || c->seq_len < 0 || c->d_k < 1 || c->d_v < 1) return ATLAS_ERR_INVALID_ARGUMENT;
   if (c->window < 1 || c->chunk < 1) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -166,10 +199,11 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   // sequences x chunks must fit one grid dimension of the coefficient kernel
   const long n_seq = (long)c->batch * c->heads;
   if (n_seq > (1L << 20) || n_seq * ((c->seq_len + c->chunk - 1) / c->chunk) > 0x7fffffffL) return ATLAS_ERR_INVALID_ARGUMENT;
-  if (c->kernel < ATLAS_KERNEL_AUTO || c->kernel > ATLAS_KERNEL_STREAMED) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (c->kernel < ATLAS_KERNEL_AUTO || c->kernel > ATLAS_KERNEL_GROUPED) return ATLAS_ERR_INVALID_ARGUMENT;
   if (out) *out = nullptr;
   if (sout) *sout = nullptr;
   if (tout) *tout = nullptr;
+  if (gout) *gout = nullptr;
   // Muon: the per-sequence family, plain linear or MLP memory
   if (muon && (c->mlp_layernorm || c->mlp_gated || (c->kernel != ATLAS_KERNEL_AUTO && c->kernel != ATLAS_KERNEL_PER_SEQUENCE)))
     return ATLAS_ERR_UNSUPPORTED;
@@ -182,7 +216,7 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
     }
     if (c->kernel == ATLAS_KERNEL_STREAMED) return ATLAS_ERR_UNSUPPORTED;
   }
-  if (!muon && c->kernel != ATLAS_KERNEL_PER_SEQUENCE) {
+  if (!muon && c->kernel != ATLAS_KERNEL_PER_SEQUENCE && c->kernel != ATLAS_KERNEL_GROUPED) {
     const ShardedVariant* sv = find_sharded(c);
     if (sv) {
       if (sout) *sout = sv;
@@ -195,6 +229,15 @@ static atlas_status check_config(const atlas_mem_config* c, const Variant** out,
   if (c->kernel == ATLAS_KERNEL_AUTO && tv) {
     if (tout) *tout = tv;
     return ATLAS_OK;
+  }
+  // wide feature maps: the grouped family
+  if (!muon && (c->kernel == ATLAS_KERNEL_AUTO || c->kernel == ATLAS_KERNEL_GROUPED)) {
+    const GroupedVariant* gv = find_grouped(c);
+    if (gv) {
+      if (gout) *gout = gv;
+      return ATLAS_OK;
+    }
+    if (c->kernel == ATLAS_KERNEL_GROUPED) return ATLAS_ERR_UNSUPPORTED;
   }
   const int h = c->memory == ATLAS_MEM_MLP ? c->mlp_hidden : 0;
   const int need_w = c->chunk + c->window - 1;
@@ -236,7 +279,8 @@ static atlas_status setup_handle(const atlas_mem_config* cfg, atlas_mem_s* h) {
   const Variant* var = nullptr;
   const ShardedVariant* svar = nullptr;
   const StreamVariant* tvar = nullptr;
-  atlas_status s = check_config(cfg, &var, &svar, &tvar);
+  const GroupedVariant* gvar = nullptr;
+  atlas_status s = check_config(cfg, &var, &svar, &tvar, &gvar);
   if (s != ATLAS_OK) return s;
   *h = atlas_mem_s();
   h->magic = kMagic;
@@ -244,13 +288,15 @@ static atlas_status setup_handle(const atlas_mem_config* cfg, atlas_mem_s* h) {
   h->var = var;
   h->svar = svar;
   h->tvar = tvar;
+  h->gvar = gvar;
   h->ctrl = nullptr;
   h->lay = make_layout(cfg);
   h->n_seq = cfg->batch * cfg->heads;
   h->nchunks = (cfg->seq_len + cfg->chunk - 1) / cfg->chunk;
   h->coef_stride = var ? coef_stride(var->bc, var->wp)
                  : svar ? coef_stride(svar->bc, svar->wp, true)
-                        : coef_stride(tvar->bc, tvar->wp, true, true);
+                 : tvar ? coef_stride(tvar->bc, tvar->wp, true, true)
+                        : coef_stride(64, 128, true);
   h->device = -1;
   h->ws = nullptr;
   h->coef = nullptr;
@@ -278,8 +324,11 @@ static WsPlan plan_workspace(const atlas_mem_s* h) {
   WsPlan pl;
   // sharded, and streamed: exchange buffers / tile-major state per sequence,
   // then the control words (error word + one barrier counter per sequence)
-  const bool grouped = h->svar || h->tvar;
-  const size_t xbytes = h->svar ? h->svar->xbytes() : h->tvar ? h->tvar->xbytes() : 0;
+  const bool grouped = h->svar || h->tvar || h->gvar;
+  const size_t xbytes = h->svar   ? h->svar->xbytes()
+                        : h->tvar ? h->tvar->xbytes()
+                        : h->gvar ? h->gvar->seq_bytes(h->nchunks)
+                                  : 0;
   const size_t ctrl_grouped = align_up(xbytes * (size_t)h->n_seq, 256);
   const size_t members = (size_t)h->n_seq * h->group;
   pl.mws_off = h->var ? align_up(h->var->ws_bytes * members, 256) : 0;
@@ -330,7 +379,9 @@ __global__ void copy_error_word(unsigned* dst, const unsigned* ctrl) {
 
 extern "C" {
 
-atlas_status atlas_mem_supported(const atlas_mem_config* cfg) { return check_config(cfg, nullptr, nullptr, nullptr); }
+atlas_status atlas_mem_supported(const atlas_mem_config* cfg) {
+  return check_config(cfg, nullptr, nullptr, nullptr, nullptr);
+}
 
 atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   if (!out) return ATLAS_ERR_INVALID_ARGUMENT;
@@ -445,6 +496,38 @@ static atlas_status forward_impl(const atlas_mem_s* h, const void* q, const void
   kp.seq_stride = h->lay.seq_stride;
   kp.off_count = h->lay.count;
 
+  if (h->gvar) {
+    GroupedParams gp;
+    gp.q = q;
+    gp.k = k;
+    gp.v = v;
+    gp.gamma = gamma;
+    gp.state = (char*)state;
+    gp.out = out;
+    gp.gws = h->ws;
+    gp.gseq_bytes = h->gvar->seq_bytes(h->nchunks);
+    gp.ctrl = h->ctrl;
+    gp.coef = h->coef;
+    gp.n_seq = h->n_seq;
+    gp.N = c.seq_len;
+    gp.c = c.window;
+    gp.nchunks = h->nchunks;
+    gp.coef_stride = h->coef_stride;
+    gp.seq_stride = h->lay.seq_stride;
+    gp.off_weights = h->lay.weights;
+    gp.off_momentum = h->lay.momentum;
+    gp.off_halo_k = h->lay.halo_k;
+    gp.off_halo_v = h->lay.halo_v;
+    gp.off_halo_g = h->lay.halo_g;
+    gp.off_count = h->lay.count;
+    gp.grad_scale = c.grad_scale;
+    gp.momentum = c.momentum;
+    gp.bias = c.bias;
+    gp.residual = c.mlp_residual;
+    e = h->gvar->launch(gp, kp, (hipStream_t)stream, h->ev_before, h->ev_after);
+    if (e != hipSuccess) return hip_fail(e);
+    return ATLAS_OK;
+  }
   if (h->svar || h->tvar) {
     ShardedParams sp;
     sp.q = q;
@@ -570,7 +653,8 @@ atlas_status atlas_mem_set_kernel_events(atlas_mem_t h, void* before, void* afte
 
 int atlas_mem_kernel_family(atlas_mem_t h) {
   if (!h || h->magic != kMagic) return -1;
-  return h->var ? ATLAS_KERNEL_PER_SEQUENCE : h->svar ? ATLAS_KERNEL_SHARDED : ATLAS_KERNEL_STREAMED;
+  return h->var ? ATLAS_KERNEL_PER_SEQUENCE : h->svar ? ATLAS_KERNEL_SHARDED : h->tvar ? ATLAS_KERNEL_STREAMED
+                                                                                    : ATLAS_KERNEL_GROUPED;
 }
 
 atlas_status atlas_mem_device_errors(atlas_mem_t h, unsigned* flags) {

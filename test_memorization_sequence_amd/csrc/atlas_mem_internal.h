@@ -210,6 +210,32 @@ struct ShardedParams {
   int gated;       // MLP: f = r + W2 (gelu(W1 x) .* (W3 x)) (per-sequence kernel)
 };
 
+// Grouped MLP kernel family (wide feature maps): G workgroups of one XCD per
+// sequence, 16 hidden units each; phi of every key and query precomputed per
+// call into the workspace (gws, gseq_bytes per sequence).
+struct GroupedParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gamma;
+  char* state;
+  void* out;
+  char* gws;        // per sequence: exchange buffers, then the phi buffers
+  size_t gseq_bytes;
+  unsigned* ctrl;   // [0] error word, [1 + s] barrier counter of sequence s
+  float* coef;      // the Q1 kernel writes Q1 into the coefficient blocks
+  int n_seq, N, c, nchunks, coef_stride;
+  size_t seq_stride, off_weights, off_momentum, off_halo_k, off_halo_v, off_halo_g, off_count;
+  float grad_scale;
+  int momentum, bias, residual;
+};
+
+template <int PHI, int DK, int PD, int DV, int H, int G>
+hipError_t launch_grouped(const GroupedParams& gp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
+                          hipEvent_t ev1);
+template <int PHI, int DK, int PD, int DV, int H, int G>
+size_t grouped_seq_bytes(int nchunks);
+
 template <int D, int DV, int H, int G, int WP, int BC>
 hipError_t launch_sharded(const ShardedParams& sp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
                           hipEvent_t ev1);

@@ -52,7 +52,7 @@ def test_enum_fields_are_checked():
     c = _cfg()
     c.grad_scale = float("nan")
     assert binding.supported(c) == binding.ERR_INVALID
-    for bad in (4, 7, -1):
+    for bad in (5, 7, -1):
         c = _cfg()
         c.kernel = bad
         assert binding.supported(c) == binding.ERR_INVALID
@@ -72,6 +72,15 @@ def test_kernel_family_selection():
         assert binding.supported(binding.config_of(WORKLOADS[name], "streamed")) == ok
     for name in ("atlas_long", "linear_poly2", "linear64_delta"):
         assert binding.supported(binding.config_of(WORKLOADS[name], "streamed")) == binding.ERR_UNSUPPORTED
+    # grouped family: the MLP memories (any feature map, chunk 64, c <= 64, l2 / dot bias)
+    for name in ("atlas_long", "layer_scale", "mlp64"):
+        assert binding.supported(binding.config_of(WORKLOADS[name], "grouped")) == ok, name
+    for name in ("linear_poly2", "linear64_delta"):
+        assert binding.supported(binding.config_of(WORKLOADS[name], "grouped")) == binding.ERR_UNSUPPORTED
+    for wl in (replace(WORKLOADS["atlas_long"], bias="lp", bias_p=3.0), replace(WORKLOADS["atlas_long"], layernorm=True),
+               replace(WORKLOADS["atlas_long"], gated=True), replace(WORKLOADS["atlas_long"], optimizer="muon"),
+               replace(WORKLOADS["atlas_long"], chunk=32, window=32)):
+        assert binding.supported(binding.config_of(wl, "grouped")) == binding.ERR_UNSUPPORTED
 
 
 def test_other_attentional_biases():

@@ -58,7 +58,7 @@ SMALL_N = 3 * 64 + 17   # three full chunks and a ragged tail
 # explicitly, the streamed families
 GROUPED = [n for n in ORDER if WORKLOADS[n].memory == "mlp" and WORKLOADS[n].feature_map == "identity"]
 CASES = ([(n, "auto") for n in ORDER] + [(n, "per_sequence") for n in ORDER if WORKLOADS[n].memory == "mlp"]
-         + [(n, k) for n in GROUPED for k in ("sharded", "streamed")])
+         + [(n, k) for n in GROUPED for k in ("sharded", "streamed", "grouped")])
 
 
 @pytest.mark.parametrize("recipe", ["preset", "lively"])
@@ -81,7 +81,8 @@ def test_parity_small(B, name, kernel, recipe):
 
 
 @pytest.mark.parametrize("name,kernel", [("linear_poly2", "auto"), ("mlp64", "sharded"), ("layer_scale", "sharded"),
-                                         ("atlas_long", "auto"), ("mlp64", "streamed"), ("layer_scale", "streamed")])
+                                         ("atlas_long", "auto"), ("mlp64", "streamed"), ("layer_scale", "streamed"),
+                                         ("atlas_long", "per_sequence"), ("layer_scale", "grouped")])
 def test_streaming_split_is_bitwise_equal(B, name, kernel):
     """Two calls with a chunk-aligned split equal one call, bit for bit."""
     binding, H = B
@@ -106,7 +107,7 @@ def test_streaming_split_is_bitwise_equal(B, name, kernel):
     assert torch.equal(st1, st2)
 
 
-@pytest.mark.parametrize("kernel", ["sharded", "streamed"])
+@pytest.mark.parametrize("kernel", ["sharded", "streamed", "grouped"])
 def test_deterministic(B, kernel):
     binding, H = B
     wl = lively(WORKLOADS["layer_scale"].with_shape(batch=1, heads=3, seq_len=SMALL_N))
@@ -125,7 +126,8 @@ def test_deterministic(B, kernel):
 
 @pytest.mark.parametrize("n", [0, 1, 37, 64, 65])
 @pytest.mark.parametrize("name,kernel", [("linear64_delta", "auto"), ("mlp64", "sharded"), ("layer_scale", "sharded"),
-                                         ("mlp64", "streamed"), ("layer_scale", "streamed")])
+                                         ("mlp64", "streamed"), ("layer_scale", "streamed"), ("atlas_long", "auto"),
+                                         ("mlp64", "grouped")])
 def test_short_and_empty_calls(B, name, kernel, n):
     """N = 0 leaves the state alone; N < chunk is one partial chunk."""
     binding, H = B
@@ -145,7 +147,7 @@ def test_short_and_empty_calls(B, name, kernel, n):
     assert r["halo_exact"] and r["count_exact"], r
 
 
-@pytest.mark.parametrize("kernel", ["sharded", "streamed"])
+@pytest.mark.parametrize("kernel", ["sharded", "streamed", "grouped"])
 def test_alpha_one_erases_exactly(B, kernel):
     """alpha = 1, theta = 0: weights become exactly zero and y = q exactly."""
     binding, H = B
@@ -181,7 +183,8 @@ def test_theta_zero_keeps_weights_exactly(B):
     assert H.rel_l2(out.float().cpu().numpy().reshape(out_o.shape), out_o) <= 2e-2
 
 
-@pytest.mark.parametrize("name,kernel", [(n, "auto") for n in ORDER] + [(n, "sharded") for n in GROUPED])
+@pytest.mark.parametrize("name,kernel", [(n, "auto") for n in ORDER] + [(n, "sharded") for n in GROUPED]
+                         + [(n, "grouped") for n in GROUPED])
 def test_full_size_sampled(B, name, kernel):
     """Full shapes in the benchmark's launch configuration; the oracle replays
     the first two chunks of the first and last sequence."""
@@ -228,7 +231,7 @@ def test_forward_rejects_bad_arguments(B):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("kernel", ["sharded", "streamed"])
+@pytest.mark.parametrize("kernel", ["sharded", "streamed", "grouped"])
 @pytest.mark.parametrize("name", ["mlp64", "layer_scale"])
 def test_window_wider_than_one_chunk_row_block(B, name, kernel):
     """c = 33 on the mlp64 shape (window 96 rows) and c = 17 on layer_scale."""
@@ -256,7 +259,7 @@ def test_kernel_families_agree(B):
     inputs, w0 = H.prepare(wl)
     dev = H.to_device(wl, inputs)
     outs = []
-    for kernel in ("sharded", "per_sequence", "streamed"):
+    for kernel in ("sharded", "per_sequence", "streamed", "grouped"):
         mem = binding.AtlasMem(wl, kernel)
         assert mem.family() == kernel
         st = mem.new_state(torch.from_numpy(w0))
