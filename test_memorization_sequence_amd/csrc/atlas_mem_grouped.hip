@@ -94,8 +94,15 @@ struct GShape {
   static constexpr size_t oD1T = oD2 + align_up(WP * LV * 2, 256);   // D1^T [16][LT]
   static constexpr size_t oAh = oD1T + align_up(HL * LT * 2, 256);   // Ahat [BC][LU]
   static constexpr size_t oQ2 = oAh + align_up(BC * LU * 2, 256);    // Q2 [BC][LT]
-  static constexpr size_t oF = oQ2 + align_up(BC * LT * 2, 256);     // cA[BC] cB[BC] cM[WP] cS[WP] P
+  static constexpr size_t oC = oQ2 + align_up(BC * LT * 2, 256);     // C [BC][WP] f32 (coefficient block)
+  static constexpr size_t oF = oC + BC * WP * 4;                      // cA[BC] cB[BC] cM[WP] cS[WP] P
   static constexpr size_t lds = oF + (2 * BC + 2 * WP + 4) * 4;
+  // the reduce-scatter and the output reduction split their partial sums over
+  // all 256 threads: NPAIR (row, 4 values) pairs, G / NSPLIT partials per thread
+  static constexpr int NPAIR = RW * (DV / 4), NSPLIT = 256 / NPAIR;
+  static constexpr int NPAIR_O = RQ * (DV / 4), NSPLIT_O = 256 / NPAIR_O;
+  static_assert(256 % NPAIR == 0 && G % NSPLIT == 0 && 256 % NPAIR_O == 0 && G % NSPLIT_O == 0, "split");
+  static_assert((NSPLIT - 1) * NPAIR * 16 + (NSPLIT_O - 1) * NPAIR_O * 16 <= BC * LT * 2, "combine scratch in Q2");
   static_assert(lds <= 163840, "LDS budget of one CU");
   // exchange workspace per sequence (bytes)
   static constexpr size_t xY = 0;                                          // [2][G][WP][DV] f32
@@ -298,6 +305,8 @@ grouped_kernel(GroupedParams p) {
   bf16* D1T = reinterpret_cast<bf16*>(smem + S::oD1T);
   bf16* Ah = reinterpret_cast<bf16*>(smem + S::oAh);
   bf16* Q2 = reinterpret_cast<bf16*>(smem + S::oQ2);
+  float* Cl = reinterpret_cast<float*>(smem + S::oC);
+  float4* comb = reinterpret_cast<float4*>(smem + S::oQ2);   // partial-sum scratch (Q2 is dead then)
   float* cA = reinterpret_cast<float*>(smem + S::oF);
   float* cB = cA + BC;
   float* cM = cB + BC;
@@ -351,25 +360,35 @@ grouped_kernel(GroupedParams p) {
   };
   write_images();
 
-  // reduce the retrieval partials of chunk pc (query rows owned by this member) into out
+  // reduce the retrieval partials of chunk pc (query rows owned by this member)
+  // into out: NSPLIT_O threads per (row, 4 values), each over G / NSPLIT_O
+  // partials, combined through LDS
   auto reduce_out = [&](int pc) {
+    constexpr int NP = S::NPAIR_O, NS = S::NSPLIT_O, PER = G / NS;
     const int pt0 = pc * BC, pte = min(N, pt0 + BC) - 1;
-    if (tid < RQ * (DV / 4)) {
-      const int qq = pm * RQ + tid / (DV / 4), o4 = (tid % (DV / 4)) * 4;
-      if (pt0 + qq <= pte) {
-        const float* yo = yobuf + (size_t)(pc & 1) * G * BC * DV;
-        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (res) {
-          const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(q + (size_t)(pt0 + qq) * DK + o4);
-          y = make_float4((float)r4[0], (float)r4[1], (float)r4[2], (float)r4[3]);
-        }
-#pragma unroll 8
-        for (int pp = 0; pp < G; ++pp) {
-          const float4 part = *reinterpret_cast<const float4*>(yo + ((size_t)pp * BC + qq) * DV + o4);
-          y.x += part.x; y.y += part.y; y.z += part.z; y.w += part.w;
-        }
-        *reinterpret_cast<bf16x4*>(out + (size_t)(pt0 + qq) * DV + o4) = bf16x4{(bf16)y.x, (bf16)y.y, (bf16)y.z, (bf16)y.w};
+    const int e = tid % NP, h = tid / NP;
+    const int qq = pm * RQ + e / (DV / 4), o4 = (e % (DV / 4)) * 4;
+    const float* yo = yobuf + (size_t)(pc & 1) * G * BC * DV + (size_t)qq * DV + o4;
+    float4 part[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) part[u] = *reinterpret_cast<const float4*>(yo + (size_t)(h * PER + u) * BC * DV);
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) { y.x += part[u].x; y.y += part[u].y; y.z += part[u].z; y.w += part[u].w; }
+    float4* cmb = comb + (S::NSPLIT - 1) * S::NPAIR;
+    if (h > 0) cmb[(h - 1) * NP + e] = y;
+    __syncthreads();
+    if (h == 0 && pt0 + qq <= pte) {
+#pragma unroll
+      for (int u = 1; u < NS; ++u) {
+        const float4 o = cmb[(u - 1) * NP + e];
+        y.x += o.x; y.y += o.y; y.z += o.z; y.w += o.w;
       }
+      if (res) {
+        const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(q + (size_t)(pt0 + qq) * DK + o4);
+        y.x += (float)r4[0]; y.y += (float)r4[1]; y.z += (float)r4[2]; y.w += (float)r4[3];
+      }
+      *reinterpret_cast<bf16x4*>(out + (size_t)(pt0 + qq) * DV + o4) = bf16x4{(bf16)y.x, (bf16)y.y, (bf16)y.z, (bf16)y.w};
     }
   };
 
@@ -383,20 +402,39 @@ grouped_kernel(GroupedParams p) {
     const float* Cc = coef + 2 * BC + 4 + 2 * WP;                                    // [BC][WP] f32
     const bf16* Q1g = reinterpret_cast<const bf16*>(coef + 2 * BC + 4 + 2 * WP + BC * WP);   // [BC][WP]
 
-    // ---- coefficients of the chunk
+    // ---- coefficients of the chunk; C straight into LDS (complete after the
+    // first group barrier's wait for every memory access)
+    {
+      const __amdgpu_buffer_rsrc_t rc = buffer_of(Cc, (unsigned)(BC * WP * 4));
+      rows_to_lds<16, BC, WP * 4, WP * 4, 4>(rc, reinterpret_cast<char*>(Cl), fresh(wave), fresh(lane),
+                                            [&](int row) { return row * WP * 4; });
+    }
     if (tid < BC) { cA[tid] = coef[tid]; cB[tid] = coef[BC + tid]; }
     if (tid < WP) { cM[tid] = coef[2 * BC + 4 + tid]; cS[tid] = coef[2 * BC + 4 + WP + tid]; }
     if (tid == 0) cP[0] = coef[2 * BC];
     __syncthreads();   // (also: the images of the previous update are complete)
 
-    // ---- forward Z = X W1^T  [rows R0.. (2 tiles) x 16 units], K = DP
+    // ---- forward Z = X W1^T  [rows R0.. (2 tiles) x 16 units], K = DP; the
+    // X fragments of step s + PF are loaded before step s computes
     f32x4 Z[2] = {zero4(), zero4()};
-#pragma unroll 4
-    for (int s = 0; s < DP / 32; ++s) {
-      const bf16x8 bw = ld_nat(W1i, LF, 0, 32 * s, lane);
+    {
+      constexpr int NS = DP / 32, PF = 5;
+      bf16x8 xf[PF + 1][2];
+      auto load = [&](int st, bf16x8* dst) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        Z[mt] = mma(gload8(rxr, ((t0 + R0 + 16 * mt + c16) * DP + 32 * s + 8 * g) * 2), bw, Z[mt]);
+        for (int mt = 0; mt < 2; ++mt) dst[mt] = gload8(rxr, ((t0 + R0 + 16 * mt + c16) * DP + 32 * st + 8 * g) * 2);
+      };
+#pragma unroll
+      for (int st = 0; st < PF && st < NS; ++st) load(st, xf[st]);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        if (st + PF < NS) load(st + PF, xf[(st + PF) % (PF + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 bw = ld_nat(W1i, LF, 0, 32 * st, lane);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) Z[mt] = mma(xf[st % (PF + 1)][mt], bw, Z[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     f32x4 GP[2];   // gelu'(Z)
 #pragma unroll
@@ -412,7 +450,9 @@ grouped_kernel(GroupedParams p) {
       }
     __syncthreads();
 
-    // ---- partial window forward Y_p = A W2_p^T  [rows R0.. x DV], K = 16 units
+    // ---- partial window forward Y_p = A W2_p^T  [rows R0.. x DV], K = 16 units,
+    // computed transposed (W2_p A^T) so that each lane holds four adjacent
+    // values of one row: one 16-byte store per tile
     {
       const int yb = ((sl * G + pm) * WP) * DV * 4;
 #pragma unroll
@@ -420,9 +460,8 @@ grouped_kernel(GroupedParams p) {
         const bf16x4 a = *reinterpret_cast<const bf16x4*>(Al + (R0 + 16 * mt + c16) * LU + 4 * g);
 #pragma unroll
         for (int nt = 0; nt < DV / 16; ++nt) {
-          const f32x4 y = mma16(a, ld_tr16(W2i, LV, 16 * nt, 0, lane), zero4());
-#pragma unroll
-          for (int r = 0; r < 4; ++r) gstore1(y[r], rxy, yb + ((R0 + 16 * mt + 4 * g + r) * DV + 16 * nt + c16) * 4);
+          const f32x4 y = mma16(ld_tr16(W2i, LV, 16 * nt, 0, lane), a, zero4());
+          buf_store4(y, rxy, yb + ((R0 + 16 * mt + c16) * DV + 16 * nt + 4 * g) * 4, 0);
         }
       }
     }
@@ -433,44 +472,55 @@ grouped_kernel(GroupedParams p) {
     }
 
     // ---- reduce-scatter: this member's window rows -> D2 rows; the previous chunk's outputs
-    if (tid < RW * (DV / 4)) {
-      const int w = pm * RW + tid / (DV / 4), o4 = (tid % (DV / 4)) * 4;
-      const float* yb = ybuf + (size_t)sl * G * WP * DV;
+    {
+      constexpr int NP = S::NPAIR, NS = S::NSPLIT, PER = G / NS;
+      const int e = tid % NP, h = tid / NP;
+      const int w = pm * RW + e / (DV / 4), o4 = (e % (DV / 4)) * 4;
       float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
       if (!dot) {
-#pragma unroll 8
-        for (int pp = 0; pp < G; ++pp) {
-          const float4 part = *reinterpret_cast<const float4*>(yb + ((size_t)pp * WP + w) * DV + o4);
-          y.x += part.x; y.y += part.y; y.z += part.z; y.w += part.w;
-        }
+        const float* yb = ybuf + (size_t)sl * G * WP * DV + (size_t)w * DV + o4;
+        float4 part[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) part[u] = *reinterpret_cast<const float4*>(yb + (size_t)(h * PER + u) * WP * DV);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) { y.x += part[u].x; y.y += part[u].y; y.z += part[u].z; y.w += part[u].w; }
       }
-      const int i = t0 - (c - 1) + w;
-      float4 pv = make_float4(0.f, 0.f, 0.f, 0.f), pr = pv;
-      float pg = 0.f;
-      if (w < W && i >= -halo_valid && i <= te) {
-        if (i >= 0) {
-          const bf16x4 vv = *reinterpret_cast<const bf16x4*>(v + (size_t)i * DV + o4);
-          pv = make_float4((float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]);
-          if (res) {
-            const bf16x4 rr = *reinterpret_cast<const bf16x4*>(k + (size_t)i * DK + o4);
-            pr = make_float4((float)rr[0], (float)rr[1], (float)rr[2], (float)rr[3]);
+      if (h > 0) comb[(h - 1) * NP + e] = y;
+      __syncthreads();
+      if (h == 0) {
+#pragma unroll
+        for (int u = 1; u < NS; ++u) {
+          const float4 o = comb[(u - 1) * NP + e];
+          y.x += o.x; y.y += o.y; y.z += o.z; y.w += o.w;
+        }
+        const int i = t0 - (c - 1) + w;
+        float4 pv = make_float4(0.f, 0.f, 0.f, 0.f), pr = pv;
+        float pg = 0.f;
+        if (w < W && i >= -halo_valid && i <= te) {
+          if (i >= 0) {
+            const bf16x4 vv = *reinterpret_cast<const bf16x4*>(v + (size_t)i * DV + o4);
+            pv = make_float4((float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]);
+            if (res) {
+              const bf16x4 rr = *reinterpret_cast<const bf16x4*>(k + (size_t)i * DK + o4);
+              pr = make_float4((float)rr[0], (float)rr[1], (float)rr[2], (float)rr[3]);
+            }
+            pg = gam_in[i];
+          } else {
+            pv = *reinterpret_cast<const float4*>(hv + (c - 1 + i) * DV + o4);
+            if (res) pr = *reinterpret_cast<const float4*>(hk + (c - 1 + i) * DK + o4);
+            pg = hg[c - 1 + i];
           }
-          pg = gam_in[i];
-        } else {
-          pv = *reinterpret_cast<const float4*>(hv + (c - 1 + i) * DV + o4);
-          if (res) pr = *reinterpret_cast<const float4*>(hk + (c - 1 + i) * DK + o4);
-          pg = hg[c - 1 + i];
         }
+        const float sg = s_grad * pg;
+        bf16x4 d4;
+        if (dot) {
+          d4 = bf16x4{(bf16)(-sg * pv.x), (bf16)(-sg * pv.y), (bf16)(-sg * pv.z), (bf16)(-sg * pv.w)};
+        } else {
+          d4 = bf16x4{(bf16)(sg * (pr.x + y.x - pv.x)), (bf16)(sg * (pr.y + y.y - pv.y)),
+                      (bf16)(sg * (pr.z + y.z - pv.z)), (bf16)(sg * (pr.w + y.w - pv.w))};
+        }
+        *reinterpret_cast<bf16x4*>(d2buf + ((size_t)sl * WP + w) * DV + o4) = d4;
       }
-      const float sg = s_grad * pg;
-      bf16x4 d4;
-      if (dot) {
-        d4 = bf16x4{(bf16)(-sg * pv.x), (bf16)(-sg * pv.y), (bf16)(-sg * pv.z), (bf16)(-sg * pv.w)};
-      } else {
-        d4 = bf16x4{(bf16)(sg * (pr.x + y.x - pv.x)), (bf16)(sg * (pr.y + y.y - pv.y)),
-                    (bf16)(sg * (pr.z + y.z - pv.z)), (bf16)(sg * (pr.w + y.w - pv.w))};
-      }
-      *reinterpret_cast<bf16x4*>(d2buf + ((size_t)sl * WP + w) * DV + o4) = d4;
     }
     if (ch > 0) reduce_out(ch - 1);
     group_barrier(ctr, G * (++nbar), err);
@@ -478,9 +528,18 @@ grouped_kernel(GroupedParams p) {
     // ---- all-gather D2 -> LDS [WP][LV]
     {
       const bf16* d2b = d2buf + (size_t)sl * WP * DV;
-      for (int e = tid; e < WP * (DV / 8); e += 256) {
-        const int w = e / (DV / 8), o8 = (e % (DV / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(D2 + w * LV + o8) = *reinterpret_cast<const bf16x8*>(d2b + (size_t)w * DV + o8);
+      constexpr int NG = WP * (DV / 8) / 256;
+      static_assert(WP * (DV / 8) % 256 == 0, "whole passes");
+      bf16x8 t8[NG];
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int e = tid + 256 * u;
+        t8[u] = *reinterpret_cast<const bf16x8*>(d2b + (size_t)(e / (DV / 8)) * DV + (e % (DV / 8)) * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < NG; ++u) {
+        const int e = tid + 256 * u;
+        *reinterpret_cast<bf16x8*>(D2 + (e / (DV / 8)) * LV + (e % (DV / 8)) * 8) = t8[u];
       }
     }
     __syncthreads();
@@ -505,11 +564,20 @@ grouped_kernel(GroupedParams p) {
     {
       f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
       const int qrow = t0 + Q0 + c16;
-#pragma unroll 4
-      for (int s = 0; s < DP / 32; ++s) {
-        const bf16x8 xq = gload8(rxq, (qrow * DP + 32 * s + 8 * g) * 2);
-        a1 = mma(xq, ld_nat(W1i, LF, 0, 32 * s, lane), a1);
-        if (mom) a2 = mma(xq, ld_nat(S1i, LF, 0, 32 * s, lane), a2);
+      {
+        constexpr int NS = DP / 32, PF = 8;
+        bf16x8 xf[PF + 1];
+#pragma unroll
+        for (int st = 0; st < PF && st < NS; ++st) xf[st] = gload8(rxq, (qrow * DP + 32 * st + 8 * g) * 2);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          if (st + PF < NS) xf[(st + PF) % (PF + 1)] = gload8(rxq, (qrow * DP + 32 * (st + PF) + 8 * g) * 2);
+          __builtin_amdgcn_sched_barrier(0);
+          const bf16x8 xq = xf[st % (PF + 1)];
+          a1 = mma(xq, ld_nat(W1i, LF, 0, 32 * st, lane), a1);
+          if (mom) a2 = mma(xq, ld_nat(S1i, LF, 0, 32 * st, lane), a2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 #pragma unroll
       for (int s = 0; s < WP / 32; ++s) {
@@ -533,30 +601,33 @@ grouped_kernel(GroupedParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qq = Q0 + 4 * g + r, w = 16 * nt + c16;
-          Q2[qq * LT + w] = (bf16)(Cc[qq * WP + w] * acc[r]);
+          Q2[qq * LT + w] = (bf16)(Cl[qq * WP + w] * acc[r]);
         }
       }
     }
 
     // ---- retrieval, layer 2 partial: A_q Ah W2^T + B_q Ah S2^T - Q2 D2  [Q0.. x DV]
     {
+      // transposed (value rows x queries): lane holds four adjacent values of
+      // query Q0 + (l & 15), one 16-byte store per tile
       const int yo = ((sl * G + pm) * BC) * DV * 4;
       const bf16x4 ah = *reinterpret_cast<const bf16x4*>(Ah + (Q0 + c16) * LU + 4 * g);
       bf16x8 q2f[WP / 32];
 #pragma unroll
       for (int s = 0; s < WP / 32; ++s) q2f[s] = ld_nat(Q2, LT, Q0, 32 * s, lane);
+      const int qq = Q0 + c16;
+      const float ca = cA[qq], cb = cB[qq];
 #pragma unroll
       for (int nt = 0; nt < DV / 16; ++nt) {
-        const f32x4 b1 = mma16(ah, ld_tr16(W2i, LV, 16 * nt, 0, lane), zero4());
-        const f32x4 b2 = mom ? mma16(ah, ld_tr16(S2i, LV, 16 * nt, 0, lane), zero4()) : zero4();
+        const f32x4 b1 = mma16(ld_tr16(W2i, LV, 16 * nt, 0, lane), ah, zero4());
+        const f32x4 b2 = mom ? mma16(ld_tr16(S2i, LV, 16 * nt, 0, lane), ah, zero4()) : zero4();
         f32x4 b3 = zero4();
 #pragma unroll
-        for (int s = 0; s < WP / 32; ++s) b3 = mma(q2f[s], ld_tr_nat(D2, LV, 16 * nt, 32 * s, lane), b3);
+        for (int s = 0; s < WP / 32; ++s) b3 = mma(ld_tr_nat(D2, LV, 16 * nt, 32 * s, lane), q2f[s], b3);
+        f32x4 y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qq = Q0 + 4 * g + r;
-          gstore1(cA[qq] * b1[r] + cB[qq] * b2[r] - b3[r], rxo, yo + (qq * DV + 16 * nt + c16) * 4);
-        }
+        for (int r = 0; r < 4; ++r) y[r] = ca * b1[r] + cb * b2[r] - b3[r];
+        buf_store4(y, rxo, yo + (qq * DV + 16 * nt + 4 * g) * 4, 0);
       }
     }
 
@@ -571,15 +642,23 @@ grouped_kernel(GroupedParams p) {
         bm[s] = ld_nat_scaled(D1T, LT, 0, 32 * s, lane, cM);
         bs[s] = ld_nat_scaled(D1T, LT, 0, 32 * s, lane, cS);
       }
-#pragma unroll
-      for (int t = 0; t < NFW; ++t) {
-        f32x4 um = zero4(), us = zero4();
+      // X^T fragments of tile t + 1 are loaded before tile t computes
+      bf16x8 xf[2][WP / 32];
+      auto load = [&](int t, bf16x8* dst) {
         const int f = fb + 16 * t + c16;
 #pragma unroll
+        for (int s = 0; s < WP / 32; ++s) dst[s] = gload8(rxt, (f * (int)NR + t0 + 32 * s + 8 * g) * 2);
+      };
+      load(0, xf[0]);
+#pragma unroll
+      for (int t = 0; t < NFW; ++t) {
+        if (t + 1 < NFW) load(t + 1, xf[(t + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 um = zero4(), us = zero4();
+#pragma unroll
         for (int s = 0; s < WP / 32; ++s) {
-          const bf16x8 xt = gload8(rxt, ((size_t)f * NR + t0 + 32 * s + 8 * g) * 2);
-          um = mma(bm[s], xt, um);
-          if (mom) us = mma(bs[s], xt, us);
+          um = mma(bm[s], xf[t & 1][s], um);
+          if (mom) us = mma(bs[s], xf[t & 1][s], us);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -587,6 +666,7 @@ grouped_kernel(GroupedParams p) {
           W1T[t][r] = Ate * w1 + Bte * s1 - um[r];
           S1T[t][r] = Pc * s1 - us[r];
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // W2 [value rows x 16 units]: (cM .* D2)^T A, K = WP
 #pragma unroll
