@@ -420,9 +420,14 @@ grouped_kernel(GroupedParams p) {
     {
       constexpr int NS = DP / 32, PF = 5;
       bf16x8 xf[PF + 1][2];
+      // each member walks the K steps from its own starting step, so that the
+      // 32 members of a group do not all read the same L2 lines at once
+      const int k0 = pm % NS;
+      auto kstep = [&](int st) { const int k = st + k0; return k < NS ? k : k - NS; };
       auto load = [&](int st, bf16x8* dst) {
+        const int ks = kstep(st);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) dst[mt] = gload8(rxr, ((t0 + R0 + 16 * mt + c16) * DP + 32 * st + 8 * g) * 2);
+        for (int mt = 0; mt < 2; ++mt) dst[mt] = gload8(rxr, ((t0 + R0 + 16 * mt + c16) * DP + 32 * ks + 8 * g) * 2);
       };
 #pragma unroll
       for (int st = 0; st < PF && st < NS; ++st) load(st, xf[st]);
@@ -430,7 +435,7 @@ grouped_kernel(GroupedParams p) {
       for (int st = 0; st < NS; ++st) {
         if (st + PF < NS) load(st + PF, xf[(st + PF) % (PF + 1)]);
         __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 bw = ld_nat(W1i, LF, 0, 32 * st, lane);
+        const bf16x8 bw = ld_nat(W1i, LF, 0, 32 * kstep(st), lane);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) Z[mt] = mma(xf[st % (PF + 1)][mt], bw, Z[mt]);
         __builtin_amdgcn_sched_barrier(0);
@@ -566,16 +571,19 @@ grouped_kernel(GroupedParams p) {
       const int qrow = t0 + Q0 + c16;
       {
         constexpr int NS = DP / 32, PF = 8;
+        const int k0 = pm % NS;   // per-member starting step, as in the forward
+        auto kstep = [&](int st) { const int k = st + k0; return k < NS ? k : k - NS; };
         bf16x8 xf[PF + 1];
 #pragma unroll
-        for (int st = 0; st < PF && st < NS; ++st) xf[st] = gload8(rxq, (qrow * DP + 32 * st + 8 * g) * 2);
+        for (int st = 0; st < PF && st < NS; ++st) xf[st] = gload8(rxq, (qrow * DP + 32 * kstep(st) + 8 * g) * 2);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          if (st + PF < NS) xf[(st + PF) % (PF + 1)] = gload8(rxq, (qrow * DP + 32 * (st + PF) + 8 * g) * 2);
+          if (st + PF < NS) xf[(st + PF) % (PF + 1)] = gload8(rxq, (qrow * DP + 32 * kstep(st + PF) + 8 * g) * 2);
           __builtin_amdgcn_sched_barrier(0);
           const bf16x8 xq = xf[st % (PF + 1)];
-          a1 = mma(xq, ld_nat(W1i, LF, 0, 32 * st, lane), a1);
-          if (mom) a2 = mma(xq, ld_nat(S1i, LF, 0, 32 * st, lane), a2);
+          const int ks = kstep(st);
+          a1 = mma(xq, ld_nat(W1i, LF, 0, 32 * ks, lane), a1);
+          if (mom) a2 = mma(xq, ld_nat(S1i, LF, 0, 32 * ks, lane), a2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
