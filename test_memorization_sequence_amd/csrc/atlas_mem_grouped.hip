@@ -119,86 +119,100 @@ struct GShape {
   __host__ __device__ static size_t seq_bytes(int nch) { return align_up(oXQ(nch) + (size_t)nch * BC * DP * 2, 256); }
 };
 
-// pair table of the degree-2 block: idx -> (a, b), a <= b, row-major upper triangle
-template <int P> struct Pairs {
-  static constexpr int NP = P * (P + 1) / 2;
-  uint8_t a[NP > 0 ? NP : 1], b[NP > 0 ? NP : 1];
-  __device__ void fill() {
-    for (int idx = threadIdx.x; idx < NP; idx += blockDim.x) {
-      int aa = 0, off = 0;
-      while (idx >= off + (P - aa)) { off += P - aa; ++aa; }
-      a[idx] = (uint8_t)aa;
-      b[idx] = (uint8_t)(aa + idx - off);
-    }
-  }
-};
-
-// feature f of a raw row (fp32 values of bf16 numbers); products in fp32
-template <class S>
-__device__ __forceinline__ float phi_of(const float* row, int f, const Pairs<(S::PHI == PHI_POLY2 ? S::DK : S::PD)>& pt) {
-  if (f < S::DK) return row[f];
-  if constexpr (S::PHI == PHI_POLY2) {
-    if (f < S::D) { const int p = f - S::DK; return row[pt.a[p]] * row[pt.b[p]]; }
-  } else if constexpr (S::PHI == PHI_RAW_POLY2) {
-    if (f < S::DK + S::PD) return row[f - S::DK];
-    if (f < S::D) { const int p = f - S::DK - S::PD; return row[pt.a[p]] * row[pt.b[p]]; }
-  }
-  return 0.f;
+// ----------------------------------------------------------------------------- phi kernel
+// Degree-2 block: pair index p -> (a, b), a <= b < P, row-major upper triangle
+// (row a starts at off(a) = a P - a (a - 1) / 2): the root of the quadratic,
+// then a correction of the float estimate by one row either way.
+template <int P>
+__device__ __forceinline__ void pair_of(int p, int& a, int& b) {
+  constexpr float B2 = 2.f * P + 1.f;
+  int aa = (int)((B2 - sqrtf(B2 * B2 - 8.f * (float)p)) * 0.5f);
+  aa = max(0, min(P - 1, aa));
+  auto off = [](int x) { return x * P - x * (x - 1) / 2; };
+  if (off(aa) > p) --aa;
+  else if (aa + 1 < P && off(aa + 1) <= p) ++aa;
+  a = aa;
+  b = aa + p - off(aa);
 }
 
-// ----------------------------------------------------------------------------- phi kernel
-// Blocks of 64 rows: per sequence, rows_k(nch)/64 key blocks, then nch query
-// blocks.  Key row i is token i - (c - 1): from the input, from the state's
-// halo (tokens before the call that the sequence has seen), else zero.
+// Where feature f of phi comes from: zero (kind 0), raw component a (kind 1)
+// or the product of raw components a and b (kind 2).
+struct FeatureSrc { int kind, a, b; };
+template <class S>
+__device__ __forceinline__ FeatureSrc feature_src(int f) {
+  if (f < S::DK) return {1, f, 0};
+  if constexpr (S::PHI == PHI_POLY2) {
+    if (f < S::D) { FeatureSrc r{2, 0, 0}; pair_of<S::DK>(f - S::DK, r.a, r.b); return r; }
+  } else if constexpr (S::PHI == PHI_RAW_POLY2) {
+    if (f < S::DK + S::PD) return {1, f - S::DK, 0};
+    if (f < S::D) { FeatureSrc r{2, 0, 0}; pair_of<S::PD>(f - S::DK - S::PD, r.a, r.b); return r; }
+  }
+  return {0, 0, 0};
+}
+// The value of one feature from a raw row in LDS (products in fp32).
+__device__ __forceinline__ float feature_val(const float* row, const FeatureSrc& fs) {
+  if (fs.kind == 0) return 0.f;
+  const float x = row[fs.a];
+  return fs.kind == 1 ? x : x * row[fs.b];
+}
+
+// Blocks of 32 tokens: per sequence rows_k(nch) / 32 key blocks (key row i is
+// token i - (c - 1): the input for tokens of the call, the state's halo for
+// earlier tokens the sequence has seen, else zero), then 2 nch query blocks.
+// The raw rows go to LDS as floats; each thread then writes 16 bytes at a
+// time: 8 consecutive features of one row, or (keys) 8 consecutive tokens of
+// one feature of the feature-major copy.
 template <class S>
 __global__ void __launch_bounds__(256) phi_kernel(GroupedParams p) {
-  constexpr int DK = S::DK, DP = S::DP, LP = DP + 8;
-  extern __shared__ __attribute__((aligned(256))) char smem[];
-  float* raw = reinterpret_cast<float*>(smem);                                   // [64][DK]
-  bf16* tile = reinterpret_cast<bf16*>(smem + align_up(64 * DK * 4, 256));       // [64][LP]
-  __shared__ Pairs<(S::PHI == PHI_POLY2 ? S::DK : S::PD)> pt;
-  const int nch = p.nchunks, kb = (int)S::rows_k(nch) / 64, per_seq = kb + nch;
+  constexpr int DK = S::DK, DP = S::DP, F8 = DP / 8, RB = 32;
+  __shared__ float raw[RB][DK + 1];
+  const int nch = p.nchunks, NR = (int)S::rows_k(nch), kb = NR / RB, per_seq = kb + 2 * nch;
   const int seq = (int)(blockIdx.x / (unsigned)per_seq), blk = (int)(blockIdx.x % (unsigned)per_seq);
   const bool keys = blk < kb;
-  const int r0 = 64 * (keys ? blk : blk - kb);
-  const int N = p.N, c = p.c;
+  const int r0 = RB * (keys ? blk : blk - kb);
+  const int N = p.N, c1 = p.c - 1;
   const char* st = p.state + (size_t)seq * p.seq_stride;
   const int64_t cnt = *reinterpret_cast<const int64_t*>(st + p.off_count);
-  const int halo_valid = (int)min<int64_t>(cnt, (int64_t)(c - 1));
+  const int halo_valid = (int)min<int64_t>(cnt, (int64_t)c1);
   const float* hk = reinterpret_cast<const float*>(st + p.off_halo_k);
   const bf16* src = reinterpret_cast<const bf16*>(keys ? p.k : p.q) + (size_t)seq * N * DK;
-  pt.fill();
-  if (blk == 0 && threadIdx.x == 0)   // before the recurrence starts: no member has reported yet
-    *reinterpret_cast<unsigned*>(p.gws + (size_t)seq * p.gseq_bytes + S::xMask) = 0u;
-  for (int e = threadIdx.x; e < 64 * DK; e += 256) {
-    const int r = e / DK, d = e % DK;
-    const int tok = keys ? r0 + r - (c - 1) : r0 + r;
-    float x = 0.f;
-    if (tok >= 0 && tok < N) x = (float)src[(size_t)tok * DK + d];
-    else if (keys && tok < 0 && tok >= -halo_valid) x = (float)(bf16)hk[(c - 1 + tok) * DK + d];
-    raw[e] = x;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * DP; e += 256) {
-    const int r = e / DP, f = e % DP;
-    tile[r * LP + f] = (bf16)phi_of<S>(raw + r * DK, f, pt);
-  }
-  __syncthreads();
   char* ws = p.gws + (size_t)seq * p.gseq_bytes;
+  if (blk == 0 && threadIdx.x == 0)   // before the recurrence starts: no member has reported yet
+    *reinterpret_cast<unsigned*>(ws + S::xMask) = 0u;
+  for (int e = threadIdx.x; e < RB * (DK / 8); e += 256) {
+    const int r = e / (DK / 8), d8 = (e % (DK / 8)) * 8;
+    const int tok = keys ? r0 + r - c1 : r0 + r;
+    float x[8];
+    if (tok >= 0 && tok < N) {
+      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(src + (size_t)tok * DK + d8);
+#pragma unroll
+      for (int z = 0; z < 8; ++z) x[z] = (float)v8[z];
+    } else {
+      const bool h = keys && tok < 0 && tok >= -halo_valid;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) x[z] = h ? (float)(bf16)hk[(c1 + tok) * DK + d8 + z] : 0.f;
+    }
+#pragma unroll
+    for (int z = 0; z < 8; ++z) raw[r][d8 + z] = x[z];
+  }
+  __syncthreads();
   bf16* rows = reinterpret_cast<bf16*>(ws + (keys ? S::oXR(nch) : S::oXQ(nch)));
-  for (int e = threadIdx.x; e < 64 * (DP / 8); e += 256) {
-    const int r = e / (DP / 8), f8 = (e % (DP / 8)) * 8;
-    *reinterpret_cast<bf16x8*>(rows + (size_t)(r0 + r) * DP + f8) = *reinterpret_cast<const bf16x8*>(tile + r * LP + f8);
+  for (int e = threadIdx.x; e < RB * F8; e += 256) {
+    const int r = e / F8, f0 = (e % F8) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int z = 0; z < 8; ++z) v[z] = (bf16)feature_val(raw[r], feature_src<S>(f0 + z));
+    *reinterpret_cast<bf16x8*>(rows + (size_t)(r0 + r) * DP + f0) = v;
   }
   if (keys) {
-    const size_t NR = S::rows_k(nch);
     bf16* cols = reinterpret_cast<bf16*>(ws + S::oXT(nch));
-    for (int e = threadIdx.x; e < DP * 8; e += 256) {
-      const int f = e / 8, part = e % 8;
+    for (int e = threadIdx.x; e < DP * (RB / 8); e += 256) {
+      const int f = e / (RB / 8), t8 = (e % (RB / 8)) * 8;
+      const FeatureSrc fs = feature_src<S>(f);
       bf16x8 v;
 #pragma unroll
-      for (int z = 0; z < 8; ++z) v[z] = tile[(8 * part + z) * LP + f];
-      *reinterpret_cast<bf16x8*>(cols + (size_t)f * NR + r0 + 8 * part) = v;
+      for (int z = 0; z < 8; ++z) v[z] = (bf16)feature_val(raw[t8 + z], fs);
+      *reinterpret_cast<bf16x8*>(cols + (size_t)f * NR + r0 + t8) = v;
     }
   }
 }
@@ -750,18 +764,15 @@ hipError_t launch_grouped(const GroupedParams& gp, const CoeffParams& kp, hipStr
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static bool attr_set = false;
-  const size_t phi_lds = align_up(64 * DK * 4, 256) + 64 * (S::DP + 8) * 2;
   if (!attr_set) {
     // allow more than the default dynamic LDS; a refusal shows up at launch
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped::grouped_kernel<S>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped::phi_kernel<S>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)phi_lds);
     (void)hipGetLastError();
     attr_set = true;
   }
-  const unsigned per_seq = (unsigned)(S::rows_k(gp.nchunks) / 64 + gp.nchunks);
-  hipLaunchKernelGGL((grouped::phi_kernel<S>), dim3(per_seq * (unsigned)gp.n_seq), dim3(256), phi_lds, stream, gp);
+  const unsigned per_seq = (unsigned)(S::rows_k(gp.nchunks) / 32 + 2 * (size_t)gp.nchunks);
+  hipLaunchKernelGGL((grouped::phi_kernel<S>), dim3(per_seq * (unsigned)gp.n_seq), dim3(256), 0, stream, gp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((grouped::q1_phi_kernel<S>), dim3((unsigned)gp.nchunks * (unsigned)gp.n_seq), dim3(256), 0,
                      stream, gp);
