@@ -45,7 +45,8 @@ MEASURED_TRAFFIC = {
 
 # translation unit of each recurrent kernel
 KERNEL_SOURCE = {"stream_mlp_kernel": "atlas_mem_stream.hip", "sharded_mlp_kernel": "atlas_mem_sharded.hip",
-                 "chunk_kernel": "atlas_mem_kernels.hip", "grouped_kernel": "atlas_mem_grouped.hip"}
+                 "chunk_kernel": "atlas_mem_kernels.hip", "grouped_kernel": "atlas_mem_grouped.hip",
+                 "linear_rec_kernel": "atlas_mem_grouped.hip"}
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -149,6 +150,9 @@ def kernel_name(binding, wl, family):
     """Name of the recurrent kernel a call runs for this workload and family."""
     if family == "auto":
         family = binding.AtlasMem(wl, "auto").family()
+    if family == "grouped" and wl.memory == "linear":
+        # the events bracket the recurrence and the retrieval that follows it
+        return "linear_rec_kernel"
     return {"sharded": "sharded_mlp_kernel", "streamed": "stream_mlp_kernel", "per_sequence": "chunk_kernel",
             "grouped": "grouped_kernel"}[family]
 

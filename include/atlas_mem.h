@@ -89,12 +89,15 @@ enum { ATLAS_OPT_GD = 0, ATLAS_OPT_MUON = 1 };
  * units), the fp32 weights and momentum read and written once per chunk in
  * one fused pass.  SHARDED and STREAMED serve the MLP memory with the
  * identity feature map, d_k == d_v and bf16 io (SHARDED: the l2 and
- * dot-product biases and no layer norm).  GROUPED: the hidden units of each
- * sequence split over a group of workgroups of one XCD (16 per workgroup),
- * weights resident in registers, phi of every key and query computed once
- * per call into the workspace; the MLP memory on any feature map with the
- * l2 or dot-product bias, bf16 io, chunk 64, c <= 64, no layer norm, no
- * gated memory, gradient descent.  AUTO picks the fastest family measured
+ * dot-product biases and no layer norm).  GROUPED: phi of every key and
+ * query computed once per call into the workspace, the state resident in
+ * registers; for the MLP memory the hidden units of each sequence split over
+ * a group of workgroups of one XCD (16 per workgroup), for the linear memory
+ * one workgroup per sequence runs the chunk chain and the retrieval of every
+ * chunk runs afterwards, all chunks at once.  It serves the shapes of its
+ * compiled table with the l2 or dot-product bias, bf16 io, chunk 64,
+ * c <= 64, no layer norm, no gated memory, gradient descent.  AUTO picks
+ * the fastest family measured
  * for the shape: STREAMED where marked so (large hidden layers), else
  * SHARDED, else STREAMED, else GROUPED, else PER_SEQUENCE.                 */
 enum { ATLAS_KERNEL_AUTO = 0, ATLAS_KERNEL_PER_SEQUENCE = 1, ATLAS_KERNEL_SHARDED = 2, ATLAS_KERNEL_STREAMED = 3,

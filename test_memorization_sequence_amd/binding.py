@@ -198,7 +198,7 @@ class AtlasMem:
             raise AtlasError(rc, "atlas_mem_set_kernel_events")
 
     def family(self) -> str:
-        """Kernel family this handle runs ("per_sequence", "sharded", "streamed")."""
+        """Kernel family this handle runs ("per_sequence", "sharded", "streamed", "grouped")."""
         code = lib().atlas_mem_kernel_family(self.handle)
         return {v: k for k, v in KERNEL.items()}[code]
 

@@ -67,13 +67,14 @@ typedef hipError_t (*GroupedLaunchFn)(const GroupedParams&, const CoeffParams&, 
 
 struct GroupedVariant {
   const char* name;
-  int phi, dk, pd, dv, h, g;
+  int phi, dk, pd, dv, h, g, wp;   // h = 0: linear memory
   size_t (*seq_bytes)(int);
   GroupedLaunchFn launch;
 };
 
-#define ATLAS_GROUPED(NAME, PHI, DK, PD, DV, H, G) \
-  {#NAME, PHI, DK, PD, DV, H, G, &grouped_seq_bytes<PHI, DK, PD, DV, H, G>, &launch_grouped<PHI, DK, PD, DV, H, G>},
+#define ATLAS_GROUPED(NAME, PHI, DK, PD, DV, H, G, WP)                                             \
+  {#NAME, PHI, DK, PD, DV, H, G, WP, &grouped_seq_bytes<PHI, DK, PD, DV, H, G, WP>, \
+   &launch_grouped<PHI, DK, PD, DV, H, G, WP>},
 static const GroupedVariant kGrouped[] = {
 #include "atlas_mem_grouped_variants.inc"
 };
@@ -152,19 +153,21 @@ static const StreamVariant* find_streamed(const atlas_mem_config* c) {
 }
 
 static const GroupedVariant* find_grouped(const atlas_mem_config* c) {
-  if (c->memory != ATLAS_MEM_MLP || c->io_dtype != ATLAS_BF16 || c->optimizer != ATLAS_OPT_GD) return nullptr;
+  if (c->io_dtype != ATLAS_BF16 || c->optimizer != ATLAS_OPT_GD) return nullptr;
   if (c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
   if (c->mlp_layernorm || c->mlp_gated) return nullptr;
   if (c->chunk != 64 || c->window > 64) return nullptr;
+  const int h = c->memory == ATLAS_MEM_MLP ? c->mlp_hidden : 0;
+  const int nch = (c->seq_len + c->chunk - 1) / c->chunk;
+  const GroupedVariant* best = nullptr;
   for (const GroupedVariant& v : kGrouped) {
-    if (v.phi != c->feature_map || v.dk != c->d_k || v.pd != pd_of(c) || v.dv != c->d_v || v.h != c->mlp_hidden)
-      continue;
-    // the kernels address one sequence's workspace through 32-bit offsets
-    const int nch = (c->seq_len + c->chunk - 1) / c->chunk;
-    if (v.seq_bytes(nch) >= (1u << 31)) return nullptr;
-    return &v;
+    if (v.phi != c->feature_map || v.dk != c->d_k || v.pd != pd_of(c) || v.dv != c->d_v || v.h != h) continue;
+    if (v.wp < c->chunk + c->window - 1) continue;
+    if (!best || v.wp < best->wp) best = &v;
   }
-  return nullptr;
+  // the kernels address one sequence's workspace through 32-bit offsets
+  if (best && best->seq_bytes(nch) >= (1u << 31)) return nullptr;
+  return best;
 }
 
 // Exactly one of *out, *sout, *tout, *gout is set on success.
@@ -296,7 +299,7 @@ static atlas_status setup_handle(const atlas_mem_config* cfg, atlas_mem_s* h) {
   h->coef_stride = var ? coef_stride(var->bc, var->wp)
                  : svar ? coef_stride(svar->bc, svar->wp, true)
                  : tvar ? coef_stride(tvar->bc, tvar->wp, true, true)
-                        : coef_stride(64, 128, true);
+                        : coef_stride(64, gvar->wp, true);
   h->device = -1;
   h->ws = nullptr;
   h->coef = nullptr;

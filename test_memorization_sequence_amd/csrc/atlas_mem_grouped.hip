@@ -752,11 +752,384 @@ grouped_kernel(GroupedParams p) {
   }
 }
 
+
+// ----------------------------------------------------------------------------- linear memory
+// Linear memory M [DV][D] (Titans review sec. 3.1: matrix memory; ATLAS review
+// sec. 3.1 for the feature map) on the same phi buffers and Q1 blocks.  The
+// recurrence needs per chunk only the window forward, D and the update, so it
+// runs on one workgroup per sequence with M and S fp32 in registers; it leaves
+// the chunk-start images of M and S (bf16) and D of every chunk behind, and
+// the retrieval then runs for all chunks at once:
+//   linear_rec_kernel  Y = X M^T over the window rows at the chunk-start
+//                      state, D = s gamma (Y - V) (dot bias: -s gamma V),
+//                      M <- A_te M + B_te S - (cM .* D)^T X,
+//                      S <- P S - (cS .* D)^T X;
+//   linear_ret_kernel  y_t = A_t M0 phi(q_t) + B_t S0 phi(q_t) - sum_w Q1[t][w] D_w
+//                      (M0, S0 the chunk-start state), one workgroup per
+//                      (sequence, chunk).
+template <int PHI_, int DK_, int PD_, int DV_, int WP_>
+struct LShape {
+  static constexpr int PHI = PHI_, DK = DK_, PD = PD_, DV = DV_, WP = WP_;
+  static constexpr int D = feature_dim(PHI_, DK_, PD_);
+  static constexpr int DP = (D + 63) / 64 * 64;   // features, padded to 4 waves x 16-row tiles
+  static constexpr int BC = 64;
+  static constexpr int NOT = DV / 16, NFT = DP / 16, NWT = WP / 16;
+  static constexpr int YPW = NOT * NWT / 4;       // window-forward tiles per wave
+  static constexpr int FPW = NFT / 4;             // update feature tiles per wave
+  static_assert(DV % 16 == 0 && (NOT * NWT) % 4 == 0, "value tiles");
+  static_assert(WP % 32 == 0 && WP >= BC && WP <= 128, "window rows");
+  static_assert(DK % 8 == 0, "phi rows");
+  static_assert(FPW * NOT <= 18, "state registers: 8 FPW NOT per lane");
+  // LDS (bf16 pitches: multiples of 8, 16-byte rows)
+  static constexpr int LF = DP + 8, LV = DV + 8;
+  static constexpr size_t oMi = 0;                                  // M image [DV][LF]
+  static constexpr size_t oD2 = oMi + align_up(DV * LF * 2, 256);   // D [WP][LV]
+  static constexpr size_t oF = oD2 + align_up(WP * LV * 2, 256);    // [2] x (cA[BC] cB[BC] cM[WP] cS[WP] P)
+  static constexpr int NCF = 2 * BC + 2 * WP + 4;
+  static constexpr size_t lds = oF + 2 * NCF * 4;
+  static_assert(lds <= 163840, "LDS budget of one CU");
+  // workspace per sequence (bytes): a word the phi kernel clears (unused
+  // here), the chunk-start images [nch][2][DV][DP] (M, then S), D of every
+  // chunk [nch][WP][DV], then the phi buffers as in the MLP shapes
+  static constexpr size_t xMask = 0;
+  __host__ __device__ static size_t rows_k(int nch) { return (size_t)nch * BC + BC; }
+  __host__ __device__ static size_t oImg(int) { return 256; }
+  __host__ __device__ static size_t oDg(int nch) { return align_up(oImg(nch) + (size_t)nch * 2 * DV * DP * 2, 256); }
+  __host__ __device__ static size_t oXR(int nch) { return align_up(oDg(nch) + (size_t)nch * WP * DV * 2, 256); }
+  __host__ __device__ static size_t oXT(int nch) { return align_up(oXR(nch) + rows_k(nch) * DP * 2, 256); }
+  __host__ __device__ static size_t oXQ(int nch) { return align_up(oXT(nch) + rows_k(nch) * DP * 2, 256); }
+  __host__ __device__ static size_t seq_bytes(int nch) { return align_up(oXQ(nch) + (size_t)nch * BC * DP * 2, 256); }
+};
+
+template <class S>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+linear_rec_kernel(GroupedParams p) {
+  constexpr int DK = S::DK, DV = S::DV, D = S::D, DP = S::DP, BC = S::BC, WP = S::WP;
+  constexpr int NOT = S::NOT, YPW = S::YPW, FPW = S::FPW, LF = S::LF, LV = S::LV, NCF = S::NCF;
+  extern __shared__ __attribute__((aligned(256))) char smem[];
+  const int seq = (int)blockIdx.x;
+  if (seq >= p.n_seq) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int N = p.N, c = p.c, W = BC + c - 1, nch = p.nchunks;
+  const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT;
+  const float s_grad = p.grad_scale;
+
+  char* st = p.state + (size_t)seq * p.seq_stride;
+  float* Wt = reinterpret_cast<float*>(st + p.off_weights);
+  float* Mo = reinterpret_cast<float*>(st + p.off_momentum);
+  float* hk = reinterpret_cast<float*>(st + p.off_halo_k);
+  float* hv = reinterpret_cast<float*>(st + p.off_halo_v);
+  float* hg = reinterpret_cast<float*>(st + p.off_halo_g);
+  int64_t* cnt = reinterpret_cast<int64_t*>(st + p.off_count);
+  const int halo_valid = (int)min<int64_t>(*cnt, (int64_t)(c - 1));
+  const bf16* k = reinterpret_cast<const bf16*>(p.k) + (size_t)seq * N * DK;
+  const bf16* v = reinterpret_cast<const bf16*>(p.v) + (size_t)seq * N * DV;
+  const float* gam_in = p.gamma + (size_t)seq * N;
+
+  char* ws = p.gws + (size_t)seq * p.gseq_bytes;
+  const size_t NR = S::rows_k(nch);
+  const __amdgpu_buffer_rsrc_t rxr = buffer_of(ws + S::oXR(nch), (unsigned)(NR * DP * 2));
+  const __amdgpu_buffer_rsrc_t rxt = buffer_of(ws + S::oXT(nch), (unsigned)(NR * DP * 2));
+  bf16* img = reinterpret_cast<bf16*>(ws + S::oImg(nch));
+  bf16* dg = reinterpret_cast<bf16*>(ws + S::oDg(nch));
+
+  bf16* Mi = reinterpret_cast<bf16*>(smem + S::oMi);
+  bf16* D2l = reinterpret_cast<bf16*>(smem + S::oD2);
+  float* cf = reinterpret_cast<float*>(smem + S::oF);   // two coefficient sets, by chunk parity
+
+  // ---- state into registers: MT[m][o][r] = M[16 o + c16][16 (wave + 4 m) + 4 g + r], same for S
+  f32x4 MT[FPW][NOT], ST[FPW][NOT];
+  {
+    const __amdgpu_buffer_rsrc_t rw = buffer_of(Wt, (unsigned)((size_t)DV * D * 4));
+    const __amdgpu_buffer_rsrc_t rm = buffer_of(Mo, mom ? (unsigned)((size_t)DV * D * 4) : 0u);
+#pragma unroll
+    for (int m = 0; m < FPW; ++m)
+#pragma unroll
+      for (int o = 0; o < NOT; ++o)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * (wave + 4 * m) + 4 * g + r;
+          const int off = f < D ? ((16 * o + c16) * D + f) * 4 : kZeroOffset;
+          MT[m][o][r] = gload1(rw, off);
+          ST[m][o][r] = gload1(rm, off);
+        }
+  }
+  // images of the chunk-start state of chunk chn: M into LDS (the window
+  // forward's operand), M and S into the workspace (the retrieval's)
+  auto write_images = [&](int chn) {
+    bf16* im = img + (size_t)chn * 2 * DV * DP;
+#pragma unroll
+    for (int m = 0; m < FPW; ++m)
+#pragma unroll
+      for (int o = 0; o < NOT; ++o) {
+        const int f0 = 16 * (wave + 4 * m) + 4 * g, orow = 16 * o + c16;
+        const bf16x4 wv{(bf16)MT[m][o][0], (bf16)MT[m][o][1], (bf16)MT[m][o][2], (bf16)MT[m][o][3]};
+        const bf16x4 sv{(bf16)ST[m][o][0], (bf16)ST[m][o][1], (bf16)ST[m][o][2], (bf16)ST[m][o][3]};
+        *reinterpret_cast<bf16x4*>(Mi + orow * LF + f0) = wv;
+        *reinterpret_cast<bf16x4*>(im + (size_t)orow * DP + f0) = wv;
+        *reinterpret_cast<bf16x4*>(im + (size_t)(DV + orow) * DP + f0) = sv;
+      }
+  };
+  write_images(0);
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int t0 = ch * BC;
+    const int te = min(N, t0 + BC) - 1;
+    float* cA = cf + (ch & 1) * NCF;
+    float* cB = cA + BC;
+    float* cM = cB + BC;
+    float* cS = cM + WP;
+    float* cP = cS + WP;
+    {
+      const float* coef = p.coef + ((size_t)seq * nch + ch) * p.coef_stride;
+      if (tid < BC) { cA[tid] = coef[tid]; cB[tid] = coef[BC + tid]; }
+      if (tid < WP) { cM[tid] = coef[2 * BC + 4 + tid]; cS[tid] = coef[2 * BC + 4 + WP + tid]; }
+      if (tid == 0) cP[0] = coef[2 * BC];
+    }
+    __syncthreads();   // coefficients and the M image of the chunk-start state
+
+    // ---- window forward, transposed: Y^T [value rows x window rows], K = DP.
+    // Wave tiles i = wave + 4u: value tile i % NOT, window tile i / NOT; the
+    // X fragments of step s + PF are loaded before step s computes.
+    f32x4 Y[YPW];
+#pragma unroll
+    for (int u = 0; u < YPW; ++u) Y[u] = zero4();
+    {
+      constexpr int NS = DP / 32, PF = 4;
+      bf16x8 xf[PF + 1][YPW];
+      auto load = [&](int s, bf16x8* dst) {
+#pragma unroll
+        for (int u = 0; u < YPW; ++u) {
+          const int wt = (wave + 4 * u) / NOT;
+          dst[u] = gload8(rxr, ((t0 + 16 * wt + c16) * DP + 32 * s + 8 * g) * 2);
+        }
+      };
+#pragma unroll
+      for (int s = 0; s < PF && s < NS; ++s) load(s, xf[s]);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s + PF < NS) load(s + PF, xf[(s + PF) % (PF + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < YPW; ++u) {
+          const int ot = (wave + 4 * u) % NOT;
+          Y[u] = mma(ld_nat(Mi, LF, 16 * ot, 32 * s, lane), xf[s % (PF + 1)][u], Y[u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // ---- D = s gamma (Y - V) (dot: -s gamma V) of the valid window rows, zero
+    // elsewhere: into LDS [WP][LV] and the workspace [WP][DV]
+#pragma unroll
+    for (int u = 0; u < YPW; ++u) {
+      const int ot = (wave + 4 * u) % NOT, wt = (wave + 4 * u) / NOT;
+      const int w = 16 * wt + c16, o4 = 16 * ot + 4 * g;
+      const int i = t0 - (c - 1) + w;
+      const bool valid = w < W && i >= -halo_valid && i <= te;
+      float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
+      float pg = 0.f;
+      if (valid) {
+        if (i >= 0) {
+          const bf16x4 vv = *reinterpret_cast<const bf16x4*>(v + (size_t)i * DV + o4);
+          pv = make_float4((float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]);
+          pg = gam_in[i];
+        } else {
+          pv = *reinterpret_cast<const float4*>(hv + (c - 1 + i) * DV + o4);
+          pg = hg[c - 1 + i];
+        }
+      }
+      const float sg = s_grad * pg;
+      float d[4];
+      d[0] = dot ? -sg * pv.x : sg * (Y[u][0] - pv.x);
+      d[1] = dot ? -sg * pv.y : sg * (Y[u][1] - pv.y);
+      d[2] = dot ? -sg * pv.z : sg * (Y[u][2] - pv.z);
+      d[3] = dot ? -sg * pv.w : sg * (Y[u][3] - pv.w);
+      const bf16x4 d4 = valid ? bf16x4{(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]}
+                              : bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+      *reinterpret_cast<bf16x4*>(D2l + w * LV + o4) = d4;
+      *reinterpret_cast<bf16x4*>(dg + ((size_t)ch * WP + w) * DV + o4) = d4;
+    }
+    __syncthreads();   // D complete
+
+    // ---- update, transposed: (cM .* D)^T X as [feature rows x value cols], K = WP;
+    // the wave's feature tiles 16 (wave + 4 m), every value tile
+    {
+      const int ce = te - t0;
+      const float Ate = cA[ce], Bte = cB[ce], Pc = cP[0];
+      bf16x8 bm[NOT][WP / 32], bs[NOT][WP / 32];
+#pragma unroll
+      for (int o = 0; o < NOT; ++o)
+#pragma unroll
+        for (int s = 0; s < WP / 32; ++s) {
+          const bf16x8 d = ld_tr_nat(D2l, LV, 16 * o, 32 * s, lane);
+          bm[o][s] = scaled_k(d, cM + 32 * s + 8 * g);
+          bs[o][s] = scaled_k(d, cS + 32 * s + 8 * g);
+        }
+      // X^T fragments of feature tile m + 1 are loaded before tile m computes
+      bf16x8 xf[2][WP / 32];
+      auto load = [&](int m, bf16x8* dst) {
+        const int f = 16 * (wave + 4 * m) + c16;
+#pragma unroll
+        for (int s = 0; s < WP / 32; ++s) dst[s] = gload8(rxt, (f * (int)NR + t0 + 32 * s + 8 * g) * 2);
+      };
+      load(0, xf[0]);
+#pragma unroll
+      for (int m = 0; m < FPW; ++m) {
+        if (m + 1 < FPW) load(m + 1, xf[(m + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int o = 0; o < NOT; ++o) {
+          f32x4 um = zero4(), us = zero4();
+#pragma unroll
+          for (int s = 0; s < WP / 32; ++s) {
+            um = mma(xf[m & 1][s], bm[o][s], um);
+            if (mom) us = mma(xf[m & 1][s], bs[o][s], us);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float w0 = MT[m][o][r], s0 = ST[m][o][r];
+            MT[m][o][r] = Ate * w0 + Bte * s0 - um[r];
+            ST[m][o][r] = Pc * s0 - us[r];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // every wave is past its reads of the M image (the window forward ended
+    // before the last barrier): the next chunk's images
+    if (ch + 1 < nch) write_images(ch + 1);
+  }
+
+  // ---- the state back to memory
+  {
+    const __amdgpu_buffer_rsrc_t rw = buffer_of(Wt, (unsigned)((size_t)DV * D * 4));
+    const __amdgpu_buffer_rsrc_t rm = buffer_of(Mo, mom ? (unsigned)((size_t)DV * D * 4) : 0u);
+#pragma unroll
+    for (int m = 0; m < FPW; ++m)
+#pragma unroll
+      for (int o = 0; o < NOT; ++o)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * (wave + 4 * m) + 4 * g + r;
+          const int off = f < D ? ((16 * o + c16) * D + f) * 4 : kZeroOffset;
+          gstore1(MT[m][o][r], rw, off);
+          gstore1(ST[m][o][r], rm, off);
+        }
+  }
+  // halo and count (every wave has read the old halo before the first
+  // chunk's second barrier)
+  __syncthreads();
+  if (tid < 64) {
+    for (int j = 0; j < c - 1; ++j) {
+      const int i = N - (c - 1) + j;
+      for (int d = lane; d < DK; d += 64) hk[j * DK + d] = i >= 0 ? (float)k[(size_t)i * DK + d] : hk[(N + j) * DK + d];
+      for (int o = lane; o < DV; o += 64) hv[j * DV + o] = i >= 0 ? (float)v[(size_t)i * DV + o] : hv[(N + j) * DV + o];
+      if (lane == 0) hg[j] = i >= 0 ? gam_in[i] : hg[N + j];
+    }
+    if (lane == 0) *cnt += N;
+  }
+}
+
+// One workgroup per (sequence, chunk); wave w owns query rows 16 w .. +15.
+// Computed transposed ([value rows x queries]) so that each lane holds four
+// adjacent values of one query: one 8-byte store per tile.
+template <class S>
+__global__ void __launch_bounds__(256) linear_ret_kernel(GroupedParams p) {
+  constexpr int DV = S::DV, DP = S::DP, BC = S::BC, WP = S::WP, NOT = S::NOT, LV = S::LV;
+  __shared__ __attribute__((aligned(16))) bf16 D2l[WP * LV];
+  const int nch = p.nchunks;
+  const int ch = (int)(blockIdx.x % (unsigned)nch), seq = (int)(blockIdx.x / (unsigned)nch);
+  const int t0 = ch * BC, te = min(p.N, t0 + BC) - 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const bool mom = p.momentum != 0;
+  const char* ws = p.gws + (size_t)seq * p.gseq_bytes;
+  const __amdgpu_buffer_rsrc_t rxq = buffer_of(ws + S::oXQ(nch), (unsigned)((size_t)nch * BC * DP * 2));
+  const __amdgpu_buffer_rsrc_t rim =
+      buffer_of(ws + S::oImg(nch) + (size_t)ch * 2 * DV * DP * 2, (unsigned)(2 * DV * DP * 2));
+  const bf16* dg = reinterpret_cast<const bf16*>(ws + S::oDg(nch)) + (size_t)ch * WP * DV;
+  const float* coef = p.coef + ((size_t)seq * nch + ch) * p.coef_stride;
+  const bf16* Q1g = reinterpret_cast<const bf16*>(coef + 2 * BC + 4 + 2 * WP + BC * WP);   // [BC][WP]
+  bf16* out = reinterpret_cast<bf16*>(p.out) + (size_t)seq * p.N * DV;
+
+  for (int e = tid; e < WP * DV / 8; e += 256) {
+    const int w = e / (DV / 8), o8 = (e % (DV / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(D2l + w * LV + o8) = *reinterpret_cast<const bf16x8*>(dg + w * DV + o8);
+  }
+  f32x4 a1[NOT], a2[NOT], a3[NOT];
+#pragma unroll
+  for (int o = 0; o < NOT; ++o) a1[o] = a2[o] = a3[o] = zero4();
+  const int qrow = t0 + 16 * wave + c16;
+#pragma unroll 2
+  for (int s = 0; s < DP / 32; ++s) {
+    const bf16x8 xq = gload8(rxq, (qrow * DP + 32 * s + 8 * g) * 2);
+#pragma unroll
+    for (int o = 0; o < NOT; ++o) {
+      a1[o] = mma(gload8(rim, ((16 * o + c16) * DP + 32 * s + 8 * g) * 2), xq, a1[o]);
+      if (mom) a2[o] = mma(gload8(rim, ((DV + 16 * o + c16) * DP + 32 * s + 8 * g) * 2), xq, a2[o]);
+    }
+  }
+  __syncthreads();   // D in LDS
+#pragma unroll
+  for (int s = 0; s < WP / 32; ++s) {
+    const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(Q1g + (16 * wave + c16) * WP + 32 * s + 8 * g);
+#pragma unroll
+    for (int o = 0; o < NOT; ++o) a3[o] = mma(ld_tr_nat(D2l, LV, 16 * o, 32 * s, lane), q1, a3[o]);
+  }
+  const int t = 16 * wave + c16;
+  if (t0 + t <= te) {
+    const float ca = coef[t], cb = coef[BC + t];
+#pragma unroll
+    for (int o = 0; o < NOT; ++o) {
+      const bf16x4 y{(bf16)(ca * a1[o][0] + cb * a2[o][0] - a3[o][0]), (bf16)(ca * a1[o][1] + cb * a2[o][1] - a3[o][1]),
+                     (bf16)(ca * a1[o][2] + cb * a2[o][2] - a3[o][2]), (bf16)(ca * a1[o][3] + cb * a2[o][3] - a3[o][3])};
+      *reinterpret_cast<bf16x4*>(out + (size_t)(t0 + t) * DV + 16 * o + 4 * g) = y;
+    }
+  }
+}
+
 }  // namespace grouped
 
-template <int PHI, int DK, int PD, int DV, int H, int G>
+template <int PHI, int DK, int PD, int DV, int WP>
+hipError_t launch_linear(const GroupedParams& gp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
+                         hipEvent_t ev1) {
+  typedef grouped::LShape<PHI, DK, PD, DV, WP> S;
+  if (gp.N == 0 || gp.n_seq == 0) return hipSuccess;
+  hipLaunchKernelGGL((coeff_kernel<S::BC, S::WP>), dim3((unsigned)kp.nchunks * (unsigned)gp.n_seq), dim3(256), 0,
+                     stream, kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped::linear_rec_kernel<S>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
+    (void)hipGetLastError();
+    attr_set = true;
+  }
+  const unsigned per_seq = (unsigned)(S::rows_k(gp.nchunks) / 32 + 2 * (size_t)gp.nchunks);
+  hipLaunchKernelGGL((grouped::phi_kernel<S>), dim3(per_seq * (unsigned)gp.n_seq), dim3(256), 0, stream, gp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((grouped::q1_phi_kernel<S>), dim3((unsigned)gp.nchunks * (unsigned)gp.n_seq), dim3(256), 0,
+                     stream, gp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((grouped::linear_rec_kernel<S>), dim3((unsigned)gp.n_seq), dim3(256), S::lds, stream, gp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((grouped::linear_ret_kernel<S>), dim3((unsigned)gp.nchunks * (unsigned)gp.n_seq), dim3(256), 0,
+                     stream, gp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+template <int PHI, int DK, int PD, int DV, int H, int G, int WP>
 hipError_t launch_grouped(const GroupedParams& gp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
                           hipEvent_t ev1) {
+  if constexpr (H == 0) {
+    static_assert(G == 1, "the linear memory runs one workgroup per sequence");
+    return launch_linear<PHI, DK, PD, DV, WP>(gp, kp, stream, ev0, ev1);
+  } else {
+  static_assert(WP == 128, "window rows of the grouped MLP kernel");
   typedef grouped::GShape<PHI, DK, PD, DV, H, G> S;
   if (gp.N == 0 || gp.n_seq == 0) return hipSuccess;
   hipLaunchKernelGGL((coeff_kernel<S::BC, S::WP>), dim3((unsigned)kp.nchunks * (unsigned)gp.n_seq), dim3(256), 0,
@@ -783,15 +1156,19 @@ hipError_t launch_grouped(const GroupedParams& gp, const CoeffParams& kp, hipStr
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;
+  }
 }
 
-template <int PHI, int DK, int PD, int DV, int H, int G>
-size_t grouped_seq_bytes(int nchunks) { return grouped::GShape<PHI, DK, PD, DV, H, G>::seq_bytes(nchunks); }
+template <int PHI, int DK, int PD, int DV, int H, int G, int WP>
+size_t grouped_seq_bytes(int nchunks) {
+  if constexpr (H == 0) return grouped::LShape<PHI, DK, PD, DV, WP>::seq_bytes(nchunks);
+  else return grouped::GShape<PHI, DK, PD, DV, H, G>::seq_bytes(nchunks);
+}
 
-#define ATLAS_GROUPED(NAME, PHI, DK, PD, DV, H, G)                                                             \
-  template hipError_t launch_grouped<PHI, DK, PD, DV, H, G>(const GroupedParams&, const CoeffParams&, hipStream_t, \
-                                                            hipEvent_t, hipEvent_t);                           \
-  template size_t grouped_seq_bytes<PHI, DK, PD, DV, H, G>(int);
+#define ATLAS_GROUPED(NAME, PHI, DK, PD, DV, H, G, WP)                                                       \
+  template hipError_t launch_grouped<PHI, DK, PD, DV, H, G, WP>(const GroupedParams&, const CoeffParams&,      \
+                                                                hipStream_t, hipEvent_t, hipEvent_t);          \
+  template size_t grouped_seq_bytes<PHI, DK, PD, DV, H, G, WP>(int);
 #include "atlas_mem_grouped_variants.inc"
 #undef ATLAS_GROUPED
 

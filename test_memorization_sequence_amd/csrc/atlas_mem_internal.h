@@ -230,10 +230,11 @@ struct GroupedParams {
   int momentum, bias, residual;
 };
 
-template <int PHI, int DK, int PD, int DV, int H, int G>
+// H = 0: the linear memory (G = 1); WP: window rows of the coefficient blocks
+template <int PHI, int DK, int PD, int DV, int H, int G, int WP>
 hipError_t launch_grouped(const GroupedParams& gp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
                           hipEvent_t ev1);
-template <int PHI, int DK, int PD, int DV, int H, int G>
+template <int PHI, int DK, int PD, int DV, int H, int G, int WP>
 size_t grouped_seq_bytes(int nchunks);
 
 template <int D, int DV, int H, int G, int WP, int BC>

@@ -73,10 +73,16 @@ def test_kernel_family_selection():
     for name in ("atlas_long", "linear_poly2", "linear64_delta"):
         assert binding.supported(binding.config_of(WORKLOADS[name], "streamed")) == binding.ERR_UNSUPPORTED
     # grouped family: the MLP memories (any feature map, chunk 64, c <= 64, l2 / dot bias)
-    for name in ("atlas_long", "layer_scale", "mlp64"):
+    # and the bf16 linear memories of its table; not fp32 io
+    for name in ("atlas_long", "layer_scale", "mlp64", "linear_poly2"):
         assert binding.supported(binding.config_of(WORKLOADS[name], "grouped")) == ok, name
-    for name in ("linear_poly2", "linear64_delta"):
-        assert binding.supported(binding.config_of(WORKLOADS[name], "grouped")) == binding.ERR_UNSUPPORTED
+    assert binding.supported(binding.config_of(WORKLOADS["linear64_delta"], "grouped")) == binding.ERR_UNSUPPORTED
+    assert binding.supported(binding.config_of(replace(WORKLOADS["linear64_delta"], io_dtype="bf16"), "grouped")) == ok
+    for kw in (dict(window=64), dict(window=33), dict(bias="dot"), dict(momentum=False)):
+        assert binding.supported(binding.config_of(replace(WORKLOADS["linear_poly2"], **kw), "grouped")) == ok, kw
+    for kw in (dict(bias="lp", bias_p=3.0), dict(optimizer="muon"), dict(d_v=64), dict(chunk=32, window=16)):
+        wl = replace(WORKLOADS["linear_poly2"], **kw)
+        assert binding.supported(binding.config_of(wl, "grouped")) == binding.ERR_UNSUPPORTED, kw
     for wl in (replace(WORKLOADS["atlas_long"], bias="lp", bias_p=3.0), replace(WORKLOADS["atlas_long"], layernorm=True),
                replace(WORKLOADS["atlas_long"], gated=True), replace(WORKLOADS["atlas_long"], optimizer="muon"),
                replace(WORKLOADS["atlas_long"], chunk=32, window=32)):
