@@ -47,6 +47,7 @@ namespace grouped {
 using namespace mfma;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // v_mfma_f32_16x16x16_bf16: lane l supplies row (l & 15) and k = 4 (l >> 4) .. +3
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
@@ -784,14 +785,25 @@ struct LShape {
   static constexpr int LF = DP + 8, LV = DV + 8;
   static constexpr size_t oMi = 0;                                  // M image [DV][LF]
   static constexpr size_t oD2 = oMi + align_up(DV * LF * 2, 256);   // D [WP][LV]
-  static constexpr size_t oF = oD2 + align_up(WP * LV * 2, 256);    // [2] x (cA[BC] cB[BC] cM[WP] cS[WP] P)
+  // two coefficient sets by chunk parity, each the head of the coefficient
+  // block as the coefficient kernel writes it: A[BC] B[BC] P (+3) cM[WP] cS[WP]
+  static constexpr size_t oF = oD2 + align_up(WP * LV * 2, 256);
   static constexpr int NCF = 2 * BC + 2 * WP + 4;
-  static constexpr size_t lds = oF + 2 * NCF * 4;
+  // the window's feature-major rows X^T [DP][WP] for the update, when they fit
+  static constexpr size_t oXTl = oF + align_up(2 * NCF * 4, 256);
+  static constexpr bool XT_LDS = oXTl + (size_t)DP * WP * 2 <= 163840;
+  static constexpr size_t lds = XT_LDS ? oXTl + (size_t)DP * WP * 2 : oF + 2 * NCF * 4;
   static_assert(lds <= 163840, "LDS budget of one CU");
   // workspace per sequence (bytes): a word the phi kernel clears (unused
   // here), the chunk-start images [nch][2][DV][DP] (M, then S), D of every
   // chunk [nch][WP][DV], then the phi buffers as in the MLP shapes
   static constexpr size_t xMask = 0;
+  // element (o, f) of a chunk-start image (M or S, DV x DP bf16): feature
+  // quad f / 4 major, then o % 16, then the value tile o / 16, then f % 4
+  static_assert(NOT % 2 == 0, "images are stored 8 values at a time");
+  __host__ __device__ static size_t img_pos(int o, int f) {
+    return ((size_t)(f >> 2) * 16 + (o & 15)) * (4 * NOT) + (o >> 4) * 4 + (f & 3);
+  }
   __host__ __device__ static size_t rows_k(int nch) { return (size_t)nch * BC + BC; }
   __host__ __device__ static size_t oImg(int) { return 256; }
   __host__ __device__ static size_t oDg(int nch) { return align_up(oImg(nch) + (size_t)nch * 2 * DV * DP * 2, 256); }
@@ -799,6 +811,20 @@ struct LShape {
   __host__ __device__ static size_t oXT(int nch) { return align_up(oXR(nch) + rows_k(nch) * DP * 2, 256); }
   __host__ __device__ static size_t oXQ(int nch) { return align_up(oXT(nch) + rows_k(nch) * DP * 2, 256); }
   __host__ __device__ static size_t seq_bytes(int nch) { return align_up(oXQ(nch) + (size_t)nch * BC * DP * 2, 256); }
+};
+
+// X^T rows [DP][WP] of one window into LDS (row-major, pitch WP) by direct
+// loads of 1 KB per wave instruction.  J instructions cover exactly R rows, so
+// each lane's J byte offsets are fixed for the call and only a wave-uniform
+// offset moves with the super block and the window.
+template <class S>
+struct XtStage {
+  static constexpr int RB = S::WP * 2;   // bytes per row
+  static constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+  static constexpr int J = RB / gcd(RB, 1024);   // lcm(RB, 1024) / 1024
+  static constexpr int R = J * 1024 / RB;
+  static constexpr int NSB = S::DP / R;
+  static_assert(S::DP % R == 0 && NSB % 4 == 0, "whole super blocks, the same count per wave");
 };
 
 template <class S>
@@ -810,7 +836,8 @@ linear_rec_kernel(GroupedParams p) {
   extern __shared__ __attribute__((aligned(256))) char smem[];
   const int seq = (int)blockIdx.x;
   if (seq >= p.n_seq) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
   const int N = p.N, c = p.c, W = BC + c - 1, nch = p.nchunks;
   const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT;
   const float s_grad = p.grad_scale;
@@ -837,6 +864,8 @@ linear_rec_kernel(GroupedParams p) {
   bf16* Mi = reinterpret_cast<bf16*>(smem + S::oMi);
   bf16* D2l = reinterpret_cast<bf16*>(smem + S::oD2);
   float* cf = reinterpret_cast<float*>(smem + S::oF);   // two coefficient sets, by chunk parity
+  bf16* XTl = reinterpret_cast<bf16*>(smem + S::oXTl);
+  const float* coef0 = p.coef + (size_t)seq * nch * p.coef_stride;
 
   // ---- state into registers: MT[m][o][r] = M[16 o + c16][16 (wave + 4 m) + 4 g + r], same for S
   f32x4 MT[FPW][NOT], ST[FPW][NOT];
@@ -855,48 +884,135 @@ linear_rec_kernel(GroupedParams p) {
           ST[m][o][r] = gload1(rm, off);
         }
   }
-  // images of the chunk-start state of chunk chn: M into LDS (the window
-  // forward's operand), M and S into the workspace (the retrieval's)
+  // images of the chunk-start state of chunk chn: M into LDS [o][f] (the
+  // window forward's operand); M and S into the workspace (the retrieval's)
+  // in the quad-major order of S::img_pos, where a lane's values for all
+  // value tiles at one feature quad are adjacent and a wave's store covers
+  // one contiguous 64 NOT-element run
   auto write_images = [&](int chn) {
     bf16* im = img + (size_t)chn * 2 * DV * DP;
 #pragma unroll
-    for (int m = 0; m < FPW; ++m)
+    for (int m = 0; m < FPW; ++m) {
+      const int f0 = 16 * (wave + 4 * m) + 4 * g;
+      bf16 wq[4 * NOT], sq[4 * NOT];
 #pragma unroll
       for (int o = 0; o < NOT; ++o) {
-        const int f0 = 16 * (wave + 4 * m) + 4 * g, orow = 16 * o + c16;
+        const int orow = 16 * o + c16;
         const bf16x4 wv{(bf16)MT[m][o][0], (bf16)MT[m][o][1], (bf16)MT[m][o][2], (bf16)MT[m][o][3]};
-        const bf16x4 sv{(bf16)ST[m][o][0], (bf16)ST[m][o][1], (bf16)ST[m][o][2], (bf16)ST[m][o][3]};
         *reinterpret_cast<bf16x4*>(Mi + orow * LF + f0) = wv;
-        *reinterpret_cast<bf16x4*>(im + (size_t)orow * DP + f0) = wv;
-        *reinterpret_cast<bf16x4*>(im + (size_t)(DV + orow) * DP + f0) = sv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          wq[4 * o + r] = wv[r];
+          sq[4 * o + r] = (bf16)ST[m][o][r];
+        }
       }
+      const size_t q0 = S::img_pos(c16, f0);
+#pragma unroll
+      for (int h = 0; h < NOT / 2; ++h) {
+        *reinterpret_cast<bf16x8*>(im + q0 + 8 * h) = *reinterpret_cast<const bf16x8*>(wq + 8 * h);
+        *reinterpret_cast<bf16x8*>(im + (size_t)DV * DP + q0 + 8 * h) = *reinterpret_cast<const bf16x8*>(sq + 8 * h);
+      }
+    }
   };
   write_images(0);
+
+  // Per chunk: the window forward, D, the update; then, at the end of the
+  // chunk, everything the next one needs that does not depend on the state:
+  // its coefficients and window values (registers), and, where they fit, its
+  // X^T rows (LDS, by direct loads; the window forward reads X from them
+  // through transposed LDS reads).  Those loads are issued after the image
+  // stores and waited for before the next chunk's first barrier, so store
+  // drain and load latency overlap.
+  constexpr int NCR = (NCF + 255) / 256;
+  const __amdgpu_buffer_rsrc_t rv = buffer_of(v, (unsigned)((size_t)N * DV * 2));
+  const __amdgpu_buffer_rsrc_t rgm = buffer_of(gam_in, (unsigned)((size_t)N * 4));
+  const __amdgpu_buffer_rsrc_t rhv = buffer_of(hv, (unsigned)((c - 1) * DV * 4));
+  const __amdgpu_buffer_rsrc_t rhg = buffer_of(hg, (unsigned)((c - 1) * 4));
+  // this lane's byte offsets in X^T for the staging of a window
+  int xt_voff[XtStage<S>::J];
+#pragma unroll
+  for (int j = 0; j < XtStage<S>::J; ++j) {
+    const int off = j * 1024 + lane * 16;
+    xt_voff[j] = (off / XtStage<S>::RB) * (int)NR * 2 + off % XtStage<S>::RB;
+  }
+  float cnext[NCR];
+  float4 pv[YPW];
+  float pg[YPW];
+  auto fetch = [&](int chn) {
+    const int t0n = chn * BC, ten = min(N, t0n + BC) - 1;
+    const float* cn = coef0 + (size_t)chn * p.coef_stride;
+#pragma unroll
+    for (int u = 0; u < NCR; ++u) cnext[u] = tid + 256 * u < NCF ? cn[tid + 256 * u] : 0.f;
+    // branch-free: both sources are read through range-checked descriptors;
+    // the one not meant reads zero at an offset out of range, so the sum is
+    // the valid value
+#pragma unroll
+    for (int u = 0; u < YPW; ++u) {
+      const int ot = (wave + 4 * u) % NOT, wt = (wave + 4 * u) / NOT;
+      const int w = 16 * wt + c16, o4 = 16 * ot + 4 * g;
+      const int i = t0n - (c - 1) + w;
+      const bool valid = w < W && i >= -halo_valid && i <= ten;
+      const bool cur = valid && i >= 0, old = valid && i < 0;
+      const u32x2 vv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+          rv, cur ? (i * DV + o4) * 2 : kZeroOffset, 0, 0));
+      const f32x4 hv4 = buf_load4(rhv, old ? ((c - 1 + i) * DV + o4) * 4 : kZeroOffset, 0);
+      const float gc = gload1(rgm, cur ? i * 4 : kZeroOffset);
+      const float gh = gload1(rhg, old ? (c - 1 + i) * 4 : kZeroOffset);
+      const bf16x4 vb = __builtin_bit_cast(bf16x4, vv);
+      pv[u] = make_float4((float)vb[0] + hv4[0], (float)vb[1] + hv4[1], (float)vb[2] + hv4[2], (float)vb[3] + hv4[3]);
+      pg[u] = gc + gh;
+    }
+    if constexpr (S::XT_LDS) {
+      typedef XtStage<S> X;
+#pragma unroll
+      for (int k = 0; k < X::NSB / 4; ++k) {
+        const int sb = wave + 4 * k;
+        const int soff = (sb * X::R * (int)NR + t0n) * 2;
+#pragma unroll
+        for (int j = 0; j < X::J; ++j)
+          buf_load_lds16(rxt, reinterpret_cast<char*>(XTl) + (sb * X::J + j) * 1024, xt_voff[j], soff);
+      }
+    }
+  };
+  auto store_coef = [&](int chn) {
+    float* cn = cf + (chn & 1) * NCF;
+#pragma unroll
+    for (int u = 0; u < NCR; ++u)
+      if (tid + 256 * u < NCF) cn[tid + 256 * u] = cnext[u];
+  };
+  fetch(0);
+  wait_vmem();
+  store_coef(0);
 
   for (int ch = 0; ch < nch; ++ch) {
     const int t0 = ch * BC;
     const int te = min(N, t0 + BC) - 1;
-    float* cA = cf + (ch & 1) * NCF;
-    float* cB = cA + BC;
-    float* cM = cB + BC;
-    float* cS = cM + WP;
-    float* cP = cS + WP;
-    {
-      const float* coef = p.coef + ((size_t)seq * nch + ch) * p.coef_stride;
-      if (tid < BC) { cA[tid] = coef[tid]; cB[tid] = coef[BC + tid]; }
-      if (tid < WP) { cM[tid] = coef[2 * BC + 4 + tid]; cS[tid] = coef[2 * BC + 4 + WP + tid]; }
-      if (tid == 0) cP[0] = coef[2 * BC];
-    }
-    __syncthreads();   // coefficients and the M image of the chunk-start state
+    const float* cA = cf + (ch & 1) * NCF;
+    const float* cB = cA + BC;
+    const float* cP = cA + 2 * BC;
+    const float* cM = cA + 2 * BC + 4;
+    const float* cS = cM + WP;
+    __syncthreads();   // coefficients, the M image of the chunk-start state, X^T
 
+    __builtin_amdgcn_sched_barrier(0);
     // ---- window forward, transposed: Y^T [value rows x window rows], K = DP.
-    // Wave tiles i = wave + 4u: value tile i % NOT, window tile i / NOT; the
-    // X fragments of step s + PF are loaded before step s computes.
+    // Wave tiles i = wave + 4u: value tile i % NOT, window tile i / NOT.
     f32x4 Y[YPW];
 #pragma unroll
     for (int u = 0; u < YPW; ++u) Y[u] = zero4();
-    {
-      constexpr int NS = DP / 32, PF = 4;
+    if constexpr (S::XT_LDS) {
+#pragma unroll 2
+      for (int s = 0; s < DP / 32; ++s) {
+#pragma unroll
+        for (int u = 0; u < YPW; ++u) {
+          const int ot = (wave + 4 * u) % NOT, wt = (wave + 4 * u) / NOT;
+          Y[u] = mma(ld_nat(Mi, LF, 16 * ot, 32 * s, lane), ld_tr_nat(XTl, WP, 16 * wt, 32 * s, lane), Y[u]);
+        }
+      }
+    } else {
+      // X rows from the phi buffer; the fragments of step s + PF are loaded
+      // before step s computes
+      constexpr int NS = DP / 32, PF = 3;
       bf16x8 xf[PF + 1][YPW];
       auto load = [&](int s, bf16x8* dst) {
 #pragma unroll
@@ -919,32 +1035,21 @@ linear_rec_kernel(GroupedParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // ---- D = s gamma (Y - V) (dot: -s gamma V) of the valid window rows, zero
-    // elsewhere: into LDS [WP][LV] and the workspace [WP][DV]
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- D = s gamma (Y - V) (dot: -s gamma V) of the valid window rows
+    // (zero elsewhere: pg = 0 there): into LDS [WP][LV] and the workspace [WP][DV]
 #pragma unroll
     for (int u = 0; u < YPW; ++u) {
       const int ot = (wave + 4 * u) % NOT, wt = (wave + 4 * u) / NOT;
       const int w = 16 * wt + c16, o4 = 16 * ot + 4 * g;
       const int i = t0 - (c - 1) + w;
       const bool valid = w < W && i >= -halo_valid && i <= te;
-      float4 pv = make_float4(0.f, 0.f, 0.f, 0.f);
-      float pg = 0.f;
-      if (valid) {
-        if (i >= 0) {
-          const bf16x4 vv = *reinterpret_cast<const bf16x4*>(v + (size_t)i * DV + o4);
-          pv = make_float4((float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]);
-          pg = gam_in[i];
-        } else {
-          pv = *reinterpret_cast<const float4*>(hv + (c - 1 + i) * DV + o4);
-          pg = hg[c - 1 + i];
-        }
-      }
-      const float sg = s_grad * pg;
+      const float sg = s_grad * pg[u];
       float d[4];
-      d[0] = dot ? -sg * pv.x : sg * (Y[u][0] - pv.x);
-      d[1] = dot ? -sg * pv.y : sg * (Y[u][1] - pv.y);
-      d[2] = dot ? -sg * pv.z : sg * (Y[u][2] - pv.z);
-      d[3] = dot ? -sg * pv.w : sg * (Y[u][3] - pv.w);
+      d[0] = dot ? -sg * pv[u].x : sg * (Y[u][0] - pv[u].x);
+      d[1] = dot ? -sg * pv[u].y : sg * (Y[u][1] - pv[u].y);
+      d[2] = dot ? -sg * pv[u].z : sg * (Y[u][2] - pv[u].z);
+      d[3] = dot ? -sg * pv[u].w : sg * (Y[u][3] - pv[u].w);
       const bf16x4 d4 = valid ? bf16x4{(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]}
                               : bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
       *reinterpret_cast<bf16x4*>(D2l + w * LV + o4) = d4;
@@ -952,6 +1057,7 @@ linear_rec_kernel(GroupedParams p) {
     }
     __syncthreads();   // D complete
 
+    __builtin_amdgcn_sched_barrier(0);
     // ---- update, transposed: (cM .* D)^T X as [feature rows x value cols], K = WP;
     // the wave's feature tiles 16 (wave + 4 m), every value tile
     {
@@ -971,7 +1077,10 @@ linear_rec_kernel(GroupedParams p) {
       auto load = [&](int m, bf16x8* dst) {
         const int f = 16 * (wave + 4 * m) + c16;
 #pragma unroll
-        for (int s = 0; s < WP / 32; ++s) dst[s] = gload8(rxt, (f * (int)NR + t0 + 32 * s + 8 * g) * 2);
+        for (int s = 0; s < WP / 32; ++s) {
+          if constexpr (S::XT_LDS) dst[s] = ld_nat(XTl, WP, 16 * (wave + 4 * m), 32 * s, lane);
+          else dst[s] = gload8(rxt, (f * (int)NR + t0 + 32 * s + 8 * g) * 2);
+        }
       };
       load(0, xf[0]);
 #pragma unroll
@@ -996,9 +1105,20 @@ linear_rec_kernel(GroupedParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // every wave is past its reads of the M image (the window forward ended
-    // before the last barrier): the next chunk's images
-    if (ch + 1 < nch) write_images(ch + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- the next chunk's images (the window forward's reads of the M image
+    // ended before the last barrier), then its inputs.  X^T in LDS is
+    // overwritten only once every wave is past its update; the coefficient
+    // set of chunk ch + 1 was last read in chunk ch - 1.
+    if (ch + 1 < nch) {
+      write_images(ch + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (S::XT_LDS) __syncthreads();
+      fetch(ch + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (S::XT_LDS) wait_vmem();
+      store_coef(ch + 1);
+    }
   }
 
   // ---- the state back to memory
@@ -1060,13 +1180,20 @@ __global__ void __launch_bounds__(256) linear_ret_kernel(GroupedParams p) {
 #pragma unroll
   for (int o = 0; o < NOT; ++o) a1[o] = a2[o] = a3[o] = zero4();
   const int qrow = t0 + 16 * wave + c16;
+  // row 16 o + c16, features 32 s + 8 g .. +7 of an image: two quads
+  auto img_frag = [&](int base, int o, int s) {
+    const int q = (int)S::img_pos(16 * o + c16, 32 * s + 8 * g);
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rim, (base + q) * 2, 0, 0));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rim, (base + q + 64 * NOT) * 2, 0, 0));
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
 #pragma unroll 2
   for (int s = 0; s < DP / 32; ++s) {
     const bf16x8 xq = gload8(rxq, (qrow * DP + 32 * s + 8 * g) * 2);
 #pragma unroll
     for (int o = 0; o < NOT; ++o) {
-      a1[o] = mma(gload8(rim, ((16 * o + c16) * DP + 32 * s + 8 * g) * 2), xq, a1[o]);
-      if (mom) a2[o] = mma(gload8(rim, ((DV + 16 * o + c16) * DP + 32 * s + 8 * g) * 2), xq, a2[o]);
+      a1[o] = mma(img_frag(0, o, s), xq, a1[o]);
+      if (mom) a2[o] = mma(img_frag(DV * DP, o, s), xq, a2[o]);
     }
   }
   __syncthreads();   // D in LDS
