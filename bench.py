@@ -46,7 +46,7 @@ MEASURED_TRAFFIC = {
 # translation unit of each recurrent kernel
 KERNEL_SOURCE = {"stream_mlp_kernel": "atlas_mem_stream.hip", "sharded_mlp_kernel": "atlas_mem_sharded.hip",
                  "chunk_kernel": "atlas_mem_kernels.hip", "grouped_kernel": "atlas_mem_grouped.hip",
-                 "linear_rec_kernel": "atlas_mem_grouped.hip"}
+                 "linear_rec_kernel": "atlas_mem_linear.hip"}
 
 
 def kernel_source_hash(kernel: str) -> str:

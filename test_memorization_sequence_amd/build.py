@@ -11,6 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libatlas_mem.so")
 SOURCES = ["atlas_mem_kernels.hip", "atlas_mem_sharded.hip", "atlas_mem_stream.hip", "atlas_mem_grouped.hip",
+           "atlas_mem_linear.hip",
            "atlas_mem_api.hip", "atlas_prologue.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

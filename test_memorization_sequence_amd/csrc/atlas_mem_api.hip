@@ -10,6 +10,7 @@
 
 #include "atlas_mem.h"
 #include "atlas_mem_internal.h"
+#include "atlas_mem_linear.h"
 
 namespace atlas {
 
@@ -72,13 +73,15 @@ struct GroupedVariant {
   GroupedLaunchFn launch;
 };
 
-#define ATLAS_GROUPED(NAME, PHI, DK, PD, DV, H, G, WP)                                             \
-  {#NAME, PHI, DK, PD, DV, H, G, WP, &grouped_seq_bytes<PHI, DK, PD, DV, H, G, WP>, \
-   &launch_grouped<PHI, DK, PD, DV, H, G, WP>},
+#define ATLAS_GROUPED(NAME, PHI, DK, PD, DV, H, G) \
+  {#NAME, PHI, DK, PD, DV, H, G, 128, &grouped_seq_bytes<PHI, DK, PD, DV, H, G>, &launch_grouped<PHI, DK, PD, DV, H, G>},
+#define ATLAS_LINEAR(NAME, PHI, DK, PD, DV, WP) \
+  {#NAME, PHI, DK, PD, DV, 0, 1, WP, &linear_seq_bytes<PHI, DK, PD, DV, WP>, &launch_linear<PHI, DK, PD, DV, WP>},
 static const GroupedVariant kGrouped[] = {
 #include "atlas_mem_grouped_variants.inc"
 };
 #undef ATLAS_GROUPED
+#undef ATLAS_LINEAR
 
 }  // namespace atlas
 

@@ -63,11 +63,6 @@ __device__ __forceinline__ void buf_load_lds(__amdgpu_buffer_rsrc_t r, void* dst
   if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voff, 0, 0, 0);
   else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 4, voff, 0, 0, 0);
 }
-// The same with a wave-uniform byte offset soff added to voff.
-__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* dst, int voff, int soff) {
-  typedef __attribute__((address_space(3))) void* lds_ptr;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voff, soff, 0, 0);
-}
 // wait for every vector-memory access of this wave (loads to LDS included)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
 constexpr int kZeroOffset = 0x7FFFFF00;   // beyond every buffer the kernels address

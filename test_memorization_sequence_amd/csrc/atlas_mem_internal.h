@@ -230,11 +230,10 @@ struct GroupedParams {
   int momentum, bias, residual;
 };
 
-// H = 0: the linear memory (G = 1); WP: window rows of the coefficient blocks
-template <int PHI, int DK, int PD, int DV, int H, int G, int WP>
+template <int PHI, int DK, int PD, int DV, int H, int G>
 hipError_t launch_grouped(const GroupedParams& gp, const CoeffParams& kp, hipStream_t stream, hipEvent_t ev0,
                           hipEvent_t ev1);
-template <int PHI, int DK, int PD, int DV, int H, int G, int WP>
+template <int PHI, int DK, int PD, int DV, int H, int G>
 size_t grouped_seq_bytes(int nchunks);
 
 template <int D, int DV, int H, int G, int WP, int BC>
