@@ -42,6 +42,8 @@ __device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); 
 __device__ __forceinline__ float sigm(float z) { return 1.f / (1.f + __expf(-z)); }
 
 constexpr int TOK = 32;   // tokens per wave
+constexpr int TB = 8;     // tokens per load batch
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D, int K>
 __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
@@ -76,37 +78,80 @@ __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
   const int g = lane / p.r, jj = lane - g * p.r;
   const float gvv = g < 4 ? p.gv[(g * p.H + h) * p.r + jj] : 0.f;
   const float gbb = g < 4 ? p.gb[g * p.H + h] : 0.f;
-  for (int n = n0; n < n1; ++n) {
-    const bf16* row = p.P + (size_t)(b * p.N + n) * p.ncol;
+  // Tokens in batches of TB: every projection value of the batch is loaded
+  // first (rows past the run re-read its last row and are not stored), so
+  // one memory latency covers TB tokens; then the batch is computed in order.
+  for (int nb = n0; nb < n1; nb += TB) {
+    float x[TB][3][DPL], xg[TB], gq[TB];
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      const bf16* src = row + m * HD + h * D + lane * DPL;
-      float acc[DPL];
-      float ss = 0.f;
+    for (int t = 0; t < TB; ++t) {
+      const int n = min(nb + t, n1 - 1);
+      const bf16* row = p.P + (size_t)(b * p.N + n) * p.ncol;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        win[m][i][K - 1] = (float)src[i];
-        float a = 0.f;
+      for (int m = 0; m < 3; ++m) {
+        const bf16* src = row + m * HD + h * D + lane * DPL;
+        if constexpr (DPL == 2) {
+          const bf16x2 v2 = *reinterpret_cast<const bf16x2*>(src);
+          x[t][m][0] = (float)v2[0];
+          x[t][m][1] = (float)v2[1];
+        } else {
 #pragma unroll
-        for (int j = 0; j < K; ++j) a = fmaf(tap[m][i][j], win[m][i][j], a);
-#pragma unroll
-        for (int j = 0; j + 1 < K; ++j) win[m][i][j] = win[m][i][j + 1];
-        acc[i] = silu(a);
-        ss = fmaf(acc[i], acc[i], ss);
+          for (int i = 0; i < DPL; ++i) x[t][m][i] = (float)src[i];
+        }
       }
-      float scale = 1.f;
-      if (m < 2) {
-#pragma unroll
-        for (int s2 = 32; s2 >= 1; s2 >>= 1) ss += __shfl_xor(ss, s2);
-        scale = 1.f / fmaxf(sqrtf(ss), 1e-12f);
-      }
-      bf16* o = outs[m] + ((size_t)(b * p.H + h) * p.N + n) * D + lane * DPL;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) o[i] = (bf16)(acc[i] * scale);
+      xg[t] = g < 4 ? (float)row[3 * HD + lane] : 0.f;
     }
-    float u = g < 4 ? (float)row[3 * HD + lane] * gvv : 0.f;
-    for (int s2 = 1; s2 < p.r; s2 <<= 1) u += __shfl_xor(u, s2);   // within aligned groups of r lanes
-    if (g < 4 && jj == 0) p.gate[g][(size_t)(b * p.H + h) * p.N + n] = sigm(u + gbb);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const int n = nb + t;
+      if (n >= n1) break;
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        float acc[DPL];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          win[m][i][K - 1] = x[t][m][i];
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < K; ++j) a = fmaf(tap[m][i][j], win[m][i][j], a);
+#pragma unroll
+          for (int j = 0; j + 1 < K; ++j) win[m][i][j] = win[m][i][j + 1];
+          acc[i] = silu(a);
+          ss = fmaf(acc[i], acc[i], ss);
+        }
+        float scale = 1.f;
+        if (m < 2) {
+#pragma unroll
+          for (int s2 = 32; s2 >= 1; s2 >>= 1) ss += __shfl_xor(ss, s2);
+          scale = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+        }
+        bf16* o = outs[m] + ((size_t)(b * p.H + h) * p.N + n) * D + lane * DPL;
+        if constexpr (DPL == 2) {
+          *reinterpret_cast<bf16x2*>(o) = bf16x2{(bf16)(acc[0] * scale), (bf16)(acc[1] * scale)};
+        } else {
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) o[i] = (bf16)(acc[i] * scale);
+        }
+      }
+      float u = xg[t] * gvv;
+      for (int s2 = 1; s2 < p.r; s2 <<= 1) u += __shfl_xor(u, s2);   // within aligned groups of r lanes
+      gq[t] = sigm(u + gbb);
+    }
+    // the batch's gates: lane g r of each of the four groups writes TB
+    // consecutive values of its gate (32 bytes) rather than one per token
+    if (g < 4 && jj == 0) {
+      float* dst = p.gate[g] + (size_t)(b * p.H + h) * p.N + nb;
+      if (n1 - nb >= TB && ((uintptr_t)dst & 15) == 0) {
+#pragma unroll
+        for (int t = 0; t < TB; t += 4)
+          *reinterpret_cast<float4*>(dst + t) = make_float4(gq[t], gq[t + 1], gq[t + 2], gq[t + 3]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+          if (nb + t < n1) dst[t] = gq[t];
+      }
+    }
   }
 }
 
