@@ -38,8 +38,10 @@ struct Params {
   int B, N, H, K, r, ncol;
 };
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
-__device__ __forceinline__ float sigm(float z) { return 1.f / (1.f + __expf(-z)); }
+// SiLU and the logistic with the hardware reciprocal (about 1 ulp in fp32;
+// the outputs are bf16): z -> -inf gives rcp(inf) = 0, z -> +inf gives 1
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+__device__ __forceinline__ float sigm(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 constexpr int TOK = 32;   // tokens per wave
 constexpr int TB = 8;     // tokens per load batch
@@ -72,7 +74,9 @@ __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j + 1 < K; ++j) {
         const int src = n0 - (K - 1) + j;
-        win[m][i][j] = src >= 0 ? (float)p.P[(size_t)(b * p.N + src) * p.ncol + ch] : 0.f;
+        // a ring when K divides the batch (token n in slot n mod K; n0 is a
+        // multiple of TB), else oldest first
+        win[m][i][TB % K == 0 ? (j + 1) % K : j] = src >= 0 ? (float)p.P[(size_t)(b * p.N + src) * p.ncol + ch] : 0.f;
       }
     }
   const int g = lane / p.r, jj = lane - g * p.r;
@@ -111,12 +115,18 @@ __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) {
-          win[m][i][K - 1] = x[t][m][i];
           float a = 0.f;
+          if constexpr (TB % K == 0) {
+            win[m][i][t % K] = x[t][m][i];
 #pragma unroll
-          for (int j = 0; j < K; ++j) a = fmaf(tap[m][i][j], win[m][i][j], a);
+            for (int j = 0; j < K; ++j) a = fmaf(tap[m][i][j], win[m][i][(t + 1 + j) % K], a);
+          } else {
+            win[m][i][K - 1] = x[t][m][i];
 #pragma unroll
-          for (int j = 0; j + 1 < K; ++j) win[m][i][j] = win[m][i][j + 1];
+            for (int j = 0; j < K; ++j) a = fmaf(tap[m][i][j], win[m][i][j], a);
+#pragma unroll
+            for (int j = 0; j + 1 < K; ++j) win[m][i][j] = win[m][i][j + 1];
+          }
           acc[i] = silu(a);
           ss = fmaf(acc[i], acc[i], ss);
         }
@@ -124,7 +134,7 @@ __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
         if (m < 2) {
 #pragma unroll
           for (int s2 = 32; s2 >= 1; s2 >>= 1) ss += __shfl_xor(ss, s2);
-          scale = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+          scale = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(|x|, 1e-12)
         }
         bf16* o = outs[m] + ((size_t)(b * p.H + h) * p.N + n) * D + lane * DPL;
         if constexpr (DPL == 2) {
