@@ -22,9 +22,13 @@
 
 #include "atlas_prologue.h"
 #include "atlas_mem_internal.h"
+#include "atlas_mem_frag.h"
 
 namespace atlas {
 namespace prologue {
+
+using mfma::buffer_of;
+using mfma::kZeroOffset;
 
 struct Params {
   const bf16* P;       // [B*N][ncol] projections
@@ -38,6 +42,30 @@ struct Params {
   int B, N, H, K, r, ncol;
 };
 
+// Cross-lane sums by DPP moves (full-rate vector ops, no LDS round trip):
+// xor 1 and xor 2 within quads, then the half-row and row mirrors, leave the
+// sum of each aligned group of 2, 4, 8 or 16 lanes in all of its lanes.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float group_sum(float v, int width) {
+  if (width >= 2) v += dppf<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (width >= 4) v += dppf<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (width >= 8) v += dppf<0x141>(v);   // row_half_mirror
+  if (width >= 16) v += dppf<0x140>(v);  // row_mirror
+  return v;
+}
+// the sum over all 64 lanes, the same in every lane
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum(v, 16);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // SiLU and the logistic with the hardware reciprocal (about 1 ulp in fp32;
 // the outputs are bf16): z -> -inf gives rcp(inf) = 0, z -> +inf gives 1
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
@@ -46,6 +74,7 @@ __device__ __forceinline__ float sigm(float z) { return __builtin_amdgcn_rcpf(1.
 constexpr int TOK = 32;   // tokens per wave
 constexpr int TB = 8;     // tokens per load batch
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 template <int D, int K>
 __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
@@ -85,26 +114,41 @@ __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
   // Tokens in batches of TB: every projection value of the batch is loaded
   // first (rows past the run re-read its last row and are not stored), so
   // one memory latency covers TB tokens; then the batch is computed in order.
+  // the batch's rows through one descriptor (base and token offsets in
+  // scalar registers, this lane's column offsets fixed for the run); gate
+  // columns past the 4 r the ranks use read zero
+  const int voff_m = (h * D + lane * DPL) * 2;
+  const int voff_g = g < 4 ? (3 * HD + lane) * 2 : kZeroOffset;
   for (int nb = n0; nb < n1; nb += TB) {
     float x[TB][3][DPL], xg[TB], gq[TB];
+    const int nlast = n1 - 1 - nb;
+    const __amdgpu_buffer_rsrc_t rp = buffer_of(p.P + (size_t)(b * p.N + nb) * p.ncol, (unsigned)(TB * p.ncol * 2));
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
-      const int n = min(nb + t, n1 - 1);
-      const bf16* row = p.P + (size_t)(b * p.N + n) * p.ncol;
+      const int soff = min(t, nlast) * p.ncol * 2;
 #pragma unroll
       for (int m = 0; m < 3; ++m) {
-        const bf16* src = row + m * HD + h * D + lane * DPL;
-        if constexpr (DPL == 2) {
-          const bf16x2 v2 = *reinterpret_cast<const bf16x2*>(src);
+        if constexpr (DPL == 1) {
+          x[t][m][0] = (float)__builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(rp, voff_m + m * HD * 2, soff, 0));
+        } else if constexpr (DPL == 2) {
+          const bf16x2 v2 = __builtin_bit_cast(bf16x2, __builtin_amdgcn_raw_buffer_load_b32(rp, voff_m + m * HD * 2, soff, 0));
           x[t][m][0] = (float)v2[0];
           x[t][m][1] = (float)v2[1];
         } else {
+          static_assert(DPL % 4 == 0, "channels per lane");
 #pragma unroll
-          for (int i = 0; i < DPL; ++i) x[t][m][i] = (float)src[i];
+          for (int i = 0; i < DPL; i += 4) {
+            const bf16x4 v4 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(rp, voff_m + (m * HD + i) * 2, soff, 0));
+#pragma unroll
+            for (int z = 0; z < 4; ++z) x[t][m][i + z] = (float)v4[z];
+          }
         }
       }
-      xg[t] = g < 4 ? (float)row[3 * HD + lane] : 0.f;
+      xg[t] = (float)__builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(rp, voff_g, soff, 0));
     }
+    bf16* ob[3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) ob[m] = outs[m] + ((size_t)(b * p.H + h) * p.N + nb) * D + lane * DPL;
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       const int n = nb + t;
@@ -132,11 +176,10 @@ __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
         }
         float scale = 1.f;
         if (m < 2) {
-#pragma unroll
-          for (int s2 = 32; s2 >= 1; s2 >>= 1) ss += __shfl_xor(ss, s2);
+          ss = wave_sum(ss);
           scale = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(|x|, 1e-12)
         }
-        bf16* o = outs[m] + ((size_t)(b * p.H + h) * p.N + n) * D + lane * DPL;
+        bf16* o = ob[m] + t * D;
         if constexpr (DPL == 2) {
           *reinterpret_cast<bf16x2*>(o) = bf16x2{(bf16)(acc[0] * scale), (bf16)(acc[1] * scale)};
         } else {
@@ -145,7 +188,7 @@ __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
         }
       }
       float u = xg[t] * gvv;
-      for (int s2 = 1; s2 < p.r; s2 <<= 1) u += __shfl_xor(u, s2);   // within aligned groups of r lanes
+      u = group_sum(u, p.r);   // within aligned groups of r lanes
       gq[t] = sigm(u + gbb);
     }
     // the batch's gates: lane g r of each of the four groups writes TB
