@@ -81,7 +81,8 @@ __global__ void __launch_bounds__(256) prologue_kernel(Params p) {
   constexpr int DPL = D / 64;
   const int lane = threadIdx.x & 63;
   const int tiles = (p.N + TOK - 1) / TOK;
-  const long item = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform (scalar registers): the row descriptors below need it
+  const long item = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const long items = (long)p.B * tiles * p.H;
   if (item >= items) return;
   const int h = (int)(item % p.H);
