@@ -227,7 +227,7 @@ grouped_kernel(GroupedParams p) {
   auto reduce_out = [&](int pc) {
     constexpr int NP = S::NPAIR_O, NS = S::NSPLIT_O, PER = G / NS;
     const int pt0 = pc * BC, pte = min(N, pt0 + BC) - 1;
-    const int e = tid % NP, h = tid / NP;
+    const int tf = fresh(tid), e = tf % NP, h = tf / NP;
     const int qq = pm * RQ + e / (DV / 4), o4 = (e % (DV / 4)) * 4;
     const float* yo = yobuf + (size_t)(pc & 1) * G * BC * DV + (size_t)qq * DV + o4;
     float4 part[PER];
@@ -340,7 +340,7 @@ grouped_kernel(GroupedParams p) {
     // ---- reduce-scatter: this member's window rows -> D2 rows; the previous chunk's outputs
     {
       constexpr int NP = S::NPAIR, NS = S::NSPLIT, PER = G / NS;
-      const int e = tid % NP, h = tid / NP;
+      const int tf = fresh(tid), e = tf % NP, h = tf / NP;
       const int w = pm * RW + e / (DV / 4), o4 = (e % (DV / 4)) * 4;
       float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
       if (!dot) {
@@ -399,12 +399,12 @@ grouped_kernel(GroupedParams p) {
       bf16x8 t8[NG];
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int e = tid + 256 * u;
+        const int e = fresh(tid) + 256 * u;
         t8[u] = *reinterpret_cast<const bf16x8*>(d2b + (size_t)(e / (DV / 8)) * DV + (e % (DV / 8)) * 8);
       }
 #pragma unroll
       for (int u = 0; u < NG; ++u) {
-        const int e = tid + 256 * u;
+        const int e = fresh(tid) + 256 * u;
         *reinterpret_cast<bf16x8*>(D2 + (e / (DV / 8)) * LV + (e % (DV / 8)) * 8) = t8[u];
       }
     }
