@@ -35,10 +35,11 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 MEASURED_TRAFFIC = {
     # (workload, kernel, optimizer, tokens per sequence), l2 bias, plain memory
     ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "b920309114fffec3", "bytes": 75.08e9},
-    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "7e4638cf1ae49799", "bytes": 28.13e9},
-    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "9aa8cf83d3cedd91", "bytes": 91.84e9},
+    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "adf685316c69b214", "bytes": 27.91e9},
+    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "fa58fd57df42e5c3", "bytes": 91.68e9},
     ("linear64_delta", "chunk_kernel", "gd", 1024): {"src": "fa58fd57df42e5c3", "bytes": 1.67e6},
-    ("linear_poly2", "chunk_kernel", "gd", 4096): {"src": "fa58fd57df42e5c3", "bytes": 65.76e6},
+    # the recurrence and the retrieval after it (the pair the kernel events bracket)
+    ("linear_poly2", "linear_rec_kernel", "gd", 4096): {"src": "50154b8d85754b04", "bytes": 0.344e9},
     ("mlp64", "sharded_mlp_kernel", "gd", 8192): {"src": "82f6190e28b55961", "bytes": 1.797e9},
 }
 
