@@ -579,6 +579,9 @@ stream_mlp_kernel(ShardedParams p) {
   const int wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const __amdgpu_buffer_rsrc_t rT = buffer_of(xw + S::xTS, 4u * H * D * 4);
   const __amdgpu_buffer_rsrc_t rW = buffer_of(W1g, 2u * H * D * 4);
+  // without momentum the caller's momentum is never touched (a descriptor of
+  // size zero: loads read zeros, stores are dropped) and the tile-major copy
+  // of S holds the zeros the first pass read, so S stays zero without branches
   const __amdgpu_buffer_rsrc_t rM = buffer_of(S1g, mom ? 2u * H * D * 4 : 0u);
   const __amdgpu_buffer_rsrc_t rAG = buffer_of(xw + S::xAG, (unsigned)S::ag_bytes);
   const int vT = (threadIdx.x & 63) * 16;                                   // tile-major
@@ -618,7 +621,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
     for (int t = 0; t < ND; ++t) {
       pW1[t] = ld1(0, tiled, J, t);
-      pS1[t] = mom ? ld1(1, tiled, J, t) : zero4();
+      pS1[t] = ld1(1, tiled, J, t);   // without momentum: zeros (see below)
     }
 #pragma unroll
     for (int a = 0; a < NU; ++a)
@@ -933,7 +936,7 @@ stream_mlp_kernel(ShardedParams p) {
           S1T[t][r] = Pc * s1 - us[r];
         }
         st1(W1T[t], 0, dst_t, J, t);
-        if (mom) st1(S1T[t], 1, dst_t, J, t);
+        st1(S1T[t], 1, dst_t, J, t);
       }
       __syncthreads();   // Ah complete; every wave is done with the W2 image
 
@@ -948,7 +951,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
         for (int bb = 0; bb < NDT; ++bb) {
           W2T[a][bb] = ld2(0, src_t, J, a, bb);
-          S2T[a][bb] = mom ? ld2(1, src_t, J, a, bb) : zero4();
+          S2T[a][bb] = ld2(1, src_t, J, a, bb);
         }
       // (the next pass's first tile is fetched after the chunk inputs are staged)
       if (J + 1 < J0 + NJ) prefetch(J + 1, src_t);
@@ -1010,7 +1013,7 @@ stream_mlp_kernel(ShardedParams p) {
               S2T[a][bb][r] = Pc * s2 - us[r];
             }
             st2(W2T[a][bb], 0, dst_t, J, a, bb);
-            if (mom) st2(S2T[a][bb], 1, dst_t, J, a, bb);
+            st2(S2T[a][bb], 1, dst_t, J, a, bb);
           }
         }
       }
@@ -1090,12 +1093,23 @@ stream_mlp_kernel(ShardedParams p) {
     if (more) stage_next(ch + 1);
     if constexpr (G > 1) {
       if (more) xadd(xYh_at(par, 1 - pm), yh);
+      // every tile is loaded (the ones of the other half are not used), all
+      // before the first add, so the partner's partials cost one round trip
       const f32x4* d = reinterpret_cast<const f32x4*>(xw + xYp_at(par, 1 - pm)) + threadIdx.x;
+      f32x4 tp[NQ][NDT];
 #pragma unroll
       for (int m = 0; m < NQ; ++m)
-        if (m >= mlo && m < mlo + MQ)
 #pragma unroll
-          for (int bb = 0; bb < NDT; ++bb) yp[m][bb] += d[(m * NDT + bb) * 256];
+        for (int bb = 0; bb < NDT; ++bb) tp[m][bb] = d[(m * NDT + bb) * 256];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < NQ; ++m) {
+        const bool mine = m >= mlo && m < mlo + MQ;
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yp[m][bb][r] += mine ? tp[m][bb][r] : 0.f;
+      }
     }
     if constexpr (lnorm) {
       // y = r + LN(u) on this member's rows: mean and variance of each row of

@@ -564,3 +564,31 @@ def test_full_grid_state(B, variant, recipe):
         if key in r:
             assert r[key] <= tol, (key, r)
     assert r["halo_exact"] and r["count_exact"], r
+
+
+@pytest.mark.parametrize("kernel", ["sharded", "streamed", "grouped", "per_sequence"])
+@pytest.mark.parametrize("name", ["mlp64", "layer_scale"])
+def test_parity_without_momentum(B, name, kernel):
+    """No momentum (eta = 0, the state holds no momentum block): S stays zero
+    in every family."""
+    binding, H = B
+    from dataclasses import replace
+    wl = replace(lively(WORKLOADS[name]), momentum=False, eta_u=None).with_shape(batch=1, heads=2, seq_len=SMALL_N)
+    _say(f"[no momentum] {name} kernel={kernel}")
+    inputs, w0 = H.prepare(wl)
+    mem = binding.AtlasMem(wl, kernel)
+    assert mem.family() == kernel
+    dev = H.to_device(wl, inputs)
+    st = mem.new_state(torch.from_numpy(w0))
+    out = H.gpu_run(mem, wl, dev, st)
+    torch.cuda.synchronize()
+    assert mem.device_errors() == 0
+    st_g = H.gpu_state_np(mem, st)
+    from oracle import oracle as O
+    out_o, st_o, _ = O.run_workload(wl, inputs, w0)
+    r = H.compare(wl, inputs, out.float().cpu().numpy(), st_g, out_o, st_o)
+    _say(f"[no momentum] {name} kernel={kernel}: {r}")
+    for key in ("out", "memory_part", "weights"):
+        if key in r:
+            assert r[key] <= H.tol_of(wl), (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
