@@ -1,0 +1,238 @@
+"""CPU replay of the global-memory index arithmetic of the grouped-family
+kernels (the MLP kernel of atlas_mem_grouped.hip, the linear kernels of
+atlas_mem_linear.hip and the phi / Q1 kernels of atlas_mem_phi.h): every
+offset a lane forms is recomputed here, for every wave, lane, chunk and tile
+the kernels visit, at the library's shapes and ragged lengths, and checked
+against the size of the array it addresses.  Accesses through range-checked
+buffer descriptors are checked too, so that an index out of range (which the
+hardware would silently turn into a zero) is caught as a bug.
+
+The formulas restate the kernels' own expressions; a change of a kernel's
+indexing must be mirrored here (the test then proves the new indices before
+any GPU run).
+"""
+import numpy as np
+import pytest
+
+BC = 64
+PHI_IDENTITY, PHI_POLY2, PHI_RAW_POLY2 = 0, 1, 2
+
+
+def feature_dim(phi, dk, pd):
+    if phi == PHI_IDENTITY:
+        return dk
+    if phi == PHI_POLY2:
+        return dk + dk * (dk + 1) // 2
+    return dk + pd + pd * (pd + 1) // 2
+
+
+def align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+LANE = np.arange(64)
+G4, C16 = LANE >> 4, LANE & 15
+
+
+def check(offs, size, what):
+    offs = np.asarray(offs)
+    if offs.size:
+        assert offs.min() >= 0 and offs.max() < size, (what, int(offs.min()), int(offs.max()), size)
+
+
+# ----------------------------------------------------------------------------- MLP kernel
+def grouped_mlp(phi, dk, pd, dv, h, g, n, c):
+    D = feature_dim(phi, dk, pd)
+    DP = (D + 63) // 64 * 64
+    WP, HL = 128, h // g
+    NFW, NDW, RW, RQ = DP // 64, dv // 64, WP // g, BC // g
+    nch = -(-n // BC)
+    NR = nch * BC + BC
+    W = BC + c - 1
+    assert HL == 16 and W <= WP
+    xr_size = NR * DP * 2          # bytes: key rows, the feature-major copy
+    xq_size = nch * BC * DP * 2
+    xy_size = 2 * g * WP * dv * 4
+    xo_size = 2 * g * BC * dv * 4
+    state_w = (h * D + dv * h) * 4
+    npair = RW * (dv // 4)
+    nsplit = 256 // npair
+    per = g // nsplit
+    npair_o = RQ * (dv // 4)
+    nsplit_o = 256 // npair_o
+    per_o = g // nsplit_o
+    for pm in range(g):
+        j0 = HL * pm
+        for wave in range(4):
+            fb = 16 * NFW * wave
+            # state slices (kZeroOffset for padded features is out of range on purpose)
+            for t in range(NFW):
+                f = fb + 16 * t + C16
+                for r in range(4):
+                    off = ((j0 + 4 * G4 + r) * D + f) * 4
+                    check(off[f < D], state_w, "W1 state")
+            for t in range(NDW):
+                for r in range(4):
+                    check((h * D + (16 * (NDW * wave + t) + 4 * G4 + r) * h + j0 + C16) * 4, state_w, "W2 state")
+            R0, Q0 = 32 * wave, 16 * wave
+            for ch in range(nch):
+                t0 = ch * BC
+                sl = ch & 1
+                for ks in range(DP // 32):
+                    for mt in range(2):
+                        check(((t0 + R0 + 16 * mt + C16) * DP + 32 * ks + 8 * G4) * 2 + 15, xr_size, "forward X")
+                    check(((t0 + Q0 + C16) * DP + 32 * ks + 8 * G4) * 2 + 15, xq_size, "query rows")
+                yb = ((sl * g + pm) * WP) * dv * 4
+                for mt in range(2):
+                    for nt in range(dv // 16):
+                        check(yb + ((R0 + 16 * mt + C16) * dv + 16 * nt + 4 * G4) * 4 + 15, xy_size, "Y partials")
+                yo = ((sl * g + pm) * BC) * dv * 4
+                for nt in range(dv // 16):
+                    check(yo + ((Q0 + C16) * dv + 16 * nt + 4 * G4) * 4 + 15, xo_size, "output partials")
+                for t in range(NFW):
+                    f = fb + 16 * t + C16
+                    for s in range(WP // 32):
+                        check((f * NR + t0 + 32 * s + 8 * G4) * 2 + 15, xr_size, "update X^T")
+        # reduce-scatter and output reduction (all 256 threads)
+        tid = np.arange(256)
+        e, hh = tid % npair, tid // npair
+        w = pm * RW + e // (dv // 4)
+        o4 = (e % (dv // 4)) * 4
+        assert w.max() < WP
+        for sl in range(2):
+            for u in range(per):
+                check((sl * g * WP * dv + w * dv + o4 + (hh * per + u) * WP * dv) * 4 + 15, xy_size, "reduce-scatter")
+            check(((sl * WP + w) * dv + o4) * 2 + 7, 2 * WP * dv * 2, "D2 rows")
+        e, hh = tid % npair_o, tid // npair_o
+        qq = pm * RQ + e // (dv // 4)
+        o4 = (e % (dv // 4)) * 4
+        assert qq.max() < BC
+        for pc in range(2):
+            for u in range(per_o):
+                check(((pc & 1) * g * BC * dv + qq * dv + o4 + (hh * per_o + u) * BC * dv) * 4 + 15, xo_size,
+                      "output reduction")
+        for ch in range(nch):
+            t0, te = ch * BC, min(n, ch * BC + BC) - 1
+            rows = t0 + qq
+            check(((rows[rows <= te]) * dv + o4[rows <= te]) * 2 + 7, n * dv * 2, "output rows")
+            # window values of the reduce-scatter rows
+            e = tid % npair
+            w = pm * RW + e // (dv // 4)
+            i = t0 - (c - 1) + w
+            ok = (w < W) & (i <= te)
+            check((i[ok & (i >= 0)] * dv) * 2, n * dv * 2, "value rows")
+            hi = (c - 1 + i[ok & (i < 0) & (i >= -(c - 1))])
+            if hi.size:
+                check(hi * dv * 4, (c - 1) * dv * 4, "halo values")
+
+
+GROUPED_SHAPES = {"atlas_long": (PHI_RAW_POLY2, 128, 32, 128, 512, 32), "layer_scale": (PHI_IDENTITY, 128, 0, 128, 512, 32),
+                  "mlp64": (PHI_IDENTITY, 64, 0, 64, 256, 16)}
+
+
+@pytest.mark.parametrize("name", list(GROUPED_SHAPES))
+@pytest.mark.parametrize("n,c", [(1, 1), (37, 64), (64, 32), (65, 64), (209, 33), (4 * 64, 64)])
+def test_grouped_mlp_indices(name, n, c):
+    grouped_mlp(*GROUPED_SHAPES[name], n, c)
+
+
+# ----------------------------------------------------------------------------- linear kernels
+def img_pos(o, f, nout):
+    return ((f >> 2) * 16 + (o & 15)) * (4 * nout) + (o >> 4) * 4 + (f & 3)
+
+
+def linear(phi, dk, pd, dv, wp, n, c):
+    D = feature_dim(phi, dk, pd)
+    DP = (D + 63) // 64 * 64
+    NOT, NFT, NWT = dv // 16, DP // 16, wp // 16
+    YPW, FPW = NOT * NWT // 4, NFT // 4
+    assert BC + c - 1 <= wp
+    nch = -(-n // BC)
+    NR = nch * BC + BC
+    img_elems = nch * 2 * dv * DP
+    dg_elems = nch * wp * dv
+    xr_size = NR * DP * 2
+    # X^T staging: J 1-KB instructions cover R rows of wp*2 bytes
+    rb = wp * 2
+    J = rb // np.gcd(rb, 1024)
+    R = J * 1024 // rb
+    NSB = DP // R
+    assert DP % R == 0 and NSB % 4 == 0
+    # the image order is a bijection onto [0, dv * DP)
+    o, f = np.meshgrid(np.arange(dv), np.arange(DP), indexing="ij")
+    pos = img_pos(o, f, NOT)
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(dv * DP))
+    for wave in range(4):
+        for m in range(FPW):
+            f0 = 16 * (wave + 4 * m) + 4 * G4
+            q0 = img_pos(C16, f0, NOT)
+            assert (q0 % 8 == 0).all()
+            for chn in range(nch):
+                check(chn * 2 * dv * DP + dv * DP + q0 + 8 * (NOT // 2 - 1) + 7, img_elems, "S image")
+        for ch in range(nch):
+            t0 = ch * BC
+            for u in range(YPW):
+                ot, wt = (wave + 4 * u) % NOT, (wave + 4 * u) // NOT
+                w = 16 * wt + C16
+                check(((ch * wp + w) * dv + 16 * ot + 4 * G4) + 3, dg_elems, "D rows")
+                for s in range(DP // 32):
+                    check(((t0 + 16 * wt + C16) * DP + 32 * s + 8 * G4) * 2 + 15, xr_size, "window X")
+            for k in range(NSB // 4):
+                sb = wave + 4 * k
+                soff = (sb * R * NR + t0) * 2
+                for j in range(J):
+                    off = j * 1024 + LANE * 16
+                    voff = (off // rb) * NR * 2 + off % rb
+                    check(voff + soff + 15, xr_size, "X^T staging")
+                    assert (sb * J + j) * 1024 + 1023 < DP * wp * 2
+    # retrieval: the image operand as two 8-byte halves
+    for ch in range(nch):
+        for o_t in range(NOT):
+            for s in range(DP // 32):
+                q = img_pos(16 * o_t + C16, 32 * s + 8 * G4, NOT)
+                check(dv * DP + q + 64 * NOT + 3, 2 * dv * DP, "retrieval image")
+
+
+LINEAR_SHAPES = {"poly2_w96": (PHI_POLY2, 32, 32, 32, 96), "poly2_w128": (PHI_POLY2, 32, 32, 32, 128),
+                 "id64_w64": (PHI_IDENTITY, 64, 0, 64, 64)}
+
+
+@pytest.mark.parametrize("name", list(LINEAR_SHAPES))
+@pytest.mark.parametrize("n", [1, 37, 64, 65, 209, 1024])
+def test_linear_indices(name, n):
+    shape = LINEAR_SHAPES[name]
+    for c in (1, 16, 33, 64):
+        if BC + c - 1 <= shape[-1]:
+            linear(*shape, n, c)
+
+
+# ----------------------------------------------------------------------------- phi and Q1 kernels
+@pytest.mark.parametrize("phi,dk,pd,wp", [(PHI_RAW_POLY2, 128, 32, 128), (PHI_POLY2, 32, 32, 96), (PHI_IDENTITY, 64, 0, 64)])
+@pytest.mark.parametrize("n", [1, 65, 209])
+def test_phi_and_q1_indices(phi, dk, pd, wp, n):
+    D = feature_dim(phi, dk, pd)
+    DP = (D + 63) // 64 * 64
+    nch = -(-n // BC)
+    NR = nch * BC + BC
+    assert NR % 32 == 0
+    per_seq = NR // 32 + 2 * nch
+    for blk in range(per_seq):
+        keys = blk < NR // 32
+        r0 = 32 * (blk if keys else blk - NR // 32)
+        # the row pass: e = tid, tid + 256, ... < 32 DP / 8 -> row r0 + e / (DP / 8)
+        e = np.arange(32 * (DP // 8))
+        rows = r0 + e // (DP // 8)
+        limit = NR if keys else nch * BC
+        check((rows * DP + (e % (DP // 8)) * 8) * 2 + 15, limit * DP * 2, "phi rows")
+        if keys:
+            f = np.arange(DP)[:, None]
+            t8 = np.arange(4)[None, :] * 8
+            check(f * NR + r0 + t8 + 7, NR * DP, "feature-major keys")
+    # Q1: query tile `wave`, all window tiles
+    for ch in range(nch):
+        t0 = ch * BC
+        for wave in range(4):
+            for s in range(DP // 32):
+                check(((t0 + 16 * wave + C16) * DP + 32 * s + 8 * G4) * 2 + 15, nch * BC * DP * 2, "Q1 queries")
+                for nt in range(wp // 16):
+                    check(((t0 + 16 * nt + C16) * DP + 32 * s + 8 * G4) * 2 + 15, NR * DP * 2, "Q1 keys")
