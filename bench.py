@@ -160,7 +160,7 @@ def kernel_name(binding, wl, family):
 
 def bench_prologue(args, wl):
     """The fused prologue on the workload's shape: d_model = heads * d_k,
-    K = 4 taps, gate rank 16.  One JSON line; the projection GEMM (rocBLAS)
+    K = 4 taps, gate rank 16.  One JSON line; the projection GEMM
     and the fused kernel are timed apart with HIP events on the call's
     stream.  The kernel is HBM-bound: it reads the projections once and
     writes q, k, v and the gates once."""

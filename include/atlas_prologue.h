@@ -9,7 +9,7 @@
  *
  * Per sequence b and token t:
  *   P_t     = W x_t          W = [Wq; Wk; Wv; U_alpha; U_eta; U_theta; U_gamma]
- *                            (one GEMM: rocBLAS, bf16 in, fp32 accumulate, bf16 P)
+ *                            (one GEMM: bf16 in, fp32 accumulate, bf16 P)
  *   c_t     = sum_{j<K} w_conv[ch][j] P_{t-(K-1)+j}[ch]    for the 3*H*d q/k/v
  *                            channels; tokens before the sequence start count as
  *                            zero (each call starts its sequences)
@@ -42,7 +42,7 @@ typedef struct {
 typedef struct atlas_prologue_s* atlas_prologue_t;
 
 /* Validates cfg and allocates the projection workspace (B*N rows of
- * 3*H*d + 4*r bf16) and a BLAS handle on the current device.
+ * 3*H*d + 4*r bf16) on the current device.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (d_head, taps or rank outside the
  * built range), OUT_OF_MEMORY, HIP.                                        */
 atlas_status atlas_prologue_init(const atlas_prologue_config* cfg, atlas_prologue_t* out);
@@ -56,8 +56,7 @@ atlas_status atlas_prologue_init(const atlas_prologue_config* cfg, atlas_prologu
  *   q, k    [B][H][N][d], v [B][H][N][d]   bf16 outputs
  *   alpha, eta, theta, gamma [B][H][N]      fp32 outputs
  * Device pointers, 16-byte aligned (fp32 parameters and gates: 4-byte).
- * Errors: INVALID_ARGUMENT (bad handle or pointer), HIP (launch or BLAS
- * failure).                                                                */
+ * Errors: INVALID_ARGUMENT (bad handle or pointer), HIP (launch failure). */
 atlas_status atlas_prologue_forward(atlas_prologue_t h, const void* x, const void* w, const float* w_conv,
                                     const float* gate_v, const float* gate_b, void* q, void* k, void* v,
                                     float* alpha, float* eta, float* theta, float* gamma, void* stream);
@@ -67,7 +66,7 @@ atlas_status atlas_prologue_forward(atlas_prologue_t h, const void* x, const voi
  * and `gemm_before` right before the GEMM; NULLs clear it.                  */
 atlas_status atlas_prologue_set_events(atlas_prologue_t h, void* gemm_before, void* before, void* after);
 
-/* Releases the workspace, the BLAS handle and the handle (NULL accepted).   */
+/* Releases the workspace and the handle (NULL accepted).                    */
 atlas_status atlas_prologue_free(atlas_prologue_t h);
 
 #ifdef __cplusplus

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libatlas_mem.so")
 SOURCES = ["atlas_mem_kernels.hip", "atlas_mem_sharded.hip", "atlas_mem_stream.hip", "atlas_mem_grouped.hip",
            "atlas_mem_linear.hip",
-           "atlas_mem_api.hip", "atlas_prologue.hip"]
+           "atlas_mem_api.hip", "atlas_prologue.hip", "atlas_prologue_gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -26,9 +26,19 @@ FLAGS = [
 ]
 
 
+# The projection GEMM keeps its 64 accumulator tiles per wave in the
+# accumulation registers for the whole K loop, so it is built without the
+# VGPR form of the MFMA results.
+NO_VGPR_FORM = {"atlas_prologue_gemm.hip"}
+
+
 def _compile(src: str) -> tuple[str, str]:
     obj = os.path.join(CSRC, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    flags = FLAGS
+    if src in NO_VGPR_FORM:
+        flags = [f for i, f in enumerate(FLAGS)
+                 if f != "-amdgpu-mfma-vgpr-form=1" and not (f == "-mllvm" and FLAGS[i + 1] == "-amdgpu-mfma-vgpr-form=1")]
+    cmd = [HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops' is not a recognized" not in l)
     if r.returncode != 0:
@@ -48,8 +58,7 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    # rocBLAS for the prologue's projection GEMM (a plain library GEMM)
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp, "-lrocblas"]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -1,6 +1,6 @@
 // atlas_prologue.hip -- the fused prologue (include/atlas_prologue.h): one
-// rocBLAS GEMM for every projection of x, then one gfx950 kernel for the
-// rest of each token's work.
+// projection GEMM for every projection of x (atlas_prologue_gemm.hip), then
+// one gfx950 kernel for the rest of each token's work.
 //
 // Kernel layout: one wave per (run of TOK consecutive tokens of one sequence,
 // head), head fastest, so the waves of a workgroup share the tokens'
@@ -15,7 +15,6 @@
 // are written once.
 
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <cstdio>
 #include <new>
@@ -23,6 +22,7 @@
 #include "atlas_prologue.h"
 #include "atlas_mem_internal.h"
 #include "atlas_mem_frag.h"
+#include "atlas_prologue_gemm.h"
 
 namespace atlas {
 namespace prologue {
@@ -230,7 +230,6 @@ struct atlas_prologue_s {
   uint32_t magic;
   atlas_prologue_config cfg;
   int device;
-  rocblas_handle blas;
   atlas::bf16* P;
   hipEvent_t ev_gemm, ev_before, ev_after;
 };
@@ -262,7 +261,6 @@ atlas_status atlas_prologue_init(const atlas_prologue_config* cfg, atlas_prologu
   h->magic = kProMagic;
   h->cfg = *cfg;
   h->P = nullptr;
-  h->blas = nullptr;
   h->ev_gemm = h->ev_before = h->ev_after = nullptr;
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) {
@@ -276,12 +274,6 @@ atlas_status atlas_prologue_init(const atlas_prologue_config* cfg, atlas_prologu
     (void)hipGetLastError();
     delete h;
     return ATLAS_ERR_OUT_OF_MEMORY;
-  }
-  if (rocblas_create_handle(&h->blas) != rocblas_status_success) {
-    atlas::record_hip_error("rocblas_create_handle failed");
-    (void)hipFree(h->P);
-    delete h;
-    return ATLAS_ERR_HIP;
   }
   *out = h;
   return ATLAS_OK;
@@ -310,19 +302,10 @@ atlas_status atlas_prologue_forward(atlas_prologue_t h, const void* x, const voi
     atlas::record_hip_error(hipGetErrorString(e));
     return ATLAS_ERR_HIP;
   }
-  // P^T [ncol][rows] (column-major) = W [ncol][d_model] . x^T:  op(A) = W from
-  // its column-major view [d_model][ncol] transposed, B = x^T [d_model][rows]
-  const float one = 1.f, zero = 0.f;
-  rocblas_status bs = rocblas_set_stream(h->blas, st);
-  if (bs == rocblas_status_success)
-    bs = rocblas_gemm_ex(h->blas, rocblas_operation_transpose, rocblas_operation_none, ncol, rows, c.d_model, &one, w,
-                         rocblas_datatype_bf16_r, c.d_model, x, rocblas_datatype_bf16_r, c.d_model, &zero, h->P,
-                         rocblas_datatype_bf16_r, ncol, h->P, rocblas_datatype_bf16_r, ncol, rocblas_datatype_f32_r,
-                         rocblas_gemm_algo_standard, 0, 0);
-  if (bs != rocblas_status_success) {
-    char msg[96];
-    std::snprintf(msg, sizeof msg, "rocblas_gemm_ex failed (status %d)", (int)bs);
-    atlas::record_hip_error(msg);
+  // P [rows][ncol] = x [rows][d_model] . W^T, W [ncol][d_model]
+  if ((e = atlas::prologue::gemm_nt_bf16((const atlas::bf16*)x, (const atlas::bf16*)w, h->P, rows, ncol, c.d_model, st)) !=
+      hipSuccess) {
+    atlas::record_hip_error(hipGetErrorString(e));
     return ATLAS_ERR_HIP;
   }
   atlas::prologue::Params p;
@@ -375,13 +358,8 @@ atlas_status atlas_prologue_free(atlas_prologue_t h) {
   if (!h) return ATLAS_OK;
   if (h->magic != kProMagic) return ATLAS_ERR_INVALID_ARGUMENT;
   h->magic = 0;
-  const rocblas_status bs = h->blas ? rocblas_destroy_handle(h->blas) : rocblas_status_success;
   const hipError_t e = h->P ? hipFree(h->P) : hipSuccess;
   delete h;
-  if (bs != rocblas_status_success) {
-    atlas::record_hip_error("rocblas_destroy_handle failed");
-    return ATLAS_ERR_HIP;
-  }
   if (e != hipSuccess) {
     atlas::record_hip_error(hipGetErrorString(e));
     return ATLAS_ERR_HIP;

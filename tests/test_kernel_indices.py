@@ -236,3 +236,86 @@ def test_phi_and_q1_indices(phi, dk, pd, wp, n):
                 check(((t0 + 16 * wave + C16) * DP + 32 * s + 8 * G4) * 2 + 15, nch * BC * DP * 2, "Q1 queries")
                 for nt in range(wp // 16):
                     check(((t0 + 16 * nt + C16) * DP + 32 * s + 8 * G4) * 2 + 15, NR * DP * 2, "Q1 keys")
+
+
+# ----------------------------------------------------------------------------- projection GEMM
+def gemm_nt(M, N, K):
+    """atlas_prologue_gemm.hip: tile order, LDS-direct load offsets with the
+    granule swizzle, the zero-filled K tail and stages past the last, the
+    fragment read offsets, and the output offsets."""
+    BM = BN = 256
+    BK, ROWB, GM = 64, 128, 4
+    tiles_m, tiles_n = -(-M // BM), -(-N // BN)
+    T = tiles_m * tiles_n
+    T8 = -(-T // 8)
+    seen = set()
+    for blk in range(8 * T8):
+        t = (blk & 7) * T8 + (blk >> 3)
+        if t >= T:
+            continue
+        band = t // (GM * tiles_n)
+        i = t - band * GM * tiles_n
+        gm = min(GM, tiles_m - band * GM)
+        tm, tn = band * GM + i % gm, i // gm
+        assert 0 <= tm < tiles_m and 0 <= tn < tiles_n
+        seen.add((tm, tn))
+    assert len(seen) == T
+    nk = -(-K // BK)
+    ktail = K - (nk - 1) * BK
+    far, zero_off = 0x40000000, 0x7FFFFF00
+    g = [(LANE & 7) ^ (4 * p + (LANE >> 4)) for p in range(2)]
+    voff = [(LANE >> 3) * K * 2 + (g[p] << 4) for p in range(2)]
+    voff_last = [np.where(8 * g[p] < ktail, voff[p], zero_off) for p in range(2)]
+    # the first tile of each operand (the largest valid row count; a partial
+    # tile only shrinks its descriptor)
+    size = {False: min(BM, M) * K * 2, True: min(BN, N) * K * 2}
+    for wave in range(4):
+        for s in range(nk + 2):
+            kofs = s * ROWB if s < nk else far
+            cover = set()
+            for q in range(16):
+                row = 64 * wave + 8 * (q & 7)
+                vo = voff_last[q & 1] if s == nk - 1 else voff[q & 1]
+                off = vo.astype(np.int64) + row * K * 2 + kofs
+                assert off.max() < 2 ** 32
+                dst = (s & 1) * 2 * BM * ROWB + (0 if q < 8 else BM * ROWB) + row * ROWB + LANE * 16
+                assert dst.max() + 16 <= 4 * BM * ROWB
+                inb = off < size[q >= 8]
+                if s >= nk:
+                    assert not inb.any()
+                    continue
+                r, k = off // (K * 2), (off % (K * 2)) // 2
+                # an in-range granule lies inside its row, in this stage, below K
+                assert (r[inb] == row + (LANE[inb] >> 3)).all()
+                assert (k[inb] >= s * BK).all() and (k[inb] + 8 <= min(K, s * BK + BK)).all()
+                # and lands in the swizzled slot of its granule
+                rr = (dst % (BM * ROWB)) // ROWB
+                slot = (dst % ROWB) // 16
+                assert ((slot == (((k - s * BK) // 8) ^ ((rr >> 1) & 7))) | ~inb).all()
+                cover.update((q >= 8, int(o)) for o in off[inb])
+            if s < nk:
+                # every granule of this wave's valid rows below K is loaded once
+                want = min(BK, K - s * BK) // 8
+                rows_a = max(0, min(64, M - 64 * wave))
+                rows_b = max(0, min(64, N - 64 * wave))
+                assert len(cover) == (rows_a + rows_b) * want
+    for kk in range(2):
+        fo = (LANE & 15) * ROWB + (((4 * kk + (LANE >> 4)) ^ ((LANE & 15) >> 1)) << 4)
+        for r0 in range(0, 256, 16):
+            r = r0 + (LANE & 15)
+            assert (((fo % ROWB) // 16) == ((4 * kk + (LANE >> 4)) ^ ((r >> 1) & 7))).all()
+            assert (r0 * ROWB + fo).max() + 16 <= BM * ROWB
+    for wm in range(2):
+        for wn in range(2):
+            for i in range(8):
+                col = 128 * wn + 16 * i + 4 * (LANE >> 4)
+                for j in range(8):
+                    row = 128 * wm + 16 * j + (LANE & 15)
+                    vo = np.where(col < N, (row * N + col) * 2, zero_off)
+                    assert vo.max() < 2 ** 31
+
+
+@pytest.mark.parametrize("M,N,K", [(131072, 4672, 1536), (1000, 100, 64), (300, 260, 192), (64, 4, 8),
+                                   (513, 1028, 1000), (256 * 9, 768, 1536 + 24)])
+def test_projection_gemm_indices(M, N, K):
+    gemm_nt(M, N, K)
