@@ -9,7 +9,7 @@
  *
  * Per sequence b and token t:
  *   P_t     = W x_t          W = [Wq; Wk; Wv; U_alpha; U_eta; U_theta; U_gamma]
- *                            (one GEMM: bf16 in, fp32 accumulate, bf16 P)
+ *                            (bf16 in, fp32 accumulate, P rounded to bf16)
  *   c_t     = sum_{j<K} w_conv[ch][j] P_{t-(K-1)+j}[ch]    for the 3*H*d q/k/v
  *                            channels; tokens before the sequence start count as
  *                            zero (each call starts its sequences)
@@ -17,6 +17,12 @@
  *   q, k    <- x / max(|x|_2, 1e-12) per head over its d channels
  *   gate_g  = sigmoid(V_g (U_g x_t) + b_g) per head, g = alpha, eta, theta, gamma
  * The outputs are laid out as atlas_mem_forward takes them.
+ *
+ * Two paths with the same bits: one kernel that keeps each tile of P on
+ * chip and applies the per-token steps to it (the default where it serves
+ * the shape: d 64, 128 or 256, 3*H*d a multiple of 256, one sequence of x
+ * below 1 GiB), and a projection GEMM into a workspace followed by a
+ * per-token kernel (every other shape).
  *
  * Errors as in atlas_mem.h: nothing throws, every call returns a status.
  */
@@ -41,8 +47,8 @@ typedef struct {
 
 typedef struct atlas_prologue_s* atlas_prologue_t;
 
-/* Validates cfg and allocates the projection workspace (B*N rows of
- * 3*H*d + 4*r bf16) on the current device.
+/* Validates cfg; on the current device, allocates the projection workspace
+ * (B*N rows of 3*H*d + 4*r bf16) if the one-kernel path does not serve it.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED (d_head, taps or rank outside the
  * built range), OUT_OF_MEMORY, HIP.                                        */
 atlas_status atlas_prologue_init(const atlas_prologue_config* cfg, atlas_prologue_t* out);
@@ -61,9 +67,15 @@ atlas_status atlas_prologue_forward(atlas_prologue_t h, const void* x, const voi
                                     const float* gate_v, const float* gate_b, void* q, void* k, void* v,
                                     float* alpha, float* eta, float* theta, float* gamma, void* stream);
 
-/* Timing hook: while set, each forward records `before` and `after`
- * (caller-owned hipEvent_t) around the fused kernel that follows the GEMM,
- * and `gemm_before` right before the GEMM; NULLs clear it.                  */
+/* Path selection, for tests and timing: fused = 1 takes the one-kernel path
+ * (UNSUPPORTED where it does not serve the shape), 0 the two-kernel path
+ * (allocates its workspace on first use: OUT_OF_MEMORY).  Not to be called
+ * while a forward of this handle may run.                                  */
+atlas_status atlas_prologue_set_fused(atlas_prologue_t h, int fused);
+
+/* Timing hook: while set, each forward records `gemm_before` first, then
+ * `before` and `after` (caller-owned hipEvent_t) around the per-token kernel
+ * of the two-kernel path, or around the one kernel; NULLs clear it.        */
 atlas_status atlas_prologue_set_events(atlas_prologue_t h, void* gemm_before, void* before, void* after);
 
 /* Releases the workspace and the handle (NULL accepted).                    */

@@ -104,6 +104,8 @@ def lib():
         L.atlas_prologue_forward.restype = ctypes.c_int
         L.atlas_prologue_set_events.argtypes = [vp] * 4
         L.atlas_prologue_set_events.restype = ctypes.c_int
+        L.atlas_prologue_set_fused.argtypes = [vp, ctypes.c_int]
+        L.atlas_prologue_set_fused.restype = ctypes.c_int
         L.atlas_prologue_free.argtypes = [vp]
         L.atlas_prologue_free.restype = ctypes.c_int
         _lib = L
@@ -275,6 +277,11 @@ class AtlasPrologue:
         rc = lib().atlas_prologue_set_events(self.handle, raw(gemm_before), raw(before), raw(after))
         if rc != OK:
             raise AtlasError(rc, "atlas_prologue_set_events")
+
+    def set_fused(self, fused: bool):
+        rc = lib().atlas_prologue_set_fused(self.handle, 1 if fused else 0)
+        if rc != OK:
+            raise AtlasError(rc, "atlas_prologue_set_fused")
 
     def forward(self, x, w, w_conv, gate_v, gate_b, q, k, v, alpha, eta, theta, gamma, stream=None):
         if stream is None:

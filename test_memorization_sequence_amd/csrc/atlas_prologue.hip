@@ -1,6 +1,9 @@
-// atlas_prologue.hip -- the fused prologue (include/atlas_prologue.h): one
-// projection GEMM for every projection of x (atlas_prologue_gemm.hip), then
-// one gfx950 kernel for the rest of each token's work.
+// atlas_prologue.hip -- the fused prologue (include/atlas_prologue.h).  By
+// default one kernel (atlas_prologue_gemm.hip) computes the projections tile
+// by tile and applies the rest of each token's work to the tile in LDS.  The
+// two-kernel path below -- the projection GEMM into a workspace, then
+// prologue_kernel -- serves the shapes the fused kernel does not and gives
+// the same bits.
 //
 // Kernel layout: one wave per (run of TOK consecutive tokens of one sequence,
 // head), head fastest, so the waves of a workgroup share the tokens'
@@ -23,6 +26,7 @@
 #include "atlas_mem_internal.h"
 #include "atlas_mem_frag.h"
 #include "atlas_prologue_gemm.h"
+#include "atlas_prologue_math.h"
 
 namespace atlas {
 namespace prologue {
@@ -41,35 +45,6 @@ struct Params {
   float* gate[4];
   int B, N, H, K, r, ncol;
 };
-
-// Cross-lane sums by DPP moves (full-rate vector ops, no LDS round trip):
-// xor 1 and xor 2 within quads, then the half-row and row mirrors, leave the
-// sum of each aligned group of 2, 4, 8 or 16 lanes in all of its lanes.
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float group_sum(float v, int width) {
-  if (width >= 2) v += dppf<0xB1>(v);    // quad_perm [1,0,3,2]
-  if (width >= 4) v += dppf<0x4E>(v);    // quad_perm [2,3,0,1]
-  if (width >= 8) v += dppf<0x141>(v);   // row_half_mirror
-  if (width >= 16) v += dppf<0x140>(v);  // row_mirror
-  return v;
-}
-// the sum over all 64 lanes, the same in every lane
-__device__ __forceinline__ float wave_sum(float v) {
-  v = group_sum(v, 16);
-  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return (r0 + r1) + (r2 + r3);
-}
-
-// SiLU and the logistic with the hardware reciprocal (about 1 ulp in fp32;
-// the outputs are bf16): z -> -inf gives rcp(inf) = 0, z -> +inf gives 1
-__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
-__device__ __forceinline__ float sigm(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 constexpr int TOK = 32;   // tokens per wave
 constexpr int TB = 8;     // tokens per load batch
@@ -230,9 +205,14 @@ struct atlas_prologue_s {
   uint32_t magic;
   atlas_prologue_config cfg;
   int device;
-  atlas::bf16* P;
+  atlas::bf16* P;   // projections of the two-kernel path (null until needed)
+  int fused;        // the one-kernel path serves this shape and is selected
   hipEvent_t ev_gemm, ev_before, ev_after;
 };
+
+static bool fused_ok(const atlas_prologue_config& c) {
+  return atlas::prologue::fused_supported(c.d_head, c.heads, c.gate_rank, c.seq_len, c.d_model);
+}
 
 static const uint32_t kProMagic = 0xA7A5F10Bu;
 
@@ -268,9 +248,10 @@ atlas_status atlas_prologue_init(const atlas_prologue_config* cfg, atlas_prologu
     delete h;
     return ATLAS_ERR_HIP;
   }
+  h->fused = fused_ok(*cfg) ? 1 : 0;
   const size_t rows = (size_t)cfg->batch * cfg->seq_len;
   const size_t ncol = 3 * (size_t)cfg->heads * cfg->d_head + 4 * (size_t)cfg->gate_rank;
-  if (rows && hipMalloc(&h->P, rows * ncol * sizeof(atlas::bf16)) != hipSuccess) {
+  if (!h->fused && rows && hipMalloc(&h->P, rows * ncol * sizeof(atlas::bf16)) != hipSuccess) {
     (void)hipGetLastError();
     delete h;
     return ATLAS_ERR_OUT_OF_MEMORY;
@@ -301,6 +282,35 @@ atlas_status atlas_prologue_forward(atlas_prologue_t h, const void* x, const voi
   if (h->ev_gemm && (e = hipEventRecord(h->ev_gemm, st)) != hipSuccess) {
     atlas::record_hip_error(hipGetErrorString(e));
     return ATLAS_ERR_HIP;
+  }
+  if (h->fused) {
+    atlas::prologue::FusedParams f{};
+    f.x = (const atlas::bf16*)x;
+    f.w = (const atlas::bf16*)w;
+    f.w_conv = w_conv;
+    f.gv = gate_v;
+    f.gb = gate_b;
+    f.q = (atlas::bf16*)q;
+    f.k = (atlas::bf16*)k;
+    f.v = (atlas::bf16*)v;
+    f.gate[0] = alpha;
+    f.gate[1] = eta;
+    f.gate[2] = theta;
+    f.gate[3] = gamma;
+    f.B = c.batch;
+    f.N = c.seq_len;
+    f.dm = c.d_model;
+    f.H = c.heads;
+    f.K = c.conv_taps;
+    f.r = c.gate_rank;
+    f.ncol = ncol;
+    if ((h->ev_before && (e = hipEventRecord(h->ev_before, st)) != hipSuccess) ||
+        (e = atlas::prologue::fused_prologue(f, c.d_head, st)) != hipSuccess ||
+        (h->ev_after && (e = hipEventRecord(h->ev_after, st)) != hipSuccess)) {
+      atlas::record_hip_error(hipGetErrorString(e));
+      return ATLAS_ERR_HIP;
+    }
+    return ATLAS_OK;
   }
   // P [rows][ncol] = x [rows][d_model] . W^T, W [ncol][d_model]
   if ((e = atlas::prologue::gemm_nt_bf16((const atlas::bf16*)x, (const atlas::bf16*)w, h->P, rows, ncol, c.d_model, st)) !=
@@ -343,6 +353,29 @@ atlas_status atlas_prologue_forward(atlas_prologue_t h, const void* x, const voi
     atlas::record_hip_error(hipGetErrorString(e));
     return ATLAS_ERR_HIP;
   }
+  return ATLAS_OK;
+}
+
+atlas_status atlas_prologue_set_fused(atlas_prologue_t h, int fused) {
+  if (!h || h->magic != kProMagic) return ATLAS_ERR_INVALID_ARGUMENT;
+  if (fused) {
+    if (!fused_ok(h->cfg)) return ATLAS_ERR_UNSUPPORTED;
+    h->fused = 1;
+    return ATLAS_OK;
+  }
+  const atlas_prologue_config& c = h->cfg;
+  const size_t rows = (size_t)c.batch * c.seq_len;
+  const size_t ncol = 3 * (size_t)c.heads * c.d_head + 4 * (size_t)c.gate_rank;
+  if (!h->P && rows) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return ATLAS_ERR_INVALID_ARGUMENT;
+    if (hipMalloc(&h->P, rows * ncol * sizeof(atlas::bf16)) != hipSuccess) {
+      (void)hipGetLastError();
+      h->P = nullptr;
+      return ATLAS_ERR_OUT_OF_MEMORY;
+    }
+  }
+  h->fused = 0;
   return ATLAS_OK;
 }
 

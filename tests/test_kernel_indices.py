@@ -319,3 +319,96 @@ def gemm_nt(M, N, K):
                                    (513, 1028, 1000), (256 * 9, 768, 1536 + 24)])
 def test_projection_gemm_indices(M, N, K):
     gemm_nt(M, N, K)
+
+
+def fused_prologue(B, N, dm, H, d, K, r):
+    """The one-kernel prologue: row tiles along each sequence with a window of
+    K - 1 recomputed rows, the P tile in LDS (16-byte granule swizzle), the
+    epilogue's rows, heads, window reads, norm-part block and output offsets.
+    Every output element is written exactly once."""
+    BM = BN = 256
+    halo = K - 1
+    KP = 4 if K <= 4 else 8
+    HD = H * d
+    ncol = 3 * HD + 4 * r
+    assert (3 * HD) % BN == 0
+    tps = 1 + ((N - BM + (BM - halo) - 1) // (BM - halo) if N > BM else 0)
+    tiles_n = -(-ncol // BN)
+    DPL, HPT = d // 64, BN // d
+    WPH = 4 // HPT
+    TB = 16
+    lds_p = 128 * 1024
+    wave_floats = TB * 64 + TB
+    lds_total = lds_p + 4 * wave_floats * 4
+    assert lds_total <= 160 * 1024
+    assert 4 * H * (r + 1) <= 4 * wave_floats   # the gate tile's V and b
+
+    def ptile(t, c16):
+        return t * 512 + ((c16 ^ (t & 15)) << 4)
+
+    # the P tile writes: every (row, 8-byte quarter-granule) exactly once
+    seen = set()
+    for wave in range(4):
+        wm, wn = wave >> 1, wave & 1
+        for i in range(8):
+            for j in range(8):
+                t = 128 * wm + 16 * j + (LANE & 15)
+                cg = 32 * wn + 4 * i + (LANE >> 4)
+                a = np.array([ptile(int(tt_), int(c) >> 1) for tt_, c in zip(t, cg)]) + (cg & 1) * 8
+                assert a.min() >= 0 and (a + 8).max() <= lds_p
+                seen.update(int(x) for x in a)
+    assert len(seen) == 256 * 64
+    written = {m: np.zeros((B, H, N), np.int32) for m in range(3)}
+    gates = np.zeros((4, B, H, N), np.int32)
+    for b in range(B):
+        for tt in range(tps):
+            row0 = tt * (BM - halo)
+            assert row0 < N and row0 * dm * 2 + 255 * dm * 2 + 0x40000000 < 2 ** 32
+            nvalid = min(BM, N - row0)
+            out_lo = 0 if tt == 0 else halo
+            for tn in range(tiles_n):
+                n0 = tn * BN
+                if n0 >= 3 * HD:
+                    for tid in range(256):
+                        t = out_lo + tid
+                        if t >= nvalid:
+                            continue
+                        for c in range(0, 4 * r, 4):
+                            a = ptile(t, c >> 3) + (c & 4) * 2
+                            assert a + 8 <= lds_p
+                        for g in range(4):
+                            gates[g, b, :, row0 + t] += 1
+                    continue
+                for wave in range(4):
+                    hh, part = wave // WPH, wave % WPH
+                    c0 = n0 + hh * d
+                    m, h = c0 // HD, (c0 % HD) // d
+                    assert m < 3 and h < H
+                    ln = nvalid - out_lo
+                    t_beg = out_lo + (part * ln) // WPH
+                    t_end = out_lo + ((part + 1) * ln) // WPH
+                    col = hh * d + LANE * DPL
+                    assert ((col % 8) + DPL <= 8).all()
+                    # window rows before the first: clamped at 0; rows the real
+                    # taps reach lie in the tile (or precede the sequence)
+                    assert t_beg - halo >= 0 or tt == 0
+                    for t in list(range(max(0, t_beg - KP + 1), t_beg)) + list(range(t_beg, t_end)):
+                        a = np.array([ptile(t, int(c) >> 3) for c in col]) + (col & 7) * 2
+                        assert a.min() >= 0 and (a + 2 * DPL).max() <= lds_p
+                    # the wave's norm parts and scales
+                    base = lds_p + wave * wave_floats * 4
+                    assert base + (TB * 64 + TB) * 4 <= lds_total
+                    written[m][b, h, row0 + t_beg:row0 + t_end] += 1
+                    chan = c0 + LANE * DPL
+                    assert (chan + DPL - 1).max() < 3 * HD
+    for m in range(3):
+        assert (written[m] == 1).all(), m
+    assert (gates == 1).all()
+
+
+@pytest.mark.parametrize("B,N,dm,H,d,K,r", [(2, 37, 256, 2, 128, 4, 16), (1, 256, 512, 2, 128, 4, 16),
+                                            (2, 257, 256, 2, 128, 4, 16), (1, 1000, 384, 2, 128, 4, 16),
+                                            (2, 509, 256, 4, 64, 1, 4), (1, 777, 320, 4, 64, 8, 1),
+                                            (1, 600, 512, 1, 256, 3, 8), (1, 16384, 1536, 12, 128, 4, 16)])
+def test_fused_prologue_indices(B, N, dm, H, d, K, r):
+    fused_prologue(B, N, dm, H, d, K, r)
