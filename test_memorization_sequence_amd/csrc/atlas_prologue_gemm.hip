@@ -376,8 +376,11 @@ fused_prologue_kernel(FusedParams p) {
       tz[i][j] = jj >= 0 ? wc[jj] : 0.f;
     }
   }
+  // the lane's byte within a row before the swizzle (granule col >> 3, byte
+  // (col & 7) 2): the slot is the granule ^ (t & 15), one xor-add per row
+  const int lb = ((col >> 3) << 4) | ((col & 7) * 2);
   auto ld = [&](int t, float (&x)[DPL]) {
-    const char* a = ptile(smem, t, col >> 3) + (col & 7) * 2;
+    const char* a = smem + ((lb ^ ((t & 15) << 4)) + t * 512);
     if constexpr (DPL == 1) {
       x[0] = (float)*reinterpret_cast<const bf16*>(a);
     } else if constexpr (DPL == 2) {
@@ -402,7 +405,11 @@ fused_prologue_kernel(FusedParams p) {
     for (int i = 0; i < DPL; ++i) win[i][j] = t >= 0 ? x[i] : 0.f;
   }
   float* parts = blk + wave * EPI_WAVE_FLOATS;   // [TB][64] parts, then TB scales
-  bf16* out = (m == 0 ? p.q : m == 1 ? p.k : p.v) + (((size_t)b * p.H + h) * p.N + row0) * D + lane * DPL;
+  // this head's output rows through a descriptor: the row offset is the
+  // same for every lane (a scalar offset), the lane's channels a fixed one
+  const __amdgpu_buffer_rsrc_t ro =
+      rsrc((m == 0 ? p.q : m == 1 ? p.k : p.v) + ((size_t)b * p.H + h) * p.N * D, (unsigned)(p.N * D * 2));
+  const int ovoff = lane * DPL * 2;
   for (int tb = t_beg; tb < t_end; tb += TB) {
     float x[TB][DPL], o[TB][DPL];
 #pragma unroll
@@ -427,23 +434,23 @@ fused_prologue_kernel(FusedParams p) {
 #pragma unroll
     for (int u = 0; u < TB; ++u) scale[u] = 1.f;
     if (m < 2) {
-      // lane u < TB: row tb + u's parts, summed as group_sum(16) then the
-      // four rows' totals, as seen by lane 0 of each row
+      // lane 4 u + g: group g of row tb + u's 64 parts, summed as
+      // group_sum(16) leaves it in lane 0 of that row; then the four groups'
+      // totals meet as (g0 + g1) + (g2 + g3) by quad moves
       asm volatile("" ::: "memory");
-      if (lane < TB) {
-        const float* v = parts + lane * 64;
-        float row[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 p0 = *reinterpret_cast<const float4*>(v + 16 * g);
-          const float4 p1 = *reinterpret_cast<const float4*>(v + 16 * g + 4);
-          const float4 p2 = *reinterpret_cast<const float4*>(v + 16 * g + 8);
-          const float4 p3 = *reinterpret_cast<const float4*>(v + 16 * g + 12);
-          row[g] = (((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w))) +
-                   (((p2.x + p2.y) + (p2.z + p2.w)) + ((p3.x + p3.y) + (p3.z + p3.w)));
-        }
-        const float ss = (row[0] + row[1]) + (row[2] + row[3]);
-        parts[TB * 64 + lane] = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(|x|, 1e-12)
+      {
+        static_assert(TB == 16, "four lanes per row of the batch");
+        const int u = lane >> 2, g = lane & 3;
+        const float* v = parts + u * 64 + 16 * g;
+        const float4 p0 = *reinterpret_cast<const float4*>(v);
+        const float4 p1 = *reinterpret_cast<const float4*>(v + 4);
+        const float4 p2 = *reinterpret_cast<const float4*>(v + 8);
+        const float4 p3 = *reinterpret_cast<const float4*>(v + 12);
+        const float rg = (((p0.x + p0.y) + (p0.z + p0.w)) + ((p1.x + p1.y) + (p1.z + p1.w))) +
+                         (((p2.x + p2.y) + (p2.z + p2.w)) + ((p3.x + p3.y) + (p3.z + p3.w)));
+        const float pair = rg + dppf<0xB1>(rg);      // g0 + g1 in lane g = 0, g2 + g3 in lane g = 2
+        const float ss = pair + dppf<0x4E>(pair);    // (g0 + g1) + (g2 + g3) in lane g = 0
+        if (g == 0) parts[TB * 64 + u] = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(|x|, 1e-12)
       }
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -459,12 +466,17 @@ fused_prologue_kernel(FusedParams p) {
     for (int u = 0; u < TB; ++u) {
       const int t = tb + u;
       if (t >= t_end) break;
-      bf16* o_t = out + (size_t)t * D;
-      if constexpr (DPL == 2) {
-        *reinterpret_cast<bf16x2*>(o_t) = bf16x2{(bf16)(o[u][0] * scale[u]), (bf16)(o[u][1] * scale[u])};
+      const int so = (row0 + t) * D * 2;
+      if constexpr (DPL == 1) {
+        const bf16 y = (bf16)(o[u][0] * scale[u]);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, y), ro, ovoff, so, 0);
+      } else if constexpr (DPL == 2) {
+        const bf16x2 y{(bf16)(o[u][0] * scale[u]), (bf16)(o[u][1] * scale[u])};
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, y), ro, ovoff, so, 0);
       } else {
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) o_t[i] = (bf16)(o[u][i] * scale[u]);
+        const bf16x4 y{(bf16)(o[u][0] * scale[u]), (bf16)(o[u][1] * scale[u]), (bf16)(o[u][2] * scale[u]),
+                       (bf16)(o[u][3] * scale[u])};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, y), ro, ovoff, so, 0);
       }
     }
     asm volatile("" ::: "memory");   // this batch's reads of the parts before the next batch's writes
@@ -494,7 +506,9 @@ bool fused_supported(int d_head, int heads, int gate_rank, int seq_len, int d_mo
   if (4L * heads * (gate_rank + 1) > GATE_PARAM_FLOATS) return false;   // the gate tile's V and b in LDS
   // one sequence's rows through a 32-bit descriptor, with room for the
   // scalar offsets that send loads past it
-  return (long)seq_len * d_model * 2 < (1L << 30) && (long)BM * d_model * 2 < (1L << 29);
+  // (and one head's output rows through another)
+  return (long)seq_len * d_model * 2 < (1L << 30) && (long)BM * d_model * 2 < (1L << 29) &&
+         (long)seq_len * d_head * 2 < (1L << 31);
 }
 
 hipError_t fused_prologue(const FusedParams& p0, int d_head, hipStream_t st) {
