@@ -138,7 +138,6 @@ static const ShardedVariant* find_sharded(const atlas_mem_config* c) {
 
 static const StreamVariant* find_streamed(const atlas_mem_config* c) {
   if (c->memory != ATLAS_MEM_MLP || c->feature_map != ATLAS_PHI_IDENTITY || c->io_dtype != ATLAS_BF16) return nullptr;
-  if (c->mlp_layernorm && c->bias != ATLAS_BIAS_L2 && c->bias != ATLAS_BIAS_DOT) return nullptr;
   if (c->mlp_gated) return nullptr;
   if (c->d_k != c->d_v) return nullptr;
   // the kernel addresses one sequence's inputs and coefficients through

@@ -106,7 +106,8 @@ struct TShape {
 
 // SHAPE: 0 for the l2 and dot-product biases, BIAS_LP or BIAS_HUBER for the
 // biases that form D2 from whole error rows; LNORM: the layer-norm memory
-// r + LN(W2 gelu(W1 x)) (with SHAPE 0).  Each instance holds only its own code.
+// r + LN(W2 gelu(W1 x)) (with any bias but dot under a SHAPE).  Each instance
+// holds only its own code.
 template <class S, int SHAPE, bool LNORM>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -139,7 +140,10 @@ stream_mlp_kernel(ShardedParams p) {
   const float s_grad = p.grad_scale;
   // l_p and Huber biases reshape the errors once whole rows are known
   constexpr bool shaped = SHAPE != 0, huber = SHAPE == BIAS_HUBER, lnorm = LNORM;
-  static_assert(!(LNORM && SHAPE != 0), "layer norm with the l2 / dot biases");
+  // the layer norm's scratch follows the Huber deltas when both are in use
+  static_assert(!(LNORM && SHAPE == BIAS_HUBER) ||
+                    (size_t)(WP + (4 * WP + 2 * BC) * S::NW) * 4 <= S::oW2 - S::oAT,
+                "layer-norm scratch after the Huber deltas fits AT");
   const float ln_eps = p.ln_eps;
   const float bias_p = p.bias_p, sign_alpha = p.sign_alpha;
 
@@ -176,7 +180,7 @@ stream_mlp_kernel(ShardedParams p) {
   float* rn = dlw + WP;
   // layer norm: per-wave partial row sums in the same region, four arrays
   // [NW][WP] for the window rows, two [NW][BC] for the output rows
-  float* lnS = reinterpret_cast<float*>(smem + S::oAT);
+  float* lnS = reinterpret_cast<float*>(smem + S::oAT) + (LNORM && SHAPE == BIAS_HUBER ? WP : 0);
   bf16* W2L = reinterpret_cast<bf16*>(smem + S::oW2);
   bf16* An = W2L;
   bf16* Ah = reinterpret_cast<bf16*>(smem + S::oAh);
@@ -392,10 +396,12 @@ stream_mlp_kernel(ShardedParams p) {
     return v + __shfl_xor(v, 32);
   };
   auto across = [&](const float* P, int n, int w) { return ((P[w] + P[n + w]) + P[2 * n + w]) + P[3 * n + w]; };
-  // Layer norm (l2 / dot biases): the branch u is in yh (window sums), t
-  // holds v - r (l2) or v (dot).  Mean and variance of u per row (two
-  // passes), nhat = (u - mean) / sd, the slope g = nhat - t (l2) or -t (dot),
-  // then D2 = s gamma (g - mean(g) - nhat mean(g nhat)) / sd.
+  // Layer norm: the branch u is in yh (window sums), t holds v - r (l2, l_p,
+  // Huber) or v (dot).  Mean and variance of u per row (two passes),
+  // nhat = (u - mean) / sd, the error e = nhat - t = y - v, the slope g = e
+  // (l2), -t (dot), the l_p or Huber slope of e (Huber: the row's |e|_2
+  // against its delta, a third pass), then
+  // D2 = s gamma (g - mean(g) - nhat mean(g nhat)) / sd.
   auto ln_d2 = [&](const float (&t)[NT][NDT][4]) __attribute__((always_inline)) {
     const int lane = fresh(threadIdx.x) & 63, g = lane >> 4, c16 = lane & 15, wv = threadIdx.x >> 6;
     const int dvw = S::DVW * wv;
@@ -431,15 +437,51 @@ stream_mlp_kernel(ShardedParams p) {
     }
     __syncthreads();
 #pragma unroll
+    for (int m = 0; m < NT; ++m) rs[m] = 1.f / sqrtf(across(B_, WP, 16 * m + c16) * (1.f / DV) + ln_eps);
+    bool small[NT];
+    float dl[NT];
+#pragma unroll
     for (int m = 0; m < NT; ++m) {
-      rs[m] = 1.f / sqrtf(across(B_, WP, 16 * m + c16) * (1.f / DV) + ln_eps);
+      small[m] = true;
+      dl[m] = 0.f;
+    }
+    if constexpr (huber) {
+      // every wave read A_ (the means) before the barrier above
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        float s2 = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < NDT; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = (yh[m][bb][r] - mu[m]) * rs[m] - t[m][bb][r];
+            s2 = fmaf(e, e, s2);
+          }
+        s2 = rowsum(s2);
+        if (g == 0) A_[wv * WP + 16 * m + c16] = s2;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const int w = 16 * m + c16;
+        dl[m] = dlw[w];
+        small[m] = sqrtf(across(A_, WP, w)) <= dl[m];
+      }
+    }
+    auto slope = [&](float nh, float tv, int m) {
+      if constexpr (huber) return huber_slope(nh - tv, small[m], dl[m], sign_alpha);
+      else if constexpr (shaped) return lp_slope(nh - tv, bias_p, sign_alpha);
+      else return dot ? -tv : nh - tv;
+    };
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
       float s1 = 0.f, s2 = 0.f;
 #pragma unroll
       for (int bb = 0; bb < NDT; ++bb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float nh = (yh[m][bb][r] - mu[m]) * rs[m];
-          const float gg = dot ? -t[m][bb][r] : nh - t[m][bb][r];
+          const float gg = slope(nh, t[m][bb][r], m);
           s1 += gg;
           s2 = fmaf(gg, nh, s2);
         }
@@ -462,7 +504,7 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float nh = (yh[m][bb][r] - mu[m]) * rs[m];
-          const float gg = dot ? -t[m][bb][r] : nh - t[m][bb][r];
+          const float gg = slope(nh, t[m][bb][r], m);
           d[r] = (bf16)(sg * (gg - mg - nh * mgn) * rs[m]);
         }
         *reinterpret_cast<bf16x4*>(D2 + w * LV + dvw + 16 * bb + 4 * g) = d;
@@ -506,8 +548,8 @@ stream_mlp_kernel(ShardedParams p) {
         }
       }
     }
-    if constexpr (shaped) shape_d2();
     if constexpr (lnorm) ln_d2(tln);
+    else if constexpr (shaped) shape_d2();
   };
   // chunks >= 1, l_p / Huber: the errors from the staged value rows Vw
   auto shaped_d2_lds = [&](const bf16* Vw, const bf16* Xw) {
@@ -1173,8 +1215,8 @@ stream_mlp_kernel(ShardedParams p) {
     if (more) {
       wait_vmem();       // this wave's loads into LDS have landed
       __syncthreads();   // and everyone's
-      if constexpr (shaped) shaped_d2_lds(W2L, Xn);
-      else if constexpr (lnorm) ln_d2_lds(W2L, Xn);
+      if constexpr (lnorm) ln_d2_lds(W2L, Xn);
+      else if constexpr (shaped) shaped_d2_lds(W2L, Xn);
       else finish_d2_lds(W2L, Xn);
       prefetch(J0, dst_t);
       bf16* tmp = Xc;
@@ -1210,13 +1252,17 @@ hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipSt
                      stream, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // instance: 0 plain, 1 l_p, 2 Huber, 3 layer norm
-  const int inst = sp.layernorm ? 3 : sp.bias == BIAS_LP ? 1 : sp.bias == BIAS_HUBER ? 2 : 0;
-  const void* fns[4] = {reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, 0, false>),
+  // instance: 0 plain, 1 l_p, 2 Huber, 3 layer norm (l2 / dot), 4 layer norm
+  // with l_p, 5 layer norm with Huber
+  const int shape = sp.bias == BIAS_LP ? 1 : sp.bias == BIAS_HUBER ? 2 : 0;
+  const int inst = sp.layernorm ? (shape == 0 ? 3 : 3 + shape) : shape;
+  const void* fns[6] = {reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, 0, false>),
                         reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_LP, false>),
                         reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_HUBER, false>),
-                        reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, 0, true>)};
-  static bool attr_set[4] = {false, false, false, false};
+                        reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, 0, true>),
+                        reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_LP, true>),
+                        reinterpret_cast<const void*>(&streamed::stream_mlp_kernel<S, BIAS_HUBER, true>)};
+  static bool attr_set[6] = {false, false, false, false, false, false};
   if (!attr_set[inst]) {
     // allow more than the default dynamic LDS; a refusal shows up at launch
     (void)hipFuncSetAttribute(fns[inst], hipFuncAttributeMaxDynamicSharedMemorySize, (int)S::lds);
@@ -1225,14 +1271,14 @@ hipError_t launch_streamed(const ShardedParams& sp, const CoeffParams& kp, hipSt
   }
   const unsigned blocks = G == 1 ? (unsigned)sp.n_seq : (unsigned)((sp.n_seq + 7) / 8) * 8u * G;
   if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
-  if (inst == 1)
-    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_LP, false>), dim3(blocks), dim3(256), S::lds, stream, sp);
-  else if (inst == 2)
-    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_HUBER, false>), dim3(blocks), dim3(256), S::lds, stream, sp);
-  else if (inst == 3)
-    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, 0, true>), dim3(blocks), dim3(256), S::lds, stream, sp);
-  else
-    hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, 0, false>), dim3(blocks), dim3(256), S::lds, stream, sp);
+  switch (inst) {
+    case 1: hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_LP, false>), dim3(blocks), dim3(256), S::lds, stream, sp); break;
+    case 2: hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_HUBER, false>), dim3(blocks), dim3(256), S::lds, stream, sp); break;
+    case 3: hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, 0, true>), dim3(blocks), dim3(256), S::lds, stream, sp); break;
+    case 4: hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_LP, true>), dim3(blocks), dim3(256), S::lds, stream, sp); break;
+    case 5: hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, BIAS_HUBER, true>), dim3(blocks), dim3(256), S::lds, stream, sp); break;
+    default: hipLaunchKernelGGL((streamed::stream_mlp_kernel<S, 0, false>), dim3(blocks), dim3(256), S::lds, stream, sp); break;
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return e;
   return hipSuccess;

@@ -106,9 +106,8 @@ def test_other_attentional_biases():
 
 
 def test_layernorm_memory_configs():
-    """The LN variant needs an MLP and 0 < eps < 1; the per-sequence family
-    serves it with every bias, the streamed family with the l2 / dot biases,
-    the sharded family not at all."""
+    """The LN variant needs an MLP and 0 < eps < 1; the per-sequence and the
+    streamed families serve it with every bias, the sharded family not at all."""
     ok, inv, uns = binding.OK, binding.ERR_INVALID, binding.ERR_UNSUPPORTED
     ln = lambda name, **kw: replace(WORKLOADS[name], layernorm=True, **kw)
     assert binding.supported(binding.config_of(ln("linear_poly2"))) == inv
@@ -122,7 +121,8 @@ def test_layernorm_memory_configs():
     assert binding.supported(binding.config_of(ln("layer_scale"), "sharded")) == uns
     assert binding.supported(binding.config_of(ln("layer_scale"), "streamed")) == ok
     assert binding.supported(binding.config_of(ln("layer_scale", bias="dot"), "streamed")) == ok
-    assert binding.supported(binding.config_of(ln("layer_scale", bias="lp", bias_p=3.0), "streamed")) == uns
+    for bias in ("lp", "huber"):
+        assert binding.supported(binding.config_of(ln("layer_scale", bias=bias, bias_p=3.0), "streamed")) == ok
     c = binding.config_of(WORKLOADS["mlp64"])
     c.mlp_layernorm = 2
     assert binding.supported(c) == inv

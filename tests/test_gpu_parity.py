@@ -385,12 +385,13 @@ def test_short_calls_other_biases(B, bias, n):
 # to 22 % (tests/test_layernorm_conditioning.py measures it).  Parity is
 # checked on the cases whose own sensitivity is small.
 LN_MLPS = [n for n in ORDER if WORKLOADS[n].memory == "mlp"]
-LN_CASES = ([(n, b, "lively") for n in LN_MLPS for b in ("l2", "dot", "lp3")] + [("mlp64", "huber_smooth", "lively")]
+LN_CASES = ([(n, b, "lively") for n in LN_MLPS for b in ("l2", "dot", "lp3")]
+            + [("mlp64", "huber_smooth", "lively")]
             + [(n, b, "preset") for n in ("atlas_long", "layer_scale") for b in ("l2", "dot")])
-# AUTO: the streamed family for the identity-map MLPs with the l2 / dot
-# biases, the per-sequence family otherwise; the former also per-sequence
+# AUTO: the streamed family for the identity-map MLPs (every bias), the
+# per-sequence family otherwise; the former also per-sequence
 LN_RUNS = ([(n, b, r, "auto") for n, b, r in LN_CASES]
-           + [(n, b, r, "per_sequence") for n, b, r in LN_CASES if n in GROUPED and b in ("l2", "dot")])
+           + [(n, b, r, "per_sequence") for n, b, r in LN_CASES if n in GROUPED])
 
 
 @pytest.mark.parametrize("name,bias,recipe,kernel", LN_RUNS)
@@ -403,7 +404,7 @@ def test_parity_layernorm_memory(B, name, bias, recipe, kernel):
     _say(f"[parity-ln] {name} {bias} {recipe} {kernel} B=1 H=2 N={SMALL_N}")
     binding, H = B
     inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl, kernel=kernel)
-    want = kernel if kernel != "auto" else "streamed" if name in GROUPED and bias in ("l2", "dot") else "per_sequence"
+    want = kernel if kernel != "auto" else "streamed" if name in GROUPED else "per_sequence"
     assert mem.family() == want
     r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
     _say(f"[parity-ln] {name} {bias} {recipe} ({mem.family()}): {r}")

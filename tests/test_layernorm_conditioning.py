@@ -33,7 +33,8 @@ def _sensitivity(name, bias, recipe):
     return max(rel(out1, out), rel(st1["mem"], st["mem"]), rel(st1["mom"], st["mom"]))
 
 
-@pytest.mark.parametrize("name,bias,recipe", [("mlp64", "l2", "lively"), ("layer_scale", "l2", "preset")])
+@pytest.mark.parametrize("name,bias,recipe", [("mlp64", "l2", "lively"), ("layer_scale", "l2", "preset"),
+                                              ("mlp64", "huber_smooth", "lively")])
 def test_cases_used_for_parity_are_well_conditioned(name, bias, recipe):
     assert _sensitivity(name, bias, recipe) < 1e-2
 
