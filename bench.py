@@ -35,7 +35,7 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 MEASURED_TRAFFIC = {
     # (workload, kernel, optimizer, tokens per sequence), l2 bias, plain memory
     ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "a7f34259c17c8213", "bytes": 76.10e9},
-    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "adf685316c69b214", "bytes": 27.91e9},
+    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "89b04162e0245e22", "bytes": 27.94e9},
     ("layer_scale", "chunk_kernel", "muon", 64): {"src": "fa58fd57df42e5c3", "bytes": 91.68e9},
     ("linear64_delta", "chunk_kernel", "gd", 1024): {"src": "fa58fd57df42e5c3", "bytes": 1.67e6},
     # the recurrence and the retrieval after it (the pair the kernel events bracket)

@@ -45,6 +45,31 @@
 #include "atlas_mem_phi.h"
 
 namespace atlas {
+
+// The group barrier (atlas_mem_group.h) in two halves, so that work that
+// needs neither the partners' data nor their arrival runs between them:
+// group_arrive publishes this workgroup's stores and its arrival,
+// group_wait waits for the others (bounded; see group_barrier).
+__device__ __forceinline__ void group_arrive(unsigned* ctr) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(ctr, 1u);
+}
+__device__ __forceinline__ void group_wait(unsigned* ctr, unsigned target, unsigned* err) {
+  if (threadIdx.x == 0) {
+    unsigned polls = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+      if (++polls > (1u << 24)) {
+        atomicOr(err, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  asm volatile("buffer_inv sc0" ::: "memory");
+}
 namespace grouped {
 
 using namespace mfma;
@@ -331,7 +356,32 @@ grouped_kernel(GroupedParams p) {
         }
       }
     }
-    group_barrier(ctr, G * (++nbar), err);
+    // the retrieval's terms of the chunk-start state, A_q Xq W1^T and
+    // B_q Xq S1^T (this member's 16 units; queries from L2, the state
+    // images in LDS), need neither the partners' partials nor D1: they run
+    // between this member's arrival at the barrier and its wait
+    group_arrive(ctr);
+    f32x4 ra1 = zero4(), ra2 = zero4();
+    {
+      const int qrow = t0 + Q0 + c16;
+      constexpr int NS = DP / 32, PF = 8;
+      const int k0 = pm % NS;   // per-member starting step, as in the forward
+      auto kstep = [&](int st) { const int k = st + k0; return k < NS ? k : k - NS; };
+      bf16x8 xf[PF + 1];
+#pragma unroll
+      for (int st = 0; st < PF && st < NS; ++st) xf[st] = gload8(rxq, (qrow * DP + 32 * kstep(st) + 8 * g) * 2);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        if (st + PF < NS) xf[(st + PF) % (PF + 1)] = gload8(rxq, (qrow * DP + 32 * kstep(st + PF) + 8 * g) * 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 xq = xf[st % (PF + 1)];
+        const int ks = kstep(st);
+        ra1 = mma(xq, ld_nat(W1i, LF, 0, 32 * ks, lane), ra1);
+        if (mom) ra2 = mma(xq, ld_nat(S1i, LF, 0, 32 * ks, lane), ra2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    group_wait(ctr, G * (++nbar), err);
     if (ch == 0 && tid == 0) {
       const unsigned m = __hip_atomic_load(xmask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (__builtin_popcount(m) != 1) atomicOr(err, 2u);
@@ -388,8 +438,13 @@ grouped_kernel(GroupedParams p) {
         *reinterpret_cast<bf16x4*>(d2buf + ((size_t)sl * WP + w) * DV + o4) = d4;
       }
     }
+    // the previous chunk's outputs need neither this barrier nor the
+    // partners' D2 rows (their partials were published at the first
+    // barrier, and their slot is rewritten only after the next one): they
+    // are reduced between this member's arrival and its wait
+    group_arrive(ctr);
     if (ch > 0) reduce_out(ch - 1);
-    group_barrier(ctr, G * (++nbar), err);
+    group_wait(ctr, G * (++nbar), err);
 
     // ---- all-gather D2 -> LDS [WP][LV]
     {
@@ -427,27 +482,10 @@ grouped_kernel(GroupedParams p) {
     __syncthreads();
 
     // ---- retrieval, layer 1: Zq = A_q Xq W1^T + B_q Xq S1^T - Q1 D1  [query rows Q0.. x 16 units]
+    // (the first two terms were formed during the first barrier)
     {
-      f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4();
-      const int qrow = t0 + Q0 + c16;
-      {
-        constexpr int NS = DP / 32, PF = 8;
-        const int k0 = pm % NS;   // per-member starting step, as in the forward
-        auto kstep = [&](int st) { const int k = st + k0; return k < NS ? k : k - NS; };
-        bf16x8 xf[PF + 1];
-#pragma unroll
-        for (int st = 0; st < PF && st < NS; ++st) xf[st] = gload8(rxq, (qrow * DP + 32 * kstep(st) + 8 * g) * 2);
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          if (st + PF < NS) xf[(st + PF) % (PF + 1)] = gload8(rxq, (qrow * DP + 32 * kstep(st + PF) + 8 * g) * 2);
-          __builtin_amdgcn_sched_barrier(0);
-          const bf16x8 xq = xf[st % (PF + 1)];
-          const int ks = kstep(st);
-          a1 = mma(xq, ld_nat(W1i, LF, 0, 32 * ks, lane), a1);
-          if (mom) a2 = mma(xq, ld_nat(S1i, LF, 0, 32 * ks, lane), a2);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      const f32x4 a1 = ra1, a2 = ra2;
+      f32x4 a3 = zero4();
 #pragma unroll
       for (int s = 0; s < WP / 32; ++s) {
         const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(Q1g + (Q0 + c16) * WP + 32 * s + 8 * g);
