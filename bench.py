@@ -35,12 +35,12 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 MEASURED_TRAFFIC = {
     # (workload, kernel, optimizer, tokens per sequence), l2 bias, plain memory
     ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "a7f34259c17c8213", "bytes": 76.10e9},
-    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "89b04162e0245e22", "bytes": 27.94e9},
+    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "a571c0e17f53322c", "bytes": 27.74e9},
     ("layer_scale", "chunk_kernel", "muon", 64): {"src": "fa58fd57df42e5c3", "bytes": 91.68e9},
     ("linear64_delta", "chunk_kernel", "gd", 1024): {"src": "fa58fd57df42e5c3", "bytes": 1.67e6},
     # the recurrence and the retrieval after it (the pair the kernel events bracket)
     ("linear_poly2", "linear_rec_kernel", "gd", 4096): {"src": "50154b8d85754b04", "bytes": 0.344e9},
-    ("mlp64", "sharded_mlp_kernel", "gd", 8192): {"src": "82f6190e28b55961", "bytes": 1.797e9},
+    ("mlp64", "sharded_mlp_kernel", "gd", 8192): {"src": "25408e691000463a", "bytes": 1.778e9},
 }
 
 

@@ -42,6 +42,7 @@
 #include "atlas_mem_coeff.h"
 #include "atlas_mem_frag.h"
 #include "atlas_mem_group.h"
+#include "atlas_mem_group_split.h"
 
 namespace atlas {
 namespace sharded {
@@ -396,9 +397,14 @@ sharded_mlp_kernel(ShardedParams p) {
         }
         *reinterpret_cast<bf16x4*>(d2b + (size_t)w * DV + o4) = d4;
       }
-      if (ch > 0) reduce_out(ch - 1);
     }
-    group_barrier(ctr, G * (++nbar), err);
+    // the previous chunk's outputs need neither this barrier nor the
+    // partners' D2 rows (their partials were published at the first
+    // barrier, and their slot is rewritten only after the next one): they
+    // are reduced between this member's arrival and its wait
+    group_arrive(ctr);
+    if (ch > 0) reduce_out(ch - 1);
+    group_wait(ctr, G * (++nbar), err);
 
     // ---- all-gather D2 -> D2 [tok][dv], D2T [dv][tok]
     {
