@@ -37,6 +37,7 @@
 #include "atlas_mem_frag.h"
 #include "atlas_mem_bias.h"
 #include "atlas_mem_group.h"
+#include "atlas_mem_group_split.h"
 
 namespace atlas {
 namespace streamed {
@@ -1126,13 +1127,17 @@ stream_mlp_kernel(ShardedParams p) {
             for (int bb = 0; bb < NDT; ++bb) d[(m * NDT + bb) * 256] = yp[m][bb];
       }
       if (more) xput(xYh_at(par, pm), yh);
-      group_barrier(ctr, G * (++nbar), err);
+      // ---- the next chunk's inputs into LDS, in flight during the wait for
+      // the partner, its reads and the output stores: every wave is past
+      // its last read of the target regions once it has arrived (the
+      // residual rows are in registers already)
+      group_arrive(ctr);
+      if (more) stage_next(ch + 1);
+      group_wait(ctr, G * (++nbar), err);
     } else {
       __syncthreads();
+      if (more) stage_next(ch + 1);
     }
-    // ---- the next chunk's inputs into LDS, in flight during the partner's
-    // reads and the output stores
-    if (more) stage_next(ch + 1);
     if constexpr (G > 1) {
       if (more) xadd(xYh_at(par, 1 - pm), yh);
       // every tile is loaded (the ones of the other half are not used), all
