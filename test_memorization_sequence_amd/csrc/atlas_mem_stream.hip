@@ -38,6 +38,7 @@
 #include "atlas_mem_bias.h"
 #include "atlas_mem_group.h"
 #include "atlas_mem_group_split.h"
+#include "atlas_mem_lds_sync.h"
 
 namespace atlas {
 namespace streamed {
@@ -88,15 +89,17 @@ struct TShape {
   // the partial sums A' W2'^T [NT][NDT] and y [NQ][NDT] as per-lane f32x4
   // tiles in lane order (both members use the same lane layout)
   static constexpr size_t tile_bytes = 256 * 16;
-  // the state between passes, tile-major: W1, S1, W2, S2 (fp32), each wave's
-  // f32x4 tile 1 KB contiguous
+  // the state between passes: one block per super tile J and wave w (block
+  // J * NW + w) of lane-ordered f32x4 tiles, 1 KB each: this wave's W1 rows
+  // [ND], S1 rows [ND], W2 values [NU][NDT], S2 values [NU][NDT] (fp32), then
+  // A = gelu(Z) and gelu'(Z) of the tile at the next window [NT] (bf16, saved
+  // for the next pass, which is spared the recomputation of Z)
+  static constexpr int TW1 = 0, TS1 = ND, TW2 = 2 * ND, TS2 = 2 * ND + NU * NDT, TAG = 2 * ND + 2 * NU * NDT;
+  static constexpr int NTB = TAG + NT;            // tiles per block
+  static constexpr size_t SB = (size_t)NTB * 1024;
   static constexpr size_t xTS = 0;
-  // A = gelu(Z) and gelu'(Z) of every super tile for the next pass (bf16,
-  // NT lane-ordered 1 KB chunks per wave and tile): saves the next pass the
-  // recomputation of Z
-  static constexpr size_t xAG = xTS + 4ull * H * D * 4;
-  static constexpr size_t ag_bytes = (size_t)(H / HJ) * NW * NT * 1024;
-  static constexpr size_t xYh = xAG + ag_bytes;
+  static constexpr size_t ts_bytes = (size_t)(H / HJ) * NW * SB;
+  static constexpr size_t xYh = xTS + ts_bytes;
   static constexpr size_t xYp = xYh + 2ull * G * NT * NDT * tile_bytes;
   static constexpr size_t xbytes = G == 1 ? xYh : xYp + 2ull * G * NQ * NDT * tile_bytes;
   static_assert(D == DV, "one tile-major stride for both layers");
@@ -366,7 +369,7 @@ stream_mlp_kernel(ShardedParams p) {
         s2 += __shfl_xor(s2, 32);
         if (g == 0) rn[wv * WP + 16 * m + c16] = s2;
       }
-      __syncthreads();
+      lds_sync();
     }
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
@@ -421,7 +424,7 @@ stream_mlp_kernel(ShardedParams p) {
       sum = rowsum(sum);
       if (g == 0) A_[wv * WP + 16 * m + c16] = sum;
     }
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       mu[m] = across(A_, WP, 16 * m + c16) * (1.f / DV);
@@ -436,7 +439,7 @@ stream_mlp_kernel(ShardedParams p) {
       sum = rowsum(sum);
       if (g == 0) B_[wv * WP + 16 * m + c16] = sum;
     }
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int m = 0; m < NT; ++m) rs[m] = 1.f / sqrtf(across(B_, WP, 16 * m + c16) * (1.f / DV) + ln_eps);
     bool small[NT];
@@ -461,7 +464,7 @@ stream_mlp_kernel(ShardedParams p) {
         s2 = rowsum(s2);
         if (g == 0) A_[wv * WP + 16 * m + c16] = s2;
       }
-      __syncthreads();
+      lds_sync();
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
         const int w = 16 * m + c16;
@@ -493,7 +496,7 @@ stream_mlp_kernel(ShardedParams p) {
         E_[wv * WP + 16 * m + c16] = s2;
       }
     }
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       const int w = 16 * m + c16;
@@ -610,47 +613,71 @@ stream_mlp_kernel(ShardedParams p) {
     }
   };
 
-  // state tiles of super tile J (see the layout notes at the top): uniform
-  // tile base + one lane offset + a compile-time offset per tile
-  // Two layouts of the state: the row-major one of the call's state buffer
-  // (W1 [H][D], W2 [DV][H], the momentum alike), read by the first pass and
-  // written by the last, and the tile-major copy in the workspace used by the
-  // passes in between, in which every access of a wave is one contiguous
-  // 1 KB block.  Buffer accesses: a per-lane byte offset (constant for the
-  // call) and a wave-uniform scalar offset; the layout is chosen by selecting
-  // descriptor and offsets, so exactly one access is issued.
+  // State tiles.  Two layouts: the row-major one of the call's state buffer
+  // (W1 [H][D], W2 [DV][H], the momentum alike), copied into the workspace's
+  // blocks before the first pass and back after the last, and the blocks
+  // (see the layout notes at the top), in which every access of a wave is one
+  // contiguous 1 KB tile.  A block access is the lane offset vT, the tile's
+  // place within its 4 KB (the compiler keeps the three sums of vT in
+  // registers, or folds them into the instruction's immediate offset) and a
+  // wave-uniform scalar offset in steps of 4 KB.
   const int wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const __amdgpu_buffer_rsrc_t rT = buffer_of(xw + S::xTS, 4u * H * D * 4);
-  const __amdgpu_buffer_rsrc_t rW = buffer_of(W1g, 2u * H * D * 4);
-  // without momentum the caller's momentum is never touched (a descriptor of
-  // size zero: loads read zeros, stores are dropped) and the tile-major copy
-  // of S holds the zeros the first pass read, so S stays zero without branches
-  const __amdgpu_buffer_rsrc_t rM = buffer_of(S1g, mom ? 2u * H * D * 4 : 0u);
-  const __amdgpu_buffer_rsrc_t rAG = buffer_of(xw + S::xAG, (unsigned)S::ag_bytes);
-  const int vT = (threadIdx.x & 63) * 16;                                   // tile-major
-  const int vW1 = (threadIdx.x & 15) * D * 4 + ((threadIdx.x >> 4) & 3) * 16;  // row-major W1 / S1
-  const int vW2 = (threadIdx.x & 15) * H * 4 + ((threadIdx.x >> 4) & 3) * 16;  // row-major W2 / S2
-  // which: 0 = W1, 1 = S1
-  auto ld1 = [&](int which, bool tiled, int J, int t) -> f32x4 {
-    const int so_t = ((J * 4 + wave_s) * ND + t) * 1024 + which * H * D * 4;
-    const int so_r = (J * HJ + 16 * wave_s) * D * 4 + 64 * t;
-    return buf_load4(tiled ? rT : which ? rM : rW, tiled ? vT : vW1, tiled ? so_t : so_r);
+  const __amdgpu_buffer_rsrc_t rT = buffer_of(xw + S::xTS, (unsigned)S::ts_bytes);
+  const int vT = (threadIdx.x & 63) * 16;
+  auto blk = [&](int J, int T) { return (J * S::NW + wave_s) * (int)S::SB + (T / 4) * 4096; };
+  auto tld = [&](int J, int T) -> f32x4 { return buf_load4(rT, vT + (T % 4) * 1024, blk(J, T)); };
+  auto tst = [&](const f32x4& x, int J, int T) { buf_store4(x, rT, vT + (T % 4) * 1024, blk(J, T)); };
+  // which: 0 = W1, 1 = S1 (tile t of this wave's rows)
+  auto ld1 = [&](int which, int J, int t) { return tld(J, (which ? S::TS1 : S::TW1) + t); };
+  auto st1 = [&](const f32x4& x, int which, int J, int t) { tst(x, J, (which ? S::TS1 : S::TW1) + t); };
+  // which: 0 = W2, 1 = S2 (unit tile a, value tile bb of this wave's rows)
+  auto ld2 = [&](int which, int J, int a, int bb) { return tld(J, (which ? S::TS2 : S::TW2) + a * NDT + bb); };
+  auto st2 = [&](const f32x4& x, int which, int J, int a, int bb) {
+    tst(x, J, (which ? S::TS2 : S::TW2) + a * NDT + bb);
   };
-  auto st1 = [&](const f32x4& v, int which, bool tiled, int J, int t) {
-    const int so_t = ((J * 4 + wave_s) * ND + t) * 1024 + which * H * D * 4;
-    const int so_r = (J * HJ + 16 * wave_s) * D * 4 + 64 * t;
-    buf_store4(v, tiled ? rT : which ? rM : rW, tiled ? vT : vW1, tiled ? so_t : so_r);
-  };
-  // which: 0 = W2, 1 = S2
-  auto ld2 = [&](int which, bool tiled, int J, int a, int bb) -> f32x4 {
-    const int so_t = ((J * 4 + wave_s) * (NU * NDT) + a * NDT + bb) * 1024 + (2 + which) * H * D * 4;
-    const int so_r = H * D * 4 + (S::DVW * wave_s + 16 * bb) * H * 4 + (J * HJ + 16 * a) * 4;
-    return buf_load4(tiled ? rT : which ? rM : rW, tiled ? vT : vW2, tiled ? so_t : so_r);
-  };
-  auto st2 = [&](const f32x4& v, int which, bool tiled, int J, int a, int bb) {
-    const int so_t = ((J * 4 + wave_s) * (NU * NDT) + a * NDT + bb) * 1024 + (2 + which) * H * D * 4;
-    const int so_r = H * D * 4 + (S::DVW * wave_s + 16 * bb) * H * 4 + (J * HJ + 16 * a) * 4;
-    buf_store4(v, tiled ? rT : which ? rM : rW, tiled ? vT : vW2, tiled ? so_t : so_r);
+  // Row-major <-> blocks: each lane moves the f32x4 it holds in both (the
+  // MFMA tile layout: unit row 16 w + (l & 15), four columns at 4 (l >> 4)).
+  // Without momentum the caller's momentum is never touched (a descriptor of
+  // size zero: loads read zeros, stores are dropped) and the blocks' S holds
+  // the zeros read here, so S stays zero without branches.
+  auto convert = [&](bool to_blocks) {
+    const __amdgpu_buffer_rsrc_t rW = buffer_of(W1g, 2u * H * D * 4);
+    const __amdgpu_buffer_rsrc_t rM = buffer_of(S1g, mom ? 2u * H * D * 4 : 0u);
+    const int vW1 = (threadIdx.x & 15) * D * 4 + ((threadIdx.x >> 4) & 3) * 16;
+    const int vW2 = (threadIdx.x & 15) * H * 4 + ((threadIdx.x >> 4) & 3) * 16;
+    for (int J = J0; J < J0 + NJ; ++J) {
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const __amdgpu_buffer_rsrc_t r = which ? rM : rW;
+        f32x4 x[ND], y[NU][NDT];
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+          const int so = (J * HJ + 16 * wave_s) * D * 4 + 64 * t;
+          x[t] = to_blocks ? buf_load4(r, vW1, so) : ld1(which, J, t);
+        }
+#pragma unroll
+        for (int a = 0; a < NU; ++a)
+#pragma unroll
+          for (int bb = 0; bb < NDT; ++bb) {
+            const int so = H * D * 4 + (S::DVW * wave_s + 16 * bb) * H * 4 + (J * HJ + 16 * a) * 4;
+            y[a][bb] = to_blocks ? buf_load4(r, vW2, so) : ld2(which, J, a, bb);
+          }
+#pragma unroll
+        for (int t = 0; t < ND; ++t) {
+          const int so = (J * HJ + 16 * wave_s) * D * 4 + 64 * t;
+          if (to_blocks) st1(x[t], which, J, t);
+          else buf_store4(x[t], r, vW1, so);
+        }
+#pragma unroll
+        for (int a = 0; a < NU; ++a)
+#pragma unroll
+          for (int bb = 0; bb < NDT; ++bb) {
+            const int so = H * D * 4 + (S::DVW * wave_s + 16 * bb) * H * 4 + (J * HJ + 16 * a) * 4;
+            if (to_blocks) st2(y[a][bb], which, J, a, bb);
+            else buf_store4(y[a][bb], r, vW2, so);
+          }
+      }
+    }
   };
 
   // State prefetch, one super tile ahead, into loop-carried registers: the
@@ -658,18 +685,18 @@ stream_mlp_kernel(ShardedParams p) {
   // issued after the loads the current tile still waits for (vmcnt retires in
   // order), so no wait in the current tile covers them.
   f32x4 pW1[ND], pS1[ND], pW2[NU][NDT], pAG[NT];
-  auto prefetch = [&](int J, bool tiled) {
+  auto prefetch = [&](int J) {
 #pragma unroll
-    for (int i = 0; i < NT; ++i) pAG[i] = buf_load4(rAG, vT, ((J * 4 + wave_s) * NT + i) * 1024);
+    for (int i = 0; i < NT; ++i) pAG[i] = tld(J, S::TAG + i);
 #pragma unroll
     for (int t = 0; t < ND; ++t) {
-      pW1[t] = ld1(0, tiled, J, t);
-      pS1[t] = ld1(1, tiled, J, t);   // without momentum: zeros (see below)
+      pW1[t] = ld1(0, J, t);
+      pS1[t] = ld1(1, J, t);   // without momentum: zeros
     }
 #pragma unroll
     for (int a = 0; a < NU; ++a)
 #pragma unroll
-      for (int bb = 0; bb < NDT; ++bb) pW2[a][bb] = ld2(0, tiled, J, a, bb);
+      for (int bb = 0; bb < NDT; ++bb) pW2[a][bb] = ld2(0, J, a, bb);
   };
 
   // Forward of super tile J on a window Xs with first-layer rows W1 (this
@@ -703,8 +730,8 @@ stream_mlp_kernel(ShardedParams p) {
     }
 #pragma unroll
     for (int i = 0; i < NT / 2; ++i) {
-      buf_store4(__builtin_bit_cast(f32x4, ca[i]), rAG, vT, ((J * 4 + wave_s) * NT + i) * 1024);
-      buf_store4(__builtin_bit_cast(f32x4, cd[i]), rAG, vT, ((J * 4 + wave_s) * NT + NT / 2 + i) * 1024);
+      tst(__builtin_bit_cast(f32x4, ca[i]), J, S::TAG + i);
+      tst(__builtin_bit_cast(f32x4, cd[i]), J, S::TAG + NT / 2 + i);
     }
   };
   // A' W2'^T of the tile into the window sums (after An^T is complete)
@@ -793,6 +820,9 @@ stream_mlp_kernel(ShardedParams p) {
     }
   };
 
+  // ---- the state into the blocks
+  convert(true);
+
   // ---- prologue: inputs of chunk 0 (and the keys of chunk 1), then chunk 0's forward
   if (nchunks > 0) {
     WinRegs w0, w1;
@@ -817,11 +847,11 @@ stream_mlp_kernel(ShardedParams p) {
     for (int J = J0; J < J0 + NJ; ++J) {
       f32x4 W1T[ND], W2T[NU][NDT];
 #pragma unroll
-      for (int t = 0; t < ND; ++t) W1T[t] = ld1(0, false, J, t);
+      for (int t = 0; t < ND; ++t) W1T[t] = ld1(0, J, t);
 #pragma unroll
       for (int a = 0; a < NU; ++a)
 #pragma unroll
-        for (int bb = 0; bb < NDT; ++bb) W2T[a][bb] = ld2(0, false, J, a, bb);
+        for (int bb = 0; bb < NDT; ++bb) W2T[a][bb] = ld2(0, J, a, bb);
       forward_tile(Xc, W1T, J);
       __syncthreads();
       window_sums(W2T);
@@ -834,7 +864,7 @@ stream_mlp_kernel(ShardedParams p) {
       group_barrier(ctr, G * (++nbar), err);
       xadd(xYh_at(par, 1 - pm), yh);
     }
-    prefetch(J0, false);
+    prefetch(J0);
     finish_d2(0, d0, Xc);
     __syncthreads();
   }
@@ -843,7 +873,6 @@ stream_mlp_kernel(ShardedParams p) {
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t0 = ch * BC, te = min(N, t0 + BC) - 1, ce = te - t0;
     const bool more = ch + 1 < nchunks;
-    const bool src_t = ch > 0, dst_t = more;   // state layouts read and written by this pass
     const float Ate = cA[ce], Bte = cB[ce], Pc = cP[0];
     // Ah W2^T, Ah S2^T (scaled by A_q, B_q at the end), held transposed like
     // yh: tile [m][bb] gives lane l the query row 16 m + (l & 15) and the value
@@ -899,7 +928,7 @@ stream_mlp_kernel(ShardedParams p) {
         }
         *reinterpret_cast<bf16x4*>(AT + (16 * wave + c16) * LT + 16 * m + 4 * g) = a4;
       }
-      __syncthreads();   // W2 image, AT
+      lds_sync();   // W2 image, AT
 
       // ---- D1 = (D2 W2) .* gelu'(Z) [tok x 16 units], then perm32 operands over tokens
       bf16x8 fd[NT / 2], fm[NT / 2], fs[NT / 2];
@@ -978,10 +1007,10 @@ stream_mlp_kernel(ShardedParams p) {
           W1T[t][r] = Ate * w1 + Bte * s1 - um[r];
           S1T[t][r] = Pc * s1 - us[r];
         }
-        st1(W1T[t], 0, dst_t, J, t);
-        st1(S1T[t], 1, dst_t, J, t);
+        st1(W1T[t], 0, J, t);
+        st1(S1T[t], 1, J, t);
       }
-      __syncthreads();   // Ah complete; every wave is done with the W2 image
+      lds_sync();   // Ah complete; every wave is done with the W2 image
 
       // ---- next chunk's forward on the updated rows: A' -> An^T, saved for the next pass
       if (more) forward_tile(Xn, W1T, J);
@@ -993,11 +1022,11 @@ stream_mlp_kernel(ShardedParams p) {
       for (int a = 0; a < NU; ++a)
 #pragma unroll
         for (int bb = 0; bb < NDT; ++bb) {
-          W2T[a][bb] = ld2(0, src_t, J, a, bb);
-          S2T[a][bb] = ld2(1, src_t, J, a, bb);
+          W2T[a][bb] = ld2(0, J, a, bb);
+          S2T[a][bb] = ld2(1, J, a, bb);
         }
       // (the next pass's first tile is fetched after the chunk inputs are staged)
-      if (J + 1 < J0 + NJ) prefetch(J + 1, src_t);
+      if (J + 1 < J0 + NJ) prefetch(J + 1);
       // ---- Q2 partial: Ah A^T, this wave's 16 query rows [q x tok]
 #pragma unroll
       for (int k0 = 0; k0 < HJ; k0 += 32) {
@@ -1055,17 +1084,17 @@ stream_mlp_kernel(ShardedParams p) {
               W2T[a][bb][r] = Ate * w2 + Bte * s2 - um[r];
               S2T[a][bb][r] = Pc * s2 - us[r];
             }
-            st2(W2T[a][bb], 0, dst_t, J, a, bb);
-            st2(S2T[a][bb], 1, dst_t, J, a, bb);
+            st2(W2T[a][bb], 0, J, a, bb);
+            st2(S2T[a][bb], 1, J, a, bb);
           }
         }
       }
       // ---- next chunk's window sums A' W2'^T [tok x this wave's dv]
       if (more) {
-        __syncthreads();   // An^T complete
+        lds_sync();   // An^T complete
         window_sums(W2T);
       }
-      __syncthreads();
+      lds_sync();
     }
 
     // ---- end of the pass: Q2 = C .* (Ah A^T) -> Q2^T [tok][q]
@@ -1079,7 +1108,7 @@ stream_mlp_kernel(ShardedParams p) {
       *reinterpret_cast<bf16x4*>(Q2T + (16 * m + c16) * LQ + 16 * wave + 4 * g) = c4;
     }
     }
-    __syncthreads();
+    lds_sync();
     // this member's part of y - q = A_q Ah W2^T + B_q Ah S2^T - Q2 D2 (transposed tiles)
     f32x4 yp[NQ][NDT];
     {
@@ -1135,7 +1164,7 @@ stream_mlp_kernel(ShardedParams p) {
       if (more) stage_next(ch + 1);
       group_wait(ctr, G * (++nbar), err);
     } else {
-      __syncthreads();
+      lds_sync();
       if (more) stage_next(ch + 1);
     }
     if constexpr (G > 1) {
@@ -1175,7 +1204,7 @@ stream_mlp_kernel(ShardedParams p) {
         sum = rowsum(sum);
         if (g == 0) OA[wv * BC + 16 * mi + c16] = sum;
       }
-      __syncthreads();
+      lds_sync();
 #pragma unroll
       for (int mi = 0; mi < MQ; ++mi) {
         mu[mi] = across(OA, BC, 16 * mi + c16) * (1.f / DV);
@@ -1190,7 +1219,7 @@ stream_mlp_kernel(ShardedParams p) {
         sum = rowsum(sum);
         if (g == 0) OB[wv * BC + 16 * mi + c16] = sum;
       }
-      __syncthreads();
+      lds_sync();
 #pragma unroll
       for (int mi = 0; mi < MQ; ++mi) {
         rs[mi] = 1.f / sqrtf(across(OB, BC, 16 * mi + c16) * (1.f / DV) + ln_eps);
@@ -1219,17 +1248,20 @@ stream_mlp_kernel(ShardedParams p) {
     }
     if (more) {
       wait_vmem();       // this wave's loads into LDS have landed
-      __syncthreads();   // and everyone's
+      lds_sync();   // and everyone's
       if constexpr (lnorm) ln_d2_lds(W2L, Xn);
       else if constexpr (shaped) shaped_d2_lds(W2L, Xn);
       else finish_d2_lds(W2L, Xn);
-      prefetch(J0, dst_t);
+      prefetch(J0);
       bf16* tmp = Xc;
       Xc = Xn;
       Xn = tmp;
-      __syncthreads();
+      lds_sync();
     }
   }
+
+  // ---- the state back to the caller's layout
+  convert(false);
 
   // ---- halo and count (every read of the old halo happened in the
   // prologue; with G = 2 the barrier orders it after the partner's reads)
