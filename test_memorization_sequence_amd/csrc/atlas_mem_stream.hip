@@ -45,6 +45,10 @@ namespace streamed {
 
 using namespace mfma;
 
+__device__ __forceinline__ bf16x8 zero8() {
+  return bf16x8{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+}
+
 template <int D_, int DV_, int H_, int WP_, int BC_, int G_>
 struct TShape {
   static constexpr int D = D_, DV = DV_, H = H_, WP = WP_, BC = BC_, G = G_;
@@ -950,11 +954,15 @@ stream_mlp_kernel(ShardedParams p) {
             const float lo = d1[2 * s][r] * z[2 * s][r], hi = d1[2 * s + 1][r] * z[2 * s + 1][r];
             fd[s][r] = (bf16)(-lo);
             fd[s][4 + r] = (bf16)(-hi);
-            fm[s][r] = (bf16)(lo * cM[tl]);
-            fm[s][4 + r] = (bf16)(hi * cM[th]);
-            fs[s][r] = (bf16)(lo * cS[tl]);
-            fs[s][4 + r] = (bf16)(hi * cS[th]);
+            fm[s][r] = (bf16)(-(lo * cM[tl]));
+            fm[s][4 + r] = (bf16)(-(hi * cM[th]));
+            fs[s][r] = (bf16)(-(lo * cS[tl]));
+            fs[s][4 + r] = (bf16)(-(hi * cS[th]));
           }
+        // without momentum S and its operands are zero, so every momentum
+        // product below is an exact zero and needs no branch
+#pragma unroll
+        for (int s = 0; s < NT / 2; ++s) fs[s] = mom ? fs[s] : zero8();
       }
 
       // ---- Zq^T = A_q (W1 Xq^T) + B_q (S1 Xq^T) - D1^T Q1^T [16 units x q]; Ah = gelu
@@ -974,7 +982,7 @@ stream_mlp_kernel(ShardedParams p) {
           for (int m = 0; m < NQ; ++m) {
             const bf16x8 xb = ld_perm(Xq, LX, 16 * m, 32 * s, lane);
             a1[m] = mma(aw, xb, a1[m]);
-            if (mom) a2[m] = mma(as, xb, a2[m]);
+            a2[m] = mma(as, xb, a2[m]);
           }
         }
 #pragma unroll
@@ -991,22 +999,26 @@ stream_mlp_kernel(ShardedParams p) {
         }
       }
 
-      // ---- W1/S1 update [d x 16 units]; written back at once
+      // ---- W1/S1 update [d x 16 units]: the products accumulate onto the
+      // decayed state (their operands fm, fs carry the minus sign); written
+      // back at once
 #pragma unroll
       for (int t = 0; t < ND; ++t) {
-        f32x4 um = zero4(), us = zero4();
+        f32x4 um, us;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float w1 = W1T[t][r], s1 = S1T[t][r];
+          um[r] = Ate * w1 + Bte * s1;
+          us[r] = Pc * s1;
+        }
 #pragma unroll
         for (int s = 0; s < NT / 2; ++s) {
           const bf16x8 xa = ld_tr_perm(Xc, LX, 16 * t, 32 * s, lane);
           um = mma(xa, fm[s], um);
-          if (mom) us = mma(xa, fs[s], us);
+          us = mma(xa, fs[s], us);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float w1 = W1T[t][r], s1 = S1T[t][r];
-          W1T[t][r] = Ate * w1 + Bte * s1 - um[r];
-          S1T[t][r] = Pc * s1 - us[r];
-        }
+        W1T[t] = um;
+        S1T[t] = us;
         st1(W1T[t], 0, J, t);
         st1(S1T[t], 1, J, t);
       }
@@ -1049,12 +1061,13 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
           for (int bb = 0; bb < NDT; ++bb) {
             yw[m][bb] = mma(bw[bb], ah, yw[m][bb]);
-            if (mom) ys[m][bb] = mma(bs[bb], ah, ys[m][bb]);
+            ys[m][bb] = mma(bs[bb], ah, ys[m][bb]);
           }
         }
       }
       // ---- W2/S2 update [units x this wave's dv]: A^T (cM .* D2), the D2
-      // operand scaled along the tokens; written back at once
+      // operand scaled along the tokens (and negated: the products accumulate
+      // onto the decayed state); written back at once
       {
         bf16x8 dm[NDT][NT / 2], ds[NDT][NT / 2];
 #pragma unroll
@@ -1062,8 +1075,15 @@ stream_mlp_kernel(ShardedParams p) {
 #pragma unroll
           for (int s = 0; s < NT / 2; ++s) {
             const bf16x8 bd = ld_tr_nat(D2, LV, dvw + 16 * bb, 32 * s, lane);
-            dm[bb][s] = scaled_k(bd, cM + 32 * s + 8 * g);
-            ds[bb][s] = scaled_k(bd, cS + 32 * s + 8 * g);
+            const float* sm = cM + 32 * s + 8 * g;
+            const float* ss = cS + 32 * s + 8 * g;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float x = (float)bd[i];
+              dm[bb][s][i] = (bf16)(-(x * sm[i]));
+              ds[bb][s][i] = (bf16)(-(x * ss[i]));
+            }
+            ds[bb][s] = mom ? ds[bb][s] : zero8();
           }
 #pragma unroll
         for (int a = 0; a < NU; ++a) {
@@ -1072,18 +1092,20 @@ stream_mlp_kernel(ShardedParams p) {
           for (int s = 0; s < NT / 2; ++s) at[s] = ld_nat(AT, LT, 16 * a, 32 * s, lane);
 #pragma unroll
           for (int bb = 0; bb < NDT; ++bb) {
-            f32x4 um = zero4(), us = zero4();
-#pragma unroll
-            for (int s = 0; s < NT / 2; ++s) {
-              um = mma(at[s], dm[bb][s], um);
-              if (mom) us = mma(at[s], ds[bb][s], us);
-            }
+            f32x4 um, us;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float w2 = W2T[a][bb][r], s2 = S2T[a][bb][r];
-              W2T[a][bb][r] = Ate * w2 + Bte * s2 - um[r];
-              S2T[a][bb][r] = Pc * s2 - us[r];
+              um[r] = Ate * w2 + Bte * s2;
+              us[r] = Pc * s2;
             }
+#pragma unroll
+            for (int s = 0; s < NT / 2; ++s) {
+              um = mma(at[s], dm[bb][s], um);
+              us = mma(at[s], ds[bb][s], us);
+            }
+            W2T[a][bb] = um;
+            S2T[a][bb] = us;
             st2(W2T[a][bb], 0, J, a, bb);
             st2(S2T[a][bb], 1, J, a, bb);
           }
