@@ -223,7 +223,8 @@ atlas_status atlas_mem_forward_ex(atlas_mem_t h,
  * that overlap on one device (two streams, two threads) race and give wrong
  * results.  errors (device, optional, 4-byte aligned) receives the call's
  * device error word after its kernels (0: none; bit 0: a group barrier timed
- * out and the outputs are invalid); it replaces atlas_mem_device_errors.
+ * out and the outputs are invalid; bit 1: the workgroups of one sequence did
+ * not all run on one XCD); it replaces atlas_mem_device_errors.
  * Errors: as atlas_mem_forward_ex, plus SCRATCH_TOO_SMALL; UNSUPPORTED /
  * INVALID_ARGUMENT for a config atlas_mem_init would reject.               */
 atlas_status atlas_mem_forward_noalloc(const atlas_mem_config* cfg,
@@ -247,8 +248,9 @@ int atlas_mem_kernel_family(atlas_mem_t h);
 
 /* Device-side error word of the handle's last forward call (0: none; bit 0:
  * a group barrier of the sharded, streamed or grouped kernel timed out, its
- * outputs are invalid; bit 1: the workgroups of one grouped-kernel sequence
- * did not all run on one XCD, so their exchanges were not ordered).
+ * outputs are invalid; bit 1: the workgroups of one sequence (sharded group,
+ * streamed pair or grouped group) did not all run on one XCD, so their
+ * exchanges were not ordered and the outputs are invalid).
  * Synchronises the device.  Errors: INVALID_ARGUMENT, HIP.                 */
 atlas_status atlas_mem_device_errors(atlas_mem_t h, unsigned* flags);
 

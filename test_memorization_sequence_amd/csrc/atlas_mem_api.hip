@@ -338,7 +338,7 @@ static WsPlan plan_workspace(const atlas_mem_s* h) {
   const size_t members = (size_t)h->n_seq * h->group;
   pl.mws_off = h->var ? align_up(h->var->ws_bytes * members, 256) : 0;
   const size_t pctrl_off = align_up(pl.mws_off + h->mws_stride * members, 256);
-  const size_t ctrl_bytes = align_up((1 + (size_t)h->n_seq) * 4, 256);
+  const size_t ctrl_bytes = align_up((1 + 2 * (size_t)h->n_seq) * 4, 256);
   pl.ws_bytes = h->var ? pctrl_off + (h->group > 1 ? ctrl_bytes : 0) : grouped ? ctrl_grouped + ctrl_bytes : 0;
   pl.ctrl_off = h->var ? pctrl_off : ctrl_grouped;
   pl.has_ctrl = grouped || h->group > 1;
@@ -410,7 +410,7 @@ atlas_status atlas_mem_init(const atlas_mem_config* cfg, atlas_mem_t* out) {
   }
   bind_workspace(&tmp, pl, ws, coef);
   if (tmp.ctrl) {
-    if ((e = hipMemset(tmp.ctrl, 0, (1 + (size_t)tmp.n_seq) * 4)) != hipSuccess) {
+    if ((e = hipMemset(tmp.ctrl, 0, (1 + 2 * (size_t)tmp.n_seq) * 4)) != hipSuccess) {
       (void)hipFree(ws);
       (void)hipFree(coef);
       return hip_fail(e);

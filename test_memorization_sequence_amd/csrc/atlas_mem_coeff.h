@@ -31,6 +31,7 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   __shared__ double G[BC + 1];      // prefix sums of e_{n->te} theta_n
   if (p.ctrl != nullptr && chunk == 0 && threadIdx.x == 0) {
     p.ctrl[1 + seq] = 0u;            // group barrier counter of this sequence
+    p.ctrl[1 + gridDim.x / (unsigned)p.nchunks + seq] = 0u;   // XCDs its members ran on
     if (seq == 0) p.ctrl[0] = 0u;    // error word of the call
   }
   float* out = p.coef + ((size_t)seq * p.nchunks + chunk) * p.coef_stride;
@@ -96,6 +97,7 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
     if (n < nb) {
       float K = 1.f, e = 1.f;
       F[n][n] = th[n];
+#pragma unroll 8
       for (int t = n + 1; t < nb; ++t) {
         e *= et[t];
         K = (1.f - al[t]) * K + e;
@@ -108,6 +110,7 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   }
   if (threadIdx.x == 64) {
     float a = 1.f, b = 0.f, e0 = 1.f;
+#pragma unroll 8
     for (int t = 0; t < BC; ++t) {
       if (t < nb) {
         a *= 1.f - al[t];
@@ -127,6 +130,7 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   if (threadIdx.x < BC) {
     const int t = threadIdx.x;
     double acc = 0.0;
+#pragma unroll 8
     for (int n = 0; n < BC; ++n) {
       acc += F[t][n];
       F[t][n] = acc;
@@ -134,6 +138,7 @@ __global__ void __launch_bounds__(256) coeff_kernel(CoeffParams p) {
   } else if (threadIdx.x == BC) {
     double acc = 0.0;
     G[0] = 0.0;
+#pragma unroll 8
     for (int n = 0; n < BC; ++n) {
       acc += (double)Gv[n];
       G[n + 1] = acc;

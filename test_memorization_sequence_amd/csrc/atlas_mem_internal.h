@@ -141,7 +141,7 @@ struct CoeffParams {
   const float* theta;
   const char* state;
   float* coef;
-  unsigned* ctrl;   // sharded kernel: [0] error word, [1 + s] barrier counter of sequence s; else null
+  unsigned* ctrl;   // groups: [0] error word, [1 + s] barrier counter and [1 + n + s] XCD mask of sequence s (n sequences); else null
   const void* q;    // Q1 precompute (sharded kernel): bf16 queries and keys [seq][N][d]
   const void* k;
   size_t off_halo_k;

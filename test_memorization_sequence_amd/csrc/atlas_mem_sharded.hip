@@ -133,6 +133,8 @@ sharded_mlp_kernel(ShardedParams p) {
   float* yobuf = reinterpret_cast<float*>(xw + S::xYo);
   unsigned* ctr = p.ctrl + 1 + seq;
   unsigned* err = p.ctrl;
+  unsigned* xmask = p.ctrl + 1 + p.n_seq + seq;
+  if (tid == 0) report_xcc(xmask);
   unsigned nbar = 0;
 
   bf16* RX = reinterpret_cast<bf16*>(smem + S::oRX);
@@ -349,6 +351,7 @@ sharded_mlp_kernel(ShardedParams p) {
       }
     }
     group_barrier(ctr, G * (++nbar), err);
+    if (ch == 0 && tid == 0) check_xcc(xmask, err);
 
     // ---- reduce-scatter: this member's window rows -> D2 rows; previous chunk's outputs
     {

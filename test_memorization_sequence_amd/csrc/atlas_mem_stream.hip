@@ -140,6 +140,8 @@ stream_mlp_kernel(ShardedParams p) {
   const int J0 = pm * NJ;   // first super tile of this member
   unsigned* ctr = G > 1 ? p.ctrl + 1 + seq : nullptr;
   unsigned* err = p.ctrl;
+  unsigned* xmask = G > 1 ? p.ctrl + 1 + p.n_seq + seq : nullptr;
+  if (G > 1 && threadIdx.x == 0) report_xcc(xmask);
   unsigned nbar = 0;
   char* xw = p.xws + (size_t)seq * S::xbytes;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
@@ -866,6 +868,7 @@ stream_mlp_kernel(ShardedParams p) {
       const int par = 1;   // chunk 0 uses parity 0; the prologue the other slot
       xput(xYh_at(par, pm), yh);
       group_barrier(ctr, G * (++nbar), err);
+      if (tid == 0) check_xcc(xmask, err);
       xadd(xYh_at(par, 1 - pm), yh);
     }
     prefetch(J0);
