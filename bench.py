@@ -34,13 +34,13 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 # changed kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
     # (workload, kernel, optimizer, tokens per sequence), l2 bias, plain memory
-    ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "d3417b4354857f00", "bytes": 76.61e9},
-    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "a571c0e17f53322c", "bytes": 27.74e9},
-    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "fa58fd57df42e5c3", "bytes": 91.68e9},
-    ("linear64_delta", "chunk_kernel", "gd", 1024): {"src": "fa58fd57df42e5c3", "bytes": 1.67e6},
+    ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "ae24a0f87f9294ed", "bytes": 76.61e9},
+    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "7c03cf83fdf18b80", "bytes": 27.74e9},
+    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "2ec9a9f67155db0a", "bytes": 91.88e9},
+    ("linear64_delta", "chunk_kernel", "gd", 1024): {"src": "2ec9a9f67155db0a", "bytes": 1.67e6},
     # the recurrence and the retrieval after it (the pair the kernel events bracket)
-    ("linear_poly2", "linear_rec_kernel", "gd", 4096): {"src": "50154b8d85754b04", "bytes": 0.344e9},
-    ("mlp64", "sharded_mlp_kernel", "gd", 8192): {"src": "25408e691000463a", "bytes": 1.778e9},
+    ("linear_poly2", "linear_rec_kernel", "gd", 4096): {"src": "420997f0416615d7", "bytes": 0.344e9},
+    ("mlp64", "sharded_mlp_kernel", "gd", 8192): {"src": "a1d54f08b69eceb5", "bytes": 1.782e9},
 }
 
 
