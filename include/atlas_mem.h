@@ -162,8 +162,12 @@ typedef struct {
 } atlas_mem_state_layout;
 
 /* Validates cfg, selects the kernels and allocates the device workspace on
- * the current HIP device.  No kernel is launched.  On success *out holds a
- * handle that must be released with atlas_mem_free.
+ * the current HIP device.  No kernel is launched.  cfg describes one memory
+ * per (batch, head) sequence: its form (Titans review sec. 3.1, "Memory
+ * Architecture"), the feature map (ATLAS review sec. 3.1), the window c of
+ * the Omega rule (ATLAS review sec. 3.2), the chunk b (ATLAS review sec. 3.3)
+ * and the attentional bias (Miras review, "Alternative Attentional Biases").
+ * On success *out holds a handle that must be released with atlas_mem_free.
  * Errors: INVALID_ARGUMENT (bad or inconsistent sizes, null out),
  * UNSUPPORTED (no kernel for this shape: see atlas_mem_supported),
  * OUT_OF_MEMORY, HIP.                                                      */
@@ -178,7 +182,12 @@ size_t atlas_mem_state_bytes(atlas_mem_t h);
 atlas_status atlas_mem_state_layout_of(atlas_mem_t h, atlas_mem_state_layout* out);
 
 /* Runs one call over seq_len tokens of every sequence, enqueued on `stream`
- * (no host synchronisation, no allocation).  Chunks start at the call's
+ * (no host synchronisation, no allocation): the chunked update of the
+ * memory and the per-token retrieval defined at the top of this file (ATLAS
+ * review sec. 3.3 "Parallelizing Omega Rule"; Titans review sec. 3.2 "How to
+ * Parallelize the Long-term Memory Training").  stream is a hipStream_t
+ * passed as void*, so that this header needs no HIP header (NULL: the
+ * default stream).  Chunks start at the call's
  * first token, so a call split in two equals one call when the first part's
  * length is a multiple of the chunk.
  *   q, k   [B][H][N][d_k]   io_dtype, contiguous
