@@ -29,7 +29,7 @@ def _cfg(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(window=65), binding.ERR_UNSUPPORTED),         # c > chunk
-    (dict(hidden=384), binding.ERR_UNSUPPORTED),        # no kernel for this width
+    (dict(hidden=320), binding.ERR_UNSUPPORTED),        # no kernel for this width
     (dict(d_k=64), binding.ERR_INVALID),                # residual needs d_k == d_v
     (dict(batch=0), binding.ERR_INVALID),
     (dict(seq_len=-1), binding.ERR_INVALID),

@@ -80,6 +80,36 @@ def test_parity_small(B, name, kernel, recipe):
     assert r["halo_exact"] and r["count_exact"], r
 
 
+# Streamed shapes beyond the workloads' own: hidden widths 3 d and 2 d at
+# d = 128, and the window c = 1 (64 window rows).
+EXTRA_STREAMED = {"h384": dict(hidden=384), "h256": dict(hidden=256), "c1": dict(window=1)}
+
+
+@pytest.mark.parametrize("recipe", ["preset", "lively"])
+@pytest.mark.parametrize("bias", ["l2", "lp3"])
+@pytest.mark.parametrize("shape", list(EXTRA_STREAMED))
+def test_parity_extra_streamed_shapes(B, shape, bias, recipe):
+    from dataclasses import replace
+    wl = replace(WORKLOADS["layer_scale"], **EXTRA_STREAMED[shape])
+    if bias != "l2":
+        wl = _with_bias(wl, bias)
+    wl = wl.with_shape(batch=1, heads=2, seq_len=SMALL_N)
+    if recipe == "lively":
+        wl = lively(wl)
+    _say(f"[parity-shape] layer_scale {shape} {bias} {recipe} B=1 H=2 N={SMALL_N}")
+    binding, H = B
+    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl, kernel="auto")
+    assert mem.family() == "streamed"
+    r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
+    _say(f"[parity-shape] {shape} {bias} {recipe}: {r}")
+    tol = H.tol_of(wl)
+    assert np.isfinite(out_g).all()
+    for key in ("out", "memory_part", "weights", "momentum"):
+        if key in r:
+            assert r[key] <= tol, (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
+
+
 @pytest.mark.parametrize("name,kernel", [("linear_poly2", "auto"), ("mlp64", "sharded"), ("layer_scale", "sharded"),
                                          ("atlas_long", "auto"), ("mlp64", "streamed"), ("layer_scale", "streamed"),
                                          ("atlas_long", "per_sequence"), ("layer_scale", "grouped")])
