@@ -327,8 +327,9 @@ struct WsPlan {
 
 static WsPlan plan_workspace(const atlas_mem_s* h) {
   WsPlan pl;
-  // sharded, and streamed: exchange buffers / tile-major state per sequence,
-  // then the control words (error word + one barrier counter per sequence)
+  // sharded, and streamed: exchange buffers / state blocks per sequence, then
+  // the control words (error word, one barrier counter per sequence, one XCD
+  // mask per sequence)
   const bool grouped = h->svar || h->tvar || h->gvar;
   const size_t xbytes = h->svar   ? h->svar->xbytes()
                         : h->tvar ? h->tvar->xbytes()
