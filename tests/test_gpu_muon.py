@@ -75,7 +75,9 @@ MUON_CASES = [("linear64_delta", 3 * 64 + 17, {}), ("linear_poly2", 3 * 64 + 17,
               ("mlp64", 2 * 64 + 5, {"window": 8}), ("mlp64", 2 * 64 + 5, {"ns_steps": 2}),
               ("mlp64", 2 * 64 + 5, {"bias": "lp", "bias_p": 3.0}),
               ("mlp64", 2 * 64 + 5, {"bias": "huber", "sign_alpha": 16.0}),
-              ("layer_scale", 64 + 9, {})]
+              ("layer_scale", 64 + 9, {}),
+              # shapes beyond the workloads': hidden width 2 d, and the window c = 1
+              ("layer_scale", 64 + 9, {"hidden": 256}), ("layer_scale", 64 + 9, {"window": 1})]
 
 
 @pytest.mark.parametrize("recipe", ["preset", "lively"])

@@ -522,6 +522,32 @@ def test_parity_gated_memory(B, name, bias, recipe, std):
     assert r["halo_exact"] and r["count_exact"], r
 
 
+@pytest.mark.parametrize("recipe", ["preset", "lively"])
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("shape", list(EXTRA_STREAMED))
+def test_parity_extra_per_sequence_shapes(B, shape, gated, recipe):
+    """The same extra shapes on the per-sequence family, plain and gated (the
+    gated memory runs on this family only)."""
+    from dataclasses import replace
+    wl = replace(WORKLOADS["layer_scale"], **EXTRA_STREAMED[shape])
+    if gated:
+        wl = replace(wl, gated=True, init_std=0.2)
+    wl = wl.with_shape(batch=1, heads=2, seq_len=SMALL_N)
+    if recipe == "lively":
+        wl = lively(wl)
+    _say(f"[parity-shape-ps] layer_scale {shape} gated={gated} {recipe} B=1 H=2 N={SMALL_N}")
+    binding, H = B
+    inputs, out_g, st_g, out_o, st_o, mem = _run_both(B, wl, kernel="per_sequence")
+    r = H.compare(wl, inputs, out_g, st_g, out_o, st_o)
+    _say(f"[parity-shape-ps] {shape} gated={gated} {recipe}: {r}")
+    tol = H.tol_of(wl)
+    assert np.isfinite(out_g).all()
+    for key in ("out", "memory_part", "weights", "momentum"):
+        if key in r:
+            assert r[key] <= tol, (key, r)
+    assert r["halo_exact"] and r["count_exact"], r
+
+
 @pytest.mark.parametrize("variant", ["lp3", "huber_smooth", "huber", "layernorm", "layernorm_dot", "gated"])
 def test_full_size_sampled_variants(B, variant):
     """The layer-scale shape in the benchmark's launch configuration
