@@ -34,13 +34,13 @@ CSRC = os.path.join(ROOT, "test_memorization_sequence_amd", "csrc")
 # changed kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
     # (workload, kernel, optimizer, tokens per sequence), l2 bias, plain memory
-    ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "acd0e9f4bb0d734a", "bytes": 76.62e9},
-    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "7c03cf83fdf18b80", "bytes": 27.74e9},
-    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "58a492dd7367f3f2", "bytes": 92.0e9},
-    ("linear64_delta", "chunk_kernel", "gd", 1024): {"src": "58a492dd7367f3f2", "bytes": 1.67e6},
+    ("layer_scale", "stream_mlp_kernel", "gd", 16384): {"src": "c1bb50a4302709b0", "bytes": 76.59e9},
+    ("atlas_long", "grouped_kernel", "gd", 32768): {"src": "f796b652af5fe317", "bytes": 27.73e9},
+    ("layer_scale", "chunk_kernel", "muon", 64): {"src": "fc044794f9a08d4f", "bytes": 91.9e9},
+    ("linear64_delta", "chunk_kernel", "gd", 1024): {"src": "fc044794f9a08d4f", "bytes": 1.67e6},
     # the recurrence and the retrieval after it (the pair the kernel events bracket)
     ("linear_poly2", "linear_rec_kernel", "gd", 4096): {"src": "420997f0416615d7", "bytes": 0.344e9},
-    ("mlp64", "sharded_mlp_kernel", "gd", 8192): {"src": "a1d54f08b69eceb5", "bytes": 1.782e9},
+    ("mlp64", "sharded_mlp_kernel", "gd", 8192): {"src": "a93810f9f3be7fb4", "bytes": 1.779e9},
 }
 
 

@@ -6,14 +6,6 @@
 
 namespace atlas {
 
-// Monotonic arrival counter per group; barrier number `k` (1, 2, ...) waits
-// for G*k arrivals.  The members of a group share one XCD and its L2, so no
-// device-wide cache write-back or L2 invalidation is needed: every wave waits
-// until its own stores are complete (they write through the CU's L1), the
-// counter is a device-scope atomic, and after the wait every wave invalidates
-// its CU's L1 (vector cache) so that later loads read the partners' data from
-// L2.  Bounded: about 2^24 polls, then the call's error word is set and every
-// later wait returns at once.
 // The XCD (HW_REG_XCC_ID[3:0]) the calling wave runs on.  The members of a
 // group report it into a mask word (one bit per XCD) before their first
 // barrier and check after it that one bit is set: a placement that breaks the
@@ -26,6 +18,14 @@ __device__ __forceinline__ void check_xcc(const unsigned* mask, unsigned* err) {
   if (__builtin_popcount(m) != 1) atomicOr(err, 2u);
 }
 
+// Monotonic arrival counter per group; barrier number `k` (1, 2, ...) waits
+// for G*k arrivals.  The members of a group share one XCD and its L2, so no
+// device-wide cache write-back or L2 invalidation is needed: every wave waits
+// until its own stores are complete (they write through the CU's L1), the
+// counter is a device-scope atomic, and after the wait every wave invalidates
+// its CU's L1 (vector cache) so that later loads read the partners' data from
+// L2.  Bounded: about 2^24 polls, then the call's error word is set and every
+// later wait returns at once.
 __device__ __forceinline__ void group_barrier(unsigned* ctr, unsigned target, unsigned* err) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

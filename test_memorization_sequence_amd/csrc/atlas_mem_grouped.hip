@@ -121,12 +121,9 @@ grouped_kernel(GroupedParams p) {
   unsigned* err = p.ctrl;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   unsigned* xmask = reinterpret_cast<unsigned*>(p.gws + (size_t)seq * p.gseq_bytes + S::xMask);
-  if (tid == 0) {
-    // the barrier needs every member on one L2: each member reports the XCD it
-    // runs on (HW_REG_XCC_ID[3:0]); checked after the first group barrier
-    const unsigned hw = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
-    atomicOr(xmask, 1u << (hw & 15u));
-  }
+  // the barrier needs every member on one L2: each member reports the XCD it
+  // runs on; checked after the first group barrier
+  if (tid == 0) report_xcc(xmask);
 
   const int N = p.N, c = p.c, W = BC + c - 1, nch = p.nchunks;
   const bool mom = p.momentum != 0, dot = p.bias == BIAS_DOT, res = p.residual != 0;
@@ -359,10 +356,7 @@ grouped_kernel(GroupedParams p) {
       }
     }
     group_wait(ctr, G * (++nbar), err);
-    if (ch == 0 && tid == 0) {
-      const unsigned m = __hip_atomic_load(xmask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__builtin_popcount(m) != 1) atomicOr(err, 2u);
-    }
+    if (ch == 0 && tid == 0) check_xcc(xmask, err);
 
     // ---- reduce-scatter: this member's window rows -> D2 rows; the previous chunk's outputs
     {
