@@ -1,6 +1,7 @@
 """CPU replay of the global-memory index arithmetic of the grouped-family
 kernels (the MLP kernel of atlas_mem_grouped.hip, the linear kernels of
-atlas_mem_linear.hip and the phi / Q1 kernels of atlas_mem_phi.h): every
+atlas_mem_linear.hip and the phi / Q1 kernels of atlas_mem_phi.h), of the
+prologue's GEMM kernels and of the streamed kernel's state blocks: every
 offset a lane forms is recomputed here, for every wave, lane, chunk and tile
 the kernels visit, at the library's shapes and ragged lengths, and checked
 against the size of the array it addresses.  Accesses through range-checked
@@ -412,3 +413,43 @@ def fused_prologue(B, N, dm, H, d, K, r):
                                             (1, 600, 512, 1, 256, 3, 8), (1, 16384, 1536, 12, 128, 4, 16)])
 def test_fused_prologue_indices(B, N, dm, H, d, K, r):
     fused_prologue(B, N, dm, H, d, K, r)
+
+
+# ----------------------------------------------------------------------------- streamed state blocks
+# The streamed kernel (atlas_mem_stream.hip) keeps the state between passes in
+# blocks, one per super tile J (HJ = 64 hidden units) and wave w: block
+# J * 4 + w holds that wave's W1 rows [ND], S1 rows [ND], W2 values [NU][NDT],
+# S2 values [NU][NDT] (fp32) and A, gelu'(Z) [NT] (bf16), each a 1 KB tile in
+# lane order.  A tile access is lane offset 16 l, the tile's place within its
+# 4 KB (immediate offset) and a wave-uniform scalar offset in 4 KB steps; the
+# exchange slots follow the blocks.
+STREAMED_SHAPES = [(128, 128, 512, 96), (128, 128, 512, 64), (128, 128, 384, 96), (128, 128, 256, 96),
+                   (64, 64, 256, 64), (64, 64, 256, 96)]
+
+
+@pytest.mark.parametrize("D,DV,H,WP", STREAMED_SHAPES)
+def test_streamed_state_blocks(D, DV, H, WP):
+    NW, HJ = 4, 64
+    ND, NU, NDT, NT = D // 16, HJ // 16, DV // NW // 16, WP // 16
+    TW1, TS1, TW2, TS2, TAG = 0, ND, 2 * ND, 2 * ND + NU * NDT, 2 * ND + 2 * NU * NDT
+    NTB = TAG + NT
+    SB = NTB * 1024
+    ts_bytes = (H // HJ) * NW * SB
+    # the fp32 state fills exactly the W1/S1/W2/S2 tiles of all blocks
+    assert (H // HJ) * NW * (2 * ND + 2 * NU * NDT) * 1024 == 2 * H * D * 4 + 2 * DV * H * 4
+    cover = np.zeros(ts_bytes // 16, dtype=np.int32)
+    for J in range(H // HJ):
+        for w in range(NW):
+            tiles = ([TW1 + t for t in range(ND)] + [TS1 + t for t in range(ND)]
+                     + [TW2 + a * NDT + b for a in range(NU) for b in range(NDT)]
+                     + [TS2 + a * NDT + b for a in range(NU) for b in range(NDT)]
+                     + [TAG + i for i in range(NT)])
+            assert sorted(tiles) == list(range(NTB))
+            for T in tiles:
+                imm = (T % 4) * 1024
+                assert imm < 4096   # the MUBUF immediate offset field
+                offs = (J * NW + w) * SB + (T // 4) * 4096 + imm + 16 * LANE
+                check(offs + 15, ts_bytes, ("block", J, w, T))
+                cover[offs // 16] += 1
+    # every 16 bytes of the blocks belong to exactly one lane of one tile
+    assert (cover == 1).all()
